@@ -1,0 +1,12 @@
+"""MI355X-native fused multi-tenant LoRA layer over an FP8 / MXFP4 base GEMM.
+
+The compute lives in the HIP library ``liblora_lowp.so`` (gfx950 kernels behind the C
+ABI in ``include/lora_lowp.h``); :mod:`precision_gemm_amd.ops` is its Python binding on
+torch device tensors.  Build the library with ``python -m precision_gemm_amd.build``.
+"""
+
+from .ops import (  # noqa: F401
+    LORA_FUSE_SHRINK, LORA_W_FP8_E4M3, LORA_W_MXFP4_E2M1, Adapters, LowpWeight, Segments,
+    alloc_workspace, build_segments, expand, gemm_lowp_lora_epilogue, plan_info, quant_act_mxfp8,
+    shrink, version, workspace_bytes, workspace_status,
+)

@@ -1,0 +1,108 @@
+// Device helpers shared by the gfx950 kernels: bf16 handling, the MXFP8 block
+// quantiser, and thin wrappers over the CDNA4 matrix instructions.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+
+namespace lora {
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest even (inputs are finite; NaN maps to a quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t b = __float_as_uint(f);
+  if ((b & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  b += 0x7fffu + ((b >> 16) & 1u);
+  return b >> 16;
+}
+
+// ---------------------------------------------------------------------------------
+// MXFP8 quantisation of one 32-element block (OCP Microscaling v1.0, e4m3 elements):
+//   scale code = E + 127 with E = floor(log2 max|x|) - 8, clamped to [-127, 127];
+//   element = RNE_e4m3(clamp(x * 2^-E, +-448)).
+// For a bf16 maximum with biased exponent field ef >= 1, floor(log2 max) = ef - 127, so
+// the code is ef - 8; zero and subnormal maxima (ef == 0) and ef <= 8 give E = -127,
+// code 0.  |bits| compares as an unsigned integer in the order of |x|.
+// The conversion uses v_cvt_pk_fp8_f32 (round to nearest even, OCP e4m3fn on gfx950);
+// its inputs are already clamped, and it keeps the sign of zero.
+// ---------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t mx_block_code(const uint4 (&in)[4]) {
+  us2 m = {0, 0};
+  const us2 mask = {0x7fff, 0x7fff};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t w[4] = {in[i].x, in[i].y, in[i].z, in[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      us2 v = __builtin_bit_cast(us2, w[j]) & mask;
+      m = __builtin_elementwise_max(m, v);
+    }
+  }
+  uint32_t mx = m.x > m.y ? m.x : m.y;
+  uint32_t ef = mx >> 7;
+  return ef > 8u ? ef - 8u : 0u;
+}
+
+__device__ __forceinline__ uint32_t cvt4_fp8(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+__device__ __forceinline__ float clamp448(float v) { return __builtin_fminf(__builtin_fmaxf(v, -448.f), 448.f); }
+
+// Quantise 32 bf16 (64 bytes in `in`) with scale code `code` into 32 e4m3 codes (out[2]).
+__device__ __forceinline__ void mx_block_quant(const uint4 (&in)[4], uint32_t code, uint4 (&out)[2]) {
+  const float inv = __uint_as_float((254u - code) << 23);  // 2^(127 - code) = 2^-E, exact
+  uint32_t r[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t w[4] = {in[i].x, in[i].y, in[i].z, in[i].w};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float a = clamp448(bf16_lo(w[2 * h]) * inv), b = clamp448(bf16_hi(w[2 * h]) * inv);
+      float c = clamp448(bf16_lo(w[2 * h + 1]) * inv), d = clamp448(bf16_hi(w[2 * h + 1]) * inv);
+      r[2 * i + h] = cvt4_fp8(a, b, c, d);
+    }
+  }
+  out[0] = make_uint4(r[0], r[1], r[2], r[3]);
+  out[1] = make_uint4(r[4], r[5], r[6], r[7]);
+}
+
+// ---------------------------------------------------------------------------------
+// Scaled MFMA, 16x16x128, gfx950.  Operand layout (measured with a one-instruction
+// probe against a CPU model, lane l, g = l / 16, row/column = l % 16):
+//   fp8 operand (8 dwords): bytes 0..15 hold k = 16g .. 16g+15, bytes 16..31 hold
+//                           k = 64+16g .. 64+16g+15;
+//   fp4 operand (4 dwords): nibble q (byte q/2, low nibble first) holds k = 32g + q;
+//   scale operand (byte 0): row/column l % 16, K-block g (k = 32g .. 32g+31);
+//   result: lane l, element v -> row 4g + v, column l % 16.
+// ---------------------------------------------------------------------------------
+template <int FMT_B>
+__device__ __forceinline__ v4f mfma_scaled_16x16x128(const uint4& alo, const uint4& ahi, const uint4& blo,
+                                                     const uint4& bhi, v4f acc, int sa, int sb) {
+  v8i a = {(int)alo.x, (int)alo.y, (int)alo.z, (int)alo.w, (int)ahi.x, (int)ahi.y, (int)ahi.z, (int)ahi.w};
+  v8i b = {(int)blo.x, (int)blo.y, (int)blo.z, (int)blo.w, (int)bhi.x, (int)bhi.y, (int)bhi.z, (int)bhi.w};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, FMT_B, 0, sa, 0, sb);
+}
+
+// bf16 MFMA 16x16x32.  A and B operands have mirrored layouts (lane l: row/column
+// l % 16, eight k values for lane group l / 16), so any fixed assignment of the eight
+// k values of a lane group works as long as both operands use it; the result layout
+// is that of every 16x16 MFMA (row 4g + v, column l % 16).
+__device__ __forceinline__ v4f mfma_bf16_16x16x32(const uint4& a, const uint4& b, v4f acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), acc, 0,
+                                                 0, 0);
+}
+
+__device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+__device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
+
+}  // namespace lora

@@ -1,0 +1,252 @@
+// C-ABI host layer: argument checks, the tile plan, workspace layout and launches.
+// Every check runs before anything is enqueued; nothing here allocates or synchronises.
+#include <stdint.h>
+#include <string.h>
+
+#include "lora_kernels.hpp"
+
+using namespace lora;
+
+namespace {
+
+constexpr int SPIN_LIMIT = 1 << 22;  // bounded wait in the fused launch (~0.5 s)
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
+inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
+inline int pow2_floor(long v) {
+  int p = 1;
+  while ((long)p * 2 <= v) p *= 2;
+  return p;
+}
+
+lora_status check_sizes(int32_t T, int32_t K, int32_t N) {
+  if (T < 0 || K <= 0 || N <= 0) return LORA_ERR_INVALID_ARG;
+  if (T > 65536 || K % 128 != 0 || N % 64 != 0) return LORA_ERR_UNSUPPORTED;
+  return LORA_OK;
+}
+
+lora_status check_adapters(int32_t n_adapters, int32_t r_max) {
+  if (n_adapters < 1 || r_max < 1) return LORA_ERR_INVALID_ARG;
+  if (n_adapters > MAX_ADAPTERS || r_max > MAX_RANK || r_max % 8 != 0) return LORA_ERR_UNSUPPORTED;
+  return LORA_OK;
+}
+
+// Tile plan: a pure function of the sizes, so lora_workspace_bytes and every call agree.
+LayerPlan make_plan(int T, int K, int N, int n_ad, int r_max, int fmt) {
+  LayerPlan pl{};
+  pl.fmt = fmt;
+  if (T <= 16) {
+    pl.TT = 1; pl.CT = 1; pl.XQ = false;
+  } else if (T <= 64) {
+    pl.TT = 4; pl.CT = 1; pl.XQ = false;
+  } else if (T <= 128) {
+    pl.TT = 8; pl.CT = (N % 128 == 0) ? 2 : 1; pl.XQ = false;
+  } else {
+    pl.TT = 8; pl.CT = (N % 256 == 0) ? 4 : ((N % 128 == 0) ? 2 : 1); pl.XQ = true;
+  }
+  pl.KC = (pl.TT == 1) ? 1024 : ((pl.TT <= 4) ? 512 : 256);
+  const int WN = 64 * pl.CT;
+  pl.n_cb = N / WN;
+  pl.n_tb = ceil_div(T, 16 * pl.TT);
+  const int tiles = pl.n_cb * pl.n_tb;
+  const int max_split = std::max(1, K / pl.KC);
+  int ks = (tiles >= 384) ? 1 : std::min(max_split, ceil_div(512, tiles));
+  ks = std::max(ks, 1);
+  pl.krange = ceil_div(ceil_div(K, ks), pl.KC) * pl.KC;
+  pl.ksplit = ceil_div(K, pl.krange);
+  pl.n_gemm_wg = tiles * pl.ksplit;
+
+  int kcs = pow2_floor(std::max<long>(1, (long)K * n_ad / 512));
+  kcs = std::min(std::max(kcs, 256), 2048);
+  pl.shrink_KC = kcs;
+  pl.shrink_nchunks = ceil_div(K, kcs);
+  pl.shrink_tg = (T > 64) ? 4 : 1;
+  pl.n_shrink_wg = n_ad * pl.shrink_nchunks;
+
+  // regions of the down-projection first: their offsets do not depend on N
+  size_t off = 0;
+  pl.off_ctrl = off;    off += 256;
+  pl.off_adctr = off;   off += round256((size_t)n_ad * 4);
+  pl.off_spart = off;   off += (pl.shrink_nchunks > 1) ? round256((size_t)pl.shrink_nchunks * T * r_max * 4) : 0;
+  pl.off_t = off;       off += round256((size_t)T * r_max * 4);
+  pl.off_tilectr = off; off += round256((size_t)tiles * 4);
+  pl.off_gpart = off;
+  if (pl.ksplit > 1) off += round256((size_t)tiles * pl.ksplit * 4 * pl.TT * pl.CT * 256 * 4);
+  pl.off_xq = off;      if (pl.XQ) off += round256((size_t)T * K);
+  pl.off_xsc = off;     if (pl.XQ) off += round256((size_t)T * (K / 32));
+  pl.total = off;
+  return pl;
+}
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char* lora_status_string(lora_status s) {
+  switch (s) {
+    case LORA_OK: return "ok";
+    case LORA_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, bad size or format)";
+    case LORA_ERR_UNSUPPORTED: return "unsupported size (see the limits in lora_lowp.h)";
+    case LORA_ERR_WORKSPACE: return "workspace missing or too small";
+    case LORA_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* lora_version(void) { return "lora_lowp gfx950 kernels v1 (scaled-MFMA base GEMM, bf16-MFMA adapters)"; }
+
+size_t lora_workspace_bytes(int32_t T, int32_t K, int32_t N, int32_t n_adapters, int32_t r_max) {
+  if (check_sizes(T, K, N) != LORA_OK || check_adapters(n_adapters, r_max) != LORA_OK) return 0;
+  if (T == 0) return 256;
+  return make_plan(T, K, N, n_adapters, r_max, LORA_W_FP8_E4M3).total;
+}
+
+lora_status lora_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace || !aligned16(workspace)) return LORA_ERR_INVALID_ARG;
+  return launch_fill_zero(workspace, workspace_bytes, as_stream(stream)) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+lora_status lora_workspace_status(const void* workspace, int32_t* status_dev, void* stream) {
+  if (!workspace || !status_dev) return LORA_ERR_INVALID_ARG;
+  const char* ctrl = reinterpret_cast<const char*>(workspace);
+  hipError_t e = hipMemcpyAsync(status_dev, ctrl + 8, 4, hipMemcpyDeviceToDevice, as_stream(stream));
+  return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+lora_status lora_build_segments(const int32_t* adapter_id, int32_t T, int32_t n_adapters, int32_t* seg_indptr,
+                                int32_t* sorted_tok, int32_t* err_word, void* stream) {
+  if (T < 0 || n_adapters < 1) return LORA_ERR_INVALID_ARG;
+  if (T > 65536 || n_adapters > MAX_ADAPTERS) return LORA_ERR_UNSUPPORTED;
+  if (!seg_indptr || !err_word) return LORA_ERR_INVALID_ARG;
+  if (T > 0 && (!adapter_id || !sorted_tok)) return LORA_ERR_INVALID_ARG;
+  hipError_t e = launch_build_segments(adapter_id, T, n_adapters, seg_indptr, sorted_tok, err_word, as_stream(stream));
+  return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+lora_status lora_quant_act_mxfp8(const uint16_t* x, int32_t T, int32_t K, uint8_t* x_q, uint8_t* x_sc,
+                                 void* stream) {
+  if (T < 0 || K <= 0) return LORA_ERR_INVALID_ARG;
+  if (K % 32 != 0 || T > 65536) return LORA_ERR_UNSUPPORTED;
+  if (T == 0) return LORA_OK;
+  if (!x || !x_q || !x_sc || !aligned16(x) || !aligned16(x_q)) return LORA_ERR_INVALID_ARG;
+  return launch_quant(x, T, K, x_q, x_sc, as_stream(stream)) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+lora_status lora_shrink(const uint16_t* x, int32_t T, int32_t K, const int32_t* seg_indptr,
+                        const int32_t* sorted_tok, const uint64_t* A_ptrs, const int32_t* ranks,
+                        int32_t n_adapters, int32_t r_max, float* t, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  lora_status st = check_sizes(T, K, 64);
+  if (st != LORA_OK) return st;
+  if ((st = check_adapters(n_adapters, r_max)) != LORA_OK) return st;
+  if (T == 0) return LORA_OK;
+  if (!x || !seg_indptr || !sorted_tok || !A_ptrs || !ranks || !t) return LORA_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(t)) return LORA_ERR_INVALID_ARG;
+  const LayerPlan pl = make_plan(T, K, 64, n_adapters, r_max, LORA_W_FP8_E4M3);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < pl.off_tilectr) return LORA_ERR_WORKSPACE;
+  char* ws = reinterpret_cast<char*>(workspace);
+  ShrinkParams sp{};
+  sp.x = x; sp.T = T; sp.K = K;
+  sp.seg_indptr = seg_indptr; sp.sorted_tok = sorted_tok;
+  sp.A_ptrs = A_ptrs; sp.ranks = ranks; sp.n_ad = n_adapters; sp.r_max = r_max;
+  sp.t = t;
+  sp.part = reinterpret_cast<float*>(ws + pl.off_spart);
+  sp.ad_ctr = reinterpret_cast<int*>(ws + pl.off_adctr);
+  sp.KC = pl.shrink_KC; sp.nchunks = pl.shrink_nchunks;
+  hipError_t e = launch_shrink(pl.shrink_tg, pl.n_shrink_wg, as_stream(stream), sp);
+  return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+lora_status lora_expand(const float* t, int32_t T, int32_t N, const int32_t* adapter_id, const uint64_t* B_ptrs,
+                        const int32_t* ranks, const float* scales, int32_t n_adapters, int32_t r_max, uint16_t* y,
+                        void* stream) {
+  lora_status st = check_sizes(T, 128, N);
+  if (st != LORA_OK) return st;
+  if ((st = check_adapters(n_adapters, r_max)) != LORA_OK) return st;
+  if (T == 0) return LORA_OK;
+  if (!t || !adapter_id || !B_ptrs || !ranks || !scales || !y) return LORA_ERR_INVALID_ARG;
+  if (!aligned16(t) || !aligned16(y)) return LORA_ERR_INVALID_ARG;
+  ExpandParams p{};
+  p.t = t; p.T = T; p.N = N; p.r_max = r_max; p.n_ad = n_adapters;
+  p.ids = adapter_id; p.B_ptrs = B_ptrs; p.ranks = ranks; p.scales = scales; p.y = y;
+  return launch_expand(p, as_stream(stream)) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+lora_status gemm_lowp_lora_epilogue(const uint16_t* x, int32_t T, int32_t K, int32_t N, int32_t w_fmt,
+                                    const uint8_t* w_q, const void* w_scale, float* t, const int32_t* adapter_id,
+                                    const int32_t* seg_indptr, const int32_t* sorted_tok, const uint64_t* A_ptrs,
+                                    const uint64_t* B_ptrs, const int32_t* ranks, const float* scales,
+                                    int32_t n_adapters, int32_t r_max, uint16_t* y, uint32_t flags,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  lora_status st = check_sizes(T, K, N);
+  if (st != LORA_OK) return st;
+  if ((st = check_adapters(n_adapters, r_max)) != LORA_OK) return st;
+  if (w_fmt != LORA_W_FP8_E4M3 && w_fmt != LORA_W_MXFP4_E2M1) return LORA_ERR_INVALID_ARG;
+  if (flags & ~(uint32_t)LORA_FUSE_SHRINK) return LORA_ERR_INVALID_ARG;
+  if (T == 0) return LORA_OK;
+  if (!x || !w_q || !w_scale || !y) return LORA_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_q) || !aligned16(y)) return LORA_ERR_INVALID_ARG;
+  const bool fused = (flags & LORA_FUSE_SHRINK) != 0;
+  const bool lora = fused || t != nullptr;
+  if (lora && (!adapter_id || !B_ptrs || !ranks || !scales)) return LORA_ERR_INVALID_ARG;
+  if (fused && (!seg_indptr || !sorted_tok || !A_ptrs)) return LORA_ERR_INVALID_ARG;
+  if (t && !aligned16(t)) return LORA_ERR_INVALID_ARG;
+  const LayerPlan pl = make_plan(T, K, N, n_adapters, r_max, w_fmt);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < pl.total) return LORA_ERR_WORKSPACE;
+  char* ws = reinterpret_cast<char*>(workspace);
+  hipStream_t s = as_stream(stream);
+
+  uint8_t* xq = reinterpret_cast<uint8_t*>(ws + pl.off_xq);
+  uint8_t* xsc = reinterpret_cast<uint8_t*>(ws + pl.off_xsc);
+  if (pl.XQ && launch_quant(x, T, K, xq, xsc, s) != hipSuccess) return LORA_ERR_HIP;
+
+  float* t_used = t ? t : reinterpret_cast<float*>(ws + pl.off_t);
+  int* ctrl = reinterpret_cast<int*>(ws + pl.off_ctrl);
+
+  ShrinkParams sp{};
+  if (fused) {
+    sp.x = x; sp.T = T; sp.K = K;
+    sp.seg_indptr = seg_indptr; sp.sorted_tok = sorted_tok;
+    sp.A_ptrs = A_ptrs; sp.ranks = ranks; sp.n_ad = n_adapters; sp.r_max = r_max;
+    sp.t = t_used;
+    sp.part = reinterpret_cast<float*>(ws + pl.off_spart);
+    sp.ad_ctr = reinterpret_cast<int*>(ws + pl.off_adctr);
+    sp.KC = pl.shrink_KC; sp.nchunks = pl.shrink_nchunks;
+  }
+  GemmParams gp{};
+  gp.x = x; gp.xq = xq; gp.xsc = xsc;
+  gp.T = T; gp.K = K; gp.N = N;
+  gp.wq = w_q;
+  gp.ws_fp8 = (w_fmt == LORA_W_FP8_E4M3) ? reinterpret_cast<const float*>(w_scale) : nullptr;
+  gp.ws_fp4 = (w_fmt == LORA_W_MXFP4_E2M1) ? reinterpret_cast<const uint8_t*>(w_scale) : nullptr;
+  gp.t = t_used; gp.r_max = r_max;
+  gp.ids = adapter_id; gp.B_ptrs = B_ptrs; gp.ranks = ranks; gp.scales = scales; gp.n_ad = n_adapters;
+  gp.y = y;
+  gp.ksplit = pl.ksplit; gp.krange = pl.krange; gp.n_cb = pl.n_cb; gp.n_tb = pl.n_tb;
+  gp.gpart = reinterpret_cast<float*>(ws + pl.off_gpart);
+  gp.tile_ctr = reinterpret_cast<int*>(ws + pl.off_tilectr);
+  gp.lora = lora ? 1 : 0;
+  gp.n_shrink = fused ? pl.n_shrink_wg : 0;
+  gp.shrink_done = ctrl + 0;
+  gp.wait_done = ctrl + 1;
+  gp.status = ctrl + 2;
+  gp.spin_limit = SPIN_LIMIT;
+  return launch_layer(pl, s, sp, gp) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+/* Introspection for tests and the benchmark: the plan chosen for these sizes. */
+int32_t lora_plan_info(int32_t T, int32_t K, int32_t N, int32_t n_adapters, int32_t r_max, int32_t w_fmt,
+                       int32_t* out, int32_t n_out) {
+  if (check_sizes(T, K, N) != LORA_OK || check_adapters(n_adapters, r_max) != LORA_OK || T == 0) return -1;
+  const LayerPlan pl = make_plan(T, K, N, n_adapters, r_max, w_fmt);
+  const int32_t v[] = {pl.TT, pl.CT, pl.XQ ? 1 : 0, pl.KC, pl.ksplit, pl.krange, pl.n_cb, pl.n_tb, pl.n_gemm_wg,
+                       pl.shrink_KC, pl.shrink_nchunks, pl.shrink_tg, pl.n_shrink_wg};
+  const int32_t n = (int32_t)(sizeof(v) / sizeof(v[0]));
+  for (int32_t i = 0; i < n && i < n_out; ++i) out[i] = v[i];
+  return n;
+}
+
+}  // extern "C"

@@ -1,0 +1,29 @@
+"""Upload a generated workload to the device in the library's storage layouts.
+
+Layout only (no arithmetic): A_a^T [r_a, K] and B_a^T [N, r_a] are transposed copies of
+the drawn A_a [K, r_a] and B_a [r_a, N]; x is the bf16 tensor of the drawn bits.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from precision_gemm_amd.ops import Adapters, LowpWeight
+
+
+def bf16_tensor(bits: np.ndarray, device="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def upload(wl, device="cuda"):
+    """Return (x, weight, adapters, ids) as device objects for workload ``wl``."""
+    x = bf16_tensor(wl.x, device)
+    q = torch.from_numpy(np.ascontiguousarray(wl.w_q)).to(device)
+    s = torch.from_numpy(np.ascontiguousarray(wl.w_scale)).to(device)
+    w = LowpWeight(wl.fmt, q, s)
+    At = [bf16_tensor(np.ascontiguousarray(a.T), device) for a in wl.A]
+    Bt = [bf16_tensor(np.ascontiguousarray(b.T), device) for b in wl.B]
+    ad = Adapters(At, Bt, torch.from_numpy(np.asarray(wl.scale, np.float32)).to(device))
+    ids = torch.from_numpy(np.asarray(wl.ids, np.int32)).to(device)
+    return x, w, ad, ids
