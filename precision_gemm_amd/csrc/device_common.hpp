@@ -103,6 +103,37 @@ __device__ __forceinline__ v4f mfma_bf16_16x16x32(const uint4& a, const uint4& b
 
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// ---------------------------------------------------------------------------------
+// Data handed between workgroups inside one launch (split-K partial sums, the
+// down-projection t, arrival counters).  The eight XCDs of an MI355X each have their
+// own L2, and those L2s are not coherent with each other.  An agent-scope fence would
+// make plain stores visible by writing back (buffer_wbl2) or invalidating (buffer_inv)
+// the entire L2 of the XCD, which stalls every workgroup streaming through it.
+// Instead, every value that crosses workgroups is written with an agent-coherent store
+// (relaxed agent-scope atomic store: global_store ... sc1, written through past the L2)
+// and read with an agent-coherent load (global_load ... sc1).  A writer waits for its
+// stores to complete (s_waitcnt vmcnt(0)) and passes a workgroup barrier before one
+// thread bumps the arrival counter with a relaxed agent-scope atomic; a reader acts
+// only after observing the counter.
+// ---------------------------------------------------------------------------------
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ld_agent(const int* p) {
+  return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int add_agent(int* p, int v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void set_agent(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// wait until every memory operation this wave issued has completed
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }
+
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
 }  // namespace lora

@@ -222,8 +222,8 @@ __device__ void shrink_item(const ShrinkParams& p, int item, char* smem) {
         for (int v = 0; v < 4; ++v) {
           const int pos = tg0 + tt * 16 + 4 * g + v;
           if (pos < L && j < r) {
-            if (single) p.t[(long)p.sorted_tok[s0 + pos] * p.r_max + j] = sum[v];
-            else p.part[((long)c * p.T + (s0 + pos)) * p.r_max + j] = sum[v];
+            if (single) st_agent(p.t + (long)p.sorted_tok[s0 + pos] * p.r_max + j, sum[v]);
+            else st_agent(p.part + ((long)c * p.T + (s0 + pos)) * p.r_max + j, sum[v]);
           }
         }
       }
@@ -233,28 +233,27 @@ __device__ void shrink_item(const ShrinkParams& p, int item, char* smem) {
     // columns j in [r, r_max) of this segment's t rows are zero
     for (int idx = tid; idx < L * (p.r_max - r); idx += 256) {
       const int pos = idx / (p.r_max - r), j = r + idx % (p.r_max - r);
-      p.t[(long)p.sorted_tok[s0 + pos] * p.r_max + j] = 0.f;
+      st_agent(p.t + (long)p.sorted_tok[s0 + pos] * p.r_max + j, 0.f);
     }
     return;
   }
   // last-arriver reduction over the chunks of adapter a
-  __threadfence();
+  wait_stores();
   __syncthreads();
   if (tid == 0) {
-    const int prev = atomicAdd(&p.ad_ctr[a], 1);
+    const int prev = add_agent(&p.ad_ctr[a], 1);
     *flag = (prev == p.nchunks - 1);
   }
   __syncthreads();
   if (!*flag) return;
-  __threadfence();
   for (int idx = tid; idx < L * p.r_max; idx += 256) {
     const int pos = idx / p.r_max, j = idx % p.r_max;
     float sum = 0.f;
     if (j < r)
-      for (int cc = 0; cc < p.nchunks; ++cc) sum += __builtin_nontemporal_load(p.part + ((long)cc * p.T + (s0 + pos)) * p.r_max + j);
-    p.t[(long)p.sorted_tok[s0 + pos] * p.r_max + j] = sum;
+      for (int cc = 0; cc < p.nchunks; ++cc) sum += ld_agent(p.part + ((long)cc * p.T + (s0 + pos)) * p.r_max + j);
+    st_agent(p.t + (long)p.sorted_tok[s0 + pos] * p.r_max + j, sum);
   }
-  if (tid == 0) atomicExch(&p.ad_ctr[a], 0);
+  if (tid == 0) set_agent(&p.ad_ctr[a], 0);
 }
 
 template <int TG, int U>
@@ -444,16 +443,17 @@ __device__ void gemm_item(const GemmParams& p, int item, char* smem) {
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) *reinterpret_cast<v4f*>(mine + ((tt * CT + ct) * 64 + lane) * 4) = acc[tt][ct];
-    __threadfence();
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) st_agent(mine + ((tt * CT + ct) * 64 + lane) * 4 + v, acc[tt][ct][v]);
+    wait_stores();
     __syncthreads();
     if (tid == 0) {
-      const int prev = atomicAdd(&p.tile_ctr[tile], 1);
+      const int prev = add_agent(&p.tile_ctr[tile], 1);
       *flag = (prev == p.ksplit - 1);
     }
     __syncthreads();
     if (!*flag) return;
-    __threadfence();
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
@@ -462,15 +462,13 @@ __device__ void gemm_item(const GemmParams& p, int item, char* smem) {
         for (int k2 = 0; k2 < p.ksplit; ++k2) {
           const float* src = p.gpart + (((long)tile * p.ksplit + k2) * 4 + wave) * PER_WAVE + ((tt * CT + ct) * 64 + lane) * 4;
           v4f v;
-          v[0] = __builtin_nontemporal_load(src + 0);
-          v[1] = __builtin_nontemporal_load(src + 1);
-          v[2] = __builtin_nontemporal_load(src + 2);
-          v[3] = __builtin_nontemporal_load(src + 3);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = ld_agent(src + e);
           sum += v;
         }
         acc[tt][ct] = sum;
       }
-    if (tid == 0) atomicExch(&p.tile_ctr[tile], 0);
+    if (tid == 0) set_agent(&p.tile_ctr[tile], 0);
   }
 
   // ---- epilogue: channel scale
@@ -488,21 +486,20 @@ __device__ void gemm_item(const GemmParams& p, int item, char* smem) {
     if (p.n_shrink > 0) {
       if (tid == 0) {
         int spins = 0;
-        while (__hip_atomic_load(p.shrink_done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < p.n_shrink) {
+        while (ld_agent(p.shrink_done) < p.n_shrink) {
           __builtin_amdgcn_s_sleep(4);
           if (++spins > p.spin_limit) {
-            atomicExch(p.status, 1);
+            set_agent(p.status, 1);
             break;
           }
         }
-        const int prev = atomicAdd(p.wait_done, 1);
+        const int prev = add_agent(p.wait_done, 1);
         if (prev == ntiles - 1) {
-          atomicExch(p.shrink_done, 0);
-          atomicExch(p.wait_done, 0);
+          set_agent(p.shrink_done, 0);
+          set_agent(p.wait_done, 0);
         }
       }
       __syncthreads();
-      __threadfence();
     }
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
@@ -524,12 +521,13 @@ __device__ void gemm_item(const GemmParams& p, int item, char* smem) {
           uint4 aop = zero4();
           if (mine && j < r) {
             const float* tp = p.t + (long)tok * p.r_max + j;
-            const float4 t0 = *reinterpret_cast<const float4*>(tp);
-            const float4 t1 = *reinterpret_cast<const float4*>(tp + 4);
-            aop.x = f32_to_bf16_rne(sa * t0.x) | (f32_to_bf16_rne(sa * t0.y) << 16);
-            aop.y = f32_to_bf16_rne(sa * t0.z) | (f32_to_bf16_rne(sa * t0.w) << 16);
-            aop.z = f32_to_bf16_rne(sa * t1.x) | (f32_to_bf16_rne(sa * t1.y) << 16);
-            aop.w = f32_to_bf16_rne(sa * t1.z) | (f32_to_bf16_rne(sa * t1.w) << 16);
+            float tv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) tv[e] = sa * ld_agent(tp + e);
+            aop.x = f32_to_bf16_rne(tv[0]) | (f32_to_bf16_rne(tv[1]) << 16);
+            aop.y = f32_to_bf16_rne(tv[2]) | (f32_to_bf16_rne(tv[3]) << 16);
+            aop.z = f32_to_bf16_rne(tv[4]) | (f32_to_bf16_rne(tv[5]) << 16);
+            aop.w = f32_to_bf16_rne(tv[6]) | (f32_to_bf16_rne(tv[7]) << 16);
           }
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) {
@@ -563,9 +561,9 @@ __global__ __launch_bounds__(256) void k_layer(ShrinkParams sp, GemmParams gp) {
   const int b = blockIdx.x;
   if (b < gp.n_shrink) {
     shrink_item<TG, U>(sp, b, smem);
-    __threadfence();
+    wait_stores();
     __syncthreads();
-    if (threadIdx.x == 0) __hip_atomic_fetch_add(gp.shrink_done, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) add_agent(gp.shrink_done, 1);
     return;
   }
   gemm_item<FMT, TT, CT, XQ>(gp, b - gp.n_shrink, smem);
