@@ -36,11 +36,20 @@
  *    breaks this rule contributes no adapter term (and its rows of t are not written).
  *
  * Data layouts:
- *  - W, FP8 (LORA_W_FP8_E4M3): w_q uint8 [N][K] e4m3fn codes (K contiguous),
- *    w_scale float [N], one scale per output channel; dequant = w_scale[n]*code.
- *  - W, MXFP4 (LORA_W_MXFP4_E2M1): w_q uint8 [N][K/2] e2m1 codes, element k of
- *    row n in the low nibble of byte k/2 when k is even, high nibble when odd;
- *    w_scale uint8 [N][K/32] e8m0 codes, one per 32 consecutive k.
+ *  - W, FP8 (LORA_W_FP8_E4M3), row-major form: w_q uint8 [N][K] e4m3fn codes (K
+ *    contiguous), w_scale float [N], one scale per output channel; dequant =
+ *    w_scale[n]*code.
+ *  - W, MXFP4 (LORA_W_MXFP4_E2M1), row-major form: w_q uint8 [N][K/2] e2m1 codes,
+ *    element k of row n in the low nibble of byte k/2 when k is even, high nibble
+ *    when odd; w_scale uint8 [N][K/32] e8m0 codes, one per 32 consecutive k.
+ *  - gemm_lowp_lora_epilogue reads W in the packed form made once by
+ *    lora_pack_weight (same bytes, reordered so that each 16-byte load of the GEMM
+ *    reads 1 KB of consecutive memory; the FP8 channel scales stay as they are):
+ *      FP8:   [N/16][K/128][h = 0,1][l = 0..63][16 B]: 16 codes of channel
+ *             16*nt + l%16 at k = 128*ks + 64*h + 16*(l/16) ..
+ *      MXFP4: [N/16][K/128][l][16 B]: 32 codes of channel 16*nt + l%16 at
+ *             k = 128*ks + 32*(l/16) .., and scales [N/16][K/128][l] (one byte:
+ *             the code of k-block 4*ks + l/16).
  *  - Adapter a: A_a [K][r_a] is stored as A_a^T, bf16 [r_a][K] (K contiguous),
  *    and B_a [r_a][N] as B_a^T, bf16 [N][r_a] (r_a contiguous) -- the weights of
  *    the linear maps K -> r_a and r_a -> N in out-by-in order, so that both matrix
@@ -112,6 +121,13 @@ lora_status lora_build_segments(const int32_t* adapter_id, int32_t T, int32_t n_
                                 int32_t* seg_indptr, int32_t* sorted_tok, int32_t* err_word,
                                 void* stream);
 
+/* Reorder a row-major W (codes, and for MXFP4 its block scales) into the packed form
+ * that gemm_lowp_lora_epilogue reads (see "Data layouts").  An offline step, like the
+ * quantisation of W itself.  FP8: scale and scale_packed are ignored (may be NULL).
+ * Not in place.  N % 64 == 0, K % 128 == 0. */
+lora_status lora_pack_weight(int32_t w_fmt, const uint8_t* q, const uint8_t* scale, int32_t N, int32_t K,
+                             uint8_t* q_packed, uint8_t* scale_packed, void* stream);
+
 /* MXFP8 quantisation of bf16 activations x [T][K] -> x_q uint8 [T][K] e4m3fn codes,
  * x_sc uint8 [T][K/32] e8m0 codes, by the rule in the header comment.  Bit-exact;
  * the same device function quantises x inside gemm_lowp_lora_epilogue. */
@@ -122,7 +138,9 @@ lora_status lora_quant_act_mxfp8(const uint16_t* x, int32_t T, int32_t K,
  * first; "Punica" README: SGMV over segments):
  *   t[tok, j] = sum_k x[tok, k] * A_a[k, j]  for every tok in segment a, j < r_a,
  * fp32 accumulation of exact bf16 products, written in original token order,
- * zero for j >= r_a.  Split-K with a fixed-order reduction: bitwise deterministic. */
+ * zero for j >= r_a.  Fixed summation order: bitwise deterministic.  The standalone
+ * down-projection needs no scratch memory: workspace may be NULL (kept in the
+ * signature so that callers can pass the layer's workspace). */
 lora_status lora_shrink(const uint16_t* x, int32_t T, int32_t K,
                         const int32_t* seg_indptr, const int32_t* sorted_tok,
                         const uint64_t* A_ptrs, const int32_t* ranks,
@@ -145,7 +163,8 @@ lora_status lora_expand(const float* t, int32_t T, int32_t N,
  *  - flags & LORA_FUSE_SHRINK: the down-projection runs in the same launch (t is an
  *    output, may be NULL).  Otherwise t is an input (from lora_shrink); t == NULL
  *    then means "base GEMM only" and the adapter arguments may be NULL.
- *  - w_fmt: LORA_W_FP8_E4M3 or LORA_W_MXFP4_E2M1 (w_q / w_scale as above).
+ *  - w_fmt: LORA_W_FP8_E4M3 or LORA_W_MXFP4_E2M1; w_q (and for MXFP4 w_scale) in the
+ *    packed form made by lora_pack_weight; for FP8 w_scale is float [N].
  * y is written, not accumulated into. */
 lora_status gemm_lowp_lora_epilogue(const uint16_t* x, int32_t T, int32_t K, int32_t N,
                                     int32_t w_fmt, const uint8_t* w_q, const void* w_scale,
@@ -164,11 +183,11 @@ lora_status gemm_lowp_lora_epilogue(const uint16_t* x, int32_t T, int32_t K, int
 lora_status lora_workspace_status(const void* workspace, int32_t* status_dev, void* stream);
 
 /* Introspection for tests and benchmarks: writes the tile plan chosen for these sizes
- * into out[0..n_out) (host array) as {token tiles per workgroup, column tiles per
- * wave, separate x-quantisation pass, K-chunk, K-splits, K-range, column blocks,
- * token blocks, GEMM workgroups, down-projection K-chunk, its chunks, its token
- * tiles per pass, its workgroups} and returns the number of entries (13), or -1 for
- * sizes outside the limits.  Pure host function. */
+ * into out[0..n_out) (host array) as {token tiles of 16 per workgroup, column tiles of
+ * 16 per wave, waves along N, waves along K, separate x-quantisation pass, K-chunk,
+ * K-splits, K-range, column blocks, token blocks, GEMM workgroups, down-projection token
+ * block, its rank groups, its K-parts, its workgroups} and returns the number of entries
+ * (15), or -1 for sizes outside the limits.  Pure host function. */
 int32_t lora_plan_info(int32_t T, int32_t K, int32_t N, int32_t n_adapters, int32_t r_max, int32_t w_fmt,
                        int32_t* out, int32_t n_out);
 

@@ -30,6 +30,7 @@ _SIGNATURES = {
     "lora_expand": (c_i32, [c_vp, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_vp, c_vp]),
     "gemm_lowp_lora_epilogue": (c_i32, [c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                         c_vp, c_vp, c_vp, c_i32, c_i32, c_vp, c_u32, c_vp, c_size, c_vp]),
+    "lora_pack_weight": (c_i32, [c_i32, c_vp, c_vp, c_i32, c_i32, c_vp, c_vp, c_vp]),
     "lora_plan_info": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(c_i32), c_i32]),
 }
 

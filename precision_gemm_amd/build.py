@@ -19,9 +19,12 @@ SOURCES = ["lora_kernels.hip", "lora_api.cpp"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops off: no v_pk_{add,mul,fma}_f32 in the device code.
+# atomic optimizer off: it rewrites a single-lane atomic with return into a wave-level
+# scan whose result is consumed at once, which forces a wait for every load in flight.
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wno-unused-result",
 ]
 

@@ -101,7 +101,17 @@ __device__ __forceinline__ v4f mfma_bf16_16x16x32(const uint4& a, const uint4& b
                                                  0, 0);
 }
 
-__device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+// 16-byte load from global memory.  The address-space cast makes the compiler emit
+// global_load (counted by vmcnt only) rather than flat_load, which also counts in lgkmcnt
+// and forces full waits.
+__device__ __forceinline__ uint4 ldg16(const void* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((address_space(1))) const uint4 g_uint4;
+  return *(g_uint4*)(reinterpret_cast<uintptr_t>(p));
+#else
+  return *reinterpret_cast<const uint4*>(p);  // host pass only; never executed
+#endif
+}
 
 // ---------------------------------------------------------------------------------
 // Data handed between workgroups inside one launch (split-K partial sums, the
@@ -130,6 +140,12 @@ __device__ __forceinline__ int add_agent(int* p, int v) {
 }
 __device__ __forceinline__ void set_agent(int* p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent_u64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_agent_u64(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // wait until every memory operation this wave issued has completed
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }

@@ -9,7 +9,7 @@ using namespace lora;
 
 namespace {
 
-constexpr int SPIN_LIMIT = 1 << 22;  // bounded wait in the fused launch (~0.5 s)
+constexpr int SPIN_LIMIT = 1 << 23;  // bounded waits in the fused launch (about a second)
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -33,48 +33,61 @@ lora_status check_adapters(int32_t n_adapters, int32_t r_max) {
 }
 
 // Tile plan: a pure function of the sizes, so lora_workspace_bytes and every call agree.
-LayerPlan make_plan(int T, int K, int N, int n_ad, int r_max, int fmt) {
+// fused: the down-projection runs in the layer launch (its K may then be split into parts
+// that the GEMM epilogue adds up); otherwise it runs alone and writes the final t.
+LayerPlan make_plan(int T, int K, int N, int n_ad, int r_max, int fmt, bool fused = true) {
   LayerPlan pl{};
   pl.fmt = fmt;
   if (T <= 16) {
-    pl.TT = 1; pl.CT = 1; pl.XQ = false;
+    pl.TT = 1; pl.CT = 2; pl.WC = 1; pl.WK = 4; pl.XQ = false;
   } else if (T <= 64) {
-    pl.TT = 4; pl.CT = 1; pl.XQ = false;
+    pl.TT = 4; pl.CT = 1; pl.WC = 4; pl.WK = 1; pl.XQ = false;
   } else if (T <= 128) {
-    pl.TT = 8; pl.CT = (N % 128 == 0) ? 2 : 1; pl.XQ = false;
+    pl.TT = 8; pl.CT = 2; pl.WC = 2; pl.WK = 2; pl.XQ = false;
   } else {
-    pl.TT = 8; pl.CT = (N % 256 == 0) ? 4 : ((N % 128 == 0) ? 2 : 1); pl.XQ = true;
+    pl.TT = 8; pl.WC = 4; pl.WK = 1; pl.XQ = true;
+    pl.CT = (N % 128 == 0) ? 2 : 1;
   }
-  pl.KC = (pl.TT == 1) ? 1024 : ((pl.TT <= 4) ? 512 : 256);
-  const int WN = 64 * pl.CT;
+  pl.KC = (pl.TT == 1) ? 2048 : ((pl.TT <= 4) ? 512 : 256);
+  const int WN = pl.WC * pl.CT * 16;
   pl.n_cb = N / WN;
   pl.n_tb = ceil_div(T, 16 * pl.TT);
   const int tiles = pl.n_cb * pl.n_tb;
   const int max_split = std::max(1, K / pl.KC);
-  int ks = (tiles >= 384) ? 1 : std::min(max_split, ceil_div(512, tiles));
+  // split K over workgroups only when there are too few tiles to fill the GPU: the
+  // split-K hand-over adds dependent memory round trips to the critical path
+  int ks = (tiles >= 128) ? 1 : std::min(max_split, ceil_div(512, tiles));
   ks = std::max(ks, 1);
   pl.krange = ceil_div(ceil_div(K, ks), pl.KC) * pl.KC;
   pl.ksplit = ceil_div(K, pl.krange);
   pl.n_gemm_wg = tiles * pl.ksplit;
 
-  int kcs = pow2_floor(std::max<long>(1, (long)K * n_ad / 512));
-  kcs = std::min(std::max(kcs, 256), 2048);
-  pl.shrink_KC = kcs;
-  pl.shrink_nchunks = ceil_div(K, kcs);
-  pl.shrink_tg = (T > 64) ? 4 : 1;
-  pl.n_shrink_wg = n_ad * pl.shrink_nchunks;
+  // down-projection: item = (adapter, token block, group of 16*jper ranks, K-part)
+  if (T <= 128) {
+    pl.s_tblk = ceil_div(T, 16) * 16;
+    pl.s_ntblk = 1;
+    pl.s_jper = 1;
+    pl.s_njg = ceil_div(r_max, 16);
+  } else {
+    pl.s_tblk = 64;
+    pl.s_ntblk = ceil_div(T, 64);
+    pl.s_jper = 2;
+    pl.s_njg = ceil_div(r_max, 32);
+  }
+  int kparts = 1;
+  if (fused && T <= 64) kparts = std::min(4, std::max(1, K / 1024));  // latency-bound decode: split K
+  pl.s_kpart_len = ceil_div(ceil_div(K, kparts), 256) * 256;
+  pl.s_kparts = ceil_div(K, pl.s_kpart_len);
+  pl.n_shrink_wg = n_ad * pl.s_ntblk * pl.s_njg * pl.s_kparts;
 
-  // regions of the down-projection first: their offsets do not depend on N
   size_t off = 0;
-  pl.off_ctrl = off;    off += 256;
-  pl.off_adctr = off;   off += round256((size_t)n_ad * 4);
-  pl.off_spart = off;   off += (pl.shrink_nchunks > 1) ? round256((size_t)pl.shrink_nchunks * T * r_max * 4) : 0;
-  pl.off_t = off;       off += round256((size_t)T * r_max * 4);
-  pl.off_tilectr = off; off += round256((size_t)tiles * 4);
+  pl.off_ctrl = off;  off += 256;
+  pl.off_ttag = off;  off += round256((size_t)pl.s_kparts * T * r_max * 8);
+  pl.off_gflag = off; off += round256((size_t)tiles * pl.ksplit * 4);
   pl.off_gpart = off;
-  if (pl.ksplit > 1) off += round256((size_t)tiles * pl.ksplit * 4 * pl.TT * pl.CT * 256 * 4);
-  pl.off_xq = off;      if (pl.XQ) off += round256((size_t)T * K);
-  pl.off_xsc = off;     if (pl.XQ) off += round256((size_t)T * (K / 32));
+  if (pl.ksplit > 1) off += round256((size_t)tiles * pl.ksplit * pl.WC * pl.TT * pl.CT * 256 * 4);
+  pl.off_xq = off;    if (pl.XQ) off += round256((size_t)T * K);
+  pl.off_xsc = off;   if (pl.XQ) off += round256((size_t)T * (K / 32));
   pl.total = off;
   return pl;
 }
@@ -139,24 +152,24 @@ lora_status lora_shrink(const uint16_t* x, int32_t T, int32_t K, const int32_t* 
                         const int32_t* sorted_tok, const uint64_t* A_ptrs, const int32_t* ranks,
                         int32_t n_adapters, int32_t r_max, float* t, void* workspace, size_t workspace_bytes,
                         void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;  // the standalone down-projection needs no scratch memory
   lora_status st = check_sizes(T, K, 64);
   if (st != LORA_OK) return st;
   if ((st = check_adapters(n_adapters, r_max)) != LORA_OK) return st;
   if (T == 0) return LORA_OK;
   if (!x || !seg_indptr || !sorted_tok || !A_ptrs || !ranks || !t) return LORA_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(t)) return LORA_ERR_INVALID_ARG;
-  const LayerPlan pl = make_plan(T, K, 64, n_adapters, r_max, LORA_W_FP8_E4M3);
-  if (!workspace || !aligned16(workspace) || workspace_bytes < pl.off_tilectr) return LORA_ERR_WORKSPACE;
-  char* ws = reinterpret_cast<char*>(workspace);
+  const LayerPlan pl = make_plan(T, K, 64, n_adapters, r_max, LORA_W_FP8_E4M3, /*fused=*/false);
   ShrinkParams sp{};
   sp.x = x; sp.T = T; sp.K = K;
   sp.seg_indptr = seg_indptr; sp.sorted_tok = sorted_tok;
   sp.A_ptrs = A_ptrs; sp.ranks = ranks; sp.n_ad = n_adapters; sp.r_max = r_max;
-  sp.t = t;
-  sp.part = reinterpret_cast<float*>(ws + pl.off_spart);
-  sp.ad_ctr = reinterpret_cast<int*>(ws + pl.off_adctr);
-  sp.KC = pl.shrink_KC; sp.nchunks = pl.shrink_nchunks;
-  hipError_t e = launch_shrink(pl.shrink_tg, pl.n_shrink_wg, as_stream(stream), sp);
+  sp.ids = nullptr;  // standalone: tokens come from the segments only
+  sp.t_out = t; sp.t_tag = nullptr;
+  sp.tblk = pl.s_tblk; sp.n_tblk = pl.s_ntblk; sp.n_jg = pl.s_njg; sp.jper = pl.s_jper;
+  sp.kparts = pl.s_kparts; sp.kpart_len = pl.s_kpart_len;
+  hipError_t e = launch_shrink(pl, as_stream(stream), sp);
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
@@ -203,18 +216,19 @@ lora_status gemm_lowp_lora_epilogue(const uint16_t* x, int32_t T, int32_t K, int
   uint8_t* xsc = reinterpret_cast<uint8_t*>(ws + pl.off_xsc);
   if (pl.XQ && launch_quant(x, T, K, xq, xsc, s) != hipSuccess) return LORA_ERR_HIP;
 
-  float* t_used = t ? t : reinterpret_cast<float*>(ws + pl.off_t);
   int* ctrl = reinterpret_cast<int*>(ws + pl.off_ctrl);
+  uint64_t* ttag = reinterpret_cast<uint64_t*>(ws + pl.off_ttag);
 
   ShrinkParams sp{};
   if (fused) {
     sp.x = x; sp.T = T; sp.K = K;
     sp.seg_indptr = seg_indptr; sp.sorted_tok = sorted_tok;
     sp.A_ptrs = A_ptrs; sp.ranks = ranks; sp.n_ad = n_adapters; sp.r_max = r_max;
-    sp.t = t_used;
-    sp.part = reinterpret_cast<float*>(ws + pl.off_spart);
-    sp.ad_ctr = reinterpret_cast<int*>(ws + pl.off_adctr);
-    sp.KC = pl.shrink_KC; sp.nchunks = pl.shrink_nchunks;
+    sp.ids = adapter_id;
+    sp.t_out = t;  // may be null
+    sp.t_tag = ttag;
+    sp.tblk = pl.s_tblk; sp.n_tblk = pl.s_ntblk; sp.n_jg = pl.s_njg; sp.jper = pl.s_jper;
+    sp.kparts = pl.s_kparts; sp.kpart_len = pl.s_kpart_len;
   }
   GemmParams gp{};
   gp.x = x; gp.xq = xq; gp.xsc = xsc;
@@ -222,19 +236,34 @@ lora_status gemm_lowp_lora_epilogue(const uint16_t* x, int32_t T, int32_t K, int
   gp.wq = w_q;
   gp.ws_fp8 = (w_fmt == LORA_W_FP8_E4M3) ? reinterpret_cast<const float*>(w_scale) : nullptr;
   gp.ws_fp4 = (w_fmt == LORA_W_MXFP4_E2M1) ? reinterpret_cast<const uint8_t*>(w_scale) : nullptr;
-  gp.t = t_used; gp.r_max = r_max;
+  gp.t = fused ? nullptr : t;
+  gp.t_out = (fused && pl.s_kparts > 1) ? t : nullptr;
+  gp.t_tag = fused ? ttag : nullptr;
+  gp.t_kparts = pl.s_kparts;
+  gp.r_max = r_max;
   gp.ids = adapter_id; gp.B_ptrs = B_ptrs; gp.ranks = ranks; gp.scales = scales; gp.n_ad = n_adapters;
   gp.y = y;
   gp.ksplit = pl.ksplit; gp.krange = pl.krange; gp.n_cb = pl.n_cb; gp.n_tb = pl.n_tb;
   gp.gpart = reinterpret_cast<float*>(ws + pl.off_gpart);
-  gp.tile_ctr = reinterpret_cast<int*>(ws + pl.off_tilectr);
+  gp.gflag = reinterpret_cast<int*>(ws + pl.off_gflag);
   gp.lora = lora ? 1 : 0;
   gp.n_shrink = fused ? pl.n_shrink_wg : 0;
-  gp.shrink_done = ctrl + 0;
-  gp.wait_done = ctrl + 1;
-  gp.status = ctrl + 2;
+  gp.ctrl = ctrl;
   gp.spin_limit = SPIN_LIMIT;
   return launch_layer(pl, s, sp, gp) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+lora_status lora_pack_weight(int32_t w_fmt, const uint8_t* q, const uint8_t* scale, int32_t N, int32_t K,
+                             uint8_t* q_packed, uint8_t* scale_packed, void* stream) {
+  if (w_fmt != LORA_W_FP8_E4M3 && w_fmt != LORA_W_MXFP4_E2M1) return LORA_ERR_INVALID_ARG;
+  if (N <= 0 || K <= 0) return LORA_ERR_INVALID_ARG;
+  if (N % 64 != 0 || K % 128 != 0) return LORA_ERR_UNSUPPORTED;
+  if (!q || !q_packed || !aligned16(q) || !aligned16(q_packed)) return LORA_ERR_INVALID_ARG;
+  if (w_fmt == LORA_W_MXFP4_E2M1 && (!scale || !scale_packed)) return LORA_ERR_INVALID_ARG;
+  if (q == q_packed) return LORA_ERR_INVALID_ARG;  // not in place
+  hipError_t e = launch_pack_weight(w_fmt, q, reinterpret_cast<const uint8_t*>(scale), N, K, q_packed, scale_packed,
+                                    as_stream(stream));
+  return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
 /* Introspection for tests and the benchmark: the plan chosen for these sizes. */
@@ -242,8 +271,8 @@ int32_t lora_plan_info(int32_t T, int32_t K, int32_t N, int32_t n_adapters, int3
                        int32_t* out, int32_t n_out) {
   if (check_sizes(T, K, N) != LORA_OK || check_adapters(n_adapters, r_max) != LORA_OK || T == 0) return -1;
   const LayerPlan pl = make_plan(T, K, N, n_adapters, r_max, w_fmt);
-  const int32_t v[] = {pl.TT, pl.CT, pl.XQ ? 1 : 0, pl.KC, pl.ksplit, pl.krange, pl.n_cb, pl.n_tb, pl.n_gemm_wg,
-                       pl.shrink_KC, pl.shrink_nchunks, pl.shrink_tg, pl.n_shrink_wg};
+  const int32_t v[] = {pl.TT, pl.CT, pl.WC, pl.WK, pl.XQ ? 1 : 0, pl.KC, pl.ksplit, pl.krange, pl.n_cb,
+                       pl.n_tb, pl.n_gemm_wg, pl.s_tblk, pl.s_njg, pl.s_kparts, pl.n_shrink_wg};
   const int32_t n = (int32_t)(sizeof(v) / sizeof(v[0]));
   for (int32_t i = 0; i < n && i < n_out; ++i) out[i] = v[i];
   return n;

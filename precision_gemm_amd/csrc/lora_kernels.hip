@@ -7,68 +7,79 @@
 // the adapter down-projection runs first, the low-precision GEMM streams its weights
 // meanwhile, and the up-projection of every tenant is added in the GEMM's epilogue.
 //
-// Kernels (all with 256-thread workgroups = 4 wave64 unless stated):
-//   k_build_segments  one 1024-thread workgroup: stable counting sort of tokens by adapter.
+// Kernels (256-thread workgroups = 4 wave64):
+//   k_build_segments  stable counting sort of tokens by adapter (one workgroup).
 //   k_quant_mxfp8     MXFP8 quantisation of bf16 activations (one thread per 32-block).
-//   k_shrink          down-projection t = x @ A_a per segment on bf16 MFMA, split-K with a
-//                     fixed-order last-arriver reduction (deterministic).
-//   k_expand          standalone up-projection y += s_a t @ B_a (the unfused schedule).
-//   k_layer           role-split launch: workgroups [0, n_shrink) run the down-projection,
-//                     the rest run the scaled-MFMA base GEMM whose epilogue waits for t.
+//   k_shrink          down-projection t = x @ A_a per segment on bf16 MFMA (unfused schedule).
+//   k_expand          up-projection y += s_a t @ B_a as its own launch (unfused schedule).
+//   k_layer           one launch for the layer: workgroups [0, n_shrink) compute the
+//                     down-projection, the others the scaled-MFMA base GEMM, whose
+//                     epilogue waits for t only when it needs it.
+//
+// Hand-over between workgroups of one launch uses agent-coherent loads/stores (see
+// device_common.hpp) and a per-launch tag instead of counters that need resetting:
+// every workgroup first reads the workspace's launch epoch E; values handed over are
+// stored together with tag = E + 1 and a reader waits until it sees that tag.  The last
+// workgroup to start (counted with one relaxed atomic) advances E when it ends, which is
+// safe because every workgroup has read E before being counted.  A workgroup only ever
+// waits for workgroups with lower ids, and the hardware dispatches workgroups in id
+// order, so waits cannot deadlock; every wait is bounded and reports a status on expiry.
 #include "device_common.hpp"
 #include "lora_kernels.hpp"
 
 namespace lora {
 
 // ======================================================================================
-// Segment builder
+// Segment builder: seg_indptr (CSR over adapter ids) and sorted_tok (stable order)
 // ======================================================================================
+constexpr int SEG_THREADS = 256;
+
 __global__ __launch_bounds__(SEG_THREADS) void k_build_segments(const int* __restrict__ ids, int T, int n_ad,
                                                                 int* __restrict__ seg_indptr,
                                                                 int* __restrict__ sorted_tok, int* __restrict__ err) {
   __shared__ int cnt[MAX_ADAPTERS];
-  __shared__ int part[SEG_THREADS];
+  __shared__ int wsum[SEG_THREADS / 64];
   __shared__ int first_bad;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) first_bad = 0x7fffffff;
   for (int a = tid; a < n_ad; a += SEG_THREADS) cnt[a] = 0;
   __syncthreads();
   // 1. counts (LDS atomics: order-independent)
   for (int t = tid; t < T; t += SEG_THREADS) {
-    int a = ids[t];
+    const int a = ids[t];
     if (a >= 0 && a < n_ad) atomicAdd(&cnt[a], 1);
     else atomicMin(&first_bad, t);
   }
   __syncthreads();
-  // 2. exclusive scan: each thread sums a contiguous slice, then a scan over threads
+  // 2. exclusive scan: a contiguous slice per thread, a wave scan, then the wave totals
   const int per = (n_ad + SEG_THREADS - 1) / SEG_THREADS;
   const int lo = min(tid * per, n_ad), hi = min(lo + per, n_ad);
   int s = 0;
   for (int a = lo; a < hi; ++a) s += cnt[a];
-  part[tid] = s;
-  __syncthreads();
-  for (int off = 1; off < SEG_THREADS; off <<= 1) {
-    int v = (tid >= off) ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
+  int incl = s;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
   }
-  int base = (tid > 0) ? part[tid - 1] : 0;
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int base = incl - s;
+  for (int w = 0; w < wave; ++w) base += wsum[w];
   for (int a = lo; a < hi; ++a) {
-    int c = cnt[a];
+    const int c = cnt[a];
     seg_indptr[a] = base;
     cnt[a] = base;  // becomes the write cursor of adapter a
     base += c;
   }
-  if (tid == SEG_THREADS - 1) seg_indptr[n_ad] = part[SEG_THREADS - 1];
+  if (tid == SEG_THREADS - 1) seg_indptr[n_ad] = base;
   if (tid == 0) *err = (first_bad == 0x7fffffff) ? 0 : first_bad + 1;
   __syncthreads();
   // 3. stable placement by one wave, 64 tokens at a time in token order.  Lanes with the
   //    same adapter are grouped with a ballot; a lane's slot is the cursor plus the number
   //    of lower lanes in its group, so equal ids keep their token order.
-  if (tid < 64) {
+  if (wave == 0) {
     volatile int* cur = cnt;
-    const int lane = tid;
     const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int t0 = 0; t0 < T; t0 += 64) {
       const int t = t0 + lane;
@@ -89,7 +100,7 @@ __global__ __launch_bounds__(SEG_THREADS) void k_build_segments(const int* __res
 }
 
 // ======================================================================================
-// MXFP8 activation quantisation (standalone; the GEMM loader calls the same functions)
+// MXFP8 activation quantisation (standalone; the GEMM loader uses the same functions)
 // ======================================================================================
 __global__ __launch_bounds__(256) void k_quant_mxfp8(const uint16_t* __restrict__ x, int T, int K,
                                                      uint8_t* __restrict__ xq, uint8_t* __restrict__ xsc) {
@@ -117,149 +128,245 @@ __global__ __launch_bounds__(256) void k_fill_zero(uint32_t* __restrict__ p, siz
 }
 
 // ======================================================================================
-// Down-projection ("shrink"): one workgroup per (adapter a, K-chunk c).
-// A_a is stored transposed, bf16 [r_a][K].  Both MFMA operands are then rows with K
-// contiguous: the x operand is 16 tokens of segment a (gathered through sorted_tok),
-// the A operand is 16 ranks.  Lane (i = l%16, g = l/16) loads 32 contiguous bytes
-// (k = k0+16g .. k0+16g+15) of its row and feeds them to two 16x16x32 MFMAs; both
-// operands use the same k assignment, so the products pair up.  The four waves split
-// the chunk's 64-wide k-steps; their sums meet in LDS in wave order, and the chunks of
-// one adapter are summed in chunk order by whichever workgroup arrives last.
+// Packed weight layout.  For each tile of 16 output channels (row tile nt) and each
+// 128-wide k-step ks, the bytes one wave loads for the scaled MFMA's W operand are stored
+// contiguously in lane order (lane l = 16g + j: channel 16nt + j, lane group g), so every
+// 16-byte load instruction of the GEMM reads 1 KB of consecutive memory:
+//   FP8:   [N/16][K/128][half h][lane l][16 B], lane l holds k = 128ks + 64h + 16g .. +15
+//   MXFP4: [N/16][K/128][lane l][16 B],          lane l holds k = 128ks + 32g .. +31
+//          scales [N/16][K/128][lane l] (1 byte), the e8m0 code of k-block 4ks + g
+// One thread per 16-byte chunk of the packed codes.
 // ======================================================================================
-template <int TG, int U>
-__device__ void shrink_item(const ShrinkParams& p, int item, char* smem) {
-  const int a = item / p.nchunks, c = item % p.nchunks;
-  const int s0 = p.seg_indptr[a], s1 = p.seg_indptr[a + 1];
-  const int L = s1 - s0;
-  if (L <= 0) return;
-  const int r = p.ranks[a];
-  if (r < 8 || r > p.r_max || (r & 7)) return;  // unsupported rank: adapter skipped
-  const uint16_t* __restrict__ A = reinterpret_cast<const uint16_t*>(p.A_ptrs[a]);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, g = lane >> 4;
-  const int k_begin = c * p.KC, k_end = min(p.K, k_begin + p.KC);
-  const int nsteps = (k_end - k_begin) >> 6;
-  const int JT = (r + 15) >> 4;
-  float* red = reinterpret_cast<float*>(smem);           // [4 waves][TG][4][64 lanes][4]
-  int* flag = reinterpret_cast<int*>(smem + 4 * TG * 4 * 256 * sizeof(float));
-  const bool single = (p.nchunks == 1);
+__global__ __launch_bounds__(256) void k_pack_weight(int fmt, const uint8_t* __restrict__ q,
+                                                     const uint8_t* __restrict__ sc, int N, int K,
+                                                     uint8_t* __restrict__ qp, uint8_t* __restrict__ scp) {
+  const int ksteps = K / 128;
+  const long chunks = (fmt == LORA_W_FP8_E4M3) ? (long)N * K / 16 : (long)N * K / 32;
+  for (long c = (long)blockIdx.x * blockDim.x + threadIdx.x; c < chunks; c += (long)gridDim.x * blockDim.x) {
+    const int l = (int)(c & 63), j = l & 15, g = l >> 4;
+    if (fmt == LORA_W_FP8_E4M3) {
+      const int h = (int)((c >> 6) & 1);
+      const long rest = c >> 7;
+      const long ks = rest % ksteps, nt = rest / ksteps;
+      const long n = nt * 16 + j, k = ks * 128 + h * 64 + g * 16;
+      *reinterpret_cast<uint4*>(qp + c * 16) = ldg16(q + n * K + k);
+    } else {
+      const long rest = c >> 6;
+      const long ks = rest % ksteps, nt = rest / ksteps;
+      const long n = nt * 16 + j;
+      *reinterpret_cast<uint4*>(qp + c * 16) = ldg16(q + n * (K / 2) + ks * 64 + g * 16);
+      scp[c] = sc[n * (K / 32) + ks * 4 + g];
+    }
+  }
+}
 
-  const uint16_t* arow[4];
-  bool av[4];
+// ======================================================================================
+// Launch epoch (see the file comment)
+// ======================================================================================
+// thread 0 issues the epoch load before any bulk load of the workgroup
+__device__ __forceinline__ int wg_epoch_load(const int* ctrl) {
+  return (threadIdx.x == 0) ? ld_agent(ctrl + CTRL_EPOCH) : 0;
+}
+
+// thread 0: publish the epoch to LDS and count this workgroup as started.  The increment
+// carries a data dependency on the epoch value, so it is performed after the load.
+__device__ __forceinline__ int wg_epoch_publish(int* ctrl, int e, int* lds_epoch) {
+  int started = 0;
+  if (threadIdx.x == 0) {
+    *lds_epoch = e;
+    started = add_agent(ctrl + CTRL_STARTED, 1 + (e < 0 ? 1 : 0));
+  }
+  return started;
+}
+
+__device__ __forceinline__ void wg_epoch_end(int* ctrl, int e, int started) {
+  if (threadIdx.x == 0 && started == (int)gridDim.x - 1) {
+    set_agent(ctrl + CTRL_STARTED, 0);
+    set_agent(ctrl + CTRL_EPOCH, e + 1);
+  }
+}
+
+__device__ __forceinline__ uint64_t tagged(float v, uint32_t tag) {
+  return ((uint64_t)tag << 32) | (uint64_t)__float_as_uint(v);
+}
+
+// Bounded wait until a tagged word carries `tag`; on expiry the status word is set and the
+// stale value is used, so the kernel always finishes.
+__device__ __forceinline__ uint64_t wait_tag(const uint64_t* p, uint64_t v, uint32_t tag, int* ctrl, int spin_limit) {
+  int spins = 0;
+  while ((uint32_t)(v >> 32) != tag) {
+    __builtin_amdgcn_s_sleep(2);
+    if (++spins > spin_limit) {
+      set_agent(ctrl + CTRL_STATUS, 1);
+      break;
+    }
+    v = ld_agent_u64(p);
+  }
+  return v;
+}
+
+// ======================================================================================
+// Down-projection ("shrink").  Work item = (adapter a, token block of its segment,
+// group of 16*JP ranks, K-part).  A_a is stored transposed, bf16 [r_a][K], so both MFMA
+// operands are rows with K contiguous: the x operand is 16 tokens of segment a (gathered
+// through sorted_tok), the A operand is 16 ranks.  Lane (i = l%16, g = l/16) loads 32
+// contiguous bytes (k = k0+16g .. k0+16g+15) of its row and feeds them to two 16x16x32
+// MFMAs; both operands use the same k assignment, so the products pair up.  The four
+// waves take interleaved 64-wide k-steps, with the loads of the next U steps in flight
+// while the current ones are multiplied; the wave sums meet in LDS in wave order.
+// Output: t (or its K-part) for each token of the block, in original token order.
+// ======================================================================================
+// In the fused launch (ctrl != null) the workgroup publishes the launch epoch once its
+// first loads are in flight (or when it finds no work); the tag is read after a barrier.
+template <int TG, int JP, int U>
+__device__ void shrink_item(const ShrinkParams& p, int item, char* smem, int* ctrl, int e, int* lds_epoch,
+                            int* started) {
+  bool published = false;
+  auto publish = [&]() {
+    if (ctrl && !published) *started = wg_epoch_publish(ctrl, e, lds_epoch);
+    published = true;
+  };
+  const int kp = item % p.kparts;
+  int rest = item / p.kparts;
+  const int jg = rest % p.n_jg;
+  rest /= p.n_jg;
+  const int tb = rest % p.n_tblk;
+  const int a = rest / p.n_tblk;
+  // With at most 16 tokens (and ids at hand) the workgroup takes all token rows and keeps
+  // the rows of adapter a: no dependent loads of seg_indptr and sorted_tok before x.
+  const bool direct = (p.ids != nullptr) && (p.T <= 16);
+  const int s0 = direct ? 0 : p.seg_indptr[a];
+  const int L = direct ? p.T : p.seg_indptr[a + 1] - s0;
+  const int tok_begin = tb * p.tblk;
+  const int r = p.ranks[a];
+  const int j_begin = jg * JP * 16;
+  // no work: empty token block, unsupported rank (adapter skipped), or ranks beyond r_a
+  if (tok_begin >= L || r < 8 || r > p.r_max || (r & 7) || j_begin >= r) {
+    publish();
+    return;
+  }
+  const int tok_end = min(L, tok_begin + p.tblk);
+  const int njt = min(JP, (r - j_begin + 15) >> 4);
+  const uint16_t* __restrict__ A = reinterpret_cast<const uint16_t*>(p.A_ptrs[a]);
+  // wave index as a scalar: conditions derived from it must compile to branches, since an
+  // MFMA executes for every lane whatever the EXEC mask
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, li = lane & 15,
+            g = lane >> 4;
+  const int k_begin = kp * p.kpart_len, k_end = min(p.K, k_begin + p.kpart_len);
+  const int nsteps = (k_end - k_begin) >> 6;
+  float* red = reinterpret_cast<float*>(smem);  // [4 waves][TG][JP][64 lanes][4]
+
+  const uint16_t* arow[JP];
 #pragma unroll
-  for (int jt = 0; jt < 4; ++jt) {
-    const int j = jt * 16 + li;
-    av[jt] = (jt < JT) && (j < r);
-    arow[jt] = A + (long)(av[jt] ? j : 0) * p.K + 16 * g;
+  for (int jt = 0; jt < JP; ++jt) {
+    const int j = j_begin + jt * 16 + li;
+    arow[jt] = A + (long)((jt < njt && j < r) ? j : 0) * p.K + k_begin + 16 * g;
   }
 
-  for (int tg0 = 0; tg0 < L; tg0 += TG * 16) {
-    const int ntt = min(TG, (L - tg0 + 15) >> 4);
+  for (int t0 = tok_begin; t0 < tok_end; t0 += TG * 16) {
+    const int ntt = min(TG, (tok_end - t0 + 15) >> 4);
     const uint16_t* xrow[TG];
-    bool xv[TG];
 #pragma unroll
     for (int tt = 0; tt < TG; ++tt) {
-      const int pos = tg0 + tt * 16 + li;
-      xv[tt] = (tt < ntt) && (pos < L);
-      xrow[tt] = p.x + (long)(xv[tt] ? p.sorted_tok[s0 + pos] : 0) * p.K + 16 * g;
+      const int pos = min(t0 + tt * 16 + li, tok_end - 1);
+      xrow[tt] = p.x + (long)(direct ? pos : p.sorted_tok[s0 + pos]) * p.K + k_begin + 16 * g;
     }
-    v4f acc[TG][4];
+    v4f acc[TG][JP];
 #pragma unroll
     for (int tt = 0; tt < TG; ++tt)
 #pragma unroll
-      for (int jt = 0; jt < 4; ++jt) acc[tt][jt] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int jt = 0; jt < JP; ++jt) acc[tt][jt] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    for (int s = wave; s < nsteps; s += 4 * U) {
-      uint4 xa[U][TG][2], aa[U][4][2];
+    // Loads are unconditional with clamped (always valid) addresses: a predicated load
+    // would compile to a branch that waits for it, serialising the stream.  Rows past the
+    // segment or the rank read a valid row and only feed outputs that are discarded;
+    // k-steps past the range are skipped at the MFMA (uniform branch).
+    uint4 xa[2][U][TG][2], aa[2][U][JP][2];
+    auto load = [&](int buf, int sbase) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int su = s + 4 * u;
-        const int k0 = k_begin + su * 64;
-        const bool sv = su < nsteps;
+        const int k0 = min(sbase + 4 * u, nsteps - 1) * 64;
 #pragma unroll
         for (int tt = 0; tt < TG; ++tt) {
-          const bool v = sv && xv[tt];
-          xa[u][tt][0] = v ? ldg16(xrow[tt] + k0) : zero4();
-          xa[u][tt][1] = v ? ldg16(xrow[tt] + k0 + 8) : zero4();
+          xa[buf][u][tt][0] = ldg16(xrow[tt] + k0);
+          xa[buf][u][tt][1] = ldg16(xrow[tt] + k0 + 8);
         }
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
-          const bool v = sv && av[jt];
-          aa[u][jt][0] = v ? ldg16(arow[jt] + k0) : zero4();
-          aa[u][jt][1] = v ? ldg16(arow[jt] + k0 + 8) : zero4();
+        for (int jt = 0; jt < JP; ++jt) {
+          aa[buf][u][jt][0] = ldg16(arow[jt] + k0);
+          aa[buf][u][jt][1] = ldg16(arow[jt] + k0 + 8);
         }
       }
+    };
+    auto mma = [&](int buf, int sbase) {
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+      for (int u = 0; u < U; ++u) {
+        if (sbase + 4 * u >= nsteps) break;
 #pragma unroll
-        for (int tt = 0; tt < TG; ++tt) {
-          if (tt >= ntt) continue;
+        for (int tt = 0; tt < TG; ++tt)
 #pragma unroll
-          for (int jt = 0; jt < 4; ++jt) {
-            if (jt >= JT) continue;
-            acc[tt][jt] = mfma_bf16_16x16x32(xa[u][tt][0], aa[u][jt][0], acc[tt][jt]);
-            acc[tt][jt] = mfma_bf16_16x16x32(xa[u][tt][1], aa[u][jt][1], acc[tt][jt]);
+          for (int jt = 0; jt < JP; ++jt) {
+            if (tt >= ntt || jt >= njt) continue;
+            acc[tt][jt] = mfma_bf16_16x16x32(xa[buf][u][tt][0], aa[buf][u][jt][0], acc[tt][jt]);
+            acc[tt][jt] = mfma_bf16_16x16x32(xa[buf][u][tt][1], aa[buf][u][jt][1], acc[tt][jt]);
           }
-        }
+      }
+    };
+    load(0, wave);
+    for (int s = wave; s < nsteps; s += 8 * U) {
+      load(1, s + 4 * U);
+      mma(0, s);
+      load(0, s + 8 * U);
+      mma(1, s + 4 * U);
     }
+    publish();  // the epoch is needed only for the stores below
     // cross-wave sum in fixed wave order
 #pragma unroll
     for (int tt = 0; tt < TG; ++tt)
 #pragma unroll
-      for (int jt = 0; jt < 4; ++jt)
-        if (tt < ntt && jt < JT)
-          *reinterpret_cast<v4f*>(red + (((wave * TG + tt) * 4 + jt) * 64 + lane) * 4) = acc[tt][jt];
+      for (int jt = 0; jt < JP; ++jt)
+        *reinterpret_cast<v4f*>(red + (((wave * TG + tt) * JP + jt) * 64 + lane) * 4) = acc[tt][jt];
     __syncthreads();
+    const uint32_t tag = ctrl ? (uint32_t)(*lds_epoch) + 1u : 0u;
 #pragma unroll
     for (int tt = 0; tt < TG; ++tt)
 #pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
-        if (tt >= ntt || jt >= JT || ((tt * 4 + jt) & 3) != wave) continue;
-        v4f sum = *reinterpret_cast<const v4f*>(red + (((0 * TG + tt) * 4 + jt) * 64 + lane) * 4);
+      for (int jt = 0; jt < JP; ++jt) {
+        if (tt >= ntt || jt >= njt || ((tt * JP + jt) & 3) != wave) continue;
+        v4f sum = *reinterpret_cast<const v4f*>(red + (((0 * TG + tt) * JP + jt) * 64 + lane) * 4);
 #pragma unroll
-        for (int w = 1; w < 4; ++w) sum += *reinterpret_cast<const v4f*>(red + (((w * TG + tt) * 4 + jt) * 64 + lane) * 4);
-        const int j = jt * 16 + li;
+        for (int w = 1; w < 4; ++w)
+          sum += *reinterpret_cast<const v4f*>(red + (((w * TG + tt) * JP + jt) * 64 + lane) * 4);
+        const int j = j_begin + jt * 16 + li;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int pos = tg0 + tt * 16 + 4 * g + v;
-          if (pos < L && j < r) {
-            if (single) st_agent(p.t + (long)p.sorted_tok[s0 + pos] * p.r_max + j, sum[v]);
-            else st_agent(p.part + ((long)c * p.T + (s0 + pos)) * p.r_max + j, sum[v]);
+          const int pos = t0 + tt * 16 + 4 * g + v;
+          if (pos < tok_end && j < r && (!direct || p.ids[pos] == a)) {
+            const long tok = direct ? pos : p.sorted_tok[s0 + pos];
+            if (p.t_tag) st_agent_u64(p.t_tag + ((long)kp * p.T + tok) * p.r_max + j, tagged(sum[v], tag));
+            if (p.t_out && p.kparts == 1) p.t_out[tok * p.r_max + j] = sum[v];
           }
         }
       }
     __syncthreads();
   }
-  if (single) {
-    // columns j in [r, r_max) of this segment's t rows are zero
-    for (int idx = tid; idx < L * (p.r_max - r); idx += 256) {
-      const int pos = idx / (p.r_max - r), j = r + idx % (p.r_max - r);
-      st_agent(p.t + (long)p.sorted_tok[s0 + pos] * p.r_max + j, 0.f);
+  // columns j in [r, r_max) of the caller's t are zero
+  if (p.t_out && jg == 0 && kp == 0 && r < p.r_max) {
+    const int w = p.r_max - r;
+    for (int idx = tid; idx < (tok_end - tok_begin) * w; idx += 256) {
+      const int pos = tok_begin + idx / w;
+      if (direct && p.ids[pos] != a) continue;
+      const long tok = direct ? pos : p.sorted_tok[s0 + pos];
+      p.t_out[tok * p.r_max + r + idx % w] = 0.f;
     }
-    return;
   }
-  // last-arriver reduction over the chunks of adapter a
-  wait_stores();
-  __syncthreads();
-  if (tid == 0) {
-    const int prev = add_agent(&p.ad_ctr[a], 1);
-    *flag = (prev == p.nchunks - 1);
-  }
-  __syncthreads();
-  if (!*flag) return;
-  for (int idx = tid; idx < L * p.r_max; idx += 256) {
-    const int pos = idx / p.r_max, j = idx % p.r_max;
-    float sum = 0.f;
-    if (j < r)
-      for (int cc = 0; cc < p.nchunks; ++cc) sum += ld_agent(p.part + ((long)cc * p.T + (s0 + pos)) * p.r_max + j);
-    st_agent(p.t + (long)p.sorted_tok[s0 + pos] * p.r_max + j, sum);
-  }
-  if (tid == 0) set_agent(&p.ad_ctr[a], 0);
 }
 
-template <int TG, int U>
+template <int TG, int JP, int U>
 __global__ __launch_bounds__(256) void k_shrink(ShrinkParams p) {
   extern __shared__ __align__(16) char smem[];
-  shrink_item<TG, U>(p, blockIdx.x, smem);
+  int started = 0;
+  shrink_item<TG, JP, U>(p, blockIdx.x, smem, nullptr, 0, nullptr, &started);
 }
 
 // ======================================================================================
@@ -296,59 +403,101 @@ __global__ __launch_bounds__(256) void k_expand(ExpandParams p) {
 // ======================================================================================
 // Base GEMM with the LoRA epilogue.
 //
-// Workgroup tile: TT*16 tokens x WN = 4*CT*16 output channels over a K-range; wave w owns
-// columns [w*CT*16, (w+1)*CT*16) of the tile and all its tokens.  Per K-chunk of KC:
-//   1. every lane issues the loads of its W fragments for the whole chunk straight into
-//      registers (each W byte is read by exactly one lane of one workgroup per K-split);
-//   2. the workgroup converts the chunk of x to MXFP8 (or copies pre-quantised codes)
-//      into LDS, one 32-block per thread-iteration, rows padded by 16 bytes so that the
-//      16 lanes of a lane group hit distinct banks;
-//   3. per 128-wide k-step each wave reads its TT x-fragments from LDS once and issues
-//      TT*CT scaled MFMAs (x scale from the MX block, W scale 1.0 for FP8 or the MXFP4
-//      block scale).
-// K-splits write their accumulators to the workspace in lane order; the last split of a
-// tile to arrive sums all of them in split order and runs the epilogue.
-// Epilogue: FP8 channel scale; then, in fused mode, wait until every down-projection
-// workgroup has finished (bounded spin on an agent-scope counter); then for each token
-// tile and each adapter present in it, one bf16 MFMA per 32 ranks adds
-// (s_a * t[tok]) @ B_a to the rows of that adapter's tokens; round to bf16 and store.
+// Workgroup tile: TT*16 tokens x WN = WC*CT*16 output channels over a K-range.  The four
+// waves form a WC x WK grid: wave (wc, wk) owns columns [wc*CT*16, (wc+1)*CT*16) of the
+// tile and the k-steps s with s % WK == wk.  Per K-chunk of KC:
+//   * the x loads of the chunk are issued before its W loads (loads retire in order, so
+//     x can be quantised while W is still in flight), and the loads of chunk c+1 are
+//     issued before the MFMAs of chunk c;
+//   * W fragments go straight from HBM into registers (each W byte is read by exactly one
+//     lane of one workgroup per K-split);
+//   * the workgroup converts the chunk of x to MXFP8 (or copies pre-quantised codes) into
+//     LDS, rows padded by 16 bytes so the 16 lanes of a lane group hit distinct banks;
+//   * per 128-wide k-step a wave reads its TT x-fragments from LDS once and issues TT*CT
+//     scaled MFMAs (x scale from the MX block; W scale 1.0 for FP8, the block scale for
+//     MXFP4).
+// The WK wave sums meet in LDS in wave order.  With a K-split over workgroups, the splits
+// other than the last store their sums and a tagged flag; the last split of the tile
+// (highest id) waits for the flags, adds the sums in split order and runs the epilogue.
+// Epilogue: FP8 channel scale; then, if the layer has adapters, the distinct adapters of
+// the token block are listed, t is gathered (waiting for its tag in the fused launch) and
+// stored pre-scaled as bf16 in LDS, B_a^T slices for the tile's columns are staged in LDS,
+// and for each token tile and each adapter present in it one bf16 MFMA per 32 ranks adds
+// (s_a t[tok]) @ B_a to the rows of that adapter's tokens; finally bf16 stores (RNE).
 // ======================================================================================
 template <int TT>
 struct ChunkK {
-  static constexpr int KC = (TT == 1) ? 1024 : ((TT <= 4) ? 512 : 256);
+  static constexpr int KC = (TT == 1) ? 2048 : ((TT <= 4) ? 512 : 256);
   static constexpr int STEPS = KC / 128;
-  static constexpr int ROW = KC + 16;  // LDS row stride in bytes
+  static constexpr int ROW = KC + 16;                     // LDS row stride in bytes
+  static constexpr int NBLK = TT * 16 * (KC / 32) / 256;  // 32-blocks of x per thread per chunk
 };
 
-template <int FMT, int TT, int CT, bool XQ>
-__device__ void gemm_item(const GemmParams& p, int item, char* smem) {
-  constexpr int KC = ChunkK<TT>::KC, STEPS = ChunkK<TT>::STEPS, ROW = ChunkK<TT>::ROW;
-  constexpr int WN = 4 * CT * 16;
-  constexpr int FMTB = (FMT == LORA_W_FP8_E4M3) ? 0 : 4;
-  uint8_t* xs = reinterpret_cast<uint8_t*>(smem);               // [TT*16][ROW]
-  uint8_t* ss = xs + TT * 16 * ROW;                             // [TT*16][KC/32]
-  int* flag = reinterpret_cast<int*>(ss + TT * 16 * (KC / 32) + 16);
+constexpr int EPI_LIST_MAX = 128;
+constexpr int EPI_BBUF = 32768;                   // bytes of B staged per batch
+constexpr int EPI_BCHUNKS = EPI_BBUF / 16 / 256;  // 16-byte chunks per thread per batch
+constexpr int EPI_TE = 8;                         // t elements per thread per gather batch
+constexpr int MAX_KPARTS = 4;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, g = lane >> 4;
+template <int TT>
+struct EpiLayout {
+  static constexpr int ROWS = TT * 16;
+  // byte offsets inside the epilogue's LDS area
+  static constexpr int ROWAD = 0;                          // int [ROWS]: adapter of the row (-1: none)
+  static constexpr int ROWRK = ROWAD + ROWS * 4;           // int [ROWS]: its rank
+  static constexpr int ROWSC = ROWRK + ROWS * 4;           // float [ROWS]: its scale
+  static constexpr int LIST = ROWSC + ROWS * 4;            // int4 [EPI_LIST_MAX]: a, r, offset, first chunk
+  static constexpr int META = LIST + EPI_LIST_MAX * 16;    // int [16]
+  static constexpr int TB = META + 64;                     // bf16 [ROWS][MAX_RANK]
+  static constexpr int BS = TB + ROWS * MAX_RANK * 2;      // bf16 B staging
+  static constexpr int BYTES = BS + EPI_BBUF;
+};
+
+template <int TT, int CT, int WC, int WK>
+struct GemmSmem {
+  using CK = ChunkK<TT>;
+  static constexpr int MAIN = TT * 16 * CK::ROW + TT * 16 * (CK::KC / 32);
+  static constexpr int RED = (WK - 1) * WC * TT * CT * 256 * 4;
+  static constexpr int EPI = EpiLayout<TT>::BYTES;
+  static constexpr int M1 = MAIN > RED ? MAIN : RED;
+  static constexpr int BYTES = M1 > EPI ? M1 : EPI;
+};
+
+template <int FMT, int TT, int CT, int WC, int WK, bool XQ>
+__device__ void gemm_item(const GemmParams& p, int item, char* smem, int e, int* lds_epoch, int* started) {
+  using CK = ChunkK<TT>;
+  constexpr int KC = CK::KC, STEPS = CK::STEPS, ROW = CK::ROW, NBLK = CK::NBLK;
+  constexpr int SPW = STEPS / WK;  // k-steps per wave per chunk
+  constexpr int WN = WC * CT * 16;
+  constexpr int FMTB = (FMT == LORA_W_FP8_E4M3) ? 0 : 4;
+  constexpr int ROWS = TT * 16;
+  static_assert(STEPS % WK == 0, "k-steps per chunk must split evenly over the k-waves");
+  static_assert(NBLK >= 1, "chunk too small for the workgroup");
+  uint8_t* xs = reinterpret_cast<uint8_t*>(smem);  // [ROWS][ROW]
+  uint8_t* ss = xs + ROWS * ROW;                    // [ROWS][KC/32]
+
+  // wave index as a scalar (see the down-projection)
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, li = lane & 15,
+            g = lane >> 4;
+  const int wc = wave % WC, wk = wave / WC;
   const int ks = item % p.ksplit;
   const int tile = item / p.ksplit;
   const int cb = tile % p.n_cb, tb = tile / p.n_cb;
-  const int row0 = tb * TT * 16;
-  const int nw0 = cb * WN + wave * CT * 16;
+  const int row0 = tb * ROWS;
+  const int n_tile0 = cb * WN;
+  const int nw0 = n_tile0 + wc * CT * 16;
   const int K = p.K;
 
+  // packed W (see k_pack_weight): per 16-channel tile and k-step, 2 KB (FP8) or 1 KB
+  // (MXFP4) in lane order, plus 64 scale bytes for MXFP4
+  constexpr int WSTEP = (FMT == LORA_W_FP8_E4M3) ? 2048 : 1024;
   const uint8_t* wrow[CT];
   const uint8_t* wsrow[CT];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
-    const long n = nw0 + ct * 16 + li;
-    if (FMT == LORA_W_FP8_E4M3) {
-      wrow[ct] = p.wq + n * K + 16 * g;
-      wsrow[ct] = nullptr;
-    } else {
-      wrow[ct] = p.wq + n * (K / 2) + 16 * g;
-      wsrow[ct] = p.ws_fp4 + n * (K / 32) + g;
-    }
+    const long nt = (nw0 + ct * 16) / 16;
+    wrow[ct] = p.wq + nt * (K / 128) * WSTEP + lane * 16;
+    wsrow[ct] = (FMT == LORA_W_FP8_E4M3) ? nullptr : p.ws_fp4 + nt * (K / 128) * 64 + lane;
   }
 
   v4f acc[TT][CT];
@@ -357,122 +506,233 @@ __device__ void gemm_item(const GemmParams& p, int item, char* smem) {
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) acc[tt][ct] = v4f{0.f, 0.f, 0.f, 0.f};
 
+  // adapter, rank and scale of row `tid` of the token block, fetched now (before the bulk
+  // loads, which retire after them) and used in the epilogue
+  int row_a = -1, row_r = 0;
+  float row_s = 0.f;
+  if (p.lora && ks == p.ksplit - 1 && tid < ROWS) {
+    const int tok = row0 + tid;
+    const int a = p.ids[min(tok, p.T - 1)];
+    if (tok < p.T && a >= 0 && a < p.n_ad) {
+      row_a = a;
+      row_r = p.ranks[a];
+      row_s = p.scales[a];
+      if (row_r < 8 || row_r > p.r_max || (row_r & 7)) row_a = -1;  // unsupported rank: skipped
+    }
+    if (row_a < 0) row_r = 0;
+  }
+
   const int kb = ks * p.krange, ke = min(K, kb + p.krange);
-  for (int kc0 = kb; kc0 < ke; kc0 += KC) {
-    const int kcl = min(KC, ke - kc0);
-    const int nsteps = kcl >> 7;
-    // 1. W fragments of the chunk
-    uint4 wlo[STEPS][CT], whi[STEPS][CT];
-    int wsc[STEPS][CT];
+  const int nchunks = (ke - kb + KC - 1) / KC;
+  // Every tile walks its K-range from a different place (chunk and step rotation), so that
+  // the workgroups do not all hit the same HBM channels with rows that are K bytes apart.
+  const int crot = tile % nchunks;
+  const int srot = (tile * 5) & (STEPS - 1);
+  auto chunk_k0 = [&](int c) { return kb + ((c + crot) % nchunks) * KC; };
+
+  // register staging, two chunks ahead: x (raw bf16 or pre-quantised) and W
+  uint4 xr[2][NBLK][4];
+  uint32_t xcode[2][NBLK];
+  uint4 wlo[2][SPW][CT], whi[2][SPW][CT];
+  int wsc[2][SPW][CT];
+
+  auto load_x = [&](int buf, int c) {
+    const int kc0 = chunk_k0(c);
+    const int bpr = min(KC, ke - kc0) >> 5;
+    // unconditional loads from clamped addresses (see the down-projection): rows past T
+    // repeat row T-1 and only feed rows that are never stored; blocks past the chunk end
+    // are never read back from LDS
 #pragma unroll
-    for (int s = 0; s < STEPS; ++s)
+    for (int m = 0; m < NBLK; ++m) {
+      const int b = tid + 256 * m;
+      const int row = b / (KC / 32), k32 = min(b % (KC / 32), bpr - 1);
+      const long tok = min(row0 + row, p.T - 1);
+      if (XQ) {
+        const uint8_t* src = p.xq + tok * K + kc0 + k32 * 32;
+        xr[buf][m][0] = ldg16(src);
+        xr[buf][m][1] = ldg16(src + 16);
+        xcode[buf][m] = p.xsc[tok * (K / 32) + (kc0 >> 5) + k32];
+      } else {
+        const uint16_t* src = p.x + tok * K + kc0 + k32 * 32;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xr[buf][m][q] = ldg16(src + 8 * q);
+      }
+    }
+  };
+  // physical k-step of logical step s in a chunk of nsteps steps
+  auto phys_step = [&](int s, int nsteps) { return (s + srot) % nsteps; };
+  auto load_w = [&](int buf, int c) {
+    const int kc0 = chunk_k0(c);
+    const int nsteps = min(KC, ke - kc0) >> 7;
+    // k-steps past the range load step 0 again; their MFMAs are skipped
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+      const int s = wk + WK * i;
+      const long ksg = (kc0 >> 7) + (s < nsteps ? phys_step(s, nsteps) : 0);  // global k-step
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
-        const int k = kc0 + s * 128;
-        if (s < nsteps) {
-          if (FMT == LORA_W_FP8_E4M3) {
-            wlo[s][ct] = ldg16(wrow[ct] + k);
-            whi[s][ct] = ldg16(wrow[ct] + k + 64);
-            wsc[s][ct] = 127;
-          } else {
-            wlo[s][ct] = ldg16(wrow[ct] + k / 2);
-            whi[s][ct] = zero4();
-            wsc[s][ct] = wsrow[ct][k / 32];
-          }
+        if (FMT == LORA_W_FP8_E4M3) {
+          wlo[buf][i][ct] = ldg16(wrow[ct] + ksg * WSTEP);
+          whi[buf][i][ct] = ldg16(wrow[ct] + ksg * WSTEP + 1024);
+          wsc[buf][i][ct] = 127;
         } else {
-          wlo[s][ct] = zero4();
-          whi[s][ct] = zero4();
-          wsc[s][ct] = 127;
+          wlo[buf][i][ct] = ldg16(wrow[ct] + ksg * WSTEP);
+          whi[buf][i][ct] = zero4();
+          wsc[buf][i][ct] = (int)wsrow[ct][ksg * 64];
         }
       }
-    // 2. x chunk -> MXFP8 in LDS
-    const int bpr = kcl >> 5;  // 32-blocks per row in this chunk
-    const int nblk = TT * 16 * bpr;
-    for (int b = tid; b < nblk; b += 256) {
-      const int row = b / bpr, k32 = b - row * bpr;
-      const int tok = row0 + row;
-      uint4 out[2];
-      uint32_t code = 0;
-      if (tok < p.T) {
-        if (XQ) {
-          const uint8_t* src = p.xq + (long)tok * K + kc0 + k32 * 32;
-          out[0] = ldg16(src);
-          out[1] = ldg16(src + 16);
-          code = p.xsc[(long)tok * (K / 32) + (kc0 >> 5) + k32];
-        } else {
-          const uint16_t* src = p.x + (long)tok * K + kc0 + k32 * 32;
-          uint4 in[4];
+    }
+  };
+  auto stage_x = [&](int buf) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) in[i] = ldg16(src + 8 * i);
-          code = mx_block_code(in);
-          mx_block_quant(in, code, out);
-        }
+    for (int m = 0; m < NBLK; ++m) {
+      const int b = tid + 256 * m;
+      const int row = b / (KC / 32), k32 = b % (KC / 32);
+      uint4 out[2];
+      uint32_t code;
+      if (XQ) {
+        out[0] = xr[buf][m][0];
+        out[1] = xr[buf][m][1];
+        code = xcode[buf][m];
       } else {
-        out[0] = zero4();
-        out[1] = zero4();
+        code = mx_block_code(xr[buf][m]);
+        mx_block_quant(xr[buf][m], code, out);
       }
       *reinterpret_cast<uint4*>(xs + row * ROW + k32 * 32) = out[0];
       *reinterpret_cast<uint4*>(xs + row * ROW + k32 * 32 + 16) = out[1];
       ss[row * (KC / 32) + k32] = (uint8_t)code;
     }
-    __syncthreads();
-    // 3. MFMAs
+  };
+  auto mma_chunk = [&](int buf, int c) {
+    const int kc0 = chunk_k0(c);
+    const int nsteps = min(KC, ke - kc0) >> 7;
 #pragma unroll
-    for (int s = 0; s < STEPS; ++s) {
+    for (int i = 0; i < SPW; ++i) {
+      const int s = wk + WK * i;
       if (s >= nsteps) break;
+      const int sp = phys_step(s, nsteps);
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) {
         const int row = tt * 16 + li;
-        const uint8_t* xp = xs + row * ROW + s * 128 + 16 * g;
+        const uint8_t* xp = xs + row * ROW + sp * 128 + 16 * g;
         const uint4 alo = *reinterpret_cast<const uint4*>(xp);
         const uint4 ahi = *reinterpret_cast<const uint4*>(xp + 64);
-        const int sa = ss[row * (KC / 32) + s * 4 + g];
+        const int sa = ss[row * (KC / 32) + sp * 4 + g];
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
-          acc[tt][ct] = mfma_scaled_16x16x128<FMTB>(alo, ahi, wlo[s][ct], whi[s][ct], acc[tt][ct], sa, wsc[s][ct]);
+          acc[tt][ct] = mfma_scaled_16x16x128<FMTB>(alo, ahi, wlo[buf][i][ct], whi[buf][i][ct], acc[tt][ct], sa,
+                                                     wsc[buf][i][ct]);
       }
+    }
+  };
+
+  // chunks 0 and 1 in flight before anything waits; chunk c+2 is issued while chunk c is
+  // multiplied.  x of a chunk is always issued before its W (loads retire in order).
+  load_x(0, 0);
+  load_w(0, 0);
+  if (nchunks > 1) {
+    load_x(1, 1);
+    load_w(1, 1);
+  }
+  for (int c = 0; c < nchunks; c += 2) {
+    stage_x(0);
+    __syncthreads();
+    if (c + 2 < nchunks) load_x(0, c + 2);
+    mma_chunk(0, c);
+    if (c + 2 < nchunks) load_w(0, c + 2);
+    __syncthreads();
+    if (c + 1 >= nchunks) break;
+    stage_x(1);
+    __syncthreads();
+    if (c + 3 < nchunks) load_x(1, c + 3);
+    mma_chunk(1, c + 1);
+    if (c + 3 < nchunks) load_w(1, c + 3);
+    __syncthreads();
+  }
+  // publish the launch epoch only now: waiting for it earlier would stall wave 0
+  *started = wg_epoch_publish(p.ctrl, e, lds_epoch);
+  __syncthreads();
+  const uint32_t tag = (uint32_t)(*lds_epoch) + 1u;
+
+  // ---- sums of the WK k-waves, in wave order, end up in the waves with wk == 0
+  if (WK > 1) {
+    float* red = reinterpret_cast<float*>(smem);
+    if (wk > 0) {
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+          *reinterpret_cast<v4f*>(red + ((((wk - 1) * WC + wc) * TT + tt) * CT + ct) * 256 + lane * 4) = acc[tt][ct];
+    }
+    __syncthreads();
+    if (wk == 0) {
+#pragma unroll
+      for (int w = 1; w < WK; ++w)
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct)
+            acc[tt][ct] +=
+                *reinterpret_cast<const v4f*>(red + ((((w - 1) * WC + wc) * TT + tt) * CT + ct) * 256 + lane * 4);
     }
     __syncthreads();
   }
 
-  // ---- K-split reduction (deterministic: summed in split order by the last arriver)
-  const int ntiles = p.n_cb * p.n_tb;
+  // ---- K-split over workgroups: producers store sums + flag, the last split reduces
   if (p.ksplit > 1) {
     constexpr int PER_WAVE = TT * CT * 256;
-    float* mine = p.gpart + (((long)tile * p.ksplit + ks) * 4 + wave) * PER_WAVE;
+    const long tile_base = (long)tile * p.ksplit;
+    if (ks < p.ksplit - 1) {
+      if (wk == 0) {
+        float* mine = p.gpart + ((tile_base + ks) * WC + wc) * PER_WAVE;
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
+        for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) st_agent(mine + ((tt * CT + ct) * 64 + lane) * 4 + v, acc[tt][ct][v]);
-    wait_stores();
-    __syncthreads();
-    if (tid == 0) {
-      const int prev = add_agent(&p.tile_ctr[tile], 1);
-      *flag = (prev == p.ksplit - 1);
+          for (int ct = 0; ct < CT; ++ct) {
+            uint64_t* d = reinterpret_cast<uint64_t*>(mine + ((tt * CT + ct) * 64 + lane) * 4);
+            st_agent_u64(d, ((uint64_t)__float_as_uint(acc[tt][ct][1]) << 32) | __float_as_uint(acc[tt][ct][0]));
+            st_agent_u64(d + 1, ((uint64_t)__float_as_uint(acc[tt][ct][3]) << 32) | __float_as_uint(acc[tt][ct][2]));
+          }
+      }
+      wait_stores();
+      __syncthreads();
+      if (tid == 0) set_agent(p.gflag + tile_base + ks, (int)tag);
+      return;
+    }
+    // the reducer: wait for every producer of this tile
+    for (int k2 = tid; k2 < p.ksplit - 1; k2 += 256) {
+      int spins = 0;
+      while ((uint32_t)ld_agent(p.gflag + tile_base + k2) != tag) {
+        __builtin_amdgcn_s_sleep(2);
+        if (++spins > p.spin_limit) {
+          set_agent(p.ctrl + CTRL_STATUS, 1);
+          break;
+        }
+      }
     }
     __syncthreads();
-    if (!*flag) return;
+    if (wk == 0) {
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
+      for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        v4f sum = v4f{0.f, 0.f, 0.f, 0.f};
-        for (int k2 = 0; k2 < p.ksplit; ++k2) {
-          const float* src = p.gpart + (((long)tile * p.ksplit + k2) * 4 + wave) * PER_WAVE + ((tt * CT + ct) * 64 + lane) * 4;
-          v4f v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = ld_agent(src + e);
-          sum += v;
+        for (int ct = 0; ct < CT; ++ct) {
+          v4f sum = v4f{0.f, 0.f, 0.f, 0.f};
+          for (int k2 = 0; k2 < p.ksplit - 1; ++k2) {
+            const uint64_t* src = reinterpret_cast<const uint64_t*>(p.gpart + ((tile_base + k2) * WC + wc) * PER_WAVE +
+                                                                    ((tt * CT + ct) * 64 + lane) * 4);
+            const uint64_t u0 = ld_agent_u64(src), u1 = ld_agent_u64(src + 1);
+            sum[0] += __uint_as_float((uint32_t)u0);
+            sum[1] += __uint_as_float((uint32_t)(u0 >> 32));
+            sum[2] += __uint_as_float((uint32_t)u1);
+            sum[3] += __uint_as_float((uint32_t)(u1 >> 32));
+          }
+          acc[tt][ct] = sum + acc[tt][ct];
         }
-        acc[tt][ct] = sum;
-      }
-    if (tid == 0) set_agent(&p.tile_ctr[tile], 0);
+    }
   }
 
   // ---- epilogue: channel scale
-  if (FMT == LORA_W_FP8_E4M3) {
+  if (FMT == LORA_W_FP8_E4M3 && wk == 0) {
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
       const float sw = p.ws_fp8[nw0 + ct * 16 + li];
@@ -483,134 +743,255 @@ __device__ void gemm_item(const GemmParams& p, int item, char* smem) {
 
   // ---- epilogue: adapter up-projection
   if (p.lora) {
-    if (p.n_shrink > 0) {
-      if (tid == 0) {
-        int spins = 0;
-        while (ld_agent(p.shrink_done) < p.n_shrink) {
-          __builtin_amdgcn_s_sleep(4);
-          if (++spins > p.spin_limit) {
-            set_agent(p.status, 1);
-            break;
-          }
-        }
-        const int prev = add_agent(p.wait_done, 1);
-        if (prev == ntiles - 1) {
-          set_agent(p.shrink_done, 0);
-          set_agent(p.wait_done, 0);
-        }
-      }
-      __syncthreads();
+    using EL = EpiLayout<TT>;
+    int* rowad = reinterpret_cast<int*>(smem + EL::ROWAD);
+    int* rowrk = reinterpret_cast<int*>(smem + EL::ROWRK);
+    float* rowsc = reinterpret_cast<float*>(smem + EL::ROWSC);
+    int4* list = reinterpret_cast<int4*>(smem + EL::LIST);
+    int* meta = reinterpret_cast<int*>(smem + EL::META);
+    uint16_t* tbuf = reinterpret_cast<uint16_t*>(smem + EL::TB);
+    uint16_t* bsb = reinterpret_cast<uint16_t*>(smem + EL::BS);
+    // (1) adapter, rank and scale of every row (fetched at the start)
+    if (tid < ROWS) {
+      rowad[tid] = row_a;
+      rowrk[tid] = row_r;
+      rowsc[tid] = row_s;
     }
+    __syncthreads();
+    // (2) distinct adapters in order of first appearance, and the first batch of them
+    //     whose B_a^T slices fit the staging buffer (one wave)
+    auto plan_batch = [&](int e_begin, int nl) {  // lane 0 of wave 0
+      int bytes = 0, e2 = e_begin, chunks = 0;
+      while (e2 < nl && bytes + WN * list[e2].y * 2 <= EPI_BBUF) {
+        list[e2].z = bytes / 2;  // element offset in the staging buffer
+        list[e2].w = chunks;     // first 16-byte chunk of this adapter
+        bytes += WN * list[e2].y * 2;
+        chunks += WN * list[e2].y / 8;
+        ++e2;
+      }
+      meta[1] = e2;
+      meta[2] = chunks;
+    };
+    if (wave == 0) {
+      int nl = 0;
+      for (int c0 = 0; c0 < ROWS; c0 += 64) {
+        const int a = (c0 + lane < ROWS) ? rowad[c0 + lane] : -1;
+        bool fresh = a >= 0;
+        for (int e2 = 0; e2 < nl; ++e2) fresh = fresh && (list[e2].x != a);
+        unsigned long long pending = __ballot(fresh);
+        while (pending) {
+          const int leader = __ffsll((long long)pending) - 1;
+          const int la = __shfl(a, leader);
+          if (lane == 0) list[nl] = make_int4(la, p.ranks[la], 0, 0);
+          ++nl;
+          pending &= ~__ballot(fresh && a == la);
+        }
+      }
+      if (lane == 0) {
+        meta[0] = nl;
+        plan_batch(0, nl);
+      }
+    }
+    __syncthreads();
+    const int nl = __builtin_amdgcn_readfirstlane(meta[0]);
+    // B chunks of a batch: loaded into registers, then stored to LDS
+    uint4 breg[EPI_BCHUNKS];
+    int bdst[EPI_BCHUNKS];
+    auto load_batch = [&](int e_begin, int e_end, int nch) {
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      const int tok = row0 + tt * 16 + li;  // A-operand row of this lane
-      const int a = (tok < p.T) ? p.ids[tok] : -1;
-      const bool valid = (a >= 0 && a < p.n_ad);
-      unsigned long long pending = __ballot(valid && g == 0);
-      while (pending) {
-        const int leader = __ffsll((long long)pending) - 1;
-        const int la = __shfl(a, leader);
-        const unsigned long long same = __ballot(valid && g == 0 && a == la);
-        const bool mine = valid && (a == la);
-        const int rk = p.ranks[la];
-        const int r = (rk < 8 || rk > p.r_max || (rk & 7)) ? 0 : rk;  // unsupported rank: skipped
-        const float sa = p.scales[la];
-        const uint16_t* __restrict__ Bt = reinterpret_cast<const uint16_t*>(p.B_ptrs[la]);
-        for (int j0 = 0; j0 < r; j0 += 32) {
-          const int j = j0 + 8 * g;
-          uint4 aop = zero4();
-          if (mine && j < r) {
-            const float* tp = p.t + (long)tok * p.r_max + j;
-            float tv[8];
+      for (int m = 0; m < EPI_BCHUNKS; ++m) {
+        const int c = min(tid + 256 * m, nch - 1);  // nch >= 1: a batch holds an adapter
+        int e2 = e_begin;
+        while (e2 + 1 < e_end && list[e2 + 1].w <= c) ++e2;
+        const int4 ent = list[e2];
+        const int cc = c - ent.w, per = ent.y / 8;
+        const int n = cc / per, jj = cc - n * per;
+        const uint16_t* Bt = reinterpret_cast<const uint16_t*>(p.B_ptrs[ent.x]);
+        breg[m] = ldg16(Bt + (long)(n_tile0 + n) * ent.y + jj * 8);
+        bdst[m] = (tid + 256 * m < nch) ? ent.z + n * ent.y + jj * 8 : -1;
+      }
+    };
+    auto mma_batch = [&](int e_begin, int e_end) {
+      if (wk != 0) return;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) tv[e] = sa * ld_agent(tp + e);
-            aop.x = f32_to_bf16_rne(tv[0]) | (f32_to_bf16_rne(tv[1]) << 16);
-            aop.y = f32_to_bf16_rne(tv[2]) | (f32_to_bf16_rne(tv[3]) << 16);
-            aop.z = f32_to_bf16_rne(tv[4]) | (f32_to_bf16_rne(tv[5]) << 16);
-            aop.w = f32_to_bf16_rne(tv[6]) | (f32_to_bf16_rne(tv[7]) << 16);
-          }
+      for (int tt = 0; tt < TT; ++tt) {
+        const int rad = rowad[tt * 16 + li];
+        for (int e2 = e_begin; e2 < e_end; ++e2) {
+          int4 ent = list[e2];  // same for every lane: made scalar so the loops below branch
+          ent.x = __builtin_amdgcn_readfirstlane(ent.x);
+          ent.y = __builtin_amdgcn_readfirstlane(ent.y);
+          ent.z = __builtin_amdgcn_readfirstlane(ent.z);
+          if (!__ballot(rad == ent.x)) continue;  // adapter absent from this token tile
+          const bool mine = (rad == ent.x);
+          for (int j0 = 0; j0 < ent.y; j0 += 32) {
+            const int j = j0 + 8 * g;
+            const uint4 aop =
+                (mine && j < ent.y) ? *reinterpret_cast<const uint4*>(tbuf + (tt * 16 + li) * MAX_RANK + j) : zero4();
 #pragma unroll
-          for (int ct = 0; ct < CT; ++ct) {
-            const long n = nw0 + ct * 16 + li;
-            const uint4 bop = (j < r) ? ldg16(Bt + n * r + j) : zero4();
-            acc[tt][ct] = mfma_bf16_16x16x32(aop, bop, acc[tt][ct]);
+            for (int ct = 0; ct < CT; ++ct) {
+              const int n = wc * CT * 16 + ct * 16 + li;
+              const uint4 bop = (j < ent.y) ? *reinterpret_cast<const uint4*>(bsb + ent.z + n * ent.y + j) : zero4();
+              acc[tt][ct] = mfma_bf16_16x16x32(aop, bop, acc[tt][ct]);
+            }
           }
         }
-        pending &= ~same;
       }
+    };
+    int e0 = 0;
+    int e1 = __builtin_amdgcn_readfirstlane(meta[1]), nch = __builtin_amdgcn_readfirstlane(meta[2]);
+    // (3) the first batch's B loads go out together with the t loads: one round trip
+    if (nl > 0) load_batch(0, e1, nch);
+    // (4) t rows -> LDS as bf16 pre-scaled by s_a (zero beyond the row's rank)
+    const int nel = ROWS * p.r_max;
+    for (int base = 0; base < nel && nl > 0; base += 256 * EPI_TE) {
+      float vals[EPI_TE];
+      if (p.t_tag) {
+        uint64_t raw[EPI_TE][MAX_KPARTS];
+        // all loads first (unconditional, clamped addresses), then the tag checks
+        long addr[EPI_TE];
+        bool need[EPI_TE];
+#pragma unroll
+        for (int m = 0; m < EPI_TE; ++m) {
+          const int idx = min(base + tid + 256 * m, nel - 1);
+          const int i = idx / p.r_max, j = idx - i * p.r_max;
+          need[m] = (base + tid + 256 * m < nel) && j < rowrk[i];
+          addr[m] = (long)min(row0 + i, p.T - 1) * p.r_max + j;
+#pragma unroll
+          for (int k2 = 0; k2 < MAX_KPARTS; ++k2)
+            raw[m][k2] = ld_agent_u64(p.t_tag + (long)min(k2, p.t_kparts - 1) * p.T * p.r_max + addr[m]);
+        }
+#pragma unroll
+        for (int m = 0; m < EPI_TE; ++m) {
+          float v = 0.f;
+#pragma unroll
+          for (int k2 = 0; k2 < MAX_KPARTS; ++k2) {
+            if (need[m] && k2 < p.t_kparts) {
+              const uint64_t w = wait_tag(p.t_tag + (long)k2 * p.T * p.r_max + addr[m], raw[m][k2], tag, p.ctrl,
+                                          p.spin_limit);
+              v += __uint_as_float((uint32_t)w);
+            }
+          }
+          vals[m] = v;
+        }
+      } else {
+        float raw[EPI_TE];
+#pragma unroll
+        for (int m = 0; m < EPI_TE; ++m) {
+          const int idx = min(base + tid + 256 * m, nel - 1);
+          const int i = idx / p.r_max;
+          raw[m] = p.t[(long)min(row0 + i, p.T - 1) * p.r_max + (idx - i * p.r_max)];
+        }
+#pragma unroll
+        for (int m = 0; m < EPI_TE; ++m) {
+          const int idx = base + tid + 256 * m;
+          const int i = min(idx, nel - 1) / p.r_max, j = min(idx, nel - 1) - i * p.r_max;
+          vals[m] = (idx < nel && j < rowrk[i]) ? raw[m] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < EPI_TE; ++m) {
+        const int idx = base + tid + 256 * m;
+        if (idx < nel) {
+          const int i = idx / p.r_max, j = idx - i * p.r_max;
+          tbuf[i * MAX_RANK + j] = (uint16_t)f32_to_bf16_rne(vals[m] * rowsc[i]);
+          if (p.t_out && cb == 0 && row0 + i < p.T && rowad[i] >= 0) p.t_out[(long)(row0 + i) * p.r_max + j] = vals[m];
+        }
+      }
+    }
+    // (5) batches: stage B in LDS, multiply; the next batch is planned by one lane
+    while (e0 < nl) {
+#pragma unroll
+      for (int m = 0; m < EPI_BCHUNKS; ++m)
+        if (bdst[m] >= 0) *reinterpret_cast<uint4*>(bsb + bdst[m]) = breg[m];
+      __syncthreads();
+      mma_batch(e0, e1);
+      __syncthreads();
+      e0 = e1;
+      if (e0 >= nl) break;
+      if (tid == 0) plan_batch(e0, nl);
+      __syncthreads();
+      e1 = __builtin_amdgcn_readfirstlane(meta[1]);
+      nch = __builtin_amdgcn_readfirstlane(meta[2]);
+      load_batch(e0, e1, nch);
     }
   }
 
   // ---- store bf16 (round to nearest even)
+  if (wk == 0) {
 #pragma unroll
-  for (int tt = 0; tt < TT; ++tt)
+    for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      const int n = nw0 + ct * 16 + li;
+      for (int ct = 0; ct < CT; ++ct) {
+        const int n = nw0 + ct * 16 + li;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int tok = row0 + tt * 16 + 4 * g + v;
-        if (tok < p.T) p.y[(long)tok * p.N + n] = (uint16_t)f32_to_bf16_rne(acc[tt][ct][v]);
+        for (int v = 0; v < 4; ++v) {
+          const int tok = row0 + tt * 16 + 4 * g + v;
+          if (tok < p.T) p.y[(long)tok * p.N + n] = (uint16_t)f32_to_bf16_rne(acc[tt][ct][v]);
+        }
       }
-    }
+  }
 }
 
-template <int FMT, int TT, int CT, bool XQ, int TG, int U>
+template <int FMT, int TT, int CT, int WC, int WK, bool XQ, int TG, int JP, int U>
 __global__ __launch_bounds__(256) void k_layer(ShrinkParams sp, GemmParams gp) {
   extern __shared__ __align__(16) char smem[];
+  __shared__ int lds_epoch;
+  const int e = wg_epoch_load(gp.ctrl);
   const int b = blockIdx.x;
+  int started = 0;
   if (b < gp.n_shrink) {
-    shrink_item<TG, U>(sp, b, smem);
-    wait_stores();
-    __syncthreads();
-    if (threadIdx.x == 0) add_agent(gp.shrink_done, 1);
-    return;
+    shrink_item<TG, JP, U>(sp, b, smem, gp.ctrl, e, &lds_epoch, &started);
+  } else {
+    gemm_item<FMT, TT, CT, WC, WK, XQ>(gp, b - gp.n_shrink, smem, e, &lds_epoch, &started);
   }
-  gemm_item<FMT, TT, CT, XQ>(gp, b - gp.n_shrink, smem);
+  wg_epoch_end(gp.ctrl, e, started);
 }
 
 // ======================================================================================
 // Launchers
 // ======================================================================================
-size_t shrink_smem_bytes(int TG) { return (size_t)4 * TG * 4 * 256 * sizeof(float) + 64; }
-
-template <int TT>
-size_t gemm_smem_bytes() {
-  return (size_t)TT * 16 * ChunkK<TT>::ROW + TT * 16 * (ChunkK<TT>::KC / 32) + 64;
+template <int TG, int JP, int U>
+constexpr size_t shrink_smem() {
+  return (size_t)4 * TG * JP * 256 * sizeof(float);
 }
 
-template <typename KernelT>
-static hipError_t launch(KernelT kern, int grid, size_t smem, hipStream_t stream, const ShrinkParams& sp,
-                         const GemmParams& gp) {
+template <typename KernelT, typename... Args>
+static hipError_t launch_k(KernelT kern, int grid, size_t smem, hipStream_t stream, Args... args) {
   if (smem > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)smem);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), smem, stream, sp, gp);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), smem, stream, args...);
   return hipGetLastError();
 }
 
-template <int FMT, int TT, int CT, bool XQ>
-static hipError_t launch_layer_t(int tg, int grid, hipStream_t stream, const ShrinkParams& sp, const GemmParams& gp) {
-  const size_t sm = std::max(gemm_smem_bytes<TT>(), gp.n_shrink > 0 ? shrink_smem_bytes(tg) : (size_t)0);
-  if (tg == 1) return launch(k_layer<FMT, TT, CT, XQ, 1, 4>, grid, sm, stream, sp, gp);
-  return launch(k_layer<FMT, TT, CT, XQ, 4, 1>, grid, sm, stream, sp, gp);
+template <int FMT, int TT, int CT, int WC, int WK, bool XQ>
+static hipError_t launch_layer_t(const LayerPlan& pl, int grid, hipStream_t stream, const ShrinkParams& sp,
+                                 const GemmParams& gp) {
+  // the down-projection shape goes with the GEMM shape: decode (one 16-rank tile per
+  // workgroup, two-step prefetch) or prefill (four token and two rank tiles)
+  constexpr int TG = XQ ? 4 : 1, JP = XQ ? 2 : 1, U = XQ ? 1 : 2;
+  if (pl.s_jper != JP) return hipErrorInvalidValue;
+  const size_t sm = std::max((size_t)GemmSmem<TT, CT, WC, WK>::BYTES, gp.n_shrink > 0 ? shrink_smem<TG, JP, U>() : (size_t)0);
+  return launch_k(k_layer<FMT, TT, CT, WC, WK, XQ, TG, JP, U>, grid, sm, stream, sp, gp);
 }
+
+#define LORA_LAYER_CASE(TT_, CT_, WC_, WK_, XQ_)                                    \
+  if (pl.TT == TT_ && pl.CT == CT_ && pl.WC == WC_ && pl.WK == WK_ && pl.XQ == XQ_) \
+    return launch_layer_t<FMT, TT_, CT_, WC_, WK_, XQ_>(pl, grid, stream, sp, gp);
 
 template <int FMT>
 static hipError_t launch_layer_f(const LayerPlan& pl, int grid, hipStream_t stream, const ShrinkParams& sp,
                                  const GemmParams& gp) {
-  const int tg = pl.shrink_tg;
-  if (pl.TT == 1 && pl.CT == 1 && !pl.XQ) return launch_layer_t<FMT, 1, 1, false>(tg, grid, stream, sp, gp);
-  if (pl.TT == 4 && pl.CT == 1 && !pl.XQ) return launch_layer_t<FMT, 4, 1, false>(tg, grid, stream, sp, gp);
-  if (pl.TT == 8 && pl.CT == 1 && !pl.XQ) return launch_layer_t<FMT, 8, 1, false>(tg, grid, stream, sp, gp);
-  if (pl.TT == 8 && pl.CT == 2 && !pl.XQ) return launch_layer_t<FMT, 8, 2, false>(tg, grid, stream, sp, gp);
-  if (pl.TT == 8 && pl.CT == 1 && pl.XQ) return launch_layer_t<FMT, 8, 1, true>(tg, grid, stream, sp, gp);
-  if (pl.TT == 8 && pl.CT == 2 && pl.XQ) return launch_layer_t<FMT, 8, 2, true>(tg, grid, stream, sp, gp);
-  if (pl.TT == 8 && pl.CT == 4 && pl.XQ) return launch_layer_t<FMT, 8, 4, true>(tg, grid, stream, sp, gp);
+  LORA_LAYER_CASE(1, 2, 1, 4, false)
+  LORA_LAYER_CASE(4, 1, 4, 1, false)
+  LORA_LAYER_CASE(8, 2, 2, 2, false)
+  LORA_LAYER_CASE(8, 1, 4, 1, true)
+  LORA_LAYER_CASE(8, 2, 4, 1, true)
   return hipErrorInvalidValue;
 }
+#undef LORA_LAYER_CASE
 
 hipError_t launch_layer(const LayerPlan& pl, hipStream_t stream, const ShrinkParams& sp, const GemmParams& gp) {
   const int grid = gp.n_shrink + pl.n_gemm_wg;
@@ -618,17 +999,10 @@ hipError_t launch_layer(const LayerPlan& pl, hipStream_t stream, const ShrinkPar
   return launch_layer_f<LORA_W_MXFP4_E2M1>(pl, grid, stream, sp, gp);
 }
 
-hipError_t launch_shrink(int tg, int grid, hipStream_t stream, const ShrinkParams& sp) {
-  const size_t sm = shrink_smem_bytes(tg);
-  if (tg == 1) {
-    hipLaunchKernelGGL((k_shrink<1, 4>), dim3(grid), dim3(256), sm, stream, sp);
-  } else {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_shrink<4, 1>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_shrink<4, 1>), dim3(grid), dim3(256), sm, stream, sp);
-  }
-  return hipGetLastError();
+hipError_t launch_shrink(const LayerPlan& pl, hipStream_t stream, const ShrinkParams& sp) {
+  if (pl.s_jper == 1) return launch_k(k_shrink<1, 1, 2>, pl.n_shrink_wg, shrink_smem<1, 1, 2>(), stream, sp);
+  if (pl.s_jper == 2) return launch_k(k_shrink<4, 2, 1>, pl.n_shrink_wg, shrink_smem<4, 2, 1>(), stream, sp);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_build_segments(const int* ids, int T, int n_ad, int* seg, int* sorted, int* err, hipStream_t s) {
@@ -645,6 +1019,14 @@ hipError_t launch_quant(const uint16_t* x, int T, int K, uint8_t* xq, uint8_t* x
 
 hipError_t launch_expand(const ExpandParams& p, hipStream_t s) {
   hipLaunchKernelGGL(k_expand, dim3((p.N + 255) / 256, p.T), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_weight(int fmt, const uint8_t* q, const uint8_t* sc, int N, int K, uint8_t* qp, uint8_t* scp,
+                              hipStream_t s) {
+  const long chunks = (fmt == LORA_W_FP8_E4M3) ? (long)N * K / 16 : (long)N * K / 32;
+  const int grid = (int)std::min<long>((chunks + 255) / 256, 16384);
+  hipLaunchKernelGGL(k_pack_weight, dim3(grid), dim3(256), 0, s, fmt, q, sc, N, K, qp, scp);
   return hipGetLastError();
 }
 

@@ -11,22 +11,32 @@
 
 namespace lora {
 
-constexpr int SEG_THREADS = 1024;
 constexpr int MAX_ADAPTERS = 8192;
 constexpr int MAX_RANK = 64;
+
+// Workspace control block (int32 words at the start of every workspace)
+enum : int {
+  CTRL_EPOCH = 0,    // number of fused launches completed on this workspace (tag = epoch + 1)
+  CTRL_STARTED = 1,  // workgroups of the current launch that have read the epoch
+  CTRL_STATUS = 2,   // non-zero: a bounded wait gave up
+};
 
 struct ShrinkParams {
   const uint16_t* x;
   int T, K;
   const int* seg_indptr;
   const int* sorted_tok;
+  const int* ids;          // fused launch with T <= 16: tokens found by id (may be null)
   const uint64_t* A_ptrs;  // A_a^T, bf16 [r_a][K]
   const int* ranks;
   int n_ad, r_max;
-  float* t;     // [T][r_max], original token order
-  float* part;  // [nchunks][T][r_max], rows in sorted order (split-K partial sums)
-  int* ad_ctr;  // [n_ad] arrival counters, zero between calls
-  int KC, nchunks;
+  float* t_out;        // plain fp32 [T][r_max] (may be null in the fused launch)
+  uint64_t* t_tag;     // tagged [kparts][T][r_max] (fused launch only, else null)
+  int tblk;            // tokens of one segment per workgroup item (multiple of 16)
+  int n_tblk;          // token blocks per adapter
+  int n_jg;            // rank groups per adapter (16 * jper ranks each)
+  int jper;            // 16-rank tiles per group (1..4)
+  int kparts, kpart_len;
 };
 
 struct GemmParams {
@@ -35,9 +45,12 @@ struct GemmParams {
   const uint8_t* xsc;  // and scales
   int T, K, N;
   const uint8_t* wq;
-  const float* ws_fp8;   // FP8 channel scales [N]
-  const uint8_t* ws_fp4; // MXFP4 block scales [N][K/32]
-  const float* t;        // [T][r_max]
+  const float* ws_fp8;    // FP8 channel scales [N]
+  const uint8_t* ws_fp4;  // MXFP4 block scales [N][K/32]
+  const float* t;         // plain t (unfused), or null
+  float* t_out;           // fused launch: the caller's t, written when t_kparts > 1 (may be null)
+  const uint64_t* t_tag;  // tagged t partials (fused), or null
+  int t_kparts;
   int r_max;
   const int* ids;
   const uint64_t* B_ptrs;  // B_a^T, bf16 [N][r_a]
@@ -46,13 +59,11 @@ struct GemmParams {
   int n_ad;
   uint16_t* y;
   int ksplit, krange, n_cb, n_tb;
-  float* gpart;   // K-split partial accumulators
-  int* tile_ctr;  // [tiles] arrival counters
-  int lora;       // add the adapter term
-  int n_shrink;   // down-projection workgroups in the same launch (0: none)
-  int* shrink_done;
-  int* wait_done;
-  int* status;
+  float* gpart;    // K-split partial accumulators
+  int* gflag;      // [tiles][ksplit] tags of finished K-split producers
+  int lora;        // add the adapter term
+  int n_shrink;    // down-projection workgroups at the front of the grid
+  int* ctrl;       // workspace control block
   int spin_limit;
 };
 
@@ -69,20 +80,23 @@ struct ExpandParams {
 // Tile plan for one (T, K, N, n_adapters, r_max, format); a pure function of these.
 struct LayerPlan {
   int fmt;
-  int TT, CT;       // token tiles of 16 per workgroup, column tiles of 16 per wave
-  bool XQ;          // x is quantised by a separate pass into the workspace
-  int KC;           // K-chunk staged in LDS
+  int TT, CT, WC, WK;  // token tiles per workgroup, column tiles per wave, wave grid (columns x k)
+  bool XQ;             // x is quantised by a separate pass into the workspace
+  int KC;              // K-chunk staged in LDS
   int ksplit, krange, n_cb, n_tb, n_gemm_wg;
-  int shrink_KC, shrink_nchunks, shrink_tg, n_shrink_wg;
+  // down-projection decomposition
+  int s_tblk, s_ntblk, s_njg, s_jper, s_kparts, s_kpart_len, n_shrink_wg;
   // workspace layout (byte offsets)
-  size_t off_ctrl, off_adctr, off_tilectr, off_spart, off_t, off_gpart, off_xq, off_xsc, total;
+  size_t off_ctrl, off_ttag, off_gflag, off_gpart, off_xq, off_xsc, total;
 };
 
 hipError_t launch_build_segments(const int* ids, int T, int n_ad, int* seg, int* sorted, int* err, hipStream_t s);
 hipError_t launch_quant(const uint16_t* x, int T, int K, uint8_t* xq, uint8_t* xsc, hipStream_t s);
-hipError_t launch_shrink(int tg, int grid, hipStream_t stream, const ShrinkParams& sp);
+hipError_t launch_shrink(const LayerPlan& pl, hipStream_t stream, const ShrinkParams& sp);
 hipError_t launch_expand(const ExpandParams& p, hipStream_t s);
 hipError_t launch_layer(const LayerPlan& pl, hipStream_t stream, const ShrinkParams& sp, const GemmParams& gp);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_pack_weight(int fmt, const uint8_t* q, const uint8_t* sc, int N, int K, uint8_t* qp, uint8_t* scp,
+                              hipStream_t s);
 
 }  // namespace lora

@@ -41,11 +41,14 @@ def _dev(t: torch.Tensor, name: str, dtype=None) -> torch.Tensor:
 @dataclass
 class LowpWeight:
     """Base weight on the device: fmt "fp8" (q uint8 [N,K], scale float32 [N]) or
-    "mxfp4" (q uint8 [N,K/2], scale uint8 [N,K/32])."""
+    "mxfp4" (q uint8 [N,K/2], scale uint8 [N,K/32]).  ``packed`` says whether q (and the
+    MXFP4 scales) are in the packed form the GEMM reads (see :func:`pack_weight`); the
+    tensors keep their [N, ...] shapes either way."""
 
     fmt: str
     q: torch.Tensor
     scale: torch.Tensor
+    packed: bool = False
 
     @property
     def N(self) -> int:
@@ -54,6 +57,23 @@ class LowpWeight:
     @property
     def K(self) -> int:
         return self.q.shape[1] * (1 if self.fmt == "fp8" else 2)
+
+
+def pack_weight(w: LowpWeight) -> LowpWeight:
+    """Reorder a row-major weight into the packed form (lora_pack_weight), once, offline."""
+    if w.packed:
+        return w
+    _dev(w.q, "q", torch.uint8)
+    qp = torch.empty_like(w.q)
+    if w.fmt == "mxfp4":
+        sp = torch.empty_like(w.scale)
+        sc_in, sc_out = _ptr(w.scale), _ptr(sp)
+    else:
+        sp = w.scale
+        sc_in = sc_out = _ptr(None)
+    check("lora_pack_weight", lib().lora_pack_weight(_FMT[w.fmt], _ptr(w.q), sc_in, w.N, w.K, _ptr(qp), sc_out,
+                                                     _stream()))
+    return LowpWeight(w.fmt, qp, sp, packed=True)
 
 
 @dataclass
@@ -125,8 +145,8 @@ def plan_info(T, K, N, n_adapters, r_max, fmt="fp8") -> dict:
     n = lib().lora_plan_info(T, K, N, n_adapters, r_max, _FMT[fmt], buf, 16)
     if n < 0:
         raise ValueError("sizes outside the library's limits")
-    keys = ["TT", "CT", "XQ", "KC", "ksplit", "krange", "n_cb", "n_tb", "n_gemm_wg",
-            "shrink_KC", "shrink_nchunks", "shrink_tg", "n_shrink_wg"]
+    keys = ["TT", "CT", "WC", "WK", "XQ", "KC", "ksplit", "krange", "n_cb", "n_tb", "n_gemm_wg",
+            "s_tblk", "s_njg", "s_kparts", "n_shrink_wg"]
     return dict(zip(keys, list(buf)[:n]))
 
 
@@ -180,6 +200,8 @@ def gemm_lowp_lora_epilogue(x: torch.Tensor, w: LowpWeight, seg: Segments | None
     launch (``t``, if given, receives it); otherwise ``t`` is an input and ``t=None``
     computes the base GEMM only."""
     _dev(x, "x", torch.bfloat16)
+    if not w.packed:
+        raise ValueError("the GEMM reads W in the packed form: call pack_weight(w) once first")
     T, K = x.shape
     N = w.N
     if y is None:

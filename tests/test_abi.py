@@ -42,9 +42,9 @@ def test_workspace_bytes(L):
 
 def test_plan_info(L):
     buf = (ctypes.c_int32 * 16)()
-    assert L.lora_plan_info(16, 4096, 6144, 1, 16, 0, buf, 16) == 13
-    assert buf[0] == 1 and buf[8] > 0
-    assert L.lora_plan_info(4096, 4096, 4096, 8, 64, 0, buf, 16) == 13 and buf[2] == 1
+    assert L.lora_plan_info(16, 4096, 6144, 1, 16, 0, buf, 16) == 15
+    assert buf[0] == 1 and buf[10] > 0
+    assert L.lora_plan_info(4096, 4096, 4096, 8, 64, 0, buf, 16) == 15 and buf[4] == 1
     assert L.lora_plan_info(16, 100, 6144, 1, 16, 0, buf, 16) == -1
 
 
@@ -88,10 +88,13 @@ def test_other_entry_points_validation(L):
     assert L.lora_quant_act_mxfp8(FAKE, 4, 48, FAKE, FAKE, NULL) == UNSUPPORTED
     assert L.lora_quant_act_mxfp8(NULL, 4, 64, FAKE, FAKE, NULL) == INVALID
     assert L.lora_quant_act_mxfp8(FAKE, 0, 64, FAKE, FAKE, NULL) == LORA_OK
-    assert L.lora_shrink(FAKE, 4, 256, FAKE, FAKE, FAKE, FAKE, 2, 8, FAKE, NULL, 0, NULL) == WORKSPACE
     assert L.lora_shrink(FAKE, 4, 250, FAKE, FAKE, FAKE, FAKE, 2, 8, FAKE, NULL, 0, NULL) == UNSUPPORTED
     assert L.lora_shrink(NULL, 4, 256, FAKE, FAKE, FAKE, FAKE, 2, 8, FAKE, NULL, 0, NULL) == INVALID
     assert L.lora_expand(FAKE, 4, 256, FAKE, FAKE, FAKE, FAKE, 2, 8, NULL, NULL) == INVALID
     assert L.lora_expand(FAKE, 4, 250, FAKE, FAKE, FAKE, FAKE, 2, 8, FAKE, NULL) == UNSUPPORTED
     assert L.lora_workspace_init(NULL, 16, NULL) == INVALID
+    assert L.lora_pack_weight(0, FAKE, NULL, 100, 256, FAKE, NULL, NULL) == UNSUPPORTED
+    assert L.lora_pack_weight(1, FAKE, NULL, 128, 256, FAKE, NULL, NULL) == INVALID   # MXFP4 needs scales
+    assert L.lora_pack_weight(0, FAKE, NULL, 128, 256, FAKE, NULL, NULL) == INVALID   # in place
+    assert L.lora_pack_weight(3, FAKE, NULL, 128, 256, MISALIGNED, NULL, NULL) == INVALID
     assert L.lora_workspace_status(NULL, FAKE, NULL) == INVALID

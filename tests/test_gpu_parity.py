@@ -180,3 +180,36 @@ def test_expand_standalone_matches_oracle():
     torch.cuda.synchronize()
     from gpu_util import bf16_to_f64
     assert_y_close(bf16_to_f64(y), ref["y"], "unfused expand")
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+def test_pack_weight_layout(fmt):
+    """The packed W layout, checked byte for byte against its definition in lora_lowp.h."""
+    import torch
+    import precision_gemm_amd as P
+    rng = np.random.default_rng(6)
+    N, K = 128, 512
+    kb = K if fmt == "fp8" else K // 2
+    q = rng.integers(0, 256, (N, kb), dtype=np.uint8)
+    sc = rng.integers(0, 256, (N, K // 32), dtype=np.uint8) if fmt == "mxfp4" else rng.random(N).astype(np.float32)
+    w = P.pack_weight(P.LowpWeight(fmt, torch.from_numpy(q).cuda(), torch.from_numpy(sc).cuda()))
+    got = w.q.cpu().numpy().reshape(-1)
+    lanes = np.arange(64)
+    j, g = lanes % 16, lanes // 16
+    ref = []
+    for nt in range(N // 16):
+        for ks in range(K // 128):
+            if fmt == "fp8":
+                for h in range(2):
+                    for l in range(64):
+                        k0 = ks * 128 + h * 64 + g[l] * 16
+                        ref.append(q[nt * 16 + j[l], k0:k0 + 16])
+            else:
+                for l in range(64):
+                    b0 = ks * 64 + g[l] * 16
+                    ref.append(q[nt * 16 + j[l], b0:b0 + 16])
+    assert np.array_equal(got, np.concatenate(ref))
+    if fmt == "mxfp4":
+        sref = np.array([sc[nt * 16 + j[l], ks * 4 + g[l]] for nt in range(N // 16) for ks in range(K // 128)
+                         for l in range(64)], np.uint8)
+        assert np.array_equal(w.scale.cpu().numpy().reshape(-1), sref)

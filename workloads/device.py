@@ -1,7 +1,8 @@
 """Upload a generated workload to the device in the library's storage layouts.
 
 Layout only (no arithmetic): A_a^T [r_a, K] and B_a^T [N, r_a] are transposed copies of
-the drawn A_a [K, r_a] and B_a [r_a, N]; x is the bf16 tensor of the drawn bits.
+the drawn A_a [K, r_a] and B_a [r_a, N]; x is the bf16 tensor of the drawn bits; W is
+reordered into the packed form by the library's lora_pack_weight.
 """
 
 from __future__ import annotations
@@ -9,7 +10,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from precision_gemm_amd.ops import Adapters, LowpWeight
+from precision_gemm_amd.ops import Adapters, LowpWeight, pack_weight
 
 
 def bf16_tensor(bits: np.ndarray, device="cuda") -> torch.Tensor:
@@ -21,7 +22,7 @@ def upload(wl, device="cuda"):
     x = bf16_tensor(wl.x, device)
     q = torch.from_numpy(np.ascontiguousarray(wl.w_q)).to(device)
     s = torch.from_numpy(np.ascontiguousarray(wl.w_scale)).to(device)
-    w = LowpWeight(wl.fmt, q, s)
+    w = pack_weight(LowpWeight(wl.fmt, q, s))  # offline re-layout for the GEMM
     At = [bf16_tensor(np.ascontiguousarray(a.T), device) for a in wl.A]
     Bt = [bf16_tensor(np.ascontiguousarray(b.T), device) for b in wl.B]
     ad = Adapters(At, Bt, torch.from_numpy(np.asarray(wl.scale, np.float32)).to(device))
