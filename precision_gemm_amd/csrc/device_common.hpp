@@ -57,6 +57,37 @@ __device__ __forceinline__ uint32_t cvt4_fp8(float a, float b, float c, float d)
 
 __device__ __forceinline__ float clamp448(float v) { return __builtin_fminf(__builtin_fmaxf(v, -448.f), 448.f); }
 
+// Largest |x| of 8 bf16 (one 16-byte piece of a block), as 15-bit magnitude bits.
+__device__ __forceinline__ uint32_t absmax8_bits(const uint4& in) {
+  const us2 mask = {0x7fff, 0x7fff};
+  us2 m = __builtin_bit_cast(us2, in.x) & mask;
+  m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, in.y) & mask);
+  m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, in.z) & mask);
+  m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, in.w) & mask);
+  return m.x > m.y ? m.x : m.y;
+}
+
+// Scale code of a block from its largest magnitude bits (the rule above).
+__device__ __forceinline__ uint32_t mx_code_from_bits(uint32_t mx) {
+  const uint32_t ef = mx >> 7;
+  return ef > 8u ? ef - 8u : 0u;
+}
+
+// Quantise one 16-byte piece (8 bf16) of a block with the block's scale code into 8
+// e4m3 codes.
+__device__ __forceinline__ uint2 mx_piece_quant(const uint4& in, uint32_t code) {
+  const float inv = __uint_as_float((254u - code) << 23);  // 2^(127 - code) = 2^-E, exact
+  const uint32_t w[4] = {in.x, in.y, in.z, in.w};
+  uint32_t r[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float a = clamp448(bf16_lo(w[2 * h]) * inv), b = clamp448(bf16_hi(w[2 * h]) * inv);
+    float c = clamp448(bf16_lo(w[2 * h + 1]) * inv), d = clamp448(bf16_hi(w[2 * h + 1]) * inv);
+    r[h] = cvt4_fp8(a, b, c, d);
+  }
+  return make_uint2(r[0], r[1]);
+}
+
 // Quantise 32 bf16 (64 bytes in `in`) with scale code `code` into 32 e4m3 codes (out[2]).
 __device__ __forceinline__ void mx_block_quant(const uint4 (&in)[4], uint32_t code, uint4 (&out)[2]) {
   const float inv = __uint_as_float((254u - code) << 23);  // 2^(127 - code) = 2^-E, exact

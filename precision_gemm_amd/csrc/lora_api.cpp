@@ -41,14 +41,16 @@ LayerPlan make_plan(int T, int K, int N, int n_ad, int r_max, int fmt, bool fuse
   if (T <= 16) {
     pl.TT = 1; pl.CT = 2; pl.WC = 1; pl.WK = 4; pl.XQ = false;
   } else if (T <= 64) {
-    pl.TT = 4; pl.CT = 1; pl.WC = 4; pl.WK = 1; pl.XQ = false;
+    // 128 channels per workgroup: with the down-projection's workgroups the grid stays
+    // within one workgroup per CU for the widest decode layers
+    pl.TT = 4; pl.CT = (N % 128 == 0) ? 2 : 1; pl.WC = 4; pl.WK = 1; pl.XQ = false;
   } else if (T <= 128) {
     pl.TT = 8; pl.CT = 2; pl.WC = 2; pl.WK = 2; pl.XQ = false;
   } else {
     pl.TT = 8; pl.WC = 4; pl.WK = 1; pl.XQ = true;
     pl.CT = (N % 128 == 0) ? 2 : 1;
   }
-  pl.KC = (pl.TT == 1) ? 2048 : ((pl.TT <= 4) ? 512 : 256);
+  pl.KC = (pl.TT == 1) ? 2048 : ((pl.TT <= 4 && pl.CT == 1) ? 512 : 256);
   const int WN = pl.WC * pl.CT * 16;
   pl.n_cb = N / WN;
   pl.n_tb = ceil_div(T, 16 * pl.TT);
@@ -75,7 +77,8 @@ LayerPlan make_plan(int T, int K, int N, int n_ad, int r_max, int fmt, bool fuse
     pl.s_njg = ceil_div(r_max, 32);
   }
   int kparts = 1;
-  if (fused && T <= 64) kparts = std::min(4, std::max(1, K / 1024));  // latency-bound decode: split K
+  // latency-bound single-tile decode: split K so that t is ready early
+  if (fused && T <= 16) kparts = std::min(4, std::max(1, K / 1024));
   pl.s_kpart_len = ceil_div(ceil_div(K, kparts), 256) * 256;
   pl.s_kparts = ceil_div(K, pl.s_kpart_len);
   pl.n_shrink_wg = n_ad * pl.s_ntblk * pl.s_njg * pl.s_kparts;
@@ -87,7 +90,7 @@ LayerPlan make_plan(int T, int K, int N, int n_ad, int r_max, int fmt, bool fuse
   pl.off_gpart = off;
   if (pl.ksplit > 1) off += round256((size_t)tiles * pl.ksplit * pl.WC * pl.TT * pl.CT * 256 * 4);
   pl.off_xq = off;    if (pl.XQ) off += round256((size_t)T * K);
-  pl.off_xsc = off;   if (pl.XQ) off += round256((size_t)T * (K / 32));
+  pl.off_xsc = off;   if (pl.XQ) off += round256((size_t)T * (K / 32) + 8);  // + 8: padding read by a partial last chunk
   pl.total = off;
   return pl;
 }

@@ -102,23 +102,25 @@ __global__ __launch_bounds__(SEG_THREADS) void k_build_segments(const int* __res
 // ======================================================================================
 // MXFP8 activation quantisation (standalone; the GEMM loader uses the same functions)
 // ======================================================================================
+// One thread per 16-byte piece (8 elements): each wave reads 1 KB of x per load, and
+// the four lanes holding a 32-block combine their maxima with two lane swaps.
+__device__ __forceinline__ uint32_t quad_swap1(uint32_t v) {  // value of lane ^ 1 (DPP quad_perm 1,0,3,2)
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t quad_swap2(uint32_t v) {  // value of lane ^ 2 (DPP quad_perm 2,3,0,1)
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
+}
 __global__ __launch_bounds__(256) void k_quant_mxfp8(const uint16_t* __restrict__ x, int T, int K,
                                                      uint8_t* __restrict__ xq, uint8_t* __restrict__ xsc) {
-  const int nb = K / 32;
-  const long total = (long)T * nb;
-  for (long b = (long)blockIdx.x * blockDim.x + threadIdx.x; b < total; b += (long)gridDim.x * blockDim.x) {
-    const long row = b / nb, kb = b % nb;
-    const uint16_t* src = x + row * K + kb * 32;
-    uint4 in[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) in[i] = ldg16(src + 8 * i);
-    const uint32_t code = mx_block_code(in);
-    uint4 out[2];
-    mx_block_quant(in, code, out);
-    uint8_t* dst = xq + row * K + kb * 32;
-    *reinterpret_cast<uint4*>(dst) = out[0];
-    *reinterpret_cast<uint4*>(dst + 16) = out[1];
-    xsc[b] = (uint8_t)code;
+  const long total = (long)T * (K / 8);  // a multiple of 4: whole blocks, so quads stay together
+  for (long P = (long)blockIdx.x * blockDim.x + threadIdx.x; P < total; P += (long)gridDim.x * blockDim.x) {
+    const uint4 in = ldg16(x + P * 8);
+    uint32_t mx = absmax8_bits(in);
+    mx = max(mx, quad_swap1(mx));
+    mx = max(mx, quad_swap2(mx));
+    const uint32_t code = mx_code_from_bits(mx);
+    *reinterpret_cast<uint2*>(xq + P * 8) = mx_piece_quant(in, code);
+    if ((P & 3) == 0) xsc[P >> 2] = (uint8_t)code;
   }
 }
 
@@ -425,54 +427,59 @@ __global__ __launch_bounds__(256) void k_expand(ExpandParams p) {
 // and for each token tile and each adapter present in it one bf16 MFMA per 32 ranks adds
 // (s_a t[tok]) @ B_a to the rows of that adapter's tokens; finally bf16 stores (RNE).
 // ======================================================================================
-template <int TT>
+template <int TT, int CT>
 struct ChunkK {
-  static constexpr int KC = (TT == 1) ? 2048 : ((TT <= 4) ? 512 : 256);
+  // K-chunk: two chunks of x and W are held in registers, so the chunk shrinks as the
+  // workgroup tile grows (the host plan uses the same rule)
+  static constexpr int KC = (TT == 1) ? 2048 : ((TT <= 4 && CT == 1) ? 512 : 256);
   static constexpr int STEPS = KC / 128;
-  static constexpr int ROW = KC + 16;                     // LDS row stride in bytes
-  static constexpr int NBLK = TT * 16 * (KC / 32) / 256;  // 32-blocks of x per thread per chunk
+  static constexpr int ROW = KC + 16;  // LDS row stride in bytes
 };
 
-constexpr int EPI_LIST_MAX = 128;
-constexpr int EPI_BBUF = 32768;                   // bytes of B staged per batch
-constexpr int EPI_BCHUNKS = EPI_BBUF / 16 / 256;  // 16-byte chunks per thread per batch
-constexpr int EPI_TE = 8;                         // t elements per thread per gather batch
+constexpr int EPI_TE = 8;       // t elements per thread per gather batch
 constexpr int MAX_KPARTS = 4;
+// B-operand loads of the up-projection: a ring of RING items, all but one in flight
+// (shorter for the widest tiles, whose accumulators leave fewer registers)
+template <int TT, int CT>
+constexpr int epi_ring() { return TT >= 8 ? 4 : 8; }
+constexpr int TSTR = MAX_RANK + 8;  // bf16 row stride of the staged t (the pad spreads the rows over LDS banks)
 
-template <int TT>
+template <int TT, int CT, int WC, int WK>
 struct EpiLayout {
   static constexpr int ROWS = TT * 16;
   // byte offsets inside the epilogue's LDS area
-  static constexpr int ROWAD = 0;                          // int [ROWS]: adapter of the row (-1: none)
-  static constexpr int ROWRK = ROWAD + ROWS * 4;           // int [ROWS]: its rank
-  static constexpr int ROWSC = ROWRK + ROWS * 4;           // float [ROWS]: its scale
-  static constexpr int LIST = ROWSC + ROWS * 4;            // int4 [EPI_LIST_MAX]: a, r, offset, first chunk
-  static constexpr int META = LIST + EPI_LIST_MAX * 16;    // int [16]
-  static constexpr int TB = META + 64;                     // bf16 [ROWS][MAX_RANK]
-  static constexpr int BS = TB + ROWS * MAX_RANK * 2;      // bf16 B staging
-  static constexpr int BYTES = BS + EPI_BBUF;
+  static constexpr int ROWAD = 0;                    // int [ROWS]: adapter of the row (-1: none)
+  static constexpr int ROWRK = ROWAD + ROWS * 4;     // int [ROWS]: its rank
+  static constexpr int ROWSC = ROWRK + ROWS * 4;     // float [ROWS]: its scale
+  static constexpr int ROWBP = ROWSC + ROWS * 4;     // uint64 [ROWS]: address of its B^T
+  static constexpr int ITEMS = ROWBP + ROWS * 8;     // int [2 * ROWS]: up-projection work items
+  static constexpr int LEAD = ITEMS + ROWS * 8;      // int [ROWS]: token tiles of the row's adapter (leader rows)
+  static constexpr int META = LEAD + ROWS * 4;       // int [16]
+  static constexpr int TB = META + 64;               // bf16 [ROWS][TSTR]: s_a * t
+  static constexpr int LRED = TB + ROWS * TSTR * 2;  // float [WK-1][WC][TT][CT][256]: k-wave sums
+  static constexpr int BYTES = LRED + (WK - 1) * WC * TT * CT * 256 * 4;
+  static_assert(ROWBP % 8 == 0 && TB % 16 == 0 && LRED % 16 == 0, "epilogue LDS alignment");
 };
 
 template <int TT, int CT, int WC, int WK>
 struct GemmSmem {
-  using CK = ChunkK<TT>;
+  using CK = ChunkK<TT, CT>;
   static constexpr int MAIN = TT * 16 * CK::ROW + TT * 16 * (CK::KC / 32);
   static constexpr int RED = (WK - 1) * WC * TT * CT * 256 * 4;
-  static constexpr int EPI = EpiLayout<TT>::BYTES;
+  static constexpr int EPI = EpiLayout<TT, CT, WC, WK>::BYTES;
   static constexpr int M1 = MAIN > RED ? MAIN : RED;
   static constexpr int BYTES = M1 > EPI ? M1 : EPI;
 };
 
 template <int FMT, int TT, int CT, int WC, int WK, bool XQ>
 __device__ void gemm_item(const GemmParams& p, int item, char* smem, int e, int* lds_epoch, int* started) {
-  using CK = ChunkK<TT>;
-  constexpr int KC = CK::KC, STEPS = CK::STEPS, ROW = CK::ROW, NBLK = CK::NBLK;
+  using CK = ChunkK<TT, CT>;
+  constexpr int KC = CK::KC, STEPS = CK::STEPS, ROW = CK::ROW;
   constexpr int SPW = STEPS / WK;  // k-steps per wave per chunk
   constexpr int WN = WC * CT * 16;
   constexpr int FMTB = (FMT == LORA_W_FP8_E4M3) ? 0 : 4;
   constexpr int ROWS = TT * 16;
   static_assert(STEPS % WK == 0, "k-steps per chunk must split evenly over the k-waves");
-  static_assert(NBLK >= 1, "chunk too small for the workgroup");
   uint8_t* xs = reinterpret_cast<uint8_t*>(smem);  // [ROWS][ROW]
   uint8_t* ss = xs + ROWS * ROW;                    // [ROWS][KC/32]
 
@@ -506,21 +513,10 @@ __device__ void gemm_item(const GemmParams& p, int item, char* smem, int e, int*
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) acc[tt][ct] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // adapter, rank and scale of row `tid` of the token block, fetched now (before the bulk
-  // loads, which retire after them) and used in the epilogue
-  int row_a = -1, row_r = 0;
-  float row_s = 0.f;
-  if (p.lora && ks == p.ksplit - 1 && tid < ROWS) {
-    const int tok = row0 + tid;
-    const int a = p.ids[min(tok, p.T - 1)];
-    if (tok < p.T && a >= 0 && a < p.n_ad) {
-      row_a = a;
-      row_r = p.ranks[a];
-      row_s = p.scales[a];
-      if (row_r < 8 || row_r > p.r_max || (row_r & 7)) row_a = -1;  // unsupported rank: skipped
-    }
-    if (row_a < 0) row_r = 0;
-  }
+  // adapter of row `tid` of the token block for the epilogue: the id is loaded before the
+  // bulk loads, its rank, scale and B address right after the first ones (loads retire
+  // in order, so none of these waits for more than the id)
+  const int id_raw = p.lora ? p.ids[min(row0 + min(tid, ROWS - 1), p.T - 1)] : -1;
 
   const int kb = ks * p.krange, ke = min(K, kb + p.krange);
   const int nchunks = (ke - kb + KC - 1) / KC;
@@ -530,32 +526,58 @@ __device__ void gemm_item(const GemmParams& p, int item, char* smem, int e, int*
   const int srot = (tile * 5) & (STEPS - 1);
   auto chunk_k0 = [&](int c) { return kb + ((c + crot) % nchunks) * KC; };
 
-  // register staging, two chunks ahead: x (raw bf16 or pre-quantised) and W
-  uint4 xr[2][NBLK][4];
-  uint32_t xcode[2][NBLK];
+  // register staging, two chunks ahead: x (raw bf16 or pre-quantised) and W.
+  // Pre-quantised x is read in 16-byte pieces, piece P = tid + 256 m of the chunk's rows,
+  // so that each wave's load covers 1 KB of a row.  Raw bf16 x is read a 32-block per
+  // thread (four 16-byte loads), so that the thread quantises the whole block itself: a
+  // piece layout would need a cross-lane maximum per block, which measured slower.
+  constexpr int PPR = KC / 16;               // MXFP8 pieces per row and chunk
+  constexpr int NP = ROWS * PPR / 256;       // MXFP8 pieces per thread and chunk
+  constexpr int NBLK = ROWS * (KC / 32) / 256;  // bf16 32-blocks per thread and chunk
+  constexpr int NX = XQ ? NP : 4 * NBLK;     // 16-byte registers per chunk
+  static_assert(NP >= 1 && NBLK >= 1 && NBLK * 256 == ROWS * (KC / 32), "chunk does not split evenly");
+  uint4 xr[2][NX];
+  // pre-quantised x: the chunk's scale codes, ROWS x 8 bytes, are one 1 KB load of wave 0
+  // (lane l: rows 2l and 2l+1)
+  static_assert(!XQ || (KC == 256 && ROWS == 128), "scale staging assumes 8 codes per row and 128 rows");
+  uint2 xsc2[2][2];
   uint4 wlo[2][SPW][CT], whi[2][SPW][CT];
   int wsc[2][SPW][CT];
 
   auto load_x = [&](int buf, int c) {
     const int kc0 = chunk_k0(c);
-    const int bpr = min(KC, ke - kc0) >> 5;
-    // unconditional loads from clamped addresses (see the down-projection): rows past T
-    // repeat row T-1 and only feed rows that are never stored; blocks past the chunk end
-    // are never read back from LDS
+    // unconditional loads from clamped addresses: rows past T repeat row T-1 and only
+    // feed rows that are never stored; pieces and blocks past the chunk end are never
+    // read back from LDS
+    if (XQ) {
+      const int ppr = min(KC, ke - kc0) / 16;
 #pragma unroll
-    for (int m = 0; m < NBLK; ++m) {
-      const int b = tid + 256 * m;
-      const int row = b / (KC / 32), k32 = min(b % (KC / 32), bpr - 1);
-      const long tok = min(row0 + row, p.T - 1);
-      if (XQ) {
-        const uint8_t* src = p.xq + tok * K + kc0 + k32 * 32;
-        xr[buf][m][0] = ldg16(src);
-        xr[buf][m][1] = ldg16(src + 16);
-        xcode[buf][m] = p.xsc[tok * (K / 32) + (kc0 >> 5) + k32];
-      } else {
+      for (int m = 0; m < NP; ++m) {
+        const int P = tid + 256 * m;
+        const int row = P / PPR, pp = min(P % PPR, ppr - 1);
+        const long tok = min(row0 + row, p.T - 1);
+        xr[buf][m] = ldg16(p.xq + tok * K + kc0 + pp * 16);
+      }
+    } else {
+      const int bpr = min(KC, ke - kc0) >> 5;
+#pragma unroll
+      for (int m = 0; m < NBLK; ++m) {
+        const int b = tid + 256 * m;
+        const int row = b / (KC / 32), k32 = min(b % (KC / 32), bpr - 1);
+        const long tok = min(row0 + row, p.T - 1);
         const uint16_t* src = p.x + tok * K + kc0 + k32 * 32;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) xr[buf][m][q] = ldg16(src + 8 * q);
+        for (int q = 0; q < 4; ++q) xr[buf][4 * m + q] = ldg16(src + 8 * q);
+      }
+    }
+    if (XQ && wave == 0) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        // two 4-byte loads (rows are 4-byte aligned); in a partial last chunk the second
+        // may read codes past the row, which are never used (the workspace pads the array)
+        const long tok = min(row0 + 2 * lane + h, p.T - 1);
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(p.xsc + tok * (K / 32) + (kc0 >> 5));
+        xsc2[buf][h] = make_uint2(src[0], src[1]);
       }
     }
   };
@@ -584,24 +606,29 @@ __device__ void gemm_item(const GemmParams& p, int item, char* smem, int e, int*
     }
   };
   auto stage_x = [&](int buf) {
+    if (XQ) {
 #pragma unroll
-    for (int m = 0; m < NBLK; ++m) {
-      const int b = tid + 256 * m;
-      const int row = b / (KC / 32), k32 = b % (KC / 32);
-      uint4 out[2];
-      uint32_t code;
-      if (XQ) {
-        out[0] = xr[buf][m][0];
-        out[1] = xr[buf][m][1];
-        code = xcode[buf][m];
-      } else {
-        code = mx_block_code(xr[buf][m]);
-        mx_block_quant(xr[buf][m], code, out);
+      for (int m = 0; m < NP; ++m) {
+        const int P = tid + 256 * m;
+        const int row = P / PPR, pp = P % PPR;
+        *reinterpret_cast<uint4*>(xs + row * ROW + pp * 16) = xr[buf][m];
       }
-      *reinterpret_cast<uint4*>(xs + row * ROW + k32 * 32) = out[0];
-      *reinterpret_cast<uint4*>(xs + row * ROW + k32 * 32 + 16) = out[1];
-      ss[row * (KC / 32) + k32] = (uint8_t)code;
+    } else {
+#pragma unroll
+      for (int m = 0; m < NBLK; ++m) {
+        const int b = tid + 256 * m;
+        const int row = b / (KC / 32), k32 = b % (KC / 32);
+        const uint4 in[4] = {xr[buf][4 * m], xr[buf][4 * m + 1], xr[buf][4 * m + 2], xr[buf][4 * m + 3]};
+        const uint32_t code = mx_block_code(in);
+        uint4 out[2];
+        mx_block_quant(in, code, out);
+        *reinterpret_cast<uint4*>(xs + row * ROW + k32 * 32) = out[0];
+        *reinterpret_cast<uint4*>(xs + row * ROW + k32 * 32 + 16) = out[1];
+        ss[row * (KC / 32) + k32] = (uint8_t)code;
+      }
     }
+    if (XQ && wave == 0)
+      *reinterpret_cast<uint4*>(ss + lane * 16) = make_uint4(xsc2[buf][0].x, xsc2[buf][0].y, xsc2[buf][1].x, xsc2[buf][1].y);
   };
   auto mma_chunk = [&](int buf, int c) {
     const int kc0 = chunk_k0(c);
@@ -633,6 +660,17 @@ __device__ void gemm_item(const GemmParams& p, int item, char* smem, int e, int*
   if (nchunks > 1) {
     load_x(1, 1);
     load_w(1, 1);
+  }
+  const bool row_ok = p.lora && ks == p.ksplit - 1 && tid < ROWS && row0 + tid < p.T && id_raw >= 0 &&
+                      id_raw < p.n_ad;
+  int row_r = 0;
+  float row_s = 0.f;
+  uint64_t row_bp = 0;
+  if (p.lora) {  // unconditional loads from a valid index
+    const int ac = row_ok ? id_raw : 0;
+    row_r = p.ranks[ac];
+    row_s = p.scales[ac];
+    row_bp = p.B_ptrs[ac];
   }
   for (int c = 0; c < nchunks; c += 2) {
     stage_x(0);
@@ -743,107 +781,119 @@ __device__ void gemm_item(const GemmParams& p, int item, char* smem, int e, int*
 
   // ---- epilogue: adapter up-projection
   if (p.lora) {
-    using EL = EpiLayout<TT>;
+    using EL = EpiLayout<TT, CT, WC, WK>;
     int* rowad = reinterpret_cast<int*>(smem + EL::ROWAD);
     int* rowrk = reinterpret_cast<int*>(smem + EL::ROWRK);
     float* rowsc = reinterpret_cast<float*>(smem + EL::ROWSC);
-    int4* list = reinterpret_cast<int4*>(smem + EL::LIST);
+    uint64_t* rowbp = reinterpret_cast<uint64_t*>(smem + EL::ROWBP);
+    int* items = reinterpret_cast<int*>(smem + EL::ITEMS);
     int* meta = reinterpret_cast<int*>(smem + EL::META);
     uint16_t* tbuf = reinterpret_cast<uint16_t*>(smem + EL::TB);
-    uint16_t* bsb = reinterpret_cast<uint16_t*>(smem + EL::BS);
-    // (1) adapter, rank and scale of every row (fetched at the start)
+    float* lred = reinterpret_cast<float*>(smem + EL::LRED);
+    // (1) adapter, rank, scale and B address of every row; a rank outside the limits
+    //     drops the row's adapter term
     if (tid < ROWS) {
-      rowad[tid] = row_a;
-      rowrk[tid] = row_r;
+      const bool ok = row_ok && row_r >= 8 && row_r <= p.r_max && (row_r & 7) == 0;
+      rowad[tid] = ok ? id_raw : -1;
+      rowrk[tid] = ok ? row_r : 0;
       rowsc[tid] = row_s;
+      rowbp[tid] = row_bp;
     }
     __syncthreads();
-    // (2) distinct adapters in order of first appearance, and the first batch of them
-    //     whose B_a^T slices fit the staging buffer (one wave)
-    auto plan_batch = [&](int e_begin, int nl) {  // lane 0 of wave 0
-      int bytes = 0, e2 = e_begin, chunks = 0;
-      while (e2 < nl && bytes + WN * list[e2].y * 2 <= EPI_BBUF) {
-        list[e2].z = bytes / 2;  // element offset in the staging buffer
-        list[e2].w = chunks;     // first 16-byte chunk of this adapter
-        bytes += WN * list[e2].y * 2;
-        chunks += WN * list[e2].y / 8;
-        ++e2;
+    // (2) work items: one per adapter present in the token block and 32 of its ranks, in
+    //     order of the adapter's first row (its leader), with the set of 16-row token tiles
+    //     that hold its rows; each item's B operands then serve all those tiles
+    int* lead = reinterpret_cast<int*>(smem + EL::LEAD);
+    int my_lead = -1;
+    if (tid < ROWS) {
+      lead[tid] = 0;
+      const int a = rowad[tid];
+      if (a >= 0) {
+        my_lead = tid;
+        for (int l = 0; l < tid; ++l)
+          if (rowad[l] == a) {
+            my_lead = l;
+            break;
+          }
       }
-      meta[1] = e2;
-      meta[2] = chunks;
-    };
+    }
+    __syncthreads();
+    if (my_lead >= 0) atomicOr(lead + my_lead, 1 << (tid >> 4));
+    __syncthreads();
     if (wave == 0) {
-      int nl = 0;
+      int n = 0;
       for (int c0 = 0; c0 < ROWS; c0 += 64) {
-        const int a = (c0 + lane < ROWS) ? rowad[c0 + lane] : -1;
-        bool fresh = a >= 0;
-        for (int e2 = 0; e2 < nl; ++e2) fresh = fresh && (list[e2].x != a);
-        unsigned long long pending = __ballot(fresh);
-        while (pending) {
-          const int leader = __ffsll((long long)pending) - 1;
-          const int la = __shfl(a, leader);
-          if (lane == 0) list[nl] = make_int4(la, p.ranks[la], 0, 0);
-          ++nl;
-          pending &= ~__ballot(fresh && a == la);
+        const int row = c0 + lane;
+        const int mask = (row < ROWS) ? lead[row] : 0;  // non-zero only for leader rows
+        const int nb = mask ? ((rowrk[row] + 31) >> 5) : 0;
+        int incl = nb;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const int v = __shfl_up(incl, d);
+          if (lane >= d) incl += v;
         }
+        for (int b = 0; b < nb; ++b) items[n + incl - nb + b] = row | (b << 8) | (mask << 16);
+        n += __shfl(incl, 63);
       }
-      if (lane == 0) {
-        meta[0] = nl;
-        plan_batch(0, nl);
-      }
+      if (lane == 0) meta[0] = n;
     }
     __syncthreads();
-    const int nl = __builtin_amdgcn_readfirstlane(meta[0]);
-    // B chunks of a batch: loaded into registers, then stored to LDS
-    uint4 breg[EPI_BCHUNKS];
-    int bdst[EPI_BCHUNKS];
-    auto load_batch = [&](int e_begin, int e_end, int nch) {
+    const int n_items = __builtin_amdgcn_readfirstlane(meta[0]);
+    // items of this wave: wk, wk + WK, ... (the waves sharing columns split the items)
+    const int cnt = (n_items > wk) ? (n_items - wk + WK - 1) / WK : 0;
+
+    // B operands straight from HBM into a ring of registers: lane (li, g) of column tile
+    // ct needs B_a^T[n][j .. j+7] with n its column and j = 32*block + 8g, 16 contiguous
+    // bytes.  Addresses are clamped into the row (j <= r - 8); lanes with j >= r get
+    // zero operands below.  Items past the end reload the last one.
+    constexpr int RING = epi_ring<TT, CT>();
+    uint4 bq[RING][CT];
+    auto issue = [&](int slot_dummy, int m, uint4 (&dst)[CT]) {
+      (void)slot_dummy;
+      const int it = items[min(wk + WK * m, n_items - 1)];
+      const int row = it & 255, jb = (it >> 8) & 255;
+      const int r = __builtin_amdgcn_readfirstlane(rowrk[row]);
+      const uint64_t bp = rowbp[row];
+      const uint64_t bpu = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(bp >> 32)) << 32) |
+                           (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bp);
+      const uint16_t* Bt = reinterpret_cast<const uint16_t*>(bpu);
+      const int j = min(jb * 32 + 8 * g, r - 8);
 #pragma unroll
-      for (int m = 0; m < EPI_BCHUNKS; ++m) {
-        const int c = min(tid + 256 * m, nch - 1);  // nch >= 1: a batch holds an adapter
-        int e2 = e_begin;
-        while (e2 + 1 < e_end && list[e2 + 1].w <= c) ++e2;
-        const int4 ent = list[e2];
-        const int cc = c - ent.w, per = ent.y / 8;
-        const int n = cc / per, jj = cc - n * per;
-        const uint16_t* Bt = reinterpret_cast<const uint16_t*>(p.B_ptrs[ent.x]);
-        breg[m] = ldg16(Bt + (long)(n_tile0 + n) * ent.y + jj * 8);
-        bdst[m] = (tid + 256 * m < nch) ? ent.z + n * ent.y + jj * 8 : -1;
-      }
+      for (int ct = 0; ct < CT; ++ct) dst[ct] = ldg16(Bt + (long)(nw0 + ct * 16 + li) * r + j);
     };
-    auto mma_batch = [&](int e_begin, int e_end) {
-      if (wk != 0) return;
+    v4f lacc[TT][CT];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) lacc[tt][ct] = v4f{0.f, 0.f, 0.f, 0.f};
+    auto consume = [&](int m, const uint4 (&src)[CT]) {
+      const int it = __builtin_amdgcn_readfirstlane(items[wk + WK * m]);
+      const int row = it & 255, jb = (it >> 8) & 255, mask = it >> 16;
+      const int a = __builtin_amdgcn_readfirstlane(rowad[row]);
+      const int r = __builtin_amdgcn_readfirstlane(rowrk[row]);
+      const int j = jb * 32 + 8 * g;  // <= 56
+      const bool valid = j < r;
+      uint4 bop[CT];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) bop[ct] = valid ? src[ct] : zero4();
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) {
-        const int rad = rowad[tt * 16 + li];
-        for (int e2 = e_begin; e2 < e_end; ++e2) {
-          int4 ent = list[e2];  // same for every lane: made scalar so the loops below branch
-          ent.x = __builtin_amdgcn_readfirstlane(ent.x);
-          ent.y = __builtin_amdgcn_readfirstlane(ent.y);
-          ent.z = __builtin_amdgcn_readfirstlane(ent.z);
-          if (!__ballot(rad == ent.x)) continue;  // adapter absent from this token tile
-          const bool mine = (rad == ent.x);
-          for (int j0 = 0; j0 < ent.y; j0 += 32) {
-            const int j = j0 + 8 * g;
-            const uint4 aop =
-                (mine && j < ent.y) ? *reinterpret_cast<const uint4*>(tbuf + (tt * 16 + li) * MAX_RANK + j) : zero4();
+        if (!((mask >> tt) & 1)) continue;  // uniform: adapter absent from this token tile
+        const int myrow = tt * 16 + li;
+        const uint4 tv = *reinterpret_cast<const uint4*>(tbuf + myrow * TSTR + j);
+        const uint4 aop = (valid && rowad[myrow] == a) ? tv : zero4();
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-              const int n = wc * CT * 16 + ct * 16 + li;
-              const uint4 bop = (j < ent.y) ? *reinterpret_cast<const uint4*>(bsb + ent.z + n * ent.y + j) : zero4();
-              acc[tt][ct] = mfma_bf16_16x16x32(aop, bop, acc[tt][ct]);
-            }
-          }
-        }
+        for (int ct = 0; ct < CT; ++ct) lacc[tt][ct] = mfma_bf16_16x16x32(aop, bop[ct], lacc[tt][ct]);
       }
     };
-    int e0 = 0;
-    int e1 = __builtin_amdgcn_readfirstlane(meta[1]), nch = __builtin_amdgcn_readfirstlane(meta[2]);
-    // (3) the first batch's B loads go out together with the t loads: one round trip
-    if (nl > 0) load_batch(0, e1, nch);
+    // (3) the first RING - 1 items' B loads go out before the t loads
+    if (cnt > 0) {
+#pragma unroll
+      for (int d = 0; d < RING - 1; ++d) issue(d, d, bq[d]);
+    }
     // (4) t rows -> LDS as bf16 pre-scaled by s_a (zero beyond the row's rank)
     const int nel = ROWS * p.r_max;
-    for (int base = 0; base < nel && nl > 0; base += 256 * EPI_TE) {
+    for (int base = 0; base < nel && n_items > 0; base += 256 * EPI_TE) {
       float vals[EPI_TE];
       if (p.t_tag) {
         uint64_t raw[EPI_TE][MAX_KPARTS];
@@ -893,26 +943,48 @@ __device__ void gemm_item(const GemmParams& p, int item, char* smem, int e, int*
         const int idx = base + tid + 256 * m;
         if (idx < nel) {
           const int i = idx / p.r_max, j = idx - i * p.r_max;
-          tbuf[i * MAX_RANK + j] = (uint16_t)f32_to_bf16_rne(vals[m] * rowsc[i]);
+          tbuf[i * TSTR + j] = (uint16_t)f32_to_bf16_rne(vals[m] * rowsc[i]);
           if (p.t_out && cb == 0 && row0 + i < p.T && rowad[i] >= 0) p.t_out[(long)(row0 + i) * p.r_max + j] = vals[m];
         }
       }
     }
-    // (5) batches: stage B in LDS, multiply; the next batch is planned by one lane
-    while (e0 < nl) {
+    __syncthreads();
+    // (5) one bf16 MFMA per item and column tile, RING - 1 items of B in flight
+    for (int m0 = 0; m0 < cnt; m0 += RING) {
 #pragma unroll
-      for (int m = 0; m < EPI_BCHUNKS; ++m)
-        if (bdst[m] >= 0) *reinterpret_cast<uint4*>(bsb + bdst[m]) = breg[m];
+      for (int d = 0; d < RING; ++d) {
+        issue(0, m0 + d + RING - 1, bq[(d + RING - 1) % RING]);
+        if (m0 + d >= cnt) break;
+        consume(m0 + d, bq[d]);
+      }
+    }
+    // (6) the k-waves' adapter sums, in wave order, join the base in the waves with wk == 0
+    if (WK > 1) {
+      if (wk > 0) {
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct)
+            *reinterpret_cast<v4f*>(lred + ((((wk - 1) * WC + wc) * TT + tt) * CT + ct) * 256 + lane * 4) =
+                lacc[tt][ct];
+      }
       __syncthreads();
-      mma_batch(e0, e1);
-      __syncthreads();
-      e0 = e1;
-      if (e0 >= nl) break;
-      if (tid == 0) plan_batch(e0, nl);
-      __syncthreads();
-      e1 = __builtin_amdgcn_readfirstlane(meta[1]);
-      nch = __builtin_amdgcn_readfirstlane(meta[2]);
-      load_batch(e0, e1, nch);
+      if (wk == 0) {
+#pragma unroll
+        for (int w = 1; w < WK; ++w)
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+              lacc[tt][ct] +=
+                  *reinterpret_cast<const v4f*>(lred + ((((w - 1) * WC + wc) * TT + tt) * CT + ct) * 256 + lane * 4);
+      }
+    }
+    if (wk == 0) {
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) acc[tt][ct] += lacc[tt][ct];
     }
   }
 
@@ -986,6 +1058,7 @@ static hipError_t launch_layer_f(const LayerPlan& pl, int grid, hipStream_t stre
                                  const GemmParams& gp) {
   LORA_LAYER_CASE(1, 2, 1, 4, false)
   LORA_LAYER_CASE(4, 1, 4, 1, false)
+  LORA_LAYER_CASE(4, 2, 4, 1, false)
   LORA_LAYER_CASE(8, 2, 2, 2, false)
   LORA_LAYER_CASE(8, 1, 4, 1, true)
   LORA_LAYER_CASE(8, 2, 4, 1, true)
@@ -1011,7 +1084,7 @@ hipError_t launch_build_segments(const int* ids, int T, int n_ad, int* seg, int*
 }
 
 hipError_t launch_quant(const uint16_t* x, int T, int K, uint8_t* xq, uint8_t* xsc, hipStream_t s) {
-  const long blocks = ((long)T * (K / 32) + 255) / 256;
+  const long blocks = ((long)T * (K / 8) + 255) / 256;
   const int grid = (int)std::min<long>(blocks, 8192);
   hipLaunchKernelGGL(k_quant_mxfp8, dim3(grid), dim3(256), 0, s, x, T, K, xq, xsc);
   return hipGetLastError();

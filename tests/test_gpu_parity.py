@@ -94,6 +94,7 @@ EDGE = [
     (129, 256, 512, "fp8", [32, 16], 7),
     (200, 512, 384, "mxfp4", [8, 64, 16], 8),
     (300, 768, 256, "fp8", [48, 8, 16, 64], 9),
+    (150, 640, 192, "fp8", [16, 32], 10),  # pre-quantised x with a partial last K-chunk
 ]
 
 
