@@ -44,9 +44,9 @@ LayerPlan make_plan(int T, int K, int N, int n_ad, int r_max, int fmt, bool fuse
     // 128 channels per workgroup: with the down-projection's workgroups the grid stays
     // within one workgroup per CU for the widest decode layers
     pl.TT = 4; pl.CT = (N % 128 == 0) ? 2 : 1; pl.WC = 4; pl.WK = 1; pl.XQ = false;
-  } else if (T <= 128) {
-    pl.TT = 8; pl.CT = 2; pl.WC = 2; pl.WK = 2; pl.XQ = false;
   } else {
+    // 128 tokens per tile: x is quantised once by a pre-pass (every column tile reads
+    // it), and 128 channels per workgroup halve those reads
     pl.TT = 8; pl.WC = 4; pl.WK = 1; pl.XQ = true;
     pl.CT = (N % 128 == 0) ? 2 : 1;
   }
@@ -65,20 +65,22 @@ LayerPlan make_plan(int T, int K, int N, int n_ad, int r_max, int fmt, bool fuse
   pl.n_gemm_wg = tiles * pl.ksplit;
 
   // down-projection: item = (adapter, token block, group of 16*jper ranks, K-part)
+  int kparts = 1;
   if (T <= 128) {
+    pl.s_cfg = 0;
     pl.s_tblk = ceil_div(T, 16) * 16;
     pl.s_ntblk = 1;
     pl.s_jper = 1;
     pl.s_njg = ceil_div(r_max, 16);
+    // latency-bound single-tile decode: split K so that t is ready early
+    if (fused && T <= 16) kparts = std::min(4, std::max(1, K / 1024));
   } else {
+    pl.s_cfg = 1;
     pl.s_tblk = 64;
     pl.s_ntblk = ceil_div(T, 64);
     pl.s_jper = 2;
     pl.s_njg = ceil_div(r_max, 32);
   }
-  int kparts = 1;
-  // latency-bound single-tile decode: split K so that t is ready early
-  if (fused && T <= 16) kparts = std::min(4, std::max(1, K / 1024));
   pl.s_kpart_len = ceil_div(ceil_div(K, kparts), 256) * 256;
   pl.s_kparts = ceil_div(K, pl.s_kpart_len);
   pl.n_shrink_wg = n_ad * pl.s_ntblk * pl.s_njg * pl.s_kparts;

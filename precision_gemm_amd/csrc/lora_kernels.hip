@@ -221,7 +221,7 @@ __device__ __forceinline__ uint64_t wait_tag(const uint64_t* p, uint64_t v, uint
 // In the fused launch (ctrl != null) the workgroup publishes the launch epoch once its
 // first loads are in flight (or when it finds no work); the tag is read after a barrier.
 template <int TG, int JP, int U>
-__device__ void shrink_item(const ShrinkParams& p, int item, char* smem, int* ctrl, int e, int* lds_epoch,
+__device__ __forceinline__ void shrink_item(const ShrinkParams& p, int item, char* smem, int* ctrl, int e, int* lds_epoch,
                             int* started) {
   bool published = false;
   auto publish = [&]() {
@@ -437,7 +437,6 @@ struct ChunkK {
 };
 
 constexpr int EPI_TE = 8;       // t elements per thread per gather batch
-constexpr int MAX_KPARTS = 4;
 // B-operand loads of the up-projection: a ring of RING items, all but one in flight
 // (shorter for the widest tiles, whose accumulators leave fewer registers)
 template <int TT, int CT>
@@ -454,7 +453,10 @@ struct EpiLayout {
   static constexpr int ROWBP = ROWSC + ROWS * 4;     // uint64 [ROWS]: address of its B^T
   static constexpr int ITEMS = ROWBP + ROWS * 8;     // int [2 * ROWS]: up-projection work items
   static constexpr int LEAD = ITEMS + ROWS * 8;      // int [ROWS]: token tiles of the row's adapter (leader rows)
-  static constexpr int META = LEAD + ROWS * 4;       // int [16]
+  static constexpr int LEADOF = LEAD + ROWS * 4;     // int [ROWS]: leader row of the row's adapter (-1: none)
+  static constexpr int MINE = LEADOF + ROWS * 4;     // int [ROWS]: leader rows whose adapter this K-split adds
+  static constexpr int RLIST = MINE + ROWS * 4;      // int [ROWS]: rows whose t this K-split needs
+  static constexpr int META = RLIST + ROWS * 4;      // int [16]
   static constexpr int TB = META + 64;               // bf16 [ROWS][TSTR]: s_a * t
   static constexpr int LRED = TB + ROWS * TSTR * 2;  // float [WK-1][WC][TT][CT][256]: k-wave sums
   static constexpr int BYTES = LRED + (WK - 1) * WC * TT * CT * 256 * 4;
@@ -472,13 +474,14 @@ struct GemmSmem {
 };
 
 template <int FMT, int TT, int CT, int WC, int WK, bool XQ>
-__device__ void gemm_item(const GemmParams& p, int item, char* smem, int e, int* lds_epoch, int* started) {
+__device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* smem, int e, int* lds_epoch, int* started) {
   using CK = ChunkK<TT, CT>;
   constexpr int KC = CK::KC, STEPS = CK::STEPS, ROW = CK::ROW;
   constexpr int SPW = STEPS / WK;  // k-steps per wave per chunk
   constexpr int WN = WC * CT * 16;
   constexpr int FMTB = (FMT == LORA_W_FP8_E4M3) ? 0 : 4;
   constexpr int ROWS = TT * 16;
+  constexpr int KP = (TT == 1) ? 4 : 1;  // K-parts of t the epilogue adds (the host plan stays within it)
   static_assert(STEPS % WK == 0, "k-steps per chunk must split evenly over the k-waves");
   uint8_t* xs = reinterpret_cast<uint8_t*>(smem);  // [ROWS][ROW]
   uint8_t* ss = xs + ROWS * ROW;                    // [ROWS][KC/32]
@@ -661,7 +664,7 @@ __device__ void gemm_item(const GemmParams& p, int item, char* smem, int e, int*
     load_x(1, 1);
     load_w(1, 1);
   }
-  const bool row_ok = p.lora && ks == p.ksplit - 1 && tid < ROWS && row0 + tid < p.T && id_raw >= 0 &&
+  const bool row_ok = p.lora && tid < ROWS && row0 + tid < p.T && id_raw >= 0 &&
                       id_raw < p.n_ad;
   int row_r = 0;
   float row_s = 0.f;
@@ -716,60 +719,7 @@ __device__ void gemm_item(const GemmParams& p, int item, char* smem, int e, int*
     __syncthreads();
   }
 
-  // ---- K-split over workgroups: producers store sums + flag, the last split reduces
-  if (p.ksplit > 1) {
-    constexpr int PER_WAVE = TT * CT * 256;
-    const long tile_base = (long)tile * p.ksplit;
-    if (ks < p.ksplit - 1) {
-      if (wk == 0) {
-        float* mine = p.gpart + ((tile_base + ks) * WC + wc) * PER_WAVE;
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-          for (int ct = 0; ct < CT; ++ct) {
-            uint64_t* d = reinterpret_cast<uint64_t*>(mine + ((tt * CT + ct) * 64 + lane) * 4);
-            st_agent_u64(d, ((uint64_t)__float_as_uint(acc[tt][ct][1]) << 32) | __float_as_uint(acc[tt][ct][0]));
-            st_agent_u64(d + 1, ((uint64_t)__float_as_uint(acc[tt][ct][3]) << 32) | __float_as_uint(acc[tt][ct][2]));
-          }
-      }
-      wait_stores();
-      __syncthreads();
-      if (tid == 0) set_agent(p.gflag + tile_base + ks, (int)tag);
-      return;
-    }
-    // the reducer: wait for every producer of this tile
-    for (int k2 = tid; k2 < p.ksplit - 1; k2 += 256) {
-      int spins = 0;
-      while ((uint32_t)ld_agent(p.gflag + tile_base + k2) != tag) {
-        __builtin_amdgcn_s_sleep(2);
-        if (++spins > p.spin_limit) {
-          set_agent(p.ctrl + CTRL_STATUS, 1);
-          break;
-        }
-      }
-    }
-    __syncthreads();
-    if (wk == 0) {
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          v4f sum = v4f{0.f, 0.f, 0.f, 0.f};
-          for (int k2 = 0; k2 < p.ksplit - 1; ++k2) {
-            const uint64_t* src = reinterpret_cast<const uint64_t*>(p.gpart + ((tile_base + k2) * WC + wc) * PER_WAVE +
-                                                                    ((tt * CT + ct) * 64 + lane) * 4);
-            const uint64_t u0 = ld_agent_u64(src), u1 = ld_agent_u64(src + 1);
-            sum[0] += __uint_as_float((uint32_t)u0);
-            sum[1] += __uint_as_float((uint32_t)(u0 >> 32));
-            sum[2] += __uint_as_float((uint32_t)u1);
-            sum[3] += __uint_as_float((uint32_t)(u1 >> 32));
-          }
-          acc[tt][ct] = sum + acc[tt][ct];
-        }
-    }
-  }
-
-  // ---- epilogue: channel scale
+  // ---- epilogue: channel scale (of this K-split's sum: the splits are added scaled)
   if (FMT == LORA_W_FP8_E4M3 && wk == 0) {
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
@@ -779,7 +729,7 @@ __device__ void gemm_item(const GemmParams& p, int item, char* smem, int e, int*
     }
   }
 
-  // ---- epilogue: adapter up-projection
+  // ---- epilogue: adapter up-projection (this K-split's share of the adapters)
   if (p.lora) {
     using EL = EpiLayout<TT, CT, WC, WK>;
     int* rowad = reinterpret_cast<int*>(smem + EL::ROWAD);
@@ -804,28 +754,42 @@ __device__ void gemm_item(const GemmParams& p, int item, char* smem, int e, int*
     //     order of the adapter's first row (its leader), with the set of 16-row token tiles
     //     that hold its rows; each item's B operands then serve all those tiles
     int* lead = reinterpret_cast<int*>(smem + EL::LEAD);
+    int* leadof = reinterpret_cast<int*>(smem + EL::LEADOF);
+    int* mine = reinterpret_cast<int*>(smem + EL::MINE);
+    int* rowlist = reinterpret_cast<int*>(smem + EL::RLIST);
     int my_lead = -1;
     if (tid < ROWS) {
       lead[tid] = 0;
+      mine[tid] = 0;
       const int a = rowad[tid];
-      if (a >= 0) {
+      if (a >= 0) {  // first row with the same adapter: four rows per LDS read, no early exit
         my_lead = tid;
-        for (int l = 0; l < tid; ++l)
-          if (rowad[l] == a) {
-            my_lead = l;
-            break;
-          }
+        for (int l0 = 0; l0 < tid; l0 += 4) {
+          const int4 v = *reinterpret_cast<const int4*>(rowad + l0);
+          if (v.w == a && l0 + 3 < tid) my_lead = min(my_lead, l0 + 3);
+          if (v.z == a && l0 + 2 < tid) my_lead = min(my_lead, l0 + 2);
+          if (v.y == a && l0 + 1 < tid) my_lead = min(my_lead, l0 + 1);
+          if (v.x == a) my_lead = min(my_lead, l0);
+        }
       }
     }
+    if (tid < ROWS) leadof[tid] = my_lead;
     __syncthreads();
     if (my_lead >= 0) atomicOr(lead + my_lead, 1 << (tid >> 4));
     __syncthreads();
+    // With a K-split the tile's adapters are dealt round-robin (in leader order) to its
+    // splits: each split adds the up-projection of its share to its own sum.
     if (wave == 0) {
-      int n = 0;
+      int n = 0, n_lead = 0;
       for (int c0 = 0; c0 < ROWS; c0 += 64) {
         const int row = c0 + lane;
         const int mask = (row < ROWS) ? lead[row] : 0;  // non-zero only for leader rows
-        const int nb = mask ? ((rowrk[row] + 31) >> 5) : 0;
+        const unsigned long long bl = __ballot(mask != 0);
+        const int ord = n_lead + __popcll(bl & ((1ull << lane) - 1ull));
+        n_lead += __popcll(bl);
+        const bool own = mask != 0 && (ord % p.ksplit) == ks;
+        if (own) mine[row] = 1;
+        const int nb = own ? ((rowrk[row] + 31) >> 5) : 0;
         int incl = nb;
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
@@ -835,10 +799,23 @@ __device__ void gemm_item(const GemmParams& p, int item, char* smem, int e, int*
         for (int b = 0; b < nb; ++b) items[n + incl - nb + b] = row | (b << 8) | (mask << 16);
         n += __shfl(incl, 63);
       }
-      if (lane == 0) meta[0] = n;
+      // rows whose t this split needs (rows of its adapters), in row order
+      int nr = 0;
+      for (int c0 = 0; c0 < ROWS; c0 += 64) {
+        const int row = c0 + lane;
+        const bool need = row < ROWS && rowrk[row] > 0 && mine[max(leadof[row], 0)];
+        const unsigned long long bl = __ballot(need);
+        if (need) rowlist[nr + __popcll(bl & ((1ull << lane) - 1ull))] = row;
+        nr += __popcll(bl);
+      }
+      if (lane == 0) {
+        meta[0] = n;
+        meta[1] = nr;
+      }
     }
     __syncthreads();
     const int n_items = __builtin_amdgcn_readfirstlane(meta[0]);
+    const int n_rows = __builtin_amdgcn_readfirstlane(meta[1]);
     // items of this wave: wk, wk + WK, ... (the waves sharing columns split the items)
     const int cnt = (n_items > wk) ? (n_items - wk + WK - 1) / WK : 0;
 
@@ -891,30 +868,31 @@ __device__ void gemm_item(const GemmParams& p, int item, char* smem, int e, int*
 #pragma unroll
       for (int d = 0; d < RING - 1; ++d) issue(d, d, bq[d]);
     }
-    // (4) t rows -> LDS as bf16 pre-scaled by s_a (zero beyond the row's rank)
-    const int nel = ROWS * p.r_max;
-    for (int base = 0; base < nel && n_items > 0; base += 256 * EPI_TE) {
+    // (4) t of the rows this split needs -> LDS as bf16 pre-scaled by s_a (zero beyond the
+    //     row's rank); the other rows of tbuf are never selected
+    const int nel = n_rows * p.r_max;
+    for (int base = 0; base < nel; base += 256 * EPI_TE) {
       float vals[EPI_TE];
       if (p.t_tag) {
-        uint64_t raw[EPI_TE][MAX_KPARTS];
+        uint64_t raw[EPI_TE][KP];
         // all loads first (unconditional, clamped addresses), then the tag checks
         long addr[EPI_TE];
         bool need[EPI_TE];
 #pragma unroll
         for (int m = 0; m < EPI_TE; ++m) {
           const int idx = min(base + tid + 256 * m, nel - 1);
-          const int i = idx / p.r_max, j = idx - i * p.r_max;
+          const int q = idx / p.r_max, i = rowlist[q], j = idx - q * p.r_max;
           need[m] = (base + tid + 256 * m < nel) && j < rowrk[i];
-          addr[m] = (long)min(row0 + i, p.T - 1) * p.r_max + j;
+          addr[m] = (long)(row0 + i) * p.r_max + j;
 #pragma unroll
-          for (int k2 = 0; k2 < MAX_KPARTS; ++k2)
+          for (int k2 = 0; k2 < KP; ++k2)
             raw[m][k2] = ld_agent_u64(p.t_tag + (long)min(k2, p.t_kparts - 1) * p.T * p.r_max + addr[m]);
         }
 #pragma unroll
         for (int m = 0; m < EPI_TE; ++m) {
           float v = 0.f;
 #pragma unroll
-          for (int k2 = 0; k2 < MAX_KPARTS; ++k2) {
+          for (int k2 = 0; k2 < KP; ++k2) {
             if (need[m] && k2 < p.t_kparts) {
               const uint64_t w = wait_tag(p.t_tag + (long)k2 * p.T * p.r_max + addr[m], raw[m][k2], tag, p.ctrl,
                                           p.spin_limit);
@@ -928,23 +906,23 @@ __device__ void gemm_item(const GemmParams& p, int item, char* smem, int e, int*
 #pragma unroll
         for (int m = 0; m < EPI_TE; ++m) {
           const int idx = min(base + tid + 256 * m, nel - 1);
-          const int i = idx / p.r_max;
-          raw[m] = p.t[(long)min(row0 + i, p.T - 1) * p.r_max + (idx - i * p.r_max)];
+          const int q = idx / p.r_max;
+          raw[m] = p.t[(long)(row0 + rowlist[q]) * p.r_max + (idx - q * p.r_max)];
         }
 #pragma unroll
         for (int m = 0; m < EPI_TE; ++m) {
           const int idx = base + tid + 256 * m;
-          const int i = min(idx, nel - 1) / p.r_max, j = min(idx, nel - 1) - i * p.r_max;
-          vals[m] = (idx < nel && j < rowrk[i]) ? raw[m] : 0.f;
+          const int q = min(idx, nel - 1) / p.r_max, j = min(idx, nel - 1) - q * p.r_max;
+          vals[m] = (idx < nel && j < rowrk[rowlist[q]]) ? raw[m] : 0.f;
         }
       }
 #pragma unroll
       for (int m = 0; m < EPI_TE; ++m) {
         const int idx = base + tid + 256 * m;
         if (idx < nel) {
-          const int i = idx / p.r_max, j = idx - i * p.r_max;
+          const int q = idx / p.r_max, i = rowlist[q], j = idx - q * p.r_max;
           tbuf[i * TSTR + j] = (uint16_t)f32_to_bf16_rne(vals[m] * rowsc[i]);
-          if (p.t_out && cb == 0 && row0 + i < p.T && rowad[i] >= 0) p.t_out[(long)(row0 + i) * p.r_max + j] = vals[m];
+          if (p.t_out && cb == 0) p.t_out[(long)(row0 + i) * p.r_max + j] = vals[m];
         }
       }
     }
@@ -985,6 +963,60 @@ __device__ void gemm_item(const GemmParams& p, int item, char* smem, int e, int*
       for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) acc[tt][ct] += lacc[tt][ct];
+    }
+  }
+
+  // ---- K-split over workgroups: producers store their (scaled, adapter-including) sums
+  //      and a flag, the last split adds them in split order
+  if (p.ksplit > 1) {
+    constexpr int PER_WAVE = TT * CT * 256;
+    const long tile_base = (long)tile * p.ksplit;
+    if (ks < p.ksplit - 1) {
+      if (wk == 0) {
+        float* mine = p.gpart + ((tile_base + ks) * WC + wc) * PER_WAVE;
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            uint64_t* d = reinterpret_cast<uint64_t*>(mine + ((tt * CT + ct) * 64 + lane) * 4);
+            st_agent_u64(d, ((uint64_t)__float_as_uint(acc[tt][ct][1]) << 32) | __float_as_uint(acc[tt][ct][0]));
+            st_agent_u64(d + 1, ((uint64_t)__float_as_uint(acc[tt][ct][3]) << 32) | __float_as_uint(acc[tt][ct][2]));
+          }
+      }
+      wait_stores();
+      __syncthreads();
+      if (tid == 0) set_agent(p.gflag + tile_base + ks, (int)tag);
+      return;
+    }
+    // the reducer: wait for every producer of this tile
+    for (int k2 = tid; k2 < p.ksplit - 1; k2 += 256) {
+      int spins = 0;
+      while ((uint32_t)ld_agent(p.gflag + tile_base + k2) != tag) {
+        __builtin_amdgcn_s_sleep(2);
+        if (++spins > p.spin_limit) {
+          set_agent(p.ctrl + CTRL_STATUS, 1);
+          break;
+        }
+      }
+    }
+    __syncthreads();
+    if (wk == 0) {
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          v4f sum = v4f{0.f, 0.f, 0.f, 0.f};
+          for (int k2 = 0; k2 < p.ksplit - 1; ++k2) {
+            const uint64_t* src = reinterpret_cast<const uint64_t*>(p.gpart + ((tile_base + k2) * WC + wc) * PER_WAVE +
+                                                                    ((tt * CT + ct) * 64 + lane) * 4);
+            const uint64_t u0 = ld_agent_u64(src), u1 = ld_agent_u64(src + 1);
+            sum[0] += __uint_as_float((uint32_t)u0);
+            sum[1] += __uint_as_float((uint32_t)(u0 >> 32));
+            sum[2] += __uint_as_float((uint32_t)u1);
+            sum[3] += __uint_as_float((uint32_t)(u1 >> 32));
+          }
+          acc[tt][ct] = sum + acc[tt][ct];
+        }
     }
   }
 
@@ -1038,30 +1070,30 @@ static hipError_t launch_k(KernelT kern, int grid, size_t smem, hipStream_t stre
   return hipGetLastError();
 }
 
-template <int FMT, int TT, int CT, int WC, int WK, bool XQ>
+template <int FMT, int TT, int CT, int WC, int WK, bool XQ, int TG, int JP, int U>
 static hipError_t launch_layer_t(const LayerPlan& pl, int grid, hipStream_t stream, const ShrinkParams& sp,
                                  const GemmParams& gp) {
-  // the down-projection shape goes with the GEMM shape: decode (one 16-rank tile per
-  // workgroup, two-step prefetch) or prefill (four token and two rank tiles)
-  constexpr int TG = XQ ? 4 : 1, JP = XQ ? 2 : 1, U = XQ ? 1 : 2;
-  if (pl.s_jper != JP) return hipErrorInvalidValue;
-  const size_t sm = std::max((size_t)GemmSmem<TT, CT, WC, WK>::BYTES, gp.n_shrink > 0 ? shrink_smem<TG, JP, U>() : (size_t)0);
+  const size_t sm =
+      std::max((size_t)GemmSmem<TT, CT, WC, WK>::BYTES, gp.n_shrink > 0 ? shrink_smem<TG, JP, U>() : (size_t)0);
   return launch_k(k_layer<FMT, TT, CT, WC, WK, XQ, TG, JP, U>, grid, sm, stream, sp, gp);
 }
 
-#define LORA_LAYER_CASE(TT_, CT_, WC_, WK_, XQ_)                                    \
-  if (pl.TT == TT_ && pl.CT == CT_ && pl.WC == WC_ && pl.WK == WK_ && pl.XQ == XQ_) \
-    return launch_layer_t<FMT, TT_, CT_, WC_, WK_, XQ_>(pl, grid, stream, sp, gp);
+// GEMM tile (TT, CT, WC, WK, XQ) and down-projection shape: decode (cfg 0: one 16-rank
+// tile, two-step prefetch) or prefill (cfg 1: four token tiles, two rank tiles)
+#define LORA_LAYER_CASE(TT_, CT_, WC_, WK_, XQ_, CFG_, TG_, JP_, U_)                                      \
+  if (pl.TT == TT_ && pl.CT == CT_ && pl.WC == WC_ && pl.WK == WK_ && pl.XQ == XQ_ && pl.s_cfg == CFG_) \
+    return launch_layer_t<FMT, TT_, CT_, WC_, WK_, XQ_, TG_, JP_, U_>(pl, grid, stream, sp, gp);
 
 template <int FMT>
 static hipError_t launch_layer_f(const LayerPlan& pl, int grid, hipStream_t stream, const ShrinkParams& sp,
                                  const GemmParams& gp) {
-  LORA_LAYER_CASE(1, 2, 1, 4, false)
-  LORA_LAYER_CASE(4, 1, 4, 1, false)
-  LORA_LAYER_CASE(4, 2, 4, 1, false)
-  LORA_LAYER_CASE(8, 2, 2, 2, false)
-  LORA_LAYER_CASE(8, 1, 4, 1, true)
-  LORA_LAYER_CASE(8, 2, 4, 1, true)
+  LORA_LAYER_CASE(1, 2, 1, 4, false, 0, 1, 1, 4)
+  LORA_LAYER_CASE(4, 1, 4, 1, false, 0, 1, 1, 4)
+  LORA_LAYER_CASE(4, 2, 4, 1, false, 0, 1, 1, 4)
+  LORA_LAYER_CASE(8, 1, 4, 1, true, 0, 1, 1, 4)
+  LORA_LAYER_CASE(8, 2, 4, 1, true, 0, 1, 1, 4)
+  LORA_LAYER_CASE(8, 1, 4, 1, true, 1, 4, 2, 1)
+  LORA_LAYER_CASE(8, 2, 4, 1, true, 1, 4, 2, 1)
   return hipErrorInvalidValue;
 }
 #undef LORA_LAYER_CASE
@@ -1073,8 +1105,8 @@ hipError_t launch_layer(const LayerPlan& pl, hipStream_t stream, const ShrinkPar
 }
 
 hipError_t launch_shrink(const LayerPlan& pl, hipStream_t stream, const ShrinkParams& sp) {
-  if (pl.s_jper == 1) return launch_k(k_shrink<1, 1, 2>, pl.n_shrink_wg, shrink_smem<1, 1, 2>(), stream, sp);
-  if (pl.s_jper == 2) return launch_k(k_shrink<4, 2, 1>, pl.n_shrink_wg, shrink_smem<4, 2, 1>(), stream, sp);
+  if (pl.s_cfg == 0) return launch_k(k_shrink<1, 1, 4>, pl.n_shrink_wg, shrink_smem<1, 1, 4>(), stream, sp);
+  if (pl.s_cfg == 1) return launch_k(k_shrink<4, 2, 1>, pl.n_shrink_wg, shrink_smem<4, 2, 1>(), stream, sp);
   return hipErrorInvalidValue;
 }
 

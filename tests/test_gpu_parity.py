@@ -95,10 +95,14 @@ EDGE = [
     (200, 512, 384, "mxfp4", [8, 64, 16], 8),
     (300, 768, 256, "fp8", [48, 8, 16, 64], 9),
     (150, 640, 192, "fp8", [16, 32], 10),  # pre-quantised x with a partial last K-chunk
+    # many adapters with a few tokens each: up-projection by the down-projection workgroups
+    (96, 8192, 192, "fp8", [8, 16, 32, 64] * 20, 11),
+    (200, 4096, 256, "mxfp4", [64, 8, 32, 16, 48] * 14, 12),
+    (130, 1024, 320, "fp8", [16, 64] * 32, 13),
 ]
 
 
-@pytest.mark.parametrize("case", EDGE, ids=[f"T{c[0]}_K{c[1]}_N{c[2]}_{c[3]}" for c in EDGE])
+@pytest.mark.parametrize("case", EDGE, ids=[f"T{c[0]}_K{c[1]}_N{c[2]}_{c[3]}_a{len(c[4])}" for c in EDGE])
 @pytest.mark.parametrize("fused", [True, False], ids=["fused", "unfused"])
 def test_edge_shapes(case, fused):
     T, K, N, fmt, ranks, seed = case
