@@ -99,6 +99,9 @@ def main():
     ap.add_argument("--sets", type=int, default=0, help="input copies to rotate over (0: enough for 2x 256 MB)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph replay")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="after the timed region, run three plain device copies of this many MiB (untimed): "
+                         "the reference that scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
@@ -234,6 +237,14 @@ def main():
         "device_status": status,
         "kernel_sha": sha,
     }
+    if args.copy_mb > 0:
+        src = torch.ones(args.copy_mb << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = src.numel()
+        del src, dst
     if not args.no_cpu:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl)

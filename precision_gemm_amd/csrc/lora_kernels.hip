@@ -436,7 +436,6 @@ struct ChunkK {
   static constexpr int ROW = KC + 16;  // LDS row stride in bytes
 };
 
-constexpr int EPI_TE = 8;       // t elements per thread per gather batch
 // B-operand loads of the up-projection: a ring of RING items, all but one in flight
 // (shorter for the widest tiles, whose accumulators leave fewer registers)
 template <int TT, int CT>
@@ -446,7 +445,8 @@ constexpr int TSTR = MAX_RANK + 8;  // bf16 row stride of the staged t (the pad 
 template <int TT, int CT, int WC, int WK>
 struct EpiLayout {
   static constexpr int ROWS = TT * 16;
-  // byte offsets inside the epilogue's LDS area
+  // per-row metadata of the up-projection, built during the main loop in an LDS area of
+  // its own (byte offsets from that area)
   static constexpr int ROWAD = 0;                    // int [ROWS]: adapter of the row (-1: none)
   static constexpr int ROWRK = ROWAD + ROWS * 4;     // int [ROWS]: its rank
   static constexpr int ROWSC = ROWRK + ROWS * 4;     // float [ROWS]: its scale
@@ -457,10 +457,12 @@ struct EpiLayout {
   static constexpr int MINE = LEADOF + ROWS * 4;     // int [ROWS]: leader rows whose adapter this K-split adds
   static constexpr int RLIST = MINE + ROWS * 4;      // int [ROWS]: rows whose t this K-split needs
   static constexpr int META = RLIST + ROWS * 4;      // int [16]
-  static constexpr int TB = META + 64;               // bf16 [ROWS][TSTR]: s_a * t
+  static constexpr int MD_BYTES = META + 64;
+  // after the main loop, over the x staging area (offsets from the start)
+  static constexpr int TB = 0;                       // bf16 [ROWS][TSTR]: s_a * t
   static constexpr int LRED = TB + ROWS * TSTR * 2;  // float [WK-1][WC][TT][CT][256]: k-wave sums
-  static constexpr int BYTES = LRED + (WK - 1) * WC * TT * CT * 256 * 4;
-  static_assert(ROWBP % 8 == 0 && TB % 16 == 0 && LRED % 16 == 0, "epilogue LDS alignment");
+  static constexpr int POST = LRED + (WK - 1) * WC * TT * CT * 256 * 4;
+  static_assert(ROWBP % 8 == 0 && LRED % 16 == 0, "epilogue LDS alignment");
 };
 
 template <int TT, int CT, int WC, int WK>
@@ -468,9 +470,10 @@ struct GemmSmem {
   using CK = ChunkK<TT, CT>;
   static constexpr int MAIN = TT * 16 * CK::ROW + TT * 16 * (CK::KC / 32);
   static constexpr int RED = (WK - 1) * WC * TT * CT * 256 * 4;
-  static constexpr int EPI = EpiLayout<TT, CT, WC, WK>::BYTES;
+  static constexpr int POST = EpiLayout<TT, CT, WC, WK>::POST;
   static constexpr int M1 = MAIN > RED ? MAIN : RED;
-  static constexpr int BYTES = M1 > EPI ? M1 : EPI;
+  static constexpr int MD = ((M1 > POST ? M1 : POST) + 15) & ~15;  // metadata area, kept through the loop
+  static constexpr int BYTES = MD + EpiLayout<TT, CT, WC, WK>::MD_BYTES;
 };
 
 template <int FMT, int TT, int CT, int WC, int WK, bool XQ>
@@ -482,6 +485,9 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   constexpr int FMTB = (FMT == LORA_W_FP8_E4M3) ? 0 : 4;
   constexpr int ROWS = TT * 16;
   constexpr int KP = (TT == 1) ? 4 : 1;  // K-parts of t the epilogue adds (the host plan stays within it)
+  // t elements per thread per gather batch: the whole block's t (ROWS x 64) in one batch,
+  // so that the gather costs one memory round trip
+  constexpr int EPI_TE = (KP == 1) ? (ROWS * MAX_RANK + 255) / 256 : 8;
   static_assert(STEPS % WK == 0, "k-steps per chunk must split evenly over the k-waves");
   uint8_t* xs = reinterpret_cast<uint8_t*>(smem);  // [ROWS][ROW]
   uint8_t* ss = xs + ROWS * ROW;                    // [ROWS][KC/32]
@@ -675,6 +681,92 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
     row_s = p.scales[ac];
     row_bp = p.B_ptrs[ac];
   }
+  // up-projection metadata (adapter list, work items, rows whose t is needed), built once
+  // the first chunk is multiplied: its LDS latency then overlaps the loads in flight
+  using EL = EpiLayout<TT, CT, WC, WK>;
+  char* md = smem + GemmSmem<TT, CT, WC, WK>::MD;
+  int* rowad = reinterpret_cast<int*>(md + EL::ROWAD);
+  int* rowrk = reinterpret_cast<int*>(md + EL::ROWRK);
+  float* rowsc = reinterpret_cast<float*>(md + EL::ROWSC);
+  uint64_t* rowbp = reinterpret_cast<uint64_t*>(md + EL::ROWBP);
+  int* items = reinterpret_cast<int*>(md + EL::ITEMS);
+  int* lead = reinterpret_cast<int*>(md + EL::LEAD);
+  int* leadof = reinterpret_cast<int*>(md + EL::LEADOF);
+  int* mine = reinterpret_cast<int*>(md + EL::MINE);
+  int* rowlist = reinterpret_cast<int*>(md + EL::RLIST);
+  int* meta = reinterpret_cast<int*>(md + EL::META);
+  auto prepare_epilogue = [&]() {
+    // (1) adapter, rank, scale and B address of every row; a rank outside the limits
+    //     drops the row's adapter term
+    if (tid < ROWS) {
+      const bool ok = row_ok && row_r >= 8 && row_r <= p.r_max && (row_r & 7) == 0;
+      rowad[tid] = ok ? id_raw : -1;
+      rowrk[tid] = ok ? row_r : 0;
+      rowsc[tid] = row_s;
+      rowbp[tid] = row_bp;
+    }
+    __syncthreads();
+    // (2) work items: one per adapter present in the token block and 32 of its ranks, in
+    //     order of the adapter's first row (its leader), with the set of 16-row token tiles
+    //     that hold its rows; each item's B operands then serve all those tiles
+    int my_lead = -1;
+    if (tid < ROWS) {
+      lead[tid] = 0;
+      mine[tid] = 0;
+      const int a = rowad[tid];
+      if (a >= 0) {  // first row with the same adapter: four rows per LDS read, no early exit
+        my_lead = tid;
+        for (int l0 = 0; l0 < tid; l0 += 4) {
+          const int4 v = *reinterpret_cast<const int4*>(rowad + l0);
+          if (v.w == a && l0 + 3 < tid) my_lead = min(my_lead, l0 + 3);
+          if (v.z == a && l0 + 2 < tid) my_lead = min(my_lead, l0 + 2);
+          if (v.y == a && l0 + 1 < tid) my_lead = min(my_lead, l0 + 1);
+          if (v.x == a) my_lead = min(my_lead, l0);
+        }
+      }
+    }
+    if (tid < ROWS) leadof[tid] = my_lead;
+    __syncthreads();
+    if (my_lead >= 0) atomicOr(lead + my_lead, 1 << (tid >> 4));
+    __syncthreads();
+    // With a K-split the tile's adapters are dealt round-robin (in leader order) to its
+    // splits: each split adds the up-projection of its share to its own sum.
+    if (wave == 0) {
+      int n = 0, n_lead = 0;
+      for (int c0 = 0; c0 < ROWS; c0 += 64) {
+        const int row = c0 + lane;
+        const int mask = (row < ROWS) ? lead[row] : 0;  // non-zero only for leader rows
+        const unsigned long long bl = __ballot(mask != 0);
+        const int ord = n_lead + __popcll(bl & ((1ull << lane) - 1ull));
+        n_lead += __popcll(bl);
+        const bool own = mask != 0 && (ord % p.ksplit) == ks;
+        if (own) mine[row] = 1;
+        const int nb = own ? ((rowrk[row] + 31) >> 5) : 0;
+        int incl = nb;
+  #pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const int v = __shfl_up(incl, d);
+          if (lane >= d) incl += v;
+        }
+        for (int b = 0; b < nb; ++b) items[n + incl - nb + b] = row | (b << 8) | (mask << 16);
+        n += __shfl(incl, 63);
+      }
+      // rows whose t this split needs (rows of its adapters), in row order
+      int nr = 0;
+      for (int c0 = 0; c0 < ROWS; c0 += 64) {
+        const int row = c0 + lane;
+        const bool need = row < ROWS && rowrk[row] > 0 && mine[max(leadof[row], 0)];
+        const unsigned long long bl = __ballot(need);
+        if (need) rowlist[nr + __popcll(bl & ((1ull << lane) - 1ull))] = row;
+        nr += __popcll(bl);
+      }
+      if (lane == 0) {
+        meta[0] = n;
+        meta[1] = nr;
+      }
+    }
+  };
+
   for (int c = 0; c < nchunks; c += 2) {
     stage_x(0);
     __syncthreads();
@@ -682,6 +774,10 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
     mma_chunk(0, c);
     if (c + 2 < nchunks) load_w(0, c + 2);
     __syncthreads();
+    if (c == 0 && p.lora) {
+      prepare_epilogue();
+      __syncthreads();
+    }
     if (c + 1 >= nchunks) break;
     stage_x(1);
     __syncthreads();
@@ -731,88 +827,8 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
 
   // ---- epilogue: adapter up-projection (this K-split's share of the adapters)
   if (p.lora) {
-    using EL = EpiLayout<TT, CT, WC, WK>;
-    int* rowad = reinterpret_cast<int*>(smem + EL::ROWAD);
-    int* rowrk = reinterpret_cast<int*>(smem + EL::ROWRK);
-    float* rowsc = reinterpret_cast<float*>(smem + EL::ROWSC);
-    uint64_t* rowbp = reinterpret_cast<uint64_t*>(smem + EL::ROWBP);
-    int* items = reinterpret_cast<int*>(smem + EL::ITEMS);
-    int* meta = reinterpret_cast<int*>(smem + EL::META);
     uint16_t* tbuf = reinterpret_cast<uint16_t*>(smem + EL::TB);
     float* lred = reinterpret_cast<float*>(smem + EL::LRED);
-    // (1) adapter, rank, scale and B address of every row; a rank outside the limits
-    //     drops the row's adapter term
-    if (tid < ROWS) {
-      const bool ok = row_ok && row_r >= 8 && row_r <= p.r_max && (row_r & 7) == 0;
-      rowad[tid] = ok ? id_raw : -1;
-      rowrk[tid] = ok ? row_r : 0;
-      rowsc[tid] = row_s;
-      rowbp[tid] = row_bp;
-    }
-    __syncthreads();
-    // (2) work items: one per adapter present in the token block and 32 of its ranks, in
-    //     order of the adapter's first row (its leader), with the set of 16-row token tiles
-    //     that hold its rows; each item's B operands then serve all those tiles
-    int* lead = reinterpret_cast<int*>(smem + EL::LEAD);
-    int* leadof = reinterpret_cast<int*>(smem + EL::LEADOF);
-    int* mine = reinterpret_cast<int*>(smem + EL::MINE);
-    int* rowlist = reinterpret_cast<int*>(smem + EL::RLIST);
-    int my_lead = -1;
-    if (tid < ROWS) {
-      lead[tid] = 0;
-      mine[tid] = 0;
-      const int a = rowad[tid];
-      if (a >= 0) {  // first row with the same adapter: four rows per LDS read, no early exit
-        my_lead = tid;
-        for (int l0 = 0; l0 < tid; l0 += 4) {
-          const int4 v = *reinterpret_cast<const int4*>(rowad + l0);
-          if (v.w == a && l0 + 3 < tid) my_lead = min(my_lead, l0 + 3);
-          if (v.z == a && l0 + 2 < tid) my_lead = min(my_lead, l0 + 2);
-          if (v.y == a && l0 + 1 < tid) my_lead = min(my_lead, l0 + 1);
-          if (v.x == a) my_lead = min(my_lead, l0);
-        }
-      }
-    }
-    if (tid < ROWS) leadof[tid] = my_lead;
-    __syncthreads();
-    if (my_lead >= 0) atomicOr(lead + my_lead, 1 << (tid >> 4));
-    __syncthreads();
-    // With a K-split the tile's adapters are dealt round-robin (in leader order) to its
-    // splits: each split adds the up-projection of its share to its own sum.
-    if (wave == 0) {
-      int n = 0, n_lead = 0;
-      for (int c0 = 0; c0 < ROWS; c0 += 64) {
-        const int row = c0 + lane;
-        const int mask = (row < ROWS) ? lead[row] : 0;  // non-zero only for leader rows
-        const unsigned long long bl = __ballot(mask != 0);
-        const int ord = n_lead + __popcll(bl & ((1ull << lane) - 1ull));
-        n_lead += __popcll(bl);
-        const bool own = mask != 0 && (ord % p.ksplit) == ks;
-        if (own) mine[row] = 1;
-        const int nb = own ? ((rowrk[row] + 31) >> 5) : 0;
-        int incl = nb;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-          const int v = __shfl_up(incl, d);
-          if (lane >= d) incl += v;
-        }
-        for (int b = 0; b < nb; ++b) items[n + incl - nb + b] = row | (b << 8) | (mask << 16);
-        n += __shfl(incl, 63);
-      }
-      // rows whose t this split needs (rows of its adapters), in row order
-      int nr = 0;
-      for (int c0 = 0; c0 < ROWS; c0 += 64) {
-        const int row = c0 + lane;
-        const bool need = row < ROWS && rowrk[row] > 0 && mine[max(leadof[row], 0)];
-        const unsigned long long bl = __ballot(need);
-        if (need) rowlist[nr + __popcll(bl & ((1ull << lane) - 1ull))] = row;
-        nr += __popcll(bl);
-      }
-      if (lane == 0) {
-        meta[0] = n;
-        meta[1] = nr;
-      }
-    }
     __syncthreads();
     const int n_items = __builtin_amdgcn_readfirstlane(meta[0]);
     const int n_rows = __builtin_amdgcn_readfirstlane(meta[1]);
@@ -871,35 +887,40 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
     // (4) t of the rows this split needs -> LDS as bf16 pre-scaled by s_a (zero beyond the
     //     row's rank); the other rows of tbuf are never selected
     const int nel = n_rows * p.r_max;
+    auto put = [&](int idx, float v) {  // element idx of the row list: staged t and the caller's t
+      const int q = idx / p.r_max, i = rowlist[q], j = idx - q * p.r_max;
+      tbuf[i * TSTR + j] = (uint16_t)f32_to_bf16_rne(v * rowsc[i]);
+      if (p.t_out && cb == 0) p.t_out[(long)(row0 + i) * p.r_max + j] = v;
+    };
     for (int base = 0; base < nel; base += 256 * EPI_TE) {
-      float vals[EPI_TE];
       if (p.t_tag) {
-        uint64_t raw[EPI_TE][KP];
         // all loads first (unconditional, clamped addresses), then the tag checks
-        long addr[EPI_TE];
-        bool need[EPI_TE];
+        uint64_t raw[EPI_TE][KP];
 #pragma unroll
         for (int m = 0; m < EPI_TE; ++m) {
           const int idx = min(base + tid + 256 * m, nel - 1);
-          const int q = idx / p.r_max, i = rowlist[q], j = idx - q * p.r_max;
-          need[m] = (base + tid + 256 * m < nel) && j < rowrk[i];
-          addr[m] = (long)(row0 + i) * p.r_max + j;
+          const int q = idx / p.r_max, j = idx - q * p.r_max;
+          const long addr = (long)(row0 + rowlist[q]) * p.r_max + j;
 #pragma unroll
           for (int k2 = 0; k2 < KP; ++k2)
-            raw[m][k2] = ld_agent_u64(p.t_tag + (long)min(k2, p.t_kparts - 1) * p.T * p.r_max + addr[m]);
+            raw[m][k2] = ld_agent_u64(p.t_tag + (long)min(k2, p.t_kparts - 1) * p.T * p.r_max + addr);
         }
 #pragma unroll
         for (int m = 0; m < EPI_TE; ++m) {
+          const int idx = base + tid + 256 * m;
+          if (idx >= nel) continue;
+          const int q = idx / p.r_max, i = rowlist[q], j = idx - q * p.r_max;
+          const long addr = (long)(row0 + i) * p.r_max + j;
           float v = 0.f;
 #pragma unroll
           for (int k2 = 0; k2 < KP; ++k2) {
-            if (need[m] && k2 < p.t_kparts) {
-              const uint64_t w = wait_tag(p.t_tag + (long)k2 * p.T * p.r_max + addr[m], raw[m][k2], tag, p.ctrl,
-                                          p.spin_limit);
+            if (j < rowrk[i] && k2 < p.t_kparts) {
+              const uint64_t w =
+                  wait_tag(p.t_tag + (long)k2 * p.T * p.r_max + addr, raw[m][k2], tag, p.ctrl, p.spin_limit);
               v += __uint_as_float((uint32_t)w);
             }
           }
-          vals[m] = v;
+          put(idx, v);
         }
       } else {
         float raw[EPI_TE];
@@ -912,17 +933,9 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
 #pragma unroll
         for (int m = 0; m < EPI_TE; ++m) {
           const int idx = base + tid + 256 * m;
-          const int q = min(idx, nel - 1) / p.r_max, j = min(idx, nel - 1) - q * p.r_max;
-          vals[m] = (idx < nel && j < rowrk[rowlist[q]]) ? raw[m] : 0.f;
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < EPI_TE; ++m) {
-        const int idx = base + tid + 256 * m;
-        if (idx < nel) {
-          const int q = idx / p.r_max, i = rowlist[q], j = idx - q * p.r_max;
-          tbuf[i * TSTR + j] = (uint16_t)f32_to_bf16_rne(vals[m] * rowsc[i]);
-          if (p.t_out && cb == 0) p.t_out[(long)(row0 + i) * p.r_max + j] = vals[m];
+          if (idx >= nel) continue;
+          const int q = idx / p.r_max, j = idx - q * p.r_max;
+          put(idx, j < rowrk[rowlist[q]] ? raw[m] : 0.f);
         }
       }
     }
