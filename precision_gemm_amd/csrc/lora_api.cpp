@@ -42,8 +42,10 @@ LayerPlan make_plan(int T, int K, int N, int n_ad, int r_max, int fmt, bool fuse
     pl.TT = 1; pl.CT = 2; pl.WC = 1; pl.WK = 4; pl.XQ = false;
   } else if (T <= 64) {
     // 128 channels per workgroup: with the down-projection's workgroups the grid stays
-    // within one workgroup per CU for the widest decode layers
-    pl.TT = 4; pl.CT = (N % 128 == 0) ? 2 : 1; pl.WC = 4; pl.WK = 1; pl.XQ = false;
+    // within one workgroup per CU for the widest decode layers.  x is quantised once by a
+    // pre-pass: every workgroup reads all of x, and MXFP8 halves those reads (measured: the
+    // pass pays for its launch at 64 tokens, not at 16)
+    pl.TT = 4; pl.CT = (N % 128 == 0) ? 2 : 1; pl.WC = 4; pl.WK = 1; pl.XQ = (pl.CT == 2);
   } else {
     // 128 tokens per tile: x is quantised once by a pre-pass (every column tile reads
     // it), and 128 channels per workgroup halve those reads

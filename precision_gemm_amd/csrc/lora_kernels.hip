@@ -33,20 +33,24 @@ namespace lora {
 // Segment builder: seg_indptr (CSR over adapter ids) and sorted_tok (stable order)
 // ======================================================================================
 constexpr int SEG_THREADS = 256;
+constexpr int SEG_CACHE = 4096;  // batches up to this size keep their ids in LDS between the passes
 
 __global__ __launch_bounds__(SEG_THREADS) void k_build_segments(const int* __restrict__ ids, int T, int n_ad,
                                                                 int* __restrict__ seg_indptr,
                                                                 int* __restrict__ sorted_tok, int* __restrict__ err) {
   __shared__ int cnt[MAX_ADAPTERS];
+  __shared__ int ids_s[SEG_CACHE];
   __shared__ int wsum[SEG_THREADS / 64];
   __shared__ int first_bad;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) first_bad = 0x7fffffff;
   for (int a = tid; a < n_ad; a += SEG_THREADS) cnt[a] = 0;
   __syncthreads();
-  // 1. counts (LDS atomics: order-independent)
+  // 1. counts (LDS atomics: order-independent); ids read from memory once
+  const bool cached = T <= SEG_CACHE;
   for (int t = tid; t < T; t += SEG_THREADS) {
     const int a = ids[t];
+    if (cached) ids_s[t] = a;
     if (a >= 0 && a < n_ad) atomicAdd(&cnt[a], 1);
     else atomicMin(&first_bad, t);
   }
@@ -83,7 +87,7 @@ __global__ __launch_bounds__(SEG_THREADS) void k_build_segments(const int* __res
     const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int t0 = 0; t0 < T; t0 += 64) {
       const int t = t0 + lane;
-      const int a = (t < T) ? ids[t] : -1;
+      const int a = (t < T) ? (cached ? ids_s[t] : ids[t]) : -1;
       const bool ok = (a >= 0 && a < n_ad);
       unsigned long long pending = __ballot(ok);
       while (pending) {
@@ -436,10 +440,9 @@ struct ChunkK {
   static constexpr int ROW = KC + 16;  // LDS row stride in bytes
 };
 
-// B-operand loads of the up-projection: a ring of RING items, all but one in flight
-// (shorter for the widest tiles, whose accumulators leave fewer registers)
-template <int TT, int CT>
-constexpr int epi_ring() { return TT >= 8 ? 4 : 8; }
+// B_a^T slices of the up-projection are staged in LDS, in slots of WN x r_max bf16, up to
+// EPI_BSTAGE bytes at a time (one batch: normally all the adapters of the tile)
+constexpr int EPI_BSTAGE = 96 * 1024;
 constexpr int TSTR = MAX_RANK + 8;  // bf16 row stride of the staged t (the pad spreads the rows over LDS banks)
 
 template <int TT, int CT, int WC, int WK>
@@ -452,7 +455,9 @@ struct EpiLayout {
   static constexpr int ROWSC = ROWRK + ROWS * 4;     // float [ROWS]: its scale
   static constexpr int ROWBP = ROWSC + ROWS * 4;     // uint64 [ROWS]: address of its B^T
   static constexpr int ITEMS = ROWBP + ROWS * 8;     // int [2 * ROWS]: up-projection work items
-  static constexpr int LEAD = ITEMS + ROWS * 8;      // int [ROWS]: token tiles of the row's adapter (leader rows)
+  static constexpr int IOFF = ITEMS + ROWS * 8;      // int [2 * ROWS]: LDS offset of the item's B slice
+  static constexpr int LROW = IOFF + ROWS * 8;       // int [ROWS]: leader rows of this split's adapters, in order
+  static constexpr int LEAD = LROW + ROWS * 4;       // int [ROWS]: token tiles of the row's adapter (leader rows)
   static constexpr int LEADOF = LEAD + ROWS * 4;     // int [ROWS]: leader row of the row's adapter (-1: none)
   static constexpr int MINE = LEADOF + ROWS * 4;     // int [ROWS]: leader rows whose adapter this K-split adds
   static constexpr int RLIST = MINE + ROWS * 4;      // int [ROWS]: rows whose t this K-split needs
@@ -473,7 +478,8 @@ struct GemmSmem {
   static constexpr int POST = EpiLayout<TT, CT, WC, WK>::POST;
   static constexpr int M1 = MAIN > RED ? MAIN : RED;
   static constexpr int MD = ((M1 > POST ? M1 : POST) + 15) & ~15;  // metadata area, kept through the loop
-  static constexpr int BYTES = MD + EpiLayout<TT, CT, WC, WK>::MD_BYTES;
+  static constexpr int STG = (MD + EpiLayout<TT, CT, WC, WK>::MD_BYTES + 1023) & ~1023;  // B staging
+  static constexpr int BYTES = STG + EPI_BSTAGE;
 };
 
 template <int FMT, int TT, int CT, int WC, int WK, bool XQ>
@@ -546,10 +552,11 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   constexpr int NX = XQ ? NP : 4 * NBLK;     // 16-byte registers per chunk
   static_assert(NP >= 1 && NBLK >= 1 && NBLK * 256 == ROWS * (KC / 32), "chunk does not split evenly");
   uint4 xr[2][NX];
-  // pre-quantised x: the chunk's scale codes, ROWS x 8 bytes, are one 1 KB load of wave 0
-  // (lane l: rows 2l and 2l+1)
-  static_assert(!XQ || (KC == 256 && ROWS == 128), "scale staging assumes 8 codes per row and 128 rows");
-  uint2 xsc2[2][2];
+  // pre-quantised x: the chunk's scale codes, ROWS x 8 bytes, are one load of wave 0
+  // (lane l: rows SRL*l .. SRL*l + SRL - 1)
+  static_assert(!XQ || (KC == 256 && (ROWS == 64 || ROWS == 128)), "scale staging: 8 codes per row, 64 or 128 rows");
+  constexpr int SRL = (ROWS >= 64) ? ROWS / 64 : 1;
+  uint2 xsc2[2][SRL];
   uint4 wlo[2][SPW][CT], whi[2][SPW][CT];
   int wsc[2][SPW][CT];
 
@@ -581,10 +588,10 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
     }
     if (XQ && wave == 0) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < SRL; ++h) {
         // two 4-byte loads (rows are 4-byte aligned); in a partial last chunk the second
         // may read codes past the row, which are never used (the workspace pads the array)
-        const long tok = min(row0 + 2 * lane + h, p.T - 1);
+        const long tok = min(row0 + SRL * lane + h, p.T - 1);
         const uint32_t* src = reinterpret_cast<const uint32_t*>(p.xsc + tok * (K / 32) + (kc0 >> 5));
         xsc2[buf][h] = make_uint2(src[0], src[1]);
       }
@@ -636,8 +643,13 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
         ss[row * (KC / 32) + k32] = (uint8_t)code;
       }
     }
-    if (XQ && wave == 0)
-      *reinterpret_cast<uint4*>(ss + lane * 16) = make_uint4(xsc2[buf][0].x, xsc2[buf][0].y, xsc2[buf][1].x, xsc2[buf][1].y);
+    if (XQ && wave == 0) {
+      if (SRL == 2)
+        *reinterpret_cast<uint4*>(ss + lane * 16) =
+            make_uint4(xsc2[buf][0].x, xsc2[buf][0].y, xsc2[buf][SRL - 1].x, xsc2[buf][SRL - 1].y);
+      else
+        *reinterpret_cast<uint2*>(ss + lane * 8) = xsc2[buf][0];
+    }
   };
   auto mma_chunk = [&](int buf, int c) {
     const int kc0 = chunk_k0(c);
@@ -695,6 +707,11 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   int* mine = reinterpret_cast<int*>(md + EL::MINE);
   int* rowlist = reinterpret_cast<int*>(md + EL::RLIST);
   int* meta = reinterpret_cast<int*>(md + EL::META);
+  int* ioff = reinterpret_cast<int*>(md + EL::IOFF);
+  int* lrow = reinterpret_cast<int*>(md + EL::LROW);
+  char* stg = smem + GemmSmem<TT, CT, WC, WK>::STG;
+  const int slot = WN * p.r_max * 2;  // bytes of one B slice slot (a multiple of 512)
+  const int spb = EPI_BSTAGE / slot;  // slots per batch (>= 6)
   auto prepare_epilogue = [&]() {
     // (1) adapter, rank, scale and B address of every row; a rank outside the limits
     //     drops the row's adapter term
@@ -732,7 +749,7 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
     // With a K-split the tile's adapters are dealt round-robin (in leader order) to its
     // splits: each split adds the up-projection of its share to its own sum.
     if (wave == 0) {
-      int n = 0, n_lead = 0;
+      int n = 0, n_lead = 0, n_own = 0;
       for (int c0 = 0; c0 < ROWS; c0 += 64) {
         const int row = c0 + lane;
         const int mask = (row < ROWS) ? lead[row] : 0;  // non-zero only for leader rows
@@ -741,6 +758,11 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
         n_lead += __popcll(bl);
         const bool own = mask != 0 && (ord % p.ksplit) == ks;
         if (own) mine[row] = 1;
+        // this split's k-th adapter: B slice in slot k % spb of batch k / spb
+        const unsigned long long bo = __ballot(own);
+        const int k = n_own + __popcll(bo & ((1ull << lane) - 1ull));
+        n_own += __popcll(bo);
+        if (own) lrow[k] = row;
         const int nb = own ? ((rowrk[row] + 31) >> 5) : 0;
         int incl = nb;
   #pragma unroll
@@ -748,7 +770,10 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
           const int v = __shfl_up(incl, d);
           if (lane >= d) incl += v;
         }
-        for (int b = 0; b < nb; ++b) items[n + incl - nb + b] = row | (b << 8) | (mask << 16);
+        for (int b = 0; b < nb; ++b) {
+          items[n + incl - nb + b] = row | (b << 8) | (mask << 9) | ((k / spb) << 17);
+          ioff[n + incl - nb + b] = (k % spb) * slot;
+        }
         n += __shfl(incl, 63);
       }
       // rows whose t this split needs (rows of its adapters), in row order
@@ -763,6 +788,7 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
       if (lane == 0) {
         meta[0] = n;
         meta[1] = nr;
+        meta[2] = n_own;
       }
     }
   };
@@ -832,58 +858,64 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
     __syncthreads();
     const int n_items = __builtin_amdgcn_readfirstlane(meta[0]);
     const int n_rows = __builtin_amdgcn_readfirstlane(meta[1]);
-    // items of this wave: wk, wk + WK, ... (the waves sharing columns split the items)
-    const int cnt = (n_items > wk) ? (n_items - wk + WK - 1) / WK : 0;
+    const int n_own = __builtin_amdgcn_readfirstlane(meta[2]);
+    const int n_batch = (n_own + spb - 1) / spb;
 
-    // B operands straight from HBM into a ring of registers: lane (li, g) of column tile
-    // ct needs B_a^T[n][j .. j+7] with n its column and j = 32*block + 8g, 16 contiguous
-    // bytes.  Addresses are clamped into the row (j <= r - 8); lanes with j >= r get
-    // zero operands below.  Items past the end reload the last one.
-    constexpr int RING = epi_ring<TT, CT>();
-    uint4 bq[RING][CT];
-    auto issue = [&](int slot_dummy, int m, uint4 (&dst)[CT]) {
-      (void)slot_dummy;
-      const int it = items[min(wk + WK * m, n_items - 1)];
-      const int row = it & 255, jb = (it >> 8) & 255;
-      const int r = __builtin_amdgcn_readfirstlane(rowrk[row]);
-      const uint64_t bp = rowbp[row];
-      const uint64_t bpu = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(bp >> 32)) << 32) |
-                           (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bp);
-      const uint16_t* Bt = reinterpret_cast<const uint16_t*>(bpu);
-      const int j = min(jb * 32 + 8 * g, r - 8);
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) dst[ct] = ldg16(Bt + (long)(nw0 + ct * 16 + li) * r + j);
+    // B_a^T rows n_tile0 .. n_tile0 + WN - 1 of one adapter are WN * r_a contiguous bf16;
+    // the waves copy the slices of a batch straight into their LDS slots (16 bytes per
+    // lane, 1 KB per wave load), leader k of the batch by wave k % 4
+    auto stage_b = [&](int b) {
+      const int k1 = min(n_own, (b + 1) * spb);
+      for (int k = b * spb + wave; k < k1; k += 4) {
+        const int row = lrow[k];
+        const int r = __builtin_amdgcn_readfirstlane(rowrk[row]);
+        const uint64_t bp = rowbp[row];
+        const uint64_t bpu = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(bp >> 32)) << 32) |
+                             (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bp);
+        const char* src = reinterpret_cast<const char*>(bpu) + (long)n_tile0 * r * 2;
+        char* dst = stg + (k % spb) * slot;
+        const int bytes = WN * r * 2;
+        for (int c = 0; c < bytes; c += 1024) {
+          if (c + lane * 16 < bytes)
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + c + lane * 16),
+                                             (__attribute__((address_space(3))) void*)(dst + c), 16, 0, 0);
+        }
+      }
     };
     v4f lacc[TT][CT];
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) lacc[tt][ct] = v4f{0.f, 0.f, 0.f, 0.f};
-    auto consume = [&](int m, const uint4 (&src)[CT]) {
-      const int it = __builtin_amdgcn_readfirstlane(items[wk + WK * m]);
-      const int row = it & 255, jb = (it >> 8) & 255, mask = it >> 16;
-      const int a = __builtin_amdgcn_readfirstlane(rowad[row]);
-      const int r = __builtin_amdgcn_readfirstlane(rowrk[row]);
+    // one bf16 MFMA per item, token tile and column tile; B operands from the staged slice
+    // (lane (li, g): B_a^T[n][j .. j+7], j = 32*block + 8g, zero for j >= r_a).  The item
+    // descriptors of 64 items at a time sit one per lane and are read with readlane, and the
+    // adapters of the lane's own rows are kept in registers, so an item issues its operand
+    // reads without a chain of dependent LDS loads.
+    int myad[TT];
+    auto consume = [&](int it, int off, int a, int r) {  // wave-uniform descriptor
+      const int jb = (it >> 8) & 1, mask = (it >> 9) & 255;
       const int j = jb * 32 + 8 * g;  // <= 56
       const bool valid = j < r;
+      const int jc = min(j, r - 8);
       uint4 bop[CT];
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) bop[ct] = valid ? src[ct] : zero4();
+      for (int ct = 0; ct < CT; ++ct) {
+        const int nl = wc * CT * 16 + ct * 16 + li;
+        const uint4 bv = *reinterpret_cast<const uint4*>(stg + off + (nl * r + jc) * 2);
+        bop[ct] = valid ? bv : zero4();
+      }
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) {
         if (!((mask >> tt) & 1)) continue;  // uniform: adapter absent from this token tile
-        const int myrow = tt * 16 + li;
-        const uint4 tv = *reinterpret_cast<const uint4*>(tbuf + myrow * TSTR + j);
-        const uint4 aop = (valid && rowad[myrow] == a) ? tv : zero4();
+        const uint4 tv = *reinterpret_cast<const uint4*>(tbuf + (tt * 16 + li) * TSTR + j);
+        const uint4 aop = (valid && myad[tt] == a) ? tv : zero4();
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) lacc[tt][ct] = mfma_bf16_16x16x32(aop, bop[ct], lacc[tt][ct]);
       }
     };
-    // (3) the first RING - 1 items' B loads go out before the t loads
-    if (cnt > 0) {
-#pragma unroll
-      for (int d = 0; d < RING - 1; ++d) issue(d, d, bq[d]);
-    }
+    // (3) the first batch of B slices goes out before the t loads
+    if (n_batch > 0) stage_b(0);
     // (4) t of the rows this split needs -> LDS as bf16 pre-scaled by s_a (zero beyond the
     //     row's rank); the other rows of tbuf are never selected
     const int nel = n_rows * p.r_max;
@@ -939,15 +971,31 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
         }
       }
     }
-    __syncthreads();
-    // (5) one bf16 MFMA per item and column tile, RING - 1 items of B in flight
-    for (int m0 = 0; m0 < cnt; m0 += RING) {
+    // (5) per batch: wait for this wave's copies, then every wave multiplies its items
+    //     (the waves sharing columns split them: item i goes to wave i % WK)
+    for (int b = 0; b < n_batch; ++b) {
+      if (b > 0) stage_b(b);
+      wait_stores();  // all of this wave's memory operations, the LDS copies included
+      __syncthreads();
+      if (b == 0) {
 #pragma unroll
-      for (int d = 0; d < RING; ++d) {
-        issue(0, m0 + d + RING - 1, bq[(d + RING - 1) % RING]);
-        if (m0 + d >= cnt) break;
-        consume(m0 + d, bq[d]);
+        for (int tt = 0; tt < TT; ++tt) myad[tt] = rowad[tt * 16 + li];
       }
+      // this wave's items wk, wk + WK, ...: descriptors of 64 of them per lane load
+      for (int i0 = wk; i0 < n_items; i0 += 64 * WK) {
+        const int iq = min(i0 + WK * lane, n_items - 1);
+        const int it_l = items[iq], off_l = ioff[iq];
+        const int row_l = it_l & 255;
+        const int a_l = rowad[row_l], r_l = rowrk[row_l];
+        const int n_here = min(64, (n_items - i0 + WK - 1) / WK);
+        for (int q = 0; q < n_here; ++q) {
+          const int it = __builtin_amdgcn_readlane(it_l, q);
+          if ((it >> 17) != b) continue;  // uniform
+          consume(it, __builtin_amdgcn_readlane(off_l, q), __builtin_amdgcn_readlane(a_l, q),
+                  __builtin_amdgcn_readlane(r_l, q));
+        }
+      }
+      __syncthreads();  // slots are refilled by the next batch
     }
     // (6) the k-waves' adapter sums, in wave order, join the base in the waves with wk == 0
     if (WK > 1) {
@@ -1103,6 +1151,7 @@ static hipError_t launch_layer_f(const LayerPlan& pl, int grid, hipStream_t stre
   LORA_LAYER_CASE(1, 2, 1, 4, false, 0, 1, 1, 4)
   LORA_LAYER_CASE(4, 1, 4, 1, false, 0, 1, 1, 4)
   LORA_LAYER_CASE(4, 2, 4, 1, false, 0, 1, 1, 4)
+  LORA_LAYER_CASE(4, 2, 4, 1, true, 0, 1, 1, 4)
   LORA_LAYER_CASE(8, 1, 4, 1, true, 0, 1, 1, 4)
   LORA_LAYER_CASE(8, 2, 4, 1, true, 0, 1, 1, 4)
   LORA_LAYER_CASE(8, 1, 4, 1, true, 1, 4, 2, 1)
