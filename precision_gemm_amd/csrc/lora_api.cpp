@@ -51,6 +51,9 @@ LayerPlan make_plan(int T, int K, int N, int n_ad, int r_max, int fmt, bool fuse
     // it), and 128 channels per workgroup halve those reads
     pl.TT = 8; pl.WC = 4; pl.WK = 1; pl.XQ = true;
     pl.CT = (N % 128 == 0) ? 2 : 1;
+    // prefill: 64-token tiles, two workgroups per CU, so that one workgroup's start-up and
+    // epilogue latency overlaps the other's main loop
+    if (T > 128 && pl.CT == 2) pl.TT = 4;
   }
   pl.KC = (pl.TT == 1) ? 2048 : ((pl.TT <= 4 && pl.CT == 1) ? 512 : 256);
   const int WN = pl.WC * pl.CT * 16;
@@ -60,7 +63,7 @@ LayerPlan make_plan(int T, int K, int N, int n_ad, int r_max, int fmt, bool fuse
   const int max_split = std::max(1, K / pl.KC);
   // split K over workgroups only when there are too few tiles to fill the GPU: the
   // split-K hand-over adds dependent memory round trips to the critical path
-  int ks = (tiles >= 128) ? 1 : std::min(max_split, ceil_div(512, tiles));
+  int ks = (tiles >= 128) ? 1 : std::min(max_split, ceil_div(384, tiles));
   ks = std::max(ks, 1);
   pl.krange = ceil_div(ceil_div(K, ks), pl.KC) * pl.KC;
   pl.ksplit = ceil_div(K, pl.krange);
@@ -74,7 +77,8 @@ LayerPlan make_plan(int T, int K, int N, int n_ad, int r_max, int fmt, bool fuse
     pl.s_ntblk = 1;
     pl.s_jper = 1;
     pl.s_njg = ceil_div(r_max, 16);
-    // latency-bound single-tile decode: split K so that t is ready early
+    // latency-bound single-tile decode: split K so that t is ready early (measured: for the
+    // 128-token shapes K-parts only add per-item start-up round trips)
     if (fused && T <= 16) kparts = std::min(4, std::max(1, K / 1024));
   } else {
     pl.s_cfg = 1;

@@ -441,8 +441,10 @@ struct ChunkK {
 };
 
 // B_a^T slices of the up-projection are staged in LDS, in slots of WN x r_max bf16, up to
-// EPI_BSTAGE bytes at a time (one batch: normally all the adapters of the tile)
-constexpr int EPI_BSTAGE = 96 * 1024;
+// a budget of bytes at a time (one batch: normally all the adapters of the tile).  Kernels
+// that run two workgroups per CU stage less (each workgroup has half the LDS).
+template <int OCC>
+constexpr int epi_bstage() { return OCC == 2 ? 32 * 1024 : 96 * 1024; }
 constexpr int TSTR = MAX_RANK + 8;  // bf16 row stride of the staged t (the pad spreads the rows over LDS banks)
 
 template <int TT, int CT, int WC, int WK>
@@ -470,7 +472,7 @@ struct EpiLayout {
   static_assert(ROWBP % 8 == 0 && LRED % 16 == 0, "epilogue LDS alignment");
 };
 
-template <int TT, int CT, int WC, int WK>
+template <int TT, int CT, int WC, int WK, int OCC>
 struct GemmSmem {
   using CK = ChunkK<TT, CT>;
   static constexpr int MAIN = TT * 16 * CK::ROW + TT * 16 * (CK::KC / 32);
@@ -479,10 +481,10 @@ struct GemmSmem {
   static constexpr int M1 = MAIN > RED ? MAIN : RED;
   static constexpr int MD = ((M1 > POST ? M1 : POST) + 15) & ~15;  // metadata area, kept through the loop
   static constexpr int STG = (MD + EpiLayout<TT, CT, WC, WK>::MD_BYTES + 1023) & ~1023;  // B staging
-  static constexpr int BYTES = STG + EPI_BSTAGE;
+  static constexpr int BYTES = STG + epi_bstage<OCC>();
 };
 
-template <int FMT, int TT, int CT, int WC, int WK, bool XQ>
+template <int FMT, int TT, int CT, int WC, int WK, bool XQ, int KPT, int OCC>
 __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* smem, int e, int* lds_epoch, int* started) {
   using CK = ChunkK<TT, CT>;
   constexpr int KC = CK::KC, STEPS = CK::STEPS, ROW = CK::ROW;
@@ -490,9 +492,9 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   constexpr int WN = WC * CT * 16;
   constexpr int FMTB = (FMT == LORA_W_FP8_E4M3) ? 0 : 4;
   constexpr int ROWS = TT * 16;
-  constexpr int KP = (TT == 1) ? 4 : 1;  // K-parts of t the epilogue adds (the host plan stays within it)
-  // t elements per thread per gather batch: the whole block's t (ROWS x 64) in one batch,
-  // so that the gather costs one memory round trip
+  constexpr int KP = KPT;  // K-parts of t the epilogue adds (the host plan stays within it)
+  // t elements per thread per gather batch: with one K-part the whole block's t (ROWS x 64)
+  // in one batch, so that the gather costs one memory round trip
   constexpr int EPI_TE = (KP == 1) ? (ROWS * MAX_RANK + 255) / 256 : 8;
   static_assert(STEPS % WK == 0, "k-steps per chunk must split evenly over the k-waves");
   uint8_t* xs = reinterpret_cast<uint8_t*>(smem);  // [ROWS][ROW]
@@ -551,14 +553,16 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   constexpr int NBLK = ROWS * (KC / 32) / 256;  // bf16 32-blocks per thread and chunk
   constexpr int NX = XQ ? NP : 4 * NBLK;     // 16-byte registers per chunk
   static_assert(NP >= 1 && NBLK >= 1 && NBLK * 256 == ROWS * (KC / 32), "chunk does not split evenly");
-  uint4 xr[2][NX];
+  // chunks in flight (measured on the 64-token tile: three or four are no faster than two)
+  constexpr int NBUF = 2;
+  uint4 xr[NBUF][NX];
   // pre-quantised x: the chunk's scale codes, ROWS x 8 bytes, are one load of wave 0
   // (lane l: rows SRL*l .. SRL*l + SRL - 1)
   static_assert(!XQ || (KC == 256 && (ROWS == 64 || ROWS == 128)), "scale staging: 8 codes per row, 64 or 128 rows");
   constexpr int SRL = (ROWS >= 64) ? ROWS / 64 : 1;
-  uint2 xsc2[2][SRL];
-  uint4 wlo[2][SPW][CT], whi[2][SPW][CT];
-  int wsc[2][SPW][CT];
+  uint2 xsc2[NBUF][SRL];
+  uint4 wlo[NBUF][SPW][CT], whi[NBUF][SPW][CT];
+  int wsc[NBUF][SPW][CT];
 
   auto load_x = [&](int buf, int c) {
     const int kc0 = chunk_k0(c);
@@ -674,13 +678,17 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
     }
   };
 
-  // chunks 0 and 1 in flight before anything waits; chunk c+2 is issued while chunk c is
-  // multiplied.  x of a chunk is always issued before its W (loads retire in order).
+  // chunks 0 .. NBUF-1 in flight before anything waits; chunk c + NBUF is issued into the
+  // buffer of chunk c while chunk c is multiplied (x once it is staged, W after its MFMAs).
+  // x of a chunk is always issued before its W (loads retire in order).
   load_x(0, 0);
   load_w(0, 0);
-  if (nchunks > 1) {
-    load_x(1, 1);
-    load_w(1, 1);
+#pragma unroll
+  for (int u = 1; u < NBUF; ++u) {
+    if (u < nchunks) {
+      load_x(u, u);
+      load_w(u, u);
+    }
   }
   const bool row_ok = p.lora && tid < ROWS && row0 + tid < p.T && id_raw >= 0 &&
                       id_raw < p.n_ad;
@@ -696,7 +704,7 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   // up-projection metadata (adapter list, work items, rows whose t is needed), built once
   // the first chunk is multiplied: its LDS latency then overlaps the loads in flight
   using EL = EpiLayout<TT, CT, WC, WK>;
-  char* md = smem + GemmSmem<TT, CT, WC, WK>::MD;
+  char* md = smem + GemmSmem<TT, CT, WC, WK, OCC>::MD;
   int* rowad = reinterpret_cast<int*>(md + EL::ROWAD);
   int* rowrk = reinterpret_cast<int*>(md + EL::ROWRK);
   float* rowsc = reinterpret_cast<float*>(md + EL::ROWSC);
@@ -709,9 +717,9 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   int* meta = reinterpret_cast<int*>(md + EL::META);
   int* ioff = reinterpret_cast<int*>(md + EL::IOFF);
   int* lrow = reinterpret_cast<int*>(md + EL::LROW);
-  char* stg = smem + GemmSmem<TT, CT, WC, WK>::STG;
+  char* stg = smem + GemmSmem<TT, CT, WC, WK, OCC>::STG;
   const int slot = WN * p.r_max * 2;  // bytes of one B slice slot (a multiple of 512)
-  const int spb = EPI_BSTAGE / slot;  // slots per batch (>= 6)
+  const int spb = epi_bstage<OCC>() / slot;  // slots per batch (>= 2)
   auto prepare_epilogue = [&]() {
     // (1) adapter, rank, scale and B address of every row; a rank outside the limits
     //     drops the row's adapter term
@@ -793,24 +801,21 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
     }
   };
 
-  for (int c = 0; c < nchunks; c += 2) {
-    stage_x(0);
-    __syncthreads();
-    if (c + 2 < nchunks) load_x(0, c + 2);
-    mma_chunk(0, c);
-    if (c + 2 < nchunks) load_w(0, c + 2);
-    __syncthreads();
-    if (c == 0 && p.lora) {
-      prepare_epilogue();
+  for (int c = 0; c < nchunks; c += NBUF) {
+#pragma unroll
+    for (int u = 0; u < NBUF; ++u) {
+      if (c + u >= nchunks) break;
+      stage_x(u);
       __syncthreads();
+      if (c + u + NBUF < nchunks) load_x(u, c + u + NBUF);
+      mma_chunk(u, c + u);
+      if (c + u + NBUF < nchunks) load_w(u, c + u + NBUF);
+      __syncthreads();
+      if (u == 0 && c == 0 && p.lora) {
+        prepare_epilogue();
+        __syncthreads();
+      }
     }
-    if (c + 1 >= nchunks) break;
-    stage_x(1);
-    __syncthreads();
-    if (c + 3 < nchunks) load_x(1, c + 3);
-    mma_chunk(1, c + 1);
-    if (c + 3 < nchunks) load_w(1, c + 3);
-    __syncthreads();
   }
   // publish the launch epoch only now: waiting for it earlier would stall wave 0
   *started = wg_epoch_publish(p.ctrl, e, lds_epoch);
@@ -1097,8 +1102,11 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   }
 }
 
-template <int FMT, int TT, int CT, int WC, int WK, bool XQ, int TG, int JP, int U>
-__global__ __launch_bounds__(256) void k_layer(ShrinkParams sp, GemmParams gp) {
+// OCC: workgroups per CU the registers are budgeted for (2 for the 64-token prefill tile,
+// so that one workgroup's epilogue and start-up latency overlap another's main loop)
+template <int FMT, int TT, int CT, int WC, int WK, bool XQ, int TG, int JP, int U, int OCC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void k_layer(ShrinkParams sp,
+                                                                                                GemmParams gp) {
   extern __shared__ __align__(16) char smem[];
   __shared__ int lds_epoch;
   const int e = wg_epoch_load(gp.ctrl);
@@ -1107,7 +1115,9 @@ __global__ __launch_bounds__(256) void k_layer(ShrinkParams sp, GemmParams gp) {
   if (b < gp.n_shrink) {
     shrink_item<TG, JP, U>(sp, b, smem, gp.ctrl, e, &lds_epoch, &started);
   } else {
-    gemm_item<FMT, TT, CT, WC, WK, XQ>(gp, b - gp.n_shrink, smem, e, &lds_epoch, &started);
+    // K-parts of t: the single-tile decode down-projection splits K
+    constexpr int KPT = (TT == 1) ? 4 : 1;
+    gemm_item<FMT, TT, CT, WC, WK, XQ, KPT, OCC>(gp, b - gp.n_shrink, smem, e, &lds_epoch, &started);
   }
   wg_epoch_end(gp.ctrl, e, started);
 }
@@ -1131,31 +1141,32 @@ static hipError_t launch_k(KernelT kern, int grid, size_t smem, hipStream_t stre
   return hipGetLastError();
 }
 
-template <int FMT, int TT, int CT, int WC, int WK, bool XQ, int TG, int JP, int U>
+template <int FMT, int TT, int CT, int WC, int WK, bool XQ, int TG, int JP, int U, int OCC>
 static hipError_t launch_layer_t(const LayerPlan& pl, int grid, hipStream_t stream, const ShrinkParams& sp,
                                  const GemmParams& gp) {
-  const size_t sm =
-      std::max((size_t)GemmSmem<TT, CT, WC, WK>::BYTES, gp.n_shrink > 0 ? shrink_smem<TG, JP, U>() : (size_t)0);
-  return launch_k(k_layer<FMT, TT, CT, WC, WK, XQ, TG, JP, U>, grid, sm, stream, sp, gp);
+  const size_t sm = std::max((size_t)GemmSmem<TT, CT, WC, WK, OCC>::BYTES,
+                             gp.n_shrink > 0 ? shrink_smem<TG, JP, U>() : (size_t)0);
+  return launch_k(k_layer<FMT, TT, CT, WC, WK, XQ, TG, JP, U, OCC>, grid, sm, stream, sp, gp);
 }
 
-// GEMM tile (TT, CT, WC, WK, XQ) and down-projection shape: decode (cfg 0: one 16-rank
-// tile, two-step prefetch) or prefill (cfg 1: four token tiles, two rank tiles)
-#define LORA_LAYER_CASE(TT_, CT_, WC_, WK_, XQ_, CFG_, TG_, JP_, U_)                                      \
+// GEMM tile (TT, CT, WC, WK, XQ), down-projection shape (decode, cfg 0: one 16-rank tile,
+// four-step prefetch; prefill, cfg 1: four token tiles, two rank tiles) and workgroups per CU
+#define LORA_LAYER_CASE(TT_, CT_, WC_, WK_, XQ_, CFG_, TG_, JP_, U_, OCC_)                                \
   if (pl.TT == TT_ && pl.CT == CT_ && pl.WC == WC_ && pl.WK == WK_ && pl.XQ == XQ_ && pl.s_cfg == CFG_) \
-    return launch_layer_t<FMT, TT_, CT_, WC_, WK_, XQ_, TG_, JP_, U_>(pl, grid, stream, sp, gp);
+    return launch_layer_t<FMT, TT_, CT_, WC_, WK_, XQ_, TG_, JP_, U_, OCC_>(pl, grid, stream, sp, gp);
 
 template <int FMT>
 static hipError_t launch_layer_f(const LayerPlan& pl, int grid, hipStream_t stream, const ShrinkParams& sp,
                                  const GemmParams& gp) {
-  LORA_LAYER_CASE(1, 2, 1, 4, false, 0, 1, 1, 4)
-  LORA_LAYER_CASE(4, 1, 4, 1, false, 0, 1, 1, 4)
-  LORA_LAYER_CASE(4, 2, 4, 1, false, 0, 1, 1, 4)
-  LORA_LAYER_CASE(4, 2, 4, 1, true, 0, 1, 1, 4)
-  LORA_LAYER_CASE(8, 1, 4, 1, true, 0, 1, 1, 4)
-  LORA_LAYER_CASE(8, 2, 4, 1, true, 0, 1, 1, 4)
-  LORA_LAYER_CASE(8, 1, 4, 1, true, 1, 4, 2, 1)
-  LORA_LAYER_CASE(8, 2, 4, 1, true, 1, 4, 2, 1)
+  LORA_LAYER_CASE(1, 2, 1, 4, false, 0, 1, 1, 4, 1)
+  LORA_LAYER_CASE(4, 1, 4, 1, false, 0, 1, 1, 4, 1)
+  LORA_LAYER_CASE(4, 2, 4, 1, false, 0, 1, 1, 4, 1)
+  LORA_LAYER_CASE(4, 2, 4, 1, true, 0, 1, 1, 4, 1)
+  LORA_LAYER_CASE(8, 1, 4, 1, true, 0, 1, 1, 4, 1)
+  LORA_LAYER_CASE(8, 2, 4, 1, true, 0, 1, 1, 4, 1)
+  LORA_LAYER_CASE(8, 1, 4, 1, true, 1, 4, 2, 1, 1)
+  LORA_LAYER_CASE(8, 2, 4, 1, true, 1, 4, 2, 1, 1)
+  LORA_LAYER_CASE(4, 2, 4, 1, true, 1, 4, 2, 1, 2)
   return hipErrorInvalidValue;
 }
 #undef LORA_LAYER_CASE
