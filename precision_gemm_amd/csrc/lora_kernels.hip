@@ -493,9 +493,9 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   constexpr int FMTB = (FMT == LORA_W_FP8_E4M3) ? 0 : 4;
   constexpr int ROWS = TT * 16;
   constexpr int KP = KPT;  // K-parts of t the epilogue adds (the host plan stays within it)
-  // t elements per thread per gather batch: with one K-part the whole block's t (ROWS x 64)
-  // in one batch, so that the gather costs one memory round trip
-  constexpr int EPI_TE = (KP == 1) ? (ROWS * MAX_RANK + 255) / 256 : 8;
+  // t elements per thread per gather batch: the whole block's t (ROWS x 64) in one batch,
+  // so that the gather costs one memory round trip
+  constexpr int EPI_TE = (ROWS * MAX_RANK + 255) / 256;
   static_assert(STEPS % WK == 0, "k-steps per chunk must split evenly over the k-waves");
   uint8_t* xs = reinterpret_cast<uint8_t*>(smem);  // [ROWS][ROW]
   uint8_t* ss = xs + ROWS * ROW;                    // [ROWS][KC/32]
@@ -530,6 +530,10 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) acc[tt][ct] = v4f{0.f, 0.f, 0.f, 0.f};
 
+  // FP8 channel scales of the lane's columns, needed only in the epilogue
+  float chan_s[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) chan_s[ct] = (FMT == LORA_W_FP8_E4M3) ? p.ws_fp8[nw0 + ct * 16 + li] : 1.f;
   // adapter of row `tid` of the token block for the epilogue: the id is loaded before the
   // bulk loads, its rank, scale and B address right after the first ones (loads retire
   // in order, so none of these waits for more than the id)
@@ -817,6 +821,101 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
       }
     }
   }
+  // ---- up-projection loads go out as soon as the main loop ends (before the k-wave sums
+  //      and the channel scale): the first batch of B slices into LDS, then t of the rows
+  //      this split needs (all of them fit one batch of EPI_TE per thread)
+  uint16_t* tbuf = reinterpret_cast<uint16_t*>(smem + EL::TB);
+  float* lred = reinterpret_cast<float*>(smem + EL::LRED);
+  const int n_items = p.lora ? __builtin_amdgcn_readfirstlane(meta[0]) : 0;
+  const int n_rows = p.lora ? __builtin_amdgcn_readfirstlane(meta[1]) : 0;
+  const int n_own = p.lora ? __builtin_amdgcn_readfirstlane(meta[2]) : 0;
+  const int n_batch = (n_own + spb - 1) / spb;
+
+  // B_a^T rows n_tile0 .. n_tile0 + WN - 1 of one adapter are WN * r_a contiguous bf16;
+  // the waves copy the slices of a batch straight into their LDS slots (16 bytes per
+  // lane, 1 KB per wave load), leader k of the batch by wave k % 4
+  auto stage_b = [&](int b) {
+    const int k1 = min(n_own, (b + 1) * spb);
+    for (int k = b * spb + wave; k < k1; k += 4) {
+      const int row = lrow[k];
+      const int r = __builtin_amdgcn_readfirstlane(rowrk[row]);
+      const uint64_t bp = rowbp[row];
+      const uint64_t bpu = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(bp >> 32)) << 32) |
+                           (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bp);
+      const char* src = reinterpret_cast<const char*>(bpu) + (long)n_tile0 * r * 2;
+      char* dst = stg + (k % spb) * slot;
+      const int bytes = WN * r * 2;
+      for (int c = 0; c < bytes; c += 1024) {
+        if (c + lane * 16 < bytes)
+          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + c + lane * 16),
+                                           (__attribute__((address_space(3))) void*)(dst + c), 16, 0, 0);
+      }
+    }
+  };
+  v4f lacc[TT][CT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) lacc[tt][ct] = v4f{0.f, 0.f, 0.f, 0.f};
+  // one bf16 MFMA per item, token tile and column tile; B operands from the staged slice
+  // (lane (li, g): B_a^T[n][j .. j+7], j = 32*block + 8g, zero for j >= r_a).  The item
+  // descriptors of 64 items at a time sit one per lane and are read with readlane, and the
+  // adapters of the lane's own rows are kept in registers, so an item issues its operand
+  // reads without a chain of dependent LDS loads.
+  int myad[TT];
+  auto consume = [&](int it, int off, int a, int r) {  // wave-uniform descriptor
+    const int jb = (it >> 8) & 1, mask = (it >> 9) & 255;
+    const int j = jb * 32 + 8 * g;  // <= 56
+    const bool valid = j < r;
+    const int jc = min(j, r - 8);
+    uint4 bop[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const int nl = wc * CT * 16 + ct * 16 + li;
+      const uint4 bv = *reinterpret_cast<const uint4*>(stg + off + (nl * r + jc) * 2);
+      bop[ct] = valid ? bv : zero4();
+    }
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      if (!((mask >> tt) & 1)) continue;  // uniform: adapter absent from this token tile
+      const uint4 tv = *reinterpret_cast<const uint4*>(tbuf + (tt * 16 + li) * TSTR + j);
+      const uint4 aop = (valid && myad[tt] == a) ? tv : zero4();
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) lacc[tt][ct] = mfma_bf16_16x16x32(aop, bop[ct], lacc[tt][ct]);
+    }
+  };
+  const int nel = n_rows * p.r_max;
+  auto put = [&](int idx, float v) {  // element idx of the row list: staged t and the caller's t
+    const int q = idx / p.r_max, i = rowlist[q], j = idx - q * p.r_max;
+    tbuf[i * TSTR + j] = (uint16_t)f32_to_bf16_rne(v * rowsc[i]);
+    if (p.t_out && cb == 0) p.t_out[(long)(row0 + i) * p.r_max + j] = v;
+  };
+  uint64_t traw[EPI_TE][KP];
+  float tpl[EPI_TE];
+  if (p.lora) {
+    if (n_batch > 0) stage_b(0);
+    if (nel == 0) {
+      // no rows: nothing to load
+    } else if (p.t_tag) {  // unconditional loads from clamped addresses; tags checked later
+#pragma unroll
+      for (int m = 0; m < EPI_TE; ++m) {
+        const int idx = min(tid + 256 * m, nel - 1);
+        const int q = idx / p.r_max, j = idx - q * p.r_max;
+        const long addr = (long)(row0 + rowlist[q]) * p.r_max + j;
+#pragma unroll
+        for (int k2 = 0; k2 < KP; ++k2)
+          traw[m][k2] = ld_agent_u64(p.t_tag + (long)min(k2, p.t_kparts - 1) * p.T * p.r_max + addr);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < EPI_TE; ++m) {
+        const int idx = min(tid + 256 * m, nel - 1);
+        const int q = idx / p.r_max;
+        tpl[m] = p.t[(long)(row0 + rowlist[q]) * p.r_max + (idx - q * p.r_max)];
+      }
+    }
+  }
+
   // publish the launch epoch only now: waiting for it earlier would stall wave 0
   *started = wg_epoch_publish(p.ctrl, e, lds_epoch);
   __syncthreads();
@@ -850,130 +949,40 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   if (FMT == LORA_W_FP8_E4M3 && wk == 0) {
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
-      const float sw = p.ws_fp8[nw0 + ct * 16 + li];
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt) acc[tt][ct] *= sw;
+      for (int tt = 0; tt < TT; ++tt) acc[tt][ct] *= chan_s[ct];
     }
   }
 
   // ---- epilogue: adapter up-projection (this K-split's share of the adapters)
   if (p.lora) {
-    uint16_t* tbuf = reinterpret_cast<uint16_t*>(smem + EL::TB);
-    float* lred = reinterpret_cast<float*>(smem + EL::LRED);
-    __syncthreads();
-    const int n_items = __builtin_amdgcn_readfirstlane(meta[0]);
-    const int n_rows = __builtin_amdgcn_readfirstlane(meta[1]);
-    const int n_own = __builtin_amdgcn_readfirstlane(meta[2]);
-    const int n_batch = (n_own + spb - 1) / spb;
-
-    // B_a^T rows n_tile0 .. n_tile0 + WN - 1 of one adapter are WN * r_a contiguous bf16;
-    // the waves copy the slices of a batch straight into their LDS slots (16 bytes per
-    // lane, 1 KB per wave load), leader k of the batch by wave k % 4
-    auto stage_b = [&](int b) {
-      const int k1 = min(n_own, (b + 1) * spb);
-      for (int k = b * spb + wave; k < k1; k += 4) {
-        const int row = lrow[k];
-        const int r = __builtin_amdgcn_readfirstlane(rowrk[row]);
-        const uint64_t bp = rowbp[row];
-        const uint64_t bpu = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(bp >> 32)) << 32) |
-                             (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bp);
-        const char* src = reinterpret_cast<const char*>(bpu) + (long)n_tile0 * r * 2;
-        char* dst = stg + (k % spb) * slot;
-        const int bytes = WN * r * 2;
-        for (int c = 0; c < bytes; c += 1024) {
-          if (c + lane * 16 < bytes)
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + c + lane * 16),
-                                             (__attribute__((address_space(3))) void*)(dst + c), 16, 0, 0);
-        }
-      }
-    };
-    v4f lacc[TT][CT];
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) lacc[tt][ct] = v4f{0.f, 0.f, 0.f, 0.f};
-    // one bf16 MFMA per item, token tile and column tile; B operands from the staged slice
-    // (lane (li, g): B_a^T[n][j .. j+7], j = 32*block + 8g, zero for j >= r_a).  The item
-    // descriptors of 64 items at a time sit one per lane and are read with readlane, and the
-    // adapters of the lane's own rows are kept in registers, so an item issues its operand
-    // reads without a chain of dependent LDS loads.
-    int myad[TT];
-    auto consume = [&](int it, int off, int a, int r) {  // wave-uniform descriptor
-      const int jb = (it >> 8) & 1, mask = (it >> 9) & 255;
-      const int j = jb * 32 + 8 * g;  // <= 56
-      const bool valid = j < r;
-      const int jc = min(j, r - 8);
-      uint4 bop[CT];
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        const int nl = wc * CT * 16 + ct * 16 + li;
-        const uint4 bv = *reinterpret_cast<const uint4*>(stg + off + (nl * r + jc) * 2);
-        bop[ct] = valid ? bv : zero4();
-      }
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) {
-        if (!((mask >> tt) & 1)) continue;  // uniform: adapter absent from this token tile
-        const uint4 tv = *reinterpret_cast<const uint4*>(tbuf + (tt * 16 + li) * TSTR + j);
-        const uint4 aop = (valid && myad[tt] == a) ? tv : zero4();
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) lacc[tt][ct] = mfma_bf16_16x16x32(aop, bop[ct], lacc[tt][ct]);
-      }
-    };
-    // (3) the first batch of B slices goes out before the t loads
-    if (n_batch > 0) stage_b(0);
     // (4) t of the rows this split needs -> LDS as bf16 pre-scaled by s_a (zero beyond the
     //     row's rank); the other rows of tbuf are never selected
-    const int nel = n_rows * p.r_max;
-    auto put = [&](int idx, float v) {  // element idx of the row list: staged t and the caller's t
-      const int q = idx / p.r_max, i = rowlist[q], j = idx - q * p.r_max;
-      tbuf[i * TSTR + j] = (uint16_t)f32_to_bf16_rne(v * rowsc[i]);
-      if (p.t_out && cb == 0) p.t_out[(long)(row0 + i) * p.r_max + j] = v;
-    };
-    for (int base = 0; base < nel; base += 256 * EPI_TE) {
-      if (p.t_tag) {
-        // all loads first (unconditional, clamped addresses), then the tag checks
-        uint64_t raw[EPI_TE][KP];
+    if (p.t_tag) {
 #pragma unroll
-        for (int m = 0; m < EPI_TE; ++m) {
-          const int idx = min(base + tid + 256 * m, nel - 1);
-          const int q = idx / p.r_max, j = idx - q * p.r_max;
-          const long addr = (long)(row0 + rowlist[q]) * p.r_max + j;
+      for (int m = 0; m < EPI_TE; ++m) {
+        const int idx = tid + 256 * m;
+        if (idx >= nel) continue;
+        const int q = idx / p.r_max, i = rowlist[q], j = idx - q * p.r_max;
+        const long addr = (long)(row0 + i) * p.r_max + j;
+        float v = 0.f;
 #pragma unroll
-          for (int k2 = 0; k2 < KP; ++k2)
-            raw[m][k2] = ld_agent_u64(p.t_tag + (long)min(k2, p.t_kparts - 1) * p.T * p.r_max + addr);
-        }
-#pragma unroll
-        for (int m = 0; m < EPI_TE; ++m) {
-          const int idx = base + tid + 256 * m;
-          if (idx >= nel) continue;
-          const int q = idx / p.r_max, i = rowlist[q], j = idx - q * p.r_max;
-          const long addr = (long)(row0 + i) * p.r_max + j;
-          float v = 0.f;
-#pragma unroll
-          for (int k2 = 0; k2 < KP; ++k2) {
-            if (j < rowrk[i] && k2 < p.t_kparts) {
-              const uint64_t w =
-                  wait_tag(p.t_tag + (long)k2 * p.T * p.r_max + addr, raw[m][k2], tag, p.ctrl, p.spin_limit);
-              v += __uint_as_float((uint32_t)w);
-            }
+        for (int k2 = 0; k2 < KP; ++k2) {
+          if (j < rowrk[i] && k2 < p.t_kparts) {
+            const uint64_t w =
+                wait_tag(p.t_tag + (long)k2 * p.T * p.r_max + addr, traw[m][k2], tag, p.ctrl, p.spin_limit);
+            v += __uint_as_float((uint32_t)w);
           }
-          put(idx, v);
         }
-      } else {
-        float raw[EPI_TE];
+        put(idx, v);
+      }
+    } else {
 #pragma unroll
-        for (int m = 0; m < EPI_TE; ++m) {
-          const int idx = min(base + tid + 256 * m, nel - 1);
-          const int q = idx / p.r_max;
-          raw[m] = p.t[(long)(row0 + rowlist[q]) * p.r_max + (idx - q * p.r_max)];
-        }
-#pragma unroll
-        for (int m = 0; m < EPI_TE; ++m) {
-          const int idx = base + tid + 256 * m;
-          if (idx >= nel) continue;
-          const int q = idx / p.r_max, j = idx - q * p.r_max;
-          put(idx, j < rowrk[rowlist[q]] ? raw[m] : 0.f);
-        }
+      for (int m = 0; m < EPI_TE; ++m) {
+        const int idx = tid + 256 * m;
+        if (idx >= nel) continue;
+        const int q = idx / p.r_max, j = idx - q * p.r_max;
+        put(idx, j < rowrk[rowlist[q]] ? tpl[m] : 0.f);
       }
     }
     // (5) per batch: wait for this wave's copies, then every wave multiplies its items
