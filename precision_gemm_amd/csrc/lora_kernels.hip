@@ -682,16 +682,80 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
     }
   };
 
+  // ---- one-token-tile decode (16 tokens, the four waves splitting K): each wave streams
+  //      its own k-steps s = wk, wk+4, ... with x loaded straight into the MFMA operand
+  //      layout and quantised in registers, so the main loop needs no LDS and no barrier.
+  //      Lane (li, g) holds token row li at k = 16g .. 16g+15 (first half of the operand) and
+  //      64+16g .. 64+16g+15 (second half); a 32-block spans the lanes g and g^1 (16 apart),
+  //      which exchange their maxima.  The scale operand of lane (li, g) is the code of
+  //      K-block g, held by the lanes g' with g'/2 == g%2 in their first (g < 2) or second
+  //      half: lanes g = 1 and g = 2 swap one code.
+  constexpr bool STREAM = (TT == 1 && WC == 1 && WK == 4 && !XQ);
+  constexpr int SD = 4;  // k-steps of a wave in flight
+  const int nst = (ke - kb) >> 7;
+  const int nmy = (nst > wk) ? (nst - wk + 3) / 4 : 0;
+  const int srot_all = (tile * 5) % (nst > 0 ? nst : 1);
+  auto kstep = [&](int i) {  // physical k-step of the wave's i-th step (clamped, always valid)
+    const int ic = max(min(i, nmy - 1), 0);
+    const int sl = (nmy > 0) ? wk + 4 * ic : 0;
+    return (sl + srot_all) % nst;
+  };
+  uint4 sx[SD][4];
+  uint4 swl[SD][CT], swh[SD][CT];
+  int sws[SD][CT];
+  const uint16_t* xs_row = p.x + (long)min(row0 + li, p.T - 1) * K + kb + 16 * g;
+  auto s_issue = [&](int slot, int i) {
+    const int ps = kstep(i);
+    const uint16_t* xp = xs_row + ps * 128;
+    sx[slot][0] = ldg16(xp);
+    sx[slot][1] = ldg16(xp + 8);
+    sx[slot][2] = ldg16(xp + 64);
+    sx[slot][3] = ldg16(xp + 72);
+    const long ksg = (kb >> 7) + ps;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      if (FMT == LORA_W_FP8_E4M3) {
+        swl[slot][ct] = ldg16(wrow[ct] + ksg * WSTEP);
+        swh[slot][ct] = ldg16(wrow[ct] + ksg * WSTEP + 1024);
+        sws[slot][ct] = 127;
+      } else {
+        swl[slot][ct] = ldg16(wrow[ct] + ksg * WSTEP);
+        swh[slot][ct] = zero4();
+        sws[slot][ct] = (int)wsrow[ct][ksg * 64];
+      }
+    }
+  };
+  auto s_consume = [&](int slot) {
+    uint32_t m1 = max(absmax8_bits(sx[slot][0]), absmax8_bits(sx[slot][1]));
+    uint32_t m2 = max(absmax8_bits(sx[slot][2]), absmax8_bits(sx[slot][3]));
+    m1 = max(m1, (uint32_t)__shfl_xor((int)m1, 16));
+    m2 = max(m2, (uint32_t)__shfl_xor((int)m2, 16));
+    const uint32_t c1 = mx_code_from_bits(m1), c2 = mx_code_from_bits(m2);
+    const uint2 q0 = mx_piece_quant(sx[slot][0], c1), q1 = mx_piece_quant(sx[slot][1], c1);
+    const uint2 q2 = mx_piece_quant(sx[slot][2], c2), q3 = mx_piece_quant(sx[slot][3], c2);
+    const uint4 alo = make_uint4(q0.x, q0.y, q1.x, q1.y), ahi = make_uint4(q2.x, q2.y, q3.x, q3.y);
+    const uint32_t recv = (uint32_t)__shfl_xor((int)((g == 1) ? c2 : c1), 48);
+    const int sa = (int)((g == 0) ? c1 : ((g == 3) ? c2 : recv));
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+      acc[0][ct] = mfma_scaled_16x16x128<FMTB>(alo, ahi, swl[slot][ct], swh[slot][ct], acc[0][ct], sa, sws[slot][ct]);
+  };
+
   // chunks 0 .. NBUF-1 in flight before anything waits; chunk c + NBUF is issued into the
   // buffer of chunk c while chunk c is multiplied (x once it is staged, W after its MFMAs).
   // x of a chunk is always issued before its W (loads retire in order).
-  load_x(0, 0);
-  load_w(0, 0);
+  if (STREAM) {
 #pragma unroll
-  for (int u = 1; u < NBUF; ++u) {
-    if (u < nchunks) {
-      load_x(u, u);
-      load_w(u, u);
+    for (int d = 0; d < SD; ++d) s_issue(d, d);
+  } else {
+    load_x(0, 0);
+    load_w(0, 0);
+#pragma unroll
+    for (int u = 1; u < NBUF; ++u) {
+      if (u < nchunks) {
+        load_x(u, u);
+        load_w(u, u);
+      }
     }
   }
   const bool row_ok = p.lora && tid < ROWS && row0 + tid < p.T && id_raw >= 0 &&
@@ -805,7 +869,21 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
     }
   };
 
-  for (int c = 0; c < nchunks; c += NBUF) {
+  if (STREAM) {
+    for (int i0 = 0; i0 < nmy; i0 += SD) {
+#pragma unroll
+      for (int d = 0; d < SD; ++d) {
+        if (i0 + d >= nmy) break;
+        s_consume(d);
+        s_issue(d, i0 + d + SD);  // past the end: reloads the wave's last step (unused)
+      }
+    }
+    if (p.lora) {
+      prepare_epilogue();
+      __syncthreads();
+    }
+  }
+  for (int c = 0; c < (STREAM ? 0 : nchunks); c += NBUF) {
 #pragma unroll
     for (int u = 0; u < NBUF; ++u) {
       if (c + u >= nchunks) break;
