@@ -691,7 +691,8 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   //      K-block g, held by the lanes g' with g'/2 == g%2 in their first (g < 2) or second
   //      half: lanes g = 1 and g = 2 swap one code.
   constexpr bool STREAM = (TT == 1 && WC == 1 && WK == 4 && !XQ);
-  constexpr int SD = 4;  // k-steps of a wave in flight
+  constexpr int SD = 2;  // k-steps of a wave in flight (measured: 1: slower, 3 or more: the
+                         // longer memory queues cost more than the deeper prefetch gains)
   const int nst = (ke - kb) >> 7;
   const int nmy = (nst > wk) ? (nst - wk + 3) / 4 : 0;
   const int srot_all = (tile * 5) % (nst > 0 ? nst : 1);
