@@ -1238,7 +1238,7 @@ static hipError_t launch_layer_t(const LayerPlan& pl, int grid, hipStream_t stre
 }
 
 // GEMM tile (TT, CT, WC, WK, XQ), down-projection shape (decode, cfg 0: one 16-rank tile,
-// four-step prefetch; prefill, cfg 1: four token tiles, two rank tiles) and workgroups per CU
+// two-step prefetch; prefill, cfg 1: four token tiles, two rank tiles) and workgroups per CU
 #define LORA_LAYER_CASE(TT_, CT_, WC_, WK_, XQ_, CFG_, TG_, JP_, U_, OCC_)                                \
   if (pl.TT == TT_ && pl.CT == CT_ && pl.WC == WC_ && pl.WK == WK_ && pl.XQ == XQ_ && pl.s_cfg == CFG_) \
     return launch_layer_t<FMT, TT_, CT_, WC_, WK_, XQ_, TG_, JP_, U_, OCC_>(pl, grid, stream, sp, gp);
@@ -1246,12 +1246,12 @@ static hipError_t launch_layer_t(const LayerPlan& pl, int grid, hipStream_t stre
 template <int FMT>
 static hipError_t launch_layer_f(const LayerPlan& pl, int grid, hipStream_t stream, const ShrinkParams& sp,
                                  const GemmParams& gp) {
-  LORA_LAYER_CASE(1, 2, 1, 4, false, 0, 1, 1, 4, 1)
-  LORA_LAYER_CASE(4, 1, 4, 1, false, 0, 1, 1, 4, 1)
-  LORA_LAYER_CASE(4, 2, 4, 1, false, 0, 1, 1, 4, 1)
-  LORA_LAYER_CASE(4, 2, 4, 1, true, 0, 1, 1, 4, 1)
-  LORA_LAYER_CASE(8, 1, 4, 1, true, 0, 1, 1, 4, 1)
-  LORA_LAYER_CASE(8, 2, 4, 1, true, 0, 1, 1, 4, 1)
+  LORA_LAYER_CASE(1, 2, 1, 4, false, 0, 1, 1, 2, 1)
+  LORA_LAYER_CASE(4, 1, 4, 1, false, 0, 1, 1, 2, 1)
+  LORA_LAYER_CASE(4, 2, 4, 1, false, 0, 1, 1, 2, 1)
+  LORA_LAYER_CASE(4, 2, 4, 1, true, 0, 1, 1, 2, 1)
+  LORA_LAYER_CASE(8, 1, 4, 1, true, 0, 1, 1, 2, 1)
+  LORA_LAYER_CASE(8, 2, 4, 1, true, 0, 1, 1, 2, 1)
   LORA_LAYER_CASE(8, 1, 4, 1, true, 1, 4, 2, 1, 1)
   LORA_LAYER_CASE(8, 2, 4, 1, true, 1, 4, 2, 1, 1)
   LORA_LAYER_CASE(4, 2, 4, 1, true, 1, 4, 2, 1, 2)
@@ -1266,7 +1266,7 @@ hipError_t launch_layer(const LayerPlan& pl, hipStream_t stream, const ShrinkPar
 }
 
 hipError_t launch_shrink(const LayerPlan& pl, hipStream_t stream, const ShrinkParams& sp) {
-  if (pl.s_cfg == 0) return launch_k(k_shrink<1, 1, 4>, pl.n_shrink_wg, shrink_smem<1, 1, 4>(), stream, sp);
+  if (pl.s_cfg == 0) return launch_k(k_shrink<1, 1, 2>, pl.n_shrink_wg, shrink_smem<1, 1, 2>(), stream, sp);
   if (pl.s_cfg == 1) return launch_k(k_shrink<4, 2, 1>, pl.n_shrink_wg, shrink_smem<4, 2, 1>(), stream, sp);
   return hipErrorInvalidValue;
 }
