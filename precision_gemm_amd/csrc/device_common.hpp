@@ -123,6 +123,19 @@ __device__ __forceinline__ v4f mfma_scaled_16x16x128(const uint4& alo, const uin
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, FMT_B, 0, sa, 0, sb);
 }
 
+// The same with the B operand already assembled as one 32-byte register tuple: loads
+// written straight into the two halves of a tuple that lives across many instructions
+// spare the register allocator from joining two separately allocated halves later.
+template <int FMT_B>
+__device__ __forceinline__ v4f mfma_scaled_16x16x128(const uint4& alo, const uint4& ahi, const v8i& b, v4f acc, int sa,
+                                                     int sb) {
+  v8i a = {(int)alo.x, (int)alo.y, (int)alo.z, (int)alo.w, (int)ahi.x, (int)ahi.y, (int)ahi.z, (int)ahi.w};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, FMT_B, 0, sa, 0, sb);
+}
+__device__ __forceinline__ v8i join8(const uint4& lo, const uint4& hi) {
+  return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
 // bf16 MFMA 16x16x32.  A and B operands have mirrored layouts (lane l: row/column
 // l % 16, eight k values for lane group l / 16), so any fixed assignment of the eight
 // k values of a lane group works as long as both operands use it; the result layout
@@ -177,6 +190,12 @@ __device__ __forceinline__ void st_agent_u64(uint64_t* p, uint64_t v) {
 }
 __device__ __forceinline__ uint64_t ld_agent_u64(const uint64_t* p) {
   return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// the same from an address held as an integer: the global address space is stated, so
+// the load is a global (not a flat) access
+__device__ __forceinline__ uint64_t ld_agent_u64_at(uint64_t addr) {
+  typedef __attribute__((address_space(1))) uint64_t g_u64;
+  return __hip_atomic_load(reinterpret_cast<g_u64*>(addr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // wait until every memory operation this wave issued has completed
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }

@@ -691,8 +691,7 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   //      K-block g, held by the lanes g' with g'/2 == g%2 in their first (g < 2) or second
   //      half: lanes g = 1 and g = 2 swap one code.
   constexpr bool STREAM = (TT == 1 && WC == 1 && WK == 4 && !XQ);
-  constexpr int SD = 2;  // k-steps of a wave in flight (measured: 1: slower, 3 or more: the
-                         // longer memory queues cost more than the deeper prefetch gains)
+  constexpr int SD = 4;  // k-steps of a wave in flight (measured: 2, 3 and 6 are slower)
   const int nst = (ke - kb) >> 7;
   const int nmy = (nst > wk) ? (nst - wk + 3) / 4 : 0;
   const int srot_all = (tile * 5) % (nst > 0 ? nst : 1);
@@ -702,7 +701,7 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
     return (sl + srot_all) % nst;
   };
   uint4 sx[SD][4];
-  uint4 swl[SD][CT], swh[SD][CT];
+  v8i sw[SD][CT];
   int sws[SD][CT];
   const uint16_t* xs_row = p.x + (long)min(row0 + li, p.T - 1) * K + kb + 16 * g;
   auto s_issue = [&](int slot, int i) {
@@ -716,12 +715,10 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
       if (FMT == LORA_W_FP8_E4M3) {
-        swl[slot][ct] = ldg16(wrow[ct] + ksg * WSTEP);
-        swh[slot][ct] = ldg16(wrow[ct] + ksg * WSTEP + 1024);
+        sw[slot][ct] = join8(ldg16(wrow[ct] + ksg * WSTEP), ldg16(wrow[ct] + ksg * WSTEP + 1024));
         sws[slot][ct] = 127;
       } else {
-        swl[slot][ct] = ldg16(wrow[ct] + ksg * WSTEP);
-        swh[slot][ct] = zero4();
+        sw[slot][ct] = join8(ldg16(wrow[ct] + ksg * WSTEP), zero4());
         sws[slot][ct] = (int)wsrow[ct][ksg * 64];
       }
     }
@@ -739,7 +736,7 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
     const int sa = (int)((g == 0) ? c1 : ((g == 3) ? c2 : recv));
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
-      acc[0][ct] = mfma_scaled_16x16x128<FMTB>(alo, ahi, swl[slot][ct], swh[slot][ct], acc[0][ct], sa, sws[slot][ct]);
+      acc[0][ct] = mfma_scaled_16x16x128<FMTB>(alo, ahi, sw[slot][ct], acc[0][ct], sa, sws[slot][ct]);
   };
 
   // chunks 0 .. NBUF-1 in flight before anything waits; chunk c + NBUF is issued into the
@@ -870,45 +867,19 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
     }
   };
 
-  if (STREAM) {
-    for (int i0 = 0; i0 < nmy; i0 += SD) {
-#pragma unroll
-      for (int d = 0; d < SD; ++d) {
-        if (i0 + d >= nmy) break;
-        s_consume(d);
-        s_issue(d, i0 + d + SD);  // past the end: reloads the wave's last step (unused)
-      }
-    }
-    if (p.lora) {
-      prepare_epilogue();
-      __syncthreads();
-    }
-  }
-  for (int c = 0; c < (STREAM ? 0 : nchunks); c += NBUF) {
-#pragma unroll
-    for (int u = 0; u < NBUF; ++u) {
-      if (c + u >= nchunks) break;
-      stage_x(u);
-      __syncthreads();
-      if (c + u + NBUF < nchunks) load_x(u, c + u + NBUF);
-      mma_chunk(u, c + u);
-      if (c + u + NBUF < nchunks) load_w(u, c + u + NBUF);
-      __syncthreads();
-      if (u == 0 && c == 0 && p.lora) {
-        prepare_epilogue();
-        __syncthreads();
-      }
-    }
-  }
-  // ---- up-projection loads go out as soon as the main loop ends (before the k-wave sums
-  //      and the channel scale): the first batch of B slices into LDS, then t of the rows
-  //      this split needs (all of them fit one batch of EPI_TE per thread)
+  // ---- up-projection helpers: B slices into LDS and the t gather.  They go out as soon as
+  //      the tile knows its rows' adapters: in the one-tile stream while the last k-steps
+  //      are in flight, otherwise when the main loop ends (before the k-wave sums)
   uint16_t* tbuf = reinterpret_cast<uint16_t*>(smem + EL::TB);
   float* lred = reinterpret_cast<float*>(smem + EL::LRED);
-  const int n_items = p.lora ? __builtin_amdgcn_readfirstlane(meta[0]) : 0;
-  const int n_rows = p.lora ? __builtin_amdgcn_readfirstlane(meta[1]) : 0;
-  const int n_own = p.lora ? __builtin_amdgcn_readfirstlane(meta[2]) : 0;
-  const int n_batch = (n_own + spb - 1) / spb;
+  int n_items = 0, n_rows = 0, n_own = 0, n_batch = 0, nel = 0;
+  auto read_meta = [&]() {
+    n_items = __builtin_amdgcn_readfirstlane(meta[0]);
+    n_rows = __builtin_amdgcn_readfirstlane(meta[1]);
+    n_own = __builtin_amdgcn_readfirstlane(meta[2]);
+    n_batch = (n_own + spb - 1) / spb;
+    nel = n_rows * p.r_max;
+  };
 
   // B_a^T rows n_tile0 .. n_tile0 + WN - 1 of one adapter are WN * r_a contiguous bf16;
   // the waves copy the slices of a batch straight into their LDS slots (16 bytes per
@@ -931,6 +902,103 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
       }
     }
   };
+  uint64_t traw[EPI_TE][KP];
+  float tpl[EPI_TE];
+  // t of the rows this split needs (all of them fit one batch of EPI_TE per thread):
+  // tagged partials (fused) or the caller's plain t
+  auto load_t = [&]() {
+    if (nel == 0) {
+      // no rows: nothing to load
+    } else if (p.t_tag) {  // unconditional loads from clamped addresses; tags checked later
+#pragma unroll
+      for (int m = 0; m < EPI_TE; ++m) {
+        const int idx = min(tid + 256 * m, nel - 1);
+        const int q = idx / p.r_max, j = idx - q * p.r_max;
+        const long addr = (long)(row0 + rowlist[q]) * p.r_max + j;
+#pragma unroll
+        for (int k2 = 0; k2 < KP; ++k2)
+          traw[m][k2] = ld_agent_u64(p.t_tag + (long)min(k2, p.t_kparts - 1) * p.T * p.r_max + addr);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < EPI_TE; ++m) {
+        const int idx = min(tid + 256 * m, nel - 1);
+        const int q = idx / p.r_max;
+        tpl[m] = p.t[(long)(row0 + rowlist[q]) * p.r_max + (idx - q * p.r_max)];
+      }
+    }
+  };
+  // The stream's tagged t gather, issued before its last round of k-steps is multiplied:
+  // EPI_TE x KP loads per thread on every path, each from its own address (an element it
+  // needs, else a distinct word of x), so that none can be merged away and the waits for
+  // those k-steps do not have to assume that fewer loads went out after them.
+  auto load_t_stream = [&]() {
+    const int rm = max(p.r_max, 1);
+    const uint64_t* dummy = reinterpret_cast<const uint64_t*>(p.x);
+    const uint64_t tb = reinterpret_cast<uint64_t>(p.t_tag), xb = reinterpret_cast<uint64_t>(dummy);
+    const bool tag_on = p.t_tag != nullptr;
+#pragma unroll
+    for (int m = 0; m < EPI_TE; ++m) {
+      const int idx = tid + 256 * m;
+      const bool use = tag_on && idx < nel;
+      const int q = min(idx / rm, ROWS - 1), j = idx - (idx / rm) * rm;
+      const int rl = rowlist[q];  // read unconditionally (a stale value is never used)
+      const long elem = (long)(row0 + rl) * rm + j;
+#pragma unroll
+      for (int k2 = 0; k2 < KP; ++k2) {
+        const uint64_t a_use = tb + 8ull * (uint64_t)((long)min(k2, max(p.t_kparts, 1) - 1) * p.T * rm + elem);
+        const uint64_t a_dum = xb + 8ull * (uint64_t)(m * KP + k2);
+        traw[m][k2] = ld_agent_u64_at(use ? a_use : a_dum);
+      }
+    }
+  };
+
+  if (STREAM) {
+    // Rounds of SD steps, at least two.  Every round but the last consumes its SD slots
+    // and refills them (past the wave's last step a refill reloads that step, and its
+    // consumption is skipped); the last round only consumes.  The loads a round issues
+    // never depend on a branch, so every path holds the slots' loads in the same order
+    // and the compiler's waits for slot d count only the loads issued before it (a
+    // conditional round or an early exit would make it wait for all of them).
+    const int nround = max((nmy + SD - 1) / SD, 2);
+    auto s_round = [&](int r) {
+#pragma unroll
+      for (int d = 0; d < SD; ++d) {
+        if (r * SD + d < nmy) s_consume(d);
+        s_issue(d, (r + 1) * SD + d);
+      }
+    };
+    s_round(0);
+    // the adapters of the rows are known by now: the up-projection metadata, so that the
+    // t gather can go out before the last round
+    if (p.lora) {
+      prepare_epilogue();
+      __syncthreads();
+      read_meta();
+    }
+    int r = 1;
+    for (; r + 1 < nround; ++r) s_round(r);
+    load_t_stream();
+#pragma unroll
+    for (int d = 0; d < SD; ++d)
+      if (r * SD + d < nmy) s_consume(d);
+  }
+  for (int c = 0; c < (STREAM ? 0 : nchunks); c += NBUF) {
+#pragma unroll
+    for (int u = 0; u < NBUF; ++u) {
+      if (c + u >= nchunks) break;
+      stage_x(u);
+      __syncthreads();
+      if (c + u + NBUF < nchunks) load_x(u, c + u + NBUF);
+      mma_chunk(u, c + u);
+      if (c + u + NBUF < nchunks) load_w(u, c + u + NBUF);
+      __syncthreads();
+      if (u == 0 && c == 0 && p.lora) {
+        prepare_epilogue();
+        __syncthreads();
+      }
+    }
+  }
   v4f lacc[TT][CT];
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt)
@@ -963,36 +1031,19 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
       for (int ct = 0; ct < CT; ++ct) lacc[tt][ct] = mfma_bf16_16x16x32(aop, bop[ct], lacc[tt][ct]);
     }
   };
-  const int nel = n_rows * p.r_max;
   auto put = [&](int idx, float v) {  // element idx of the row list: staged t and the caller's t
     const int q = idx / p.r_max, i = rowlist[q], j = idx - q * p.r_max;
     tbuf[i * TSTR + j] = (uint16_t)f32_to_bf16_rne(v * rowsc[i]);
     if (p.t_out && cb == 0) p.t_out[(long)(row0 + i) * p.r_max + j] = v;
   };
-  uint64_t traw[EPI_TE][KP];
-  float tpl[EPI_TE];
-  if (p.lora) {
+  // ---- up-projection loads of the chunked path go out as soon as the main loop ends
+  if (!STREAM && p.lora) {
+    read_meta();
     if (n_batch > 0) stage_b(0);
-    if (nel == 0) {
-      // no rows: nothing to load
-    } else if (p.t_tag) {  // unconditional loads from clamped addresses; tags checked later
-#pragma unroll
-      for (int m = 0; m < EPI_TE; ++m) {
-        const int idx = min(tid + 256 * m, nel - 1);
-        const int q = idx / p.r_max, j = idx - q * p.r_max;
-        const long addr = (long)(row0 + rowlist[q]) * p.r_max + j;
-#pragma unroll
-        for (int k2 = 0; k2 < KP; ++k2)
-          traw[m][k2] = ld_agent_u64(p.t_tag + (long)min(k2, p.t_kparts - 1) * p.T * p.r_max + addr);
-      }
-    } else {
-#pragma unroll
-      for (int m = 0; m < EPI_TE; ++m) {
-        const int idx = min(tid + 256 * m, nel - 1);
-        const int q = idx / p.r_max;
-        tpl[m] = p.t[(long)(row0 + rowlist[q]) * p.r_max + (idx - q * p.r_max)];
-      }
-    }
+    load_t();
+  } else if (STREAM && p.lora) {
+    if (n_batch > 0) stage_b(0);
+    if (!p.t_tag) load_t();
   }
 
   // publish the launch epoch only now: waiting for it earlier would stall wave 0
