@@ -2,10 +2,10 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_qkv] [--sets S]
 
-A step is one pass of the whole hot path over one batch: the segment builder
-(lora_build_segments) followed by the fused layer call (gemm_lowp_lora_epilogue with the
-down-projection in the same launch; for prefill shapes also the MXFP8 pre-pass), from
-bf16 x to bf16 y.  The K timed steps are captured in one HIP graph and replayed once,
+A step is one pass of the whole hot path over one batch: one fused layer call
+(gemm_lowp_lora_epilogue with LORA_FUSE_SHRINK | LORA_BUILD_SEGMENTS: the segment builder,
+the down-projection and the GEMM with its LoRA epilogue in one launch; above 16 tokens
+also the MXFP8 pre-pass launch), from bf16 x and adapter ids to bf16 y.  The K timed steps are captured in one HIP graph and replayed once,
 bracketed by torch.cuda.synchronize(); inputs are resident in HBM.  Steps rotate over S
 copies of the inputs so that the weights are read from HBM rather than from the 256 MB
 Infinity Cache.
@@ -125,15 +125,28 @@ def main():
         x, w, ad, ids = upload(wl, dev)
         ws = P.alloc_workspace(wl.T, wl.K, wl.N, ad.n, ad.r_max, dev)
         y = torch.empty((wl.T, wl.N), dtype=torch.bfloat16, device=dev)
-        seg = P.build_segments(ids, ad.n)
+        seg = P.empty_segments(ids, ad.n)
         S.append(dict(x=x, w=w, ad=ad, ids=ids, ws=ws, y=y, seg=seg))
     torch.cuda.synchronize()
 
-    def step(s, with_segments=True):
+    def step(s):
         d = S[s % sets]
-        if with_segments:
-            P.build_segments(d["ids"], d["ad"].n, out=d["seg"])
-        P.gemm_lowp_lora_epilogue(d["x"], d["w"], d["seg"], d["ad"], d["ws"], fuse_shrink=True, y=d["y"])
+        P.gemm_lowp_lora_epilogue(d["x"], d["w"], d["seg"], d["ad"], d["ws"], fuse_shrink=True, y=d["y"],
+                                  build_segments=True)
+
+    # The layer kernel as the step launches it: up to 64 tokens the segment builder is a
+    # workgroup of that launch; above, the call launches the builder first, and the layer
+    # kernel alone is the call without the flag (the segments are built by then).
+    in_launch = wl.T <= 64
+    xq_pass = bool(P.plan_info(wl.T, wl.K, wl.N, S[0]["ad"].n, S[0]["ad"].r_max, wl.fmt)["XQ"])
+
+    def layer_call(s):
+        d = S[s % sets]
+        P.gemm_lowp_lora_epilogue(d["x"], d["w"], d["seg"], d["ad"], d["ws"], fuse_shrink=True, y=d["y"],
+                                  build_segments=in_launch)
+
+    def quant_call(s):  # the MXFP8 pre-pass that the call runs before the layer kernel
+        P.quant_act_mxfp8(S[s % sets]["x"])
 
     # parity of the benchmarked call against the oracle (whole layer for decode shapes)
     step(0)
@@ -166,18 +179,26 @@ def main():
             step(i)
         torch.cuda.synchronize()
         total_s = time.perf_counter() - t0
-        layer_us = None
+        layer_us = quant_us = None
     else:
-        # whole steps (segments + layer), K of them in one graph
+        # K whole steps in one graph, timed from the host
         g_all = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g_all):
             for i in range(K):
                 step(i)
-        # layer calls only, for the dominant kernel's duration
+        # K layer calls, timed with events on the launch stream: the layer kernel's
+        # duration including its launch gap (with the pre-pass where the plan has one,
+        # whose own graph below is subtracted)
         g_layer = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g_layer):
             for i in range(K):
-                step(i, with_segments=False)
+                layer_call(i)
+        g_quant = None
+        if xq_pass:
+            g_quant = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_quant):
+                for i in range(K):
+                    quant_call(i)
         g_all.replay()
         g_layer.replay()
         torch.cuda.synchronize()
@@ -185,12 +206,20 @@ def main():
         g_all.replay()
         torch.cuda.synchronize()
         total_s = time.perf_counter() - t0
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        g_layer.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        layer_us = e0.elapsed_time(e1) * 1e3 / K
+
+        def event_us(g):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            g.replay()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / K
+
+        layer_us = event_us(g_layer)
+        quant_us = event_us(g_quant) if g_quant is not None else 0.0
+        layer_us -= quant_us
     # every workspace must report a clean status
     status = max(P.workspace_status(d["ws"]) for d in S)
 
@@ -231,6 +260,7 @@ def main():
                    "timing": "eager" if args.eager else "hip graph of K steps"},
         "roofline": roof,
         "layer_us": layer_us,
+        "prepass_us": quant_us,
         "tbps": nbytes / (dom_us * 1e-6) / 1e12,
         "tflops": flops / (dom_us * 1e-6) / 1e12,
         "parity": parity,

@@ -95,7 +95,16 @@ enum {
   /* Run the adapter down-projection inside the same launch: its workgroups take the
    * lowest ids and start first, the GEMM workgroups stream W meanwhile and wait for
    * t only in their epilogue.  t (if non-NULL) receives the down-projection. */
-  LORA_FUSE_SHRINK = 1u << 0
+  LORA_FUSE_SHRINK = 1u << 0,
+  /* With LORA_FUSE_SHRINK: the same launch also builds the batch's segments from
+   * adapter_id, exactly as lora_build_segments does (one more workgroup; the
+   * down-projection workgroups that read them wait for it).  seg_indptr and
+   * sorted_tok are then outputs; the error word goes to the workspace (see
+   * lora_workspace_segment_error).  Meant for the first LoRA layer of a batch, so
+   * that the batch needs no launch of its own for the segments.  Above 64 tokens the
+   * call launches the builder just before the layer instead (the down-projection
+   * would otherwise start late); the outputs are the same. */
+  LORA_BUILD_SEGMENTS = 1u << 1
 };
 
 /* Status code as text; never NULL. */
@@ -163,13 +172,15 @@ lora_status lora_expand(const float* t, int32_t T, int32_t N,
  *  - flags & LORA_FUSE_SHRINK: the down-projection runs in the same launch (t is an
  *    output, may be NULL).  Otherwise t is an input (from lora_shrink); t == NULL
  *    then means "base GEMM only" and the adapter arguments may be NULL.
+ *  - seg_indptr / sorted_tok: read (from lora_build_segments) unless flags has
+ *    LORA_BUILD_SEGMENTS, which makes them outputs of this call.
  *  - w_fmt: LORA_W_FP8_E4M3 or LORA_W_MXFP4_E2M1; w_q (and for MXFP4 w_scale) in the
  *    packed form made by lora_pack_weight; for FP8 w_scale is float [N].
  * y is written, not accumulated into. */
 lora_status gemm_lowp_lora_epilogue(const uint16_t* x, int32_t T, int32_t K, int32_t N,
                                     int32_t w_fmt, const uint8_t* w_q, const void* w_scale,
                                     float* t, const int32_t* adapter_id,
-                                    const int32_t* seg_indptr, const int32_t* sorted_tok,
+                                    int32_t* seg_indptr, int32_t* sorted_tok,
                                     const uint64_t* A_ptrs, const uint64_t* B_ptrs,
                                     const int32_t* ranks, const float* scales,
                                     int32_t n_adapters, int32_t r_max,
@@ -181,6 +192,11 @@ lora_status gemm_lowp_lora_epilogue(const uint16_t* x, int32_t T, int32_t K, int
  * `stream`.  0 = fine; non-zero = a bounded wait in the fused launch gave up
  * (the output is then unspecified).  Cleared by lora_workspace_init. */
 lora_status lora_workspace_status(const void* workspace, int32_t* status_dev, void* stream);
+
+/* Error word of the last segment build inside gemm_lowp_lora_epilogue
+ * (LORA_BUILD_SEGMENTS) on this workspace, with the meaning of lora_build_segments'
+ * err_word: copies one int32 to *err_dev (device pointer) on `stream`. */
+lora_status lora_workspace_segment_error(const void* workspace, int32_t* err_dev, void* stream);
 
 /* Introspection for tests and benchmarks: writes the tile plan chosen for these sizes
  * into out[0..n_out) (host array) as {token tiles of 16 per workgroup, column tiles of

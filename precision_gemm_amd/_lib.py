@@ -24,6 +24,7 @@ _SIGNATURES = {
     "lora_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "lora_workspace_init": (c_i32, [c_vp, c_size, c_vp]),
     "lora_workspace_status": (c_i32, [c_vp, c_vp, c_vp]),
+    "lora_workspace_segment_error": (c_i32, [c_vp, c_vp, c_vp]),
     "lora_build_segments": (c_i32, [c_vp, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp]),
     "lora_quant_act_mxfp8": (c_i32, [c_vp, c_i32, c_i32, c_vp, c_vp, c_vp]),
     "lora_shrink": (c_i32, [c_vp, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_vp, c_vp, c_size, c_vp]),

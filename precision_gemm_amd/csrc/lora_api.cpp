@@ -140,6 +140,13 @@ lora_status lora_workspace_status(const void* workspace, int32_t* status_dev, vo
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
+lora_status lora_workspace_segment_error(const void* workspace, int32_t* err_dev, void* stream) {
+  if (!workspace || !err_dev) return LORA_ERR_INVALID_ARG;
+  const char* ctrl = reinterpret_cast<const char*>(workspace);
+  hipError_t e = hipMemcpyAsync(err_dev, ctrl + 4 * CTRL_SEGERR, 4, hipMemcpyDeviceToDevice, as_stream(stream));
+  return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
 lora_status lora_build_segments(const int32_t* adapter_id, int32_t T, int32_t n_adapters, int32_t* seg_indptr,
                                 int32_t* sorted_tok, int32_t* err_word, void* stream) {
   if (T < 0 || n_adapters < 1) return LORA_ERR_INVALID_ARG;
@@ -201,7 +208,7 @@ lora_status lora_expand(const float* t, int32_t T, int32_t N, const int32_t* ada
 
 lora_status gemm_lowp_lora_epilogue(const uint16_t* x, int32_t T, int32_t K, int32_t N, int32_t w_fmt,
                                     const uint8_t* w_q, const void* w_scale, float* t, const int32_t* adapter_id,
-                                    const int32_t* seg_indptr, const int32_t* sorted_tok, const uint64_t* A_ptrs,
+                                    int32_t* seg_indptr, int32_t* sorted_tok, const uint64_t* A_ptrs,
                                     const uint64_t* B_ptrs, const int32_t* ranks, const float* scales,
                                     int32_t n_adapters, int32_t r_max, uint16_t* y, uint32_t flags,
                                     void* workspace, size_t workspace_bytes, void* stream) {
@@ -209,8 +216,20 @@ lora_status gemm_lowp_lora_epilogue(const uint16_t* x, int32_t T, int32_t K, int
   if (st != LORA_OK) return st;
   if ((st = check_adapters(n_adapters, r_max)) != LORA_OK) return st;
   if (w_fmt != LORA_W_FP8_E4M3 && w_fmt != LORA_W_MXFP4_E2M1) return LORA_ERR_INVALID_ARG;
-  if (flags & ~(uint32_t)LORA_FUSE_SHRINK) return LORA_ERR_INVALID_ARG;
-  if (T == 0) return LORA_OK;
+  if (flags & ~(uint32_t)(LORA_FUSE_SHRINK | LORA_BUILD_SEGMENTS)) return LORA_ERR_INVALID_ARG;
+  const bool build = (flags & LORA_BUILD_SEGMENTS) != 0;
+  if (build && !(flags & LORA_FUSE_SHRINK)) return LORA_ERR_INVALID_ARG;
+  if (build && (!seg_indptr || !adapter_id || (T > 0 && !sorted_tok))) return LORA_ERR_INVALID_ARG;
+  if (T == 0) {
+    if (!build) return LORA_OK;
+    // an empty batch still has its (all-zero) segment offsets
+    if (!workspace || !aligned16(workspace) || workspace_bytes < 256) return LORA_ERR_WORKSPACE;
+    int* ctrl0 = reinterpret_cast<int*>(workspace);
+    return launch_build_segments(adapter_id, 0, n_adapters, seg_indptr, sorted_tok, ctrl0 + CTRL_SEGERR,
+                                 as_stream(stream)) == hipSuccess
+               ? LORA_OK
+               : LORA_ERR_HIP;
+  }
   if (!x || !w_q || !w_scale || !y) return LORA_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(w_q) || !aligned16(y)) return LORA_ERR_INVALID_ARG;
   const bool fused = (flags & LORA_FUSE_SHRINK) != 0;
@@ -223,11 +242,20 @@ lora_status gemm_lowp_lora_epilogue(const uint16_t* x, int32_t T, int32_t K, int
   char* ws = reinterpret_cast<char*>(workspace);
   hipStream_t s = as_stream(stream);
 
+  int* ctrl = reinterpret_cast<int*>(ws + pl.off_ctrl);
+  // Segments in the layer launch up to 64 tokens.  Beyond that the down-projection
+  // workgroups would wait for the builder at their start, and their A stream is long
+  // enough (many adapters, or long segments) that a launch of its own costs less
+  // (measured: 128 tokens x 128 adapters and 4096-token prefill got slower in-launch).
+  const bool build_in = build && T <= 64;
+  if (build && !build_in &&
+      launch_build_segments(adapter_id, T, n_adapters, seg_indptr, sorted_tok, ctrl + CTRL_SEGERR, s) != hipSuccess)
+    return LORA_ERR_HIP;
+
   uint8_t* xq = reinterpret_cast<uint8_t*>(ws + pl.off_xq);
   uint8_t* xsc = reinterpret_cast<uint8_t*>(ws + pl.off_xsc);
   if (pl.XQ && launch_quant(x, T, K, xq, xsc, s) != hipSuccess) return LORA_ERR_HIP;
 
-  int* ctrl = reinterpret_cast<int*>(ws + pl.off_ctrl);
   uint64_t* ttag = reinterpret_cast<uint64_t*>(ws + pl.off_ttag);
 
   ShrinkParams sp{};
@@ -240,6 +268,8 @@ lora_status gemm_lowp_lora_epilogue(const uint16_t* x, int32_t T, int32_t K, int
     sp.t_tag = ttag;
     sp.tblk = pl.s_tblk; sp.n_tblk = pl.s_ntblk; sp.n_jg = pl.s_njg; sp.jper = pl.s_jper;
     sp.kparts = pl.s_kparts; sp.kpart_len = pl.s_kpart_len;
+    sp.seg_wait = build_in ? 1 : 0;
+    sp.spin_limit = SPIN_LIMIT;
   }
   GemmParams gp{};
   gp.x = x; gp.xq = xq; gp.xsc = xsc;
@@ -261,6 +291,8 @@ lora_status gemm_lowp_lora_epilogue(const uint16_t* x, int32_t T, int32_t K, int
   gp.n_shrink = fused ? pl.n_shrink_wg : 0;
   gp.ctrl = ctrl;
   gp.spin_limit = SPIN_LIMIT;
+  gp.seg_build = build_in ? seg_indptr : nullptr;
+  gp.sorted_build = build_in ? sorted_tok : nullptr;
   return launch_layer(pl, s, sp, gp) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 

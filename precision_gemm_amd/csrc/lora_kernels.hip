@@ -35,24 +35,31 @@ namespace lora {
 constexpr int SEG_THREADS = 256;
 constexpr int SEG_CACHE = 4096;  // batches up to this size keep their ids in LDS between the passes
 
-__global__ __launch_bounds__(SEG_THREADS) void k_build_segments(const int* __restrict__ ids, int T, int n_ad,
-                                                                int* __restrict__ seg_indptr,
-                                                                int* __restrict__ sorted_tok, int* __restrict__ err) {
-  __shared__ int cnt[MAX_ADAPTERS];
-  __shared__ int ids_s[SEG_CACHE];
-  __shared__ int wsum[SEG_THREADS / 64];
-  __shared__ int first_bad;
+// One workgroup builds the whole result.  cnt (n_ad ints) and, for batches of up to
+// cache_cap tokens, ids_s (T ints) are LDS arrays of the caller.  COH: the outputs are
+// written with agent-coherent stores, for workgroups of the same launch that read them.
+template <bool COH>
+__device__ __forceinline__ void build_segments_wg(const int* __restrict__ ids, int T, int n_ad,
+                                                  int* __restrict__ seg_indptr, int* __restrict__ sorted_tok,
+                                                  int* __restrict__ err, int* cnt, int* ids_s, int cache_cap,
+                                                  int* wsum, int* first_bad) {
+  auto put = [](int* q, int v) {
+    if (COH)
+      set_agent(q, v);
+    else
+      *q = v;
+  };
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid == 0) first_bad = 0x7fffffff;
+  if (tid == 0) *first_bad = 0x7fffffff;
   for (int a = tid; a < n_ad; a += SEG_THREADS) cnt[a] = 0;
   __syncthreads();
   // 1. counts (LDS atomics: order-independent); ids read from memory once
-  const bool cached = T <= SEG_CACHE;
+  const bool cached = T <= cache_cap;
   for (int t = tid; t < T; t += SEG_THREADS) {
     const int a = ids[t];
     if (cached) ids_s[t] = a;
     if (a >= 0 && a < n_ad) atomicAdd(&cnt[a], 1);
-    else atomicMin(&first_bad, t);
+    else atomicMin(first_bad, t);
   }
   __syncthreads();
   // 2. exclusive scan: a contiguous slice per thread, a wave scan, then the wave totals
@@ -72,12 +79,12 @@ __global__ __launch_bounds__(SEG_THREADS) void k_build_segments(const int* __res
   for (int w = 0; w < wave; ++w) base += wsum[w];
   for (int a = lo; a < hi; ++a) {
     const int c = cnt[a];
-    seg_indptr[a] = base;
+    put(seg_indptr + a, base);
     cnt[a] = base;  // becomes the write cursor of adapter a
     base += c;
   }
-  if (tid == SEG_THREADS - 1) seg_indptr[n_ad] = base;
-  if (tid == 0) *err = (first_bad == 0x7fffffff) ? 0 : first_bad + 1;
+  if (tid == SEG_THREADS - 1) put(seg_indptr + n_ad, base);
+  if (tid == 0) put(err, (*first_bad == 0x7fffffff) ? 0 : *first_bad + 1);
   __syncthreads();
   // 3. stable placement by one wave, 64 tokens at a time in token order.  Lanes with the
   //    same adapter are grouped with a ballot; a lane's slot is the cursor plus the number
@@ -95,12 +102,27 @@ __global__ __launch_bounds__(SEG_THREADS) void k_build_segments(const int* __res
         const int la = __shfl(a, leader);
         const unsigned long long same = __ballot(ok && a == la);
         const int c0 = cur[la];
-        if (ok && a == la) sorted_tok[c0 + __popcll(same & below)] = t;
+        if (ok && a == la) put(sorted_tok + c0 + __popcll(same & below), t);
         if (lane == leader) cur[la] = c0 + __popcll(same);
         pending &= ~same;
       }
     }
   }
+}
+
+// LDS bytes of the in-launch builder: 16 words of scratch, cnt, and the id cache
+__host__ __device__ constexpr size_t seg_lds_bytes(int T, int n_ad) {
+  return 64 + 4 * (size_t)n_ad + 4 * (size_t)(T < SEG_CACHE ? T : SEG_CACHE);
+}
+
+__global__ __launch_bounds__(SEG_THREADS) void k_build_segments(const int* __restrict__ ids, int T, int n_ad,
+                                                                int* __restrict__ seg_indptr,
+                                                                int* __restrict__ sorted_tok, int* __restrict__ err) {
+  __shared__ int cnt[MAX_ADAPTERS];
+  __shared__ int ids_s[SEG_CACHE];
+  __shared__ int wsum[SEG_THREADS / 64];
+  __shared__ int first_bad;
+  build_segments_wg<false>(ids, T, n_ad, seg_indptr, sorted_tok, err, cnt, ids_s, SEG_CACHE, wsum, &first_bad);
 }
 
 // ======================================================================================
@@ -241,8 +263,29 @@ __device__ __forceinline__ void shrink_item(const ShrinkParams& p, int item, cha
   // With at most 16 tokens (and ids at hand) the workgroup takes all token rows and keeps
   // the rows of adapter a: no dependent loads of seg_indptr and sorted_tok before x.
   const bool direct = (p.ids != nullptr) && (p.T <= 16);
-  const int s0 = direct ? 0 : p.seg_indptr[a];
-  const int L = direct ? p.T : p.seg_indptr[a + 1] - s0;
+  // Segments built by workgroup 0 of this launch: wait for its tag, then read them with
+  // agent-coherent loads (another XCD's L2 may hold an older copy).
+  const bool coh = !direct && p.seg_wait;
+  if (coh) {
+    publish();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int tag = *lds_epoch + 1;
+      int spins = 0;
+      while (ld_agent(ctrl + CTRL_SEGREADY) != tag) {
+        __builtin_amdgcn_s_sleep(2);
+        if (++spins > p.spin_limit) {
+          set_agent(ctrl + CTRL_STATUS, 1);
+          break;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  auto seg_at = [&](int i) { return coh ? ld_agent(p.seg_indptr + i) : p.seg_indptr[i]; };
+  auto tok_at = [&](int i) { return coh ? ld_agent(p.sorted_tok + i) : p.sorted_tok[i]; };
+  const int s0 = direct ? 0 : seg_at(a);
+  const int L = direct ? p.T : seg_at(a + 1) - s0;
   const int tok_begin = tb * p.tblk;
   const int r = p.ranks[a];
   const int j_begin = jg * JP * 16;
@@ -275,7 +318,7 @@ __device__ __forceinline__ void shrink_item(const ShrinkParams& p, int item, cha
 #pragma unroll
     for (int tt = 0; tt < TG; ++tt) {
       const int pos = min(t0 + tt * 16 + li, tok_end - 1);
-      xrow[tt] = p.x + (long)(direct ? pos : p.sorted_tok[s0 + pos]) * p.K + k_begin + 16 * g;
+      xrow[tt] = p.x + (long)(direct ? pos : tok_at(s0 + pos)) * p.K + k_begin + 16 * g;
     }
     v4f acc[TG][JP];
 #pragma unroll
@@ -348,7 +391,7 @@ __device__ __forceinline__ void shrink_item(const ShrinkParams& p, int item, cha
         for (int v = 0; v < 4; ++v) {
           const int pos = t0 + tt * 16 + 4 * g + v;
           if (pos < tok_end && j < r && (!direct || p.ids[pos] == a)) {
-            const long tok = direct ? pos : p.sorted_tok[s0 + pos];
+            const long tok = direct ? pos : tok_at(s0 + pos);
             if (p.t_tag) st_agent_u64(p.t_tag + ((long)kp * p.T + tok) * p.r_max + j, tagged(sum[v], tag));
             if (p.t_out && p.kparts == 1) p.t_out[tok * p.r_max + j] = sum[v];
           }
@@ -362,7 +405,7 @@ __device__ __forceinline__ void shrink_item(const ShrinkParams& p, int item, cha
     for (int idx = tid; idx < (tok_end - tok_begin) * w; idx += 256) {
       const int pos = tok_begin + idx / w;
       if (direct && p.ids[pos] != a) continue;
-      const long tok = direct ? pos : p.sorted_tok[s0 + pos];
+      const long tok = direct ? pos : tok_at(s0 + pos);
       p.t_out[tok * p.r_max + r + idx % w] = 0.f;
     }
   }
@@ -1249,9 +1292,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
   extern __shared__ __align__(16) char smem[];
   __shared__ int lds_epoch;
   const int e = wg_epoch_load(gp.ctrl);
-  const int b = blockIdx.x;
+  const int nb = gp.seg_build ? 1 : 0;
+  const int b = blockIdx.x - nb;
   int started = 0;
-  if (b < gp.n_shrink) {
+  if (b < 0) {
+    // the batch's segments, built in this launch (workgroup 0): coherent stores, then
+    // the launch's tag in the control block for down-projection workgroups that read them
+    started = wg_epoch_publish(gp.ctrl, e, &lds_epoch);
+    int* w = reinterpret_cast<int*>(smem);
+    build_segments_wg<true>(gp.ids, gp.T, gp.n_ad, gp.seg_build, gp.sorted_build, gp.ctrl + CTRL_SEGERR, w + 16,
+                            w + 16 + gp.n_ad, SEG_CACHE, w, w + 4);
+    wait_stores();
+    __syncthreads();
+    if (threadIdx.x == 0) set_agent(gp.ctrl + CTRL_SEGREADY, e + 1);
+  } else if (b < gp.n_shrink) {
     shrink_item<TG, JP, U>(sp, b, smem, gp.ctrl, e, &lds_epoch, &started);
   } else {
     // K-parts of t: the single-tile decode down-projection splits K
@@ -1283,8 +1337,9 @@ static hipError_t launch_k(KernelT kern, int grid, size_t smem, hipStream_t stre
 template <int FMT, int TT, int CT, int WC, int WK, bool XQ, int TG, int JP, int U, int OCC>
 static hipError_t launch_layer_t(const LayerPlan& pl, int grid, hipStream_t stream, const ShrinkParams& sp,
                                  const GemmParams& gp) {
-  const size_t sm = std::max((size_t)GemmSmem<TT, CT, WC, WK, OCC>::BYTES,
-                             gp.n_shrink > 0 ? shrink_smem<TG, JP, U>() : (size_t)0);
+  const size_t sm = std::max(std::max((size_t)GemmSmem<TT, CT, WC, WK, OCC>::BYTES,
+                                      gp.n_shrink > 0 ? shrink_smem<TG, JP, U>() : (size_t)0),
+                             gp.seg_build ? seg_lds_bytes(gp.T, gp.n_ad) : (size_t)0);
   return launch_k(k_layer<FMT, TT, CT, WC, WK, XQ, TG, JP, U, OCC>, grid, sm, stream, sp, gp);
 }
 
@@ -1311,7 +1366,7 @@ static hipError_t launch_layer_f(const LayerPlan& pl, int grid, hipStream_t stre
 #undef LORA_LAYER_CASE
 
 hipError_t launch_layer(const LayerPlan& pl, hipStream_t stream, const ShrinkParams& sp, const GemmParams& gp) {
-  const int grid = gp.n_shrink + pl.n_gemm_wg;
+  const int grid = (gp.seg_build ? 1 : 0) + gp.n_shrink + pl.n_gemm_wg;
   if (pl.fmt == LORA_W_FP8_E4M3) return launch_layer_f<LORA_W_FP8_E4M3>(pl, grid, stream, sp, gp);
   return launch_layer_f<LORA_W_MXFP4_E2M1>(pl, grid, stream, sp, gp);
 }

@@ -19,6 +19,8 @@ enum : int {
   CTRL_EPOCH = 0,    // number of fused launches completed on this workspace (tag = epoch + 1)
   CTRL_STARTED = 1,  // workgroups of the current launch that have read the epoch
   CTRL_STATUS = 2,   // non-zero: a bounded wait gave up
+  CTRL_SEGREADY = 3, // tag of the launch whose segment builder has finished
+  CTRL_SEGERR = 4,   // error word of the last in-launch segment build
 };
 
 struct ShrinkParams {
@@ -37,6 +39,8 @@ struct ShrinkParams {
   int n_jg;            // rank groups per adapter (16 * jper ranks each)
   int jper;            // 16-rank tiles per group (1..4)
   int kparts, kpart_len;
+  int seg_wait;        // the segments are built in the same launch: wait for them, read them coherently
+  int spin_limit;
 };
 
 struct GemmParams {
@@ -65,6 +69,8 @@ struct GemmParams {
   int n_shrink;    // down-projection workgroups at the front of the grid
   int* ctrl;       // workspace control block
   int spin_limit;
+  int* seg_build;     // non-null: workgroup 0 builds seg_indptr (here) and sorted_tok from ids
+  int* sorted_build;
 };
 
 struct ExpandParams {
@@ -87,6 +93,7 @@ struct LayerPlan {
   int ksplit, krange, n_cb, n_tb, n_gemm_wg;
   // down-projection decomposition
   int s_tblk, s_ntblk, s_njg, s_jper, s_kparts, s_kpart_len, n_shrink_wg;
+  int n_build_wg;  // 1 when the launch also builds the segments
   // workspace layout (byte offsets)
   size_t off_ctrl, off_ttag, off_gflag, off_gpart, off_xq, off_xsc, total;
 };

@@ -16,6 +16,7 @@ from ._lib import check, lib
 LORA_W_FP8_E4M3 = 0
 LORA_W_MXFP4_E2M1 = 1
 LORA_FUSE_SHRINK = 1
+LORA_BUILD_SEGMENTS = 2
 
 _FMT = {"fp8": LORA_W_FP8_E4M3, "mxfp4": LORA_W_MXFP4_E2M1}
 
@@ -140,6 +141,13 @@ def workspace_status(ws: torch.Tensor) -> int:
     return int(out.item())
 
 
+def workspace_segment_error(ws: torch.Tensor) -> int:
+    """Error word of the last segment build inside the layer call on ``ws``."""
+    out = torch.zeros(1, dtype=torch.int32, device=ws.device)
+    check("lora_workspace_segment_error", lib().lora_workspace_segment_error(_ptr(ws), _ptr(out), _stream()))
+    return int(out.item())
+
+
 def plan_info(T, K, N, n_adapters, r_max, fmt="fp8") -> dict:
     buf = (ctypes.c_int32 * 16)()
     n = lib().lora_plan_info(T, K, N, n_adapters, r_max, _FMT[fmt], buf, 16)
@@ -150,15 +158,23 @@ def plan_info(T, K, N, n_adapters, r_max, fmt="fp8") -> dict:
     return dict(zip(keys, list(buf)[:n]))
 
 
+def empty_segments(adapter_id: torch.Tensor, n_adapters: int) -> Segments:
+    """Buffers for the segments of a batch (filled by build_segments, or by the layer
+    call with ``build_segments=True``)."""
+    _dev(adapter_id, "adapter_id", torch.int32)
+    T = adapter_id.numel()
+    dev = adapter_id.device
+    return Segments(adapter_id, torch.empty(n_adapters + 1, dtype=torch.int32, device=dev),
+                    torch.empty(max(T, 1), dtype=torch.int32, device=dev)[:T],
+                    torch.empty(1, dtype=torch.int32, device=dev))
+
+
 def build_segments(adapter_id: torch.Tensor, n_adapters: int, out: Segments | None = None) -> Segments:
     """Group tokens by adapter; with ``out`` the result goes into its buffers."""
     _dev(adapter_id, "adapter_id", torch.int32)
     T = adapter_id.numel()
-    dev = adapter_id.device
     if out is None:
-        out = Segments(adapter_id, torch.empty(n_adapters + 1, dtype=torch.int32, device=dev),
-                       torch.empty(max(T, 1), dtype=torch.int32, device=dev)[:T],
-                       torch.empty(1, dtype=torch.int32, device=dev))
+        out = empty_segments(adapter_id, n_adapters)
     check("lora_build_segments", lib().lora_build_segments(_ptr(adapter_id), T, n_adapters, _ptr(out.seg_indptr),
                                                            _ptr(out.sorted_tok), _ptr(out.err), _stream()))
     return out
@@ -195,10 +211,11 @@ def expand(t: torch.Tensor, seg: Segments, ad: Adapters, y: torch.Tensor) -> tor
 def gemm_lowp_lora_epilogue(x: torch.Tensor, w: LowpWeight, seg: Segments | None, ad: Adapters | None,
                             ws: torch.Tensor, *, t: torch.Tensor | None = None, fuse_shrink: bool = True,
                             y: torch.Tensor | None = None, n_adapters: int | None = None,
-                            r_max: int | None = None) -> torch.Tensor:
+                            r_max: int | None = None, build_segments: bool = False) -> torch.Tensor:
     """The fused layer.  With ``fuse_shrink`` the down-projection runs in the same
     launch (``t``, if given, receives it); otherwise ``t`` is an input and ``t=None``
-    computes the base GEMM only."""
+    computes the base GEMM only.  With ``build_segments`` the same launch also fills
+    ``seg`` (from ``seg.adapter_id``; see ``empty_segments``)."""
     _dev(x, "x", torch.bfloat16)
     if not w.packed:
         raise ValueError("the GEMM reads W in the packed form: call pack_weight(w) once first")
@@ -208,7 +225,7 @@ def gemm_lowp_lora_epilogue(x: torch.Tensor, w: LowpWeight, seg: Segments | None
         y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
     n = ad.n if ad is not None else (n_adapters or 1)
     rm = ad.r_max if ad is not None else (r_max or 8)
-    flags = LORA_FUSE_SHRINK if fuse_shrink else 0
+    flags = (LORA_FUSE_SHRINK if fuse_shrink else 0) | (LORA_BUILD_SEGMENTS if build_segments else 0)
     g = lambda o, name: _ptr(getattr(o, name)) if o is not None else _ptr(None)  # noqa: E731
     check("gemm_lowp_lora_epilogue", lib().gemm_lowp_lora_epilogue(
         _ptr(x), T, K, N, _FMT[w.fmt], _ptr(w.q), _ptr(w.scale), _ptr(t),

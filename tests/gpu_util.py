@@ -62,16 +62,26 @@ def assert_t_close(t, t_ref, what=""):
     return f
 
 
-def run_gpu(wl, *, fused=True, want_t=True, base_only=False):
-    """Run the layer on the GPU; returns dict of numpy results."""
+def run_gpu(wl, *, fused=True, want_t=True, base_only=False, build=False):
+    """Run the layer on the GPU; returns dict of numpy results.  build: the fused layer
+    call also builds the segments (no separate segment launch)."""
     import torch
     import precision_gemm_amd as P
     from workloads.device import upload
     x, w, ad, ids = upload(wl)
-    seg = P.build_segments(ids, ad.n)
     ws = P.alloc_workspace(wl.T, wl.K, wl.N, ad.n, ad.r_max)
     out = {}
-    if base_only:
+    seg = P.empty_segments(ids, ad.n) if build else P.build_segments(ids, ad.n)
+    if build:
+        seg.seg_indptr.fill_(-7)
+        seg.sorted_tok.fill_(-7)
+        t = torch.empty((wl.T, ad.r_max), dtype=torch.float32, device="cuda") if want_t else None
+        y = P.gemm_lowp_lora_epilogue(x, w, seg, ad, ws, t=t, fuse_shrink=True, build_segments=True)
+        if t is not None:
+            out["t"] = t
+        torch.cuda.synchronize()
+        seg.err.fill_(P.workspace_segment_error(ws))
+    elif base_only:
         y = P.gemm_lowp_lora_epilogue(x, w, seg, ad, ws, t=None, fuse_shrink=False)
     elif fused:
         t = torch.empty((wl.T, ad.r_max), dtype=torch.float32, device="cuda") if want_t else None

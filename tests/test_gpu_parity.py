@@ -43,6 +43,53 @@ def test_layer_matches_oracle(name, fused):
     print(f"  y max_rel={m:.2e} frob={f:.2e} t frob={tf:.2e}", flush=True)
 
 
+BUILD = [
+    # T, K, N, fmt, ranks, seed: segments built inside the layer launch
+    (4, 256, 256, "fp8", [8, 8], 21),
+    (16, 1024, 384, "fp8", [16], 22),
+    (16, 512, 256, "mxfp4", [16, 8, 32], 23),
+    (64, 1024, 512, "fp8", [16] * 32, 24),
+    (128, 2048, 256, "mxfp4", [8, 16, 32, 64] * 16, 25),
+    (300, 768, 256, "fp8", [48, 8, 16, 64], 26),
+]
+
+
+@pytest.mark.parametrize("case", BUILD, ids=[f"T{c[0]}_K{c[1]}_N{c[2]}_{c[3]}_a{len(c[4])}" for c in BUILD])
+def test_segments_built_in_layer_launch(case):
+    T, K, N, fmt, ranks, seed = case
+    print(f"[case] in-launch segments {case}", flush=True)
+    rng = np.random.default_rng(seed)
+    n = len(ranks)
+    ids = rng.integers(0, n, T)
+    wl = _custom(T, K, N, fmt, ranks, ids, seed, a_std=0.1, b_std=0.05)
+    g = run_gpu(wl, fused=True, build=True)
+    assert g["status"] == 0 and g["err"] == 0
+    seg_ref, srt_ref = oracle_segments(wl.ids, wl.n_adapters)
+    assert np.array_equal(g["seg_indptr"], seg_ref) and np.array_equal(g["sorted_tok"], srt_ref)
+    ref = run_oracle(wl)
+    assert_y_close(g["y"], ref["y"], str(case))
+    assert_t_close(g["t"].astype(np.float64), ref["t"], str(case))
+    # the same kernels with the segments from their own launch: bitwise the same y
+    g2 = run_gpu(wl, fused=True)
+    assert np.array_equal(g["y_bits"], g2["y_bits"])
+
+
+@pytest.mark.parametrize("reps", [5, 9], ids=["T40_in_launch", "T72_own_launch"])
+def test_segments_built_in_layer_launch_bad_ids(reps):
+    ids = np.array([0, 1, 7, 1, 0, -1, 1, 0] * reps, np.int32)  # > 16 tokens: the down-projection reads the segments
+    T = ids.size
+    wl = _custom(T, 512, 256, "fp8", [16, 16], np.where((ids >= 0) & (ids < 2), ids, 0), 27)
+    wl.ids = ids
+    g = run_gpu(wl, fused=True, build=True)
+    assert g["status"] == 0 and g["err"] == 3
+    good = np.flatnonzero((ids >= 0) & (ids < 2))
+    seg_ref, srt_ref = oracle_segments(ids[good], 2)
+    assert np.array_equal(g["seg_indptr"], seg_ref)
+    assert np.array_equal(g["sorted_tok"][:good.size], good[srt_ref])
+    ref = run_oracle(wl, rows=tuple(good.tolist()))
+    assert_y_close(g["y"][good], ref["y"], "valid tokens")
+
+
 def test_quant_all_bf16_patterns():
     import torch
     import precision_gemm_amd as P
