@@ -603,9 +603,11 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   // chunks in flight (measured on the 64-token tile: three or four are no faster than two)
   constexpr int NBUF = 2;
   uint4 xr[NBUF][NX];
-  // pre-quantised x: the chunk's scale codes, ROWS x 8 bytes, are one load of wave 0
+  // pre-quantised x: the chunk's scale codes, ROWS x SB bytes, are one load of wave 0
   // (lane l: rows SRL*l .. SRL*l + SRL - 1)
-  static_assert(!XQ || (KC == 256 && (ROWS == 64 || ROWS == 128)), "scale staging: 8 codes per row, 64 or 128 rows");
+  constexpr int SB = KC / 32;
+  static_assert(!XQ || ((SB == 8 || SB == 4) && (ROWS == 64 || ROWS == 128)),
+                "scale staging: 4 or 8 codes per row, 64 or 128 rows");
   constexpr int SRL = (ROWS >= 64) ? ROWS / 64 : 1;
   uint2 xsc2[NBUF][SRL];
   uint4 wlo[NBUF][SPW][CT], whi[NBUF][SPW][CT];
@@ -640,11 +642,11 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
     if (XQ && wave == 0) {
 #pragma unroll
       for (int h = 0; h < SRL; ++h) {
-        // two 4-byte loads (rows are 4-byte aligned); in a partial last chunk the second
+        // SB / 4 four-byte loads (rows are 4-byte aligned); in a partial last chunk the second
         // may read codes past the row, which are never used (the workspace pads the array)
         const long tok = min(row0 + SRL * lane + h, p.T - 1);
         const uint32_t* src = reinterpret_cast<const uint32_t*>(p.xsc + tok * (K / 32) + (kc0 >> 5));
-        xsc2[buf][h] = make_uint2(src[0], src[1]);
+        xsc2[buf][h] = make_uint2(src[0], SB == 8 ? src[1] : 0u);
       }
     }
   };
@@ -695,11 +697,15 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
       }
     }
     if (XQ && wave == 0) {
-      if (SRL == 2)
+      if (SB == 8 && SRL == 2)
         *reinterpret_cast<uint4*>(ss + lane * 16) =
             make_uint4(xsc2[buf][0].x, xsc2[buf][0].y, xsc2[buf][SRL - 1].x, xsc2[buf][SRL - 1].y);
-      else
+      else if (SB == 8)
         *reinterpret_cast<uint2*>(ss + lane * 8) = xsc2[buf][0];
+      else if (SRL == 2)
+        *reinterpret_cast<uint2*>(ss + lane * 8) = make_uint2(xsc2[buf][0].x, xsc2[buf][SRL - 1].x);
+      else
+        *reinterpret_cast<uint32_t*>(ss + lane * 4) = xsc2[buf][0].x;
     }
   };
   auto mma_chunk = [&](int buf, int c) {
@@ -789,14 +795,10 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
 #pragma unroll
     for (int d = 0; d < SD; ++d) s_issue(d, d);
   } else {
-    load_x(0, 0);
-    load_w(0, 0);
 #pragma unroll
-    for (int u = 1; u < NBUF; ++u) {
-      if (u < nchunks) {
-        load_x(u, u);
-        load_w(u, u);
-      }
+    for (int u = 0; u < NBUF; ++u) {  // past the last chunk: a chunk again (never multiplied)
+      load_x(u, u);
+      load_w(u, u);
     }
   }
   const bool row_ok = p.lora && tid < ROWS && row0 + tid < p.T && id_raw >= 0 &&
@@ -1026,27 +1028,47 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
     for (int d = 0; d < SD; ++d)
       if (r * SD + d < nmy) s_consume(d);
   }
-  for (int c = 0; c < (STREAM ? 0 : nchunks); c += NBUF) {
+  if (!STREAM) {
+    // Rounds of NBUF chunks, at least two: every round but the last refills each buffer with
+    // the chunk NBUF ahead (past the last chunk: a chunk again, never multiplied), the last
+    // round only multiplies.  As in the stream, no load depends on a branch, so the waits
+    // for a chunk's loads leave the later chunks' loads in flight.
+    const int nround = max((nchunks + NBUF - 1) / NBUF, 2);
+    auto c_round = [&](int r, bool refill) {
 #pragma unroll
-    for (int u = 0; u < NBUF; ++u) {
-      if (c + u >= nchunks) break;
-      stage_x(u);
-      __syncthreads();
-      if (c + u + NBUF < nchunks) load_x(u, c + u + NBUF);
-      mma_chunk(u, c + u);
-      if (c + u + NBUF < nchunks) load_w(u, c + u + NBUF);
-      __syncthreads();
-      if (u == 0 && c == 0 && p.lora) {
-        prepare_epilogue();
+      for (int u = 0; u < NBUF; ++u) {
+        const int c = r * NBUF + u;
+        stage_x(u);
         __syncthreads();
+        if (refill) load_x(u, c + NBUF);
+        if (c < nchunks) mma_chunk(u, c);
+        if (refill) load_w(u, c + NBUF);
+        __syncthreads();
+        if (c == 0 && p.lora) {
+          prepare_epilogue();
+          __syncthreads();
+        }
       }
-    }
+    };
+    int r = 0;
+    for (; r + 1 < nround; ++r) c_round(r, true);
+    c_round(r, false);
   }
-  v4f lacc[TT][CT];
+  // adapter sums: with k-waves a separate accumulator (summed over the waves in wave order
+  // before it joins the base), otherwise straight into the base accumulator (already scaled)
+  v4f lacc_[WK > 1 ? TT : 1][WK > 1 ? CT : 1];
+  auto lacc = [&](int tt, int ct) -> v4f& {
+    if constexpr (WK > 1)
+      return lacc_[tt][ct];
+    else
+      return acc[tt][ct];
+  };
+  if constexpr (WK > 1) {
 #pragma unroll
-  for (int tt = 0; tt < TT; ++tt)
+    for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) lacc[tt][ct] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int ct = 0; ct < CT; ++ct) lacc(tt, ct) = v4f{0.f, 0.f, 0.f, 0.f};
+  }
   // one bf16 MFMA per item, token tile and column tile; B operands from the staged slice
   // (lane (li, g): B_a^T[n][j .. j+7], j = 32*block + 8g, zero for j >= r_a).  The item
   // descriptors of 64 items at a time sit one per lane and are read with readlane, and the
@@ -1071,7 +1093,7 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
       const uint4 tv = *reinterpret_cast<const uint4*>(tbuf + (tt * 16 + li) * TSTR + j);
       const uint4 aop = (valid && myad[tt] == a) ? tv : zero4();
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) lacc[tt][ct] = mfma_bf16_16x16x32(aop, bop[ct], lacc[tt][ct]);
+      for (int ct = 0; ct < CT; ++ct) lacc(tt, ct) = mfma_bf16_16x16x32(aop, bop[ct], lacc(tt, ct));
     }
   };
   auto put = [&](int idx, float v) {  // element idx of the row list: staged t and the caller's t
@@ -1192,7 +1214,7 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct)
             *reinterpret_cast<v4f*>(lred + ((((wk - 1) * WC + wc) * TT + tt) * CT + ct) * 256 + lane * 4) =
-                lacc[tt][ct];
+                lacc(tt, ct);
       }
       __syncthreads();
       if (wk == 0) {
@@ -1202,15 +1224,15 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
           for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct)
-              lacc[tt][ct] +=
+              lacc(tt, ct) +=
                   *reinterpret_cast<const v4f*>(lred + ((((w - 1) * WC + wc) * TT + tt) * CT + ct) * 256 + lane * 4);
       }
-    }
-    if (wk == 0) {
+      if (wk == 0) {
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt)
+        for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) acc[tt][ct] += lacc[tt][ct];
+          for (int ct = 0; ct < CT; ++ct) acc[tt][ct] += lacc(tt, ct);
+      }
     }
   }
 
