@@ -51,11 +51,17 @@ LayerPlan make_plan(int T, int K, int N, int n_ad, int r_max, int fmt, bool fuse
     // it), and 128 channels per workgroup halve those reads
     pl.TT = 8; pl.WC = 4; pl.WK = 1; pl.XQ = true;
     pl.CT = (N % 128 == 0) ? 2 : 1;
-    // prefill: 64-token tiles, two workgroups per CU, so that one workgroup's start-up and
-    // epilogue latency overlaps the other's main loop
-    if (T > 128 && pl.CT == 2) pl.TT = 4;
+    // prefill: 128 x 256 tiles (each wave 128 tokens x 64 channels: four times the MFMAs
+    // per LDS read of x of the 128-channel tile), one workgroup per CU; where N is not a
+    // multiple of 256, 64-token tiles with two workgroups per CU, so that one workgroup's
+    // start-up and epilogue latency overlaps the other's main loop
+    if (T > 128 && N % 256 == 0) {
+      pl.CT = 4;
+    } else if (T > 128 && pl.CT == 2) {
+      pl.TT = 4;
+    }
   }
-  pl.KC = (pl.TT == 1) ? 2048 : ((pl.TT <= 4 && pl.CT == 1) ? 512 : 256);
+  pl.KC = (pl.TT == 1) ? 2048 : ((pl.TT <= 4 && pl.CT == 1) ? 512 : (pl.CT == 4 ? 128 : 256));
   const int WN = pl.WC * pl.CT * 16;
   pl.n_cb = N / WN;
   pl.n_tb = ceil_div(T, 16 * pl.TT);

@@ -478,7 +478,7 @@ template <int TT, int CT>
 struct ChunkK {
   // K-chunk: two chunks of x and W are held in registers, so the chunk shrinks as the
   // workgroup tile grows (the host plan uses the same rule)
-  static constexpr int KC = (TT == 1) ? 2048 : ((TT <= 4 && CT == 1) ? 512 : 256);
+  static constexpr int KC = (TT == 1) ? 2048 : ((TT <= 4 && CT == 1) ? 512 : (CT == 4 ? 128 : 256));
   static constexpr int STEPS = KC / 128;
   static constexpr int ROW = KC + 16;  // LDS row stride in bytes
 };
@@ -1383,6 +1383,7 @@ static hipError_t launch_layer_f(const LayerPlan& pl, int grid, hipStream_t stre
   LORA_LAYER_CASE(8, 1, 4, 1, true, 1, 4, 2, 1, 1)
   LORA_LAYER_CASE(8, 2, 4, 1, true, 1, 4, 2, 1, 1)
   LORA_LAYER_CASE(4, 2, 4, 1, true, 1, 4, 2, 1, 2)
+  LORA_LAYER_CASE(8, 4, 4, 1, true, 1, 4, 2, 1, 1)
   return hipErrorInvalidValue;
 }
 #undef LORA_LAYER_CASE
