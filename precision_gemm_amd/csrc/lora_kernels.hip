@@ -35,26 +35,38 @@ namespace lora {
 constexpr int SEG_THREADS = 256;
 constexpr int SEG_CACHE = 4096;  // batches up to this size keep their ids in LDS between the passes
 
-// One workgroup builds the whole result.  cnt (n_ad ints) and, for batches of up to
-// cache_cap tokens, ids_s (T ints) are LDS arrays of the caller.  COH: the outputs are
-// written with agent-coherent stores, for workgroups of the same launch that read them.
+// One workgroup builds the whole result.  LDS (caller's): cnt (n_ad ints), and for batches
+// of up to SEG_CACHE tokens the ids (T ints), the adapters present (up to T ints) and the
+// per-(adapter, token chunk) counts (up to SEG_CACHE ints).  COH: the outputs are written
+// with agent-coherent stores, for workgroups of the same launch that read them.
+//
+// Placement of a cached batch is data-parallel: the tokens are cut into C chunks, and one
+// work item per (present adapter, chunk) counts the adapter's tokens in its chunk, then,
+// after a prefix over the chunks, writes their positions in token order, which keeps the
+// sort stable.  About 2 * T comparisons per present adapter.  Larger batches (ids read
+// from memory) are placed by one wave in token order, 64 tokens at a time.
 template <bool COH>
 __device__ __forceinline__ void build_segments_wg(const int* __restrict__ ids, int T, int n_ad,
                                                   int* __restrict__ seg_indptr, int* __restrict__ sorted_tok,
-                                                  int* __restrict__ err, int* cnt, int* ids_s, int cache_cap,
-                                                  int* wsum, int* first_bad) {
+                                                  int* __restrict__ err, int* cnt, int* ids_s, int* pres, int* wcnt,
+                                                  int* wsum, int* misc) {
   auto put = [](int* q, int v) {
     if (COH)
       set_agent(q, v);
     else
       *q = v;
   };
+  int* first_bad = misc;
+  int* n_pres = misc + 1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid == 0) *first_bad = 0x7fffffff;
+  if (tid == 0) {
+    *first_bad = 0x7fffffff;
+    *n_pres = 0;
+  }
   for (int a = tid; a < n_ad; a += SEG_THREADS) cnt[a] = 0;
   __syncthreads();
   // 1. counts (LDS atomics: order-independent); ids read from memory once
-  const bool cached = T <= cache_cap;
+  const bool cached = T <= SEG_CACHE;
   for (int t = tid; t < T; t += SEG_THREADS) {
     const int a = ids[t];
     if (cached) ids_s[t] = a;
@@ -62,7 +74,8 @@ __device__ __forceinline__ void build_segments_wg(const int* __restrict__ ids, i
     else atomicMin(first_bad, t);
   }
   __syncthreads();
-  // 2. exclusive scan: a contiguous slice per thread, a wave scan, then the wave totals
+  // 2. exclusive scan: a contiguous slice per thread, a wave scan, then the wave totals;
+  //    the adapters present are listed (in any order) for the placement
   const int per = (n_ad + SEG_THREADS - 1) / SEG_THREADS;
   const int lo = min(tid * per, n_ad), hi = min(lo + per, n_ad);
   int s = 0;
@@ -80,21 +93,83 @@ __device__ __forceinline__ void build_segments_wg(const int* __restrict__ ids, i
   for (int a = lo; a < hi; ++a) {
     const int c = cnt[a];
     put(seg_indptr + a, base);
-    cnt[a] = base;  // becomes the write cursor of adapter a
+    cnt[a] = base;  // becomes the start of adapter a
+    if (cached && c > 0) pres[atomicAdd(n_pres, 1)] = a;
     base += c;
   }
   if (tid == SEG_THREADS - 1) put(seg_indptr + n_ad, base);
   if (tid == 0) put(err, (*first_bad == 0x7fffffff) ? 0 : *first_bad + 1);
   __syncthreads();
-  // 3. stable placement by one wave, 64 tokens at a time in token order.  Lanes with the
-  //    same adapter are grouped with a ballot; a lane's slot is the cursor plus the number
-  //    of lower lanes in its group, so equal ids keep their token order.
+  // 3. stable placement
+  if (cached) {
+    const int np = *n_pres;
+    if (np == 0) return;
+    // C chunks of L tokens (L a multiple of 4: the ids are read four at a time; reads past
+    // T stay inside the LDS areas and are masked)
+    const int C = min(min(T, 64), max(1, min((2 * SEG_THREADS + np - 1) / np, SEG_CACHE / np)));
+    const int L = (((T + C - 1) / C) + 3) & ~3;
+    const int items = np * C;
+    // (a) count of adapter pres[i] in chunk c; item = c * np + i, so that neighbouring lanes
+    //     read the same ids (a broadcast, not a bank conflict); counts stored per adapter
+    for (int it = tid; it < items; it += SEG_THREADS) {
+      const int i = it % np, c = it / np, a = pres[i];
+      const int t0 = c * L, t1 = min(T, t0 + L);
+      int n = 0;
+      for (int t = t0; t < t1; t += 4) {
+        const int4 v = *reinterpret_cast<const int4*>(ids_s + t);
+        n += (v.x == a) + (v.y == a && t + 1 < t1) + (v.z == a && t + 2 < t1) + (v.w == a && t + 3 < t1);
+      }
+      wcnt[i * C + c] = n;
+    }
+    __syncthreads();
+    // (b) per adapter: exclusive prefix over its C <= 64 chunks, from its start; a thread
+    //     per adapter for few chunks, a wave per adapter for many
+    if (C <= 16) {
+      for (int i = tid; i < np; i += SEG_THREADS) {
+        int run = cnt[pres[i]];
+        for (int c = 0; c < C; ++c) {
+          const int n = wcnt[i * C + c];
+          wcnt[i * C + c] = run;
+          run += n;
+        }
+      }
+    } else {
+      for (int i = wave; i < np; i += SEG_THREADS / 64) {
+        const int v = (lane < C) ? wcnt[i * C + lane] : 0;
+        int inc = v;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int u = __shfl_up(inc, off);
+          if (lane >= off) inc += u;
+        }
+        if (lane < C) wcnt[i * C + lane] = cnt[pres[i]] + inc - v;
+      }
+    }
+    __syncthreads();
+    // (c) positions, in token order within the chunk
+    for (int it = tid; it < items; it += SEG_THREADS) {
+      const int i = it % np, c = it / np, a = pres[i];
+      const int t0 = c * L, t1 = min(T, t0 + L);
+      int pos = wcnt[i * C + c];
+      for (int t = t0; t < t1; t += 4) {
+        const int4 v = *reinterpret_cast<const int4*>(ids_s + t);
+        if (v.x == a) put(sorted_tok + pos++, t);
+        if (v.y == a && t + 1 < t1) put(sorted_tok + pos++, t + 1);
+        if (v.z == a && t + 2 < t1) put(sorted_tok + pos++, t + 2);
+        if (v.w == a && t + 3 < t1) put(sorted_tok + pos++, t + 3);
+      }
+    }
+    return;
+  }
+  // one wave, 64 tokens at a time in token order.  Lanes with the same adapter are grouped
+  // with a ballot; a lane's slot is the cursor plus the number of lower lanes in its group,
+  // so equal ids keep their token order.
   if (wave == 0) {
     volatile int* cur = cnt;
     const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int t0 = 0; t0 < T; t0 += 64) {
       const int t = t0 + lane;
-      const int a = (t < T) ? (cached ? ids_s[t] : ids[t]) : -1;
+      const int a = (t < T) ? ids[t] : -1;
       const bool ok = (a >= 0 && a < n_ad);
       unsigned long long pending = __ballot(ok);
       while (pending) {
@@ -110,19 +185,25 @@ __device__ __forceinline__ void build_segments_wg(const int* __restrict__ ids, i
   }
 }
 
-// LDS bytes of the in-launch builder: 16 words of scratch, cnt, and the id cache
+// LDS bytes of the builder: 16 words of scratch, cnt, and for cached batches the ids, the
+// adapters present and the chunk counts
+__host__ __device__ constexpr int seg_cnt_words(int n_ad) { return (n_ad + 3) & ~3; }  // keeps the id cache 16-byte aligned
 __host__ __device__ constexpr size_t seg_lds_bytes(int T, int n_ad) {
-  return 64 + 4 * (size_t)n_ad + 4 * (size_t)(T < SEG_CACHE ? T : SEG_CACHE);
+  return 64 + 4 * (size_t)seg_cnt_words(n_ad) +
+         (T <= SEG_CACHE ? 4 * (size_t)((T + 3) & ~3) + 4 * (size_t)(T < n_ad ? T : n_ad) + 4 * (size_t)SEG_CACHE + 16
+                         : 0);
 }
 
 __global__ __launch_bounds__(SEG_THREADS) void k_build_segments(const int* __restrict__ ids, int T, int n_ad,
                                                                 int* __restrict__ seg_indptr,
                                                                 int* __restrict__ sorted_tok, int* __restrict__ err) {
-  __shared__ int cnt[MAX_ADAPTERS];
-  __shared__ int ids_s[SEG_CACHE];
-  __shared__ int wsum[SEG_THREADS / 64];
-  __shared__ int first_bad;
-  build_segments_wg<false>(ids, T, n_ad, seg_indptr, sorted_tok, err, cnt, ids_s, SEG_CACHE, wsum, &first_bad);
+  extern __shared__ __align__(16) char smem[];
+  int* w = reinterpret_cast<int*>(smem);
+  int* cnt = w + 16;
+  int* ids_s = cnt + seg_cnt_words(n_ad);
+  int* pres = ids_s + (T <= SEG_CACHE ? (T + 3) & ~3 : 0);
+  int* wcnt = pres + (T <= SEG_CACHE ? min(T, n_ad) : 0);
+  build_segments_wg<false>(ids, T, n_ad, seg_indptr, sorted_tok, err, cnt, ids_s, pres, wcnt, w, w + 4);
 }
 
 // ======================================================================================
@@ -1322,8 +1403,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     // the launch's tag in the control block for down-projection workgroups that read them
     started = wg_epoch_publish(gp.ctrl, e, &lds_epoch);
     int* w = reinterpret_cast<int*>(smem);
-    build_segments_wg<true>(gp.ids, gp.T, gp.n_ad, gp.seg_build, gp.sorted_build, gp.ctrl + CTRL_SEGERR, w + 16,
-                            w + 16 + gp.n_ad, SEG_CACHE, w, w + 4);
+    int* cnt = w + 16;
+    int* ids_s = cnt + seg_cnt_words(gp.n_ad);
+    int* pres = ids_s + (gp.T <= SEG_CACHE ? (gp.T + 3) & ~3 : 0);
+    int* wcnt = pres + (gp.T <= SEG_CACHE ? min(gp.T, gp.n_ad) : 0);
+    build_segments_wg<true>(gp.ids, gp.T, gp.n_ad, gp.seg_build, gp.sorted_build, gp.ctrl + CTRL_SEGERR, cnt, ids_s,
+                            pres, wcnt, w, w + 4);
     wait_stores();
     __syncthreads();
     if (threadIdx.x == 0) set_agent(gp.ctrl + CTRL_SEGREADY, e + 1);
@@ -1401,8 +1486,7 @@ hipError_t launch_shrink(const LayerPlan& pl, hipStream_t stream, const ShrinkPa
 }
 
 hipError_t launch_build_segments(const int* ids, int T, int n_ad, int* seg, int* sorted, int* err, hipStream_t s) {
-  hipLaunchKernelGGL(k_build_segments, dim3(1), dim3(SEG_THREADS), 0, s, ids, T, n_ad, seg, sorted, err);
-  return hipGetLastError();
+  return launch_k(k_build_segments, 1, seg_lds_bytes(T, n_ad), s, ids, T, n_ad, seg, sorted, err);
 }
 
 hipError_t launch_quant(const uint16_t* x, int T, int K, uint8_t* xq, uint8_t* xsc, hipStream_t s) {
