@@ -134,10 +134,10 @@ def main():
         P.gemm_lowp_lora_epilogue(d["x"], d["w"], d["seg"], d["ad"], d["ws"], fuse_shrink=True, y=d["y"],
                                   build_segments=True)
 
-    # The layer kernel as the step launches it: up to 64 tokens the segment builder is a
+    # The layer kernel as the step launches it: up to 128 tokens the segment builder is a
     # workgroup of that launch; above, the call launches the builder first, and the layer
     # kernel alone is the call without the flag (the segments are built by then).
-    in_launch = wl.T <= 64
+    in_launch = wl.T <= 128
     xq_pass = bool(P.plan_info(wl.T, wl.K, wl.N, S[0]["ad"].n, S[0]["ad"].r_max, wl.fmt)["XQ"])
 
     def layer_call(s):

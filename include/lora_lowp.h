@@ -101,7 +101,7 @@ enum {
    * down-projection workgroups that read them wait for it).  seg_indptr and
    * sorted_tok are then outputs; the error word goes to the workspace (see
    * lora_workspace_segment_error).  Meant for the first LoRA layer of a batch, so
-   * that the batch needs no launch of its own for the segments.  Above 64 tokens the
+   * that the batch needs no launch of its own for the segments.  Above 128 tokens the
    * call launches the builder just before the layer instead (the down-projection
    * would otherwise start late); the outputs are the same. */
   LORA_BUILD_SEGMENTS = 1u << 1

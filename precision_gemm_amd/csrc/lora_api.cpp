@@ -249,11 +249,11 @@ lora_status gemm_lowp_lora_epilogue(const uint16_t* x, int32_t T, int32_t K, int
   hipStream_t s = as_stream(stream);
 
   int* ctrl = reinterpret_cast<int*>(ws + pl.off_ctrl);
-  // Segments in the layer launch up to 64 tokens.  Beyond that the down-projection
-  // workgroups would wait for the builder at their start, and their A stream is long
-  // enough (many adapters, or long segments) that a launch of its own costs less
-  // (measured: 128 tokens x 128 adapters and 4096-token prefill got slower in-launch).
-  const bool build_in = build && T <= 64;
+  // Segments in the layer launch up to 128 tokens.  Beyond that the builder's own launch
+  // costs less than making the down-projection workgroups wait for it at their start
+  // (measured per step: 128 tokens x 128 adapters 190.4 us in-launch against 193.2 us;
+  // 4096-token prefill 220.1 us in-launch against 218.0 us).
+  const bool build_in = build && T <= 128;
   if (build && !build_in &&
       launch_build_segments(adapter_id, T, n_adapters, seg_indptr, sorted_tok, ctrl + CTRL_SEGERR, s) != hipSuccess)
     return LORA_ERR_HIP;

@@ -74,7 +74,7 @@ def test_segments_built_in_layer_launch(case):
     assert np.array_equal(g["y_bits"], g2["y_bits"])
 
 
-@pytest.mark.parametrize("reps", [5, 9], ids=["T40_in_launch", "T72_own_launch"])
+@pytest.mark.parametrize("reps", [5, 20], ids=["T40_in_launch", "T160_own_launch"])
 def test_segments_built_in_layer_launch_bad_ids(reps):
     ids = np.array([0, 1, 7, 1, 0, -1, 1, 0] * reps, np.int32)  # > 16 tokens: the down-projection reads the segments
     T = ids.size
