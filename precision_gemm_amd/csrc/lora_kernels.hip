@@ -912,6 +912,7 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   char* stg = smem + GemmSmem<TT, CT, WC, WK, OCC>::STG;
   const int slot = WN * p.r_max * 2;  // bytes of one B slice slot (a multiple of 512)
   const int spb = epi_bstage<OCC>() / slot;  // slots per batch (>= 2)
+  static_assert(epi_bstage<OCC>() / (WN * 8 * 2) <= 256, "stage_b keeps a wave's slices one per lane");
   auto prepare_epilogue = [&]() {
     // (1) adapter, rank, scale and B address of every row; a rank outside the limits
     //     drops the row's adapter term
@@ -1011,13 +1012,23 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   // the waves copy the slices of a batch straight into their LDS slots (16 bytes per
   // lane, 1 KB per wave load), leader k of the batch by wave k % 4
   auto stage_b = [&](int b) {
-    const int k1 = min(n_own, (b + 1) * spb);
-    for (int k = b * spb + wave; k < k1; k += 4) {
-      const int row = lrow[k];
-      const int r = __builtin_amdgcn_readfirstlane(rowrk[row]);
-      const uint64_t bp = rowbp[row];
-      const uint64_t bpu = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(bp >> 32)) << 32) |
-                           (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bp);
+    // the wave's slices k = b*spb + wave + 4j: their rank and B address are read from LDS
+    // first, one per lane, because an LDS read placed after a direct-to-LDS copy waits for
+    // that copy to land (the copies would go out one memory round trip apart)
+    const int kb0 = b * spb + wave, k1 = min(n_own, (b + 1) * spb);
+    const int nk = (k1 > kb0) ? (k1 - kb0 + 3) / 4 : 0;  // at most spb / 4 <= 64
+    int r_l = 0;
+    uint64_t bp_l = 0;
+    if (lane < nk) {
+      const int row = lrow[kb0 + 4 * lane];
+      r_l = rowrk[row];
+      bp_l = rowbp[row];
+    }
+    for (int j = 0; j < nk; ++j) {
+      const int k = kb0 + 4 * j;
+      const int r = __builtin_amdgcn_readlane(r_l, j);
+      const uint64_t bpu = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(bp_l >> 32), j) << 32) |
+                           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)bp_l, j);
       const char* src = reinterpret_cast<const char*>(bpu) + (long)n_tile0 * r * 2;
       char* dst = stg + (k % spb) * slot;
       const int bytes = WN * r * 2;
@@ -1030,28 +1041,36 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   };
   uint64_t traw[EPI_TE][KP];
   float tpl[EPI_TE];
+  // element idx = tid + 256 m of the row list: row of the block (from the list) and rank;
+  // all the list reads go out before the first use, so their latencies overlap
+  int trow[EPI_TE], tcol[EPI_TE];
+  auto t_elements = [&]() {
+    const int rm = __builtin_amdgcn_readfirstlane(p.r_max);
+#pragma unroll
+    for (int m = 0; m < EPI_TE; ++m) {
+      const int idx = min(tid + 256 * m, max(nel - 1, 0));
+      const int q = idx / rm;
+      tcol[m] = idx - q * rm;
+      trow[m] = rowlist[min(q, ROWS - 1)];
+    }
+  };
   // t of the rows this split needs (all of them fit one batch of EPI_TE per thread):
   // tagged partials (fused) or the caller's plain t
   auto load_t = [&]() {
+    t_elements();
     if (nel == 0) {
       // no rows: nothing to load
     } else if (p.t_tag) {  // unconditional loads from clamped addresses; tags checked later
 #pragma unroll
       for (int m = 0; m < EPI_TE; ++m) {
-        const int idx = min(tid + 256 * m, nel - 1);
-        const int q = idx / p.r_max, j = idx - q * p.r_max;
-        const long addr = (long)(row0 + rowlist[q]) * p.r_max + j;
+        const long addr = (long)(row0 + trow[m]) * p.r_max + tcol[m];
 #pragma unroll
         for (int k2 = 0; k2 < KP; ++k2)
           traw[m][k2] = ld_agent_u64(p.t_tag + (long)min(k2, p.t_kparts - 1) * p.T * p.r_max + addr);
       }
     } else {
 #pragma unroll
-      for (int m = 0; m < EPI_TE; ++m) {
-        const int idx = min(tid + 256 * m, nel - 1);
-        const int q = idx / p.r_max;
-        tpl[m] = p.t[(long)(row0 + rowlist[q]) * p.r_max + (idx - q * p.r_max)];
-      }
+      for (int m = 0; m < EPI_TE; ++m) tpl[m] = p.t[(long)(row0 + trow[m]) * p.r_max + tcol[m]];
     }
   };
   // The stream's tagged t gather, issued before its last round of k-steps is multiplied:
@@ -1059,17 +1078,15 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   // needs, else a distinct word of x), so that none can be merged away and the waits for
   // those k-steps do not have to assume that fewer loads went out after them.
   auto load_t_stream = [&]() {
+    t_elements();  // list reads unconditional (a stale value is never used)
     const int rm = max(p.r_max, 1);
     const uint64_t* dummy = reinterpret_cast<const uint64_t*>(p.x);
     const uint64_t tb = reinterpret_cast<uint64_t>(p.t_tag), xb = reinterpret_cast<uint64_t>(dummy);
     const bool tag_on = p.t_tag != nullptr;
 #pragma unroll
     for (int m = 0; m < EPI_TE; ++m) {
-      const int idx = tid + 256 * m;
-      const bool use = tag_on && idx < nel;
-      const int q = min(idx / rm, ROWS - 1), j = idx - (idx / rm) * rm;
-      const int rl = rowlist[q];  // read unconditionally (a stale value is never used)
-      const long elem = (long)(row0 + rl) * rm + j;
+      const bool use = tag_on && tid + 256 * m < nel;
+      const long elem = (long)(row0 + trow[m]) * rm + tcol[m];
 #pragma unroll
       for (int k2 = 0; k2 < KP; ++k2) {
         const uint64_t a_use = tb + 8ull * (uint64_t)((long)min(k2, max(p.t_kparts, 1) - 1) * p.T * rm + elem);
@@ -1177,8 +1194,7 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
       for (int ct = 0; ct < CT; ++ct) lacc(tt, ct) = mfma_bf16_16x16x32(aop, bop[ct], lacc(tt, ct));
     }
   };
-  auto put = [&](int idx, float v) {  // element idx of the row list: staged t and the caller's t
-    const int q = idx / p.r_max, i = rowlist[q], j = idx - q * p.r_max;
+  auto put = [&](int i, int j, float v) {  // t of row i, rank j: staged (scaled, bf16) and the caller's t
     tbuf[i * TSTR + j] = (uint16_t)f32_to_bf16_rne(v * rowsc[i]);
     if (p.t_out && cb == 0) p.t_out[(long)(row0 + i) * p.r_max + j] = v;
   };
@@ -1234,31 +1250,31 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   if (p.lora) {
     // (4) t of the rows this split needs -> LDS as bf16 pre-scaled by s_a (zero beyond the
     //     row's rank); the other rows of tbuf are never selected
+    int trk[EPI_TE];  // ranks of the elements' rows, read together
+#pragma unroll
+    for (int m = 0; m < EPI_TE; ++m) trk[m] = rowrk[trow[m]];
     if (p.t_tag) {
 #pragma unroll
       for (int m = 0; m < EPI_TE; ++m) {
-        const int idx = tid + 256 * m;
-        if (idx >= nel) continue;
-        const int q = idx / p.r_max, i = rowlist[q], j = idx - q * p.r_max;
+        if (tid + 256 * m >= nel) continue;
+        const int i = trow[m], j = tcol[m];
         const long addr = (long)(row0 + i) * p.r_max + j;
         float v = 0.f;
 #pragma unroll
         for (int k2 = 0; k2 < KP; ++k2) {
-          if (j < rowrk[i] && k2 < p.t_kparts) {
+          if (j < trk[m] && k2 < p.t_kparts) {
             const uint64_t w =
                 wait_tag(p.t_tag + (long)k2 * p.T * p.r_max + addr, traw[m][k2], tag, p.ctrl, p.spin_limit);
             v += __uint_as_float((uint32_t)w);
           }
         }
-        put(idx, v);
+        put(i, j, v);
       }
     } else {
 #pragma unroll
       for (int m = 0; m < EPI_TE; ++m) {
-        const int idx = tid + 256 * m;
-        if (idx >= nel) continue;
-        const int q = idx / p.r_max, j = idx - q * p.r_max;
-        put(idx, j < rowrk[rowlist[q]] ? tpl[m] : 0.f);
+        if (tid + 256 * m >= nel) continue;
+        put(trow[m], tcol[m], tcol[m] < trk[m] ? tpl[m] : 0.f);
       }
     }
     // (5) per batch: wait for this wave's copies, then every wave multiplies its items
