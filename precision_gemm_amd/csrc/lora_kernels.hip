@@ -1096,6 +1096,32 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
     }
   };
 
+  // The stream's B operands, when the tile has at most one up-projection item per wave (the
+  // single-adapter decode): each wave loads its item's operands (CT x 16 bytes per lane) with
+  // the t gather, instead of staging B slices in LDS after the loop.  A fixed count of
+  // loads on every path (x as a dummy source), as for the t gather.
+  uint4 sb[CT];
+  int sb_it = 0, sb_a = -1, sb_r = 8;
+  bool sb_on = false;
+  auto load_b_stream = [&]() {
+    sb_on = p.lora && n_items <= WK && wk < n_items;  // uniform
+    const int it = items[min(wk, 2 * ROWS - 1)];
+    const int row = it & 255;
+    sb_it = sb_on ? it : 0;
+    sb_r = sb_on ? rowrk[row] : 8;
+    sb_a = sb_on ? rowad[row] : -1;
+    const uint64_t bp = sb_on ? rowbp[row] : reinterpret_cast<uint64_t>(p.x);
+    const int j = ((sb_it >> 8) & 1) * 32 + 8 * g;
+    const int jc = min(j, sb_r - 8);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const int nl = wc * CT * 16 + ct * 16 + li;
+      const uint64_t a_b = bp + 2ull * (uint64_t)((long)(n_tile0 + nl) * sb_r + jc);
+      const uint64_t a_d = reinterpret_cast<uint64_t>(p.x) + 16ull * (uint64_t)ct;
+      sb[ct] = ldg16(reinterpret_cast<const void*>(sb_on ? a_b : a_d));
+    }
+  };
+
   if (STREAM) {
     // Rounds of SD steps, at least two.  Every round but the last consumes its SD slots
     // and refills them (past the wave's last step a refill reloads that step, and its
@@ -1122,6 +1148,7 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
     int r = 1;
     for (; r + 1 < nround; ++r) s_round(r);
     load_t_stream();
+    load_b_stream();
 #pragma unroll
     for (int d = 0; d < SD; ++d)
       if (r * SD + d < nmy) s_consume(d);
@@ -1152,21 +1179,9 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
     for (; r + 1 < nround; ++r) c_round(r, true);
     c_round(r, false);
   }
-  // adapter sums: with k-waves a separate accumulator (summed over the waves in wave order
-  // before it joins the base), otherwise straight into the base accumulator (already scaled)
-  v4f lacc_[WK > 1 ? TT : 1][WK > 1 ? CT : 1];
-  auto lacc = [&](int tt, int ct) -> v4f& {
-    if constexpr (WK > 1)
-      return lacc_[tt][ct];
-    else
-      return acc[tt][ct];
-  };
-  if constexpr (WK > 1) {
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) lacc(tt, ct) = v4f{0.f, 0.f, 0.f, 0.f};
-  }
+  // adapter sums go straight into the (already scaled) accumulator of the wave that
+  // multiplies the item; with k-waves the waves' parts are summed afterwards
+  auto lacc = [&](int tt, int ct) -> v4f& { return acc[tt][ct]; };
   // one bf16 MFMA per item, token tile and column tile; B operands from the staged slice
   // (lane (li, g): B_a^T[n][j .. j+7], j = 32*block + 8g, zero for j >= r_a).  The item
   // descriptors of 64 items at a time sit one per lane and are read with readlane, and the
@@ -1204,7 +1219,7 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
     if (n_batch > 0) stage_b(0);
     load_t();
   } else if (STREAM && p.lora) {
-    if (n_batch > 0) stage_b(0);
+    if (n_batch > 0 && n_items > WK) stage_b(0);
     if (!p.t_tag) load_t();
   }
 
@@ -1213,32 +1228,10 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   __syncthreads();
   const uint32_t tag = (uint32_t)(*lds_epoch) + 1u;
 
-  // ---- sums of the WK k-waves, in wave order, end up in the waves with wk == 0
-  if (WK > 1) {
-    float* red = reinterpret_cast<float*>(smem);
-    if (wk > 0) {
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-          *reinterpret_cast<v4f*>(red + ((((wk - 1) * WC + wc) * TT + tt) * CT + ct) * 256 + lane * 4) = acc[tt][ct];
-    }
-    __syncthreads();
-    if (wk == 0) {
-#pragma unroll
-      for (int w = 1; w < WK; ++w)
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-          for (int ct = 0; ct < CT; ++ct)
-            acc[tt][ct] +=
-                *reinterpret_cast<const v4f*>(red + ((((w - 1) * WC + wc) * TT + tt) * CT + ct) * 256 + lane * 4);
-    }
-    __syncthreads();
-  }
-
-  // ---- epilogue: channel scale (of this K-split's sum: the splits are added scaled)
-  if (FMT == LORA_W_FP8_E4M3 && wk == 0) {
+  // ---- epilogue: channel scale (of this K-split's sum: the splits are added scaled); with
+  //      k-waves every wave scales its own part, and the parts are summed after the adapter
+  //      terms are added (one LDS reduction for both)
+  if (FMT == LORA_W_FP8_E4M3) {
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
 #pragma unroll
@@ -1277,9 +1270,30 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
         put(trow[m], tcol[m], tcol[m] < trk[m] ? tpl[m] : 0.f);
       }
     }
-    // (5) per batch: wait for this wave's copies, then every wave multiplies its items
-    //     (the waves sharing columns split them: item i goes to wave i % WK)
-    for (int b = 0; b < n_batch; ++b) {
+    // (5) the stream's items with their B operands in registers ...
+    if (STREAM && n_items <= WK) {
+      __syncthreads();  // the staged t
+      if (sb_on) {
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) myad[tt] = rowad[tt * 16 + li];
+        const int jb = (sb_it >> 8) & 1, mask = (sb_it >> 9) & 255;
+        const int j = jb * 32 + 8 * g;
+        const bool valid = j < sb_r;
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+          if (!((mask >> tt) & 1)) continue;
+          const uint4 tv = *reinterpret_cast<const uint4*>(tbuf + (tt * 16 + li) * TSTR + j);
+          const uint4 aop = (valid && myad[tt] == sb_a) ? tv : zero4();
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct)
+            lacc(tt, ct) = mfma_bf16_16x16x32(aop, valid ? sb[ct] : zero4(), lacc(tt, ct));
+        }
+      }
+      __syncthreads();  // the area of the k-wave sums lies over the staged t
+    }
+    // ... otherwise per batch: wait for this wave's copies, then every wave multiplies its
+    //     items (the waves sharing columns split them: item i goes to wave i % WK)
+    for (int b = 0; b < ((STREAM && n_items <= WK) ? 0 : n_batch); ++b) {
       if (b > 0) stage_b(b);
       wait_stores();  // all of this wave's memory operations, the LDS copies included
       __syncthreads();
@@ -1303,34 +1317,31 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
       }
       __syncthreads();  // slots are refilled by the next batch
     }
-    // (6) the k-waves' adapter sums, in wave order, join the base in the waves with wk == 0
-    if (WK > 1) {
-      if (wk > 0) {
+  }
+
+  // ---- sums of the WK k-waves (base and adapter terms), in wave order, end up in the waves
+  //      with wk == 0 (the area lies over the staged t, which is no longer read)
+  if (WK > 1) {
+    float* red = reinterpret_cast<float*>(smem);
+    if (wk > 0) {
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+          *reinterpret_cast<v4f*>(red + ((((wk - 1) * WC + wc) * TT + tt) * CT + ct) * 256 + lane * 4) = acc[tt][ct];
+    }
+    __syncthreads();
+    if (wk == 0) {
+#pragma unroll
+      for (int w = 1; w < WK; ++w)
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct)
-            *reinterpret_cast<v4f*>(lred + ((((wk - 1) * WC + wc) * TT + tt) * CT + ct) * 256 + lane * 4) =
-                lacc(tt, ct);
-      }
-      __syncthreads();
-      if (wk == 0) {
-#pragma unroll
-        for (int w = 1; w < WK; ++w)
-#pragma unroll
-          for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
-              lacc(tt, ct) +=
-                  *reinterpret_cast<const v4f*>(lred + ((((w - 1) * WC + wc) * TT + tt) * CT + ct) * 256 + lane * 4);
-      }
-      if (wk == 0) {
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-          for (int ct = 0; ct < CT; ++ct) acc[tt][ct] += lacc(tt, ct);
-      }
+            acc[tt][ct] +=
+                *reinterpret_cast<const v4f*>(red + ((((w - 1) * WC + wc) * TT + tt) * CT + ct) * 256 + lane * 4);
     }
+    __syncthreads();
   }
 
   // ---- K-split over workgroups: producers store their (scaled, adapter-including) sums
