@@ -620,6 +620,9 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   // t elements per thread per gather batch: the whole block's t (ROWS x 64) in one batch,
   // so that the gather costs one memory round trip
   constexpr int EPI_TE = (ROWS * MAX_RANK + 255) / 256;
+  // the 128-row tiles gather t in two halves (registers: one half of the loads in flight)
+  constexpr int EPI_PH = (EPI_TE > 16) ? 2 : 1;
+  constexpr int EPI_TH = EPI_TE / EPI_PH;
   static_assert(STEPS % WK == 0, "k-steps per chunk must split evenly over the k-waves");
   uint8_t* xs = reinterpret_cast<uint8_t*>(smem);  // [ROWS][ROW]
   uint8_t* ss = xs + ROWS * ROW;                    // [ROWS][KC/32]
@@ -1039,38 +1042,40 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
       }
     }
   };
-  uint64_t traw[EPI_TE][KP];
-  float tpl[EPI_TE];
-  // element idx = tid + 256 m of the row list: row of the block (from the list) and rank;
+  uint64_t traw[EPI_TH][KP];
+  float tpl[EPI_TH];
+  // element idx = tid + 256 (ph * EPI_TH + m) of the row list, one word each: row (bits
+  // 0-7), rank index (8-15), the row's rank (16-23, filled in when the tags are checked);
   // all the list reads go out before the first use, so their latencies overlap
-  int trow[EPI_TE], tcol[EPI_TE];
-  auto t_elements = [&]() {
+  int tinf[EPI_TH];
+  auto trow = [&](int m) { return tinf[m] & 255; };
+  auto tcol = [&](int m) { return (tinf[m] >> 8) & 255; };
+  auto t_elements = [&](int ph) {
     const int rm = __builtin_amdgcn_readfirstlane(p.r_max);
 #pragma unroll
-    for (int m = 0; m < EPI_TE; ++m) {
-      const int idx = min(tid + 256 * m, max(nel - 1, 0));
+    for (int m = 0; m < EPI_TH; ++m) {
+      const int idx = min(tid + 256 * (ph * EPI_TH + m), max(nel - 1, 0));
       const int q = idx / rm;
-      tcol[m] = idx - q * rm;
-      trow[m] = rowlist[min(q, ROWS - 1)];
+      tinf[m] = rowlist[min(q, ROWS - 1)] | ((idx - q * rm) << 8);
     }
   };
-  // t of the rows this split needs (all of them fit one batch of EPI_TE per thread):
+  // t of the rows this split needs (all of them fit EPI_PH batches of EPI_TH per thread):
   // tagged partials (fused) or the caller's plain t
-  auto load_t = [&]() {
-    t_elements();
+  auto load_t = [&](int ph) {
+    t_elements(ph);
     if (nel == 0) {
       // no rows: nothing to load
     } else if (p.t_tag) {  // unconditional loads from clamped addresses; tags checked later
 #pragma unroll
-      for (int m = 0; m < EPI_TE; ++m) {
-        const long addr = (long)(row0 + trow[m]) * p.r_max + tcol[m];
+      for (int m = 0; m < EPI_TH; ++m) {
+        const long addr = (long)(row0 + trow(m)) * p.r_max + tcol(m);
 #pragma unroll
         for (int k2 = 0; k2 < KP; ++k2)
           traw[m][k2] = ld_agent_u64(p.t_tag + (long)min(k2, p.t_kparts - 1) * p.T * p.r_max + addr);
       }
     } else {
 #pragma unroll
-      for (int m = 0; m < EPI_TE; ++m) tpl[m] = p.t[(long)(row0 + trow[m]) * p.r_max + tcol[m]];
+      for (int m = 0; m < EPI_TH; ++m) tpl[m] = p.t[(long)(row0 + trow(m)) * p.r_max + tcol(m)];
     }
   };
   // The stream's tagged t gather, issued before its last round of k-steps is multiplied:
@@ -1078,15 +1083,16 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   // needs, else a distinct word of x), so that none can be merged away and the waits for
   // those k-steps do not have to assume that fewer loads went out after them.
   auto load_t_stream = [&]() {
-    t_elements();  // list reads unconditional (a stale value is never used)
+    static_assert(!STREAM || EPI_PH == 1, "the stream gathers t in one batch");
+    t_elements(0);  // list reads unconditional (a stale value is never used)
     const int rm = max(p.r_max, 1);
     const uint64_t* dummy = reinterpret_cast<const uint64_t*>(p.x);
     const uint64_t tb = reinterpret_cast<uint64_t>(p.t_tag), xb = reinterpret_cast<uint64_t>(dummy);
     const bool tag_on = p.t_tag != nullptr;
 #pragma unroll
-    for (int m = 0; m < EPI_TE; ++m) {
+    for (int m = 0; m < EPI_TH; ++m) {
       const bool use = tag_on && tid + 256 * m < nel;
-      const long elem = (long)(row0 + trow[m]) * rm + tcol[m];
+      const long elem = (long)(row0 + trow(m)) * rm + tcol(m);
 #pragma unroll
       for (int k2 = 0; k2 < KP; ++k2) {
         const uint64_t a_use = tb + 8ull * (uint64_t)((long)min(k2, max(p.t_kparts, 1) - 1) * p.T * rm + elem);
@@ -1217,10 +1223,10 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   if (!STREAM && p.lora) {
     read_meta();
     if (n_batch > 0) stage_b(0);
-    load_t();
+    load_t(0);
   } else if (STREAM && p.lora) {
     if (n_batch > 0 && n_items > WK) stage_b(0);
-    if (!p.t_tag) load_t();
+    if (!p.t_tag) load_t(0);
   }
 
   // publish the launch epoch only now: waiting for it earlier would stall wave 0
@@ -1230,46 +1236,55 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
 
   // ---- epilogue: channel scale (of this K-split's sum: the splits are added scaled); with
   //      k-waves every wave scales its own part, and the parts are summed after the adapter
-  //      terms are added (one LDS reduction for both)
-  if (FMT == LORA_W_FP8_E4M3) {
+  //      terms are added (one LDS reduction for both).  It comes after the t gather, so that
+  //      the accumulators stay untouched (in AGPRs) while the gather holds its registers.
+  auto scale_acc = [&]() {
+    if (FMT == LORA_W_FP8_E4M3) {
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
+      for (int ct = 0; ct < CT; ++ct) {
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt) acc[tt][ct] *= chan_s[ct];
+        for (int tt = 0; tt < TT; ++tt) acc[tt][ct] *= chan_s[ct];
+      }
     }
-  }
+  };
+  if (!p.lora) scale_acc();
 
   // ---- epilogue: adapter up-projection (this K-split's share of the adapters)
   if (p.lora) {
     // (4) t of the rows this split needs -> LDS as bf16 pre-scaled by s_a (zero beyond the
     //     row's rank); the other rows of tbuf are never selected
-    int trk[EPI_TE];  // ranks of the elements' rows, read together
 #pragma unroll
-    for (int m = 0; m < EPI_TE; ++m) trk[m] = rowrk[trow[m]];
-    if (p.t_tag) {
+    for (int ph = 0; ph < EPI_PH; ++ph) {
+      if (ph > 0) load_t(ph);
 #pragma unroll
-      for (int m = 0; m < EPI_TE; ++m) {
-        if (tid + 256 * m >= nel) continue;
-        const int i = trow[m], j = tcol[m];
-        const long addr = (long)(row0 + i) * p.r_max + j;
-        float v = 0.f;
+      for (int m = 0; m < EPI_TH; ++m) tinf[m] |= rowrk[trow(m)] << 16;  // the rows' ranks, read together
+      auto trk = [&](int m) { return tinf[m] >> 16; };
+      if (p.t_tag) {
 #pragma unroll
-        for (int k2 = 0; k2 < KP; ++k2) {
-          if (j < trk[m] && k2 < p.t_kparts) {
-            const uint64_t w =
-                wait_tag(p.t_tag + (long)k2 * p.T * p.r_max + addr, traw[m][k2], tag, p.ctrl, p.spin_limit);
-            v += __uint_as_float((uint32_t)w);
+        for (int m = 0; m < EPI_TH; ++m) {
+          if (tid + 256 * (ph * EPI_TH + m) >= nel) continue;
+          const int i = trow(m), j = tcol(m);
+          const long addr = (long)(row0 + i) * p.r_max + j;
+          float v = 0.f;
+#pragma unroll
+          for (int k2 = 0; k2 < KP; ++k2) {
+            if (j < trk(m) && k2 < p.t_kparts) {
+              const uint64_t w =
+                  wait_tag(p.t_tag + (long)k2 * p.T * p.r_max + addr, traw[m][k2], tag, p.ctrl, p.spin_limit);
+              v += __uint_as_float((uint32_t)w);
+            }
           }
+          put(i, j, v);
         }
-        put(i, j, v);
-      }
-    } else {
+      } else {
 #pragma unroll
-      for (int m = 0; m < EPI_TE; ++m) {
-        if (tid + 256 * m >= nel) continue;
-        put(trow[m], tcol[m], tcol[m] < trk[m] ? tpl[m] : 0.f);
+        for (int m = 0; m < EPI_TH; ++m) {
+          if (tid + 256 * (ph * EPI_TH + m) >= nel) continue;
+          put(trow(m), tcol(m), tcol(m) < trk(m) ? tpl[m] : 0.f);
+        }
       }
     }
+    scale_acc();
     // (5) the stream's items with their B operands in registers ...
     if (STREAM && n_items <= WK) {
       __syncthreads();  // the staged t
