@@ -7,6 +7,7 @@ always picked up.
 
 from __future__ import annotations
 
+import json
 import os
 import shutil
 import subprocess
@@ -26,7 +27,26 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wno-unused-result",
+    # per-kernel register, scratch and LDS use, kept next to the library (see resources())
+    "-Rpass-analysis=kernel-resource-usage",
 ]
+RESOURCES = LIB + ".resources.json"
+
+
+def parse_resources(stderr: str) -> dict:
+    """Per-kernel resource use from the compiler's kernel-resource-usage remarks."""
+    out, cur = {}, None
+    for line in stderr.splitlines():
+        if "[-Rpass-analysis=kernel-resource-usage]" not in line:
+            continue
+        body = line.split("remark:", 1)[1].rsplit("[-Rpass", 1)[0].strip()
+        key, _, val = body.partition(":")
+        key, val = key.strip(), val.strip()
+        if key == "Function Name":
+            cur = out.setdefault(val, {})
+        elif cur is not None:
+            cur[key] = int(val) if val.lstrip("-").isdigit() else val
+    return out
 
 
 def hipcc() -> str:
@@ -42,13 +62,26 @@ def build(verbose: bool = False) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    errs = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l)
+    lines = [l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l]
+    errs = "\n".join(l for l in lines if "kernel-resource-usage" not in l and not l.lstrip().startswith(("|", "^"))
+                     and not l.strip().isdigit())
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{errs}")
     if verbose and errs.strip():
         print(errs, file=sys.stderr)
     os.replace(tmp, LIB)
+    with open(RESOURCES, "w") as f:
+        json.dump(parse_resources(res.stderr), f, indent=1, sort_keys=True)
     return LIB
+
+
+def resources() -> dict:
+    """Resource use of every kernel of the last build (empty if none was recorded)."""
+    try:
+        with open(RESOURCES) as f:
+            return json.load(f)
+    except OSError:
+        return {}
 
 
 if __name__ == "__main__":
