@@ -95,7 +95,15 @@ LayerPlan make_plan(int T, int K, int N, int n_ad, int r_max, int fmt, bool fuse
   }
   pl.s_kpart_len = ceil_div(ceil_div(K, kparts), 256) * 256;
   pl.s_kparts = ceil_div(K, pl.s_kpart_len);
-  pl.n_shrink_wg = n_ad * pl.s_ntblk * pl.s_njg * pl.s_kparts;
+  pl.n_shrink_items = n_ad * pl.s_ntblk * pl.s_njg * pl.s_kparts;
+  // long batches in the fused launch: one workgroup per item that has tokens (most
+  // (adapter, token block) items lie past the end of their segment, and an idle workgroup
+  // still holds a CU the GEMM workgroups need).  The segments of T tokens fill at most
+  // ceil(T / tblk) + min(n_ad, T) token blocks: each adapter adds at most one partial block.
+  const int max_blocks = ceil_div(T, pl.s_tblk) + std::min(n_ad, T);
+  pl.n_shrink_wg = (fused && pl.s_cfg == 1)
+                       ? std::min(pl.n_shrink_items, max_blocks * pl.s_njg * pl.s_kparts)
+                       : pl.n_shrink_items;
 
   size_t off = 0;
   pl.off_ctrl = off;  off += 256;
@@ -275,6 +283,7 @@ lora_status gemm_lowp_lora_epilogue(const uint16_t* x, int32_t T, int32_t K, int
     sp.tblk = pl.s_tblk; sp.n_tblk = pl.s_ntblk; sp.n_jg = pl.s_njg; sp.jper = pl.s_jper;
     sp.kparts = pl.s_kparts; sp.kpart_len = pl.s_kpart_len;
     sp.seg_wait = build_in ? 1 : 0;
+    sp.compact = (pl.s_cfg == 1 && !build_in) ? 1 : 0;
     sp.spin_limit = SPIN_LIMIT;
   }
   GemmParams gp{};

@@ -329,8 +329,7 @@ __device__ __forceinline__ uint64_t wait_tag(const uint64_t* p, uint64_t v, uint
 // first loads are in flight (or when it finds no work); the tag is read after a barrier.
 template <int TG, int JP, int U>
 __device__ __forceinline__ void shrink_item(const ShrinkParams& p, int item, char* smem, int* ctrl, int e, int* lds_epoch,
-                            int* started) {
-  bool published = false;
+                                            int* started, bool& published) {
   auto publish = [&]() {
     if (ctrl && !published) *started = wg_epoch_publish(ctrl, e, lds_epoch);
     published = true;
@@ -496,7 +495,8 @@ template <int TG, int JP, int U>
 __global__ __launch_bounds__(256) void k_shrink(ShrinkParams p) {
   extern __shared__ __align__(16) char smem[];
   int started = 0;
-  shrink_item<TG, JP, U>(p, blockIdx.x, smem, nullptr, 0, nullptr, &started);
+  bool published = false;
+  shrink_item<TG, JP, U>(p, blockIdx.x, smem, nullptr, 0, nullptr, &started, published);
 }
 
 // ======================================================================================
@@ -1455,7 +1455,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     __syncthreads();
     if (threadIdx.x == 0) set_agent(gp.ctrl + CTRL_SEGREADY, e + 1);
   } else if (b < gp.n_shrink) {
-    shrink_item<TG, JP, U>(sp, b, smem, gp.ctrl, e, &lds_epoch, &started);
+    bool published = false;
+    int item = b;
+    if (sp.compact) {
+      // Long batches: most (adapter, token block) items lie past the end of their segment.
+      // Workgroup b takes the b-th item that has tokens, counted from the segment lengths
+      // (block prefix over the adapters, in LDS after the area the down-projection uses);
+      // the grid is sized for the most such items any batch of T tokens can have.
+      int* pre = reinterpret_cast<int*>(smem + sp.compact_off);  // [n_ad + 1] block prefix
+      int* wsum = pre + sp.n_ad + 1;
+      const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+      const int per = (sp.n_ad + 255) / 256;
+      const int lo = min(tid * per, sp.n_ad), hi = min(lo + per, sp.n_ad);
+      int cnt = 0;
+      for (int a = lo; a < hi; ++a) cnt += (sp.seg_indptr[a + 1] - sp.seg_indptr[a] + sp.tblk - 1) / sp.tblk;
+      int inc = cnt;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int u = __shfl_up(inc, off);
+        if (lane >= off) inc += u;
+      }
+      if (lane == 63) wsum[wave] = inc;
+      __syncthreads();
+      int base = inc - cnt;
+      for (int w = 0; w < wave; ++w) base += wsum[w];
+      for (int a = lo; a < hi; ++a) {
+        pre[a] = base;
+        base += (sp.seg_indptr[a + 1] - sp.seg_indptr[a] + sp.tblk - 1) / sp.tblk;
+      }
+      if (tid == 255) pre[sp.n_ad] = base;
+      __syncthreads();
+      const int n_valid = __builtin_amdgcn_readfirstlane(pre[sp.n_ad]) * sp.n_jg * sp.kparts;
+      if (b < n_valid) {
+        const int kp = b % sp.kparts, rest = b / sp.kparts;
+        const int jg = rest % sp.n_jg, blk = rest / sp.n_jg;
+        int lo_a = 0, hi_a = sp.n_ad;  // adapter a with pre[a] <= blk < pre[a + 1]
+        while (hi_a - lo_a > 1) {
+          const int mid = (lo_a + hi_a) >> 1;
+          if (__builtin_amdgcn_readfirstlane(pre[mid]) <= blk) lo_a = mid; else hi_a = mid;
+        }
+        const int tb = blk - __builtin_amdgcn_readfirstlane(pre[lo_a]);
+        item = (tb < sp.n_tblk) ? ((lo_a * sp.n_tblk + tb) * sp.n_jg + jg) * sp.kparts + kp : -1;
+      } else {
+        item = -1;
+      }
+    }
+    if (item >= 0) shrink_item<TG, JP, U>(sp, item, smem, gp.ctrl, e, &lds_epoch, &started, published);
+    if (!published) started = wg_epoch_publish(gp.ctrl, e, &lds_epoch);
   } else {
     // K-parts of t: the single-tile decode down-projection splits K
     constexpr int KPT = (TT == 1) ? 4 : 1;
@@ -1484,11 +1530,14 @@ static hipError_t launch_k(KernelT kern, int grid, size_t smem, hipStream_t stre
 }
 
 template <int FMT, int TT, int CT, int WC, int WK, bool XQ, int TG, int JP, int U, int OCC>
-static hipError_t launch_layer_t(const LayerPlan& pl, int grid, hipStream_t stream, const ShrinkParams& sp,
+static hipError_t launch_layer_t(const LayerPlan& pl, int grid, hipStream_t stream, const ShrinkParams& sp_in,
                                  const GemmParams& gp) {
+  ShrinkParams sp = sp_in;
+  sp.compact_off = (int)shrink_smem<TG, JP, U>();  // the block prefix lies after the down-projection's area
   const size_t sm = std::max(std::max((size_t)GemmSmem<TT, CT, WC, WK, OCC>::BYTES,
                                       gp.n_shrink > 0 ? shrink_smem<TG, JP, U>() : (size_t)0),
-                             gp.seg_build ? seg_lds_bytes(gp.T, gp.n_ad) : (size_t)0);
+                             std::max(gp.seg_build ? seg_lds_bytes(gp.T, gp.n_ad) : (size_t)0,
+                                      sp.compact ? (size_t)sp.compact_off + 4 * (size_t)(sp.n_ad + 1) + 16 : (size_t)0));
   return launch_k(k_layer<FMT, TT, CT, WC, WK, XQ, TG, JP, U, OCC>, grid, sm, stream, sp, gp);
 }
 
@@ -1522,8 +1571,8 @@ hipError_t launch_layer(const LayerPlan& pl, hipStream_t stream, const ShrinkPar
 }
 
 hipError_t launch_shrink(const LayerPlan& pl, hipStream_t stream, const ShrinkParams& sp) {
-  if (pl.s_cfg == 0) return launch_k(k_shrink<1, 1, 2>, pl.n_shrink_wg, shrink_smem<1, 1, 2>(), stream, sp);
-  if (pl.s_cfg == 1) return launch_k(k_shrink<4, 2, 1>, pl.n_shrink_wg, shrink_smem<4, 2, 1>(), stream, sp);
+  if (pl.s_cfg == 0) return launch_k(k_shrink<1, 1, 2>, pl.n_shrink_items, shrink_smem<1, 1, 2>(), stream, sp);
+  if (pl.s_cfg == 1) return launch_k(k_shrink<4, 2, 1>, pl.n_shrink_items, shrink_smem<4, 2, 1>(), stream, sp);
   return hipErrorInvalidValue;
 }
 

@@ -40,6 +40,8 @@ struct ShrinkParams {
   int jper;            // 16-rank tiles per group (1..4)
   int kparts, kpart_len;
   int seg_wait;        // the segments are built in the same launch: wait for them, read them coherently
+  int compact;         // fused launch: workgroups loop over the items with tokens (long batches)
+  int compact_off;     // LDS byte offset of the block prefix (after the down-projection's area)
   int spin_limit;
 };
 
@@ -93,6 +95,7 @@ struct LayerPlan {
   int ksplit, krange, n_cb, n_tb, n_gemm_wg;
   // down-projection decomposition
   int s_tblk, s_ntblk, s_njg, s_jper, s_kparts, s_kpart_len, n_shrink_wg;
+  int n_shrink_items;  // down-projection items (the standalone launch has one workgroup each)
   int n_build_wg;  // 1 when the launch also builds the segments
   // workspace layout (byte offsets)
   size_t off_ctrl, off_ttag, off_gflag, off_gpart, off_xq, off_xsc, total;
