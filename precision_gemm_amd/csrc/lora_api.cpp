@@ -10,6 +10,9 @@ using namespace lora;
 namespace {
 
 constexpr int SPIN_LIMIT = 1 << 23;  // bounded waits in the fused launch (about a second)
+// down-projection workgroups of a fused launch of 17 to 128 tokens (the rest of the CUs start
+// GEMM workgroups at once)
+constexpr int SHRINK_CAP = 256;
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -96,14 +99,15 @@ LayerPlan make_plan(int T, int K, int N, int n_ad, int r_max, int fmt, bool fuse
   pl.s_kpart_len = ceil_div(ceil_div(K, kparts), 256) * 256;
   pl.s_kparts = ceil_div(K, pl.s_kpart_len);
   pl.n_shrink_items = n_ad * pl.s_ntblk * pl.s_njg * pl.s_kparts;
-  // long batches in the fused launch: one workgroup per item that has tokens (most
-  // (adapter, token block) items lie past the end of their segment, and an idle workgroup
-  // still holds a CU the GEMM workgroups need).  The segments of T tokens fill at most
-  // ceil(T / tblk) + min(n_ad, T) token blocks: each adapter adds at most one partial block.
-  const int max_blocks = ceil_div(T, pl.s_tblk) + std::min(n_ad, T);
-  pl.n_shrink_wg = (fused && pl.s_cfg == 1)
-                       ? std::min(pl.n_shrink_items, max_blocks * pl.s_njg * pl.s_kparts)
-                       : pl.n_shrink_items;
+  // fused launch past 16 tokens: the down-projection workgroups take only the items that
+  // have work (an idle workgroup still holds a CU the GEMM workgroups need).  The segments
+  // of T tokens fill at most ceil(T / tblk) + min(n_ad, T) token blocks (each adapter adds
+  // at most one partial block).  Short batches cap the workgroups, each looping over its
+  // items, so that the GEMM workgroups start at once beside them.
+  const int max_items = (ceil_div(T, pl.s_tblk) + std::min(n_ad, T)) * pl.s_njg * pl.s_kparts;
+  pl.compact = fused && T > 16;
+  pl.n_shrink_wg = pl.compact ? std::min({pl.n_shrink_items, max_items, pl.s_cfg == 1 ? 1 << 30 : SHRINK_CAP})
+                              : pl.n_shrink_items;
 
   size_t off = 0;
   pl.off_ctrl = off;  off += 256;
@@ -283,7 +287,7 @@ lora_status gemm_lowp_lora_epilogue(const uint16_t* x, int32_t T, int32_t K, int
     sp.tblk = pl.s_tblk; sp.n_tblk = pl.s_ntblk; sp.n_jg = pl.s_njg; sp.jper = pl.s_jper;
     sp.kparts = pl.s_kparts; sp.kpart_len = pl.s_kpart_len;
     sp.seg_wait = build_in ? 1 : 0;
-    sp.compact = (pl.s_cfg == 1 && !build_in) ? 1 : 0;
+    sp.compact = pl.compact ? 1 : 0;
     sp.spin_limit = SPIN_LIMIT;
   }
   GemmParams gp{};

@@ -1394,22 +1394,29 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
     }
     __syncthreads();
     if (wk == 0) {
+      // the producers' sums are added to this split's in split order; all of one split's
+      // loads go out together (one memory round trip per split)
+      for (int k2 = 0; k2 < p.ksplit - 1; ++k2) {
+        const uint64_t* src =
+            reinterpret_cast<const uint64_t*>(p.gpart + ((tile_base + k2) * WC + wc) * PER_WAVE) + lane * 2;
+        uint64_t u[TT][CT][2];
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt)
+        for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          v4f sum = v4f{0.f, 0.f, 0.f, 0.f};
-          for (int k2 = 0; k2 < p.ksplit - 1; ++k2) {
-            const uint64_t* src = reinterpret_cast<const uint64_t*>(p.gpart + ((tile_base + k2) * WC + wc) * PER_WAVE +
-                                                                    ((tt * CT + ct) * 64 + lane) * 4);
-            const uint64_t u0 = ld_agent_u64(src), u1 = ld_agent_u64(src + 1);
-            sum[0] += __uint_as_float((uint32_t)u0);
-            sum[1] += __uint_as_float((uint32_t)(u0 >> 32));
-            sum[2] += __uint_as_float((uint32_t)u1);
-            sum[3] += __uint_as_float((uint32_t)(u1 >> 32));
+          for (int ct = 0; ct < CT; ++ct) {
+            u[tt][ct][0] = ld_agent_u64(src + (tt * CT + ct) * 128);
+            u[tt][ct][1] = ld_agent_u64(src + (tt * CT + ct) * 128 + 1);
           }
-          acc[tt][ct] = sum + acc[tt][ct];
-        }
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            acc[tt][ct][0] += __uint_as_float((uint32_t)u[tt][ct][0]);
+            acc[tt][ct][1] += __uint_as_float((uint32_t)(u[tt][ct][0] >> 32));
+            acc[tt][ct][2] += __uint_as_float((uint32_t)u[tt][ct][1]);
+            acc[tt][ct][3] += __uint_as_float((uint32_t)(u[tt][ct][1] >> 32));
+          }
+      }
     }
   }
 
@@ -1456,19 +1463,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     if (threadIdx.x == 0) set_agent(gp.ctrl + CTRL_SEGREADY, e + 1);
   } else if (b < gp.n_shrink) {
     bool published = false;
-    int item = b;
+    int n_valid = b + 1, stride = 1;
+    int* pre = reinterpret_cast<int*>(smem + sp.compact_off);  // [n_ad + 1] item prefix
     if (sp.compact) {
-      // Long batches: most (adapter, token block) items lie past the end of their segment.
-      // Workgroup b takes the b-th item that has tokens, counted from the segment lengths
-      // (block prefix over the adapters, in LDS after the area the down-projection uses);
-      // the grid is sized for the most such items any batch of T tokens can have.
-      int* pre = reinterpret_cast<int*>(smem + sp.compact_off);  // [n_ad + 1] block prefix
+      // Most (adapter, token block, rank group) items can be empty: token blocks past the
+      // end of a segment, rank groups past an adapter's rank.  The workgroups take the
+      // items that have work, k = b, b + n_shrink, ..., counted per adapter from the segment
+      // lengths and ranks (prefix over the adapters, in LDS after the area the
+      // down-projection uses), so that no workgroup holds a CU the GEMM needs for nothing.
+      // Segments built in this launch are waited for first (see shrink_item).
+      const bool coh = sp.seg_wait != 0;
+      if (coh) {
+        started = wg_epoch_publish(gp.ctrl, e, &lds_epoch);
+        published = true;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+          int spins = 0;
+          while (ld_agent(gp.ctrl + CTRL_SEGREADY) != lds_epoch + 1) {
+            __builtin_amdgcn_s_sleep(2);
+            if (++spins > sp.spin_limit) {
+              set_agent(gp.ctrl + CTRL_STATUS, 1);
+              break;
+            }
+          }
+        }
+        __syncthreads();
+      }
       int* wsum = pre + sp.n_ad + 1;
       const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+      auto count = [&](int a) {
+        const int len = coh ? ld_agent(sp.seg_indptr + a + 1) - ld_agent(sp.seg_indptr + a)
+                            : sp.seg_indptr[a + 1] - sp.seg_indptr[a];
+        const int r = sp.ranks[a];
+        const bool ok = r >= 8 && r <= sp.r_max && (r & 7) == 0;
+        const int nj = min(sp.n_jg, (r + 16 * JP - 1) / (16 * JP));
+        return ok ? (len + sp.tblk - 1) / sp.tblk * nj * sp.kparts : 0;
+      };
       const int per = (sp.n_ad + 255) / 256;
       const int lo = min(tid * per, sp.n_ad), hi = min(lo + per, sp.n_ad);
       int cnt = 0;
-      for (int a = lo; a < hi; ++a) cnt += (sp.seg_indptr[a + 1] - sp.seg_indptr[a] + sp.tblk - 1) / sp.tblk;
+      for (int a = lo; a < hi; ++a) cnt += count(a);
       int inc = cnt;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
@@ -1481,26 +1515,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
       for (int w = 0; w < wave; ++w) base += wsum[w];
       for (int a = lo; a < hi; ++a) {
         pre[a] = base;
-        base += (sp.seg_indptr[a + 1] - sp.seg_indptr[a] + sp.tblk - 1) / sp.tblk;
+        base += count(a);
       }
       if (tid == 255) pre[sp.n_ad] = base;
       __syncthreads();
-      const int n_valid = __builtin_amdgcn_readfirstlane(pre[sp.n_ad]) * sp.n_jg * sp.kparts;
-      if (b < n_valid) {
-        const int kp = b % sp.kparts, rest = b / sp.kparts;
-        const int jg = rest % sp.n_jg, blk = rest / sp.n_jg;
-        int lo_a = 0, hi_a = sp.n_ad;  // adapter a with pre[a] <= blk < pre[a + 1]
+      n_valid = __builtin_amdgcn_readfirstlane(pre[sp.n_ad]);
+      stride = gp.n_shrink;
+    }
+    for (int k = b; k < n_valid; k += stride) {
+      int item = k;
+      if (sp.compact) {
+        int lo_a = 0, hi_a = sp.n_ad;  // adapter a with pre[a] <= k < pre[a + 1]
         while (hi_a - lo_a > 1) {
           const int mid = (lo_a + hi_a) >> 1;
-          if (__builtin_amdgcn_readfirstlane(pre[mid]) <= blk) lo_a = mid; else hi_a = mid;
+          if (__builtin_amdgcn_readfirstlane(pre[mid]) <= k) lo_a = mid; else hi_a = mid;
         }
-        const int tb = blk - __builtin_amdgcn_readfirstlane(pre[lo_a]);
+        const int local = k - __builtin_amdgcn_readfirstlane(pre[lo_a]);
+        const int nj = min(sp.n_jg, (sp.ranks[lo_a] + 16 * JP - 1) / (16 * JP));
+        const int kp = local % sp.kparts, rest = local / sp.kparts;
+        const int jg = rest % nj, tb = rest / nj;
         item = (tb < sp.n_tblk) ? ((lo_a * sp.n_tblk + tb) * sp.n_jg + jg) * sp.kparts + kp : -1;
-      } else {
-        item = -1;
       }
+      if (item >= 0) shrink_item<TG, JP, U>(sp, item, smem, gp.ctrl, e, &lds_epoch, &started, published);
     }
-    if (item >= 0) shrink_item<TG, JP, U>(sp, item, smem, gp.ctrl, e, &lds_epoch, &started, published);
     if (!published) started = wg_epoch_publish(gp.ctrl, e, &lds_epoch);
   } else {
     // K-parts of t: the single-tile decode down-projection splits K

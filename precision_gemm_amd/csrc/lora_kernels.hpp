@@ -96,6 +96,7 @@ struct LayerPlan {
   // down-projection decomposition
   int s_tblk, s_ntblk, s_njg, s_jper, s_kparts, s_kpart_len, n_shrink_wg;
   int n_shrink_items;  // down-projection items (the standalone launch has one workgroup each)
+  bool compact;        // fused launch: the down-projection workgroups take the items that have work
   int n_build_wg;  // 1 when the launch also builds the segments
   // workspace layout (byte offsets)
   size_t off_ctrl, off_ttag, off_gflag, off_gpart, off_xq, off_xsc, total;
