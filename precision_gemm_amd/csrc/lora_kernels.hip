@@ -930,22 +930,22 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
     // (2) work items: one per adapter present in the token block and 32 of its ranks, in
     //     order of the adapter's first row (its leader), with the set of 16-row token tiles
     //     that hold its rows; each item's B operands then serve all those tiles
+    // The leader is found through a table of first rows indexed by adapter (n_ad <=
+    // MAX_ADAPTERS ints, in the B staging area, which is free until the main loop ends):
+    // the rows set their adapter's entry, then take the minimum with an LDS atomic.
     int my_lead = -1;
+    int* first_row = reinterpret_cast<int*>(stg);
+    static_assert(MAX_ADAPTERS * 4 <= epi_bstage<2>(), "first-row table in the B staging area");
+    const int a_row = (tid < ROWS) ? rowad[tid] : -1;  // -1 or an adapter index below n_ad
     if (tid < ROWS) {
       lead[tid] = 0;
       mine[tid] = 0;
-      const int a = rowad[tid];
-      if (a >= 0) {  // first row with the same adapter: four rows per LDS read, no early exit
-        my_lead = tid;
-        for (int l0 = 0; l0 < tid; l0 += 4) {
-          const int4 v = *reinterpret_cast<const int4*>(rowad + l0);
-          if (v.w == a && l0 + 3 < tid) my_lead = min(my_lead, l0 + 3);
-          if (v.z == a && l0 + 2 < tid) my_lead = min(my_lead, l0 + 2);
-          if (v.y == a && l0 + 1 < tid) my_lead = min(my_lead, l0 + 1);
-          if (v.x == a) my_lead = min(my_lead, l0);
-        }
-      }
     }
+    if (a_row >= 0) first_row[a_row] = ROWS;
+    __syncthreads();
+    if (a_row >= 0) atomicMin(first_row + a_row, tid);
+    __syncthreads();
+    if (a_row >= 0) my_lead = first_row[a_row];
     if (tid < ROWS) leadof[tid] = my_lead;
     __syncthreads();
     if (my_lead >= 0) atomicOr(lead + my_lead, 1 << (tid >> 4));
@@ -967,24 +967,24 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
         const int k = n_own + __popcll(bo & ((1ull << lane) - 1ull));
         n_own += __popcll(bo);
         if (own) lrow[k] = row;
+        // items of 32 ranks: one or two per adapter (ranks up to 64), so the inclusive prefix
+        // over the lanes is two ballot counts
+        static_assert(MAX_RANK <= 64, "at most two 32-rank items per adapter");
         const int nb = own ? ((rowrk[row] + 31) >> 5) : 0;
-        int incl = nb;
-  #pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-          const int v = __shfl_up(incl, d);
-          if (lane >= d) incl += v;
-        }
+        const unsigned long long b1 = __ballot(nb >= 1), b2 = __ballot(nb >= 2);
+        const unsigned long long le = (lane == 63) ? ~0ull : ((1ull << (lane + 1)) - 1ull);
+        const int incl = __popcll(b1 & le) + __popcll(b2 & le);
         for (int b = 0; b < nb; ++b) {
           items[n + incl - nb + b] = row | (b << 8) | (mask << 9) | ((k / spb) << 17);
           ioff[n + incl - nb + b] = (k % spb) * slot;
         }
-        n += __shfl(incl, 63);
+        n += __popcll(b1) + __popcll(b2);
       }
       // rows whose t this split needs (rows of its adapters), in row order
       int nr = 0;
       for (int c0 = 0; c0 < ROWS; c0 += 64) {
         const int row = c0 + lane;
-        const bool need = row < ROWS && rowrk[row] > 0 && mine[max(leadof[row], 0)];
+        const bool need = row < ROWS && rowrk[row] > 0 && (p.ksplit == 1 || mine[max(leadof[row], 0)]);
         const unsigned long long bl = __ballot(need);
         if (need) rowlist[nr + __popcll(bl & ((1ull << lane) - 1ull))] = row;
         nr += __popcll(bl);
