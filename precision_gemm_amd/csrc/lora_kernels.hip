@@ -599,13 +599,21 @@ struct EpiLayout {
 template <int TT, int CT, int WC, int WK, int OCC>
 struct GemmSmem {
   using CK = ChunkK<TT, CT>;
-  static constexpr int MAIN = TT * 16 * CK::ROW + TT * 16 * (CK::KC / 32);
+  // the chunked loop stages x in two buffers (chunk c + 1 is staged while chunk c is
+  // multiplied); the one-tile stream does not use them
+  static constexpr int XBUF = ((TT * 16 * CK::ROW + TT * 16 * (CK::KC / 32)) + 15) & ~15;
+  static constexpr int MAIN = (TT == 1) ? XBUF : 2 * XBUF;
   static constexpr int RED = (WK - 1) * WC * TT * CT * 256 * 4;
   static constexpr int POST = EpiLayout<TT, CT, WC, WK>::POST;
   static constexpr int M1 = MAIN > RED ? MAIN : RED;
   static constexpr int MD = ((M1 > POST ? M1 : POST) + 15) & ~15;  // metadata area, kept through the loop
   static constexpr int STG = (MD + EpiLayout<TT, CT, WC, WK>::MD_BYTES + 1023) & ~1023;  // B staging
-  static constexpr int BYTES = STG + epi_bstage<OCC>();
+  // B staging budget: what is left of the workgroup's share of the 160 KB LDS, at most
+  // epi_bstage (room for two slices of the widest tile at the largest rank)
+  static constexpr int LDS_WG = (160 * 1024 - 1024) / OCC;
+  static constexpr int BST = (epi_bstage<OCC>() < LDS_WG - STG) ? epi_bstage<OCC>() : ((LDS_WG - STG) & ~1023);
+  static_assert(BST >= 2 * WC * CT * 16 * MAX_RANK * 2, "LDS too small for two B slices");
+  static constexpr int BYTES = STG + BST;
 };
 
 template <int FMT, int TT, int CT, int WC, int WK, bool XQ, int KPT, int OCC>
@@ -624,8 +632,10 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   constexpr int EPI_PH = (EPI_TE > 16) ? 2 : 1;
   constexpr int EPI_TH = EPI_TE / EPI_PH;
   static_assert(STEPS % WK == 0, "k-steps per chunk must split evenly over the k-waves");
-  uint8_t* xs = reinterpret_cast<uint8_t*>(smem);  // [ROWS][ROW]
-  uint8_t* ss = xs + ROWS * ROW;                    // [ROWS][KC/32]
+  // x staging buffer b: [ROWS][ROW] codes, then [ROWS][KC/32] scale codes
+  constexpr int XBUF = GemmSmem<TT, CT, WC, WK, OCC>::XBUF;
+  auto xs_of = [&](int b) { return reinterpret_cast<uint8_t*>(smem) + b * XBUF; };
+  auto ss_of = [&](int b) { return reinterpret_cast<uint8_t*>(smem) + b * XBUF + ROWS * ROW; };
 
   // wave index as a scalar (see the down-projection)
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, li = lane & 15,
@@ -686,6 +696,7 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   static_assert(NP >= 1 && NBLK >= 1 && NBLK * 256 == ROWS * (KC / 32), "chunk does not split evenly");
   // chunks in flight (measured on the 64-token tile: three or four are no faster than two)
   constexpr int NBUF = 2;
+  static_assert(NBUF == 2, "x registers and LDS buffers alternate between two chunks");
   uint4 xr[NBUF][NX];
   // pre-quantised x: the chunk's scale codes, ROWS x SB bytes, are one load of wave 0
   // (lane l: rows SRL*l .. SRL*l + SRL - 1)
@@ -758,7 +769,9 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
       }
     }
   };
-  auto stage_x = [&](int buf) {
+  auto stage_x = [&](int buf) {  // x registers of buffer buf -> LDS buffer buf
+    uint8_t* xs = xs_of(buf);
+    uint8_t* ss = ss_of(buf);
     if (XQ) {
 #pragma unroll
       for (int m = 0; m < NP; ++m) {
@@ -792,7 +805,9 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
         *reinterpret_cast<uint32_t*>(ss + lane * 4) = xsc2[buf][0].x;
     }
   };
-  auto mma_chunk = [&](int buf, int c) {
+  auto mma_chunk = [&](int buf, int c) {  // LDS buffer and W registers of buffer buf
+    const uint8_t* xs = xs_of(buf);
+    const uint8_t* ss = ss_of(buf);
     const int kc0 = chunk_k0(c);
     const int nsteps = min(KC, ke - kc0) >> 7;
 #pragma unroll
@@ -914,8 +929,9 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   int* lrow = reinterpret_cast<int*>(md + EL::LROW);
   char* stg = smem + GemmSmem<TT, CT, WC, WK, OCC>::STG;
   const int slot = WN * p.r_max * 2;  // bytes of one B slice slot (a multiple of 512)
-  const int spb = epi_bstage<OCC>() / slot;  // slots per batch (>= 2)
-  static_assert(epi_bstage<OCC>() / (WN * 8 * 2) <= 256, "stage_b keeps a wave's slices one per lane");
+  constexpr int BST = GemmSmem<TT, CT, WC, WK, OCC>::BST;
+  const int spb = BST / slot;  // slots per batch (>= 2)
+  static_assert(BST / (WN * 8 * 2) <= 256, "stage_b keeps a wave's slices one per lane");
   auto prepare_epilogue = [&]() {
     // (1) adapter, rank, scale and B address of every row; a rank outside the limits
     //     drops the row's adapter term
@@ -935,7 +951,7 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
     // the rows set their adapter's entry, then take the minimum with an LDS atomic.
     int my_lead = -1;
     int* first_row = reinterpret_cast<int*>(stg);
-    static_assert(MAX_ADAPTERS * 4 <= epi_bstage<2>(), "first-row table in the B staging area");
+    static_assert(MAX_ADAPTERS * 4 <= BST, "first-row table in the B staging area");
     const int a_row = (tid < ROWS) ? rowad[tid] : -1;  // -1 or an adapter index below n_ad
     if (tid < ROWS) {
       lead[tid] = 0;
@@ -1163,17 +1179,21 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
     // Rounds of NBUF chunks, at least two: every round but the last refills each buffer with
     // the chunk NBUF ahead (past the last chunk: a chunk again, never multiplied), the last
     // round only multiplies.  As in the stream, no load depends on a branch, so the waits
-    // for a chunk's loads leave the later chunks' loads in flight.
+    // for a chunk's loads leave the later chunks' loads in flight.  x of chunk c + 1 goes
+    // into its LDS buffer while chunk c is multiplied from the other one, so each chunk
+    // takes one barrier; the x registers it frees are refilled with chunk c + 3.
     const int nround = max((nchunks + NBUF - 1) / NBUF, 2);
+    stage_x(0);
+    __syncthreads();
+    load_x(0, NBUF);
     auto c_round = [&](int r, bool refill) {
 #pragma unroll
       for (int u = 0; u < NBUF; ++u) {
         const int c = r * NBUF + u;
-        stage_x(u);
-        __syncthreads();
-        if (refill) load_x(u, c + NBUF);
         if (c < nchunks) mma_chunk(u, c);
         if (refill) load_w(u, c + NBUF);
+        if (refill || u + 1 < NBUF) stage_x(1 - u);
+        if (refill) load_x(1 - u, c + NBUF + 1);
         __syncthreads();
         if (c == 0 && p.lora) {
           prepare_epilogue();
