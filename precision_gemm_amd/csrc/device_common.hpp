@@ -22,6 +22,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return b >> 16;
 }
 
+// two floats to bf16 (round to nearest even) in one word, lo in bits 0..15: the gfx950
+// conversion instruction (finite values as f32_to_bf16_rne; NaN stays a quiet NaN)
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  const __bf16 l = (__bf16)lo, h = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
+}
+
 // ---------------------------------------------------------------------------------
 // MXFP8 quantisation of one 32-element block (OCP Microscaling v1.0, e4m3 elements):
 //   scale code = E + 127 with E = floor(log2 max|x|) - 8, clamped to [-127, 127];

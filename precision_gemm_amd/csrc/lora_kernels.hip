@@ -1441,18 +1441,53 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   }
 
   // ---- store bf16 (round to nearest even)
-  if (wk == 0) {
+  if constexpr (STREAM) {
+    if (wk == 0) {
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const int n = nw0 + ct * 16 + li;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int tok = row0 + tt * 16 + 4 * g + v;
+            if (tok < p.T) p.y[(long)tok * p.N + n] = (uint16_t)f32_to_bf16_rne(acc[tt][ct][v]);
+          }
+        }
+    }
+  } else {
+    // through LDS (the B staging area, free by now): a lane's values (four rows of one
+    // channel per 16x16 block) go in as bf16, then every thread stores 16 contiguous bytes
+    // of a row.  A 16-byte pad per row puts the four rows a lane group writes on different
+    // banks, where the tile then still fits the 16-bit offsets of the LDS writes.
+    constexpr int RS = (ROWS * (WN * 2 + 16) <= 65536) ? WN * 2 + 16 : WN * 2;
+    static_assert(WK == 1 && ROWS * RS <= BST, "output tile in the B staging area");
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
-        const int n = nw0 + ct * 16 + li;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int tok = row0 + tt * 16 + 4 * g + v;
-          if (tok < p.T) p.y[(long)tok * p.N + n] = (uint16_t)f32_to_bf16_rne(acc[tt][ct][v]);
-        }
+        char* dst = stg + (tt * 16 + 4 * g) * RS + (wc * CT * 16 + ct * 16 + li) * 2;
+        const uint32_t p01 = bf16x2_rne(acc[tt][ct][0], acc[tt][ct][1]);
+        const uint32_t p23 = bf16x2_rne(acc[tt][ct][2], acc[tt][ct][3]);
+        *reinterpret_cast<uint16_t*>(dst) = (uint16_t)p01;
+        *reinterpret_cast<uint16_t*>(dst + RS) = (uint16_t)(p01 >> 16);
+        *reinterpret_cast<uint16_t*>(dst + 2 * RS) = (uint16_t)p23;
+        *reinterpret_cast<uint16_t*>(dst + 3 * RS) = (uint16_t)(p23 >> 16);
       }
+    __syncthreads();
+    constexpr int CPR = WN / 8;  // 16-byte pieces per row
+    static_assert((ROWS * CPR) % 256 == 0, "output pieces split evenly over the threads");
+    constexpr int RPP = 256 / CPR;  // rows per pass of the workgroup
+    const int c8 = tid % CPR, r0 = tid / CPR;
+    const char* src = stg + r0 * RS + c8 * 16;
+    uint16_t* dst = p.y + (long)(row0 + r0) * p.N + n_tile0 + c8 * 8;
+    const long step = (long)RPP * p.N;
+    const int rows_left = p.T - row0 - r0;
+#pragma unroll 4
+    for (int i = 0; i < ROWS / RPP; ++i) {
+      const uint4 v = *reinterpret_cast<const uint4*>(src + i * RPP * RS);
+      if (i * RPP < rows_left) *reinterpret_cast<uint4*>(dst + i * step) = v;
+    }
   }
 }
 
