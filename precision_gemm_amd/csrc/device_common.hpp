@@ -139,6 +139,18 @@ __device__ __forceinline__ v4f mfma_scaled_16x16x128(const uint4& alo, const uin
   v8i a = {(int)alo.x, (int)alo.y, (int)alo.z, (int)alo.w, (int)ahi.x, (int)ahi.y, (int)ahi.z, (int)ahi.w};
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, FMT_B, 0, sa, 0, sb);
 }
+// The same with the A scale taken from byte `opa` (0..3) of a word of four codes; opa is
+// a constant after unrolling (the instruction encodes it).
+template <int FMT_B>
+__device__ __forceinline__ v4f mfma_scaled_16x16x128_sel(int opa, const uint4& alo, const uint4& ahi, const uint4& blo,
+                                                         const uint4& bhi, v4f acc, int sa_word, int sb) {
+  v8i a = {(int)alo.x, (int)alo.y, (int)alo.z, (int)alo.w, (int)ahi.x, (int)ahi.y, (int)ahi.z, (int)ahi.w};
+  v8i b = {(int)blo.x, (int)blo.y, (int)blo.z, (int)blo.w, (int)bhi.x, (int)bhi.y, (int)bhi.z, (int)bhi.w};
+  if (opa == 0) return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, FMT_B, 0, sa_word, 0, sb);
+  if (opa == 1) return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, FMT_B, 1, sa_word, 0, sb);
+  if (opa == 2) return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, FMT_B, 2, sa_word, 0, sb);
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, FMT_B, 3, sa_word, 0, sb);
+}
 __device__ __forceinline__ v8i join8(const uint4& lo, const uint4& hi) {
   return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }

@@ -628,14 +628,18 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   // t elements per thread per gather batch: the whole block's t (ROWS x 64) in one batch,
   // so that the gather costs one memory round trip
   constexpr int EPI_TE = (ROWS * MAX_RANK + 255) / 256;
-  // the 128-row tiles gather t in two halves (registers: one half of the loads in flight)
-  constexpr int EPI_PH = (EPI_TE > 16) ? 2 : 1;
+  // gather batches (one: the main loop's staging registers are free by then)
+  constexpr int EPI_PH = 1;
   constexpr int EPI_TH = EPI_TE / EPI_PH;
   static_assert(STEPS % WK == 0, "k-steps per chunk must split evenly over the k-waves");
   // x staging buffer b: [ROWS][ROW] codes, then [ROWS][KC/32] scale codes
   constexpr int XBUF = GemmSmem<TT, CT, WC, WK, OCC>::XBUF;
   auto xs_of = [&](int b) { return reinterpret_cast<uint8_t*>(smem) + b * XBUF; };
   auto ss_of = [&](int b) { return reinterpret_cast<uint8_t*>(smem) + b * XBUF + ROWS * ROW; };
+  // scale code of row `row`, 32-block k32 of the chunk: the TT codes a lane needs for one
+  // k-step (rows li + 16 tt, block 4 sp + g) lie next to each other
+  static_assert(TT == 1 || TT == 4 || TT == 8, "scale layout: four or eight token tiles");
+  auto sidx = [&](int row, int k32) { return (k32 * 16 + (row & 15)) * TT + (row >> 4); };
 
   // wave index as a scalar (see the down-projection)
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, li = lane & 15,
@@ -667,10 +671,14 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) acc[tt][ct] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // FP8 channel scales of the lane's columns, needed only in the epilogue
+  // FP8 channel scales of the lane's columns: the chunked loop loads them when it ends (no
+  // registers held through it), the one-tile stream at the start
   float chan_s[CT];
+  auto load_chan_s = [&]() {
 #pragma unroll
-  for (int ct = 0; ct < CT; ++ct) chan_s[ct] = (FMT == LORA_W_FP8_E4M3) ? p.ws_fp8[nw0 + ct * 16 + li] : 1.f;
+    for (int ct = 0; ct < CT; ++ct) chan_s[ct] = (FMT == LORA_W_FP8_E4M3) ? p.ws_fp8[nw0 + ct * 16 + li] : 1.f;
+  };
+  if constexpr (TT == 1) load_chan_s();
   // adapter of row `tid` of the token block for the epilogue: the id is loaded before the
   // bulk loads, its rank, scale and B address right after the first ones (loads retire
   // in order, so none of these waits for more than the id)
@@ -790,19 +798,16 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
         mx_block_quant(in, code, out);
         *reinterpret_cast<uint4*>(xs + row * ROW + k32 * 32) = out[0];
         *reinterpret_cast<uint4*>(xs + row * ROW + k32 * 32 + 16) = out[1];
-        ss[row * (KC / 32) + k32] = (uint8_t)code;
+        ss[sidx(row, k32)] = (uint8_t)code;
       }
     }
     if (XQ && wave == 0) {
-      if (SB == 8 && SRL == 2)
-        *reinterpret_cast<uint4*>(ss + lane * 16) =
-            make_uint4(xsc2[buf][0].x, xsc2[buf][0].y, xsc2[buf][SRL - 1].x, xsc2[buf][SRL - 1].y);
-      else if (SB == 8)
-        *reinterpret_cast<uint2*>(ss + lane * 8) = xsc2[buf][0];
-      else if (SRL == 2)
-        *reinterpret_cast<uint2*>(ss + lane * 8) = make_uint2(xsc2[buf][0].x, xsc2[buf][SRL - 1].x);
-      else
-        *reinterpret_cast<uint32_t*>(ss + lane * 4) = xsc2[buf][0].x;
+#pragma unroll
+      for (int h = 0; h < SRL; ++h)
+#pragma unroll
+        for (int k32 = 0; k32 < SB; ++k32)
+          ss[sidx(SRL * lane + h, k32)] =
+              (uint8_t)(((k32 < 4) ? xsc2[buf][h].x : xsc2[buf][h].y) >> (8 * (k32 & 3)));
     }
   };
   auto mma_chunk = [&](int buf, int c) {  // LDS buffer and W registers of buffer buf
@@ -815,17 +820,42 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
       const int s = wk + WK * i;
       if (s >= nsteps) break;
       const int sp = phys_step(s, nsteps);
+      // the scale codes of the lane's TT rows for this k-step: one read (the MFMA picks
+      // the byte), and the x fragment of token tile tt + 1 is read before the MFMAs of
+      // tile tt go out, so that its LDS latency overlaps them
+      const uint8_t* sb = ss + sidx(li, sp * 4 + g);
+      uint32_t sc[2];
+      if constexpr (TT == 8) {
+        const uint2 v = *reinterpret_cast<const uint2*>(sb);
+        sc[0] = v.x;
+        sc[1] = v.y;
+      } else {
+        sc[0] = *reinterpret_cast<const uint32_t*>(sb);
+        sc[1] = 0u;
+      }
+      uint4 alo[2], ahi[2];
+      auto frag = [&](int tt) {
+        const uint8_t* xp = xs + (tt * 16 + li) * ROW + sp * 128 + 16 * g;
+        alo[tt & 1] = *reinterpret_cast<const uint4*>(xp);
+        ahi[tt & 1] = *reinterpret_cast<const uint4*>(xp + 64);
+      };
+      frag(0);
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) {
-        const int row = tt * 16 + li;
-        const uint8_t* xp = xs + row * ROW + sp * 128 + 16 * g;
-        const uint4 alo = *reinterpret_cast<const uint4*>(xp);
-        const uint4 ahi = *reinterpret_cast<const uint4*>(xp + 64);
-        const int sa = ss[row * (KC / 32) + sp * 4 + g];
+        if (tt + 1 < TT) frag(tt + 1);
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
-          acc[tt][ct] = mfma_scaled_16x16x128<FMTB>(alo, ahi, wlo[buf][i][ct], whi[buf][i][ct], acc[tt][ct], sa,
-                                                     wsc[buf][i][ct]);
+          acc[tt][ct] = mfma_scaled_16x16x128_sel<FMTB>(tt & 3, alo[tt & 1], ahi[tt & 1], wlo[buf][i][ct],
+                                                         whi[buf][i][ct], acc[tt][ct], (int)sc[tt >> 2],
+                                                         wsc[buf][i][ct]);
+      }
+      // keep that order: the scale and first fragment reads, then per token tile the next
+      // fragment's reads ahead of the tile's MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        if (tt + 1 < TT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, CT, 0);
       }
     }
   };
@@ -1239,6 +1269,7 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
     tbuf[i * TSTR + j] = (uint16_t)f32_to_bf16_rne(v * rowsc[i]);
     if (p.t_out && cb == 0) p.t_out[(long)(row0 + i) * p.r_max + j] = v;
   };
+  if constexpr (TT != 1) load_chan_s();
   // ---- up-projection loads of the chunked path go out as soon as the main loop ends
   if (!STREAM && p.lora) {
     read_meta();
