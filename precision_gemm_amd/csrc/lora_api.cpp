@@ -284,6 +284,9 @@ lora_status gemm_lowp_lora_epilogue(const uint16_t* x, int32_t T, int32_t K, int
     sp.ids = adapter_id;
     sp.t_out = t;  // may be null
     sp.t_tag = ttag;
+    // past 16 tokens (one K-part): t goes to the epilogue as tagged bf16 pairs of s_a t
+    sp.t_pack = (pl.s_kparts == 1 && T > 16) ? 1 : 0;
+    sp.scales = scales;
     sp.tblk = pl.s_tblk; sp.n_tblk = pl.s_ntblk; sp.n_jg = pl.s_njg; sp.jper = pl.s_jper;
     sp.kparts = pl.s_kparts; sp.kpart_len = pl.s_kpart_len;
     sp.seg_wait = build_in ? 1 : 0;
@@ -300,6 +303,7 @@ lora_status gemm_lowp_lora_epilogue(const uint16_t* x, int32_t T, int32_t K, int
   gp.t_out = (fused && pl.s_kparts > 1) ? t : nullptr;
   gp.t_tag = fused ? ttag : nullptr;
   gp.t_kparts = pl.s_kparts;
+  gp.t_pack = (fused && pl.s_kparts == 1 && T > 16) ? 1 : 0;
   gp.r_max = r_max;
   gp.ids = adapter_id; gp.B_ptrs = B_ptrs; gp.ranks = ranks; gp.scales = scales; gp.n_ad = n_adapters;
   gp.y = y;

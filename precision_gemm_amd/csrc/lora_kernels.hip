@@ -327,7 +327,8 @@ __device__ __forceinline__ uint64_t wait_tag(const uint64_t* p, uint64_t v, uint
 // ======================================================================================
 // In the fused launch (ctrl != null) the workgroup publishes the launch epoch once its
 // first loads are in flight (or when it finds no work); the tag is read after a barrier.
-template <int TG, int JP, int U>
+// PACK: the launch may ask for t as tagged bf16 pairs (not in the one-tile stream's launch)
+template <int TG, int JP, int U, bool PACK = false>
 __device__ __forceinline__ void shrink_item(const ShrinkParams& p, int item, char* smem, int* ctrl, int e, int* lds_epoch,
                                             int* started, bool& published) {
   auto publish = [&]() {
@@ -457,6 +458,8 @@ __device__ __forceinline__ void shrink_item(const ShrinkParams& p, int item, cha
         *reinterpret_cast<v4f*>(red + (((wave * TG + tt) * JP + jt) * 64 + lane) * 4) = acc[tt][jt];
     __syncthreads();
     const uint32_t tag = ctrl ? (uint32_t)(*lds_epoch) + 1u : 0u;
+    const bool pack = PACK && p.t_pack;
+    const float s_a = pack ? p.scales[a] : 0.f;
 #pragma unroll
     for (int tt = 0; tt < TG; ++tt)
 #pragma unroll
@@ -470,9 +473,18 @@ __device__ __forceinline__ void shrink_item(const ShrinkParams& p, int item, cha
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int pos = t0 + tt * 16 + 4 * g + v;
+          const float other = pack ? __shfl_xor(sum[v], 1) : 0.f;  // rank j ^ 1, same token (uniform)
           if (pos < tok_end && j < r && (!direct || p.ids[pos] == a)) {
             const long tok = direct ? pos : tok_at(s0 + pos);
-            if (p.t_tag) st_agent_u64(p.t_tag + ((long)kp * p.T + tok) * p.r_max + j, tagged(sum[v], tag));
+            if (p.t_tag && pack) {
+              // one K-part: s_a t of ranks j, j + 1 as two bf16 under one tag (the GEMM
+              // epilogue's operands as they are)
+              if ((li & 1) == 0)
+                st_agent_u64(p.t_tag + tok * (p.r_max >> 1) + (j >> 1),
+                             ((uint64_t)tag << 32) | bf16x2_rne(sum[v] * s_a, other * s_a));
+            } else if (p.t_tag) {
+              st_agent_u64(p.t_tag + ((long)kp * p.T + tok) * p.r_max + j, tagged(sum[v], tag));
+            }
             if (p.t_out && p.kparts == 1) p.t_out[tok * p.r_max + j] = sum[v];
           }
         }
@@ -1096,11 +1108,14 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   int tinf[EPI_TH];
   auto trow = [&](int m) { return tinf[m] & 255; };
   auto tcol = [&](int m) { return (tinf[m] >> 8) & 255; };
+  // (with bf16 pairs, an element is a pair of ranks: rank index = pair index)
+  const bool tpack = !STREAM && p.t_tag && p.t_pack;
   auto t_elements = [&](int ph) {
-    const int rm = __builtin_amdgcn_readfirstlane(p.r_max);
+    const int rm = __builtin_amdgcn_readfirstlane(tpack ? p.r_max >> 1 : p.r_max);
+    const int ne = tpack ? nel >> 1 : nel;
 #pragma unroll
     for (int m = 0; m < EPI_TH; ++m) {
-      const int idx = min(tid + 256 * (ph * EPI_TH + m), max(nel - 1, 0));
+      const int idx = min(tid + 256 * (ph * EPI_TH + m), max(ne - 1, 0));
       const int q = idx / rm;
       tinf[m] = rowlist[min(q, ROWS - 1)] | ((idx - q * rm) << 8);
     }
@@ -1111,6 +1126,10 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
     t_elements(ph);
     if (nel == 0) {
       // no rows: nothing to load
+    } else if (tpack) {  // half the elements: pairs of ranks
+#pragma unroll
+      for (int m = 0; m < EPI_TH / 2; ++m)
+        traw[m][0] = ld_agent_u64(p.t_tag + (long)(row0 + trow(m)) * (p.r_max >> 1) + tcol(m));
     } else if (p.t_tag) {  // unconditional loads from clamped addresses; tags checked later
 #pragma unroll
       for (int m = 0; m < EPI_TH; ++m) {
@@ -1310,7 +1329,19 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
 #pragma unroll
       for (int m = 0; m < EPI_TH; ++m) tinf[m] |= rowrk[trow(m)] << 16;  // the rows' ranks, read together
       auto trk = [&](int m) { return tinf[m] >> 16; };
-      if (p.t_tag) {
+      if (tpack) {
+        static_assert(EPI_PH == 1 && EPI_TH % 2 == 0, "pairs: one gather batch");
+#pragma unroll
+        for (int m = 0; m < EPI_TH / 2; ++m) {
+          if (tid + 256 * m >= (nel >> 1)) continue;
+          const int i = trow(m), j = 2 * tcol(m);
+          uint32_t w2 = 0u;
+          if (j < trk(m))
+            w2 = (uint32_t)wait_tag(p.t_tag + (long)(row0 + i) * (p.r_max >> 1) + (j >> 1), traw[m][0], tag, p.ctrl,
+                                    p.spin_limit);
+          *reinterpret_cast<uint32_t*>(tbuf + i * TSTR + j) = w2;
+        }
+      } else if (p.t_tag) {
 #pragma unroll
         for (int m = 0; m < EPI_TH; ++m) {
           if (tid + 256 * (ph * EPI_TH + m) >= nel) continue;
@@ -1622,7 +1653,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
         const int jg = rest % nj, tb = rest / nj;
         item = (tb < sp.n_tblk) ? ((lo_a * sp.n_tblk + tb) * sp.n_jg + jg) * sp.kparts + kp : -1;
       }
-      if (item >= 0) shrink_item<TG, JP, U>(sp, item, smem, gp.ctrl, e, &lds_epoch, &started, published);
+      if (item >= 0) shrink_item<TG, JP, U, TT != 1>(sp, item, smem, gp.ctrl, e, &lds_epoch, &started, published);
     }
     if (!published) started = wg_epoch_publish(gp.ctrl, e, &lds_epoch);
   } else {

@@ -34,6 +34,8 @@ struct ShrinkParams {
   int n_ad, r_max;
   float* t_out;        // plain fp32 [T][r_max] (may be null in the fused launch)
   uint64_t* t_tag;     // tagged [kparts][T][r_max] (fused launch only, else null)
+  int t_pack;          // t_tag holds [T][r_max / 2] tagged bf16 pairs of s_a t (one K-part)
+  const float* scales; // adapter scales (for the pairs)
   int tblk;            // tokens of one segment per workgroup item (multiple of 16)
   int n_tblk;          // token blocks per adapter
   int n_jg;            // rank groups per adapter (16 * jper ranks each)
@@ -57,6 +59,7 @@ struct GemmParams {
   float* t_out;           // fused launch: the caller's t, written when t_kparts > 1 (may be null)
   const uint64_t* t_tag;  // tagged t partials (fused), or null
   int t_kparts;
+  int t_pack;             // t_tag holds tagged bf16 pairs of s_a t (see ShrinkParams)
   int r_max;
   const int* ids;
   const uint64_t* B_ptrs;  // B_a^T, bf16 [N][r_a]
