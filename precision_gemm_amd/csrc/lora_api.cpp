@@ -266,13 +266,19 @@ lora_status gemm_lowp_lora_epilogue(const uint16_t* x, int32_t T, int32_t K, int
   // (measured per step: 128 tokens x 128 adapters 190.4 us in-launch against 193.2 us;
   // 4096-token prefill 220.1 us in-launch against 218.0 us).
   const bool build_in = build && T <= 128;
-  if (build && !build_in &&
-      launch_build_segments(adapter_id, T, n_adapters, seg_indptr, sorted_tok, ctrl + CTRL_SEGERR, s) != hipSuccess)
-    return LORA_ERR_HIP;
-
   uint8_t* xq = reinterpret_cast<uint8_t*>(ws + pl.off_xq);
   uint8_t* xsc = reinterpret_cast<uint8_t*>(ws + pl.off_xsc);
-  if (pl.XQ && launch_quant(x, T, K, xq, xsc, s) != hipSuccess) return LORA_ERR_HIP;
+  if (build && !build_in && pl.XQ) {
+    // the builder as a workgroup of the MXFP8 pre-pass's launch
+    if (launch_quant_build(x, T, K, xq, xsc, adapter_id, n_adapters, seg_indptr, sorted_tok, ctrl + CTRL_SEGERR, s) !=
+        hipSuccess)
+      return LORA_ERR_HIP;
+  } else {
+    if (build && !build_in &&
+        launch_build_segments(adapter_id, T, n_adapters, seg_indptr, sorted_tok, ctrl + CTRL_SEGERR, s) != hipSuccess)
+      return LORA_ERR_HIP;
+    if (pl.XQ && launch_quant(x, T, K, xq, xsc, s) != hipSuccess) return LORA_ERR_HIP;
+  }
 
   uint64_t* ttag = reinterpret_cast<uint64_t*>(ws + pl.off_ttag);
 

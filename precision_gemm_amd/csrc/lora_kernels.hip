@@ -217,10 +217,10 @@ __device__ __forceinline__ uint32_t quad_swap1(uint32_t v) {  // value of lane ^
 __device__ __forceinline__ uint32_t quad_swap2(uint32_t v) {  // value of lane ^ 2 (DPP quad_perm 2,3,0,1)
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
 }
-__global__ __launch_bounds__(256) void k_quant_mxfp8(const uint16_t* __restrict__ x, int T, int K,
-                                                     uint8_t* __restrict__ xq, uint8_t* __restrict__ xsc) {
+__device__ __forceinline__ void quant_mxfp8_part(const uint16_t* __restrict__ x, int T, int K, uint8_t* __restrict__ xq,
+                                                 uint8_t* __restrict__ xsc, int block, int n_blocks) {
   const long total = (long)T * (K / 8);  // a multiple of 4: whole blocks, so quads stay together
-  for (long P = (long)blockIdx.x * blockDim.x + threadIdx.x; P < total; P += (long)gridDim.x * blockDim.x) {
+  for (long P = (long)block * 256 + threadIdx.x; P < total; P += (long)n_blocks * 256) {
     const uint4 in = ldg16(x + P * 8);
     uint32_t mx = absmax8_bits(in);
     mx = max(mx, quad_swap1(mx));
@@ -228,6 +228,28 @@ __global__ __launch_bounds__(256) void k_quant_mxfp8(const uint16_t* __restrict_
     const uint32_t code = mx_code_from_bits(mx);
     *reinterpret_cast<uint2*>(xq + P * 8) = mx_piece_quant(in, code);
     if ((P & 3) == 0) xsc[P >> 2] = (uint8_t)code;
+  }
+}
+__global__ __launch_bounds__(256) void k_quant_mxfp8(const uint16_t* __restrict__ x, int T, int K,
+                                                     uint8_t* __restrict__ xq, uint8_t* __restrict__ xsc) {
+  quant_mxfp8_part(x, T, K, xq, xsc, blockIdx.x, gridDim.x);
+}
+// The segment builder (workgroup 0) beside the MXFP8 pre-pass (the others) in one launch:
+// the two do not depend on each other, so the builder's latency hides behind the pre-pass.
+__global__ __launch_bounds__(256) void k_quant_build(const uint16_t* __restrict__ x, int T, int K,
+                                                     uint8_t* __restrict__ xq, uint8_t* __restrict__ xsc,
+                                                     const int* __restrict__ ids, int n_ad, int* __restrict__ seg_indptr,
+                                                     int* __restrict__ sorted_tok, int* __restrict__ err) {
+  extern __shared__ __align__(16) char smem[];
+  if (blockIdx.x == 0) {
+    int* w = reinterpret_cast<int*>(smem);
+    int* cnt = w + 16;
+    int* ids_s = cnt + seg_cnt_words(n_ad);
+    int* pres = ids_s + (T <= SEG_CACHE ? (T + 3) & ~3 : 0);
+    int* wcnt = pres + (T <= SEG_CACHE ? min(T, n_ad) : 0);
+    build_segments_wg<false>(ids, T, n_ad, seg_indptr, sorted_tok, err, cnt, ids_s, pres, wcnt, w, w + 4);
+  } else {
+    quant_mxfp8_part(x, T, K, xq, xsc, blockIdx.x - 1, gridDim.x - 1);
   }
 }
 
@@ -1739,6 +1761,14 @@ hipError_t launch_quant(const uint16_t* x, int T, int K, uint8_t* xq, uint8_t* x
   const int grid = (int)std::min<long>(blocks, 8192);
   hipLaunchKernelGGL(k_quant_mxfp8, dim3(grid), dim3(256), 0, s, x, T, K, xq, xsc);
   return hipGetLastError();
+}
+
+hipError_t launch_quant_build(const uint16_t* x, int T, int K, uint8_t* xq, uint8_t* xsc, const int* ids, int n_ad,
+                              int* seg, int* sorted, int* err, hipStream_t s) {
+  static_assert(SEG_THREADS == 256, "the builder runs as a 256-thread workgroup of the pre-pass");
+  const long blocks = ((long)T * (K / 8) + 255) / 256;
+  const int grid = 1 + (int)std::min<long>(blocks, 8192);
+  return launch_k(k_quant_build, grid, seg_lds_bytes(T, n_ad), s, x, T, K, xq, xsc, ids, n_ad, seg, sorted, err);
 }
 
 hipError_t launch_expand(const ExpandParams& p, hipStream_t s) {

@@ -107,6 +107,9 @@ struct LayerPlan {
 
 hipError_t launch_build_segments(const int* ids, int T, int n_ad, int* seg, int* sorted, int* err, hipStream_t s);
 hipError_t launch_quant(const uint16_t* x, int T, int K, uint8_t* xq, uint8_t* xsc, hipStream_t s);
+// the segment builder and the MXFP8 pre-pass in one launch (independent of each other)
+hipError_t launch_quant_build(const uint16_t* x, int T, int K, uint8_t* xq, uint8_t* xsc, const int* ids, int n_ad,
+                              int* seg, int* sorted, int* err, hipStream_t s);
 hipError_t launch_shrink(const LayerPlan& pl, hipStream_t stream, const ShrinkParams& sp);
 hipError_t launch_expand(const ExpandParams& p, hipStream_t s);
 hipError_t launch_layer(const LayerPlan& pl, hipStream_t stream, const ShrinkParams& sp, const GemmParams& gp);
