@@ -110,13 +110,27 @@ def test_segments_random_and_bad_ids():
     import torch
     import precision_gemm_amd as P
     rng = np.random.default_rng(5)
-    for T, n in [(1, 1), (7, 3), (64, 32), (1000, 257), (4096, 8), (5000, 2048), (300, 8192)]:
+    cases = [(1, 1), (7, 3), (64, 32), (1000, 257), (4096, 8), (5000, 2048), (300, 8192),
+             (4000, 5), (2000, 64), (2048, 65), (4096, 8, "sorted"), (3000, 3, "sorted")]
+    for case in cases:
+        T, n = case[0], case[1]
         ids = rng.integers(0, n, T).astype(np.int32)
+        if len(case) > 2:  # contiguous segments, as in a prefill batch
+            ids = np.sort(ids)
         seg = P.build_segments(torch.from_numpy(ids).cuda(), n)
         s_ref, o_ref = oracle_segments(ids, n)
         assert np.array_equal(seg.seg_indptr.cpu().numpy(), s_ref)
         assert np.array_equal(seg.sorted_tok.cpu().numpy(), o_ref)
         assert int(seg.err.item()) == 0
+    # bad ids among few adapters in a long batch: skipped, the first one reported
+    ids = rng.integers(0, 4, 3000).astype(np.int32)
+    ids[[700, 1500, 2999]] = [7, -1, 4]
+    seg = P.build_segments(torch.from_numpy(ids).cuda(), 4)
+    assert int(seg.err.item()) == 701
+    keep = np.flatnonzero((ids >= 0) & (ids < 4))
+    s_ref, o_ref = oracle_segments(ids[keep], 4)
+    assert np.array_equal(seg.seg_indptr.cpu().numpy(), s_ref)
+    assert np.array_equal(seg.sorted_tok.cpu().numpy()[:keep.size], keep[o_ref])
     ids = np.array([0, 1, 5, 1, -2, 0], np.int32)
     seg = P.build_segments(torch.from_numpy(ids).cuda(), 2)
     assert int(seg.err.item()) == 3                      # 1 + first bad token index
