@@ -32,7 +32,8 @@ namespace lora {
 // ======================================================================================
 // Segment builder: seg_indptr (CSR over adapter ids) and sorted_tok (stable order)
 // ======================================================================================
-constexpr int SEG_THREADS = 256;
+constexpr int SEG_THREADS = 1024;  // the builder's own launch (latency-bound loops: 4 waves per SIMD)
+constexpr int SEG_SCRATCH = 32;    // LDS words before cnt: 16 wave sums, then misc
 constexpr int SEG_CACHE = 4096;  // batches up to this size keep their ids in LDS between the passes
 
 // One workgroup builds the whole result.  LDS (caller's): cnt (n_ad ints), and for batches
@@ -45,7 +46,7 @@ constexpr int SEG_CACHE = 4096;  // batches up to this size keep their ids in LD
 // after a prefix over the chunks, writes their positions in token order, which keeps the
 // sort stable.  About 2 * T comparisons per present adapter.  Larger batches (ids read
 // from memory) are placed by one wave in token order, 64 tokens at a time.
-template <bool COH>
+template <bool COH, int NT>
 __device__ __forceinline__ void build_segments_wg(const int* __restrict__ ids, int T, int n_ad,
                                                   int* __restrict__ seg_indptr, int* __restrict__ sorted_tok,
                                                   int* __restrict__ err, int* cnt, int* ids_s, int* pres, int* wcnt,
@@ -63,11 +64,11 @@ __device__ __forceinline__ void build_segments_wg(const int* __restrict__ ids, i
     *first_bad = 0x7fffffff;
     *n_pres = 0;
   }
-  for (int a = tid; a < n_ad; a += SEG_THREADS) cnt[a] = 0;
+  for (int a = tid; a < n_ad; a += NT) cnt[a] = 0;
   __syncthreads();
   // 1. counts (LDS atomics: order-independent); ids read from memory once
   const bool cached = T <= SEG_CACHE;
-  for (int t = tid; t < T; t += SEG_THREADS) {
+  for (int t = tid; t < T; t += NT) {
     const int a = ids[t];
     if (cached) ids_s[t] = a;
     if (a >= 0 && a < n_ad) atomicAdd(&cnt[a], 1);
@@ -76,7 +77,7 @@ __device__ __forceinline__ void build_segments_wg(const int* __restrict__ ids, i
   __syncthreads();
   // 2. exclusive scan: a contiguous slice per thread, a wave scan, then the wave totals;
   //    the adapters present are listed (in any order) for the placement
-  const int per = (n_ad + SEG_THREADS - 1) / SEG_THREADS;
+  const int per = (n_ad + NT - 1) / NT;
   const int lo = min(tid * per, n_ad), hi = min(lo + per, n_ad);
   int s = 0;
   for (int a = lo; a < hi; ++a) s += cnt[a];
@@ -97,7 +98,7 @@ __device__ __forceinline__ void build_segments_wg(const int* __restrict__ ids, i
     if (cached && c > 0) pres[atomicAdd(n_pres, 1)] = a;
     base += c;
   }
-  if (tid == SEG_THREADS - 1) put(seg_indptr + n_ad, base);
+  if (tid == NT - 1) put(seg_indptr + n_ad, base);
   if (tid == 0) put(err, (*first_bad == 0x7fffffff) ? 0 : *first_bad + 1);
   __syncthreads();
   // 3. stable placement
@@ -106,12 +107,12 @@ __device__ __forceinline__ void build_segments_wg(const int* __restrict__ ids, i
     if (np == 0) return;
     // C chunks of L tokens (L a multiple of 4: the ids are read four at a time; reads past
     // T stay inside the LDS areas and are masked)
-    const int C = min(min(T, 64), max(1, min((2 * SEG_THREADS + np - 1) / np, SEG_CACHE / np)));
+    const int C = min(min(T, 64), max(1, min((2 * NT + np - 1) / np, SEG_CACHE / np)));
     const int L = (((T + C - 1) / C) + 3) & ~3;
     const int items = np * C;
     // (a) count of adapter pres[i] in chunk c; item = c * np + i, so that neighbouring lanes
     //     read the same ids (a broadcast, not a bank conflict); counts stored per adapter
-    for (int it = tid; it < items; it += SEG_THREADS) {
+    for (int it = tid; it < items; it += NT) {
       const int i = it % np, c = it / np, a = pres[i];
       const int t0 = c * L, t1 = min(T, t0 + L);
       int n = 0;
@@ -125,7 +126,7 @@ __device__ __forceinline__ void build_segments_wg(const int* __restrict__ ids, i
     // (b) per adapter: exclusive prefix over its C <= 64 chunks, from its start; a thread
     //     per adapter for few chunks, a wave per adapter for many
     if (C <= 16) {
-      for (int i = tid; i < np; i += SEG_THREADS) {
+      for (int i = tid; i < np; i += NT) {
         int run = cnt[pres[i]];
         for (int c = 0; c < C; ++c) {
           const int n = wcnt[i * C + c];
@@ -134,7 +135,7 @@ __device__ __forceinline__ void build_segments_wg(const int* __restrict__ ids, i
         }
       }
     } else {
-      for (int i = wave; i < np; i += SEG_THREADS / 64) {
+      for (int i = wave; i < np; i += NT / 64) {
         const int v = (lane < C) ? wcnt[i * C + lane] : 0;
         int inc = v;
 #pragma unroll
@@ -147,7 +148,7 @@ __device__ __forceinline__ void build_segments_wg(const int* __restrict__ ids, i
     }
     __syncthreads();
     // (c) positions, in token order within the chunk
-    for (int it = tid; it < items; it += SEG_THREADS) {
+    for (int it = tid; it < items; it += NT) {
       const int i = it % np, c = it / np, a = pres[i];
       const int t0 = c * L, t1 = min(T, t0 + L);
       int pos = wcnt[i * C + c];
@@ -185,11 +186,11 @@ __device__ __forceinline__ void build_segments_wg(const int* __restrict__ ids, i
   }
 }
 
-// LDS bytes of the builder: 16 words of scratch, cnt, and for cached batches the ids, the
+// LDS bytes of the builder: SEG_SCRATCH words of scratch, cnt, and for cached batches the ids, the
 // adapters present and the chunk counts
 __host__ __device__ constexpr int seg_cnt_words(int n_ad) { return (n_ad + 3) & ~3; }  // keeps the id cache 16-byte aligned
 __host__ __device__ constexpr size_t seg_lds_bytes(int T, int n_ad) {
-  return 64 + 4 * (size_t)seg_cnt_words(n_ad) +
+  return 4 * (size_t)SEG_SCRATCH + 4 * (size_t)seg_cnt_words(n_ad) +
          (T <= SEG_CACHE ? 4 * (size_t)((T + 3) & ~3) + 4 * (size_t)(T < n_ad ? T : n_ad) + 4 * (size_t)SEG_CACHE + 16
                          : 0);
 }
@@ -199,11 +200,11 @@ __global__ __launch_bounds__(SEG_THREADS) void k_build_segments(const int* __res
                                                                 int* __restrict__ sorted_tok, int* __restrict__ err) {
   extern __shared__ __align__(16) char smem[];
   int* w = reinterpret_cast<int*>(smem);
-  int* cnt = w + 16;
+  int* cnt = w + SEG_SCRATCH;
   int* ids_s = cnt + seg_cnt_words(n_ad);
   int* pres = ids_s + (T <= SEG_CACHE ? (T + 3) & ~3 : 0);
   int* wcnt = pres + (T <= SEG_CACHE ? min(T, n_ad) : 0);
-  build_segments_wg<false>(ids, T, n_ad, seg_indptr, sorted_tok, err, cnt, ids_s, pres, wcnt, w, w + 4);
+  build_segments_wg<false, SEG_THREADS>(ids, T, n_ad, seg_indptr, sorted_tok, err, cnt, ids_s, pres, wcnt, w, w + 16);
 }
 
 // ======================================================================================
@@ -220,7 +221,7 @@ __device__ __forceinline__ uint32_t quad_swap2(uint32_t v) {  // value of lane ^
 __device__ __forceinline__ void quant_mxfp8_part(const uint16_t* __restrict__ x, int T, int K, uint8_t* __restrict__ xq,
                                                  uint8_t* __restrict__ xsc, int block, int n_blocks) {
   const long total = (long)T * (K / 8);  // a multiple of 4: whole blocks, so quads stay together
-  for (long P = (long)block * 256 + threadIdx.x; P < total; P += (long)n_blocks * 256) {
+  for (long P = (long)block * blockDim.x + threadIdx.x; P < total; P += (long)n_blocks * blockDim.x) {
     const uint4 in = ldg16(x + P * 8);
     uint32_t mx = absmax8_bits(in);
     mx = max(mx, quad_swap1(mx));
@@ -236,18 +237,19 @@ __global__ __launch_bounds__(256) void k_quant_mxfp8(const uint16_t* __restrict_
 }
 // The segment builder (workgroup 0) beside the MXFP8 pre-pass (the others) in one launch:
 // the two do not depend on each other, so the builder's latency hides behind the pre-pass.
-__global__ __launch_bounds__(256) void k_quant_build(const uint16_t* __restrict__ x, int T, int K,
+// Workgroups of SEG_THREADS threads (the builder's loops are latency-bound).
+__global__ __launch_bounds__(SEG_THREADS) void k_quant_build(const uint16_t* __restrict__ x, int T, int K,
                                                      uint8_t* __restrict__ xq, uint8_t* __restrict__ xsc,
                                                      const int* __restrict__ ids, int n_ad, int* __restrict__ seg_indptr,
                                                      int* __restrict__ sorted_tok, int* __restrict__ err) {
   extern __shared__ __align__(16) char smem[];
   if (blockIdx.x == 0) {
     int* w = reinterpret_cast<int*>(smem);
-    int* cnt = w + 16;
+    int* cnt = w + SEG_SCRATCH;
     int* ids_s = cnt + seg_cnt_words(n_ad);
     int* pres = ids_s + (T <= SEG_CACHE ? (T + 3) & ~3 : 0);
     int* wcnt = pres + (T <= SEG_CACHE ? min(T, n_ad) : 0);
-    build_segments_wg<false>(ids, T, n_ad, seg_indptr, sorted_tok, err, cnt, ids_s, pres, wcnt, w, w + 4);
+    build_segments_wg<false, SEG_THREADS>(ids, T, n_ad, seg_indptr, sorted_tok, err, cnt, ids_s, pres, wcnt, w, w + 16);
   } else {
     quant_mxfp8_part(x, T, K, xq, xsc, blockIdx.x - 1, gridDim.x - 1);
   }
@@ -1252,7 +1254,9 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
     // round only multiplies.  As in the stream, no load depends on a branch, so the waits
     // for a chunk's loads leave the later chunks' loads in flight.  x of chunk c + 1 goes
     // into its LDS buffer while chunk c is multiplied from the other one, so each chunk
-    // takes one barrier; the x registers it frees are refilled with chunk c + 3.
+    // takes one barrier; the x registers it frees are refilled with chunk c + 3.  Measured:
+    // staging and refilling x ahead of the chunk's MFMAs, prefill 149.7 -> 146.3 us;
+    // with the refill after them, 156.2 us.
     const int nround = max((nchunks + NBUF - 1) / NBUF, 2);
     stage_x(0);
     __syncthreads();
@@ -1261,10 +1265,18 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
 #pragma unroll
       for (int u = 0; u < NBUF; ++u) {
         const int c = r * NBUF + u;
-        if (c < nchunks) mma_chunk(u, c);
-        if (refill) load_w(u, c + NBUF);
-        if (refill || u + 1 < NBUF) stage_x(1 - u);
-        if (refill) load_x(1 - u, c + NBUF + 1);
+        if (refill) {
+          // x of c + 1 is staged and its registers refilled before the MFMAs of c go out:
+          // both are independent of them (with fewer than three chunks the first round
+          // already passes the last one)
+          stage_x(1 - u);
+          load_x(1 - u, c + NBUF + 1);
+          if (c < nchunks) mma_chunk(u, c);
+          load_w(u, c + NBUF);
+        } else {
+          if (c < nchunks) mma_chunk(u, c);
+          if (u + 1 < NBUF) stage_x(1 - u);
+        }
         __syncthreads();
         if (c == 0 && p.lora) {
           prepare_epilogue();
@@ -1591,12 +1603,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     // the launch's tag in the control block for down-projection workgroups that read them
     started = wg_epoch_publish(gp.ctrl, e, &lds_epoch);
     int* w = reinterpret_cast<int*>(smem);
-    int* cnt = w + 16;
+    int* cnt = w + SEG_SCRATCH;
     int* ids_s = cnt + seg_cnt_words(gp.n_ad);
     int* pres = ids_s + (gp.T <= SEG_CACHE ? (gp.T + 3) & ~3 : 0);
     int* wcnt = pres + (gp.T <= SEG_CACHE ? min(gp.T, gp.n_ad) : 0);
-    build_segments_wg<true>(gp.ids, gp.T, gp.n_ad, gp.seg_build, gp.sorted_build, gp.ctrl + CTRL_SEGERR, cnt, ids_s,
-                            pres, wcnt, w, w + 4);
+    build_segments_wg<true, 256>(gp.ids, gp.T, gp.n_ad, gp.seg_build, gp.sorted_build, gp.ctrl + CTRL_SEGERR, cnt,
+                                 ids_s, pres, wcnt, w, w + 16);
     wait_stores();
     __syncthreads();
     if (threadIdx.x == 0) set_agent(gp.ctrl + CTRL_SEGREADY, e + 1);
@@ -1695,14 +1707,18 @@ constexpr size_t shrink_smem() {
 }
 
 template <typename KernelT, typename... Args>
-static hipError_t launch_k(KernelT kern, int grid, size_t smem, hipStream_t stream, Args... args) {
+static hipError_t launch_kn(KernelT kern, int grid, int threads, size_t smem, hipStream_t stream, Args... args) {
   if (smem > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)smem);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), smem, stream, args...);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), smem, stream, args...);
   return hipGetLastError();
+}
+template <typename KernelT, typename... Args>
+static hipError_t launch_k(KernelT kern, int grid, size_t smem, hipStream_t stream, Args... args) {
+  return launch_kn(kern, grid, 256, smem, stream, args...);
 }
 
 template <int FMT, int TT, int CT, int WC, int WK, bool XQ, int TG, int JP, int U, int OCC>
@@ -1753,7 +1769,7 @@ hipError_t launch_shrink(const LayerPlan& pl, hipStream_t stream, const ShrinkPa
 }
 
 hipError_t launch_build_segments(const int* ids, int T, int n_ad, int* seg, int* sorted, int* err, hipStream_t s) {
-  return launch_k(k_build_segments, 1, seg_lds_bytes(T, n_ad), s, ids, T, n_ad, seg, sorted, err);
+  return launch_kn(k_build_segments, 1, SEG_THREADS, seg_lds_bytes(T, n_ad), s, ids, T, n_ad, seg, sorted, err);
 }
 
 hipError_t launch_quant(const uint16_t* x, int T, int K, uint8_t* xq, uint8_t* xsc, hipStream_t s) {
@@ -1765,10 +1781,10 @@ hipError_t launch_quant(const uint16_t* x, int T, int K, uint8_t* xq, uint8_t* x
 
 hipError_t launch_quant_build(const uint16_t* x, int T, int K, uint8_t* xq, uint8_t* xsc, const int* ids, int n_ad,
                               int* seg, int* sorted, int* err, hipStream_t s) {
-  static_assert(SEG_THREADS == 256, "the builder runs as a 256-thread workgroup of the pre-pass");
-  const long blocks = ((long)T * (K / 8) + 255) / 256;
-  const int grid = 1 + (int)std::min<long>(blocks, 8192);
-  return launch_k(k_quant_build, grid, seg_lds_bytes(T, n_ad), s, x, T, K, xq, xsc, ids, n_ad, seg, sorted, err);
+  const long blocks = ((long)T * (K / 8) + SEG_THREADS - 1) / SEG_THREADS;
+  const int grid = 1 + (int)std::min<long>(blocks, 2048);
+  return launch_kn(k_quant_build, grid, SEG_THREADS, seg_lds_bytes(T, n_ad), s, x, T, K, xq, xsc, ids, n_ad, seg, sorted,
+                   err);
 }
 
 hipError_t launch_expand(const ExpandParams& p, hipStream_t s) {
