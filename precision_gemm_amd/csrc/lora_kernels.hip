@@ -1324,9 +1324,11 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   };
   if constexpr (TT != 1) load_chan_s();
   // ---- up-projection loads of the chunked path go out as soon as the main loop ends
+  // B operands of the 128-row tiles straight into registers; the others stage B slices in LDS
+  constexpr bool RB = !STREAM && TT >= 8;
   if (!STREAM && p.lora) {
     read_meta();
-    if (n_batch > 0) stage_b(0);
+    if (!RB && n_batch > 0) stage_b(0);
     load_t(0);
   } else if (STREAM && p.lora) {
     if (n_batch > 0 && n_items > WK) stage_b(0);
@@ -1422,9 +1424,64 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
       }
       __syncthreads();  // the area of the k-wave sums lies over the staged t
     }
+    // ... the 128-row tiles' items with their B operands straight from memory in registers,
+    //     IB items at a time (a lane loads exactly its operand: 16 bytes of B_a^T per column
+    //     tile).  Staging the slices in LDS took a memory round trip per batch of slices:
+    //     down-projection 112.5 -> 103.7 us per step this way; the 64-row gate-up tiles
+    //     (about 20 rank-16 adapters each) stay faster with the LDS slices (45.4 against 46.3) ...
+    if constexpr (RB) {
+      __syncthreads();  // the staged t
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) myad[tt] = rowad[tt * 16 + li];
+      constexpr int IB = (CT >= 4) ? 2 : 8;
+      for (int i0 = 0; i0 < n_items; i0 += 64) {
+        const int iq = min(i0 + lane, n_items - 1);
+        const int it_l = items[iq];
+        const int row_l = it_l & 255;
+        const int a_l = rowad[row_l], r_l = rowrk[row_l];
+        const uint64_t bp_l = rowbp[row_l];
+        const int n_here = min(64, n_items - i0);
+        for (int q0 = 0; q0 < n_here; q0 += IB) {
+          // IB items' loads on every path (past the end: the last item again, not used)
+          uint4 bop[IB][CT];
+          int itq[IB], aq[IB], rq[IB];
+#pragma unroll
+          for (int u = 0; u < IB; ++u) {
+            const int q = min(q0 + u, n_here - 1);
+            itq[u] = __builtin_amdgcn_readlane(it_l, q);
+            aq[u] = __builtin_amdgcn_readlane(a_l, q);
+            rq[u] = __builtin_amdgcn_readlane(r_l, q);
+            const uint64_t bpu =
+                ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(bp_l >> 32), q) << 32) |
+                (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)bp_l, q);
+            const int jc = min(((itq[u] >> 8) & 1) * 32 + 8 * g, rq[u] - 8);
+            const uint16_t* bsrc = reinterpret_cast<const uint16_t*>(bpu);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+              bop[u][ct] = ldg16(bsrc + (long)(n_tile0 + wc * CT * 16 + ct * 16 + li) * rq[u] + jc);
+          }
+#pragma unroll
+          for (int u = 0; u < IB; ++u) {
+            if (q0 + u >= n_here) continue;  // uniform
+            const int mask = (itq[u] >> 9) & 255;
+            const int j = ((itq[u] >> 8) & 1) * 32 + 8 * g;
+            const bool valid = j < rq[u];
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt) {
+              if (!((mask >> tt) & 1)) continue;  // uniform: adapter absent from this token tile
+              const uint4 tv = *reinterpret_cast<const uint4*>(tbuf + (tt * 16 + li) * TSTR + j);
+              const uint4 aop = (valid && myad[tt] == aq[u]) ? tv : zero4();
+#pragma unroll
+              for (int ct = 0; ct < CT; ++ct)
+                lacc(tt, ct) = mfma_bf16_16x16x32(aop, valid ? bop[u][ct] : zero4(), lacc(tt, ct));
+            }
+          }
+        }
+      }
+    }
     // ... otherwise per batch: wait for this wave's copies, then every wave multiplies its
     //     items (the waves sharing columns split them: item i goes to wave i % WK)
-    for (int b = 0; b < ((STREAM && n_items <= WK) ? 0 : n_batch); ++b) {
+    for (int b = 0; b < ((RB || (STREAM && n_items <= WK)) ? 0 : n_batch); ++b) {
       if (b > 0) stage_b(b);
       wait_stores();  // all of this wave's memory operations, the LDS copies included
       __syncthreads();
