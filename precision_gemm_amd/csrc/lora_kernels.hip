@@ -1645,7 +1645,8 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
 }
 
 // OCC: workgroups per CU the registers are budgeted for (2 for the 64-token prefill tile,
-// so that one workgroup's epilogue and start-up latency overlap another's main loop)
+// so that one workgroup's epilogue and start-up latency overlap another's main loop, and
+// for the one-tile stream, whose few down-projection workgroups then share CUs)
 template <int FMT, int TT, int CT, int WC, int WK, bool XQ, int TG, int JP, int U, int OCC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void k_layer(ShrinkParams sp,
                                                                                                 GemmParams gp) {
@@ -1793,13 +1794,14 @@ static hipError_t launch_layer_t(const LayerPlan& pl, int grid, hipStream_t stre
 // GEMM tile (TT, CT, WC, WK, XQ), down-projection shape (decode, cfg 0: one 16-rank tile,
 // two-step prefetch; prefill, cfg 1: four token tiles, two rank tiles) and workgroups per CU
 #define LORA_LAYER_CASE(TT_, CT_, WC_, WK_, XQ_, CFG_, TG_, JP_, U_, OCC_)                                \
-  if (pl.TT == TT_ && pl.CT == CT_ && pl.WC == WC_ && pl.WK == WK_ && pl.XQ == XQ_ && pl.s_cfg == CFG_) \
+  if (pl.TT == TT_ && pl.CT == CT_ && pl.WC == WC_ && pl.WK == WK_ && pl.XQ == XQ_ && pl.s_cfg == CFG_ && \
+      (pl.occ == OCC_ || TT_ != 1))                                                                     \
     return launch_layer_t<FMT, TT_, CT_, WC_, WK_, XQ_, TG_, JP_, U_, OCC_>(pl, grid, stream, sp, gp);
 
 template <int FMT>
 static hipError_t launch_layer_f(const LayerPlan& pl, int grid, hipStream_t stream, const ShrinkParams& sp,
                                  const GemmParams& gp) {
-  LORA_LAYER_CASE(1, 2, 1, 4, false, 0, 1, 1, 2, 1)
+  LORA_LAYER_CASE(1, 2, 1, 4, false, 0, 1, 1, 2, 2)
   LORA_LAYER_CASE(4, 1, 4, 1, false, 0, 1, 1, 2, 1)
   LORA_LAYER_CASE(4, 2, 4, 1, false, 0, 1, 1, 2, 1)
   LORA_LAYER_CASE(4, 2, 4, 1, true, 0, 1, 1, 2, 1)

@@ -94,6 +94,7 @@ struct LayerPlan {
   int TT, CT, WC, WK;  // token tiles per workgroup, column tiles per wave, wave grid (columns x k)
   bool XQ;             // x is quantised by a separate pass into the workspace
   int s_cfg;           // down-projection tile shape: 0 decode, 1 prefill
+  int occ = 1;         // workgroups per CU the one-tile stream kernel is built for
   int KC;              // K-chunk staged in LDS
   int ksplit, krange, n_cb, n_tb, n_gemm_wg;
   // down-projection decomposition
