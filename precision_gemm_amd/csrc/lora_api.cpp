@@ -10,8 +10,9 @@ using namespace lora;
 namespace {
 
 constexpr int SPIN_LIMIT = 1 << 23;  // bounded waits in the fused launch (about a second)
-// down-projection workgroups of a fused launch of 17 to 128 tokens (the rest of the CUs start
-// GEMM workgroups at once)
+// down-projection workgroups of a fused launch of 17 to 128 tokens: one per CU at most, the
+// items beyond are looped over (fewer workgroups, so that GEMM workgroups could start beside
+// them, measured slower: the A stream wants every CU)
 constexpr int SHRINK_CAP = 256;
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -108,8 +109,7 @@ LayerPlan make_plan(int T, int K, int N, int n_ad, int r_max, int fmt, bool fuse
   // fused launch past 16 tokens: the down-projection workgroups take only the items that
   // have work (an idle workgroup still holds a CU the GEMM workgroups need).  The segments
   // of T tokens fill at most ceil(T / tblk) + min(n_ad, T) token blocks (each adapter adds
-  // at most one partial block).  Short batches cap the workgroups, each looping over its
-  // items, so that the GEMM workgroups start at once beside them.
+  // at most one partial block).  Short batches cap the workgroups at SHRINK_CAP.
   const int max_items = (ceil_div(T, pl.s_tblk) + std::min(n_ad, T)) * pl.s_njg * pl.s_kparts;
   pl.compact = fused && T > 16;
   pl.n_shrink_wg = pl.compact ? std::min({pl.n_shrink_items, max_items, pl.s_cfg == 1 ? 1 << 30 : SHRINK_CAP})
