@@ -582,14 +582,16 @@ __global__ __launch_bounds__(256) void k_expand(ExpandParams p) {
 //   * per 128-wide k-step a wave reads its TT x-fragments from LDS once and issues TT*CT
 //     scaled MFMAs (x scale from the MX block; W scale 1.0 for FP8, the block scale for
 //     MXFP4).
-// The WK wave sums meet in LDS in wave order.  With a K-split over workgroups, the splits
-// other than the last store their sums and a tagged flag; the last split of the tile
-// (highest id) waits for the flags, adds the sums in split order and runs the epilogue.
+// The WK wave sums meet in LDS in wave order.  With a K-split over workgroups, each split
+// adds the adapter terms of its share of the tile's adapters to its own sum; the splits
+// other than the last store their sums and a tagged flag, and the last split of the tile
+// (highest id) waits for the flags, adds the sums in split order and stores y.
 // Epilogue: FP8 channel scale; then, if the layer has adapters, the distinct adapters of
 // the token block are listed, t is gathered (waiting for its tag in the fused launch) and
-// stored pre-scaled as bf16 in LDS, B_a^T slices for the tile's columns are staged in LDS,
-// and for each token tile and each adapter present in it one bf16 MFMA per 32 ranks adds
-// (s_a t[tok]) @ B_a to the rows of that adapter's tokens; finally bf16 stores (RNE).
+// stored pre-scaled as bf16 in LDS, and for each token tile and each adapter present in it
+// one bf16 MFMA per 32 ranks adds (s_a t[tok]) @ B_a to the rows of that adapter's tokens,
+// the B_a^T operands read from slices staged in LDS (64-row tiles) or straight from memory
+// (128-row tiles); finally bf16 stores (RNE), through LDS for the chunked tiles.
 // ======================================================================================
 template <int TT, int CT>
 struct ChunkK {
