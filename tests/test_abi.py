@@ -98,3 +98,33 @@ def test_other_entry_points_validation(L):
     assert L.lora_pack_weight(0, FAKE, NULL, 128, 256, FAKE, NULL, NULL) == INVALID   # in place
     assert L.lora_pack_weight(3, FAKE, NULL, 128, 256, MISALIGNED, NULL, NULL) == INVALID
     assert L.lora_workspace_status(NULL, FAKE, NULL) == INVALID
+
+
+def test_plan_down_projection_grid_and_k_split():
+    """Host plan (no GPU): past 128 tokens the fused launch's down-projection grid holds
+    every item that has work for any segment structure of T tokens (each adapter adds at
+    most one partial token block); from 17 to 128 tokens it holds at most one workgroup per
+    CU (the workgroups loop over the rest); K-splits keep the GEMM grid within 224
+    workgroups once a shape has fewer than 128 tiles."""
+    import numpy as np
+    from precision_gemm_amd.ops import plan_info
+    rng = np.random.default_rng(3)
+    for T, n_ad, r_max, K, N in [(129, 2, 64, 4096, 4096), (300, 40, 64, 1024, 256), (4096, 8, 64, 4096, 4096),
+                                 (1000, 257, 32, 2048, 512), (4096, 1, 16, 4096, 8192), (2048, 4096, 64, 1024, 1024)]:
+        p = plan_info(T, K, N, n_ad, r_max)
+        tblk, njg, kparts, jper = p["s_tblk"], p["s_njg"], p["s_kparts"], 2
+        for _ in range(20):
+            n_used = int(rng.integers(1, min(n_ad, T) + 1))
+            cuts = np.sort(rng.choice(np.arange(1, T), n_used - 1, replace=False)) if n_used > 1 else np.array([], int)
+            lens = np.diff(np.concatenate([[0], cuts, [T]]))
+            ranks = rng.choice(np.arange(8, r_max + 1, 8), n_used)
+            items = sum(-(-int(L) // tblk) * min(njg, -(-int(r) // (16 * jper))) * kparts for L, r in zip(lens, ranks))
+            assert items <= p["n_shrink_wg"], (T, n_ad, items, p)
+    for T, n_ad in [(17, 4), (64, 32), (128, 128), (100, 5)]:
+        p = plan_info(T, 4096, 4096, n_ad, 64)
+        assert 1 <= p["n_shrink_wg"] <= 256
+    for T, K, N in [(128, 21504, 5376), (64, 4096, 1024), (100, 2048, 2048), (4096, 4096, 4096)]:
+        p = plan_info(T, K, N, 8, 64)
+        tiles = p["n_cb"] * p["n_tb"]
+        assert p["n_gemm_wg"] == tiles * p["ksplit"]
+        assert tiles >= 128 or p["n_gemm_wg"] <= max(224, tiles), p
