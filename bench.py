@@ -104,8 +104,8 @@ def main():
                          "the reference that scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                          "(multi-GPU sharding is described in DESIGN.md, not implemented)"}))
+        print(json.dumps({"error": "the layer runs on one GPU only; --gpus must be 1 "
+                          "(sharding across GPUs is not implemented)"}))
         sys.exit(2)
 
     import torch
