@@ -27,6 +27,11 @@ Storage (H1 = K, H2 = N; W is kept [N, K] so that MX blocks run along K):
 X is the MXFP8 form of the bf16 activations (``mxquant``); the adapters read the
 bf16 x itself and A, B are bf16.  The steps below run in the order of the
 formula: base product, then each adapter's down- and up-projection, then the sum.
+
+The EpiLoRA abstract also names an engine variant that keeps the activations in
+16 bits (to narrow the mismatch between generator and trainer).  There the base
+product reads x itself: ``layer(..., act="bf16")`` gives dequant(x . W) with no
+activation quantisation (``base_gemm_bf16``); everything else is unchanged.
 """
 
 from __future__ import annotations
@@ -92,6 +97,22 @@ def _weight_quantum_exp(w: LowpWeight) -> np.ndarray:
     return -1 + E.min(axis=1)                              # e2m1 grid step 2^-1
 
 
+def _exact_products_sum(X, Wd, qx, qw):
+    """X @ Wd.T in float64, exact where a sufficient condition holds, else math.fsum.
+
+    Every product X[t,k]*Wd[n,k] is a multiple of u = 2^(qx[t] + qw[n]) and has few
+    significant bits; if sum_k |X[t,k] Wd[n,k]| < 2^52 u every partial sum is an
+    exactly representable multiple of u, so the matmul is exact in any order.
+    Entries that fail the test are recomputed with ``math.fsum`` (correctly rounded).
+    """
+    S = X @ Wd.T
+    bound = np.abs(X) @ np.abs(Wd).T
+    limit = np.ldexp(1.0, (52 + qx[:, None] + qw[None, :]).astype(np.int32))
+    for t, n in np.argwhere(~(bound < limit)):
+        S[t, n] = math.fsum(X[t] * Wd[n])
+    return S
+
+
 def base_gemm(x_q, x_sc, w: LowpWeight) -> np.ndarray:
     """dequant(X . W): float64 [T, N] from MXFP8 activations and a low-precision W.
 
@@ -107,14 +128,30 @@ def base_gemm(x_q, x_sc, w: LowpWeight) -> np.ndarray:
     Wd, col_scale = dequant_weight(w)
     if X.shape[1] != Wd.shape[1]:
         raise ValueError("K mismatch between activations and weight")
-    S = X @ Wd.T
-    bound = np.abs(X) @ np.abs(Wd).T
     qx = -9 + (np.asarray(x_sc, dtype=np.int64) - 127).min(axis=1) if X.shape[1] else np.zeros(X.shape[0], np.int64)
-    qw = _weight_quantum_exp(w)
-    limit = np.ldexp(1.0, (52 + qx[:, None] + qw[None, :]).astype(np.int32))
-    bad = np.argwhere(~(bound < limit))
-    for t, n in bad:
-        S[t, n] = math.fsum(X[t] * Wd[n])
+    S = _exact_products_sum(X, Wd, qx, _weight_quantum_exp(w))
+    if col_scale is not None:
+        S = S * col_scale[None, :]
+    return S
+
+
+def base_gemm_bf16(x_bits, w: LowpWeight) -> np.ndarray:
+    """dequant(x . W) with the bf16 activations used as they are (16-bit variant).
+
+    A bf16 value m * 2^e (0.5 <= |m| < 1) has at most 8 significant bits, so it is a
+    multiple of 2^(e-8); a row of x is a multiple of 2^qx[t] with qx[t] the least
+    such exponent over its nonzero entries.  The same exactness test as
+    ``base_gemm`` applies; the FP8 channel scale is applied once to the sum.
+    """
+    x = bf16_to_f64(np.asarray(x_bits, dtype=np.uint16))
+    Wd, col_scale = dequant_weight(w)
+    if x.shape[1] != Wd.shape[1]:
+        raise ValueError("K mismatch between activations and weight")
+    _, e = np.frexp(x)
+    e = np.where(x != 0, e.astype(np.int64) - 8, np.iinfo(np.int32).max)
+    qx = e.min(axis=1) if x.shape[1] else np.zeros(x.shape[0], np.int64)
+    qx = np.where(qx == np.iinfo(np.int32).max, 0, qx)     # all-zero row: any quantum
+    S = _exact_products_sum(x, Wd, qx, _weight_quantum_exp(w))
     if col_scale is not None:
         S = S * col_scale[None, :]
     return S
@@ -146,11 +183,12 @@ def lora_terms(x_bits, A, B, scale, seg_indptr, sorted_tok, r_max: int):
     return t, y
 
 
-def layer(x_bits, w: LowpWeight, A, B, scale, adapter_id):
+def layer(x_bits, w: LowpWeight, A, B, scale, adapter_id, act: str = "mxfp8"):
     """The whole layer, unfused.  Returns a dict of float64 / integer arrays.
 
     Keys: ``y`` (= y_base + y_lora), ``y_base``, ``y_lora``, ``t``, ``x_q``, ``x_sc``,
-    ``seg_indptr``, ``sorted_tok``.
+    ``seg_indptr``, ``sorted_tok``.  ``act`` is "mxfp8" (the base product reads the
+    MXFP8 form of x) or "bf16" (it reads x itself; ``x_q`` and ``x_sc`` are then None).
 
     ``x_bits`` uint16 [T, K] bf16; ``A``/``B`` lists of bf16 (uint16) arrays
     [K, r_a] / [r_a, N]; ``scale`` float32 [n_adapters]; ``adapter_id`` int [T].
@@ -158,8 +196,14 @@ def layer(x_bits, w: LowpWeight, A, B, scale, adapter_id):
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     n_ad = len(A)
     seg_indptr, sorted_tok = build_segments(adapter_id, n_ad)
-    x_q, x_sc = quantize_mxfp8(x_bits)
-    y_base = base_gemm(x_q, x_sc, w)
+    if act == "mxfp8":
+        x_q, x_sc = quantize_mxfp8(x_bits)
+        y_base = base_gemm(x_q, x_sc, w)
+    elif act == "bf16":
+        x_q = x_sc = None
+        y_base = base_gemm_bf16(x_bits, w)
+    else:
+        raise ValueError(f"unknown activation form {act!r}")
     r_max = max(int(np.asarray(a).shape[1]) for a in A)
     t, y_lora = lora_terms(x_bits, A, B, np.asarray(scale, dtype=np.float32), seg_indptr, sorted_tok, r_max)
     return {

@@ -7,7 +7,10 @@
 * zero-B gives exactly the base GEMM, zero-W gives exactly the adapter term;
 * invariance under token permutation and adapter relabelling;
 * one adapter reduces to plain numpy matmuls;
-* the exactness guard's fallback on a wide dynamic range.
+* the exactness guard's fallback on a wide dynamic range;
+* the 16-bit activation variant (act="bf16"): exact rational brute force, the
+  merged-weight identity on x that is not MXFP8-exact, bitwise equality with the
+  MXFP8 form where that form is exact, and its guard fallback.
 """
 
 import json
@@ -62,13 +65,14 @@ def test_golden_handworked():
     assert out["sorted_tok"].tolist() == e["sorted_tok"]
 
 
-def _exact_layer(wl):
-    """Exact rationals: base sum, channel scale, adapter terms (slow; tiny shapes only)."""
+def _exact_layer(wl, act="mxfp8"):
+    """Exact rationals: base sum, channel scale, adapter terms (slow; tiny shapes only).
+
+    act="bf16": the base sum reads the bf16 x itself (the 16-bit activation variant)."""
     from oracle.mxquant import quantize_mxfp8, dequantize_mxfp8
-    x_q, x_sc = quantize_mxfp8(wl.x)
-    X = dequantize_mxfp8(x_q, x_sc)
-    Wd, cs = L.dequant_weight(_weight(wl))
     xb = codecs.bf16_to_f64(wl.x)
+    X = dequantize_mxfp8(*quantize_mxfp8(wl.x)) if act == "mxfp8" else xb
+    Wd, cs = L.dequant_weight(_weight(wl))
     T, N = X.shape[0], Wd.shape[0]
     Xf = [[Fraction(v) for v in row] for row in X]
     Wf = [[Fraction(v) for v in row] for row in Wd]
@@ -100,6 +104,22 @@ def test_fraction_brute_force(fmt):
             # base: exact sum, one rounding for the channel scale (FP8) or none (MXFP4)
             assert abs(Fraction(out["y_base"][t, n]) - base) <= abs(base) * Fraction(1, 2 ** 52)
             assert abs(float(lora) - out["y_lora"][t, n]) <= 1e-13 * max(1.0, abs(float(lora)))
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+def test_fraction_brute_force_bf16_activations(fmt):
+    ranks = np.array([8, 4], np.int32)
+    wl = workloads.make_custom(4, 64, 24, fmt, ranks, [0, 1, 1, 0], [2.0, 0.5], seed=12, a_std=1 / 8)
+    out = L.layer(wl.x, _weight(wl), wl.A, wl.B, wl.scale, wl.ids, act="bf16")
+    assert out["x_q"] is None and out["x_sc"] is None
+    ex = _exact_layer(wl, act="bf16")
+    for t in range(4):
+        for n in range(24):
+            base, lora = ex[t][n]
+            assert abs(Fraction(out["y_base"][t, n]) - base) <= abs(base) * Fraction(1, 2 ** 52)
+            assert abs(float(lora) - out["y_lora"][t, n]) <= 1e-13 * max(1.0, abs(float(lora)))
+    # random bf16 x is not MXFP8-exact: the two activation forms must give different sums
+    assert not np.array_equal(out["y_base"], L.layer(wl.x, _weight(wl), wl.A, wl.B, wl.scale, wl.ids)["y_base"])
 
 
 def test_fraction_brute_force_tiny_workload():
@@ -138,6 +158,52 @@ def test_merged_weight_identity(fmt):
         merged = Wfull + float(wl.scale[a]) * codecs.bf16_to_f64(wl.A[a]) @ codecs.bf16_to_f64(wl.B[a])
         ref = x[t] @ merged
         assert np.allclose(out["y"][t], ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+def test_bf16_activations_merged_weight_identity_and_mxfp8_exact_case(fmt):
+    rng = np.random.default_rng(23)
+    T, K, N, n_ad = 10, 256, 48, 3
+    ranks = np.array([8, 4, 16], np.int32)
+    ids = rng.integers(0, n_ad, T)
+    wl = workloads.make_custom(T, K, N, fmt, ranks, ids, [1.0, 0.5, 2.0], seed=24)
+    # (1) arbitrary bf16 x: y = x @ (W + s_a A_a B_a) per token with x as it is
+    out = L.layer(wl.x, _weight(wl), wl.A, wl.B, wl.scale, wl.ids, act="bf16")
+    Wd, cs = L.dequant_weight(_weight(wl))
+    Wfull = (Wd * (cs[:, None] if cs is not None else 1.0)).T
+    x = codecs.bf16_to_f64(wl.x)
+    for t in range(T):
+        a = ids[t]
+        merged = Wfull + float(wl.scale[a]) * codecs.bf16_to_f64(wl.A[a]) @ codecs.bf16_to_f64(wl.B[a])
+        ref = x[t] @ merged
+        assert np.allclose(out["y"][t], ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+    # (2) x whose MXFP8 form is exact: both activation forms give the same bits
+    wl.x = _grid_x(rng, T, K)
+    a16 = L.layer(wl.x, _weight(wl), wl.A, wl.B, wl.scale, wl.ids, act="bf16")
+    a8 = L.layer(wl.x, _weight(wl), wl.A, wl.B, wl.scale, wl.ids)
+    assert np.array_equal(a16["y"], a8["y"]) and np.array_equal(a16["y_base"], a8["y_base"])
+
+
+def test_bf16_activations_guard_fallback_and_zero_rows():
+    # a row with entries 2^120 apart and an all-zero row
+    K, N = 64, 5
+    x = np.zeros((2, K), np.float32)
+    x[0, :32] = 2.0 ** 60 * np.arange(1, 33)
+    x[0, 32:] = 2.0 ** -60 * np.arange(1, 33)
+    bits = workloads.bf16_bits(x)
+    rng = np.random.default_rng(1)
+    wq = rng.integers(0, 0x7F, (N, K)).astype(np.uint8) | (rng.integers(0, 2, (N, K)) << 7).astype(np.uint8)
+    w = LowpWeight("fp8", wq, np.full(N, 0.5, np.float32))
+    y = L.base_gemm_bf16(bits, w)
+    xb = codecs.bf16_to_f64(bits)
+    Wd = codecs.decode_e4m3fn(wq)
+    for n in range(N):
+        exact = sum(Fraction(a) * Fraction(b) for a, b in zip(xb[0], Wd[n])) * Fraction(1, 2)
+        assert abs(Fraction(y[0, n]) - exact) <= abs(exact) * Fraction(1, 2 ** 53)
+    assert not y[1].any()
+    with pytest.raises(ValueError):
+        L.layer(bits, w, [workloads.bf16_bits(np.zeros((K, 4), np.float32))],
+                [workloads.bf16_bits(np.zeros((4, N), np.float32))], np.ones(1, np.float32), [0, 0], act="fp16")
 
 
 def test_zero_b_is_exactly_base_and_zero_w_is_exactly_lora():
