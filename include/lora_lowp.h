@@ -104,7 +104,16 @@ enum {
    * that the batch needs no launch of its own for the segments.  Above 128 tokens the
    * call launches the builder just before the layer instead (the down-projection
    * would otherwise start late); the outputs are the same. */
-  LORA_BUILD_SEGMENTS = 1u << 1
+  LORA_BUILD_SEGMENTS = 1u << 1,
+  /* The engine variant that keeps activations in 16 bits ("EpiLoRA" abstract, on
+   * narrowing the mismatch between generator and trainer): the base product reads the
+   * bf16 x as it is, with no MXFP8 quantisation.  W is widened to bf16 in registers
+   * (FP8 codes exactly; MXFP4 codes times their block scale, exact while the value
+   * stays in bf16's normal range: block scale codes 2 .. 252 for any e2m1 code)
+   * and the products run on bf16 MFMA with fp32 accumulation; the FP8 channel scale
+   * and the adapter terms are applied as without the flag.  Up to 16 tokens (the
+   * decode path); above that the call returns LORA_ERR_UNSUPPORTED. */
+  LORA_ACT_BF16 = 1u << 2
 };
 
 /* Status code as text; never NULL. */

@@ -6,7 +6,7 @@ torch device tensors.  Build the library with ``python -m precision_gemm_amd.bui
 """
 
 from .ops import (  # noqa: F401
-    LORA_BUILD_SEGMENTS, LORA_FUSE_SHRINK, LORA_W_FP8_E4M3, LORA_W_MXFP4_E2M1, Adapters, LowpWeight, Segments,
+    LORA_ACT_BF16, LORA_BUILD_SEGMENTS, LORA_FUSE_SHRINK, LORA_W_FP8_E4M3, LORA_W_MXFP4_E2M1, Adapters, LowpWeight, Segments,
     alloc_workspace, build_segments, empty_segments, expand, gemm_lowp_lora_epilogue, pack_weight, plan_info,
     quant_act_mxfp8, shrink, version, workspace_bytes, workspace_segment_error, workspace_status,
 )

@@ -164,6 +164,21 @@ __device__ __forceinline__ v4f mfma_bf16_16x16x32(const uint4& a, const uint4& b
                                                  0, 0);
 }
 
+// Widening of W codes to bf16 with the gfx950 scaled conversions (exact: e4m3 and e2m1
+// values times a power of two fit bf16 unless the power leaves bf16's normal range).
+// Four e4m3fn codes (byte 0 first) -> four bf16 in two dwords (element 0 in the low half).
+__device__ __forceinline__ uint2 fp8x4_to_bf16(uint32_t v) {
+  return make_uint2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, false)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, true)));
+}
+// Eight e2m1 codes (low nibble of byte 0 first) times `s` (a power of two) -> eight bf16.
+__device__ __forceinline__ uint4 fp4x8_to_bf16(uint32_t v, float s) {
+  return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 0)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 1)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 2)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 3)));
+}
+
 // 16-byte load from global memory.  The address-space cast makes the compiler emit
 // global_load (counted by vmcnt only) rather than flat_load, which also counts in lgkmcnt
 // and forces full waits.

@@ -240,9 +240,11 @@ lora_status gemm_lowp_lora_epilogue(const uint16_t* x, int32_t T, int32_t K, int
   if (st != LORA_OK) return st;
   if ((st = check_adapters(n_adapters, r_max)) != LORA_OK) return st;
   if (w_fmt != LORA_W_FP8_E4M3 && w_fmt != LORA_W_MXFP4_E2M1) return LORA_ERR_INVALID_ARG;
-  if (flags & ~(uint32_t)(LORA_FUSE_SHRINK | LORA_BUILD_SEGMENTS)) return LORA_ERR_INVALID_ARG;
+  if (flags & ~(uint32_t)(LORA_FUSE_SHRINK | LORA_BUILD_SEGMENTS | LORA_ACT_BF16)) return LORA_ERR_INVALID_ARG;
   const bool build = (flags & LORA_BUILD_SEGMENTS) != 0;
   if (build && !(flags & LORA_FUSE_SHRINK)) return LORA_ERR_INVALID_ARG;
+  const bool a16 = (flags & LORA_ACT_BF16) != 0;
+  if (a16 && T > 16) return LORA_ERR_UNSUPPORTED;  // the one-tile stream only
   if (build && (!seg_indptr || !adapter_id || (T > 0 && !sorted_tok))) return LORA_ERR_INVALID_ARG;
   if (T == 0) {
     if (!build) return LORA_OK;
@@ -261,7 +263,8 @@ lora_status gemm_lowp_lora_epilogue(const uint16_t* x, int32_t T, int32_t K, int
   if (lora && (!adapter_id || !B_ptrs || !ranks || !scales)) return LORA_ERR_INVALID_ARG;
   if (fused && (!seg_indptr || !sorted_tok || !A_ptrs)) return LORA_ERR_INVALID_ARG;
   if (t && !aligned16(t)) return LORA_ERR_INVALID_ARG;
-  const LayerPlan pl = make_plan(T, K, N, n_adapters, r_max, w_fmt);
+  LayerPlan pl = make_plan(T, K, N, n_adapters, r_max, w_fmt);
+  pl.a16 = a16;
   if (!workspace || !aligned16(workspace) || workspace_bytes < pl.total) return LORA_ERR_WORKSPACE;
   char* ws = reinterpret_cast<char*>(workspace);
   hipStream_t s = as_stream(stream);

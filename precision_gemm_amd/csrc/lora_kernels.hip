@@ -654,7 +654,7 @@ struct GemmSmem {
   static constexpr int BYTES = STG + BST;
 };
 
-template <int FMT, int TT, int CT, int WC, int WK, bool XQ, int KPT, int OCC>
+template <int FMT, int TT, int CT, int WC, int WK, bool XQ, int KPT, int OCC, bool A16>
 __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* smem, int e, int* lds_epoch, int* started) {
   using CK = ChunkK<TT, CT>;
   constexpr int KC = CK::KC, STEPS = CK::STEPS, ROW = CK::ROW;
@@ -907,6 +907,12 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   //      K-block g, held by the lanes g' with g'/2 == g%2 in their first (g < 2) or second
   //      half: lanes g = 1 and g = 2 swap one code.
   constexpr bool STREAM = (TT == 1 && WC == 1 && WK == 4 && !XQ);
+  // 16-bit activations: x enters bf16 MFMAs as it is and W is widened to bf16 in
+  // registers (FP8: the lane's codes are at the k of its x pieces; MXFP4: lane (li, g)
+  // holds k = 32g .. 32g+31, one block, so x is read there and the block scale is
+  // applied in the widening).  The one-tile stream only.
+  static_assert(!A16 || STREAM, "16-bit activations: the one-tile stream only");
+  constexpr bool A16_FP4 = A16 && FMT == LORA_W_MXFP4_E2M1;
   constexpr int SD = 4;  // k-steps of a wave in flight (measured: 2, 3 and 6 are slower)
   const int nst = (ke - kb) >> 7;
   const int nmy = (nst > wk) ? (nst - wk + 3) / 4 : 0;
@@ -919,14 +925,14 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   uint4 sx[SD][4];
   v8i sw[SD][CT];
   int sws[SD][CT];
-  const uint16_t* xs_row = p.x + (long)min(row0 + li, p.T - 1) * K + kb + 16 * g;
+  const uint16_t* xs_row = p.x + (long)min(row0 + li, p.T - 1) * K + kb + (A16_FP4 ? 32 : 16) * g;
   auto s_issue = [&](int slot, int i) {
     const int ps = kstep(i);
     const uint16_t* xp = xs_row + ps * 128;
     sx[slot][0] = ldg16(xp);
     sx[slot][1] = ldg16(xp + 8);
-    sx[slot][2] = ldg16(xp + 64);
-    sx[slot][3] = ldg16(xp + 72);
+    sx[slot][2] = ldg16(xp + (A16_FP4 ? 16 : 64));
+    sx[slot][3] = ldg16(xp + (A16_FP4 ? 24 : 72));
     const long ksg = (kb >> 7) + ps;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
@@ -939,20 +945,42 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
       }
     }
   };
-  auto s_consume = [&](int slot) {
-    uint32_t m1 = max(absmax8_bits(sx[slot][0]), absmax8_bits(sx[slot][1]));
-    uint32_t m2 = max(absmax8_bits(sx[slot][2]), absmax8_bits(sx[slot][3]));
-    m1 = max(m1, (uint32_t)__shfl_xor((int)m1, 16));
-    m2 = max(m2, (uint32_t)__shfl_xor((int)m2, 16));
-    const uint32_t c1 = mx_code_from_bits(m1), c2 = mx_code_from_bits(m2);
-    const uint2 q0 = mx_piece_quant(sx[slot][0], c1), q1 = mx_piece_quant(sx[slot][1], c1);
-    const uint2 q2 = mx_piece_quant(sx[slot][2], c2), q3 = mx_piece_quant(sx[slot][3], c2);
-    const uint4 alo = make_uint4(q0.x, q0.y, q1.x, q1.y), ahi = make_uint4(q2.x, q2.y, q3.x, q3.y);
-    const uint32_t recv = (uint32_t)__shfl_xor((int)((g == 1) ? c2 : c1), 48);
-    const int sa = (int)((g == 0) ? c1 : ((g == 3) ? c2 : recv));
+  auto s_consume_a16 = [&](int slot) {
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
-      acc[0][ct] = mfma_scaled_16x16x128<FMTB>(alo, ahi, sw[slot][ct], acc[0][ct], sa, sws[slot][ct]);
+    for (int ct = 0; ct < CT; ++ct) {
+      const v8i w = sw[slot][ct];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        uint4 b;
+        if constexpr (A16_FP4) {
+          // e8m0 code c as the float 2^(c - 127) (exact widening for codes 2 .. 252)
+          b = fp4x8_to_bf16((uint32_t)w[m], __builtin_bit_cast(float, sws[slot][ct] << 23));
+        } else {
+          const uint2 lo = fp8x4_to_bf16((uint32_t)w[2 * m]), hi = fp8x4_to_bf16((uint32_t)w[2 * m + 1]);
+          b = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        }
+        acc[0][ct] = mfma_bf16_16x16x32(sx[slot][m], b, acc[0][ct]);
+      }
+    }
+  };
+  auto s_consume = [&](int slot) {
+    if constexpr (A16) {
+      s_consume_a16(slot);
+    } else {
+      uint32_t m1 = max(absmax8_bits(sx[slot][0]), absmax8_bits(sx[slot][1]));
+      uint32_t m2 = max(absmax8_bits(sx[slot][2]), absmax8_bits(sx[slot][3]));
+      m1 = max(m1, (uint32_t)__shfl_xor((int)m1, 16));
+      m2 = max(m2, (uint32_t)__shfl_xor((int)m2, 16));
+      const uint32_t c1 = mx_code_from_bits(m1), c2 = mx_code_from_bits(m2);
+      const uint2 q0 = mx_piece_quant(sx[slot][0], c1), q1 = mx_piece_quant(sx[slot][1], c1);
+      const uint2 q2 = mx_piece_quant(sx[slot][2], c2), q3 = mx_piece_quant(sx[slot][3], c2);
+      const uint4 alo = make_uint4(q0.x, q0.y, q1.x, q1.y), ahi = make_uint4(q2.x, q2.y, q3.x, q3.y);
+      const uint32_t recv = (uint32_t)__shfl_xor((int)((g == 1) ? c2 : c1), 48);
+      const int sa = (int)((g == 0) ? c1 : ((g == 3) ? c2 : recv));
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+        acc[0][ct] = mfma_scaled_16x16x128<FMTB>(alo, ahi, sw[slot][ct], acc[0][ct], sa, sws[slot][ct]);
+    }
   };
 
   // chunks 0 .. NBUF-1 in flight before anything waits; chunk c + NBUF is issued into the
@@ -1649,7 +1677,7 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
 // OCC: workgroups per CU the registers are budgeted for (2 for the 64-token prefill tile,
 // so that one workgroup's epilogue and start-up latency overlap another's main loop, and
 // for the one-tile stream, whose few down-projection workgroups then share CUs)
-template <int FMT, int TT, int CT, int WC, int WK, bool XQ, int TG, int JP, int U, int OCC>
+template <int FMT, int TT, int CT, int WC, int WK, bool XQ, int TG, int JP, int U, int OCC, bool A16>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void k_layer(ShrinkParams sp,
                                                                                                 GemmParams gp) {
   extern __shared__ __align__(16) char smem[];
@@ -1753,7 +1781,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
   } else {
     // K-parts of t: the single-tile decode down-projection splits K
     constexpr int KPT = (TT == 1) ? 4 : 1;
-    gemm_item<FMT, TT, CT, WC, WK, XQ, KPT, OCC>(gp, b - gp.n_shrink, smem, e, &lds_epoch, &started);
+    gemm_item<FMT, TT, CT, WC, WK, XQ, KPT, OCC, A16>(gp, b - gp.n_shrink, smem, e, &lds_epoch, &started);
   }
   wg_epoch_end(gp.ctrl, e, started);
 }
@@ -1781,7 +1809,7 @@ static hipError_t launch_k(KernelT kern, int grid, size_t smem, hipStream_t stre
   return launch_kn(kern, grid, 256, smem, stream, args...);
 }
 
-template <int FMT, int TT, int CT, int WC, int WK, bool XQ, int TG, int JP, int U, int OCC>
+template <int FMT, int TT, int CT, int WC, int WK, bool XQ, int TG, int JP, int U, int OCC, bool A16 = false>
 static hipError_t launch_layer_t(const LayerPlan& pl, int grid, hipStream_t stream, const ShrinkParams& sp_in,
                                  const GemmParams& gp) {
   ShrinkParams sp = sp_in;
@@ -1790,7 +1818,7 @@ static hipError_t launch_layer_t(const LayerPlan& pl, int grid, hipStream_t stre
                                       gp.n_shrink > 0 ? shrink_smem<TG, JP, U>() : (size_t)0),
                              std::max(gp.seg_build ? seg_lds_bytes(gp.T, gp.n_ad) : (size_t)0,
                                       sp.compact ? (size_t)sp.compact_off + 4 * (size_t)(sp.n_ad + 1) + 16 : (size_t)0));
-  return launch_k(k_layer<FMT, TT, CT, WC, WK, XQ, TG, JP, U, OCC>, grid, sm, stream, sp, gp);
+  return launch_k(k_layer<FMT, TT, CT, WC, WK, XQ, TG, JP, U, OCC, A16>, grid, sm, stream, sp, gp);
 }
 
 // GEMM tile (TT, CT, WC, WK, XQ), down-projection shape (decode, cfg 0: one 16-rank tile,
@@ -1803,6 +1831,11 @@ static hipError_t launch_layer_t(const LayerPlan& pl, int grid, hipStream_t stre
 template <int FMT>
 static hipError_t launch_layer_f(const LayerPlan& pl, int grid, hipStream_t stream, const ShrinkParams& sp,
                                  const GemmParams& gp) {
+  if (pl.a16) {  // 16-bit activations: the one-tile stream
+    if (pl.TT == 1 && pl.CT == 2 && pl.WC == 1 && pl.WK == 4 && !pl.XQ && pl.s_cfg == 0 && pl.occ == 2)
+      return launch_layer_t<FMT, 1, 2, 1, 4, false, 1, 1, 2, 2, true>(pl, grid, stream, sp, gp);
+    return hipErrorInvalidValue;
+  }
   LORA_LAYER_CASE(1, 2, 1, 4, false, 0, 1, 1, 2, 2)
   LORA_LAYER_CASE(4, 1, 4, 1, false, 0, 1, 1, 2, 1)
   LORA_LAYER_CASE(4, 2, 4, 1, false, 0, 1, 1, 2, 1)

@@ -95,6 +95,7 @@ struct LayerPlan {
   bool XQ;             // x is quantised by a separate pass into the workspace
   int s_cfg;           // down-projection tile shape: 0 decode, 1 prefill
   int occ = 1;         // workgroups per CU the one-tile stream kernel is built for
+  bool a16 = false;    // base product on the bf16 activations as they are (bf16 MFMA)
   int KC;              // K-chunk staged in LDS
   int ksplit, krange, n_cb, n_tb, n_gemm_wg;
   // down-projection decomposition

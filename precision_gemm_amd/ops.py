@@ -17,6 +17,7 @@ LORA_W_FP8_E4M3 = 0
 LORA_W_MXFP4_E2M1 = 1
 LORA_FUSE_SHRINK = 1
 LORA_BUILD_SEGMENTS = 2
+LORA_ACT_BF16 = 4
 
 _FMT = {"fp8": LORA_W_FP8_E4M3, "mxfp4": LORA_W_MXFP4_E2M1}
 
@@ -211,11 +212,13 @@ def expand(t: torch.Tensor, seg: Segments, ad: Adapters, y: torch.Tensor) -> tor
 def gemm_lowp_lora_epilogue(x: torch.Tensor, w: LowpWeight, seg: Segments | None, ad: Adapters | None,
                             ws: torch.Tensor, *, t: torch.Tensor | None = None, fuse_shrink: bool = True,
                             y: torch.Tensor | None = None, n_adapters: int | None = None,
-                            r_max: int | None = None, build_segments: bool = False) -> torch.Tensor:
+                            r_max: int | None = None, build_segments: bool = False,
+                            act_bf16: bool = False) -> torch.Tensor:
     """The fused layer.  With ``fuse_shrink`` the down-projection runs in the same
     launch (``t``, if given, receives it); otherwise ``t`` is an input and ``t=None``
     computes the base GEMM only.  With ``build_segments`` the same launch also fills
-    ``seg`` (from ``seg.adapter_id``; see ``empty_segments``)."""
+    ``seg`` (from ``seg.adapter_id``; see ``empty_segments``).  With ``act_bf16`` the
+    base product reads x in bf16 as it is (16-bit activations; up to 16 tokens)."""
     _dev(x, "x", torch.bfloat16)
     if not w.packed:
         raise ValueError("the GEMM reads W in the packed form: call pack_weight(w) once first")
@@ -225,7 +228,8 @@ def gemm_lowp_lora_epilogue(x: torch.Tensor, w: LowpWeight, seg: Segments | None
         y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
     n = ad.n if ad is not None else (n_adapters or 1)
     rm = ad.r_max if ad is not None else (r_max or 8)
-    flags = (LORA_FUSE_SHRINK if fuse_shrink else 0) | (LORA_BUILD_SEGMENTS if build_segments else 0)
+    flags = ((LORA_FUSE_SHRINK if fuse_shrink else 0) | (LORA_BUILD_SEGMENTS if build_segments else 0)
+             | (LORA_ACT_BF16 if act_bf16 else 0))
     g = lambda o, name: _ptr(getattr(o, name)) if o is not None else _ptr(None)  # noqa: E731
     check("gemm_lowp_lora_epilogue", lib().gemm_lowp_lora_epilogue(
         _ptr(x), T, K, N, _FMT[w.fmt], _ptr(w.q), _ptr(w.scale), _ptr(t),

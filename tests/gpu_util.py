@@ -28,13 +28,13 @@ def named_oracle(name: str, rows: tuple | None = None):
     return run_oracle(wl, rows)
 
 
-def run_oracle(wl, rows=None):
+def run_oracle(wl, rows=None, act="mxfp8"):
     ids = np.asarray(wl.ids)
     x = wl.x
     if rows is not None:
         rows = np.asarray(rows)
         x, ids = x[rows], ids[rows]
-    return oracle_layer(x, OracleWeight(wl.fmt, wl.w_q, wl.w_scale), wl.A, wl.B, wl.scale, ids)
+    return oracle_layer(x, OracleWeight(wl.fmt, wl.w_q, wl.w_scale), wl.A, wl.B, wl.scale, ids, act=act)
 
 
 def bf16_to_f64(t) -> np.ndarray:
@@ -62,9 +62,10 @@ def assert_t_close(t, t_ref, what=""):
     return f
 
 
-def run_gpu(wl, *, fused=True, want_t=True, base_only=False, build=False):
+def run_gpu(wl, *, fused=True, want_t=True, base_only=False, build=False, act_bf16=False):
     """Run the layer on the GPU; returns dict of numpy results.  build: the fused layer
-    call also builds the segments (no separate segment launch)."""
+    call also builds the segments (no separate segment launch); act_bf16: the base
+    product on the bf16 activations as they are."""
     import torch
     import precision_gemm_amd as P
     from workloads.device import upload
@@ -76,21 +77,22 @@ def run_gpu(wl, *, fused=True, want_t=True, base_only=False, build=False):
         seg.seg_indptr.fill_(-7)
         seg.sorted_tok.fill_(-7)
         t = torch.empty((wl.T, ad.r_max), dtype=torch.float32, device="cuda") if want_t else None
-        y = P.gemm_lowp_lora_epilogue(x, w, seg, ad, ws, t=t, fuse_shrink=True, build_segments=True)
+        y = P.gemm_lowp_lora_epilogue(x, w, seg, ad, ws, t=t, fuse_shrink=True, build_segments=True,
+                                      act_bf16=act_bf16)
         if t is not None:
             out["t"] = t
         torch.cuda.synchronize()
         seg.err.fill_(P.workspace_segment_error(ws))
     elif base_only:
-        y = P.gemm_lowp_lora_epilogue(x, w, seg, ad, ws, t=None, fuse_shrink=False)
+        y = P.gemm_lowp_lora_epilogue(x, w, seg, ad, ws, t=None, fuse_shrink=False, act_bf16=act_bf16)
     elif fused:
         t = torch.empty((wl.T, ad.r_max), dtype=torch.float32, device="cuda") if want_t else None
-        y = P.gemm_lowp_lora_epilogue(x, w, seg, ad, ws, t=t, fuse_shrink=True)
+        y = P.gemm_lowp_lora_epilogue(x, w, seg, ad, ws, t=t, fuse_shrink=True, act_bf16=act_bf16)
         if t is not None:
             out["t"] = t
     else:
         t = P.shrink(x, seg, ad, ws)
-        y = P.gemm_lowp_lora_epilogue(x, w, seg, ad, ws, t=t, fuse_shrink=False)
+        y = P.gemm_lowp_lora_epilogue(x, w, seg, ad, ws, t=t, fuse_shrink=False, act_bf16=act_bf16)
         out["t"] = t
     torch.cuda.synchronize()
     out["status"] = P.workspace_status(ws)

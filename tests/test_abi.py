@@ -69,7 +69,10 @@ def test_gemm_validation(L):
     assert _gemm(L, N=100) == UNSUPPORTED
     assert _gemm(L, T=70000) == UNSUPPORTED
     assert _gemm(L, fmt=7) == INVALID
-    assert _gemm(L, flags=4) == INVALID
+    assert _gemm(L, flags=8) == INVALID                  # unknown flag
+    assert _gemm(L, flags=2) == INVALID                  # segment build without the fused down-projection
+    assert _gemm(L, flags=5, T=17) == UNSUPPORTED        # 16-bit activations: up to 16 tokens
+    assert _gemm(L, flags=5) == WORKSPACE                # ... valid otherwise (fails at the workspace)
     assert _gemm(L, x=NULL) == INVALID
     assert _gemm(L, x=MISALIGNED) == INVALID
     assert _gemm(L, A=NULL) == INVALID                   # fused needs A
@@ -128,3 +131,12 @@ def test_plan_down_projection_grid_and_k_split():
         tiles = p["n_cb"] * p["n_tb"]
         assert p["n_gemm_wg"] == tiles * p["ksplit"]
         assert tiles >= 128 or p["n_gemm_wg"] <= max(224, tiles), p
+
+
+def test_flag_values_match_header():
+    import re
+    import precision_gemm_amd as P
+    text = open(_lib.HEADER).read()
+    vals = {m.group(1): 1 << int(m.group(2)) for m in re.finditer(r"(LORA_[A-Z0-9_]+) = 1u << (\d+)", text)}
+    assert vals == {"LORA_FUSE_SHRINK": P.LORA_FUSE_SHRINK, "LORA_BUILD_SEGMENTS": P.LORA_BUILD_SEGMENTS,
+                    "LORA_ACT_BF16": P.LORA_ACT_BF16}
