@@ -1,6 +1,6 @@
 """Benchmark of the fused multi-tenant LoRA layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_qkv] [--sets S]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_qkv] [--sets S] [--act mxfp8|bf16]
 
 A step is one pass of the whole hot path over one batch: one fused layer call
 (gemm_lowp_lora_epilogue with LORA_FUSE_SHRINK | LORA_BUILD_SEGMENTS: the segment builder,
@@ -8,7 +8,8 @@ the down-projection and the GEMM with its LoRA epilogue in one launch; above 16 
 also the MXFP8 pre-pass launch), from bf16 x and adapter ids to bf16 y.  The K timed steps are captured in one HIP graph and replayed once,
 bracketed by torch.cuda.synchronize(); inputs are resident in HBM.  Steps rotate over S
 copies of the inputs so that the weights are read from HBM rather than from the 256 MB
-Infinity Cache.
+Infinity Cache.  ``--act bf16`` times the 16-bit activation variant (LORA_ACT_BF16: x
+enters the base product in bf16, W widened to bf16; up to 16 tokens).
 
 Printed: one JSON line with the metric, the roofline of the dominant kernel (the fused
 layer kernel: algorithmic bytes or FLOPs per call over its average duration, timed with
@@ -54,7 +55,7 @@ def algorithmic(wl):
     return int(nbytes), flops
 
 
-def cpu_baseline(wl, budget_s: float = 12.0):
+def cpu_baseline(wl, budget_s: float = 12.0, act: str = "mxfp8"):
     """The oracle as it stands, timed on the host on a bounded sample of the workload."""
     from oracle.layer import LowpWeight, layer
     try:
@@ -67,7 +68,7 @@ def cpu_baseline(wl, budget_s: float = 12.0):
     rows = np.arange(wl.T) if wl.T <= 256 else np.linspace(0, wl.T - 1, 256).astype(int)
     runs, t0 = 0, time.perf_counter()
     while True:
-        layer(wl.x[rows], w, wl.A, wl.B, wl.scale, np.asarray(wl.ids)[rows])
+        layer(wl.x[rows], w, wl.A, wl.B, wl.scale, np.asarray(wl.ids)[rows], act=act)
         runs += 1
         el = time.perf_counter() - t0
         if el >= budget_s or runs >= 50:
@@ -98,6 +99,8 @@ def main():
                     choices=["tiny", "decode_qkv", "decode_gateup", "prefill", "downproj_fp4"])
     ap.add_argument("--sets", type=int, default=0, help="input copies to rotate over (0: enough for 2x 256 MB)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--act", choices=["mxfp8", "bf16"], default="mxfp8",
+                    help="activations of the base product: MXFP8 (default) or bf16 as they are")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph replay")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="after the timed region, run three plain device copies of this many MiB (untimed): "
@@ -117,6 +120,10 @@ def main():
     torch.cuda.set_device(dev)
     print(f"[bench] generating {args.workload}", file=sys.stderr, flush=True)
     wl = workloads.make(args.workload)
+    a16 = args.act == "bf16"
+    if a16 and wl.T > 16:
+        print(json.dumps({"error": "--act bf16: the 16-bit activation variant takes up to 16 tokens"}))
+        sys.exit(2)
     nbytes, flops = algorithmic(wl)
     sets = args.sets or max(1, min(32, int(np.ceil(2 * 256e6 / nbytes)) + 1))
     print(f"[bench] uploading {sets} input set(s) of {nbytes / 1e6:.1f} MB", file=sys.stderr, flush=True)
@@ -132,7 +139,7 @@ def main():
     def step(s):
         d = S[s % sets]
         P.gemm_lowp_lora_epilogue(d["x"], d["w"], d["seg"], d["ad"], d["ws"], fuse_shrink=True, y=d["y"],
-                                  build_segments=True)
+                                  build_segments=True, act_bf16=a16)
 
     # The layer kernel as the step launches it: up to 128 tokens the segment builder is a
     # workgroup of that launch; above, the call launches the builder first, and the layer
@@ -143,7 +150,7 @@ def main():
     def layer_call(s):
         d = S[s % sets]
         P.gemm_lowp_lora_epilogue(d["x"], d["w"], d["seg"], d["ad"], d["ws"], fuse_shrink=True, y=d["y"],
-                                  build_segments=in_launch)
+                                  build_segments=in_launch, act_bf16=a16)
 
     def quant_call(s):  # the MXFP8 pre-pass that the call runs before the layer kernel
         P.quant_act_mxfp8(S[s % sets]["x"])
@@ -155,7 +162,8 @@ def main():
     try:
         from oracle.layer import LowpWeight, layer
         rows = np.arange(wl.T) if wl.T <= 256 else np.linspace(0, wl.T - 1, 128).astype(int)
-        ref = layer(wl.x[rows], LowpWeight(wl.fmt, wl.w_q, wl.w_scale), wl.A, wl.B, wl.scale, np.asarray(wl.ids)[rows])
+        ref = layer(wl.x[rows], LowpWeight(wl.fmt, wl.w_q, wl.w_scale), wl.A, wl.B, wl.scale, np.asarray(wl.ids)[rows],
+                    act=args.act)
         yg = S[0]["y"].float().cpu().numpy().astype(np.float64)[rows]
         dlt = yg - ref["y"]
         parity = {"max_rel": float(np.abs(dlt).max() / np.abs(ref["y"]).max()),
@@ -235,8 +243,10 @@ def main():
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS}
     sha = kernel_source_sha()
-    roof["traffic"] = stored_traffic(args.workload, sha)
-    roof["kernel"] = "k_layer (fused down-projection + scaled-MFMA GEMM + LoRA epilogue)"
+    tag = args.workload + ("_act_bf16" if a16 else "")
+    roof["traffic"] = stored_traffic(tag, sha)
+    roof["kernel"] = ("k_layer (fused down-projection + bf16-MFMA GEMM on widened W + LoRA epilogue)" if a16 else
+                      "k_layer (fused down-projection + scaled-MFMA GEMM + LoRA epilogue)")
     roof["per_call_bytes"] = nbytes
     roof["per_call_flops"] = flops
     roof["kernel_us"] = dom_us
@@ -252,9 +262,9 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8" if wl.fmt == "fp8" else "fp8xfp4",
+        "dtype": ("bf16xfp8" if wl.fmt == "fp8" else "bf16xfp4") if a16 else ("fp8" if wl.fmt == "fp8" else "fp8xfp4"),
         "data": "synthetic",
-        "config": {"workload": args.workload, "T": wl.T, "K": wl.K, "N": wl.N, "w_format": wl.fmt,
+        "config": {"workload": args.workload, "activations": args.act, "T": wl.T, "K": wl.K, "N": wl.N, "w_format": wl.fmt,
                    "adapters": wl.n_adapters, "adapters_present": int(len(np.unique(wl.ids))),
                    "ranks": sorted(set(int(r) for r in wl.ranks)), "seed": wl.seed, "input_sets": sets,
                    "timing": "eager" if args.eager else "hip graph of K steps"},
@@ -277,7 +287,7 @@ def main():
         del src, dst
     if not args.no_cpu:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(wl)
+        out["cpu_baseline"] = cpu_baseline(wl, act=args.act)
     print(json.dumps(out), flush=True)
 
 
