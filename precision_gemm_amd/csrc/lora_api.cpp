@@ -39,10 +39,13 @@ lora_status check_adapters(int32_t n_adapters, int32_t r_max) {
 // Tile plan: a pure function of the sizes, so lora_workspace_bytes and every call agree.
 // fused: the down-projection runs in the layer launch (its K may then be split into parts
 // that the GEMM epilogue adds up); otherwise it runs alone and writes the final t.
-LayerPlan make_plan(int T, int K, int N, int n_ad, int r_max, int fmt, bool fused = true) {
+// a16: 16-bit activations, which run on the one-tile stream at every T (one 16-token tile
+// per workgroup; the token tiles of a column tile share an XCD's L2 for W).
+LayerPlan make_plan(int T, int K, int N, int n_ad, int r_max, int fmt, bool fused = true, bool a16 = false) {
   LayerPlan pl{};
   pl.fmt = fmt;
-  if (T <= 16) {
+  pl.a16 = a16;
+  if (T <= 16 || a16) {
     // one-tile stream, built for two workgroups per CU (its registers and LDS fit): the
     // down-projection's few workgroups then share CUs with the GEMM's (Llama-3-8B QKV decode:
     // 14.05 to 14.13 us per step against 14.27 to 14.44)
@@ -149,7 +152,9 @@ const char* lora_version(void) { return "lora_lowp gfx950 kernels v1 (scaled-MFM
 size_t lora_workspace_bytes(int32_t T, int32_t K, int32_t N, int32_t n_adapters, int32_t r_max) {
   if (check_sizes(T, K, N) != LORA_OK || check_adapters(n_adapters, r_max) != LORA_OK) return 0;
   if (T == 0) return 256;
-  return make_plan(T, K, N, n_adapters, r_max, LORA_W_FP8_E4M3).total;
+  // the larger of the two plans (MXFP8 and 16-bit activations)
+  return std::max(make_plan(T, K, N, n_adapters, r_max, LORA_W_FP8_E4M3).total,
+                  make_plan(T, K, N, n_adapters, r_max, LORA_W_FP8_E4M3, true, true).total);
 }
 
 lora_status lora_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
@@ -244,7 +249,6 @@ lora_status gemm_lowp_lora_epilogue(const uint16_t* x, int32_t T, int32_t K, int
   const bool build = (flags & LORA_BUILD_SEGMENTS) != 0;
   if (build && !(flags & LORA_FUSE_SHRINK)) return LORA_ERR_INVALID_ARG;
   const bool a16 = (flags & LORA_ACT_BF16) != 0;
-  if (a16 && T > 16) return LORA_ERR_UNSUPPORTED;  // the one-tile stream only
   if (build && (!seg_indptr || !adapter_id || (T > 0 && !sorted_tok))) return LORA_ERR_INVALID_ARG;
   if (T == 0) {
     if (!build) return LORA_OK;
@@ -263,8 +267,7 @@ lora_status gemm_lowp_lora_epilogue(const uint16_t* x, int32_t T, int32_t K, int
   if (lora && (!adapter_id || !B_ptrs || !ranks || !scales)) return LORA_ERR_INVALID_ARG;
   if (fused && (!seg_indptr || !sorted_tok || !A_ptrs)) return LORA_ERR_INVALID_ARG;
   if (t && !aligned16(t)) return LORA_ERR_INVALID_ARG;
-  LayerPlan pl = make_plan(T, K, N, n_adapters, r_max, w_fmt);
-  pl.a16 = a16;
+  const LayerPlan pl = make_plan(T, K, N, n_adapters, r_max, w_fmt, true, a16);
   if (!workspace || !aligned16(workspace) || workspace_bytes < pl.total) return LORA_ERR_WORKSPACE;
   char* ws = reinterpret_cast<char*>(workspace);
   hipStream_t s = as_stream(stream);
@@ -300,7 +303,7 @@ lora_status gemm_lowp_lora_epilogue(const uint16_t* x, int32_t T, int32_t K, int
     sp.t_out = t;  // may be null
     sp.t_tag = ttag;
     // past 16 tokens (one K-part): t goes to the epilogue as tagged bf16 pairs of s_a t
-    sp.t_pack = (pl.s_kparts == 1 && T > 16) ? 1 : 0;
+    sp.t_pack = (pl.s_kparts == 1 && T > 16 && pl.TT != 1) ? 1 : 0;
     sp.scales = scales;
     sp.tblk = pl.s_tblk; sp.n_tblk = pl.s_ntblk; sp.n_jg = pl.s_njg; sp.jper = pl.s_jper;
     sp.kparts = pl.s_kparts; sp.kpart_len = pl.s_kpart_len;
@@ -318,7 +321,7 @@ lora_status gemm_lowp_lora_epilogue(const uint16_t* x, int32_t T, int32_t K, int
   gp.t_out = (fused && pl.s_kparts > 1) ? t : nullptr;
   gp.t_tag = fused ? ttag : nullptr;
   gp.t_kparts = pl.s_kparts;
-  gp.t_pack = (fused && pl.s_kparts == 1 && T > 16) ? 1 : 0;
+  gp.t_pack = (fused && pl.s_kparts == 1 && T > 16 && pl.TT != 1) ? 1 : 0;
   gp.r_max = r_max;
   gp.ids = adapter_id; gp.B_ptrs = B_ptrs; gp.ranks = ranks; gp.scales = scales; gp.n_ad = n_adapters;
   gp.y = y;

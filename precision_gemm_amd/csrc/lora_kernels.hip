@@ -685,7 +685,23 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   const int wc = wave % WC, wk = wave / WC;
   const int ks = item % p.ksplit;
   const int tile = item / p.ksplit;
-  const int cb = tile % p.n_cb, tb = tile / p.n_cb;
+  int cb = tile % p.n_cb, tb = tile / p.n_cb;
+  if (TT == 1 && p.n_tb > 1) {
+    // several 16-token tiles per column tile (16-bit activations past 16 tokens): the tiles
+    // of one column tile take item ids 8 apart, so that they run on one XCD (workgroups are
+    // dealt to the eight XCDs in turn) at about the same time and read W once into its L2.
+    // Column tiles beyond the last multiple of 8 keep the plain order.
+    const int full = (p.n_cb / 8) * 8;
+    if (tile < full * p.n_tb) {
+      const int j = tile / 8;
+      tb = j % p.n_tb;
+      cb = (j / p.n_tb) * 8 + tile % 8;
+    } else {
+      const int r = tile - full * p.n_tb, rest = p.n_cb - full;
+      cb = full + r % rest;
+      tb = r / rest;
+    }
+  }
   const int row0 = tb * ROWS;
   const int n_tile0 = cb * WN;
   const int nw0 = n_tile0 + wc * CT * 16;
@@ -1831,9 +1847,10 @@ static hipError_t launch_layer_t(const LayerPlan& pl, int grid, hipStream_t stre
 template <int FMT>
 static hipError_t launch_layer_f(const LayerPlan& pl, int grid, hipStream_t stream, const ShrinkParams& sp,
                                  const GemmParams& gp) {
-  if (pl.a16) {  // 16-bit activations: the one-tile stream
-    if (pl.TT == 1 && pl.CT == 2 && pl.WC == 1 && pl.WK == 4 && !pl.XQ && pl.s_cfg == 0 && pl.occ == 2)
-      return launch_layer_t<FMT, 1, 2, 1, 4, false, 1, 1, 2, 2, true>(pl, grid, stream, sp, gp);
+  if (pl.a16) {  // 16-bit activations: the one-tile stream, with either down-projection shape
+    if (!(pl.TT == 1 && pl.CT == 2 && pl.WC == 1 && pl.WK == 4 && !pl.XQ && pl.occ == 2)) return hipErrorInvalidValue;
+    if (pl.s_cfg == 0) return launch_layer_t<FMT, 1, 2, 1, 4, false, 1, 1, 2, 2, true>(pl, grid, stream, sp, gp);
+    if (pl.s_cfg == 1) return launch_layer_t<FMT, 1, 2, 1, 4, false, 4, 2, 1, 2, true>(pl, grid, stream, sp, gp);
     return hipErrorInvalidValue;
   }
   LORA_LAYER_CASE(1, 2, 1, 4, false, 0, 1, 1, 2, 2)

@@ -218,7 +218,7 @@ def gemm_lowp_lora_epilogue(x: torch.Tensor, w: LowpWeight, seg: Segments | None
     launch (``t``, if given, receives it); otherwise ``t`` is an input and ``t=None``
     computes the base GEMM only.  With ``build_segments`` the same launch also fills
     ``seg`` (from ``seg.adapter_id``; see ``empty_segments``).  With ``act_bf16`` the
-    base product reads x in bf16 as it is (16-bit activations; up to 16 tokens)."""
+    base product reads x in bf16 as it is (16-bit activations)."""
     _dev(x, "x", torch.bfloat16)
     if not w.packed:
         raise ValueError("the GEMM reads W in the packed form: call pack_weight(w) once first")

@@ -71,8 +71,8 @@ def test_gemm_validation(L):
     assert _gemm(L, fmt=7) == INVALID
     assert _gemm(L, flags=8) == INVALID                  # unknown flag
     assert _gemm(L, flags=2) == INVALID                  # segment build without the fused down-projection
-    assert _gemm(L, flags=5, T=17) == UNSUPPORTED        # 16-bit activations: up to 16 tokens
-    assert _gemm(L, flags=5) == WORKSPACE                # ... valid otherwise (fails at the workspace)
+    assert _gemm(L, flags=5) == WORKSPACE                # 16-bit activations: valid (fails at the workspace)
+    assert _gemm(L, flags=5, T=4096) == WORKSPACE
     assert _gemm(L, x=NULL) == INVALID
     assert _gemm(L, x=MISALIGNED) == INVALID
     assert _gemm(L, A=NULL) == INVALID                   # fused needs A

@@ -4,8 +4,10 @@ act="bf16" layer to the same bars as the MXFP8 path; the output's offset from th
 MXFP8 oracle must match the difference of the two oracles, so that a path that still
 quantised x would fail.
 Cases: the 16-token qkv workload at full size (fused, unfused, base only, segments
-built in the launch), 16-token batches at the gate-up and MXFP4 down-projection shapes,
-ragged and tiny shapes in both formats, and the token limit."""
+built in the launch); the 64-token gate-up and the 4096-token prefill workloads (several
+16-token tiles per column tile, prefill on sampled rows); 16-token batches at the gate-up
+and MXFP4 down-projection shapes; ragged, tiny and many-adapter shapes in both formats,
+with column-tile counts that do and do not divide into the eight XCD groups."""
 
 import numpy as np
 import pytest
@@ -16,19 +18,21 @@ from gpu_util import assert_t_close, assert_y_close, errors, named, run_gpu, run
 pytestmark = pytest.mark.gpu
 
 
-def _check(wl, g, what, base_only=False):
-    ref = run_oracle(wl, act="bf16")
+def _check(wl, g, what, base_only=False, rows=None):
+    ref = run_oracle(wl, rows, act="bf16")
     key = "y_base" if base_only else "y"
-    m, f = assert_y_close(g["y"], ref[key], what)
+    sel = slice(None) if rows is None else np.asarray(rows)
+    y = g["y"][sel]
+    m, f = assert_y_close(y, ref[key], what)
     if not base_only:
-        assert_t_close(g["t"].astype(np.float64), ref["t"], what)
+        assert_t_close(g["t"][sel].astype(np.float64), ref["t"], what)
     # x was not quantised: with d = (bf16 oracle) - (MXFP8 oracle), the output's offset
     # from the MXFP8 oracle projects onto d with coefficient ~1 (~0 if x were quantised);
     # the bf16 rounding of y is uncorrelated with d
-    y8 = run_oracle(wl)[key]
+    y8 = run_oracle(wl, rows)[key]
     d = ref[key] - y8
-    c = float(np.vdot(g["y"] - y8, d) / np.vdot(d, d))
-    _, f8 = errors(g["y"], y8)
+    c = float(np.vdot(y - y8, d) / np.vdot(d, d))
+    _, f8 = errors(y, y8)
     assert 0.8 < c < 1.2, f"{what}: projection on the activation-quantisation difference {c:.3f}"
     print(f"  y max_rel={m:.2e} frob={f:.2e} (MXFP8 oracle: frob={f8:.2e}; projection {c:.3f})", flush=True)
 
@@ -43,6 +47,18 @@ def test_decode_qkv_bf16_activations(mode):
     _check(wl, g, f"decode_qkv {mode}", base_only=(mode == "base_only"))
 
 
+@pytest.mark.parametrize("name,build", [("decode_gateup", False), ("decode_gateup", True), ("prefill", False)])
+def test_multi_tile_workloads_bf16_activations(name, build):
+    print(f"[case] act_bf16 {name} build={build}", flush=True)
+    wl = named(name)
+    rows = None
+    if name == "prefill":  # every row of y depends only on its own token
+        rows = tuple(sorted(np.random.default_rng(9).choice(wl.T, 96, replace=False).tolist()))
+    g = run_gpu(wl, fused=True, build=build, act_bf16=True)
+    assert g["status"] == 0 and g["err"] == 0
+    _check(wl, g, f"{name} build={build}", rows=rows)
+
+
 CASES = [
     # T, K, N, fmt, ranks, seed
     (16, 4096, 28672, "fp8", [16] * 32, 41),              # gate-up shape, 16 tokens
@@ -51,6 +67,11 @@ CASES = [
     (5, 256, 128, "mxfp4", [16, 8], 44),
     (13, 1152, 320, "fp8", [8, 24, 64], 45),
     (16, 640, 192, "mxfp4", [32, 16], 46),
+    (17, 512, 192, "fp8", [8, 16, 24, 32], 47),           # 6 column tiles: plain order only
+    (37, 384, 256, "mxfp4", [64, 40, 8], 48),             # 8 column tiles, 3 token tiles
+    (130, 1024, 320, "fp8", [16, 64] * 32, 49),           # 10 column tiles (8 + a tail of 2)
+    (300, 768, 256, "fp8", [48, 8, 16, 64], 50),          # down-projection tiles of 64 tokens
+    (200, 4096, 256, "mxfp4", [64, 8, 32, 16, 48] * 14, 51),
 ]
 
 
@@ -67,19 +88,14 @@ def test_shapes_bf16_activations(case, fused):
     _check(wl, g, str(case))
 
 
-def test_bf16_activations_token_limit():
-    import torch
-    import precision_gemm_amd as P
-    from precision_gemm_amd._lib import LoraError
-    from workloads.device import upload
-    print("[case] act_bf16 T=17 rejected", flush=True)
-    wl = workloads.make_custom(17, 256, 128, "fp8", [8], np.zeros(17, int), [1.0], 47)
-    x, w, ad, ids = upload(wl)
-    ws = P.alloc_workspace(wl.T, wl.K, wl.N, ad.n, ad.r_max)
-    seg = P.build_segments(ids, ad.n)
-    y = torch.full((17, 128), 3.0, dtype=torch.bfloat16, device="cuda")
-    with pytest.raises(LoraError) as ei:
-        P.gemm_lowp_lora_epilogue(x, w, seg, ad, ws, y=y, act_bf16=True)
-    assert ei.value.status == 2                  # LORA_ERR_UNSUPPORTED
-    torch.cuda.synchronize()
-    assert (y == 3.0).all()                      # nothing was enqueued
+def test_bf16_activations_deterministic_and_segments_in_prepass_launch():
+    print("[case] act_bf16 T=300 build, determinism", flush=True)
+    rng = np.random.default_rng(52)
+    ids = rng.integers(0, 6, 300)
+    wl = workloads.make_custom(300, 1024, 384, "fp8", [8, 16, 32, 64, 16, 8], ids, [1.0] * 6, 52,
+                               a_std=0.1, b_std=0.05)
+    g1 = run_gpu(wl, fused=True, build=True, act_bf16=True)
+    g2 = run_gpu(wl, fused=True, act_bf16=True)
+    assert g1["status"] == 0 and g1["err"] == 0
+    assert np.array_equal(g1["y_bits"], g2["y_bits"])
+    _check(wl, g1, "T300 build")
