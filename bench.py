@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 METRIC = "µs per fused LoRA-layer call and achieved HBM TB/s (decode) / MFMA TFLOP/s (prefill)"
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0     # dense FP8 (and FP8 x FP4) MFMA, MI355X
+BF16_PEAK_TFLOPS = 2500.0    # dense bf16 MFMA, MI355X (the 16-bit activation variant)
 CSRC = os.path.join(ROOT, "precision_gemm_amd", "csrc")
 
 
@@ -233,8 +234,8 @@ def main():
     prefill = wl.T > 256
     if prefill:
         achieved = flops / (dom_us * 1e-6) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / FP8_PEAK_TFLOPS}
+        peak = BF16_PEAK_TFLOPS if a16 else FP8_PEAK_TFLOPS
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak}
     else:
         achieved = nbytes / (dom_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
