@@ -8,6 +8,8 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 namespace lora {
 
@@ -56,13 +58,6 @@ __device__ __forceinline__ uint32_t mx_block_code(const uint4 (&in)[4]) {
   return ef > 8u ? ef - 8u : 0u;
 }
 
-__device__ __forceinline__ uint32_t cvt4_fp8(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
-  return (uint32_t)w;
-}
-
-__device__ __forceinline__ float clamp448(float v) { return __builtin_fminf(__builtin_fmaxf(v, -448.f), 448.f); }
 
 // Largest |x| of 8 bf16 (one 16-byte piece of a block), as 15-bit magnitude bits.
 __device__ __forceinline__ uint32_t absmax8_bits(const uint4& in) {
@@ -80,34 +75,48 @@ __device__ __forceinline__ uint32_t mx_code_from_bits(uint32_t mx) {
   return ef > 8u ? ef - 8u : 0u;
 }
 
+// Element codes with the gfx950 scaled conversion: the magnitudes are first clamped to
+// 448 * 2^E in the bf16 bit domain (the bits of a non-negative bf16 order as its value),
+// then v_cvt_scalef32_pk_fp8_bf16 divides by its scale operand 2^E (exact) and rounds to
+// nearest even.  For finite x this is RNE_e4m3(clamp(x * 2^-E, +-448)), the rule above:
+// checked on the GPU against the fp32 form (multiply by 2^-E, clamp, v_cvt_pk_fp8_f32)
+// for every finite bf16 pattern at scale codes 0 to 246, with no difference.
+struct MxScale {
+  us2 lim;   // bf16 bits of 448 * 2^E (= 1.75 * 2^(code - 119)), in both halves
+  float sc;  // 2^E = 2^(code - 127) as a float (a subnormal for code 0)
+};
+__device__ __forceinline__ MxScale mx_scale(uint32_t code) {
+  const unsigned short l = (unsigned short)(((code + 8u) << 7) | 0x60u);
+  return {us2{l, l}, code ? __uint_as_float(code << 23) : __uint_as_float(0x00400000u)};
+}
+// Four e4m3 codes (byte i from bf16 i, low half of w0 first) of two bf16 pairs.
+__device__ __forceinline__ uint32_t mx_cvt4(uint32_t w0, uint32_t w1, const MxScale& s) {
+  const us2 mask = {0x7fff, 0x7fff};
+  auto clampw = [&](uint32_t w) {
+    const us2 m = __builtin_elementwise_min(__builtin_bit_cast(us2, w) & mask, s.lim);
+    return __builtin_bit_cast(bf16x2, (w & 0x80008000u) | __builtin_bit_cast(uint32_t, m));
+  };
+  s16x2 r = {0, 0};
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, clampw(w0), s.sc, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, clampw(w1), s.sc, true);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
 // Quantise one 16-byte piece (8 bf16) of a block with the block's scale code into 8
 // e4m3 codes.
 __device__ __forceinline__ uint2 mx_piece_quant(const uint4& in, uint32_t code) {
-  const float inv = __uint_as_float((254u - code) << 23);  // 2^(127 - code) = 2^-E, exact
-  const uint32_t w[4] = {in.x, in.y, in.z, in.w};
-  uint32_t r[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    float a = clamp448(bf16_lo(w[2 * h]) * inv), b = clamp448(bf16_hi(w[2 * h]) * inv);
-    float c = clamp448(bf16_lo(w[2 * h + 1]) * inv), d = clamp448(bf16_hi(w[2 * h + 1]) * inv);
-    r[h] = cvt4_fp8(a, b, c, d);
-  }
-  return make_uint2(r[0], r[1]);
+  const MxScale s = mx_scale(code);
+  return make_uint2(mx_cvt4(in.x, in.y, s), mx_cvt4(in.z, in.w, s));
 }
 
 // Quantise 32 bf16 (64 bytes in `in`) with scale code `code` into 32 e4m3 codes (out[2]).
 __device__ __forceinline__ void mx_block_quant(const uint4 (&in)[4], uint32_t code, uint4 (&out)[2]) {
-  const float inv = __uint_as_float((254u - code) << 23);  // 2^(127 - code) = 2^-E, exact
+  const MxScale s = mx_scale(code);
   uint32_t r[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    uint32_t w[4] = {in[i].x, in[i].y, in[i].z, in[i].w};
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      float a = clamp448(bf16_lo(w[2 * h]) * inv), b = clamp448(bf16_hi(w[2 * h]) * inv);
-      float c = clamp448(bf16_lo(w[2 * h + 1]) * inv), d = clamp448(bf16_hi(w[2 * h + 1]) * inv);
-      r[2 * i + h] = cvt4_fp8(a, b, c, d);
-    }
+    r[2 * i] = mx_cvt4(in[i].x, in[i].y, s);
+    r[2 * i + 1] = mx_cvt4(in[i].z, in[i].w, s);
   }
   out[0] = make_uint4(r[0], r[1], r[2], r[3]);
   out[1] = make_uint4(r[4], r[5], r[6], r[7]);

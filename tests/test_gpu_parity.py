@@ -104,6 +104,22 @@ def test_quant_all_bf16_patterns():
     q_ref, s_ref = quantize_mxfp8(x)
     assert np.array_equal(xsc.cpu().numpy(), s_ref)
     assert np.array_equal(xq.cpu().numpy(), q_ref)
+    # the same patterns confined to exponent windows placed across the range, so that the
+    # blocks' scale codes cover 0 .. 246 (not only the top codes of the above)
+    rows = []
+    windows = [(24, e0) for e0 in (0, 1, 12, 40, 77, 100, 115, 126, 140, 170, 200, 231)] + [(4, 0), (8, 1), (6, 3)]
+    for width, e0 in windows:
+        e = (bits.astype(np.uint32) >> 7) & 0xFF
+        b = (bits.astype(np.uint32) & 0x807F) | (((e % width) + e0) << 7)
+        b = b[((b >> 7) & 0xFF) != 0xFF].astype(np.uint16)
+        m = (b.size // 256) * 256
+        rows.append(b[:m].reshape(-1, 256))
+    x = np.concatenate(rows)
+    xq, xsc = P.quant_act_mxfp8(bf16_tensor(x))
+    q_ref, s_ref = quantize_mxfp8(x)
+    assert np.array_equal(xsc.cpu().numpy(), s_ref)
+    assert s_ref.min() == 0 and s_ref.max() >= 240
+    assert np.array_equal(xq.cpu().numpy(), q_ref)
 
 
 def test_segments_random_and_bad_ids():
