@@ -39,13 +39,16 @@ lora_status check_adapters(int32_t n_adapters, int32_t r_max) {
 // Tile plan: a pure function of the sizes, so lora_workspace_bytes and every call agree.
 // fused: the down-projection runs in the layer launch (its K may then be split into parts
 // that the GEMM epilogue adds up); otherwise it runs alone and writes the final t.
-// a16: 16-bit activations, which run on the one-tile stream at every T (one 16-token tile
-// per workgroup; the token tiles of a column tile share an XCD's L2 for W).
+// a16: 16-bit activations: the one-tile stream up to 16 tokens, 64 x 128 tiles with bf16 x
+// staged in LDS above (where N % 128 == 0; otherwise 16-token tiles of the stream, whose
+// token tiles of a column tile share an XCD's L2 for W).
 LayerPlan make_plan(int T, int K, int N, int n_ad, int r_max, int fmt, bool fused = true, bool a16 = false) {
   LayerPlan pl{};
   pl.fmt = fmt;
   pl.a16 = a16;
-  if (T <= 16 || a16) {
+  if (a16 && T > 16 && N % 128 == 0) {
+    pl.TT = 4; pl.CT = 2; pl.WC = 4; pl.WK = 1; pl.XQ = false;
+  } else if (T <= 16 || a16) {
     // one-tile stream, built for two workgroups per CU (its registers and LDS fit): the
     // down-projection's few workgroups then share CUs with the GEMM's (Llama-3-8B QKV decode:
     // 14.05 to 14.13 us per step against 14.27 to 14.44)

@@ -634,12 +634,15 @@ struct EpiLayout {
   static_assert(ROWBP % 8 == 0 && LRED % 16 == 0, "epilogue LDS alignment");
 };
 
-template <int TT, int CT, int WC, int WK, int OCC>
+template <int TT, int CT, int WC, int WK, int OCC, bool A16 = false>
 struct GemmSmem {
   using CK = ChunkK<TT, CT>;
   // the chunked loop stages x in two buffers (chunk c + 1 is staged while chunk c is
-  // multiplied); the one-tile stream does not use them
-  static constexpr int XBUF = ((TT * 16 * CK::ROW + TT * 16 * (CK::KC / 32)) + 15) & ~15;
+  // multiplied); the one-tile stream does not use them.  MXFP8: codes and scale codes;
+  // 16-bit activations: the bf16 rows themselves
+  static constexpr int XROW16 = CK::KC * 2 + 16;
+  static constexpr int XBUF =
+      (A16 && TT != 1) ? TT * 16 * XROW16 : ((TT * 16 * CK::ROW + TT * 16 * (CK::KC / 32)) + 15) & ~15;
   static constexpr int MAIN = (TT == 1) ? XBUF : 2 * XBUF;
   static constexpr int RED = (WK - 1) * WC * TT * CT * 256 * 4;
   static constexpr int POST = EpiLayout<TT, CT, WC, WK>::POST;
@@ -671,7 +674,7 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   constexpr int EPI_TH = EPI_TE / EPI_PH;
   static_assert(STEPS % WK == 0, "k-steps per chunk must split evenly over the k-waves");
   // x staging buffer b: [ROWS][ROW] codes, then [ROWS][KC/32] scale codes
-  constexpr int XBUF = GemmSmem<TT, CT, WC, WK, OCC>::XBUF;
+  constexpr int XBUF = GemmSmem<TT, CT, WC, WK, OCC, A16>::XBUF;
   auto xs_of = [&](int b) { return reinterpret_cast<uint8_t*>(smem) + b * XBUF; };
   auto ss_of = [&](int b) { return reinterpret_cast<uint8_t*>(smem) + b * XBUF + ROWS * ROW; };
   // scale code of row `row`, 32-block k32 of the chunk: the TT codes a lane needs for one
@@ -834,6 +837,17 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   auto stage_x = [&](int buf) {  // x registers of buffer buf -> LDS buffer buf
     uint8_t* xs = xs_of(buf);
     uint8_t* ss = ss_of(buf);
+    if constexpr (A16) {  // the bf16 blocks as they are: row stride XROW16, block k32 at 64 k32
+      constexpr int XR = GemmSmem<TT, CT, WC, WK, OCC, A16>::XROW16;
+#pragma unroll
+      for (int m = 0; m < NBLK; ++m) {
+        const int b = tid + 256 * m;
+        const int row = b / (KC / 32), k32 = b % (KC / 32);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4*>(xs + row * XR + k32 * 64 + 16 * q) = xr[buf][4 * m + q];
+      }
+      return;
+    }
     if (XQ) {
 #pragma unroll
       for (int m = 0; m < NP; ++m) {
@@ -864,7 +878,60 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
               (uint8_t)(((k32 < 4) ? xsc2[buf][h].x : xsc2[buf][h].y) >> (8 * (k32 & 3)));
     }
   };
+  auto mma_chunk_a16 = [&](int buf, int c) {
+    // 16-bit activations: per k-step the lane widens its W codes of each column tile to four
+    // bf16 operands once, then per token tile reads the four 8-element x pieces at the same
+    // k (FP8: 16g, 16g+8, 64+16g, 72+16g; MXFP4: 32g .. 32g+31) and issues four bf16 MFMAs
+    constexpr int XR = GemmSmem<TT, CT, WC, WK, OCC, A16>::XROW16;
+    const uint8_t* xs = xs_of(buf);
+    const int kc0 = chunk_k0(c);
+    const int nsteps = min(KC, ke - kc0) >> 7;
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+      const int s = wk + WK * i;
+      if (s >= nsteps) break;
+      const int sp = phys_step(s, nsteps);
+      uint4 wb[CT][4];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        if constexpr (FMT == LORA_W_FP8_E4M3) {
+          const uint4 lo = wlo[buf][i][ct], hi = whi[buf][i][ct];
+          const uint32_t d[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const uint2 a = fp8x4_to_bf16(d[2 * m]), b = fp8x4_to_bf16(d[2 * m + 1]);
+            wb[ct][m] = make_uint4(a.x, a.y, b.x, b.y);
+          }
+        } else {
+          const float sc = __builtin_bit_cast(float, wsc[buf][i][ct] << 23);
+          const uint4 lo = wlo[buf][i][ct];
+          wb[ct][0] = fp4x8_to_bf16(lo.x, sc);
+          wb[ct][1] = fp4x8_to_bf16(lo.y, sc);
+          wb[ct][2] = fp4x8_to_bf16(lo.z, sc);
+          wb[ct][3] = fp4x8_to_bf16(lo.w, sc);
+        }
+      }
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        const uint8_t* xp = xs + (tt * 16 + li) * XR + sp * 256;
+        uint4 xf[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int k = (FMT == LORA_W_FP8_E4M3) ? ((m >> 1) * 64 + 16 * g + 8 * (m & 1)) : (32 * g + 8 * m);
+          xf[m] = *reinterpret_cast<const uint4*>(xp + 2 * k);
+        }
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+          for (int m = 0; m < 4; ++m) acc[tt][ct] = mfma_bf16_16x16x32(xf[m], wb[ct][m], acc[tt][ct]);
+      }
+    }
+  };
   auto mma_chunk = [&](int buf, int c) {  // LDS buffer and W registers of buffer buf
+    if constexpr (A16) {
+      mma_chunk_a16(buf, c);
+      return;
+    }
     const uint8_t* xs = xs_of(buf);
     const uint8_t* ss = ss_of(buf);
     const int kc0 = chunk_k0(c);
@@ -927,7 +994,7 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   // registers (FP8: the lane's codes are at the k of its x pieces; MXFP4: lane (li, g)
   // holds k = 32g .. 32g+31, one block, so x is read there and the block scale is
   // applied in the widening).  The one-tile stream only.
-  static_assert(!A16 || STREAM, "16-bit activations: the one-tile stream only");
+  static_assert(!A16 || STREAM || (TT == 4 && CT == 2 && !XQ), "16-bit activations: the stream or 64 x 128 tiles");
   constexpr bool A16_FP4 = A16 && FMT == LORA_W_MXFP4_E2M1;
   constexpr int SD = 4;  // k-steps of a wave in flight (measured: 2, 3 and 6 are slower)
   const int nst = (ke - kb) >> 7;
@@ -1026,7 +1093,7 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   // up-projection metadata (adapter list, work items, rows whose t is needed), built once
   // the first chunk is multiplied: its LDS latency then overlaps the loads in flight
   using EL = EpiLayout<TT, CT, WC, WK>;
-  char* md = smem + GemmSmem<TT, CT, WC, WK, OCC>::MD;
+  char* md = smem + GemmSmem<TT, CT, WC, WK, OCC, A16>::MD;
   int* rowad = reinterpret_cast<int*>(md + EL::ROWAD);
   int* rowrk = reinterpret_cast<int*>(md + EL::ROWRK);
   float* rowsc = reinterpret_cast<float*>(md + EL::ROWSC);
@@ -1039,9 +1106,9 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   int* meta = reinterpret_cast<int*>(md + EL::META);
   int* ioff = reinterpret_cast<int*>(md + EL::IOFF);
   int* lrow = reinterpret_cast<int*>(md + EL::LROW);
-  char* stg = smem + GemmSmem<TT, CT, WC, WK, OCC>::STG;
+  char* stg = smem + GemmSmem<TT, CT, WC, WK, OCC, A16>::STG;
   const int slot = WN * p.r_max * 2;  // bytes of one B slice slot (a multiple of 512)
-  constexpr int BST = GemmSmem<TT, CT, WC, WK, OCC>::BST;
+  constexpr int BST = GemmSmem<TT, CT, WC, WK, OCC, A16>::BST;
   const int spb = BST / slot;  // slots per batch (>= 2)
   static_assert(BST / (WN * 8 * 2) <= 256, "stage_b keeps a wave's slices one per lane");
   auto prepare_epilogue = [&]() {
@@ -1830,7 +1897,7 @@ static hipError_t launch_layer_t(const LayerPlan& pl, int grid, hipStream_t stre
                                  const GemmParams& gp) {
   ShrinkParams sp = sp_in;
   sp.compact_off = (int)shrink_smem<TG, JP, U>();  // the block prefix lies after the down-projection's area
-  const size_t sm = std::max(std::max((size_t)GemmSmem<TT, CT, WC, WK, OCC>::BYTES,
+  const size_t sm = std::max(std::max((size_t)GemmSmem<TT, CT, WC, WK, OCC, A16>::BYTES,
                                       gp.n_shrink > 0 ? shrink_smem<TG, JP, U>() : (size_t)0),
                              std::max(gp.seg_build ? seg_lds_bytes(gp.T, gp.n_ad) : (size_t)0,
                                       sp.compact ? (size_t)sp.compact_off + 4 * (size_t)(sp.n_ad + 1) + 16 : (size_t)0));
@@ -1847,10 +1914,15 @@ static hipError_t launch_layer_t(const LayerPlan& pl, int grid, hipStream_t stre
 template <int FMT>
 static hipError_t launch_layer_f(const LayerPlan& pl, int grid, hipStream_t stream, const ShrinkParams& sp,
                                  const GemmParams& gp) {
-  if (pl.a16) {  // 16-bit activations: the one-tile stream, with either down-projection shape
-    if (!(pl.TT == 1 && pl.CT == 2 && pl.WC == 1 && pl.WK == 4 && !pl.XQ && pl.occ == 2)) return hipErrorInvalidValue;
-    if (pl.s_cfg == 0) return launch_layer_t<FMT, 1, 2, 1, 4, false, 1, 1, 2, 2, true>(pl, grid, stream, sp, gp);
-    if (pl.s_cfg == 1) return launch_layer_t<FMT, 1, 2, 1, 4, false, 4, 2, 1, 2, true>(pl, grid, stream, sp, gp);
+  if (pl.a16) {  // 16-bit activations: the one-tile stream or 64 x 128 tiles, either down-projection shape
+    if (pl.TT == 1 && pl.CT == 2 && pl.WC == 1 && pl.WK == 4 && !pl.XQ && pl.occ == 2) {
+      if (pl.s_cfg == 0) return launch_layer_t<FMT, 1, 2, 1, 4, false, 1, 1, 2, 2, true>(pl, grid, stream, sp, gp);
+      if (pl.s_cfg == 1) return launch_layer_t<FMT, 1, 2, 1, 4, false, 4, 2, 1, 2, true>(pl, grid, stream, sp, gp);
+    }
+    if (pl.TT == 4 && pl.CT == 2 && pl.WC == 4 && pl.WK == 1 && !pl.XQ && pl.occ == 1) {
+      if (pl.s_cfg == 0) return launch_layer_t<FMT, 4, 2, 4, 1, false, 1, 1, 2, 1, true>(pl, grid, stream, sp, gp);
+      if (pl.s_cfg == 1) return launch_layer_t<FMT, 4, 2, 4, 1, false, 4, 2, 1, 1, true>(pl, grid, stream, sp, gp);
+    }
     return hipErrorInvalidValue;
   }
   LORA_LAYER_CASE(1, 2, 1, 4, false, 0, 1, 1, 2, 2)
