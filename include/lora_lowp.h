@@ -111,10 +111,9 @@ enum {
    * (FP8 codes exactly; MXFP4 codes times their block scale, exact while the value
    * stays in bf16's normal range: block scale codes 2 .. 252 for any e2m1 code)
    * and the products run on bf16 MFMA with fp32 accumulation; the FP8 channel scale
-   * and the adapter terms are applied as without the flag.  Any T: every workgroup
-   * takes one 16-token tile of one column tile (the decode kernel), and the token tiles
-   * of a column tile run together on one XCD so that W is read into its L2 once; large
-   * batches therefore run well below the bf16 MFMA peak. */
+   * and the adapter terms are applied as without the flag.  Any T: up to 16 tokens the
+   * decode stream; above, 64-token x 128-channel tiles with bf16 x staged in LDS where
+   * N % 128 == 0, else 16-token tiles of the decode stream (much slower for large T). */
   LORA_ACT_BF16 = 1u << 2
 };
 
