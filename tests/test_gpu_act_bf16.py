@@ -4,10 +4,11 @@ act="bf16" layer to the same bars as the MXFP8 path; the output's offset from th
 MXFP8 oracle must match the difference of the two oracles, so that a path that still
 quantised x would fail.
 Cases: the 16-token qkv workload at full size (fused, unfused, base only, segments
-built in the launch); the 64-token gate-up and the 4096-token prefill workloads (several
-16-token tiles per column tile, prefill on sampled rows); 16-token batches at the gate-up
-and MXFP4 down-projection shapes; ragged, tiny and many-adapter shapes in both formats,
-with column-tile counts that do and do not divide into the eight XCD groups."""
+built in the launch); the 64-token gate-up and the 4096-token prefill workloads (64 x 128
+tiles, prefill on sampled rows); 16-token batches at the gate-up and MXFP4 down-projection
+shapes; ragged, tiny and many-adapter shapes in both formats, on 64 x 128 tiles and, where
+N % 128 != 0, on 16-token stream tiles with column-tile counts of 6 and 10 (the XCD
+grouping with and without a tail)."""
 
 import numpy as np
 import pytest
@@ -67,10 +68,10 @@ CASES = [
     (5, 256, 128, "mxfp4", [16, 8], 44),
     (13, 1152, 320, "fp8", [8, 24, 64], 45),
     (16, 640, 192, "mxfp4", [32, 16], 46),
-    (17, 512, 192, "fp8", [8, 16, 24, 32], 47),           # 6 column tiles: plain order only
-    (37, 384, 256, "mxfp4", [64, 40, 8], 48),             # 8 column tiles, 3 token tiles
-    (130, 1024, 320, "fp8", [16, 64] * 32, 49),           # 10 column tiles (8 + a tail of 2)
-    (300, 768, 256, "fp8", [48, 8, 16, 64], 50),          # down-projection tiles of 64 tokens
+    (17, 512, 192, "fp8", [8, 16, 24, 32], 47),           # stream tiles, 6 column tiles: plain order only
+    (37, 384, 256, "mxfp4", [64, 40, 8], 48),             # 64 x 128 tiles, ragged
+    (130, 1024, 320, "fp8", [16, 64] * 32, 49),           # stream tiles, 10 column tiles (8 + a tail of 2)
+    (300, 768, 256, "fp8", [48, 8, 16, 64], 50),          # down-projection items of 64 tokens
     (200, 4096, 256, "mxfp4", [64, 8, 32, 16, 48] * 14, 51),
 ]
 
