@@ -143,7 +143,8 @@ def main():
     # workgroup of that launch; above, the call launches the builder first, and the layer
     # kernel alone is the call without the flag (the segments are built by then).
     in_launch = wl.T <= 128
-    xq_pass = bool(P.plan_info(wl.T, wl.K, wl.N, S[0]["ad"].n, S[0]["ad"].r_max, wl.fmt)["XQ"])
+    # (the 16-bit activation variant has no MXFP8 pre-pass)
+    xq_pass = (not a16) and bool(P.plan_info(wl.T, wl.K, wl.N, S[0]["ad"].n, S[0]["ad"].r_max, wl.fmt)["XQ"])
 
     def layer_call(s):
         d = S[s % sets]
