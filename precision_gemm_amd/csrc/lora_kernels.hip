@@ -14,7 +14,9 @@
 //   k_expand          up-projection y += s_a t @ B_a as its own launch (unfused schedule).
 //   k_layer           one launch for the layer: workgroups [0, n_shrink) compute the
 //                     down-projection, the others the scaled-MFMA base GEMM, whose
-//                     epilogue waits for t only when it needs it.
+//                     epilogue waits for t only when it needs it.  With 16-bit
+//                     activations (the "EpiLoRA" abstract's engine variant) the base GEMM
+//                     reads x in bf16 and runs on bf16 MFMA with W widened in registers.
 //
 // Hand-over between workgroups of one launch uses agent-coherent loads/stores (see
 // device_common.hpp) and a per-launch tag instead of counters that need resetting:
