@@ -176,7 +176,8 @@ lora_status lora_expand(const float* t, int32_t T, int32_t N,
                         uint16_t* y, void* stream);
 
 /* The fused layer ("EpiLoRA" abstract): low-precision base GEMM on gfx950 scaled
- * MFMA (x quantised to MXFP8 in the loader), with the epilogue applying the FP8
+ * MFMA (x quantised to MXFP8 in the loader; with LORA_ACT_BF16, bf16 x on bf16 MFMA
+ * instead), with the epilogue applying the FP8
  * channel scale and adding s_a * t[tok] @ B_a for every token's adapter before
  * the bf16 store (round to nearest even).
  *  - flags & LORA_FUSE_SHRINK: the down-projection runs in the same launch (t is an
