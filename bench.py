@@ -2,6 +2,9 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_qkv] [--sets S] [--act mxfp8|bf16]
 
+(``--workload decoder_layer``: a step is one decoder layer's four LoRA projections chained on
+one segment build; see ``decoder_layer``.)
+
 A step is one pass of the whole hot path over one batch: one fused layer call
 (gemm_lowp_lora_epilogue with LORA_FUSE_SHRINK | LORA_BUILD_SEGMENTS: the segment builder,
 the down-projection and the GEMM with its LoRA epilogue in one launch; above 16 tokens
@@ -81,6 +84,102 @@ def cpu_baseline(wl, budget_s: float = 12.0, act: str = "mxfp8"):
             "sample": sample + f" ({el:.1f} s)"}
 
 
+# one decoder layer's LoRA projections (Llama-3-8B shapes), 16-token decode, 8 adapters
+DECODER_LAYER = [("qkv", 4096, 6144, "fp8"), ("o", 4096, 4096, "fp8"), ("gate_up", 4096, 28672, "fp8"),
+                 ("down", 14336, 4096, "mxfp4")]
+DECODER_RANKS = [8, 16, 16, 32, 64, 8, 16, 32]
+
+
+def decoder_layer(args):
+    """A step is the four projections of one decoder layer chained on one segment build
+    (the first call builds the segments in its launch, the others read them)."""
+    import torch
+    import precision_gemm_amd as P
+    import workloads
+    from workloads.device import upload
+    from oracle.layer import LowpWeight, layer
+    a16 = args.act == "bf16"
+    T = 16
+    ids = np.random.default_rng(60).integers(0, len(DECODER_RANKS), T)
+    wls = [workloads.make_custom(T, K, N, fmt, DECODER_RANKS, ids, [1.0 + 0.25 * a for a in range(len(DECODER_RANKS))],
+                                 61 + i, name=name, b_std=0.02) for i, (name, K, N, fmt) in enumerate(DECODER_LAYER)]
+    nbytes = sum(algorithmic(wl)[0] for wl in wls)
+    flops = sum(algorithmic(wl)[1] for wl in wls)
+    sets = args.sets or max(1, min(32, int(np.ceil(2 * 256e6 / nbytes)) + 1))
+    print(f"[bench] uploading {sets} input set(s) of {nbytes / 1e6:.1f} MB", file=sys.stderr, flush=True)
+    S = []
+    for _ in range(sets):
+        ids_d = torch.from_numpy(np.asarray(ids, np.int32)).cuda()
+        seg = P.empty_segments(ids_d, len(DECODER_RANKS))
+        projs = []
+        for wl in wls:
+            x, w, ad, _ = upload(wl)
+            projs.append(dict(x=x, w=w, ad=ad, ws=P.alloc_workspace(T, wl.K, wl.N, ad.n, ad.r_max),
+                              y=torch.empty((T, wl.N), dtype=torch.bfloat16, device="cuda")))
+        S.append(dict(seg=seg, projs=projs))
+    torch.cuda.synchronize()
+
+    def step(s):
+        d = S[s % sets]
+        for i, q in enumerate(d["projs"]):
+            P.gemm_lowp_lora_epilogue(q["x"], q["w"], d["seg"], q["ad"], q["ws"], fuse_shrink=True, y=q["y"],
+                                      build_segments=(i == 0), act_bf16=a16)
+
+    step(0)
+    torch.cuda.synchronize()
+    worst = {"max_rel": 0.0, "frob_rel": 0.0}
+    for wl, q in zip(wls, S[0]["projs"]):
+        ref = layer(wl.x, LowpWeight(wl.fmt, wl.w_q, wl.w_scale), wl.A, wl.B, wl.scale, wl.ids, act=args.act)["y"]
+        dlt = q["y"].float().cpu().numpy().astype(np.float64) - ref
+        worst["max_rel"] = max(worst["max_rel"], float(np.abs(dlt).max() / np.abs(ref).max()))
+        worst["frob_rel"] = max(worst["frob_rel"], float(np.linalg.norm(dlt) / np.linalg.norm(ref)))
+    parity = dict(worst, rows_checked=T, projections=len(wls),
+                  **{"pass": worst["max_rel"] <= 1e-2 and worst["frob_rel"] <= 5e-3})
+    for i in range(args.warmup):
+        step(i)
+    K = args.steps
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(K):
+            step(i)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) * 1e6 / K
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ev_us = e0.elapsed_time(e1) * 1e3 / K
+    status = max(P.workspace_status(q["ws"]) for d in S for q in d["projs"])
+    achieved = nbytes / (ev_us * 1e-6) / 1e9
+    out = {
+        "metric": METRIC, "value": round(us, 3), "unit": "us/call", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": us / 1e3, "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16xfp8" if a16 else "fp8", "data": "synthetic",
+        "config": {"workload": "decoder_layer", "activations": args.act, "T": T,
+                   "projections": [f"{n}: K={k} N={m} {f}" for n, k, m, f in DECODER_LAYER],
+                   "adapters": len(DECODER_RANKS), "ranks": sorted(set(DECODER_RANKS)), "input_sets": sets,
+                   "timing": "hip graph of K steps (four layer calls each)"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "k_layer x 4 (the chain's four launches together)", "per_call_bytes": nbytes,
+                     "per_call_flops": flops, "kernel_us": ev_us},
+        "parity": parity, "device_status": status, "kernel_sha": kernel_source_sha(),
+    }
+    if not args.no_cpu:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        parts = [cpu_baseline(wl, budget_s=4.0, act=args.act) for wl in wls]
+        out["cpu_baseline"] = {"value": sum(p["value"] for p in parts), "unit": "us/call",
+                               "cores": max(p["cores"] for p in parts), "kind": "oracle",
+                               "sample": "the four projections, each: " + "; ".join(p["sample"] for p in parts)}
+    print(json.dumps(out))
+
+
 def stored_traffic(workload: str, sha: str):
     p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(p):
@@ -97,7 +196,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_qkv",
-                    choices=["tiny", "decode_qkv", "decode_gateup", "prefill", "downproj_fp4"])
+                    choices=["tiny", "decode_qkv", "decode_gateup", "prefill", "downproj_fp4", "decoder_layer"])
     ap.add_argument("--sets", type=int, default=0, help="input copies to rotate over (0: enough for 2x 256 MB)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--act", choices=["mxfp8", "bf16"], default="mxfp8",
@@ -119,6 +218,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload == "decoder_layer":
+        decoder_layer(args)
+        return
     print(f"[bench] generating {args.workload}", file=sys.stderr, flush=True)
     wl = workloads.make(args.workload)
     a16 = args.act == "bf16"
