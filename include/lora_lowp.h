@@ -31,9 +31,26 @@
  *    of such tokens.
  *  - Limits: K % 128 == 0 (whole MFMA K-steps; MX blocks are 32), N % 64 == 0,
  *    0 <= T <= 65536 (T == 0 is a no-op returning LORA_OK), 1 <= n_adapters <= 8192,
- *    r_max a multiple of 8 in [8, 64], every rank a multiple of 8 in [8, r_max].  The
- *    ranks live in device memory, so the kernels check them: an adapter whose rank
- *    breaks this rule contributes no adapter term (and its rows of t are not written).
+ *    1 <= r_max <= 64, and every rank r_a in [1, r_max] (any value: ranks differ per
+ *    adapter).  The ranks live in device memory, so the kernels check them: an
+ *    adapter whose rank is outside [1, r_max] contributes no adapter term (its rows of
+ *    t are not written) and the layer call sets bit 1 of the workspace status word
+ *    (lora_workspace_status), so the error is never silent.
+ *
+ * Where this interface departs from the problem as the pages state it (adapter
+ * A [K, r] and B [r, N] in any layout the caller likes, K a multiple of the MX block
+ * of 32), and why:
+ *  - Adapters are read in a packed form made once by lora_pack_adapter from A [K][r]
+ *    and B [r][N] row-major: A^T [rank_pad(r)][K] and B^T [N][rank_pad(r)], with
+ *    rank_pad(r) = r rounded up to a multiple of 8.  Both adapter products then read
+ *    16-byte runs along their reduction dimension straight into bf16 MFMA operands,
+ *    and any rank keeps those runs aligned.  Like the quantisation of W, this is an
+ *    offline step per adapter, not per call.
+ *  - W is read in the packed form made once by lora_pack_weight (below): each 16-byte
+ *    load of the GEMM then reads 1 KB of consecutive memory.
+ *  - K % 128 == 0 instead of K % 32: the scaled MFMA takes 128 values of K per step;
+ *    N % 64 == 0: the narrowest column tile of a workgroup is 64 channels.  Other
+ *    shapes return LORA_ERR_UNSUPPORTED (they are never computed wrongly).
  *
  * Data layouts:
  *  - W, FP8 (LORA_W_FP8_E4M3), row-major form: w_q uint8 [N][K] e4m3fn codes (K
@@ -50,17 +67,20 @@
  *      MXFP4: [N/16][K/128][l][16 B]: 32 codes of channel 16*nt + l%16 at
  *             k = 128*ks + 32*(l/16) .., and scales [N/16][K/128][l] (one byte:
  *             the code of k-block 4*ks + l/16).
- *  - Adapter a: A_a [K][r_a] is stored as A_a^T, bf16 [r_a][K] (K contiguous),
- *    and B_a [r_a][N] as B_a^T, bf16 [N][r_a] (r_a contiguous) -- the weights of
- *    the linear maps K -> r_a and r_a -> N in out-by-in order, so that both matrix
- *    products read 16-byte runs along their reduction dimension.
+ *  - Adapter a (packed by lora_pack_adapter): A_a [K][r_a] is stored as A_a^T, bf16
+ *    [rank_pad(r_a)][K] (K contiguous), and B_a [r_a][N] as B_a^T, bf16
+ *    [N][rank_pad(r_a)] (ranks contiguous) -- the weights of the linear maps
+ *    K -> r_a and r_a -> N in out-by-in order.  Rows of A_a^T and columns of B_a^T
+ *    at index >= r_a are padding: lora_pack_adapter zero-fills them, and the kernels
+ *    never let them reach a result.  16-byte aligned.
  *    A_ptrs / B_ptrs are device arrays of n_adapters device addresses (uint64),
  *    so adapters may live anywhere in device memory.  ranks int32 [n_adapters],
  *    scales float [n_adapters].
  *  - Segments (from lora_build_segments): seg_indptr int32 [n_adapters + 1] is a
  *    CSR over adapter ids (empty adapters included), sorted_tok int32 [T] lists
  *    token indices ordered by (adapter id, token index).
- *  - t: float [T][r_max], original token order, columns j >= r_a hold zero.
+ *  - t: float [T][r_max] (row stride r_max), original token order, columns
+ *    j >= r_a hold zero.
  *  - y: bf16 [T][N], original token order.
  *
  * Workspace: gemm_lowp_lora_epilogue and lora_shrink take a caller-provided
@@ -147,6 +167,16 @@ lora_status lora_build_segments(const int32_t* adapter_id, int32_t T, int32_t n_
 lora_status lora_pack_weight(int32_t w_fmt, const uint8_t* q, const uint8_t* scale, int32_t N, int32_t K,
                              uint8_t* q_packed, uint8_t* scale_packed, void* stream);
 
+/* Pack one adapter ("Punica" README, Overview: A [H1, r] and B [r, H2]) into the form
+ * the layer reads: A bf16 [K][r] row-major -> At bf16 [rank_pad(r)][K] (At[j][k] =
+ * A[k][j]); B bf16 [r][N] row-major -> Bt bf16 [N][rank_pad(r)] (Bt[n][j] = B[j][n]);
+ * padding rows of At and columns of Bt are zero.  rank_pad(r) = (r + 7) / 8 * 8.
+ * An offline step per adapter.  1 <= r <= 64 (else LORA_ERR_UNSUPPORTED, or
+ * LORA_ERR_INVALID_ARG for r < 1); At and Bt 16-byte aligned; no buffer may overlap
+ * another. */
+lora_status lora_pack_adapter(const uint16_t* A, const uint16_t* B, int32_t K, int32_t N, int32_t r,
+                              uint16_t* At, uint16_t* Bt, void* stream);
+
 /* MXFP8 quantisation of bf16 activations x [T][K] -> x_q uint8 [T][K] e4m3fn codes,
  * x_sc uint8 [T][K/32] e8m0 codes, by the rule in the header comment.  Bit-exact;
  * the same device function quantises x inside gemm_lowp_lora_epilogue. */
@@ -159,7 +189,9 @@ lora_status lora_quant_act_mxfp8(const uint16_t* x, int32_t T, int32_t K,
  * fp32 accumulation of exact bf16 products, written in original token order,
  * zero for j >= r_a.  Fixed summation order: bitwise deterministic.  The standalone
  * down-projection needs no scratch memory: workspace may be NULL (kept in the
- * signature so that callers can pass the layer's workspace). */
+ * signature so that callers can pass the layer's workspace).  An adapter whose rank is
+ * outside [1, r_max] is skipped (its rows of t are not written); the layer call that
+ * consumes t reports it. */
 lora_status lora_shrink(const uint16_t* x, int32_t T, int32_t K,
                         const int32_t* seg_indptr, const int32_t* sorted_tok,
                         const uint64_t* A_ptrs, const int32_t* ranks,
@@ -168,7 +200,8 @@ lora_status lora_shrink(const uint16_t* x, int32_t T, int32_t K,
 
 /* Adapter up-projection as its own launch (the unfused schedule the "EpiLoRA"
  * abstract replaces):  y[tok, :] = bf16( y[tok, :] + s_a * t[tok, :r_a] @ B_a ).
- * y is read and written in place. */
+ * y is read and written in place.  Tokens whose adapter id is outside
+ * [0, n_adapters) or whose adapter's rank is outside [1, r_max] are left as they are. */
 lora_status lora_expand(const float* t, int32_t T, int32_t N,
                         const int32_t* adapter_id, const uint64_t* B_ptrs,
                         const int32_t* ranks, const float* scales,
@@ -198,10 +231,11 @@ lora_status gemm_lowp_lora_epilogue(const uint16_t* x, int32_t T, int32_t K, int
                                     uint16_t* y, uint32_t flags,
                                     void* workspace, size_t workspace_bytes, void* stream);
 
-/* Device-side status word of the last gemm_lowp_lora_epilogue / lora_shrink that
- * used this workspace: copies one int32 to *status_dev (device pointer) on
- * `stream`.  0 = fine; non-zero = a bounded wait in the fused launch gave up
- * (the output is then unspecified).  Cleared by lora_workspace_init. */
+/* Device-side status word of the layer calls on this workspace since it was last
+ * initialised (bits accumulate): copies one int32 to *status_dev (device pointer) on
+ * `stream`.  0 = fine; bit 0 = a bounded wait in the fused launch gave up (the output
+ * is then unspecified); bit 1 = a token's adapter had a rank outside [1, r_max] (that
+ * adapter's term was left out).  Cleared by lora_workspace_init. */
 lora_status lora_workspace_status(const void* workspace, int32_t* status_dev, void* stream);
 
 /* Error word of the last segment build inside gemm_lowp_lora_epilogue

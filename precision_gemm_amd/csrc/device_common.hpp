@@ -228,6 +228,9 @@ __device__ __forceinline__ int add_agent(int* p, int v) {
 __device__ __forceinline__ void set_agent(int* p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void or_agent(int* p, int v) {
+  __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ void st_agent_u64(uint64_t* p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -244,5 +247,13 @@ __device__ __forceinline__ uint64_t ld_agent_u64_at(uint64_t addr) {
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }
 
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
+
+// The first n of the eight bf16 in v (element e in half e % 2 of dword e / 2), the
+// others zeroed; n <= 0 gives zero, n >= 8 gives v.  Masks the padding of an adapter
+// stored with a rank that is not a multiple of 8.
+__device__ __forceinline__ uint4 keep_bf16(const uint4& v, int n) {
+  auto m = [n](int d) -> uint32_t { return (2 * d + 1 < n) ? 0xffffffffu : ((2 * d < n) ? 0x0000ffffu : 0u); };
+  return make_uint4(v.x & m(0), v.y & m(1), v.z & m(2), v.w & m(3));
+}
 
 }  // namespace lora

@@ -32,7 +32,7 @@ lora_status check_sizes(int32_t T, int32_t K, int32_t N) {
 
 lora_status check_adapters(int32_t n_adapters, int32_t r_max) {
   if (n_adapters < 1 || r_max < 1) return LORA_ERR_INVALID_ARG;
-  if (n_adapters > MAX_ADAPTERS || r_max > MAX_RANK || r_max % 8 != 0) return LORA_ERR_UNSUPPORTED;
+  if (n_adapters > MAX_ADAPTERS || r_max > MAX_RANK) return LORA_ERR_UNSUPPORTED;
   return LORA_OK;
 }
 
@@ -42,7 +42,9 @@ lora_status check_adapters(int32_t n_adapters, int32_t r_max) {
 // a16: 16-bit activations: the one-tile stream up to 16 tokens, 64 x 128 tiles with bf16 x
 // staged in LDS above (where N % 128 == 0; otherwise 16-token tiles of the stream, whose
 // token tiles of a column tile share an XCD's L2 for W).
-LayerPlan make_plan(int T, int K, int N, int n_ad, int r_max, int fmt, bool fused = true, bool a16 = false) {
+LayerPlan make_plan(int T, int K, int N, int n_ad, int r_max_in, int fmt, bool fused = true, bool a16 = false) {
+  // internal row stride of t: the caller's r_max rounded up to whole 16-byte runs of bf16
+  const int r_max = rank_pad(r_max_in);
   LayerPlan pl{};
   pl.fmt = fmt;
   pl.a16 = a16;
@@ -214,7 +216,7 @@ lora_status lora_shrink(const uint16_t* x, int32_t T, int32_t K, const int32_t* 
   ShrinkParams sp{};
   sp.x = x; sp.T = T; sp.K = K;
   sp.seg_indptr = seg_indptr; sp.sorted_tok = sorted_tok;
-  sp.A_ptrs = A_ptrs; sp.ranks = ranks; sp.n_ad = n_adapters; sp.r_max = r_max;
+  sp.A_ptrs = A_ptrs; sp.ranks = ranks; sp.n_ad = n_adapters; sp.r_max = rank_pad(r_max); sp.r_lim = r_max;
   sp.ids = nullptr;  // standalone: tokens come from the segments only
   sp.t_out = t; sp.t_tag = nullptr;
   sp.tblk = pl.s_tblk; sp.n_tblk = pl.s_ntblk; sp.n_jg = pl.s_njg; sp.jper = pl.s_jper;
@@ -233,7 +235,7 @@ lora_status lora_expand(const float* t, int32_t T, int32_t N, const int32_t* ada
   if (!t || !adapter_id || !B_ptrs || !ranks || !scales || !y) return LORA_ERR_INVALID_ARG;
   if (!aligned16(t) || !aligned16(y)) return LORA_ERR_INVALID_ARG;
   ExpandParams p{};
-  p.t = t; p.T = T; p.N = N; p.r_max = r_max; p.n_ad = n_adapters;
+  p.t = t; p.T = T; p.N = N; p.r_lim = r_max; p.n_ad = n_adapters;
   p.ids = adapter_id; p.B_ptrs = B_ptrs; p.ranks = ranks; p.scales = scales; p.y = y;
   return launch_expand(p, as_stream(stream)) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
@@ -301,7 +303,7 @@ lora_status gemm_lowp_lora_epilogue(const uint16_t* x, int32_t T, int32_t K, int
   if (fused) {
     sp.x = x; sp.T = T; sp.K = K;
     sp.seg_indptr = seg_indptr; sp.sorted_tok = sorted_tok;
-    sp.A_ptrs = A_ptrs; sp.ranks = ranks; sp.n_ad = n_adapters; sp.r_max = r_max;
+    sp.A_ptrs = A_ptrs; sp.ranks = ranks; sp.n_ad = n_adapters; sp.r_max = rank_pad(r_max); sp.r_lim = r_max;
     sp.ids = adapter_id;
     sp.t_out = t;  // may be null
     sp.t_tag = ttag;
@@ -325,7 +327,8 @@ lora_status gemm_lowp_lora_epilogue(const uint16_t* x, int32_t T, int32_t K, int
   gp.t_tag = fused ? ttag : nullptr;
   gp.t_kparts = pl.s_kparts;
   gp.t_pack = (fused && pl.s_kparts == 1 && T > 16 && pl.TT != 1) ? 1 : 0;
-  gp.r_max = r_max;
+  gp.r_max = rank_pad(r_max);
+  gp.r_lim = r_max;
   gp.ids = adapter_id; gp.B_ptrs = B_ptrs; gp.ranks = ranks; gp.scales = scales; gp.n_ad = n_adapters;
   gp.y = y;
   gp.ksplit = pl.ksplit; gp.krange = pl.krange; gp.n_cb = pl.n_cb; gp.n_tb = pl.n_tb;
@@ -351,6 +354,22 @@ lora_status lora_pack_weight(int32_t w_fmt, const uint8_t* q, const uint8_t* sca
   hipError_t e = launch_pack_weight(w_fmt, q, reinterpret_cast<const uint8_t*>(scale), N, K, q_packed, scale_packed,
                                     as_stream(stream));
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+lora_status lora_pack_adapter(const uint16_t* A, const uint16_t* B, int32_t K, int32_t N, int32_t r, uint16_t* At,
+                              uint16_t* Bt, void* stream) {
+  if (K <= 0 || N <= 0 || r < 1) return LORA_ERR_INVALID_ARG;
+  if (r > MAX_RANK) return LORA_ERR_UNSUPPORTED;
+  if (!A || !B || !At || !Bt || !aligned16(At) || !aligned16(Bt)) return LORA_ERR_INVALID_ARG;
+  const char *a0 = reinterpret_cast<const char*>(A), *b0 = reinterpret_cast<const char*>(B);
+  const char *o0 = reinterpret_cast<const char*>(At), *p0 = reinterpret_cast<const char*>(Bt);
+  const size_t na = (size_t)K * r * 2, nb = (size_t)N * r * 2;
+  const size_t nat = (size_t)rank_pad(r) * K * 2, nbt = (size_t)N * rank_pad(r) * 2;
+  auto overlap = [](const char* x, size_t nx, const char* y, size_t ny) { return x < y + ny && y < x + nx; };
+  if (overlap(a0, na, o0, nat) || overlap(a0, na, p0, nbt) || overlap(b0, nb, o0, nat) || overlap(b0, nb, p0, nbt) ||
+      overlap(o0, nat, p0, nbt))
+    return LORA_ERR_INVALID_ARG;  // not in place
+  return launch_pack_adapter(A, B, K, N, r, At, Bt, as_stream(stream)) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
 /* Introspection for tests and the benchmark: the plan chosen for these sizes. */

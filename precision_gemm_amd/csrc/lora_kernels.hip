@@ -296,6 +296,31 @@ __global__ __launch_bounds__(256) void k_pack_weight(int fmt, const uint8_t* __r
 }
 
 // ======================================================================================
+// Adapter layout.  The pages state an adapter as A [K, r] and B [r, N] ("Punica" README,
+// Overview: A [H1, r], B [r, H2]), both row-major here.  The kernels read them as the
+// weights of the maps K -> r and r -> N in out-by-in order, so that both adapter products
+// read 16-byte runs along their reduction dimension: A^T [rank_pad(r)][K] and
+// B^T [N][rank_pad(r)], the padding rows / columns zero.  One thread per output element
+// (an offline step, like the packing of W).
+// ======================================================================================
+__global__ __launch_bounds__(256) void k_pack_adapter(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
+                                                      int K, int N, int r, uint16_t* __restrict__ At,
+                                                      uint16_t* __restrict__ Bt) {
+  const int r8 = rank_pad(r);
+  const long na = (long)r8 * K, total = na + (long)N * r8;
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (long)gridDim.x * blockDim.x) {
+    if (i < na) {
+      const int j = (int)(i / K), k = (int)(i % K);
+      At[i] = (j < r) ? A[(long)k * r + j] : (uint16_t)0;
+    } else {
+      const long q = i - na;
+      const int n = (int)(q / r8), j = (int)(q % r8);
+      Bt[q] = (j < r) ? B[(long)j * N + n] : (uint16_t)0;
+    }
+  }
+}
+
+// ======================================================================================
 // Launch epoch (see the file comment)
 // ======================================================================================
 // thread 0 issues the epoch load before any bulk load of the workgroup
@@ -303,21 +328,28 @@ __device__ __forceinline__ int wg_epoch_load(const int* ctrl) {
   return (threadIdx.x == 0) ? ld_agent(ctrl + CTRL_EPOCH) : 0;
 }
 
-// thread 0: publish the epoch to LDS and count this workgroup as started.  The increment
-// carries a data dependency on the epoch value, so it is performed after the load.
+// thread 0: publish the epoch to LDS and count this workgroup as started.  The increment's
+// operand goes through an empty asm statement that takes the epoch as an input, so the
+// compiler waits for the epoch load before the increment is issued (a value-neutral
+// dependence: the increment is always 1).
 __device__ __forceinline__ int wg_epoch_publish(int* ctrl, int e, int* lds_epoch) {
   int started = 0;
   if (threadIdx.x == 0) {
     *lds_epoch = e;
-    started = add_agent(ctrl + CTRL_STARTED, 1 + (e < 0 ? 1 : 0));
+    int one = 1;
+    asm volatile("" : "+v"(one) : "v"(e));
+    started = add_agent(ctrl + CTRL_STARTED, one);
   }
   return started;
 }
 
+// The epoch stays in [0, 2^30): tags (epoch + 1) never overflow a signed int, and a
+// workspace can serve any number of launches (a tag comes back after 2^30 launches).
+constexpr int EPOCH_MASK = 0x3fffffff;
 __device__ __forceinline__ void wg_epoch_end(int* ctrl, int e, int started) {
   if (threadIdx.x == 0 && started == (int)gridDim.x - 1) {
     set_agent(ctrl + CTRL_STARTED, 0);
-    set_agent(ctrl + CTRL_EPOCH, e + 1);
+    set_agent(ctrl + CTRL_EPOCH, (e + 1) & EPOCH_MASK);
   }
 }
 
@@ -332,7 +364,7 @@ __device__ __forceinline__ uint64_t wait_tag(const uint64_t* p, uint64_t v, uint
   while ((uint32_t)(v >> 32) != tag) {
     __builtin_amdgcn_s_sleep(2);
     if (++spins > spin_limit) {
-      set_agent(ctrl + CTRL_STATUS, 1);
+      or_agent(ctrl + CTRL_STATUS, 1);
       break;
     }
     v = ld_agent_u64(p);
@@ -382,7 +414,7 @@ __device__ __forceinline__ void shrink_item(const ShrinkParams& p, int item, cha
       while (ld_agent(ctrl + CTRL_SEGREADY) != tag) {
         __builtin_amdgcn_s_sleep(2);
         if (++spins > p.spin_limit) {
-          set_agent(ctrl + CTRL_STATUS, 1);
+          or_agent(ctrl + CTRL_STATUS, 1);
           break;
         }
       }
@@ -396,8 +428,9 @@ __device__ __forceinline__ void shrink_item(const ShrinkParams& p, int item, cha
   const int tok_begin = tb * p.tblk;
   const int r = p.ranks[a];
   const int j_begin = jg * JP * 16;
-  // no work: empty token block, unsupported rank (adapter skipped), or ranks beyond r_a
-  if (tok_begin >= L || r < 8 || r > p.r_max || (r & 7) || j_begin >= r) {
+  // no work: empty token block, a rank outside [1, r_max] (the GEMM epilogue reports it
+  // and skips the adapter term), or ranks beyond r_a
+  if (tok_begin >= L || r < 1 || r > p.r_lim || j_begin >= r) {
     publish();
     return;
   }
@@ -499,7 +532,8 @@ __device__ __forceinline__ void shrink_item(const ShrinkParams& p, int item, cha
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int pos = t0 + tt * 16 + 4 * g + v;
-          const float other = pack ? __shfl_xor(sum[v], 1) : 0.f;  // rank j ^ 1, same token (uniform)
+          float other = pack ? __shfl_xor(sum[v], 1) : 0.f;  // rank j ^ 1, same token (uniform)
+          if (j + 1 >= r) other = 0.f;                             // past the rank: a padding row of A
           if (pos < tok_end && j < r && (!direct || p.ids[pos] == a)) {
             const long tok = direct ? pos : tok_at(s0 + pos);
             if (p.t_tag && pack) {
@@ -511,20 +545,20 @@ __device__ __forceinline__ void shrink_item(const ShrinkParams& p, int item, cha
             } else if (p.t_tag) {
               st_agent_u64(p.t_tag + ((long)kp * p.T + tok) * p.r_max + j, tagged(sum[v], tag));
             }
-            if (p.t_out && p.kparts == 1) p.t_out[tok * p.r_max + j] = sum[v];
+            if (p.t_out && p.kparts == 1) p.t_out[tok * p.r_lim + j] = sum[v];
           }
         }
       }
     __syncthreads();
   }
   // columns j in [r, r_max) of the caller's t are zero
-  if (p.t_out && jg == 0 && kp == 0 && r < p.r_max) {
-    const int w = p.r_max - r;
+  if (p.t_out && jg == 0 && kp == 0 && r < p.r_lim) {
+    const int w = p.r_lim - r;
     for (int idx = tid; idx < (tok_end - tok_begin) * w; idx += 256) {
       const int pos = tok_begin + idx / w;
       if (direct && p.ids[pos] != a) continue;
       const long tok = direct ? pos : tok_at(s0 + pos);
-      p.t_out[tok * p.r_max + r + idx % w] = 0.f;
+      p.t_out[tok * p.r_lim + r + idx % w] = 0.f;
     }
   }
 }
@@ -539,7 +573,7 @@ __global__ __launch_bounds__(256) void k_shrink(ShrinkParams p) {
 
 // ======================================================================================
 // Standalone up-projection: y[tok][n] = bf16( y[tok][n] + s_a * sum_j t[tok][j] B_a[j][n] ),
-// B_a stored transposed, bf16 [N][r_a].  One workgroup per (token, 256 columns).
+// B_a stored transposed, bf16 [N][rank_pad(r_a)].  One workgroup per (token, 256 columns).
 // ======================================================================================
 __global__ __launch_bounds__(256) void k_expand(ExpandParams p) {
   __shared__ float trow[64];
@@ -548,14 +582,15 @@ __global__ __launch_bounds__(256) void k_expand(ExpandParams p) {
   const int a = p.ids[tok];
   if (a < 0 || a >= p.n_ad) return;
   const int r = p.ranks[a];
-  if (r < 8 || r > p.r_max || (r & 7)) return;  // unsupported rank: adapter skipped
-  if (threadIdx.x < 64) trow[threadIdx.x] = (threadIdx.x < r) ? p.t[(long)tok * p.r_max + threadIdx.x] : 0.f;
+  if (r < 1 || r > p.r_lim) return;  // a rank outside [1, r_max]: adapter skipped
+  if (threadIdx.x < 64) trow[threadIdx.x] = (threadIdx.x < r) ? p.t[(long)tok * p.r_lim + threadIdx.x] : 0.f;
   __syncthreads();
   if (n >= p.N) return;
-  const uint16_t* __restrict__ Bt = reinterpret_cast<const uint16_t*>(p.B_ptrs[a]) + (long)n * r;
+  const int r8 = rank_pad(r);
+  const uint16_t* __restrict__ Bt = reinterpret_cast<const uint16_t*>(p.B_ptrs[a]) + (long)n * r8;
   float acc = 0.f;
   for (int j = 0; j < r; j += 8) {
-    const uint4 b = ldg16(Bt + j);
+    const uint4 b = keep_bf16(ldg16(Bt + j), r - j);  // the padding past r_a is masked
     const uint32_t w[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -1114,11 +1149,11 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   const int spb = BST / slot;  // slots per batch (>= 2)
   static_assert(BST / (WN * 8 * 2) <= 256, "stage_b keeps a wave's slices one per lane");
   auto prepare_epilogue = [&]() {
-    // (1) adapter, rank, scale and B address of every row; a rank outside the limits
-    //     drops the row's adapter term
+    // (1) adapter, rank, scale and B address of every row; a rank outside [1, r_max]
+    //     drops the row's adapter term (adapter -2: reported after the main loop)
     if (tid < ROWS) {
-      const bool ok = row_ok && row_r >= 8 && row_r <= p.r_max && (row_r & 7) == 0;
-      rowad[tid] = ok ? id_raw : -1;
+      const bool ok = row_ok && row_r >= 1 && row_r <= p.r_lim;
+      rowad[tid] = ok ? id_raw : (row_ok ? -2 : -1);
       rowrk[tid] = ok ? row_r : 0;
       rowsc[tid] = row_s;
       rowbp[tid] = row_bp;
@@ -1186,10 +1221,14 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
         if (need) rowlist[nr + __popcll(bl & ((1ull << lane) - 1ull))] = row;
         nr += __popcll(bl);
       }
+      // any row whose adapter has a rank outside [1, r_max]
+      bool bad = false;
+      for (int c0 = 0; c0 < ROWS; c0 += 64) bad |= __ballot(c0 + lane < ROWS && rowad[c0 + lane] == -2) != 0ull;
       if (lane == 0) {
         meta[0] = n;
         meta[1] = nr;
         meta[2] = n_own;
+        meta[3] = bad ? 1 : 0;
       }
     }
   };
@@ -1229,9 +1268,10 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
       const int r = __builtin_amdgcn_readlane(r_l, j);
       const uint64_t bpu = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(bp_l >> 32), j) << 32) |
                            (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)bp_l, j);
-      const char* src = reinterpret_cast<const char*>(bpu) + (long)n_tile0 * r * 2;
+      const int r8 = rank_pad(r);  // the stored row length of B_a^T
+      const char* src = reinterpret_cast<const char*>(bpu) + (long)n_tile0 * r8 * 2;
       char* dst = stg + (k % spb) * slot;
-      const int bytes = WN * r * 2;
+      const int bytes = WN * r8 * 2;
       for (int c = 0; c < bytes; c += 1024) {
         if (c + lane * 16 < bytes)
           __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + c + lane * 16),
@@ -1279,7 +1319,7 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
       }
     } else {
 #pragma unroll
-      for (int m = 0; m < EPI_TH; ++m) tpl[m] = p.t[(long)(row0 + trow(m)) * p.r_max + tcol(m)];
+      for (int m = 0; m < EPI_TH; ++m) tpl[m] = p.t[(long)(row0 + trow(m)) * p.r_lim + min(tcol(m), p.r_lim - 1)];
     }
   };
   // The stream's tagged t gather, issued before its last round of k-steps is multiplied:
@@ -1322,11 +1362,12 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
     sb_a = sb_on ? rowad[row] : -1;
     const uint64_t bp = sb_on ? rowbp[row] : reinterpret_cast<uint64_t>(p.x);
     const int j = ((sb_it >> 8) & 1) * 32 + 8 * g;
-    const int jc = min(j, sb_r - 8);
+    const int r8 = rank_pad(sb_r);
+    const int jc = min(j, r8 - 8);
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
       const int nl = wc * CT * 16 + ct * 16 + li;
-      const uint64_t a_b = bp + 2ull * (uint64_t)((long)(n_tile0 + nl) * sb_r + jc);
+      const uint64_t a_b = bp + 2ull * (uint64_t)((long)(n_tile0 + nl) * r8 + jc);
       const uint64_t a_d = reinterpret_cast<uint64_t>(p.x) + 16ull * (uint64_t)ct;
       sb[ct] = ldg16(reinterpret_cast<const void*>(sb_on ? a_b : a_d));
     }
@@ -1416,13 +1457,14 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
     const int jb = (it >> 8) & 1, mask = (it >> 9) & 255;
     const int j = jb * 32 + 8 * g;  // <= 56
     const bool valid = j < r;
-    const int jc = min(j, r - 8);
+    const int r8 = rank_pad(r);
+    const int jc = min(j, r8 - 8);
     uint4 bop[CT];
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
       const int nl = wc * CT * 16 + ct * 16 + li;
-      const uint4 bv = *reinterpret_cast<const uint4*>(stg + off + (nl * r + jc) * 2);
-      bop[ct] = valid ? bv : zero4();
+      const uint4 bv = *reinterpret_cast<const uint4*>(stg + off + (nl * r8 + jc) * 2);
+      bop[ct] = keep_bf16(bv, r - j);  // zero past the rank (padding) and for j >= r
     }
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
@@ -1435,7 +1477,7 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   };
   auto put = [&](int i, int j, float v) {  // t of row i, rank j: staged (scaled, bf16) and the caller's t
     tbuf[i * TSTR + j] = (uint16_t)f32_to_bf16_rne(v * rowsc[i]);
-    if (p.t_out && cb == 0) p.t_out[(long)(row0 + i) * p.r_max + j] = v;
+    if (p.t_out && cb == 0 && j < p.r_lim) p.t_out[(long)(row0 + i) * p.r_lim + j] = v;
   };
   if constexpr (TT != 1) load_chan_s();
   // ---- up-projection loads of the chunked path go out as soon as the main loop ends
@@ -1450,6 +1492,8 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
     if (!p.t_tag) load_t(0);
   }
 
+  // a rank outside [1, r_max] in this tile: bit 1 of the status word
+  if (p.lora && tid == 0 && meta[3]) or_agent(p.ctrl + CTRL_STATUS, 2);
   // publish the launch epoch only now: waiting for it earlier would stall wave 0
   *started = wg_epoch_publish(p.ctrl, e, lds_epoch);
   __syncthreads();
@@ -1534,7 +1578,7 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
           const uint4 aop = (valid && myad[tt] == sb_a) ? tv : zero4();
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct)
-            lacc(tt, ct) = mfma_bf16_16x16x32(aop, valid ? sb[ct] : zero4(), lacc(tt, ct));
+            lacc(tt, ct) = mfma_bf16_16x16x32(aop, keep_bf16(sb[ct], sb_r - j), lacc(tt, ct));
         }
       }
       __syncthreads();  // the area of the k-wave sums lies over the staged t
@@ -1569,11 +1613,12 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
             const uint64_t bpu =
                 ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(bp_l >> 32), q) << 32) |
                 (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)bp_l, q);
-            const int jc = min(((itq[u] >> 8) & 1) * 32 + 8 * g, rq[u] - 8);
+            const int r8 = rank_pad(rq[u]);
+            const int jc = min(((itq[u] >> 8) & 1) * 32 + 8 * g, r8 - 8);
             const uint16_t* bsrc = reinterpret_cast<const uint16_t*>(bpu);
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct)
-              bop[u][ct] = ldg16(bsrc + (long)(n_tile0 + wc * CT * 16 + ct * 16 + li) * rq[u] + jc);
+              bop[u][ct] = ldg16(bsrc + (long)(n_tile0 + wc * CT * 16 + ct * 16 + li) * r8 + jc);
           }
 #pragma unroll
           for (int u = 0; u < IB; ++u) {
@@ -1581,6 +1626,10 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
             const int mask = (itq[u] >> 9) & 255;
             const int j = ((itq[u] >> 8) & 1) * 32 + 8 * g;
             const bool valid = j < rq[u];
+            if (rq[u] & 7) {  // uniform: a rank that is not a multiple of 8 has padding to mask
+#pragma unroll
+              for (int ct = 0; ct < CT; ++ct) bop[u][ct] = keep_bf16(bop[u][ct], rq[u] - j);
+            }
 #pragma unroll
             for (int tt = 0; tt < TT; ++tt) {
               if (!((mask >> tt) & 1)) continue;  // uniform: adapter absent from this token tile
@@ -1675,7 +1724,7 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
       while ((uint32_t)ld_agent(p.gflag + tile_base + k2) != tag) {
         __builtin_amdgcn_s_sleep(2);
         if (++spins > p.spin_limit) {
-          set_agent(p.ctrl + CTRL_STATUS, 1);
+          or_agent(p.ctrl + CTRL_STATUS, 1);
           break;
         }
       }
@@ -1806,7 +1855,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
           while (ld_agent(gp.ctrl + CTRL_SEGREADY) != lds_epoch + 1) {
             __builtin_amdgcn_s_sleep(2);
             if (++spins > sp.spin_limit) {
-              set_agent(gp.ctrl + CTRL_STATUS, 1);
+              or_agent(gp.ctrl + CTRL_STATUS, 1);
               break;
             }
           }
@@ -1819,7 +1868,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
         const int len = coh ? ld_agent(sp.seg_indptr + a + 1) - ld_agent(sp.seg_indptr + a)
                             : sp.seg_indptr[a + 1] - sp.seg_indptr[a];
         const int r = sp.ranks[a];
-        const bool ok = r >= 8 && r <= sp.r_max && (r & 7) == 0;
+        const bool ok = r >= 1 && r <= sp.r_lim;
         const int nj = min(sp.n_jg, (r + 16 * JP - 1) / (16 * JP));
         return ok ? (len + sp.tblk - 1) / sp.tblk * nj * sp.kparts : 0;
       };
@@ -1982,6 +2031,14 @@ hipError_t launch_pack_weight(int fmt, const uint8_t* q, const uint8_t* sc, int 
   const long chunks = (fmt == LORA_W_FP8_E4M3) ? (long)N * K / 16 : (long)N * K / 32;
   const int grid = (int)std::min<long>((chunks + 255) / 256, 16384);
   hipLaunchKernelGGL(k_pack_weight, dim3(grid), dim3(256), 0, s, fmt, q, sc, N, K, qp, scp);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_adapter(const uint16_t* A, const uint16_t* B, int K, int N, int r, uint16_t* At, uint16_t* Bt,
+                               hipStream_t s) {
+  const long total = (long)rank_pad(r) * (K + (long)N);
+  const int grid = (int)std::min<long>((total + 255) / 256, 4096);
+  hipLaunchKernelGGL(k_pack_adapter, dim3(grid), dim3(256), 0, s, A, B, K, N, r, At, Bt);
   return hipGetLastError();
 }
 

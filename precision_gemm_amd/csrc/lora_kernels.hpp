@@ -14,11 +14,16 @@ namespace lora {
 constexpr int MAX_ADAPTERS = 8192;
 constexpr int MAX_RANK = 64;
 
+// Stored adapters are padded to a whole number of 16-byte runs of bf16: A_a^T has
+// rank_pad(r_a) rows and B_a^T rank_pad(r_a) columns (lora_pack_adapter zero-fills the
+// padding; the kernels mask it out whatever it holds).
+__host__ __device__ constexpr int rank_pad(int r) { return (r + 7) & ~7; }
+
 // Workspace control block (int32 words at the start of every workspace)
 enum : int {
   CTRL_EPOCH = 0,    // number of fused launches completed on this workspace (tag = epoch + 1)
   CTRL_STARTED = 1,  // workgroups of the current launch that have read the epoch
-  CTRL_STATUS = 2,   // non-zero: a bounded wait gave up
+  CTRL_STATUS = 2,   // bit 0: a bounded wait gave up; bit 1: an adapter's rank was outside [1, r_max]
   CTRL_SEGREADY = 3, // tag of the launch whose segment builder has finished
   CTRL_SEGERR = 4,   // error word of the last in-launch segment build
 };
@@ -29,10 +34,12 @@ struct ShrinkParams {
   const int* seg_indptr;
   const int* sorted_tok;
   const int* ids;          // fused launch with T <= 16: tokens found by id (may be null)
-  const uint64_t* A_ptrs;  // A_a^T, bf16 [r_a][K]
+  const uint64_t* A_ptrs;  // A_a^T, bf16 [rank_pad(r_a)][K]
   const int* ranks;
-  int n_ad, r_max;
-  float* t_out;        // plain fp32 [T][r_max] (may be null in the fused launch)
+  int n_ad;
+  int r_max;           // rank_pad of the caller's r_max: row stride of the tagged t
+  int r_lim;           // the caller's r_max: largest valid rank, row stride of t_out
+  float* t_out;        // plain fp32 [T][r_lim] (may be null in the fused launch)
   uint64_t* t_tag;     // tagged [kparts][T][r_max] (fused launch only, else null)
   int t_pack;          // t_tag holds [T][r_max / 2] tagged bf16 pairs of s_a t (one K-part)
   const float* scales; // adapter scales (for the pairs)
@@ -55,14 +62,15 @@ struct GemmParams {
   const uint8_t* wq;
   const float* ws_fp8;    // FP8 channel scales [N]
   const uint8_t* ws_fp4;  // MXFP4 block scales [N][K/32]
-  const float* t;         // plain t (unfused), or null
+  const float* t;         // plain t [T][r_lim] (unfused), or null
   float* t_out;           // fused launch: the caller's t, written when t_kparts > 1 (may be null)
   const uint64_t* t_tag;  // tagged t partials (fused), or null
   int t_kparts;
   int t_pack;             // t_tag holds tagged bf16 pairs of s_a t (see ShrinkParams)
-  int r_max;
+  int r_max;              // rank_pad of the caller's r_max (internal row stride of t)
+  int r_lim;              // the caller's r_max (largest valid rank, row stride of t and t_out)
   const int* ids;
-  const uint64_t* B_ptrs;  // B_a^T, bf16 [N][r_a]
+  const uint64_t* B_ptrs;  // B_a^T, bf16 [N][rank_pad(r_a)]
   const int* ranks;
   const float* scales;
   int n_ad;
@@ -79,8 +87,8 @@ struct GemmParams {
 };
 
 struct ExpandParams {
-  const float* t;
-  int T, N, r_max, n_ad;
+  const float* t;      // [T][r_lim]
+  int T, N, r_lim, n_ad;
   const int* ids;
   const uint64_t* B_ptrs;
   const int* ranks;
@@ -118,5 +126,7 @@ hipError_t launch_layer(const LayerPlan& pl, hipStream_t stream, const ShrinkPar
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_pack_weight(int fmt, const uint8_t* q, const uint8_t* sc, int N, int K, uint8_t* qp, uint8_t* scp,
                               hipStream_t s);
+hipError_t launch_pack_adapter(const uint16_t* A, const uint16_t* B, int K, int N, int r, uint16_t* At, uint16_t* Bt,
+                               hipStream_t s);
 
 }  // namespace lora

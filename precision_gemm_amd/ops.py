@@ -78,17 +78,42 @@ def pack_weight(w: LowpWeight) -> LowpWeight:
     return LowpWeight(w.fmt, qp, sp, packed=True)
 
 
+def rank_pad(r: int) -> int:
+    """Stored rank of an adapter of rank r: r rounded up to a multiple of 8."""
+    return (int(r) + 7) // 8 * 8
+
+
+def pack_adapter(A: torch.Tensor, B: torch.Tensor):
+    """Pack one adapter, A bf16 [K, r] and B bf16 [r, N], into the form the layer reads
+    (lora_pack_adapter): returns ``(At, Bt)``, bf16 [rank_pad(r), K] and [N, rank_pad(r)]."""
+    _dev(A, "A", torch.bfloat16)
+    _dev(B, "B", torch.bfloat16)
+    K, r = A.shape
+    r2, N = B.shape
+    if r2 != r:
+        raise ValueError(f"A is [K, {r}] but B is [{r2}, N]")
+    rp = rank_pad(r)
+    At = torch.empty((rp, K), dtype=torch.bfloat16, device=A.device)
+    Bt = torch.empty((N, rp), dtype=torch.bfloat16, device=A.device)
+    check("lora_pack_adapter", lib().lora_pack_adapter(_ptr(A), _ptr(B), K, N, r, _ptr(At), _ptr(Bt), _stream()))
+    return At, Bt
+
+
 @dataclass
 class Adapters:
     """A set of LoRA adapters resident on the device.
 
-    ``At[a]`` is A_a^T (bf16 [r_a, K]) and ``Bt[a]`` is B_a^T (bf16 [N, r_a]); the
-    pointer tables, ranks and scales are device arrays built once here.
+    ``A[a]`` is bf16 [K, r_a] and ``B[a]`` bf16 [r_a, N] (the layouts of the problem
+    statement); they are packed once here by lora_pack_adapter into ``At[a]`` (bf16
+    [rank_pad(r_a), K]) and ``Bt[a]`` (bf16 [N, rank_pad(r_a)]), which the kernels read.
+    The pointer tables, ranks and scales are device arrays built once here.
     """
 
-    At: list
-    Bt: list
+    A: list
+    B: list
     scales: torch.Tensor            # float32 [n]
+    At: list = field(init=False)
+    Bt: list = field(init=False)
     ranks: torch.Tensor = field(init=False)
     A_ptrs: torch.Tensor = field(init=False)
     B_ptrs: torch.Tensor = field(init=False)
@@ -96,10 +121,10 @@ class Adapters:
 
     def __post_init__(self):
         dev = self.scales.device
-        for a, b in zip(self.At, self.Bt):
-            _dev(a, "A^T", torch.bfloat16)
-            _dev(b, "B^T", torch.bfloat16)
-        rk = [int(a.shape[0]) for a in self.At]
+        packed = [pack_adapter(a, b) for a, b in zip(self.A, self.B)]
+        self.At = [p[0] for p in packed]
+        self.Bt = [p[1] for p in packed]
+        rk = [int(a.shape[1]) for a in self.A]
         self.ranks = torch.tensor(rk, dtype=torch.int32, device=dev)
         self.r_max = max(rk)
         self.A_ptrs = torch.tensor([a.data_ptr() for a in self.At], dtype=torch.int64, device=dev)
@@ -108,7 +133,7 @@ class Adapters:
 
     @property
     def n(self) -> int:
-        return len(self.At)
+        return len(self.A)
 
 
 @dataclass

@@ -28,6 +28,19 @@ def named_oracle(name: str, rows: tuple | None = None):
     return run_oracle(wl, rows)
 
 
+def sample_rows(wl, n: int, seed: int) -> tuple:
+    """Rows for an oracle check of a long batch (every row of y depends only on its own
+    token): n random rows plus the first and the last row of every adapter's segment in
+    token order, so that the shortest segments are always checked."""
+    ids = np.asarray(wl.ids)
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(wl.T, n, replace=False).tolist())
+    for a in np.unique(ids):
+        where = np.flatnonzero(ids == a)
+        rows.update([int(where[0]), int(where[-1])])
+    return tuple(sorted(rows))
+
+
 def run_oracle(wl, rows=None, act="mxfp8"):
     ids = np.asarray(wl.ids)
     x = wl.x

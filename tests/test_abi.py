@@ -34,8 +34,10 @@ def test_workspace_bytes(L):
     assert L.lora_workspace_bytes(16, 4096, 6144, 1, 16) > 0
     assert L.lora_workspace_bytes(16, 4000, 6144, 1, 16) == 0      # K % 128
     assert L.lora_workspace_bytes(16, 4096, 6100, 1, 16) == 0      # N % 64
-    assert L.lora_workspace_bytes(16, 4096, 6144, 1, 12) == 0      # r_max % 8
-    assert L.lora_workspace_bytes(16, 4096, 6144, 1, 128) == 0     # r_max > 64
+    assert L.lora_workspace_bytes(16, 4096, 6144, 1, 12) > 0       # any r_max in [1, 64]
+    assert L.lora_workspace_bytes(16, 4096, 6144, 1, 1) > 0
+    assert L.lora_workspace_bytes(16, 4096, 6144, 1, 65) == 0      # r_max > 64
+    assert L.lora_workspace_bytes(16, 4096, 6144, 1, 0) == 0
     assert L.lora_workspace_bytes(16, 4096, 6144, 0, 16) == 0
     assert L.lora_workspace_bytes(-1, 4096, 6144, 1, 16) == 0
 
@@ -77,7 +79,10 @@ def test_gemm_validation(L):
     assert _gemm(L, x=MISALIGNED) == INVALID
     assert _gemm(L, A=NULL) == INVALID                   # fused needs A
     assert _gemm(L, flags=0, t=NULL, A=NULL, B=NULL, ids=NULL, rk=NULL, sc=NULL) == WORKSPACE  # base only: adapters optional
-    assert _gemm(L, r=12) == UNSUPPORTED
+    assert _gemm(L, r=12) == WORKSPACE                   # any r_max in [1, 64] is valid
+    assert _gemm(L, r=1) == WORKSPACE
+    assert _gemm(L, r=65) == UNSUPPORTED
+    assert _gemm(L, r=0) == INVALID
     assert _gemm(L, n=0) == INVALID
     assert _gemm(L) == WORKSPACE                         # no workspace
     assert _gemm(L, wsp=FAKE, wsb=16) == WORKSPACE       # too small
@@ -140,3 +145,40 @@ def test_flag_values_match_header():
     vals = {m.group(1): 1 << int(m.group(2)) for m in re.finditer(r"(LORA_[A-Z0-9_]+) = 1u << (\d+)", text)}
     assert vals == {"LORA_FUSE_SHRINK": P.LORA_FUSE_SHRINK, "LORA_BUILD_SEGMENTS": P.LORA_BUILD_SEGMENTS,
                     "LORA_ACT_BF16": P.LORA_ACT_BF16}
+
+
+def test_status_of_every_unsupported_shape_and_rank(L):
+    """Each limit of the header, on each call that takes it: the documented status, and
+    nothing enqueued (every pointer here is fake, so a launch would fault)."""
+    # shapes: K % 128, N % 64, T above 65536, ranks above 64, adapters above 8192
+    for kw, want in [(dict(K=4096 + 32), UNSUPPORTED), (dict(K=4096 + 96), UNSUPPORTED), (dict(K=0), INVALID),
+                     (dict(N=6144 + 32), UNSUPPORTED), (dict(N=0), INVALID), (dict(T=65537), UNSUPPORTED),
+                     (dict(r=65), UNSUPPORTED), (dict(r=-3), INVALID), (dict(n=8193), UNSUPPORTED),
+                     (dict(n=-1), INVALID)]:
+        for flags in (0, 1, 3, 5):
+            got = _gemm(L, flags=flags, **kw) if flags != 0 else _gemm(L, flags=0, t=FAKE, **kw)
+            assert got == want, (kw, flags, got)
+    assert L.lora_workspace_bytes(16, 4096 + 32, 6144, 1, 16) == 0
+    assert L.lora_workspace_bytes(70000, 4096, 6144, 1, 16) == 0
+    assert L.lora_workspace_bytes(16, 4096, 6144, 8193, 16) == 0
+    assert L.lora_shrink(FAKE, 4, 4096 + 32, FAKE, FAKE, FAKE, FAKE, 2, 8, FAKE, NULL, 0, NULL) == UNSUPPORTED
+    assert L.lora_shrink(FAKE, 4, 256, FAKE, FAKE, FAKE, FAKE, 2, 65, FAKE, NULL, 0, NULL) == UNSUPPORTED
+    assert L.lora_shrink(FAKE, 4, 256, FAKE, FAKE, FAKE, FAKE, 2, 0, FAKE, NULL, 0, NULL) == INVALID
+    assert L.lora_expand(FAKE, 4, 256, FAKE, FAKE, FAKE, FAKE, 2, 65, FAKE, NULL) == UNSUPPORTED
+    assert L.lora_expand(FAKE, 4, 256 + 32, FAKE, FAKE, FAKE, FAKE, 2, 8, FAKE, NULL) == UNSUPPORTED
+    assert L.lora_pack_weight(0, FAKE, NULL, 128, 256 + 32, MISALIGNED, NULL, NULL) == UNSUPPORTED
+    # adapters: any rank 1..64 packs; 65 and up are unsupported, 0 and below invalid
+    A, B, At, Bt = (ctypes.c_void_p(0x10000 * i) for i in (1, 2, 3, 4))
+    assert L.lora_pack_adapter(A, B, 4096, 6144, 65, At, Bt, NULL) == UNSUPPORTED
+    assert L.lora_pack_adapter(A, B, 4096, 6144, 0, At, Bt, NULL) == INVALID
+    assert L.lora_pack_adapter(A, B, 0, 6144, 4, At, Bt, NULL) == INVALID
+    assert L.lora_pack_adapter(NULL, B, 4096, 6144, 4, At, Bt, NULL) == INVALID
+    assert L.lora_pack_adapter(A, B, 4096, 6144, 4, MISALIGNED, Bt, NULL) == INVALID
+    assert L.lora_pack_adapter(A, B, 4096, 6144, 4, A, Bt, NULL) == INVALID      # not in place
+    big = ctypes.c_void_p(0x10000 + 4096 * 4 * 2 - 16)                          # overlaps the end of A
+    assert L.lora_pack_adapter(A, B, 4096, 6144, 4, big, ctypes.c_void_p(0x4000000), NULL) == INVALID
+
+
+def test_rank_pad_matches_header():
+    import precision_gemm_amd as P
+    assert [P.rank_pad(r) for r in (1, 4, 7, 8, 9, 12, 20, 60, 64)] == [8, 8, 8, 8, 16, 16, 24, 64, 64]

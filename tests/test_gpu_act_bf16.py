@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 import workloads
-from gpu_util import assert_t_close, assert_y_close, errors, named, run_gpu, run_oracle
+from gpu_util import assert_t_close, assert_y_close, errors, named, run_gpu, run_oracle, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -53,8 +53,9 @@ def test_multi_tile_workloads_bf16_activations(name, build):
     print(f"[case] act_bf16 {name} build={build}", flush=True)
     wl = named(name)
     rows = None
-    if name == "prefill":  # every row of y depends only on its own token
-        rows = tuple(sorted(np.random.default_rng(9).choice(wl.T, 96, replace=False).tolist()))
+    if name == "prefill":  # 96 random rows plus the first and last row of every segment
+        rows = sample_rows(wl, 96, 9)
+        assert 0 in rows
     g = run_gpu(wl, fused=True, build=build, act_bf16=True)
     assert g["status"] == 0 and g["err"] == 0
     _check(wl, g, f"{name} build={build}", rows=rows)

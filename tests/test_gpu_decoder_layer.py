@@ -1,9 +1,12 @@
-"""The four LoRA projections of one decoder layer (Llama-3-8B shapes, a 16-token decode
-batch, 8 adapters of mixed ranks shared by all projections) as a caller chains them: the
-first call builds the batch's segments in its own launch, the other three read them.
-The chain is captured in one HIP graph and replayed three times with eager work and
-synchronisations in between; every replay must equal the eager chain bit for bit, and
-the eager chain must match the oracle per projection (both activation forms)."""
+"""The four LoRA projections of one decoder layer (Llama-3-8B shapes, 8 adapters of mixed
+ranks shared by all projections) as a caller chains them: the first call builds the
+batch's segments in its own launch, the other three read them.  The chain is captured in
+one HIP graph and replayed three times with eager work and synchronisations in between
+(the segment buffers are overwritten with junk before each replay); every replay must
+equal the eager chain bit for bit and rebuild the segments exactly, and the eager chain
+must match the oracle per projection (both activation forms).  At 16 tokens the
+down-projection takes its rows by adapter id; at 64 tokens it reads the segments built
+by the first call, so the chain's hand-over of the segments is exercised."""
 
 import numpy as np
 import pytest
@@ -22,13 +25,14 @@ PROJ = [  # name, K, N, W format
 RANKS = [8, 16, 16, 32, 64, 8, 16, 32]
 
 
+@pytest.mark.parametrize("T", [16, 64])
 @pytest.mark.parametrize("act_bf16", [False, True], ids=["mxfp8", "bf16"])
-def test_decoder_layer_chain_in_one_graph(act_bf16):
+def test_decoder_layer_chain_in_one_graph(act_bf16, T):
     import torch
     import precision_gemm_amd as P
     from workloads.device import upload
-    print(f"[case] decoder layer chain act_bf16={act_bf16}", flush=True)
-    T = 16
+    from oracle.segments import build_segments as oracle_segments
+    print(f"[case] decoder layer chain act_bf16={act_bf16} T={T}", flush=True)
     ids = np.random.default_rng(60).integers(0, len(RANKS), T)
     wls, dev = [], []
     for i, (name, K, N, fmt) in enumerate(PROJ):
@@ -42,6 +46,7 @@ def test_decoder_layer_chain_in_one_graph(act_bf16):
         dev.append(dict(x=x, w=w, ad=ad, ws=ws, t=t, y=y))
     ids_d = torch.from_numpy(np.asarray(ids, np.int32)).cuda()
     seg = P.empty_segments(ids_d, len(RANKS))
+    seg_ref, srt_ref = oracle_segments(ids, len(RANKS))
 
     def chain():
         for i, d in enumerate(dev):
@@ -66,9 +71,12 @@ def test_decoder_layer_chain_in_one_graph(act_bf16):
         for d in dev:
             d["y"].fill_(0.0)          # eager work between the replays
         seg.seg_indptr.fill_(-7)
+        seg.sorted_tok.fill_(-7)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         for i, d in enumerate(dev):
             assert torch.equal(d["y"].view(torch.int16), eager[i]), f"replay {rep}, projection {PROJ[i][0]}"
         assert all(P.workspace_status(d["ws"]) == 0 for d in dev)
+        assert np.array_equal(seg.seg_indptr.cpu().numpy(), seg_ref)
+        assert np.array_equal(seg.sorted_tok.cpu().numpy(), srt_ref)

@@ -10,7 +10,8 @@ import numpy as np
 import pytest
 
 import workloads
-from gpu_util import (assert_t_close, assert_y_close, errors, named, named_oracle, run_gpu, run_oracle)
+from gpu_util import (assert_t_close, assert_y_close, errors, named, named_oracle, run_gpu, run_oracle,
+                      sample_rows)
 from oracle.mxquant import quantize_mxfp8
 from oracle.segments import build_segments as oracle_segments
 
@@ -20,9 +21,8 @@ NAMES = ["tiny", "decode_qkv", "decode_gateup", "prefill", "downproj_fp4"]
 
 
 def _rows_for(name):
-    if name == "prefill":  # oracle on a sample of rows: every row of y depends only on its own token
-        rng = np.random.default_rng(7)
-        return tuple(sorted(rng.choice(4096, 192, replace=False).tolist()))
+    if name == "prefill":  # oracle on 192 random rows plus the first and last row of every segment
+        return sample_rows(named(name), 192, 7)
     return None
 
 
@@ -38,6 +38,10 @@ def test_layer_matches_oracle(name, fused):
     seg_ref, srt_ref = oracle_segments(wl.ids, wl.n_adapters)
     assert np.array_equal(g["seg_indptr"], seg_ref) and np.array_equal(g["sorted_tok"], srt_ref)
     sel = slice(None) if rows is None else np.asarray(rows)
+    if rows is not None:  # the sample holds both ends of every segment (adapter 0's rows 0 .. 3 among them)
+        for a in range(wl.n_adapters):
+            where = np.flatnonzero(np.asarray(wl.ids) == a)
+            assert where[0] in rows and where[-1] in rows
     m, f = assert_y_close(g["y"][sel], ref["y"], name)
     tf = assert_t_close(g["t"][sel].astype(np.float64), ref["t"], name)
     print(f"  y max_rel={m:.2e} frob={f:.2e} t frob={tf:.2e}", flush=True)

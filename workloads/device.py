@@ -1,7 +1,7 @@
 """Upload a generated workload to the device in the library's storage layouts.
 
-Layout only (no arithmetic): A_a^T [r_a, K] and B_a^T [N, r_a] are transposed copies of
-the drawn A_a [K, r_a] and B_a [r_a, N]; x is the bf16 tensor of the drawn bits; W is
+Layout only (no arithmetic): x is the bf16 tensor of the drawn bits; the drawn A_a [K, r_a]
+and B_a [r_a, N] go up as they are and the library packs them (lora_pack_adapter); W is
 reordered into the packed form by the library's lora_pack_weight.
 """
 
@@ -23,8 +23,8 @@ def upload(wl, device="cuda"):
     q = torch.from_numpy(np.ascontiguousarray(wl.w_q)).to(device)
     s = torch.from_numpy(np.ascontiguousarray(wl.w_scale)).to(device)
     w = pack_weight(LowpWeight(wl.fmt, q, s))  # offline re-layout for the GEMM
-    At = [bf16_tensor(np.ascontiguousarray(a.T), device) for a in wl.A]
-    Bt = [bf16_tensor(np.ascontiguousarray(b.T), device) for b in wl.B]
-    ad = Adapters(At, Bt, torch.from_numpy(np.asarray(wl.scale, np.float32)).to(device))
+    A = [bf16_tensor(a, device) for a in wl.A]
+    B = [bf16_tensor(b, device) for b in wl.B]
+    ad = Adapters(A, B, torch.from_numpy(np.asarray(wl.scale, np.float32)).to(device))
     ids = torch.from_numpy(np.asarray(wl.ids, np.int32)).to(device)
     return x, w, ad, ids
