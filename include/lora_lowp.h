@@ -105,8 +105,13 @@ enum {
   LORA_ERR_INVALID_ARG = 1,   /* bad pointer, size, alignment or format        */
   LORA_ERR_UNSUPPORTED = 2,   /* valid but outside the limits listed above      */
   LORA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required     */
-  LORA_ERR_HIP = 5            /* a HIP launch or query failed                   */
+  LORA_ERR_HIP = 5,           /* a HIP launch or query failed                   */
+  LORA_ERR_SCRATCH_LIMIT = 6  /* gemm_lowp_lora_epilogue_noalloc: the sizes need more
+                                 scratch than LORA_NOALLOC_SCRATCH_BYTES           */
 };
+
+/* Scratch memory of gemm_lowp_lora_epilogue_noalloc, per GPU (bytes). */
+#define LORA_NOALLOC_SCRATCH_BYTES (32u << 20)
 
 enum { LORA_W_FP8_E4M3 = 0, LORA_W_MXFP4_E2M1 = 1 };
 
@@ -230,6 +235,30 @@ lora_status gemm_lowp_lora_epilogue(const uint16_t* x, int32_t T, int32_t K, int
                                     int32_t n_adapters, int32_t r_max,
                                     uint16_t* y, uint32_t flags,
                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* gemm_lowp_lora_epilogue for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same call with
+ * the same arguments and results, minus the workspace.  Its scratch memory is a
+ * library-owned device array of LORA_NOALLOC_SCRATCH_BYTES per GPU (32 MiB, held until
+ * the process ends); the call allocates nothing and calls no allocating routine.
+ *  - Sizes whose lora_workspace_bytes exceed LORA_NOALLOC_SCRATCH_BYTES return
+ *    LORA_ERR_SCRATCH_LIMIT and enqueue nothing (every shape of the pages' workloads
+ *    fits: the 4096-token prefill needs 18.5 MiB).
+ *  - All calls on one GPU share its array: calls on one GPU must be ordered on one
+ *    stream (calls that overlap in time on one GPU race).  The first call on a GPU, and
+ *    a call whose sizes lay the array out differently from the previous call's on that
+ *    GPU, also enqueue a fill kernel that clears the array's hand-over tags.
+ *  - The device status word and the in-launch segment builder's error word live in the
+ *    array and are not reported; callers that need the error word build the segments
+ *    with lora_build_segments. */
+lora_status gemm_lowp_lora_epilogue_noalloc(const uint16_t* x, int32_t T, int32_t K, int32_t N,
+                                            int32_t w_fmt, const uint8_t* w_q, const void* w_scale,
+                                            float* t, const int32_t* adapter_id,
+                                            int32_t* seg_indptr, int32_t* sorted_tok,
+                                            const uint64_t* A_ptrs, const uint64_t* B_ptrs,
+                                            const int32_t* ranks, const float* scales,
+                                            int32_t n_adapters, int32_t r_max,
+                                            uint16_t* y, uint32_t flags, void* stream);
 
 /* Device-side status word of the layer calls on this workspace since it was last
  * initialised (bits accumulate): copies one int32 to *status_dev (device pointer) on

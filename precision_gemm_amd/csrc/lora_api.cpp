@@ -148,6 +148,8 @@ const char* lora_status_string(lora_status s) {
     case LORA_ERR_UNSUPPORTED: return "unsupported size (see the limits in lora_lowp.h)";
     case LORA_ERR_WORKSPACE: return "workspace missing or too small";
     case LORA_ERR_HIP: return "HIP launch or runtime error";
+    case LORA_ERR_SCRATCH_LIMIT:
+      return "sizes need more than the 32 MiB of scratch memory of gemm_lowp_lora_epilogue_noalloc";
     default: return "unknown status";
   }
 }
@@ -240,12 +242,17 @@ lora_status lora_expand(const float* t, int32_t T, int32_t N, const int32_t* ada
   return launch_expand(p, as_stream(stream)) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
-lora_status gemm_lowp_lora_epilogue(const uint16_t* x, int32_t T, int32_t K, int32_t N, int32_t w_fmt,
-                                    const uint8_t* w_q, const void* w_scale, float* t, const int32_t* adapter_id,
-                                    int32_t* seg_indptr, int32_t* sorted_tok, const uint64_t* A_ptrs,
-                                    const uint64_t* B_ptrs, const int32_t* ranks, const float* scales,
-                                    int32_t n_adapters, int32_t r_max, uint16_t* y, uint32_t flags,
-                                    void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The layer call.  noalloc: the workspace is this device's scratch array, acquired here
+// once every argument has passed its checks (workspace and workspace_bytes are ignored).
+lora_status layer_call(const uint16_t* x, int32_t T, int32_t K, int32_t N, int32_t w_fmt, const uint8_t* w_q,
+                       const void* w_scale, float* t, const int32_t* adapter_id, int32_t* seg_indptr,
+                       int32_t* sorted_tok, const uint64_t* A_ptrs, const uint64_t* B_ptrs, const int32_t* ranks,
+                       const float* scales, int32_t n_adapters, int32_t r_max, uint16_t* y, uint32_t flags,
+                       void* workspace, size_t workspace_bytes, void* stream, bool noalloc) {
   lora_status st = check_sizes(T, K, N);
   if (st != LORA_OK) return st;
   if ((st = check_adapters(n_adapters, r_max)) != LORA_OK) return st;
@@ -255,6 +262,23 @@ lora_status gemm_lowp_lora_epilogue(const uint16_t* x, int32_t T, int32_t K, int
   if (build && !(flags & LORA_FUSE_SHRINK)) return LORA_ERR_INVALID_ARG;
   const bool a16 = (flags & LORA_ACT_BF16) != 0;
   if (build && (!seg_indptr || !adapter_id || (T > 0 && !sorted_tok))) return LORA_ERR_INVALID_ARG;
+  if (noalloc) {
+    // every argument that can be checked before touching the device, then the scratch
+    const LayerPlan pl0 = make_plan(std::max(T, 1), K, N, n_adapters, r_max, w_fmt, true, a16);
+    if (pl0.total > SCRATCH_BYTES) return LORA_ERR_SCRATCH_LIMIT;
+    if (T > 0) {
+      if (!x || !w_q || !w_scale || !y) return LORA_ERR_INVALID_ARG;
+      if (!aligned16(x) || !aligned16(w_q) || !aligned16(y)) return LORA_ERR_INVALID_ARG;
+      const bool lora0 = (flags & LORA_FUSE_SHRINK) != 0 || t != nullptr;
+      if (lora0 && (!adapter_id || !B_ptrs || !ranks || !scales)) return LORA_ERR_INVALID_ARG;
+      if ((flags & LORA_FUSE_SHRINK) && (!seg_indptr || !sorted_tok || !A_ptrs)) return LORA_ERR_INVALID_ARG;
+      if (t && !aligned16(t)) return LORA_ERR_INVALID_ARG;
+    } else if (!build) {
+      return LORA_OK;
+    }
+    if (scratch_acquire(as_stream(stream), pl0.off_ttag, pl0.off_gpart, &workspace) != hipSuccess) return LORA_ERR_HIP;
+    workspace_bytes = SCRATCH_BYTES;
+  }
   if (T == 0) {
     if (!build) return LORA_OK;
     // an empty batch still has its (all-zero) segment offsets
@@ -341,6 +365,30 @@ lora_status gemm_lowp_lora_epilogue(const uint16_t* x, int32_t T, int32_t K, int
   gp.seg_build = build_in ? seg_indptr : nullptr;
   gp.sorted_build = build_in ? sorted_tok : nullptr;
   return launch_layer(pl, s, sp, gp) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+lora_status gemm_lowp_lora_epilogue(const uint16_t* x, int32_t T, int32_t K, int32_t N, int32_t w_fmt,
+                                    const uint8_t* w_q, const void* w_scale, float* t, const int32_t* adapter_id,
+                                    int32_t* seg_indptr, int32_t* sorted_tok, const uint64_t* A_ptrs,
+                                    const uint64_t* B_ptrs, const int32_t* ranks, const float* scales,
+                                    int32_t n_adapters, int32_t r_max, uint16_t* y, uint32_t flags,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  return layer_call(x, T, K, N, w_fmt, w_q, w_scale, t, adapter_id, seg_indptr, sorted_tok, A_ptrs, B_ptrs, ranks,
+                    scales, n_adapters, r_max, y, flags, workspace, workspace_bytes, stream, false);
+}
+
+lora_status gemm_lowp_lora_epilogue_noalloc(const uint16_t* x, int32_t T, int32_t K, int32_t N, int32_t w_fmt,
+                                            const uint8_t* w_q, const void* w_scale, float* t,
+                                            const int32_t* adapter_id, int32_t* seg_indptr, int32_t* sorted_tok,
+                                            const uint64_t* A_ptrs, const uint64_t* B_ptrs, const int32_t* ranks,
+                                            const float* scales, int32_t n_adapters, int32_t r_max, uint16_t* y,
+                                            uint32_t flags, void* stream) {
+  return layer_call(x, T, K, N, w_fmt, w_q, w_scale, t, adapter_id, seg_indptr, sorted_tok, A_ptrs, B_ptrs, ranks,
+                    scales, n_adapters, r_max, y, flags, nullptr, 0, stream, true);
 }
 
 lora_status lora_pack_weight(int32_t w_fmt, const uint8_t* q, const uint8_t* scale, int32_t N, int32_t K,

@@ -26,6 +26,8 @@
 // safe because every workgroup has read E before being counted.  A workgroup only ever
 // waits for workgroups with lower ids, and the hardware dispatches workgroups in id
 // order, so waits cannot deadlock; every wait is bounded and reports a status on expiry.
+#include <mutex>
+
 #include "device_common.hpp"
 #include "lora_kernels.hpp"
 
@@ -2048,6 +2050,51 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
   const int grid = (int)std::min<size_t>((words + 255) / 256, 4096);
   hipLaunchKernelGGL(k_fill_zero, dim3(grid), dim3(256), 0, s, reinterpret_cast<uint32_t*>(p), words);
   return hipGetLastError();
+}
+
+// ======================================================================================
+// Scratch memory of the allocation-free layer call (gemm_lowp_lora_epilogue_noalloc):
+// a file-scope device array, one copy per GPU, held until the process ends.  In host code
+// `scratch` names a host-side stand-in, so the kernels only ever get the device address
+// that hipGetSymbolAddress returns for the current device (looked up once per device).
+// ======================================================================================
+static __device__ __align__(256) uint8_t scratch[SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+struct ScratchState {
+  void* ptr = nullptr;               // device address of this device's copy
+  size_t tag_lo = 0, tag_hi = 0;     // tagged hand-over area of the last call's layout
+};
+ScratchState g_scratch[MAX_DEVICES];
+}  // namespace
+
+hipError_t scratch_acquire(hipStream_t s, size_t tag_lo, size_t tag_hi, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ScratchState& st = g_scratch[dev];
+  if (!st.ptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    // first use on this device: the whole array starts at zero (control block, tags)
+    e = launch_fill_zero(p, SCRATCH_BYTES, s);
+    if (e != hipSuccess) return e;
+    st.ptr = p;
+  } else if (tag_lo != st.tag_lo || tag_hi != st.tag_hi) {
+    // another layout: its tagged area may hold bytes of other buffers of the last layout,
+    // which must not pass for tags of a later launch
+    e = launch_fill_zero(reinterpret_cast<char*>(st.ptr) + tag_lo, tag_hi - tag_lo, s);
+    if (e != hipSuccess) return e;
+  }
+  st.tag_lo = tag_lo;
+  st.tag_hi = tag_hi;
+  *out = st.ptr;
+  return hipSuccess;
 }
 
 }  // namespace lora

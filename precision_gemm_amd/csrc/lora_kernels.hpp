@@ -126,6 +126,12 @@ hipError_t launch_layer(const LayerPlan& pl, hipStream_t stream, const ShrinkPar
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_pack_weight(int fmt, const uint8_t* q, const uint8_t* sc, int N, int K, uint8_t* qp, uint8_t* scp,
                               hipStream_t s);
+// Allocation-free layer call: bytes of the per-device scratch array, and its device
+// address on the current device (looked up on first use, when the array is also
+// zero-filled on `s`; the tagged hand-over area [tag_lo, tag_hi) is zero-filled again on
+// `s` whenever it differs from the previous call's on this device).
+constexpr size_t SCRATCH_BYTES = (size_t)LORA_NOALLOC_SCRATCH_BYTES;
+hipError_t scratch_acquire(hipStream_t s, size_t tag_lo, size_t tag_hi, void** out);
 hipError_t launch_pack_adapter(const uint16_t* A, const uint16_t* B, int K, int N, int r, uint16_t* At, uint16_t* Bt,
                                hipStream_t s);
 

@@ -262,3 +262,31 @@ def gemm_lowp_lora_epilogue(x: torch.Tensor, w: LowpWeight, seg: Segments | None
         g(ad, "A_ptrs"), g(ad, "B_ptrs"), g(ad, "ranks"), g(ad, "scales"), n, rm,
         _ptr(y), flags, _ptr(ws), ws.numel(), _stream()))
     return y
+
+
+def gemm_lowp_lora_epilogue_noalloc(x: torch.Tensor, w: LowpWeight, seg: Segments | None, ad: Adapters | None, *,
+                                    t: torch.Tensor | None = None, fuse_shrink: bool = True,
+                                    y: torch.Tensor | None = None, n_adapters: int | None = None,
+                                    r_max: int | None = None, build_segments: bool = False,
+                                    act_bf16: bool = False) -> torch.Tensor:
+    """:func:`gemm_lowp_lora_epilogue` without a workspace: the library's per-GPU scratch
+    array serves instead (gemm_lowp_lora_epilogue_noalloc).  ``y`` (and ``t``) may be
+    passed in, so that the call itself allocates nothing."""
+    _dev(x, "x", torch.bfloat16)
+    if not w.packed:
+        raise ValueError("the GEMM reads W in the packed form: call pack_weight(w) once first")
+    T, K = x.shape
+    N = w.N
+    if y is None:
+        y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    n = ad.n if ad is not None else (n_adapters or 1)
+    rm = ad.r_max if ad is not None else (r_max or 8)
+    flags = ((LORA_FUSE_SHRINK if fuse_shrink else 0) | (LORA_BUILD_SEGMENTS if build_segments else 0)
+             | (LORA_ACT_BF16 if act_bf16 else 0))
+    g = lambda o, name: _ptr(getattr(o, name)) if o is not None else _ptr(None)  # noqa: E731
+    check("gemm_lowp_lora_epilogue_noalloc", lib().gemm_lowp_lora_epilogue_noalloc(
+        _ptr(x), T, K, N, _FMT[w.fmt], _ptr(w.q), _ptr(w.scale), _ptr(t),
+        g(seg, "adapter_id"), g(seg, "seg_indptr"), g(seg, "sorted_tok"),
+        g(ad, "A_ptrs"), g(ad, "B_ptrs"), g(ad, "ranks"), g(ad, "scales"), n, rm,
+        _ptr(y), flags, _stream()))
+    return y

@@ -182,3 +182,32 @@ def test_status_of_every_unsupported_shape_and_rank(L):
 def test_rank_pad_matches_header():
     import precision_gemm_amd as P
     assert [P.rank_pad(r) for r in (1, 4, 7, 8, 9, 12, 20, 60, 64)] == [8, 8, 8, 8, 16, 16, 24, 64, 64]
+
+
+def _noalloc(L, **kw):
+    a = dict(x=FAKE, T=16, K=4096, N=6144, fmt=0, wq=FAKE, ws=FAKE, t=NULL, ids=FAKE, seg=FAKE, srt=FAKE,
+             A=FAKE, B=FAKE, rk=FAKE, sc=FAKE, n=1, r=16, y=FAKE, flags=1, stream=NULL)
+    a.update(kw)
+    return L.gemm_lowp_lora_epilogue_noalloc(a["x"], a["T"], a["K"], a["N"], a["fmt"], a["wq"], a["ws"], a["t"],
+                                             a["ids"], a["seg"], a["srt"], a["A"], a["B"], a["rk"], a["sc"], a["n"],
+                                             a["r"], a["y"], a["flags"], a["stream"])
+
+
+def test_noalloc_checks_before_touching_the_device(L):
+    """The allocation-free call rejects sizes whose workspace exceeds its 32 MiB scratch, and
+    every bad argument, on the host before its scratch is looked up."""
+    SCRATCH_LIMIT = 6
+    assert L.lora_workspace_bytes(8192, 8192, 8192, 8, 64) > (32 << 20)
+    assert _noalloc(L, T=8192, K=8192, N=8192, n=8, r=64) == SCRATCH_LIMIT
+    assert _noalloc(L, T=8192, K=8192, N=8192, n=8, r=64, flags=3) == SCRATCH_LIMIT
+    assert L.lora_workspace_bytes(4096, 4096, 4096, 8, 64) <= (32 << 20)     # the prefill workload fits
+    assert _noalloc(L, T=-1) == INVALID
+    assert _noalloc(L, K=4000) == UNSUPPORTED
+    assert _noalloc(L, r=65) == UNSUPPORTED
+    assert _noalloc(L, flags=8) == INVALID
+    assert _noalloc(L, flags=2) == INVALID
+    assert _noalloc(L, T=0) == LORA_OK
+    assert _noalloc(L, x=NULL) == INVALID
+    assert _noalloc(L, y=MISALIGNED) == INVALID
+    assert _noalloc(L, A=NULL) == INVALID
+    assert L.lora_status_string(SCRATCH_LIMIT).startswith(b"sizes need more")
