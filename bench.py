@@ -6,9 +6,11 @@
 one segment build; see ``decoder_layer``.)
 
 A step is one pass of the whole hot path over one batch: one fused layer call
-(gemm_lowp_lora_epilogue with LORA_FUSE_SHRINK | LORA_BUILD_SEGMENTS: the segment builder,
-the down-projection and the GEMM with its LoRA epilogue in one launch; above 16 tokens
-also the MXFP8 pre-pass launch), from bf16 x and adapter ids to bf16 y.  The K timed steps are captured in one HIP graph and replayed once,
+(gemm_lowp_lora_epilogue with LORA_FUSE_SHRINK: the down-projection and the GEMM with its
+LoRA epilogue, above 16 tokens after the MXFP8 pre-pass launch, which above 128 tokens also
+runs the down-projection), from bf16 x to bf16 y, on a batch whose segments are built (one
+build serves every LoRA layer of a step).  The builder alone and the call that builds the
+segments too (LORA_BUILD_SEGMENTS) are timed beside it.  The K timed steps are captured in one HIP graph and replayed once,
 bracketed by torch.cuda.synchronize(); inputs are resident in HBM.  Steps rotate over S
 copies of the inputs so that the weights are read from HBM rather than from the 256 MB
 Infinity Cache.  ``--act bf16`` times the 16-bit activation variant (LORA_ACT_BF16: x
@@ -18,9 +20,8 @@ The default workload is the largest single-GPU configuration, the 4096-token mul
 prefill (T = K = N = 4096, FP8 W, 8 adapters of rank 64).
 
 Printed: one JSON line with the metric, the roofline of the layer call (algorithmic bytes
-or FLOPs per call over the average duration of the whole call -- segment builder, MXFP8
-pre-pass and fused layer kernel -- timed with HIP events around a graph of K calls on the
-launch stream; the layer kernel alone is reported beside it as ``kernel_only``) and the
+or FLOPs per call over the average duration of the whole call -- MXFP8 pre-pass and layer
+kernel -- timed with HIP events around a graph of K calls on the launch stream) and the
 oracle's CPU time on a bounded sample (``cpu_baseline``).
 """
 
@@ -240,25 +241,27 @@ def main():
         S.append(dict(x=x, w=w, ad=ad, ids=ids, ws=ws, y=y, seg=seg))
     torch.cuda.synchronize()
 
+    # The timed unit is the layer call on a batch whose segments are built: in a serving
+    # engine one segment build serves every LoRA layer of a step.  The builder is timed on its
+    # own, and the call that also builds the segments (LORA_BUILD_SEGMENTS, as the first LoRA
+    # layer of a batch runs it) is reported beside it as "all in".
+    for d in S:
+        P.build_segments(d["ids"], d["ad"].n, out=d["seg"])
+    torch.cuda.synchronize()
+
     def step(s):
+        d = S[s % sets]
+        P.gemm_lowp_lora_epilogue(d["x"], d["w"], d["seg"], d["ad"], d["ws"], fuse_shrink=True, y=d["y"],
+                                  act_bf16=a16)
+
+    def step_all_in(s):
         d = S[s % sets]
         P.gemm_lowp_lora_epilogue(d["x"], d["w"], d["seg"], d["ad"], d["ws"], fuse_shrink=True, y=d["y"],
                                   build_segments=True, act_bf16=a16)
 
-    # The layer kernel as the step launches it: up to 128 tokens the segment builder is a
-    # workgroup of that launch; above, the call launches the builder first, and the layer
-    # kernel alone is the call without the flag (the segments are built by then).
-    in_launch = wl.T <= 128
-    # (the 16-bit activation variant has no MXFP8 pre-pass)
-    xq_pass = (not a16) and bool(P.plan_info(wl.T, wl.K, wl.N, S[0]["ad"].n, S[0]["ad"].r_max, wl.fmt)["XQ"])
-
-    def layer_call(s):
+    def builder(s):
         d = S[s % sets]
-        P.gemm_lowp_lora_epilogue(d["x"], d["w"], d["seg"], d["ad"], d["ws"], fuse_shrink=True, y=d["y"],
-                                  build_segments=in_launch, act_bf16=a16)
-
-    def quant_call(s):  # the MXFP8 pre-pass that the call runs before the layer kernel
-        P.quant_act_mxfp8(S[s % sets]["x"])
+        P.build_segments(d["ids"], d["ad"].n, out=d["seg"])
 
     # parity of the benchmarked call against the oracle (whole layer for decode shapes)
     step(0)
@@ -299,28 +302,24 @@ def main():
             step(i)
         torch.cuda.synchronize()
         total_s = time.perf_counter() - t0
-        layer_us = quant_us = call_us = None
+        call_us = all_in_us = builder_us = None
     else:
         # K whole steps in one graph, timed from the host
         g_all = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g_all):
             for i in range(K):
                 step(i)
-        # K layer calls, timed with events on the launch stream: the layer kernel's
-        # duration including its launch gap (with the pre-pass where the plan has one,
-        # whose own graph below is subtracted)
-        g_layer = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g_layer):
+        # the same with the segments built in the call, and the builder alone
+        g_allin = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_allin):
             for i in range(K):
-                layer_call(i)
-        g_quant = None
-        if xq_pass:
-            g_quant = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g_quant):
-                for i in range(K):
-                    quant_call(i)
+                step_all_in(i)
+        g_build = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_build):
+            for i in range(K):
+                builder(i)
         g_all.replay()
-        g_layer.replay()
+        g_allin.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         g_all.replay()
@@ -337,10 +336,9 @@ def main():
             torch.cuda.synchronize()
             return e0.elapsed_time(e1) * 1e3 / K
 
-        call_us = event_us(g_all)      # the whole layer call: builder, pre-pass and layer kernel
-        layer_us = event_us(g_layer)
-        quant_us = event_us(g_quant) if g_quant is not None else 0.0
-        layer_us -= quant_us            # the layer kernel alone
+        call_us = event_us(g_all)        # the whole layer call: its pre-pass (if any) and layer kernel
+        all_in_us = event_us(g_allin)    # the same, building the segments too
+        builder_us = event_us(g_build)   # the segment builder alone
     # every workspace must report a clean status
     status = max(P.workspace_status(d["ws"]) for d in S)
 
@@ -358,15 +356,16 @@ def main():
     sha = kernel_source_sha()
     tag = args.workload + ("_act_bf16" if a16 else "")
     roof["traffic"] = stored_traffic(tag, sha)
-    roof["kernel"] = ("layer call: k_layer (fused down-projection + bf16-MFMA GEMM on widened W + LoRA epilogue)"
-                      if a16 else "layer call: segment builder + MXFP8 pre-pass (above 16 tokens) + k_layer (fused "
-                      "down-projection + scaled-MFMA GEMM + LoRA epilogue)")
+    roof["kernel"] = ("layer call: k_layer (down-projection + bf16-MFMA GEMM on widened W + LoRA epilogue)"
+                      if a16 else "layer call: MXFP8 pre-pass above 16 tokens (with the down-projection above 128 "
+                      "tokens) + k_layer (scaled-MFMA GEMM + LoRA epilogue; down-projection in the same launch up "
+                      "to 128 tokens)")
     roof["per_call_bytes"] = nbytes
     roof["per_call_flops"] = flops
     roof["call_us"] = dom_us
-    if layer_us is not None:
-        roof["kernel_only"] = {"kernel": "k_layer alone", "kernel_us": layer_us, "achieved": rate(layer_us),
-                               "frac": rate(layer_us) / peak}
+    if all_in_us is not None:
+        roof["all_in"] = {"what": "the call also builds the segments (LORA_BUILD_SEGMENTS)", "us": all_in_us,
+                          "achieved": rate(all_in_us), "frac": rate(all_in_us) / peak}
 
     out = {
         "metric": METRIC,
@@ -386,8 +385,8 @@ def main():
                    "ranks": sorted(set(int(r) for r in wl.ranks)), "seed": wl.seed, "input_sets": sets,
                    "timing": "eager" if args.eager else "hip graph of K steps"},
         "roofline": roof,
-        "layer_us": layer_us,
-        "prepass_us": quant_us,
+        "all_in_us": all_in_us,
+        "builder_us": builder_us,
         "tbps": nbytes / (dom_us * 1e-6) / 1e12,
         "tflops": flops / (dom_us * 1e-6) / 1e12,
         "parity": parity,

@@ -41,11 +41,12 @@
  * A [K, r] and B [r, N] in any layout the caller likes, K a multiple of the MX block
  * of 32), and why:
  *  - Adapters are read in a packed form made once by lora_pack_adapter from A [K][r]
- *    and B [r][N] row-major: A^T [rank_pad(r)][K] and B^T [N][rank_pad(r)], with
- *    rank_pad(r) = r rounded up to a multiple of 8.  Both adapter products then read
- *    16-byte runs along their reduction dimension straight into bf16 MFMA operands,
- *    and any rank keeps those runs aligned.  Like the quantisation of W, this is an
- *    offline step per adapter, not per call.
+ *    and B [r][N] row-major (below): A in bf16 MFMA operand order, B as B^T
+ *    [N][rank_pad(r)].  Both adapter products then read 16-byte runs along their
+ *    reduction dimension straight into bf16 MFMA operands (for A, each wave's load of a
+ *    rank tile reads 1 KB of consecutive memory), and any rank keeps those runs aligned.
+ *    Like the quantisation of W, this is an offline step per adapter, not per call;
+ *    it needs K % 64 == 0.
  *  - W is read in the packed form made once by lora_pack_weight (below): each 16-byte
  *    load of the GEMM then reads 1 KB of consecutive memory.
  *  - K % 128 == 0 instead of K % 32: the scaled MFMA takes 128 values of K per step;
@@ -67,11 +68,15 @@
  *      MXFP4: [N/16][K/128][l][16 B]: 32 codes of channel 16*nt + l%16 at
  *             k = 128*ks + 32*(l/16) .., and scales [N/16][K/128][l] (one byte:
  *             the code of k-block 4*ks + l/16).
- *  - Adapter a (packed by lora_pack_adapter): A_a [K][r_a] is stored as A_a^T, bf16
- *    [rank_pad(r_a)][K] (K contiguous), and B_a [r_a][N] as B_a^T, bf16
- *    [N][rank_pad(r_a)] (ranks contiguous) -- the weights of the linear maps
- *    K -> r_a and r_a -> N in out-by-in order.  Rows of A_a^T and columns of B_a^T
- *    at index >= r_a are padding: lora_pack_adapter zero-fills them, and the kernels
+ *  - Adapter a (packed by lora_pack_adapter), as the weights of the linear maps
+ *    K -> r_a and r_a -> N in out-by-in order:
+ *      A: ceil(r_a/16) rank tiles of 16, each [K/64][h = 0,1][l = 0..63][8] bf16 --
+ *         the 8 values of lane l = 16 g + i hold A_a[k][16 jt + i] for
+ *         k = 64 ks + 16 g + 8 h .. + 7 (the bf16 MFMA operand of rank tile jt for
+ *         that k-step; element (j, k) at ((((j/16) (K/64) + k/64) 2 + (k/8)%2) 64 +
+ *         16 ((k/16)%4) + j%16) 8 + k%8), 16 ceil(r_a/16) K values in all;
+ *      B: B_a^T, bf16 [N][rank_pad(r_a)] (ranks contiguous).
+ *    Ranks j >= r_a are padding: lora_pack_adapter zero-fills them, and the kernels
  *    never let them reach a result.  16-byte aligned.
  *    A_ptrs / B_ptrs are device arrays of n_adapters device addresses (uint64),
  *    so adapters may live anywhere in device memory.  ranks int32 [n_adapters],
@@ -173,12 +178,12 @@ lora_status lora_pack_weight(int32_t w_fmt, const uint8_t* q, const uint8_t* sca
                              uint8_t* q_packed, uint8_t* scale_packed, void* stream);
 
 /* Pack one adapter ("Punica" README, Overview: A [H1, r] and B [r, H2]) into the form
- * the layer reads: A bf16 [K][r] row-major -> At bf16 [rank_pad(r)][K] (At[j][k] =
- * A[k][j]); B bf16 [r][N] row-major -> Bt bf16 [N][rank_pad(r)] (Bt[n][j] = B[j][n]);
- * padding rows of At and columns of Bt are zero.  rank_pad(r) = (r + 7) / 8 * 8.
- * An offline step per adapter.  1 <= r <= 64 (else LORA_ERR_UNSUPPORTED, or
- * LORA_ERR_INVALID_ARG for r < 1); At and Bt 16-byte aligned; no buffer may overlap
- * another. */
+ * the layer reads (see "Data layouts"): A bf16 [K][r] row-major -> At, 16 ceil(r/16) K
+ * bf16 in operand order; B bf16 [r][N] row-major -> Bt bf16 [N][rank_pad(r)]
+ * (Bt[n][j] = B[j][n]); padding ranks are zero.  rank_pad(r) = (r + 7) / 8 * 8.
+ * An offline step per adapter.  1 <= r <= 64 and K % 64 == 0 (else
+ * LORA_ERR_UNSUPPORTED, or LORA_ERR_INVALID_ARG for r < 1); At and Bt 16-byte aligned;
+ * no buffer may overlap another. */
 lora_status lora_pack_adapter(const uint16_t* A, const uint16_t* B, int32_t K, int32_t N, int32_t r,
                               uint16_t* At, uint16_t* Bt, void* stream);
 

@@ -131,6 +131,7 @@ LayerPlan make_plan(int T, int K, int N, int n_ad, int r_max_in, int fmt, bool f
   if (pl.ksplit > 1) off += round256((size_t)tiles * pl.ksplit * pl.WC * pl.TT * pl.CT * 256 * 4);
   pl.off_xq = off;    if (pl.XQ) off += round256((size_t)T * K);
   pl.off_xsc = off;   if (pl.XQ) off += round256((size_t)T * (K / 32) + 8);  // + 8: padding read by a partial last chunk
+  pl.off_tpl = off;   if (pl.XQ && pl.s_cfg == 1) off += round256((size_t)T * r_max * 4);
   pl.total = off;
   return pl;
 }
@@ -307,9 +308,39 @@ lora_status layer_call(const uint16_t* x, int32_t T, int32_t K, int32_t N, int32
   // (measured per step: 128 tokens x 128 adapters 190.4 us in-launch against 193.2 us;
   // 4096-token prefill 220.1 us in-launch against 218.0 us).
   const bool build_in = build && T <= 128;
+  // Long batches with an MXFP8 pre-pass: the down-projection items run in the pre-pass
+  // launch, beside the quantisation, and write t as plain fp32; the layer launch is the
+  // GEMM alone (its epilogue reads that t).  In the layer launch they would hold CUs that
+  // the GEMM tiles need (prefill: 144 workgroups for ~30 us each).
+  const bool pre_shrink = fused && pl.XQ && pl.s_cfg == 1;
+  float* t_pl = pre_shrink ? (t ? t : reinterpret_cast<float*>(ws + pl.off_tpl)) : nullptr;
   uint8_t* xq = reinterpret_cast<uint8_t*>(ws + pl.off_xq);
   uint8_t* xsc = reinterpret_cast<uint8_t*>(ws + pl.off_xsc);
-  if (build && !build_in && pl.XQ) {
+  ShrinkParams sp{};
+  auto shrink_params = [&]() {
+    sp.x = x; sp.T = T; sp.K = K;
+    sp.seg_indptr = seg_indptr; sp.sorted_tok = sorted_tok;
+    sp.A_ptrs = A_ptrs; sp.ranks = ranks; sp.n_ad = n_adapters; sp.r_max = rank_pad(r_max); sp.r_lim = r_max;
+    sp.ids = adapter_id;
+    sp.scales = scales;
+    sp.tblk = pl.s_tblk; sp.n_tblk = pl.s_ntblk; sp.n_jg = pl.s_njg; sp.jper = pl.s_jper;
+    sp.kparts = pl.s_kparts; sp.kpart_len = pl.s_kpart_len;
+    sp.compact = pl.compact ? 1 : 0;
+    sp.spin_limit = SPIN_LIMIT;
+  };
+  if (pre_shrink) {
+    // the segments first (above 128 tokens never in the layer launch), then the pre-pass
+    if (build && launch_build_segments(adapter_id, T, n_adapters, seg_indptr, sorted_tok, ctrl + CTRL_SEGERR, s) !=
+                     hipSuccess)
+      return LORA_ERR_HIP;
+    shrink_params();
+    sp.t_out = t_pl;
+    sp.t_tag = nullptr;
+    sp.t_pack = 0;
+    sp.seg_wait = 0;
+    if (launch_quant_shrink(pl, sp, x, T, K, xq, xsc, s) != hipSuccess) return LORA_ERR_HIP;
+    sp = ShrinkParams{};
+  } else if (build && !build_in && pl.XQ) {
     // the builder as a workgroup of the MXFP8 pre-pass's launch
     if (launch_quant_build(x, T, K, xq, xsc, adapter_id, n_adapters, seg_indptr, sorted_tok, ctrl + CTRL_SEGERR, s) !=
         hipSuccess)
@@ -323,22 +354,14 @@ lora_status layer_call(const uint16_t* x, int32_t T, int32_t K, int32_t N, int32
 
   uint64_t* ttag = reinterpret_cast<uint64_t*>(ws + pl.off_ttag);
 
-  ShrinkParams sp{};
-  if (fused) {
-    sp.x = x; sp.T = T; sp.K = K;
-    sp.seg_indptr = seg_indptr; sp.sorted_tok = sorted_tok;
-    sp.A_ptrs = A_ptrs; sp.ranks = ranks; sp.n_ad = n_adapters; sp.r_max = rank_pad(r_max); sp.r_lim = r_max;
-    sp.ids = adapter_id;
+  const bool in_launch = fused && !pre_shrink;  // the down-projection in the layer launch
+  if (in_launch) {
+    shrink_params();
     sp.t_out = t;  // may be null
     sp.t_tag = ttag;
     // past 16 tokens (one K-part): t goes to the epilogue as tagged bf16 pairs of s_a t
     sp.t_pack = (pl.s_kparts == 1 && T > 16 && pl.TT != 1) ? 1 : 0;
-    sp.scales = scales;
-    sp.tblk = pl.s_tblk; sp.n_tblk = pl.s_ntblk; sp.n_jg = pl.s_njg; sp.jper = pl.s_jper;
-    sp.kparts = pl.s_kparts; sp.kpart_len = pl.s_kpart_len;
     sp.seg_wait = build_in ? 1 : 0;
-    sp.compact = pl.compact ? 1 : 0;
-    sp.spin_limit = SPIN_LIMIT;
   }
   GemmParams gp{};
   gp.x = x; gp.xq = xq; gp.xsc = xsc;
@@ -346,11 +369,11 @@ lora_status layer_call(const uint16_t* x, int32_t T, int32_t K, int32_t N, int32
   gp.wq = w_q;
   gp.ws_fp8 = (w_fmt == LORA_W_FP8_E4M3) ? reinterpret_cast<const float*>(w_scale) : nullptr;
   gp.ws_fp4 = (w_fmt == LORA_W_MXFP4_E2M1) ? reinterpret_cast<const uint8_t*>(w_scale) : nullptr;
-  gp.t = fused ? nullptr : t;
-  gp.t_out = (fused && pl.s_kparts > 1) ? t : nullptr;
-  gp.t_tag = fused ? ttag : nullptr;
+  gp.t = pre_shrink ? t_pl : (fused ? nullptr : t);
+  gp.t_out = (in_launch && pl.s_kparts > 1) ? t : nullptr;
+  gp.t_tag = in_launch ? ttag : nullptr;
   gp.t_kparts = pl.s_kparts;
-  gp.t_pack = (fused && pl.s_kparts == 1 && T > 16 && pl.TT != 1) ? 1 : 0;
+  gp.t_pack = (in_launch && pl.s_kparts == 1 && T > 16 && pl.TT != 1) ? 1 : 0;
   gp.r_max = rank_pad(r_max);
   gp.r_lim = r_max;
   gp.ids = adapter_id; gp.B_ptrs = B_ptrs; gp.ranks = ranks; gp.scales = scales; gp.n_ad = n_adapters;
@@ -359,11 +382,20 @@ lora_status layer_call(const uint16_t* x, int32_t T, int32_t K, int32_t N, int32
   gp.gpart = reinterpret_cast<float*>(ws + pl.off_gpart);
   gp.gflag = reinterpret_cast<int*>(ws + pl.off_gflag);
   gp.lora = lora ? 1 : 0;
-  gp.n_shrink = fused ? pl.n_shrink_wg : 0;
+  gp.n_shrink = in_launch ? pl.n_shrink_wg : 0;
   gp.ctrl = ctrl;
   gp.spin_limit = SPIN_LIMIT;
   gp.seg_build = build_in ? seg_indptr : nullptr;
   gp.sorted_build = build_in ? sorted_tok : nullptr;
+  // Long batches: every tile walks K from the same place (tiles that share W or x blocks
+  // then read them at about the same time, from L2), in the XCD-grouped tile order.  Short
+  // batches keep the rotation: their few tiles each read W alone, spread over HBM channels.
+  const int tiles = pl.n_cb * pl.n_tb;
+  const int first_gemm = (build_in ? 1 : 0) + gp.n_shrink;
+  gp.rot = (T > 128) ? 0 : 1;
+  gp.tile_group = 0;
+  if (T > 128 && pl.ksplit == 1 && tiles % 8 == 0 && first_gemm % 8 == 0 && pl.TT != 1)
+    gp.tile_group = (pl.n_cb % 4 == 0) ? 4 : ((pl.n_cb % 2 == 0) ? 2 : 1);
   return launch_layer(pl, s, sp, gp) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
@@ -407,12 +439,12 @@ lora_status lora_pack_weight(int32_t w_fmt, const uint8_t* q, const uint8_t* sca
 lora_status lora_pack_adapter(const uint16_t* A, const uint16_t* B, int32_t K, int32_t N, int32_t r, uint16_t* At,
                               uint16_t* Bt, void* stream) {
   if (K <= 0 || N <= 0 || r < 1) return LORA_ERR_INVALID_ARG;
-  if (r > MAX_RANK) return LORA_ERR_UNSUPPORTED;
+  if (r > MAX_RANK || K % 64 != 0) return LORA_ERR_UNSUPPORTED;
   if (!A || !B || !At || !Bt || !aligned16(At) || !aligned16(Bt)) return LORA_ERR_INVALID_ARG;
   const char *a0 = reinterpret_cast<const char*>(A), *b0 = reinterpret_cast<const char*>(B);
   const char *o0 = reinterpret_cast<const char*>(At), *p0 = reinterpret_cast<const char*>(Bt);
   const size_t na = (size_t)K * r * 2, nb = (size_t)N * r * 2;
-  const size_t nat = (size_t)rank_pad(r) * K * 2, nbt = (size_t)N * rank_pad(r) * 2;
+  const size_t nat = (size_t)a_tiles(r) * 16 * K * 2, nbt = (size_t)N * rank_pad(r) * 2;
   auto overlap = [](const char* x, size_t nx, const char* y, size_t ny) { return x < y + ny && y < x + nx; };
   if (overlap(a0, na, o0, nat) || overlap(a0, na, p0, nbt) || overlap(b0, nb, o0, nat) || overlap(b0, nb, p0, nbt) ||
       overlap(o0, nat, p0, nbt))

@@ -300,19 +300,24 @@ __global__ __launch_bounds__(256) void k_pack_weight(int fmt, const uint8_t* __r
 // ======================================================================================
 // Adapter layout.  The pages state an adapter as A [K, r] and B [r, N] ("Punica" README,
 // Overview: A [H1, r], B [r, H2]), both row-major here.  The kernels read them as the
-// weights of the maps K -> r and r -> N in out-by-in order, so that both adapter products
-// read 16-byte runs along their reduction dimension: A^T [rank_pad(r)][K] and
-// B^T [N][rank_pad(r)], the padding rows / columns zero.  One thread per output element
-// (an offline step, like the packing of W).
+// weights of the maps K -> r and r -> N in out-by-in order, along their reduction
+// dimension: A^T in bf16 MFMA operand order (a_index: each 16-byte lane load of a rank
+// tile reads 1 KB of consecutive memory with the others of its wave) and B^T
+// [N][rank_pad(r)], the padding rows / columns zero.  One thread per output element (an
+// offline step, like the packing of W).
 // ======================================================================================
 __global__ __launch_bounds__(256) void k_pack_adapter(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
                                                       int K, int N, int r, uint16_t* __restrict__ At,
                                                       uint16_t* __restrict__ Bt) {
   const int r8 = rank_pad(r);
-  const long na = (long)r8 * K, total = na + (long)N * r8;
+  const long na = (long)a_tiles(r) * 16 * K, total = na + (long)N * r8;
   for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (long)gridDim.x * blockDim.x) {
     if (i < na) {
-      const int j = (int)(i / K), k = (int)(i % K);
+      // i = a_index(j, k): e = k % 8, lane = 16 g + j % 16, h, ks, jt
+      const int e = (int)(i & 7), lane = (int)((i >> 3) & 63), h = (int)((i >> 9) & 1);
+      const long q = i >> 10;
+      const int ks = (int)(q % (K >> 6)), jt = (int)(q / (K >> 6));
+      const int j = jt * 16 + (lane & 15), k = ks * 64 + 16 * (lane >> 4) + 8 * h + e;
       At[i] = (j < r) ? A[(long)k * r + j] : (uint16_t)0;
     } else {
       const long q = i - na;
@@ -447,12 +452,14 @@ __device__ __forceinline__ void shrink_item(const ShrinkParams& p, int item, cha
   const int nsteps = (k_end - k_begin) >> 6;
   float* red = reinterpret_cast<float*>(smem);  // [4 waves][TG][JP][64 lanes][4]
 
+  // A_a in operand order: the lane's 16 bytes of rank tile jt for k-step ks at
+  // a_tile_off(jt, ks, h) + 8 lane (rows past r_a are zero padding of the last tile; tiles
+  // past the item's last read that tile and feed no output)
   const uint16_t* arow[JP];
+  const int nat = a_tiles(r);
 #pragma unroll
-  for (int jt = 0; jt < JP; ++jt) {
-    const int j = j_begin + jt * 16 + li;
-    arow[jt] = A + (long)((jt < njt && j < r) ? j : 0) * p.K + k_begin + 16 * g;
-  }
+  for (int jt = 0; jt < JP; ++jt) arow[jt] = A + a_tile_off(min((j_begin >> 4) + jt, nat - 1), 0, 0, p.K) + 8 * lane;
+  const int ks0 = k_begin >> 6;  // the item's first k-step
 
   for (int t0 = tok_begin; t0 < tok_end; t0 += TG * 16) {
     const int ntt = min(TG, (tok_end - t0 + 15) >> 4);
@@ -484,8 +491,8 @@ __device__ __forceinline__ void shrink_item(const ShrinkParams& p, int item, cha
         }
 #pragma unroll
         for (int jt = 0; jt < JP; ++jt) {
-          aa[buf][u][jt][0] = ldg16(arow[jt] + k0);
-          aa[buf][u][jt][1] = ldg16(arow[jt] + k0 + 8);
+          aa[buf][u][jt][0] = ldg16(arow[jt] + a_tile_off(0, ks0 + (k0 >> 6), 0, p.K));
+          aa[buf][u][jt][1] = ldg16(arow[jt] + a_tile_off(0, ks0 + (k0 >> 6), 1, p.K));
         }
       }
     };
@@ -728,6 +735,20 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   const int ks = item % p.ksplit;
   const int tile = item / p.ksplit;
   int cb = tile % p.n_cb, tb = tile / p.n_cb;
+  if (p.tile_group > 0) {
+    // XCD-grouped order (the host sets it only without a K-split, with a multiple of 8
+    // tiles and of 8 workgroups before the first GEMM workgroup).  Workgroups are dealt to
+    // the eight XCDs in turn, so items item % 8 == x run on XCD x, in the order item / 8.
+    // XCD x takes the x-th eighth of the tiles in an order that walks groups of
+    // tile_group column blocks token block by token block: the tiles an XCD runs at one
+    // time then share a few W column blocks and a few x row blocks in its L2.
+    const int per = (p.n_cb * p.n_tb) >> 3;
+    const int L = (item & 7) * per + (item >> 3);
+    const int G = p.tile_group, gsz = G * p.n_tb;
+    const int grp = L / gsz, r = L - grp * gsz;
+    tb = r / G;
+    cb = grp * G + (r - (r / G) * G);
+  }
   if (TT == 1 && p.n_tb > 1) {
     // several 16-token tiles per column tile (16-bit activations past 16 tokens): the tiles
     // of one column tile take item ids 8 apart, so that they run on one XCD (workgroups are
@@ -784,8 +805,8 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   const int nchunks = (ke - kb + KC - 1) / KC;
   // Every tile walks its K-range from a different place (chunk and step rotation), so that
   // the workgroups do not all hit the same HBM channels with rows that are K bytes apart.
-  const int crot = tile % nchunks;
-  const int srot = (tile * 5) & (STEPS - 1);
+  const int crot = p.rot ? tile % nchunks : 0;
+  const int srot = p.rot ? (tile * 5) & (STEPS - 1) : 0;
   auto chunk_k0 = [&](int c) { return kb + ((c + crot) % nchunks) * KC; };
 
   // register staging, two chunks ahead: x (raw bf16 or pre-quantised) and W.
@@ -993,28 +1014,33 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
         sc[0] = *reinterpret_cast<const uint32_t*>(sb);
         sc[1] = 0u;
       }
-      uint4 alo[2], ahi[2];
+      // fragments read FD token tiles ahead of their MFMAs (measured: two ahead on the
+      // 128 x 256 prefill tile, no faster, and the registers spill)
+      constexpr int FD = 1;
+      constexpr int FB = FD + 1;
+      uint4 alo[FB], ahi[FB];
       auto frag = [&](int tt) {
         const uint8_t* xp = xs + (tt * 16 + li) * ROW + sp * 128 + 16 * g;
-        alo[tt & 1] = *reinterpret_cast<const uint4*>(xp);
-        ahi[tt & 1] = *reinterpret_cast<const uint4*>(xp + 64);
+        alo[tt % FB] = *reinterpret_cast<const uint4*>(xp);
+        ahi[tt % FB] = *reinterpret_cast<const uint4*>(xp + 64);
       };
-      frag(0);
+#pragma unroll
+      for (int tt = 0; tt < FD; ++tt) frag(tt);
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) {
-        if (tt + 1 < TT) frag(tt + 1);
+        if (tt + FD < TT) frag(tt + FD);
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
-          acc[tt][ct] = mfma_scaled_16x16x128_sel<FMTB>(tt & 3, alo[tt & 1], ahi[tt & 1], wlo[buf][i][ct],
+          acc[tt][ct] = mfma_scaled_16x16x128_sel<FMTB>(tt & 3, alo[tt % FB], ahi[tt % FB], wlo[buf][i][ct],
                                                          whi[buf][i][ct], acc[tt][ct], (int)sc[tt >> 2],
                                                          wsc[buf][i][ct]);
       }
-      // keep that order: the scale and first fragment reads, then per token tile the next
-      // fragment's reads ahead of the tile's MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+      // keep that order: the scale and first FD fragments' reads, then per token tile the
+      // reads FD tiles ahead before the tile's MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 1 + 2 * FD, 0);
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) {
-        if (tt + 1 < TT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        if (tt + FD < TT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, CT, 0);
       }
     }
@@ -1810,6 +1836,92 @@ __device__ __forceinline__ void gemm_item(const GemmParams& p, int item, char* s
   }
 }
 
+// The down-projection role of a launch: workgroup b of the n_wg that take down-projection
+// items (the lowest ids of a fused layer launch, or the first workgroups of the pre-pass
+// launch).  ctrl == null: a launch without the launch epoch (the pre-pass), which writes t
+// as plain fp32 and publishes nothing.
+template <int TG, int JP, int U, bool PACK>
+__device__ __forceinline__ void shrink_role(const ShrinkParams& sp, int b, int n_wg, char* smem, int* ctrl, int e,
+                                            int* lds_epoch, int& started) {
+  bool published = false;
+  int n_valid = b + 1, stride = 1;
+  int* pre = reinterpret_cast<int*>(smem + sp.compact_off);  // [n_ad + 1] item prefix
+  if (sp.compact) {
+    // Most (adapter, token block, rank group) items can be empty: token blocks past the
+    // end of a segment, rank groups past an adapter's rank.  The workgroups take the
+    // items that have work, k = b, b + n_shrink, ..., counted per adapter from the segment
+    // lengths and ranks (prefix over the adapters, in LDS after the area the
+    // down-projection uses), so that no workgroup holds a CU the GEMM needs for nothing.
+    // Segments built in this launch are waited for first (see shrink_item).
+    const bool coh = sp.seg_wait != 0;
+    if (coh) {
+      started = wg_epoch_publish(ctrl, e, lds_epoch);
+      published = true;
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        int spins = 0;
+        while (ld_agent(ctrl + CTRL_SEGREADY) != *lds_epoch + 1) {
+          __builtin_amdgcn_s_sleep(2);
+          if (++spins > sp.spin_limit) {
+            or_agent(ctrl + CTRL_STATUS, 1);
+            break;
+          }
+        }
+      }
+      __syncthreads();
+    }
+    int* wsum = pre + sp.n_ad + 1;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    auto count = [&](int a) {
+      const int len = coh ? ld_agent(sp.seg_indptr + a + 1) - ld_agent(sp.seg_indptr + a)
+                          : sp.seg_indptr[a + 1] - sp.seg_indptr[a];
+      const int r = sp.ranks[a];
+      const bool ok = r >= 1 && r <= sp.r_lim;
+      const int nj = min(sp.n_jg, (r + 16 * JP - 1) / (16 * JP));
+      return ok ? (len + sp.tblk - 1) / sp.tblk * nj * sp.kparts : 0;
+    };
+    const int per = (sp.n_ad + 255) / 256;
+    const int lo = min(tid * per, sp.n_ad), hi = min(lo + per, sp.n_ad);
+    int cnt = 0;
+    for (int a = lo; a < hi; ++a) cnt += count(a);
+    int inc = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int u = __shfl_up(inc, off);
+      if (lane >= off) inc += u;
+    }
+    if (lane == 63) wsum[wave] = inc;
+    __syncthreads();
+    int base = inc - cnt;
+    for (int w = 0; w < wave; ++w) base += wsum[w];
+    for (int a = lo; a < hi; ++a) {
+      pre[a] = base;
+      base += count(a);
+    }
+    if (tid == 255) pre[sp.n_ad] = base;
+    __syncthreads();
+    n_valid = __builtin_amdgcn_readfirstlane(pre[sp.n_ad]);
+    stride = n_wg;
+  }
+  for (int k = b; k < n_valid; k += stride) {
+    int item = k;
+    if (sp.compact) {
+      int lo_a = 0, hi_a = sp.n_ad;  // adapter a with pre[a] <= k < pre[a + 1]
+      while (hi_a - lo_a > 1) {
+        const int mid = (lo_a + hi_a) >> 1;
+        if (__builtin_amdgcn_readfirstlane(pre[mid]) <= k) lo_a = mid; else hi_a = mid;
+      }
+      const int local = k - __builtin_amdgcn_readfirstlane(pre[lo_a]);
+      const int nj = min(sp.n_jg, (sp.ranks[lo_a] + 16 * JP - 1) / (16 * JP));
+      const int kp = local % sp.kparts, rest = local / sp.kparts;
+      const int jg = rest % nj, tb = rest / nj;
+      item = (tb < sp.n_tblk) ? ((lo_a * sp.n_tblk + tb) * sp.n_jg + jg) * sp.kparts + kp : -1;
+    }
+    if (item >= 0) shrink_item<TG, JP, U, PACK>(sp, item, smem, ctrl, e, lds_epoch, &started, published);
+  }
+  if (!published && ctrl) started = wg_epoch_publish(ctrl, e, lds_epoch);
+}
+
 // OCC: workgroups per CU the registers are budgeted for (2 for the 64-token prefill tile,
 // so that one workgroup's epilogue and start-up latency overlap another's main loop, and
 // for the one-tile stream, whose few down-projection workgroups then share CUs)
@@ -1837,89 +1949,207 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     __syncthreads();
     if (threadIdx.x == 0) set_agent(gp.ctrl + CTRL_SEGREADY, e + 1);
   } else if (b < gp.n_shrink) {
-    bool published = false;
-    int n_valid = b + 1, stride = 1;
-    int* pre = reinterpret_cast<int*>(smem + sp.compact_off);  // [n_ad + 1] item prefix
-    if (sp.compact) {
-      // Most (adapter, token block, rank group) items can be empty: token blocks past the
-      // end of a segment, rank groups past an adapter's rank.  The workgroups take the
-      // items that have work, k = b, b + n_shrink, ..., counted per adapter from the segment
-      // lengths and ranks (prefix over the adapters, in LDS after the area the
-      // down-projection uses), so that no workgroup holds a CU the GEMM needs for nothing.
-      // Segments built in this launch are waited for first (see shrink_item).
-      const bool coh = sp.seg_wait != 0;
-      if (coh) {
-        started = wg_epoch_publish(gp.ctrl, e, &lds_epoch);
-        published = true;
-        __syncthreads();
-        if (threadIdx.x == 0) {
-          int spins = 0;
-          while (ld_agent(gp.ctrl + CTRL_SEGREADY) != lds_epoch + 1) {
-            __builtin_amdgcn_s_sleep(2);
-            if (++spins > sp.spin_limit) {
-              or_agent(gp.ctrl + CTRL_STATUS, 1);
-              break;
-            }
-          }
-        }
-        __syncthreads();
-      }
-      int* wsum = pre + sp.n_ad + 1;
-      const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-      auto count = [&](int a) {
-        const int len = coh ? ld_agent(sp.seg_indptr + a + 1) - ld_agent(sp.seg_indptr + a)
-                            : sp.seg_indptr[a + 1] - sp.seg_indptr[a];
-        const int r = sp.ranks[a];
-        const bool ok = r >= 1 && r <= sp.r_lim;
-        const int nj = min(sp.n_jg, (r + 16 * JP - 1) / (16 * JP));
-        return ok ? (len + sp.tblk - 1) / sp.tblk * nj * sp.kparts : 0;
-      };
-      const int per = (sp.n_ad + 255) / 256;
-      const int lo = min(tid * per, sp.n_ad), hi = min(lo + per, sp.n_ad);
-      int cnt = 0;
-      for (int a = lo; a < hi; ++a) cnt += count(a);
-      int inc = cnt;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int u = __shfl_up(inc, off);
-        if (lane >= off) inc += u;
-      }
-      if (lane == 63) wsum[wave] = inc;
-      __syncthreads();
-      int base = inc - cnt;
-      for (int w = 0; w < wave; ++w) base += wsum[w];
-      for (int a = lo; a < hi; ++a) {
-        pre[a] = base;
-        base += count(a);
-      }
-      if (tid == 255) pre[sp.n_ad] = base;
-      __syncthreads();
-      n_valid = __builtin_amdgcn_readfirstlane(pre[sp.n_ad]);
-      stride = gp.n_shrink;
-    }
-    for (int k = b; k < n_valid; k += stride) {
-      int item = k;
-      if (sp.compact) {
-        int lo_a = 0, hi_a = sp.n_ad;  // adapter a with pre[a] <= k < pre[a + 1]
-        while (hi_a - lo_a > 1) {
-          const int mid = (lo_a + hi_a) >> 1;
-          if (__builtin_amdgcn_readfirstlane(pre[mid]) <= k) lo_a = mid; else hi_a = mid;
-        }
-        const int local = k - __builtin_amdgcn_readfirstlane(pre[lo_a]);
-        const int nj = min(sp.n_jg, (sp.ranks[lo_a] + 16 * JP - 1) / (16 * JP));
-        const int kp = local % sp.kparts, rest = local / sp.kparts;
-        const int jg = rest % nj, tb = rest / nj;
-        item = (tb < sp.n_tblk) ? ((lo_a * sp.n_tblk + tb) * sp.n_jg + jg) * sp.kparts + kp : -1;
-      }
-      if (item >= 0) shrink_item<TG, JP, U, TT != 1>(sp, item, smem, gp.ctrl, e, &lds_epoch, &started, published);
-    }
-    if (!published) started = wg_epoch_publish(gp.ctrl, e, &lds_epoch);
+    shrink_role<TG, JP, U, TT != 1>(sp, b, gp.n_shrink, smem, gp.ctrl, e, &lds_epoch, started);
   } else {
     // K-parts of t: the single-tile decode down-projection splits K
     constexpr int KPT = (TT == 1) ? 4 : 1;
     gemm_item<FMT, TT, CT, WC, WK, XQ, KPT, OCC, A16>(gp, b - gp.n_shrink, smem, e, &lds_epoch, &started);
   }
   wg_epoch_end(gp.ctrl, e, started);
+}
+
+// ======================================================================================
+// Pre-pass of a long batch whose segments are built: the MXFP8 quantisation of x and the
+// adapter down-projection in one pass over x.  Workgroup b takes the 16 positions
+// [16b, 16b + 16) of the sorted token order for the down-projection and the 16 rows
+// [16b, 16b + 16) of x for the quantisation: the same rows where segments are runs of
+// consecutive tokens (a prefill batch), so each row of x is then read from memory once for
+// both.  The four waves split K in quarters.  Per 64-wide k-step lane (i, g) holds
+// x[row i][k + 16g .. k + 16g + 15]: the operands of two bf16 MFMAs (rows x 32 k each) and
+// half of one of the row's MX blocks (the other half in lane i + 16(g ^ 1)).  Each adapter
+// present among the
+// 16 positions is one pass over the quarter: t[row][j] = sum_k x[row][k] A_a^T[j][k] on bf16
+// MFMA 16x16x32 for the ranks of a, with the rows of other adapters masked to zero (a tile
+// of a prefill batch holds one adapter, two where a segment ends; the first pass also
+// quantises).  The quarters' sums meet in LDS in wave order, so t is deterministic, and go
+// out as plain fp32 for the GEMM epilogue.  The down-projection thus still runs first, on
+// the bf16 x, fused with the quantisation the GEMM needs anyway, and holds no GEMM CU.
+// ======================================================================================
+constexpr int PREP_U = 2;       // k-steps of 64 in flight per wave
+constexpr int PREP_RS = 128 + 16;  // LDS row stride (bytes) of a wave's x slot: 16 rows x 64 bf16
+// One pass of a wave over its part of K: quantise (QUANT) and/or add x A_a^T for NJT rank
+// tiles.  The number of loads per step is a compile-time constant and no load or store sits
+// behind a branch, so the compiler's waits for step u leave the later steps' loads in
+// flight.
+//  - QUANT: the quantisation's rows p0 .. p0 + 15 are loaded row-contiguously, lane l taking
+//    16 bytes of row 8 i + l / 8 at piece l % 8 of the step (one load covers 8 whole
+//    128-byte lines); the quantiser works on those pieces (a block is a quad of lanes).
+//    Without SEP the same rows are the down-projection's, and their MFMA operand layout
+//    comes back through the wave's LDS slot.
+//  - SEP: the down-projection's rows (which differ from the quantisation's) are loaded in
+//    operand layout, lane (i, g) taking row i at 16 g .. 16 g + 15.
+template <bool QUANT, bool SEP, int NJT>
+__device__ __forceinline__ void prep_pass(uint8_t* __restrict__ xq, uint8_t* __restrict__ xsc, int K, int T, int p0,
+                                          const uint16_t* x, const uint16_t* xrow_s, char* slot, bool s_mine,
+                                          const uint16_t* arow0, int r, int kb, int nst, v4f (&acc)[4]) {
+  constexpr int U = PREP_U;
+  constexpr bool RELAY = QUANT && !SEP && NJT > 0;  // operands through the LDS slot
+  const int lane = threadIdx.x & 63, li = lane & 15, g = lane >> 4;
+  if (nst <= 0) return;
+  // A_a in operand order (tiles past r_a's last read that tile and are masked at the output;
+  // without an adapter, r == 0, the loads read x as a stand-in and feed nothing)
+  const uint16_t* arow[NJT > 0 ? NJT : 1];
+  const int nat = a_tiles(r);
+#pragma unroll
+  for (int jt = 0; jt < NJT; ++jt) arow[jt] = arow0 + a_tile_off(r > 0 ? min(jt, nat - 1) : 0, 0, 0, K) + 8 * lane;
+  // rows of the contiguous loads (clamped: lanes past the last row repeat row T - 1 and store
+  // the same bytes again) and of the operand-layout loads
+  const int crow0 = min(p0 + (lane >> 3), T - 1), crow1 = min(p0 + 8 + (lane >> 3), T - 1);
+  const uint16_t* xc0 = x + (long)crow0 * K + 8 * (lane & 7);
+  const uint16_t* xc1 = x + (long)crow1 * K + 8 * (lane & 7);
+  uint4 xr[U][2], xs[U][2], ar[U][NJT > 0 ? NJT : 1][2];
+  auto issue = [&](int u, int st) {  // the clamped step is always valid
+    const int k = kb + min(st, nst - 1) * 64;
+    if (QUANT) {
+      xr[u][0] = ldg16(xc0 + k);
+      xr[u][1] = ldg16(xc1 + k);
+    }
+    if (SEP && NJT > 0) {
+      xs[u][0] = ldg16(xrow_s + k);
+      xs[u][1] = ldg16(xrow_s + k + 8);
+    }
+#pragma unroll
+    for (int jt = 0; jt < NJT; ++jt) {
+      ar[u][jt][0] = ldg16(arow[jt] + a_tile_off(0, k >> 6, 0, K));
+      ar[u][jt][1] = ldg16(arow[jt] + a_tile_off(0, k >> 6, 1, K));
+    }
+  };
+  auto consume = [&](int u, int st) {
+    const int k = kb + st * 64;
+    uint4 xv[2] = {zero4(), zero4()};
+    if (QUANT) {
+      // a block is 32 values = the pieces of a quad of lanes; all four lanes store its code
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        uint32_t mx = absmax8_bits(xr[u][i]);
+        mx = max(mx, quad_swap1(mx));
+        mx = max(mx, quad_swap2(mx));
+        const uint32_t code = mx_code_from_bits(mx);
+        const int row = i ? crow1 : crow0;
+        *reinterpret_cast<uint2*>(xq + (long)row * K + k + 8 * (lane & 7)) = mx_piece_quant(xr[u][i], code);
+        xsc[(long)row * (K / 32) + (k >> 5) + ((lane & 7) >> 2)] = (uint8_t)code;
+        if (RELAY) *reinterpret_cast<uint4*>(slot + PREP_RS * (8 * i + (lane >> 3)) + 16 * (lane & 7)) = xr[u][i];
+      }
+    }
+    if (RELAY) {
+      xv[0] = *reinterpret_cast<const uint4*>(slot + PREP_RS * li + 32 * g);
+      xv[1] = *reinterpret_cast<const uint4*>(slot + PREP_RS * li + 32 * g + 16);
+    } else if (SEP && NJT > 0) {
+      xv[0] = xs[u][0];
+      xv[1] = xs[u][1];
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint4 xm = s_mine ? xv[h] : zero4();
+#pragma unroll
+      for (int jt = 0; jt < NJT; ++jt) acc[jt] = mfma_bf16_16x16x32(xm, ar[u][jt][h], acc[jt]);
+    }
+  };
+  // Rounds of U steps: every round but the last consumes its U slots and refills them
+  // (past the last step a refill loads that step again, never consumed); the last round only
+  // consumes.
+#pragma unroll
+  for (int u = 0; u < U; ++u) issue(u, u);
+  const int nround = (nst + U - 1) / U;
+  for (int rd = 0; rd + 1 < nround; ++rd) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      consume(u, rd * U + u);
+      issue(u, (rd + 1) * U + u);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if ((nround - 1) * U + u < nst) consume(u, (nround - 1) * U + u);
+}
+
+// NJT: rank tiles of 16 of the batch's largest rank (every adapter's pass runs them all;
+// the ranks past an adapter's own read its row 0 and are masked at the output).
+template <int NJT>
+__global__ __launch_bounds__(256) void k_prep_rows(ShrinkParams sp, uint8_t* __restrict__ xq, uint8_t* __restrict__ xsc) {
+  __shared__ __align__(16) float red[4][4][64][4];  // [wave][rank tile][lane][4]
+  __shared__ __align__(16) char xslot[4][16 * PREP_RS];  // each wave's x relayout slot
+  __shared__ int stok[16], sad[16];
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, li = lane & 15,
+            g = lane >> 4;
+  const int T = sp.T, K = sp.K;
+  // Workgroups are dealt to the eight XCDs in turn; XCD x takes the x-th eighth of the
+  // position blocks, a run of consecutive positions, so that the A_a of its one or two
+  // segments stays in its L2 (in plain order every XCD would stream every adapter's A_a)
+  const int nblk = gridDim.x, b = blockIdx.x;
+  const int blk = (nblk % 8 == 0) ? (b & 7) * (nblk >> 3) + (b >> 3) : b;
+  const int p0 = blk * 16;
+  const int n_valid = sp.seg_indptr[sp.n_ad];  // positions of tokens with a valid adapter
+  const int pos = p0 + li;
+  const bool s_ok = pos < n_valid;
+  const int tok_s = s_ok ? sp.sorted_tok[pos] : 0;
+  const int a_s = s_ok ? sp.ids[tok_s] : -1;
+  if (tid < 16) {
+    stok[tid] = tok_s;
+    sad[tid] = a_s;
+  }
+  // the down-projection's rows are the quantisation's rows (runs of consecutive tokens)
+  const bool same = __ballot(s_ok && tok_s != p0 + li) == 0ull;
+  // the wave's quarter of K, in steps of 64 (the last quarter may be shorter or empty)
+  const int kqs = ((K >> 2) + 63) & ~63;
+  const int kb = min(K, wave * kqs), nst = (min(K, kb + kqs) - kb) >> 6;
+  const uint16_t* xrow_s = sp.x + (long)tok_s * K + 16 * g;
+  v4f acc[4];
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt) acc[jt] = v4f{0.f, 0.f, 0.f, 0.f};
+  // one pass per adapter present (the first also quantises); lanes 0..15 stand for the rows
+  unsigned long long todo = __ballot(li == lane && s_ok);
+  bool first = true;
+  do {
+    int a = -1, r = 0;
+    if (todo) {
+      const int lead = __ffsll((long long)todo) - 1;
+      a = __builtin_amdgcn_readlane(a_s, lead);
+      todo &= ~__ballot(li == lane && s_ok && a_s == a);
+      r = sp.ranks[a];
+      if (r < 1 || r > sp.r_lim) r = 0;  // reported by the GEMM epilogue; no term
+    }
+    // no adapter (or an invalid rank): the rows read x's row 0 and the products are masked
+    const bool mine = a >= 0 && r > 0 && s_ok && a_s == a;
+    const uint16_t* arow0 = reinterpret_cast<const uint16_t*>(r > 0 ? sp.A_ptrs[a] : (uint64_t)sp.x);
+    char* slot = xslot[wave];
+    if (first && same)
+      prep_pass<true, false, NJT>(xq, xsc, K, T, p0, sp.x, xrow_s, slot, mine, arow0, r, kb, nst, acc);
+    else if (first)
+      prep_pass<true, true, NJT>(xq, xsc, K, T, p0, sp.x, xrow_s, slot, mine, arow0, r, kb, nst, acc);
+    else if (r > 0)
+      prep_pass<false, true, NJT>(xq, xsc, K, T, p0, sp.x, xrow_s, slot, mine, arow0, r, kb, nst, acc);
+    first = false;
+  } while (todo);
+  // the quarters' sums in wave order; wave w writes rank tile w of t (plain fp32, zero past
+  // the row's rank up to r_max)
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt) *reinterpret_cast<v4f*>(&red[wave][jt][lane][0]) = acc[jt];
+  __syncthreads();
+  if (!sp.t_out) return;
+  v4f sum = *reinterpret_cast<const v4f*>(&red[0][wave][lane][0]);
+#pragma unroll
+  for (int w = 1; w < 4; ++w) sum += *reinterpret_cast<const v4f*>(&red[w][wave][lane][0]);
+  const int j = wave * 16 + li;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int row = 4 * g + v;
+    if (p0 + row >= n_valid || j >= sp.r_lim) continue;
+    const int a = sad[row];
+    const int r = sp.ranks[a];
+    if (r < 1 || r > sp.r_lim) continue;
+    sp.t_out[(long)stok[row] * sp.r_lim + j] = (j < r) ? sum[v] : 0.f;
+  }
 }
 
 // ======================================================================================
@@ -2015,6 +2245,20 @@ hipError_t launch_quant(const uint16_t* x, int T, int K, uint8_t* xq, uint8_t* x
   return hipGetLastError();
 }
 
+hipError_t launch_quant_shrink(const LayerPlan& pl, const ShrinkParams& sp, const uint16_t* x, int T, int K,
+                               uint8_t* xq, uint8_t* xsc, hipStream_t s) {
+  (void)pl; (void)x; (void)K;
+  const dim3 grid((T + 15) / 16), block(256);
+  switch ((sp.r_lim + 15) / 16) {
+    case 1: hipLaunchKernelGGL(k_prep_rows<1>, grid, block, 0, s, sp, xq, xsc); break;
+    case 2: hipLaunchKernelGGL(k_prep_rows<2>, grid, block, 0, s, sp, xq, xsc); break;
+    case 3: hipLaunchKernelGGL(k_prep_rows<3>, grid, block, 0, s, sp, xq, xsc); break;
+    case 4: hipLaunchKernelGGL(k_prep_rows<4>, grid, block, 0, s, sp, xq, xsc); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_build(const uint16_t* x, int T, int K, uint8_t* xq, uint8_t* xsc, const int* ids, int n_ad,
                               int* seg, int* sorted, int* err, hipStream_t s) {
   const long blocks = ((long)T * (K / 8) + SEG_THREADS - 1) / SEG_THREADS;
@@ -2038,7 +2282,7 @@ hipError_t launch_pack_weight(int fmt, const uint8_t* q, const uint8_t* sc, int 
 
 hipError_t launch_pack_adapter(const uint16_t* A, const uint16_t* B, int K, int N, int r, uint16_t* At, uint16_t* Bt,
                                hipStream_t s) {
-  const long total = (long)rank_pad(r) * (K + (long)N);
+  const long total = (long)a_tiles(r) * 16 * K + (long)rank_pad(r) * N;
   const int grid = (int)std::min<long>((total + 255) / 256, 4096);
   hipLaunchKernelGGL(k_pack_adapter, dim3(grid), dim3(256), 0, s, A, B, K, N, r, At, Bt);
   return hipGetLastError();

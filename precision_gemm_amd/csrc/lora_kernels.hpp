@@ -14,10 +14,22 @@ namespace lora {
 constexpr int MAX_ADAPTERS = 8192;
 constexpr int MAX_RANK = 64;
 
-// Stored adapters are padded to a whole number of 16-byte runs of bf16: A_a^T has
-// rank_pad(r_a) rows and B_a^T rank_pad(r_a) columns (lora_pack_adapter zero-fills the
-// padding; the kernels mask it out whatever it holds).
+// Stored adapters (lora_pack_adapter; padding zero-filled, and masked out by the kernels
+// whatever it holds): B_a^T has rank_pad(r_a) columns (whole 16-byte runs of bf16); A_a is
+// stored in bf16 MFMA operand order for rank tiles of 16 (a_tiles(r_a) of them): element
+// (j, k) of A_a^T at a_index(j, k, K), so that the 16-byte lane loads of one rank tile and
+// one 64-wide k-step read 2 KB of consecutive memory (lane l = 16 g + i: rank 16 jt + i,
+// k = 64 ks + 16 g + 8 h .. + 7 for the halves h = 0, 1).
 __host__ __device__ constexpr int rank_pad(int r) { return (r + 7) & ~7; }
+__host__ __device__ constexpr int a_tiles(int r) { return (r + 15) >> 4; }
+__host__ __device__ constexpr long a_index(int j, int k, int K) {
+  return ((((long)(j >> 4) * (K >> 6) + (k >> 6)) * 2 + ((k >> 3) & 1)) * 64 + 16 * ((k >> 4) & 3) + (j & 15)) * 8 +
+         (k & 7);
+}
+// offset (elements) of rank tile jt, k-step ks (64 wide), half h, lane l
+__host__ __device__ constexpr long a_tile_off(int jt, int ks, int h, int K) {
+  return (((long)jt * (K >> 6) + ks) * 2 + h) * 512;
+}
 
 // Workspace control block (int32 words at the start of every workspace)
 enum : int {
@@ -34,7 +46,7 @@ struct ShrinkParams {
   const int* seg_indptr;
   const int* sorted_tok;
   const int* ids;          // fused launch with T <= 16: tokens found by id (may be null)
-  const uint64_t* A_ptrs;  // A_a^T, bf16 [rank_pad(r_a)][K]
+  const uint64_t* A_ptrs;  // A_a in operand order (a_index), a_tiles(r_a) rank tiles
   const int* ranks;
   int n_ad;
   int r_max;           // rank_pad of the caller's r_max: row stride of the tagged t
@@ -84,6 +96,8 @@ struct GemmParams {
   int spin_limit;
   int* seg_build;     // non-null: workgroup 0 builds seg_indptr (here) and sorted_tok from ids
   int* sorted_build;
+  int tile_group;     // > 0: XCD-grouped tile order, groups of this many column blocks
+  int rot;            // tiles start their K walk at different chunks (spreads HBM channels)
 };
 
 struct ExpandParams {
@@ -111,13 +125,17 @@ struct LayerPlan {
   int n_shrink_items;  // down-projection items (the standalone launch has one workgroup each)
   bool compact;        // fused launch: the down-projection workgroups take the items that have work
   int n_build_wg;  // 1 when the launch also builds the segments
-  // workspace layout (byte offsets)
-  size_t off_ctrl, off_ttag, off_gflag, off_gpart, off_xq, off_xsc, total;
+  // workspace layout (byte offsets); tpl: plain fp32 t of a down-projection run in the
+  // pre-pass launch
+  size_t off_ctrl, off_ttag, off_gflag, off_gpart, off_xq, off_xsc, off_tpl, total;
 };
 
 hipError_t launch_build_segments(const int* ids, int T, int n_ad, int* seg, int* sorted, int* err, hipStream_t s);
 hipError_t launch_quant(const uint16_t* x, int T, int K, uint8_t* xq, uint8_t* xsc, hipStream_t s);
 // the segment builder and the MXFP8 pre-pass in one launch (independent of each other)
+// the MXFP8 pre-pass with the down-projection items (plan with 64-token items) beside it
+hipError_t launch_quant_shrink(const LayerPlan& pl, const ShrinkParams& sp, const uint16_t* x, int T, int K, uint8_t* xq,
+                               uint8_t* xsc, hipStream_t s);
 hipError_t launch_quant_build(const uint16_t* x, int T, int K, uint8_t* xq, uint8_t* xsc, const int* ids, int n_ad,
                               int* seg, int* sorted, int* err, hipStream_t s);
 hipError_t launch_shrink(const LayerPlan& pl, hipStream_t stream, const ShrinkParams& sp);

@@ -79,13 +79,19 @@ def pack_weight(w: LowpWeight) -> LowpWeight:
 
 
 def rank_pad(r: int) -> int:
-    """Stored rank of an adapter of rank r: r rounded up to a multiple of 8."""
+    """Stored rank of B_a^T for an adapter of rank r: r rounded up to a multiple of 8."""
     return (int(r) + 7) // 8 * 8
+
+
+def a_rows(r: int) -> int:
+    """Rank rows of the packed A_a (whole rank tiles of 16)."""
+    return (int(r) + 15) // 16 * 16
 
 
 def pack_adapter(A: torch.Tensor, B: torch.Tensor):
     """Pack one adapter, A bf16 [K, r] and B bf16 [r, N], into the form the layer reads
-    (lora_pack_adapter): returns ``(At, Bt)``, bf16 [rank_pad(r), K] and [N, rank_pad(r)]."""
+    (lora_pack_adapter): returns ``(At, Bt)``: At bf16 [a_rows(r), K] holding A in the
+    MFMA operand order of lora_lowp.h, Bt bf16 [N, rank_pad(r)] = B^T with zero padding."""
     _dev(A, "A", torch.bfloat16)
     _dev(B, "B", torch.bfloat16)
     K, r = A.shape
@@ -93,7 +99,7 @@ def pack_adapter(A: torch.Tensor, B: torch.Tensor):
     if r2 != r:
         raise ValueError(f"A is [K, {r}] but B is [{r2}, N]")
     rp = rank_pad(r)
-    At = torch.empty((rp, K), dtype=torch.bfloat16, device=A.device)
+    At = torch.empty((a_rows(r), K), dtype=torch.bfloat16, device=A.device)
     Bt = torch.empty((N, rp), dtype=torch.bfloat16, device=A.device)
     check("lora_pack_adapter", lib().lora_pack_adapter(_ptr(A), _ptr(B), K, N, r, _ptr(At), _ptr(Bt), _stream()))
     return At, Bt

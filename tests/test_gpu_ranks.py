@@ -81,21 +81,27 @@ def test_any_rank_segments_built_in_launch(T):
 
 
 def test_pack_adapter_layout():
-    """lora_pack_adapter against its definition in lora_lowp.h, padding included."""
+    """lora_pack_adapter against its definition in lora_lowp.h, padding included: A in
+    operand order (rank tile jt, k-step ks, half h, lane l = 16 g + i, element e holds
+    A[64 ks + 16 g + 8 h + e][16 jt + i]), B as B^T with zero columns past r."""
     import torch
     import precision_gemm_amd as P
     from workloads.device import bf16_tensor
     rng = np.random.default_rng(8)
-    for K, N, r in [(256, 128, 1), (512, 192, 12), (128, 64, 60), (384, 320, 64), (256, 64, 8)]:
+    for K, N, r in [(256, 128, 1), (512, 192, 12), (128, 64, 60), (384, 320, 64), (256, 64, 8), (192, 64, 17)]:
         A = rng.integers(0, 1 << 16, (K, r), dtype=np.uint16)
         B = rng.integers(0, 1 << 16, (r, N), dtype=np.uint16)
         At, Bt = P.pack_adapter(bf16_tensor(A), bf16_tensor(B))
         torch.cuda.synchronize()
-        rp = P.rank_pad(r)
-        at = At.view(torch.int16).cpu().numpy().view(np.uint16)
+        rp, ra = P.rank_pad(r), P.a_rows(r)
+        at = At.view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1)
         bt = Bt.view(torch.int16).cpu().numpy().view(np.uint16)
-        assert at.shape == (rp, K) and bt.shape == (N, rp)
-        assert np.array_equal(at[:r], A.T) and not at[r:].any()
+        assert at.size == ra * K and bt.shape == (N, rp)
+        Apad = np.zeros((K, ra), np.uint16)
+        Apad[:, :r] = A
+        # [jt][ks][h][g][i][e] <- A[64 ks + 16 g + 8 h + e][16 jt + i]
+        ref = Apad.reshape(K // 64, 4, 2, 8, ra // 16, 16).transpose(4, 0, 2, 1, 5, 3).reshape(-1)
+        assert np.array_equal(at, ref)
         assert np.array_equal(bt[:, :r], B.T) and not bt[:, r:].any()
 
 
