@@ -185,6 +185,32 @@ def decoder_layer(args):
     print(json.dumps(out))
 
 
+def tune_shrink(args, wl):
+    """The configuration search of the down-projection (precision_gemm_amd.tune) on this
+    workload: the library's own configuration against the best one found, microseconds per
+    launch of the standalone down-projection."""
+    import torch
+    import precision_gemm_amd as P
+    from precision_gemm_amd import tune
+    from workloads.device import upload
+    x, w, ad, ids = upload(wl)
+    seg = P.build_segments(ids, ad.n)
+    torch.cuda.synchronize()
+    res = tune.tune_shrink(x, seg, ad, steps=args.tune_shrink, seed=0)
+    ref = P.shrink(x, seg, ad)
+    best_t = P.shrink_configured(x, seg, ad, tune.to_config(res.best))
+    torch.cuda.synchronize()
+    names = ("TG", "JP", "U", "TBLK", "ORDER")
+    out = {"workload": args.workload, "what": "standalone down-projection, us per launch (HIP events)",
+           "start": dict(zip(names, tune.to_config(res.start))), "start_us": res.start_cost,
+           "best": dict(zip(names, tune.to_config(res.best))), "best_us": res.best_cost,
+           "speedup": res.start_cost / res.best_cost, "steps": len(res.trace), "evaluated": len(res.evaluated),
+           "accepted": sum(1 for s in res.trace if s[3]), "t_bitwise_equal": bool(torch.equal(ref, best_t)),
+           "trace": [[s[0], dict(zip(names, tune.to_config(s[1]))), round(s[2], 3), s[3]] for s in res.trace],
+           "kernel_sha": kernel_source_sha()}
+    print(json.dumps(out), flush=True)
+
+
 def stored_traffic(workload: str, sha: str):
     p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(p):
@@ -207,6 +233,9 @@ def main():
     ap.add_argument("--act", choices=["mxfp8", "bf16"], default="mxfp8",
                     help="activations of the base product: MXFP8 (default) or bf16 as they are")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph replay")
+    ap.add_argument("--tune-shrink", type=int, default=0, metavar="STEPS",
+                    help="instead of the layer call: search the down-projection's configurations for the "
+                         "workload (STEPS steps of the stochastic search) and print the result")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="after the timed region, run three plain device copies of this many MiB (untimed): "
                          "the reference that scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -228,6 +257,9 @@ def main():
         return
     print(f"[bench] generating {args.workload}", file=sys.stderr, flush=True)
     wl = workloads.make(args.workload)
+    if args.tune_shrink:
+        tune_shrink(args, wl)
+        return
     a16 = args.act == "bf16"
     nbytes, flops = algorithmic(wl)
     sets = args.sets or max(1, min(32, int(np.ceil(2 * 256e6 / nbytes)) + 1))

@@ -208,6 +208,30 @@ lora_status lora_shrink(const uint16_t* x, int32_t T, int32_t K,
                         int32_t n_adapters, int32_t r_max,
                         float* t, void* workspace, size_t workspace_bytes, void* stream);
 
+/* The standalone down-projection (lora_shrink's result, bitwise: every configuration keeps
+ * the summation order) with an explicit configuration, for operator tuning ("Efficient
+ * multi-tenant LoRA serving via SGMV-specific operator autotuning", abstract: tiling,
+ * caching and virtual-thread scheduling of the SGMV operator chosen by a stochastic search).
+ * config [host] int32[5] = {TG, JP, U, TBLK, ORDER}:
+ *   TG   token tiles of 16 per inner step (tiling)            1, 2 or 4
+ *   JP   rank tiles of 16 per workgroup item (tiling)          1, 2 or 4
+ *   U    k-steps of 64 per prefetch buffer (caching)          1 or 2
+ *   TBLK tokens of one segment per workgroup item, a multiple of 16 (scheduling)
+ *   ORDER 0: items in workgroup-id order; 1: each XCD takes a contiguous run of items
+ *         (scheduling).
+ * Other values return LORA_ERR_UNSUPPORTED.  Other arguments as lora_shrink. */
+lora_status lora_shrink_configured(const uint16_t* x, int32_t T, int32_t K,
+                                   const int32_t* seg_indptr, const int32_t* sorted_tok,
+                                   const uint64_t* A_ptrs, const int32_t* ranks,
+                                   int32_t n_adapters, int32_t r_max, float* t,
+                                   const int32_t* config, void* stream);
+
+/* Resources of the compiled down-projection instance (TG, JP, U) on the current device:
+ * out [host] int32[3] = {registers per lane, scratch (spill) bytes per lane, LDS bytes}.
+ * LORA_ERR_UNSUPPORTED for a configuration that is not compiled; LORA_ERR_HIP without a
+ * device. */
+lora_status lora_shrink_config_info(int32_t tg, int32_t jp, int32_t u, int32_t* out);
+
 /* Adapter up-projection as its own launch (the unfused schedule the "EpiLoRA"
  * abstract replaces):  y[tok, :] = bf16( y[tok, :] + s_a * t[tok, :r_a] @ B_a ).
  * y is read and written in place.  Tokens whose adapter id is outside

@@ -34,6 +34,9 @@ _SIGNATURES = {
     "gemm_lowp_lora_epilogue_noalloc": (c_i32, [c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp,
                                                 c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_vp, c_u32, c_vp]),
     "lora_pack_weight": (c_i32, [c_i32, c_vp, c_vp, c_i32, c_i32, c_vp, c_vp, c_vp]),
+    "lora_shrink_configured": (c_i32, [c_vp, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_vp,
+                                       ctypes.POINTER(c_i32), c_vp]),
+    "lora_shrink_config_info": (c_i32, [c_i32, c_i32, c_i32, ctypes.POINTER(c_i32)]),
     "lora_pack_adapter": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]),
     "lora_plan_info": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(c_i32), c_i32]),
 }

@@ -452,6 +452,47 @@ lora_status lora_pack_adapter(const uint16_t* A, const uint16_t* B, int32_t K, i
   return launch_pack_adapter(A, B, K, N, r, At, Bt, as_stream(stream)) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
+lora_status lora_shrink_configured(const uint16_t* x, int32_t T, int32_t K, const int32_t* seg_indptr,
+                                   const int32_t* sorted_tok, const uint64_t* A_ptrs, const int32_t* ranks,
+                                   int32_t n_adapters, int32_t r_max, float* t, const int32_t* config, void* stream) {
+  lora_status st = check_sizes(T, K, 64);
+  if (st != LORA_OK) return st;
+  if ((st = check_adapters(n_adapters, r_max)) != LORA_OK) return st;
+  if (!config) return LORA_ERR_INVALID_ARG;
+  const int tg = config[0], jp = config[1], u = config[2], tblk = config[3], order = config[4];
+  auto in = [](int v, int a, int b, int c) { return v == a || v == b || v == c; };
+  if (!in(tg, 1, 2, 4) || !in(jp, 1, 2, 4) || (u != 1 && u != 2) || (order != 0 && order != 1))
+    return LORA_ERR_UNSUPPORTED;
+  if (tblk < 16 || tblk % 16 != 0 || tblk > 65536) return LORA_ERR_UNSUPPORTED;
+  if (T == 0) return LORA_OK;
+  if (!x || !seg_indptr || !sorted_tok || !A_ptrs || !ranks || !t) return LORA_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(t)) return LORA_ERR_INVALID_ARG;
+  ShrinkParams sp{};
+  sp.x = x; sp.T = T; sp.K = K;
+  sp.seg_indptr = seg_indptr; sp.sorted_tok = sorted_tok;
+  sp.A_ptrs = A_ptrs; sp.ranks = ranks; sp.n_ad = n_adapters; sp.r_max = rank_pad(r_max); sp.r_lim = r_max;
+  sp.ids = nullptr;
+  sp.t_out = t; sp.t_tag = nullptr;
+  sp.tblk = tblk; sp.n_tblk = ceil_div(T, tblk); sp.jper = jp; sp.n_jg = ceil_div(r_max, 16 * jp);
+  sp.kparts = 1; sp.kpart_len = ceil_div(K, 256) * 256;
+  sp.item_order = order;
+  const long items = (long)n_adapters * sp.n_tblk * sp.n_jg;
+  if (items > (1L << 30)) return LORA_ERR_UNSUPPORTED;
+  return launch_shrink_cfg(tg, jp, u, (int)items, as_stream(stream), sp) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+lora_status lora_shrink_config_info(int32_t tg, int32_t jp, int32_t u, int32_t* out) {
+  if (!out) return LORA_ERR_INVALID_ARG;
+  int regs = 0, spill = 0, lds = 0;
+  const hipError_t e = shrink_cfg_attr(tg, jp, u, &regs, &spill, &lds);
+  if (e == hipErrorInvalidValue) return LORA_ERR_UNSUPPORTED;
+  if (e != hipSuccess) return LORA_ERR_HIP;
+  out[0] = regs;
+  out[1] = spill;
+  out[2] = lds;
+  return LORA_OK;
+}
+
 /* Introspection for tests and the benchmark: the plan chosen for these sizes. */
 int32_t lora_plan_info(int32_t T, int32_t K, int32_t N, int32_t n_adapters, int32_t r_max, int32_t w_fmt,
                        int32_t* out, int32_t n_out) {

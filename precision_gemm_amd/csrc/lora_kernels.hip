@@ -577,7 +577,12 @@ __global__ __launch_bounds__(256) void k_shrink(ShrinkParams p) {
   extern __shared__ __align__(16) char smem[];
   int started = 0;
   bool published = false;
-  shrink_item<TG, JP, U>(p, blockIdx.x, smem, nullptr, 0, nullptr, &started, published);
+  // item order 1: workgroups are dealt to the eight XCDs in turn, and XCD x takes the x-th
+  // eighth of the items, so that items sharing an adapter's A_a and a segment's x rows run on
+  // one XCD's L2
+  const int b = blockIdx.x, nb = gridDim.x;
+  const int item = (p.item_order == 1 && nb % 8 == 0) ? (b & 7) * (nb >> 3) + (b >> 3) : b;
+  shrink_item<TG, JP, U>(p, item, smem, nullptr, 0, nullptr, &started, published);
 }
 
 // ======================================================================================
@@ -2233,6 +2238,37 @@ hipError_t launch_shrink(const LayerPlan& pl, hipStream_t stream, const ShrinkPa
   if (pl.s_cfg == 1) return launch_k(k_shrink<4, 2, 1>, pl.n_shrink_items, shrink_smem<4, 2, 1>(), stream, sp);
   return hipErrorInvalidValue;
 }
+
+// compiled configurations of the standalone down-projection (tuning)
+#define LORA_SHRINK_CFGS(X) \
+  X(1, 1, 1) X(1, 1, 2) X(1, 2, 1) X(1, 2, 2) X(1, 4, 1) X(1, 4, 2) \
+  X(2, 1, 1) X(2, 1, 2) X(2, 2, 1) X(2, 2, 2) X(2, 4, 1) X(2, 4, 2) \
+  X(4, 1, 1) X(4, 1, 2) X(4, 2, 1) X(4, 2, 2) X(4, 4, 1) X(4, 4, 2)
+
+hipError_t launch_shrink_cfg(int tg, int jp, int u, int grid, hipStream_t s, const ShrinkParams& sp) {
+#define X(TG_, JP_, U_) \
+  if (tg == TG_ && jp == JP_ && u == U_) return launch_k(k_shrink<TG_, JP_, U_>, grid, shrink_smem<TG_, JP_, U_>(), s, sp);
+  LORA_SHRINK_CFGS(X)
+#undef X
+  return hipErrorInvalidValue;
+}
+
+hipError_t shrink_cfg_attr(int tg, int jp, int u, int* regs, int* spill, int* lds) {
+  hipFuncAttributes fa{};
+  hipError_t e = hipErrorInvalidValue;
+#define X(TG_, JP_, U_)                                                                       \
+  if (tg == TG_ && jp == JP_ && u == U_) {                                                    \
+    e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(k_shrink<TG_, JP_, U_>));   \
+    *lds = (int)shrink_smem<TG_, JP_, U_>();                                                 \
+  }
+  LORA_SHRINK_CFGS(X)
+#undef X
+  if (e != hipSuccess) return e;
+  *regs = fa.numRegs;
+  *spill = (int)fa.localSizeBytes;
+  return hipSuccess;
+}
+#undef LORA_SHRINK_CFGS
 
 hipError_t launch_build_segments(const int* ids, int T, int n_ad, int* seg, int* sorted, int* err, hipStream_t s) {
   return launch_kn(k_build_segments, 1, SEG_THREADS, seg_lds_bytes(T, n_ad), s, ids, T, n_ad, seg, sorted, err);

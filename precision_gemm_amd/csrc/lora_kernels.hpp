@@ -60,6 +60,7 @@ struct ShrinkParams {
   int n_jg;            // rank groups per adapter (16 * jper ranks each)
   int jper;            // 16-rank tiles per group (1..4)
   int kparts, kpart_len;
+  int item_order;      // standalone launch: 0 items in id order, 1 each XCD a contiguous run of items
   int seg_wait;        // the segments are built in the same launch: wait for them, read them coherently
   int compact;         // fused launch: workgroups loop over the items with tokens (long batches)
   int compact_off;     // LDS byte offset of the block prefix (after the down-projection's area)
@@ -140,6 +141,12 @@ hipError_t launch_quant_build(const uint16_t* x, int T, int K, uint8_t* xq, uint
                               int* seg, int* sorted, int* err, hipStream_t s);
 hipError_t launch_shrink(const LayerPlan& pl, hipStream_t stream, const ShrinkParams& sp);
 hipError_t launch_expand(const ExpandParams& p, hipStream_t s);
+// the standalone down-projection with an explicit configuration (tuning): TG token tiles and
+// JP rank tiles per inner step, U k-steps per prefetch buffer (compiled for TG, JP in
+// {1, 2, 4}, U in {1, 2}); one workgroup per item.  shrink_cfg_attr: the instance's registers
+// per lane, scratch (spill) bytes per lane and LDS bytes.
+hipError_t launch_shrink_cfg(int tg, int jp, int u, int grid, hipStream_t s, const ShrinkParams& sp);
+hipError_t shrink_cfg_attr(int tg, int jp, int u, int* regs, int* spill, int* lds);
 hipError_t launch_layer(const LayerPlan& pl, hipStream_t stream, const ShrinkParams& sp, const GemmParams& gp);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_pack_weight(int fmt, const uint8_t* q, const uint8_t* sc, int N, int K, uint8_t* qp, uint8_t* scp,

@@ -221,15 +221,37 @@ def quant_act_mxfp8(x: torch.Tensor):
     return xq, xsc
 
 
-def shrink(x: torch.Tensor, seg: Segments, ad: Adapters, ws: torch.Tensor, t: torch.Tensor | None = None):
+def shrink(x: torch.Tensor, seg: Segments, ad: Adapters, ws: torch.Tensor | None = None,
+           t: torch.Tensor | None = None):
     _dev(x, "x", torch.bfloat16)
     T, K = x.shape
     if t is None:
         t = torch.empty((T, ad.r_max), dtype=torch.float32, device=x.device)
     check("lora_shrink", lib().lora_shrink(_ptr(x), T, K, _ptr(seg.seg_indptr), _ptr(seg.sorted_tok),
                                            _ptr(ad.A_ptrs), _ptr(ad.ranks), ad.n, ad.r_max, _ptr(t), _ptr(ws),
-                                           ws.numel(), _stream()))
+                                           0 if ws is None else ws.numel(), _stream()))
     return t
+
+
+def shrink_configured(x: torch.Tensor, seg: Segments, ad: Adapters, config, t: torch.Tensor | None = None):
+    """The standalone down-projection with an explicit configuration (TG, JP, U, TBLK, ORDER);
+    see lora_shrink_configured."""
+    _dev(x, "x", torch.bfloat16)
+    T, K = x.shape
+    if t is None:
+        t = torch.empty((T, ad.r_max), dtype=torch.float32, device=x.device)
+    cfg = (ctypes.c_int32 * 5)(*[int(v) for v in config])
+    check("lora_shrink_configured", lib().lora_shrink_configured(
+        _ptr(x), T, K, _ptr(seg.seg_indptr), _ptr(seg.sorted_tok), _ptr(ad.A_ptrs), _ptr(ad.ranks), ad.n, ad.r_max,
+        _ptr(t), cfg, _stream()))
+    return t
+
+
+def shrink_config_info(tg: int, jp: int, u: int) -> dict:
+    """Registers, spill bytes and LDS bytes of a compiled down-projection instance."""
+    out = (ctypes.c_int32 * 3)()
+    check("lora_shrink_config_info", lib().lora_shrink_config_info(tg, jp, u, out))
+    return {"regs": out[0], "spill": out[1], "lds": out[2]}
 
 
 def expand(t: torch.Tensor, seg: Segments, ad: Adapters, y: torch.Tensor) -> torch.Tensor:

@@ -211,3 +211,22 @@ def test_noalloc_checks_before_touching_the_device(L):
     assert _noalloc(L, y=MISALIGNED) == INVALID
     assert _noalloc(L, A=NULL) == INVALID
     assert L.lora_status_string(SCRATCH_LIMIT).startswith(b"sizes need more")
+
+
+def test_shrink_configured_validation(L):
+    cfg = lambda *v: (ctypes.c_int32 * 5)(*v)  # noqa: E731
+    args = lambda c, **kw: (kw.get("x", FAKE), kw.get("T", 64), kw.get("K", 1024), FAKE, FAKE, FAKE, FAKE,  # noqa: E731
+                            kw.get("n", 4), kw.get("r", 16), FAKE, c, NULL)
+    assert L.lora_shrink_configured(*args(cfg(3, 1, 1, 16, 0))) == UNSUPPORTED     # TG
+    assert L.lora_shrink_configured(*args(cfg(1, 8, 1, 16, 0))) == UNSUPPORTED     # JP
+    assert L.lora_shrink_configured(*args(cfg(1, 1, 3, 16, 0))) == UNSUPPORTED     # U
+    assert L.lora_shrink_configured(*args(cfg(1, 1, 1, 24, 0))) == UNSUPPORTED     # TBLK % 16
+    assert L.lora_shrink_configured(*args(cfg(1, 1, 1, 16, 2))) == UNSUPPORTED     # ORDER
+    assert L.lora_shrink_configured(*args(None)) == INVALID
+    assert L.lora_shrink_configured(*args(cfg(1, 1, 1, 16, 0), x=NULL)) == INVALID
+    assert L.lora_shrink_configured(*args(cfg(1, 1, 1, 16, 0), K=1000)) == UNSUPPORTED
+    assert L.lora_shrink_configured(*args(cfg(1, 1, 1, 16, 0), r=65)) == UNSUPPORTED
+    assert L.lora_shrink_configured(*args(cfg(1, 1, 1, 16, 0), T=0)) == LORA_OK
+    out = (ctypes.c_int32 * 3)()
+    assert L.lora_shrink_config_info(3, 1, 1, out) == UNSUPPORTED
+    assert L.lora_shrink_config_info(1, 1, 1, None) == INVALID
