@@ -99,8 +99,13 @@ LayerPlan make_plan(int T, int K, int N, int n_ad, int r_max_in, int fmt, bool f
     pl.s_cfg = 0;
     pl.s_tblk = ceil_div(T, 16) * 16;
     pl.s_ntblk = 1;
-    pl.s_jper = 1;
-    pl.s_njg = ceil_div(r_max, 16);
+    // The standalone launch takes all ranks of an adapter in one item (up to 64): its x rows
+    // are read once and the four rank tiles' loads are in flight together (the configuration
+    // search's choice on the one-token-per-adapter down-projection: 76 -> 35 us).  In the
+    // fused launch, beside the GEMM workgroups, items of 16 ranks measured faster
+    // (down-projection workload 96 us per call against 122 us with 64-rank items).
+    pl.s_jper = fused ? 1 : 4;
+    pl.s_njg = ceil_div(r_max, 16 * pl.s_jper);
     // latency-bound single-tile decode: split K so that t is ready early (measured: for the
     // 128-token shapes K-parts only add per-item start-up round trips)
     if (fused && T <= 16) kparts = std::min(4, std::max(1, K / 1024));

@@ -2234,7 +2234,7 @@ hipError_t launch_layer(const LayerPlan& pl, hipStream_t stream, const ShrinkPar
 }
 
 hipError_t launch_shrink(const LayerPlan& pl, hipStream_t stream, const ShrinkParams& sp) {
-  if (pl.s_cfg == 0) return launch_k(k_shrink<1, 1, 2>, pl.n_shrink_items, shrink_smem<1, 1, 2>(), stream, sp);
+  if (pl.s_cfg == 0) return launch_k(k_shrink<1, 4, 1>, pl.n_shrink_items, shrink_smem<1, 4, 1>(), stream, sp);
   if (pl.s_cfg == 1) return launch_k(k_shrink<4, 2, 1>, pl.n_shrink_items, shrink_smem<4, 2, 1>(), stream, sp);
   return hipErrorInvalidValue;
 }

@@ -76,7 +76,7 @@ def default_node(T: int):
     """The library's own choice for the standalone launch (the tile plan)."""
     if T <= 128:
         m = max(1, -(-T // 16))
-        return (1, 1, 2, 4 if m > 2 else (2 if m > 1 else 1), 0)
+        return (1, 4, 1, 4 if m > 2 else (2 if m > 1 else 1), 0)
     return (4, 2, 1, 1, 0)
 
 
