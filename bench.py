@@ -162,6 +162,32 @@ def decoder_layer(args):
     ev_us = e0.elapsed_time(e1) * 1e3 / K
     status = max(P.workspace_status(q["ws"]) for d in S for q in d["projs"])
     achieved = nbytes / (ev_us * 1e-6) / 1e9
+    # ablation: the same four projections in the per-token merged-weight formulation
+    # (lora_merged_layer, x in bf16), one input set, graph of K steps
+    d0 = S[0]
+    merged = []
+    for wl, q in zip(wls, d0["projs"]):
+        wr = P.LowpWeight(wl.fmt, torch.from_numpy(np.ascontiguousarray(wl.w_q)).cuda(),
+                          torch.from_numpy(np.ascontiguousarray(wl.w_scale)).cuda())
+        merged.append((q, wr, P.adapter_rows(q["ad"])))
+    ids_m = d0["seg"].adapter_id
+
+    def step_merged():
+        for q, wr, (rows_, ptrs) in merged:
+            P.merged_layer(q["x"], wr, ids_m, q["ad"], ptrs, y=q["y"])
+
+    step_merged()
+    gm = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gm):
+        for i in range(K):
+            step_merged()
+    gm.replay()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    gm.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    merged_us = e0.elapsed_time(e1) * 1e3 / K
     out = {
         "metric": METRIC, "value": round(us, 3), "unit": "us/call", "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": us / 1e3, "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
@@ -175,6 +201,8 @@ def decoder_layer(args):
                      "kernel": "k_layer x 4 (the chain's four launches together)", "per_call_bytes": nbytes,
                      "per_call_flops": flops, "kernel_us": ev_us},
         "parity": parity, "device_status": status, "kernel_sha": kernel_source_sha(),
+        "ablation_merged": {"what": "the four projections as per-token merged-weight layers (lora_merged_layer, "
+                                    "x in bf16), us per step", "us": merged_us, "over_fused": merged_us / ev_us},
     }
     if not args.no_cpu:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
@@ -211,6 +239,57 @@ def tune_shrink(args, wl):
     print(json.dumps(out), flush=True)
 
 
+def ablation_merged(args, wl):
+    """The per-token merged-weight formulation against the fused layer (both with x in bf16:
+    by the merged-weight identity they compute the same layer), microseconds per call from
+    HIP events around a graph of K calls, and both checked against the oracle on sampled rows."""
+    import torch
+    import precision_gemm_amd as P
+    from workloads.device import upload
+    from oracle.layer import LowpWeight, layer
+    x, w, ad, ids = upload(wl)
+    wr = P.LowpWeight(wl.fmt, torch.from_numpy(np.ascontiguousarray(wl.w_q)).cuda(),
+                      torch.from_numpy(np.ascontiguousarray(wl.w_scale)).cuda())
+    rows, ptrs = P.adapter_rows(ad)
+    seg = P.build_segments(ids, ad.n)
+    ws = P.alloc_workspace(wl.T, wl.K, wl.N, ad.n, ad.r_max)
+    y_m = torch.empty((wl.T, wl.N), dtype=torch.bfloat16, device="cuda")
+    y_f = torch.empty_like(y_m)
+    calls = {"merged": lambda: P.merged_layer(x, wr, ids, ad, ptrs, y=y_m),
+             "fused_act_bf16": lambda: P.gemm_lowp_lora_epilogue(x, w, seg, ad, ws, fuse_shrink=True, y=y_f,
+                                                                 act_bf16=True)}
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, fn in calls.items():
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(args.steps):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) * 1e3 / args.steps
+    rows_chk = np.arange(wl.T) if wl.T <= 256 else np.linspace(0, wl.T - 1, 64).astype(int)
+    ref = layer(wl.x[rows_chk], LowpWeight(wl.fmt, wl.w_q, wl.w_scale), wl.A, wl.B, wl.scale,
+                np.asarray(wl.ids)[rows_chk], act="bf16")["y"]
+    parity = {}
+    for name, yy in (("merged", y_m), ("fused_act_bf16", y_f)):
+        d = yy.float().cpu().numpy().astype(np.float64)[rows_chk] - ref
+        parity[name] = {"max_rel": float(np.abs(d).max() / np.abs(ref).max()),
+                        "frob_rel": float(np.linalg.norm(d) / np.linalg.norm(ref))}
+    out = {"workload": args.workload, "what": "us per layer call, graph of K calls, HIP events",
+           "merged_us": res["merged"], "fused_act_bf16_us": res["fused_act_bf16"],
+           "merged_over_fused": res["merged"] / res["fused_act_bf16"], "adapters_present": int(len(np.unique(wl.ids))),
+           "parity": parity, "steps": args.steps, "kernel_sha": kernel_source_sha()}
+    print(json.dumps(out), flush=True)
+
+
 def stored_traffic(workload: str, sha: str):
     p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(p):
@@ -236,6 +315,9 @@ def main():
     ap.add_argument("--tune-shrink", type=int, default=0, metavar="STEPS",
                     help="instead of the layer call: search the down-projection's configurations for the "
                          "workload (STEPS steps of the stochastic search) and print the result")
+    ap.add_argument("--ablation-merged", action="store_true",
+                    help="instead of the layer call: time the per-token merged-weight layer (lora_merged_layer) "
+                         "against the fused layer with 16-bit activations on the workload")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="after the timed region, run three plain device copies of this many MiB (untimed): "
                          "the reference that scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -259,6 +341,9 @@ def main():
     wl = workloads.make(args.workload)
     if args.tune_shrink:
         tune_shrink(args, wl)
+        return
+    if args.ablation_merged:
+        ablation_merged(args, wl)
         return
     a16 = args.act == "bf16"
     nbytes, flops = algorithmic(wl)

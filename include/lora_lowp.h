@@ -226,6 +226,24 @@ lora_status lora_shrink_configured(const uint16_t* x, int32_t T, int32_t K,
                                    int32_t n_adapters, int32_t r_max, float* t,
                                    const int32_t* config, void* stream);
 
+/* The per-token merged-weight formulation of the layer, an alternative to ablate against
+ * ("LoRA-Switch" abstract: each token's adapter is merged into the backbone weights for
+ * inference, the merges fused in one kernel):
+ *     y[t, :] = bf16( x[t] . (W_d + s_a A_a B_a) ),   a = adapter_id[t],
+ * with the merged weight formed in registers (rounded to bf16 for the MFMA) and never
+ * stored; x enters in bf16 (by the merged-weight identity this is the 16-bit activation
+ * layer).  Tokens whose adapter id or rank is invalid get the base term only.
+ *  - w_q, w_scale: W in its row-major form (see "Data layouts"), not packed;
+ *  - A_rows: per adapter, the device address of A_a as bf16 [K][rank_pad(r_a)] row-major
+ *    (the ranks past r_a read but masked);
+ *  - B_ptrs: per adapter, B_a^T packed by lora_pack_adapter.
+ * Limits as for the layer call; no workspace; one launch. */
+lora_status lora_merged_layer(const uint16_t* x, int32_t T, int32_t K, int32_t N, int32_t w_fmt,
+                              const uint8_t* w_q, const void* w_scale, const int32_t* adapter_id,
+                              const uint64_t* A_rows, const uint64_t* B_ptrs,
+                              const int32_t* ranks, const float* scales, int32_t n_adapters,
+                              int32_t r_max, uint16_t* y, void* stream);
+
 /* Resources of the compiled down-projection instance (TG, JP, U) on the current device:
  * out [host] int32[3] = {registers per lane, scratch (spill) bytes per lane, LDS bytes}.
  * LORA_ERR_UNSUPPORTED for a configuration that is not compiled; LORA_ERR_HIP without a

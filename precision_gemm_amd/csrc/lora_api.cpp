@@ -498,6 +498,25 @@ lora_status lora_shrink_config_info(int32_t tg, int32_t jp, int32_t u, int32_t* 
   return LORA_OK;
 }
 
+lora_status lora_merged_layer(const uint16_t* x, int32_t T, int32_t K, int32_t N, int32_t w_fmt, const uint8_t* w_q,
+                              const void* w_scale, const int32_t* adapter_id, const uint64_t* A_rows,
+                              const uint64_t* B_ptrs, const int32_t* ranks, const float* scales, int32_t n_adapters,
+                              int32_t r_max, uint16_t* y, void* stream) {
+  lora_status st = check_sizes(T, K, N);
+  if (st != LORA_OK) return st;
+  if ((st = check_adapters(n_adapters, r_max)) != LORA_OK) return st;
+  if (w_fmt != LORA_W_FP8_E4M3 && w_fmt != LORA_W_MXFP4_E2M1) return LORA_ERR_INVALID_ARG;
+  if (T == 0) return LORA_OK;
+  if (T > 65535 * 16) return LORA_ERR_UNSUPPORTED;
+  if (!x || !w_q || !w_scale || !adapter_id || !A_rows || !B_ptrs || !ranks || !scales || !y)
+    return LORA_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_q) || !aligned16(y)) return LORA_ERR_INVALID_ARG;
+  return launch_merged(x, T, K, N, w_fmt, w_q, w_scale, adapter_id, A_rows, B_ptrs, ranks, scales, n_adapters, r_max, y,
+                       as_stream(stream)) == hipSuccess
+             ? LORA_OK
+             : LORA_ERR_HIP;
+}
+
 /* Introspection for tests and the benchmark: the plan chosen for these sizes. */
 int32_t lora_plan_info(int32_t T, int32_t K, int32_t N, int32_t n_adapters, int32_t r_max, int32_t w_fmt,
                        int32_t* out, int32_t n_out) {

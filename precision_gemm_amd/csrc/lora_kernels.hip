@@ -2158,6 +2158,165 @@ __global__ __launch_bounds__(256) void k_prep_rows(ShrinkParams sp, uint8_t* __r
 }
 
 // ======================================================================================
+// The per-token merged-weight formulation, as an alternative to ablate against ("LoRA-Switch"
+// abstract: each token's adapter is merged into the backbone weights for inference, the merges
+// of all adapters fused in one kernel).  y[t] = bf16( x[t] . (W_d + s_a A_a B_a) ) with the
+// merged weight formed in registers and never stored: workgroup = 16 output channels x 16
+// tokens, the four waves splitting K in quarters.  Per 32-wide k-step lane (i, g) holds
+// W'[n0 + i][k] for k in {k0 + 4g .. k0 + 4g + 3} and {k0 + 16 + 4g .. k0 + 16 + 4g + 3}:
+// the delta A_a B_a comes from two bf16 MFMAs per 32 ranks (rows k, columns n: their output
+// puts exactly those four k of column i in lane (i, g)), the base term from the W codes
+// (FP8 times the channel scale, or MXFP4 times its block scale), and W' goes to bf16 as the
+// A operand of the main MFMA, whose B operand reads x at the same k.  Each adapter present in
+// the token tile is one pass (rows of other adapters masked); tokens without a valid adapter
+// get a pass with the base weight alone.  W is read in its row-major form, A_a as A rows
+// bf16 [K][rank_pad(r_a)], B_a as the packed B_a^T.
+// ======================================================================================
+struct MergedParams {
+  const uint16_t* x;
+  int T, K, N, fmt;
+  const uint8_t* wq;       // row-major codes [N][K] (FP8) or [N][K/2] (MXFP4)
+  const float* ws_fp8;     // [N]
+  const uint8_t* ws_fp4;   // [N][K/32]
+  const int* ids;
+  const uint64_t* A_rows;  // per adapter: bf16 [K][rank_pad(r)]
+  const uint64_t* B_ptrs;  // per adapter: bf16 [N][rank_pad(r)]
+  const int* ranks;
+  const float* scales;
+  int n_ad, r_lim;
+  uint16_t* y;
+};
+
+template <int FMT>
+__global__ __launch_bounds__(256) void k_merged(MergedParams p) {
+  __shared__ __align__(16) float red[4][64][4];
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, li = lane & 15,
+            g = lane >> 4;
+  const int K = p.K;
+  const int n0 = blockIdx.x * 16, t0 = blockIdx.y * 16;
+  const int n = n0 + li;
+  // the lane's token (as the main MFMA's B operand: column li) and its adapter
+  const int tok = min(t0 + li, p.T - 1);
+  const bool tok_ok = t0 + li < p.T;
+  int a_tok = tok_ok ? p.ids[tok] : -1;
+  if (a_tok >= 0 && a_tok < p.n_ad) {
+    const int r = p.ranks[a_tok];
+    if (r < 1 || r > p.r_lim) a_tok = -2;  // no adapter term (the layer call reports it)
+  } else if (tok_ok) {
+    a_tok = -2;
+  }
+  const int kq = K >> 2, kb = wave * kq, nst = kq >> 5;  // the wave's quarter, steps of 32
+  const float s_w = (FMT == LORA_W_FP8_E4M3) ? p.ws_fp8[n] : 1.f;
+  const uint16_t* xrow = p.x + (long)tok * K + 4 * g;
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  // passes: one per adapter present among lanes 0 .. 15, then one for tokens without one
+  unsigned long long todo = __ballot(li == lane && a_tok >= 0);
+  bool base_pass = __ballot(li == lane && a_tok == -2) != 0ull;
+  while (todo || base_pass) {
+    int a = -1, r = 0;
+    if (todo) {
+      a = __builtin_amdgcn_readlane(a_tok, __ffsll((long long)todo) - 1);
+      todo &= ~__ballot(li == lane && a_tok == a);
+      r = p.ranks[a];
+    } else {
+      base_pass = false;
+    }
+    const bool mine = (a >= 0) ? (a_tok == a) : (a_tok == -2);
+    const int r8 = (a >= 0) ? rank_pad(r) : 8;
+    const int nrb = (r8 + 31) >> 5;  // 32-rank blocks of the delta MFMAs
+    const float s_a = (a >= 0) ? p.scales[a] : 0.f;
+    // B_a^T of channel n, ranks 8g' .. 8g' + 7 per rank block (loop-invariant), masked past r
+    uint4 bop[2] = {zero4(), zero4()};
+    const uint16_t* arow = reinterpret_cast<const uint16_t*>(a >= 0 ? p.A_rows[a] : (uint64_t)p.x);
+    if (a >= 0) {
+      const uint16_t* bt = reinterpret_cast<const uint16_t*>(p.B_ptrs[a]) + (long)n * r8;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const int j = 32 * rb + 8 * g;
+        if (rb < nrb && j < r8) bop[rb] = keep_bf16(ldg16(bt + j), r - j);
+      }
+    }
+    // two stages in flight: the loads of step st + 1 go out before step st is multiplied
+    // (unconditional loads from clamped addresses; ranks past r_a are masked afterwards)
+    struct Stage {
+      uint32_t w[2];
+      uint2 x0, x1;
+      uint4 av[2][2];
+    };
+    // (without an adapter the stand-in rows are x's first eight values, stride 0)
+    const int jc0 = min(8 * g, r8 - 8), jc1 = min(32 + 8 * g, r8 - 8), astr = (a >= 0) ? r8 : 0;
+    auto load = [&](int st, Stage& S) {
+      const int k0 = kb + min(st, nst - 1) * 32;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (FMT == LORA_W_FP8_E4M3)
+          S.w[h] = *reinterpret_cast<const uint32_t*>(p.wq + (long)n * K + k0 + 16 * h + 4 * g);
+        else
+          S.w[h] = *reinterpret_cast<const uint16_t*>(p.wq + ((long)n * K + k0 + 16 * h + 4 * g) / 2);
+        const uint16_t* ar = arow + (long)(k0 + 16 * h + li) * astr;
+        S.av[h][0] = ldg16(ar + jc0);
+        S.av[h][1] = ldg16(ar + jc1);
+      }
+      S.x0 = *reinterpret_cast<const uint2*>(xrow + k0);
+      S.x1 = *reinterpret_cast<const uint2*>(xrow + k0 + 16);
+    };
+    auto compute = [&](const Stage& S, int st) {
+      const int k0 = kb + st * 32;
+      // delta^T tiles (rows k0 .. k0 + 15 and k0 + 16 .. k0 + 31, columns n0 .. n0 + 15)
+      v4f d[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+          if (rb < nrb) d[h] = mfma_bf16_16x16x32(keep_bf16(S.av[h][rb], r - (32 * rb + 8 * g)), bop[rb], d[h]);
+      // base weight at the same k: W[n][k0 + 16h + 4g + v]
+      float wv[2][4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (FMT == LORA_W_FP8_E4M3) {
+          const uint2 bf = fp8x4_to_bf16(S.w[h]);
+          wv[h][0] = bf16_lo(bf.x); wv[h][1] = bf16_hi(bf.x); wv[h][2] = bf16_lo(bf.y); wv[h][3] = bf16_hi(bf.y);
+        } else {
+          const float sc = __uint_as_float((uint32_t)p.ws_fp4[(long)n * (K / 32) + (k0 >> 5)] << 23);
+          const uint4 bf = fp4x8_to_bf16(S.w[h], sc);
+          wv[h][0] = bf16_lo(bf.x); wv[h][1] = bf16_hi(bf.x); wv[h][2] = bf16_lo(bf.y); wv[h][3] = bf16_hi(bf.y);
+        }
+      }
+      // merged weight to bf16 (the A operand: eight k of channel n for lane group g)
+      uint32_t wm[4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int v = 0; v < 4; v += 2)
+          wm[2 * h + v / 2] = bf16x2_rne(s_w * wv[h][v] + s_a * d[h][v], s_w * wv[h][v + 1] + s_a * d[h][v + 1]);
+      // x of the lane's token at the same k (the B operand), other adapters' tokens masked
+      const uint4 xv = mine ? make_uint4(S.x0.x, S.x0.y, S.x1.x, S.x1.y) : zero4();
+      acc = mfma_bf16_16x16x32(make_uint4(wm[0], wm[1], wm[2], wm[3]), xv, acc);
+    };
+    Stage S0, S1;
+    load(0, S0);
+    for (int st = 0; st < nst; st += 2) {
+      load(st + 1, S1);
+      compute(S0, st);
+      load(st + 2, S0);
+      if (st + 1 < nst) compute(S1, st + 1);
+    }
+  }
+  // the quarters' sums in wave order; lane (i, g) holds y[t0 + i][n0 + 4g + v]
+  *reinterpret_cast<v4f*>(&red[wave][lane][0]) = acc;
+  __syncthreads();
+  if (wave == 0) {
+    v4f sum = *reinterpret_cast<const v4f*>(&red[0][lane][0]);
+#pragma unroll
+    for (int w = 1; w < 4; ++w) sum += *reinterpret_cast<const v4f*>(&red[w][lane][0]);
+    if (tok_ok) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) p.y[(long)tok * p.N + n0 + 4 * g + v] = (uint16_t)f32_to_bf16_rne(sum[v]);
+    }
+  }
+}
+
+// ======================================================================================
 // Launchers
 // ======================================================================================
 template <int TG, int JP, int U>
@@ -2321,6 +2480,21 @@ hipError_t launch_pack_adapter(const uint16_t* A, const uint16_t* B, int K, int 
   const long total = (long)a_tiles(r) * 16 * K + (long)rank_pad(r) * N;
   const int grid = (int)std::min<long>((total + 255) / 256, 4096);
   hipLaunchKernelGGL(k_pack_adapter, dim3(grid), dim3(256), 0, s, A, B, K, N, r, At, Bt);
+  return hipGetLastError();
+}
+
+hipError_t launch_merged(const uint16_t* x, int T, int K, int N, int fmt, const uint8_t* wq, const void* wscale,
+                         const int* ids, const uint64_t* A_rows, const uint64_t* B_ptrs, const int* ranks,
+                         const float* scales, int n_ad, int r_lim, uint16_t* y, hipStream_t s) {
+  MergedParams p{};
+  p.x = x; p.T = T; p.K = K; p.N = N; p.fmt = fmt; p.wq = wq;
+  p.ws_fp8 = (fmt == LORA_W_FP8_E4M3) ? reinterpret_cast<const float*>(wscale) : nullptr;
+  p.ws_fp4 = (fmt == LORA_W_MXFP4_E2M1) ? reinterpret_cast<const uint8_t*>(wscale) : nullptr;
+  p.ids = ids; p.A_rows = A_rows; p.B_ptrs = B_ptrs; p.ranks = ranks; p.scales = scales;
+  p.n_ad = n_ad; p.r_lim = r_lim; p.y = y;
+  const dim3 grid(N / 16, (T + 15) / 16);
+  if (fmt == LORA_W_FP8_E4M3) hipLaunchKernelGGL(k_merged<LORA_W_FP8_E4M3>, grid, dim3(256), 0, s, p);
+  else hipLaunchKernelGGL(k_merged<LORA_W_MXFP4_E2M1>, grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

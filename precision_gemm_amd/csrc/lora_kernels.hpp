@@ -141,6 +141,10 @@ hipError_t launch_quant_build(const uint16_t* x, int T, int K, uint8_t* xq, uint
                               int* seg, int* sorted, int* err, hipStream_t s);
 hipError_t launch_shrink(const LayerPlan& pl, hipStream_t stream, const ShrinkParams& sp);
 hipError_t launch_expand(const ExpandParams& p, hipStream_t s);
+// the per-token merged-weight layer (an alternative formulation to ablate against)
+hipError_t launch_merged(const uint16_t* x, int T, int K, int N, int fmt, const uint8_t* wq, const void* wscale,
+                         const int* ids, const uint64_t* A_rows, const uint64_t* B_ptrs, const int* ranks,
+                         const float* scales, int n_ad, int r_lim, uint16_t* y, hipStream_t s);
 // the standalone down-projection with an explicit configuration (tuning): TG token tiles and
 // JP rank tiles per inner step, U k-steps per prefetch buffer (compiled for TG, JP in
 // {1, 2, 4}, U in {1, 2}); one workgroup per item.  shrink_cfg_attr: the instance's registers

@@ -318,3 +318,33 @@ def gemm_lowp_lora_epilogue_noalloc(x: torch.Tensor, w: LowpWeight, seg: Segment
         g(ad, "A_ptrs"), g(ad, "B_ptrs"), g(ad, "ranks"), g(ad, "scales"), n, rm,
         _ptr(y), flags, _stream()))
     return y
+
+
+def adapter_rows(ad: Adapters) -> tuple:
+    """A_a as bf16 [K, rank_pad(r_a)] row-major per adapter (zero columns past r_a) and the
+    device array of their addresses: the A operand of lora_merged_layer.  A layout copy."""
+    rows = []
+    for a in ad.A:
+        K, r = a.shape
+        t = torch.zeros((K, rank_pad(r)), dtype=torch.bfloat16, device=a.device)
+        t[:, :r].copy_(a)
+        rows.append(t)
+    ptrs = torch.tensor([t.data_ptr() for t in rows], dtype=torch.int64, device=ad.scales.device)
+    return rows, ptrs
+
+
+def merged_layer(x: torch.Tensor, w_rowmajor: LowpWeight, adapter_id: torch.Tensor, ad: Adapters, a_rows_ptrs,
+                 y: torch.Tensor | None = None) -> torch.Tensor:
+    """The per-token merged-weight layer (lora_merged_layer): W in its row-major form, A rows
+    from :func:`adapter_rows`, B_a^T from the adapter set."""
+    _dev(x, "x", torch.bfloat16)
+    if w_rowmajor.packed:
+        raise ValueError("the merged-weight layer reads W in its row-major form")
+    T, K = x.shape
+    N = w_rowmajor.N
+    if y is None:
+        y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    check("lora_merged_layer", lib().lora_merged_layer(
+        _ptr(x), T, K, N, _FMT[w_rowmajor.fmt], _ptr(w_rowmajor.q), _ptr(w_rowmajor.scale), _ptr(adapter_id),
+        _ptr(a_rows_ptrs), _ptr(ad.B_ptrs), _ptr(ad.ranks), _ptr(ad.scales), ad.n, ad.r_max, _ptr(y), _stream()))
+    return y
