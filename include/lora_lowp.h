@@ -307,6 +307,60 @@ lora_status gemm_lowp_lora_epilogue_noalloc(const uint16_t* x, int32_t T, int32_
                                             int32_t n_adapters, int32_t r_max,
                                             uint16_t* y, uint32_t flags, void* stream);
 
+/* ---- Backward: the adapters train on the frozen low-precision base ----
+ * The "EpiLoRA" abstract has the LoRA trainer compute on the serving engine's FP8 weights,
+ * with no 16-bit copy of W, and keep activations in 16 bits.  For the 16-bit-activation
+ * layer y[t] = x[t] W_d + s_a (x[t] A_a) B_a (W_d the dequantised W, frozen; A_a, B_a
+ * trained; s_a fixed) and the gradient dY of a loss with respect to y, the chain rule over
+ * each adapter's tokens R_a (its segment, "Punica" README, Overview) gives
+ *     u[t]  = dY[t] B_a^T,            dX[t] = dY[t] W_d^T + s_a u[t] A_a^T,
+ *     dA_a  = s_a sum_{t in R_a} x[t]^T u[t],   dB_a = s_a sum_{t in R_a} t_a[t]^T dY[t],
+ * with t_a[t] = x[t] A_a the forward's down-projection.  FP8 base only (MXFP4:
+ * LORA_ERR_UNSUPPORTED). */
+
+/* W^T in the packed form lora_backward reads, from the row-major FP8 codes q uint8 [N][K]:
+ * tiles of 16 rows k by 64 channels n, 1 KB each, tile (kt, ns) at byte
+ * ((kt (N/64) + ns) 64 + l) 16 for lane l = 16 g + i, whose 16 bytes hold the codes of
+ * W[64 ns + 16 g + e][16 kt + i], e = 0 .. 15.  An 8-bit copy made once, offline (the channel
+ * scales stay as they are).  N % 128 == 0, K % 128 == 0; qt 16-byte aligned; not in place. */
+lora_status lora_pack_weight_t(int32_t w_fmt, const uint8_t* q, int32_t N, int32_t K, uint8_t* qt, void* stream);
+
+/* Pack one adapter for lora_backward from A bf16 [K][r] and B bf16 [r][N] row-major:
+ *   Bop: B_a in bf16 MFMA operand order over N -- the layout lora_pack_adapter gives A, with
+ *        N in place of K: element (j, n) at ((((j/16) (N/64) + n/64) 2 + (n/8)%2) 64 +
+ *        16 ((n/16)%4) + j%16) 8 + n%8, 16 ceil(r/16) N values;
+ *   Ar:  A_a as bf16 [K][rank_pad(r)] row-major.
+ * Padding ranks are zero.  1 <= r <= 64, N % 64 == 0; Bop and Ar 16-byte aligned; no buffer
+ * may overlap another.  Like lora_pack_adapter, once per adapter (after each update of it). */
+lora_status lora_pack_adapter_bwd(const uint16_t* A, const uint16_t* B, int32_t K, int32_t N, int32_t r,
+                                  uint16_t* Bop, uint16_t* Ar, void* stream);
+
+/* Gradients of the layer above with respect to x, A_a and B_a.
+ *  - x bf16 [T][K], dy bf16 [T][N], t float [T][r_max] (the forward's down-projection, as
+ *    lora_shrink or gemm_lowp_lora_epilogue write it; columns j >= r_a are not read);
+ *  - wt_q: W^T packed by lora_pack_weight_t, w_scale float [N] (the FP8 channel scales);
+ *  - adapter_id int32 [T], seg_indptr / sorted_tok from lora_build_segments;
+ *  - Bop_ptrs / Ar_ptrs: per adapter, device addresses of Bop and Ar (lora_pack_adapter_bwd);
+ *  - outputs: dx bf16 [T][K] (round to nearest even); u float [T][r_max] (dY B_a^T, with the
+ *    layout of t); per adapter dA_a float [K][r_a] and dB_a float [r_a][N] row-major at the
+ *    addresses in dA_ptrs / dB_ptrs, written, not accumulated into (zero for an adapter
+ *    without tokens);
+ *  - status: device int32 or NULL; bit 1 is OR-ed in when an adapter with tokens has a rank
+ *    outside [1, r_max] (its dA_a and dB_a are not written and its tokens get dY W_d^T only).
+ * Arithmetic: dY W_d^T on bf16 MFMA with W widened to bf16 as code x channel scale (round to
+ * nearest even: the dequantised weight in 16 bits) and fp32 accumulation; u by the forward's
+ * down-projection kernel (exact bf16 products, fp32 sums); the fp32 factors u, t of the
+ * adapter products enter bf16 MFMAs as two bf16 terms each (about 17 bits).  Bitwise
+ * deterministic.  Tokens whose adapter id is outside [0, n_adapters) get dY W_d^T only.
+ * Limits: T <= 65536 (T == 0 zero-fills the dA_a and dB_a), K % 128 == 0, N % 128 == 0,
+ * 1 <= r_max <= 64; x, dy, wt_q, w_scale, dx, u 16-byte aligned. */
+lora_status lora_backward(const uint16_t* x, const uint16_t* dy, const float* t, int32_t T, int32_t K, int32_t N,
+                          int32_t w_fmt, const uint8_t* wt_q, const float* w_scale, const int32_t* adapter_id,
+                          const int32_t* seg_indptr, const int32_t* sorted_tok, const uint64_t* Bop_ptrs,
+                          const uint64_t* Ar_ptrs, const int32_t* ranks, const float* scales, int32_t n_adapters,
+                          int32_t r_max, uint16_t* dx, float* u, const uint64_t* dA_ptrs, const uint64_t* dB_ptrs,
+                          int32_t* status, void* stream);
+
 /* Device-side status word of the layer calls on this workspace since it was last
  * initialised (bits accumulate): copies one int32 to *status_dev (device pointer) on
  * `stream`.  0 = fine; bit 0 = a bounded wait in the fused launch gave up (the output

@@ -457,6 +457,80 @@ lora_status lora_pack_adapter(const uint16_t* A, const uint16_t* B, int32_t K, i
   return launch_pack_adapter(A, B, K, N, r, At, Bt, as_stream(stream)) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
+lora_status lora_pack_weight_t(int32_t w_fmt, const uint8_t* q, int32_t N, int32_t K, uint8_t* qt, void* stream) {
+  if (w_fmt != LORA_W_FP8_E4M3 && w_fmt != LORA_W_MXFP4_E2M1) return LORA_ERR_INVALID_ARG;
+  if (N <= 0 || K <= 0) return LORA_ERR_INVALID_ARG;
+  if (w_fmt != LORA_W_FP8_E4M3 || N % 128 != 0 || K % 128 != 0) return LORA_ERR_UNSUPPORTED;
+  if (!q || !qt || !aligned16(qt)) return LORA_ERR_INVALID_ARG;
+  const char *a = reinterpret_cast<const char*>(q), *b = reinterpret_cast<const char*>(qt);
+  const size_t n = (size_t)N * K;
+  if (a < b + n && b < a + n) return LORA_ERR_INVALID_ARG;  // not in place
+  return launch_pack_weight_t(q, N, K, qt, as_stream(stream)) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+lora_status lora_pack_adapter_bwd(const uint16_t* A, const uint16_t* B, int32_t K, int32_t N, int32_t r,
+                                  uint16_t* Bop, uint16_t* Ar, void* stream) {
+  if (K <= 0 || N <= 0 || r < 1) return LORA_ERR_INVALID_ARG;
+  if (r > MAX_RANK || N % 64 != 0) return LORA_ERR_UNSUPPORTED;
+  if (!A || !B || !Bop || !Ar || !aligned16(Bop) || !aligned16(Ar)) return LORA_ERR_INVALID_ARG;
+  const char *a0 = reinterpret_cast<const char*>(A), *b0 = reinterpret_cast<const char*>(B);
+  const char *o0 = reinterpret_cast<const char*>(Bop), *p0 = reinterpret_cast<const char*>(Ar);
+  const size_t na = (size_t)K * r * 2, nb = (size_t)N * r * 2;
+  const size_t nop = (size_t)a_tiles(r) * 16 * N * 2, nar = (size_t)K * rank_pad(r) * 2;
+  auto overlap = [](const char* x, size_t nx, const char* y, size_t ny) { return x < y + ny && y < x + nx; };
+  if (overlap(a0, na, o0, nop) || overlap(a0, na, p0, nar) || overlap(b0, nb, o0, nop) || overlap(b0, nb, p0, nar) ||
+      overlap(o0, nop, p0, nar))
+    return LORA_ERR_INVALID_ARG;  // not in place
+  return launch_pack_adapter_bwd(A, B, K, N, r, Bop, Ar, as_stream(stream)) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+lora_status lora_backward(const uint16_t* x, const uint16_t* dy, const float* t, int32_t T, int32_t K, int32_t N,
+                          int32_t w_fmt, const uint8_t* wt_q, const float* w_scale, const int32_t* adapter_id,
+                          const int32_t* seg_indptr, const int32_t* sorted_tok, const uint64_t* Bop_ptrs,
+                          const uint64_t* Ar_ptrs, const int32_t* ranks, const float* scales, int32_t n_adapters,
+                          int32_t r_max, uint16_t* dx, float* u, const uint64_t* dA_ptrs, const uint64_t* dB_ptrs,
+                          int32_t* status, void* stream) {
+  if (w_fmt != LORA_W_FP8_E4M3 && w_fmt != LORA_W_MXFP4_E2M1) return LORA_ERR_INVALID_ARG;
+  if (T < 0 || K <= 0 || N <= 0) return LORA_ERR_INVALID_ARG;
+  if (w_fmt != LORA_W_FP8_E4M3 || T > 65536 || K % 128 != 0 || N % 128 != 0) return LORA_ERR_UNSUPPORTED;
+  lora_status st = check_adapters(n_adapters, r_max);
+  if (st != LORA_OK) return st;
+  if (!ranks || !scales || !dA_ptrs || !dB_ptrs) return LORA_ERR_INVALID_ARG;
+  const hipStream_t s = as_stream(stream);
+  BwdGradParams gp{};
+  gp.x = x; gp.dy = dy; gp.u = u; gp.t = t;
+  gp.T = T; gp.K = K; gp.N = N; gp.r_lim = r_max;
+  gp.seg_indptr = seg_indptr; gp.sorted_tok = sorted_tok; gp.empty = (T == 0);
+  gp.ranks = ranks; gp.scales = scales; gp.n_ad = n_adapters;
+  gp.dA_ptrs = dA_ptrs; gp.dB_ptrs = dB_ptrs;
+  gp.nkb = K / 128; gp.nnb = N / 128; gp.status = status;
+  if (T == 0)  // no tokens: zero gradients
+    return launch_bwd_grad(gp, s) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+  if (!x || !dy || !t || !wt_q || !w_scale || !adapter_id || !seg_indptr || !sorted_tok || !Bop_ptrs || !Ar_ptrs ||
+      !dx || !u)
+    return LORA_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(dy) || !aligned16(wt_q) || !aligned16(w_scale) || !aligned16(dx) || !aligned16(u))
+    return LORA_ERR_INVALID_ARG;
+  // u = dY B_a^T: the forward's down-projection kernel over N, with B_a in A_a's place
+  const LayerPlan pl = make_plan(T, N, 64, n_adapters, r_max, LORA_W_FP8_E4M3, /*fused=*/false);
+  ShrinkParams sp{};
+  sp.x = dy; sp.T = T; sp.K = N;
+  sp.seg_indptr = seg_indptr; sp.sorted_tok = sorted_tok;
+  sp.A_ptrs = Bop_ptrs; sp.ranks = ranks; sp.n_ad = n_adapters; sp.r_max = rank_pad(r_max); sp.r_lim = r_max;
+  sp.ids = nullptr;
+  sp.t_out = u; sp.t_tag = nullptr;
+  sp.tblk = pl.s_tblk; sp.n_tblk = pl.s_ntblk; sp.n_jg = pl.s_njg; sp.jper = pl.s_jper;
+  sp.kparts = pl.s_kparts; sp.kpart_len = pl.s_kpart_len;
+  if (launch_shrink(pl, s, sp) != hipSuccess) return LORA_ERR_HIP;
+  if (launch_bwd_grad(gp, s) != hipSuccess) return LORA_ERR_HIP;
+  BwdDxParams dp{};
+  dp.dy = dy; dp.wt = wt_q; dp.wsc = w_scale; dp.T = T; dp.K = K; dp.N = N;
+  dp.u = u; dp.r_lim = r_max; dp.ids = adapter_id; dp.Ar_ptrs = Ar_ptrs; dp.ranks = ranks; dp.scales = scales;
+  dp.n_ad = n_adapters; dp.dx = dx;
+  dp.n_tb = ceil_div(T, 128); dp.n_kb = ceil_div(K, 256);
+  return launch_bwd_dx(dp, s) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
 lora_status lora_shrink_configured(const uint16_t* x, int32_t T, int32_t K, const int32_t* seg_indptr,
                                    const int32_t* sorted_tok, const uint64_t* A_ptrs, const int32_t* ranks,
                                    int32_t n_adapters, int32_t r_max, float* t, const int32_t* config, void* stream) {

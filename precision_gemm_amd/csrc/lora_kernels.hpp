@@ -161,6 +161,47 @@ hipError_t launch_pack_weight(int fmt, const uint8_t* q, const uint8_t* sc, int 
 // `s` whenever it differs from the previous call's on this device).
 constexpr size_t SCRATCH_BYTES = (size_t)LORA_NOALLOC_SCRATCH_BYTES;
 hipError_t scratch_acquire(hipStream_t s, size_t tag_lo, size_t tag_hi, void** out);
+// Backward (lora_backward.hip).  dX = dY W_d^T + s_a u A_a^T: 128 x 256 tiles, W^T packed
+// by launch_pack_weight_t, A_a rows [K][rank_pad(r_a)] (launch_pack_adapter_bwd).
+struct BwdDxParams {
+  const uint16_t* dy;      // bf16 [T][N]
+  const uint8_t* wt;       // W^T FP8 codes, packed
+  const float* wsc;        // channel scales [N]
+  int T, K, N;
+  const float* u;          // [T][r_lim]: dY B_a^T
+  int r_lim;
+  const int* ids;
+  const uint64_t* Ar_ptrs;
+  const int* ranks;
+  const float* scales;
+  int n_ad;
+  uint16_t* dx;            // bf16 [T][K]
+  int n_tb, n_kb;          // 128-row and 256-column blocks
+};
+// dA_a = s_a X_a^T U_a [K][r_a] and dB_a = s_a T_a^T dY_a [r_a][N]: one workgroup per
+// (adapter, 128 rows of K) and (adapter, 128 columns of N).
+struct BwdGradParams {
+  const uint16_t* x;       // bf16 [T][K]
+  const uint16_t* dy;      // bf16 [T][N]
+  const float* u;          // [T][r_lim]
+  const float* t;          // [T][r_lim]: the forward's down-projection
+  int T, K, N, r_lim;
+  const int* seg_indptr;
+  const int* sorted_tok;
+  int empty;               // no tokens: every gradient is zero (segments not read)
+  const int* ranks;
+  const float* scales;
+  int n_ad;
+  const uint64_t* dA_ptrs;
+  const uint64_t* dB_ptrs;
+  int nkb, nnb;
+  int* status;             // bit 1 OR-ed in for an adapter with tokens and a rank outside [1, r_lim]
+};
+hipError_t launch_pack_weight_t(const uint8_t* q, int N, int K, uint8_t* qt, hipStream_t s);
+hipError_t launch_pack_adapter_bwd(const uint16_t* A, const uint16_t* B, int K, int N, int r, uint16_t* Bop,
+                                   uint16_t* Ar, hipStream_t s);
+hipError_t launch_bwd_dx(const BwdDxParams& p, hipStream_t s);
+hipError_t launch_bwd_grad(const BwdGradParams& p, hipStream_t s);
 hipError_t launch_pack_adapter(const uint16_t* A, const uint16_t* B, int K, int N, int r, uint16_t* At, uint16_t* Bt,
                                hipStream_t s);
 

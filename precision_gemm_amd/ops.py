@@ -348,3 +348,75 @@ def merged_layer(x: torch.Tensor, w_rowmajor: LowpWeight, adapter_id: torch.Tens
         _ptr(x), T, K, N, _FMT[w_rowmajor.fmt], _ptr(w_rowmajor.q), _ptr(w_rowmajor.scale), _ptr(adapter_id),
         _ptr(a_rows_ptrs), _ptr(ad.B_ptrs), _ptr(ad.ranks), _ptr(ad.scales), ad.n, ad.r_max, _ptr(y), _stream()))
     return y
+
+
+# ---- backward: the adapters train on the frozen FP8 base (see lora_backward) ----
+
+def pack_weight_t(w: LowpWeight) -> torch.Tensor:
+    """W^T in the packed form lora_backward reads (lora_pack_weight_t), from the row-major
+    FP8 codes of ``w``; returns uint8 [N*K].  An 8-bit copy made once; the channel scales of
+    ``w`` serve as they are."""
+    if w.packed:
+        raise ValueError("lora_pack_weight_t reads W in its row-major form")
+    _dev(w.q, "q", torch.uint8)
+    qt = torch.empty(w.N * w.K, dtype=torch.uint8, device=w.q.device)
+    check("lora_pack_weight_t", lib().lora_pack_weight_t(_FMT[w.fmt], _ptr(w.q), w.N, w.K, _ptr(qt), _stream()))
+    return qt
+
+
+@dataclass
+class BackwardAdapters:
+    """The backward forms of an adapter set (lora_pack_adapter_bwd): ``Bop[a]`` bf16
+    [a_rows(r_a), N] (B_a in operand order over N) and ``Ar[a]`` bf16 [K, rank_pad(r_a)], and
+    the device arrays of their addresses.  Re-pack after the adapters change."""
+
+    Bop: list
+    Ar: list
+    Bop_ptrs: torch.Tensor
+    Ar_ptrs: torch.Tensor
+
+
+def pack_adapters_bwd(ad: Adapters) -> BackwardAdapters:
+    Bop, Ar = [], []
+    for A, B in zip(ad.A, ad.B):
+        K, r = A.shape
+        N = B.shape[1]
+        bo = torch.empty((a_rows(r), N), dtype=torch.bfloat16, device=A.device)
+        ar = torch.empty((K, rank_pad(r)), dtype=torch.bfloat16, device=A.device)
+        check("lora_pack_adapter_bwd", lib().lora_pack_adapter_bwd(_ptr(A), _ptr(B), K, N, r, _ptr(bo), _ptr(ar),
+                                                                   _stream()))
+        Bop.append(bo)
+        Ar.append(ar)
+    dev = ad.scales.device
+    return BackwardAdapters(Bop, Ar, torch.tensor([b.data_ptr() for b in Bop], dtype=torch.int64, device=dev),
+                            torch.tensor([a.data_ptr() for a in Ar], dtype=torch.int64, device=dev))
+
+
+def lora_backward(x: torch.Tensor, dy: torch.Tensor, t: torch.Tensor, wt: torch.Tensor, w_scale: torch.Tensor,
+                  seg: Segments, ad: Adapters, bw: BackwardAdapters, *, dx=None, u=None, dA=None, dB=None,
+                  status: torch.Tensor | None = None):
+    """Gradients of the 16-bit-activation layer (lora_backward): returns ``(dx, u, dA, dB)``
+    with dx bf16 [T, K], u float32 [T, r_max], dA[a] float32 [K, r_a], dB[a] float32 [r_a, N].
+    ``wt`` from :func:`pack_weight_t`, ``w_scale`` the FP8 channel scales, ``t`` the forward's
+    down-projection.  Output buffers may be passed in."""
+    _dev(x, "x", torch.bfloat16)
+    _dev(dy, "dy", torch.bfloat16)
+    T, K = x.shape
+    N = dy.shape[1]
+    dev = x.device
+    if dx is None:
+        dx = torch.empty((T, K), dtype=torch.bfloat16, device=dev)
+    if u is None:
+        u = torch.empty((T, ad.r_max), dtype=torch.float32, device=dev)
+    rk = [int(a.shape[1]) for a in ad.A]
+    if dA is None:
+        dA = [torch.empty((K, r), dtype=torch.float32, device=dev) for r in rk]
+    if dB is None:
+        dB = [torch.empty((r, N), dtype=torch.float32, device=dev) for r in rk]
+    dA_ptrs = torch.tensor([m.data_ptr() for m in dA], dtype=torch.int64, device=dev)
+    dB_ptrs = torch.tensor([m.data_ptr() for m in dB], dtype=torch.int64, device=dev)
+    check("lora_backward", lib().lora_backward(
+        _ptr(x), _ptr(dy), _ptr(t), T, K, N, LORA_W_FP8_E4M3, _ptr(wt), _ptr(w_scale), _ptr(seg.adapter_id),
+        _ptr(seg.seg_indptr), _ptr(seg.sorted_tok), _ptr(bw.Bop_ptrs), _ptr(bw.Ar_ptrs), _ptr(ad.ranks),
+        _ptr(ad.scales), ad.n, ad.r_max, _ptr(dx), _ptr(u), _ptr(dA_ptrs), _ptr(dB_ptrs), _ptr(status), _stream()))
+    return dx, u, dA, dB

@@ -230,3 +230,40 @@ def test_shrink_configured_validation(L):
     out = (ctypes.c_int32 * 3)()
     assert L.lora_shrink_config_info(3, 1, 1, out) == UNSUPPORTED
     assert L.lora_shrink_config_info(1, 1, 1, None) == INVALID
+
+
+def _bwd(L, **kw):
+    a = dict(x=FAKE, dy=FAKE, t=FAKE, T=64, K=4096, N=4096, fmt=0, wt=FAKE, ws=FAKE, ids=FAKE, seg=FAKE, srt=FAKE,
+             Bop=FAKE, Ar=FAKE, rk=FAKE, sc=FAKE, n=8, r=64, dx=FAKE, u=FAKE, dA=FAKE, dB=FAKE, status=NULL)
+    a.update(kw)
+    return L.lora_backward(a["x"], a["dy"], a["t"], a["T"], a["K"], a["N"], a["fmt"], a["wt"], a["ws"], a["ids"],
+                           a["seg"], a["srt"], a["Bop"], a["Ar"], a["rk"], a["sc"], a["n"], a["r"], a["dx"], a["u"],
+                           a["dA"], a["dB"], a["status"], NULL)
+
+
+def test_backward_validation(L):
+    """lora_backward and its packs: every limit of the header returns its status before
+    anything is enqueued (the pointers here are fake)."""
+    assert _bwd(L, fmt=1) == UNSUPPORTED          # MXFP4 base: not in the backward
+    assert _bwd(L, fmt=2) == INVALID
+    assert _bwd(L, K=4096 + 64) == UNSUPPORTED
+    assert _bwd(L, N=4096 + 64) == UNSUPPORTED    # the contraction of dX runs in 128-channel pairs of steps
+    assert _bwd(L, T=65537) == UNSUPPORTED
+    assert _bwd(L, T=-1) == INVALID
+    assert _bwd(L, r=65) == UNSUPPORTED
+    assert _bwd(L, n=0) == INVALID
+    assert _bwd(L, dA=NULL) == INVALID
+    for name in ("x", "dy", "t", "wt", "ws", "ids", "seg", "srt", "Bop", "Ar", "dx", "u"):
+        assert _bwd(L, **{name: NULL}) == INVALID, name
+    for name in ("x", "dy", "wt", "ws", "dx", "u"):
+        assert _bwd(L, **{name: MISALIGNED}) == INVALID, name
+    assert L.lora_pack_weight_t(1, FAKE, 4096, 4096, ctypes.c_void_p(0x4000000), NULL) == UNSUPPORTED
+    assert L.lora_pack_weight_t(0, FAKE, 4096 + 64, 4096, ctypes.c_void_p(0x4000000), NULL) == UNSUPPORTED
+    assert L.lora_pack_weight_t(0, FAKE, 4096, 4096, FAKE, NULL) == INVALID           # in place
+    assert L.lora_pack_weight_t(0, FAKE, 4096, 4096, MISALIGNED, NULL) == INVALID
+    A, B, O, R = (ctypes.c_void_p(0x1000000 * i) for i in (1, 2, 3, 4))
+    assert L.lora_pack_adapter_bwd(A, B, 4096, 4096, 65, O, R, NULL) == UNSUPPORTED
+    assert L.lora_pack_adapter_bwd(A, B, 4096, 4096 + 32, 8, O, R, NULL) == UNSUPPORTED
+    assert L.lora_pack_adapter_bwd(A, B, 4096, 4096, 0, O, R, NULL) == INVALID
+    assert L.lora_pack_adapter_bwd(A, B, 4096, 4096, 8, A, R, NULL) == INVALID         # not in place
+    assert L.lora_pack_adapter_bwd(A, B, 4096, 4096, 8, MISALIGNED, R, NULL) == INVALID

@@ -33,7 +33,7 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make", "make_custom", "bf16_bits", "bf16_to_f32"]
+__all__ = ["Workload", "WORKLOADS", "make", "make_custom", "grad_output", "bf16_bits", "bf16_to_f32"]
 
 
 @dataclass
@@ -161,6 +161,13 @@ def _draw(rng, name, T, K, N, fmt, ranks, ids, scale, seed, x_std, w_std, a_std,
     if zero_b:
         B = [np.zeros_like(b) for b in B]
     return Workload(name, T, K, N, fmt, x, w_q, w_s, A, B, ranks, scale, ids, seed)
+
+
+def grad_output(T: int, N: int, seed: int, std: float = 1.0) -> np.ndarray:
+    """A seeded gradient dY of a loss with respect to the layer output, bf16 bits [T, N],
+    drawn N(0, std) (the backward's input besides the forward's)."""
+    rng = np.random.default_rng(seed)
+    return bf16_bits(_normal(rng, (T, N), std))
 
 
 WORKLOADS = {
