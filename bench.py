@@ -3,7 +3,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill] [--sets S] [--act mxfp8|bf16]
 
 (``--workload decoder_layer``: a step is one decoder layer's four LoRA projections chained on
-one segment build; see ``decoder_layer``.)
+one segment build; see ``decoder_layer``.  ``--backward``: a step is one call of the layer's
+backward, lora_backward; see ``backward``.)
 
 A step is one pass of the whole hot path over one batch: one fused layer call
 (gemm_lowp_lora_epilogue with LORA_FUSE_SHRINK: the down-projection and the GEMM with its
@@ -290,6 +291,114 @@ def ablation_merged(args, wl):
     print(json.dumps(out), flush=True)
 
 
+def backward_flops(wl):
+    """Algorithmic FLOPs of one backward call: dX = dY W_d^T (2TKN) and, per token, the
+    adapter products u = dY B_a^T, s u A_a^T, and its shares of dA_a and dB_a (2 r_a each of
+    N, K, K, N)."""
+    r_tok = wl.ranks[np.asarray(wl.ids)]
+    return 2.0 * wl.T * wl.K * wl.N + float(np.sum(4.0 * r_tok * (wl.K + wl.N)))
+
+
+def backward(args, wl):
+    """A step is one lora_backward call (u, dA and dB, dX) on the workload's batch with a
+    seeded dY; K calls in one HIP graph, timed with HIP events on the launch stream; two input
+    sets alternate.  Parity of dX on sampled rows against the backward oracle."""
+    import torch
+    import precision_gemm_amd as P
+    import workloads
+    from workloads.device import bf16_tensor, upload
+    from oracle import backward as BW
+    from oracle.layer import LowpWeight as OW
+    if wl.fmt != "fp8":
+        print(json.dumps({"error": "the backward runs on an FP8 base only"}))
+        sys.exit(2)
+    dy_bits = workloads.grad_output(wl.T, wl.N, wl.seed + 1000)
+    S = []
+    for _ in range(2):
+        x, w, ad, ids = upload(wl)
+        q = torch.from_numpy(np.ascontiguousarray(wl.w_q)).cuda()
+        sc = torch.from_numpy(np.ascontiguousarray(wl.w_scale)).cuda()
+        wt = P.pack_weight_t(P.LowpWeight("fp8", q, sc))
+        del q
+        bw = P.pack_adapters_bwd(ad)
+        seg = P.build_segments(ids, ad.n)
+        t = P.shrink(x, seg, ad)                       # the forward's down-projection
+        dy = bf16_tensor(dy_bits)
+        dx = torch.empty((wl.T, wl.K), dtype=torch.bfloat16, device="cuda")
+        u = torch.empty((wl.T, ad.r_max), dtype=torch.float32, device="cuda")
+        S.append(dict(x=x, dy=dy, t=t, wt=wt, sc=sc, seg=seg, ad=ad, bw=bw, dx=dx, u=u,
+                      grads=P.alloc_grads(ad, wl.K, wl.N)))
+    torch.cuda.synchronize()
+
+    def step(i):
+        d = S[i % 2]
+        P.lora_backward(d["x"], d["dy"], d["t"], d["wt"], d["sc"], d["seg"], d["ad"], d["bw"], dx=d["dx"],
+                        u=d["u"], grads=d["grads"])
+
+    step(0)
+    torch.cuda.synchronize()
+    rows = np.arange(wl.T) if wl.T <= 256 else np.linspace(0, wl.T - 1, 128).astype(int)
+    ref = BW.lora_backward(wl.x[rows], OW(wl.fmt, wl.w_q, wl.w_scale), wl.A, wl.B, wl.scale,
+                           np.asarray(wl.ids)[rows], dy_bits[rows])
+    dxg = S[0]["dx"].float().cpu().numpy().astype(np.float64)[rows]
+    dlt = dxg - ref["dx"]
+    parity = {"dx_max_rel": float(np.abs(dlt).max() / np.abs(ref["dx"]).max()),
+              "dx_frob_rel": float(np.linalg.norm(dlt) / np.linalg.norm(ref["dx"])), "rows_checked": int(len(rows))}
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(K):
+            step(i)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    total_s = time.perf_counter() - t0
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    call_us = e0.elapsed_time(e1) * 1e3 / K
+    flops = backward_flops(wl)
+    achieved = flops / (call_us * 1e-6) / 1e12
+    out = {
+        "metric": "µs per LoRA backward call (dX, dA, dB) and MFMA TFLOP/s", "value": round(total_s * 1e6 / K, 3),
+        "unit": "us/call", "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": total_s * 1e3 / K,
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16xfp8", "data": "synthetic",
+        "config": {"workload": args.workload + "_backward", "T": wl.T, "K": wl.K, "N": wl.N, "w_format": wl.fmt,
+                   "adapters": wl.n_adapters, "ranks": sorted(set(int(r) for r in wl.ranks)),
+                   "timing": "hip graph of K steps"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None, "call_us": call_us,
+                     "per_call_flops": flops,
+                     "kernel": "backward call: down-projection of dY (u) + k_bwd_grad (dA, dB) + k_bwd_dx"},
+        "parity": parity, "kernel_sha": kernel_source_sha(),
+    }
+    if not args.no_cpu:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
+        sub = np.arange(wl.T) if wl.T <= 256 else np.linspace(0, wl.T - 1, 512).astype(int)
+        runs, c0 = 0, time.perf_counter()
+        while True:
+            BW.lora_backward(wl.x[sub], OW(wl.fmt, wl.w_q, wl.w_scale), wl.A, wl.B, wl.scale, np.asarray(wl.ids)[sub],
+                             dy_bits[sub])
+            runs += 1
+            el = time.perf_counter() - c0
+            if el >= 12.0 or runs >= 50:
+                break
+        out["cpu_baseline"] = {"value": el / runs * (wl.T / len(sub)) * 1e6, "unit": "us/call", "cores": int(cores),
+                               "kind": "oracle",
+                               "sample": f"{runs} backward oracle run(s) on {len(sub)} of {wl.T} tokens, scaled by "
+                                         f"T/{len(sub)} ({el:.1f} s)"}
+    print(json.dumps(out), flush=True)
+
+
 def stored_traffic(workload: str, sha: str):
     p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(p):
@@ -318,6 +427,8 @@ def main():
     ap.add_argument("--ablation-merged", action="store_true",
                     help="instead of the layer call: time the per-token merged-weight layer (lora_merged_layer) "
                          "against the fused layer with 16-bit activations on the workload")
+    ap.add_argument("--backward", action="store_true",
+                    help="instead of the layer call: time the backward (lora_backward) on the workload (FP8 base)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="after the timed region, run three plain device copies of this many MiB (untimed): "
                          "the reference that scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -344,6 +455,9 @@ def main():
         return
     if args.ablation_merged:
         ablation_merged(args, wl)
+        return
+    if args.backward:
+        backward(args, wl)
         return
     a16 = args.act == "bf16"
     nbytes, flops = algorithmic(wl)

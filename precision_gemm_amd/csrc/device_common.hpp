@@ -26,9 +26,10 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 
 // two floats to bf16 (round to nearest even) in one word, lo in bits 0..15: the gfx950
 // conversion instruction (finite values as f32_to_bf16_rne; NaN stays a quiet NaN)
+// (one v_cvt_pk_bf16_f32: the vector conversion keeps both halves in one instruction)
 __device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
-  const __bf16 l = (__bf16)lo, h = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
 
 // ---------------------------------------------------------------------------------

@@ -503,7 +503,7 @@ lora_status lora_backward(const uint16_t* x, const uint16_t* dy, const float* t,
   gp.seg_indptr = seg_indptr; gp.sorted_tok = sorted_tok; gp.empty = (T == 0);
   gp.ranks = ranks; gp.scales = scales; gp.n_ad = n_adapters;
   gp.dA_ptrs = dA_ptrs; gp.dB_ptrs = dB_ptrs;
-  gp.nkb = K / 128; gp.nnb = N / 128; gp.status = status;
+  gp.nkb = K / 64; gp.nnb = N / 64; gp.status = status;
   if (T == 0)  // no tokens: zero gradients
     return launch_bwd_grad(gp, s) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
   if (!x || !dy || !t || !wt_q || !w_scale || !adapter_id || !seg_indptr || !sorted_tok || !Bop_ptrs || !Ar_ptrs ||
@@ -527,7 +527,7 @@ lora_status lora_backward(const uint16_t* x, const uint16_t* dy, const float* t,
   dp.dy = dy; dp.wt = wt_q; dp.wsc = w_scale; dp.T = T; dp.K = K; dp.N = N;
   dp.u = u; dp.r_lim = r_max; dp.ids = adapter_id; dp.Ar_ptrs = Ar_ptrs; dp.ranks = ranks; dp.scales = scales;
   dp.n_ad = n_adapters; dp.dx = dx;
-  dp.n_tb = ceil_div(T, 128); dp.n_kb = ceil_div(K, 256);
+  dp.n_tb = ceil_div(T, 64); dp.n_kb = ceil_div(K, 256);
   return launch_bwd_dx(dp, s) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 

@@ -119,13 +119,15 @@ __device__ __forceinline__ int wave_min(int v) {
 // ---------------------------------------------------------------------------------
 // dX = dY W_d^T + s_a u A_a^T
 //
-// Workgroup tile: 128 rows (tokens) x 256 columns (k), four waves of 128 x 64.  Per
-// 64-channel step: dY [128][64] bf16 staged in LDS (loaded a step ahead, double buffered);
-// each wave reads its four W^T tiles (1 KB of consecutive memory each) straight into
-// registers and widens them to bf16 as code x channel scale (rounded to nearest even: the
-// dequantised weight in 16 bits); two bf16 MFMAs per 16 x 16 block cover the 64 channels
-// (lane group g supplies channels 16 g .. 16 g + 7 to the first and 16 g + 8 .. 16 g + 15
-// to the second, the same assignment on both operands).
+// Workgroup tile: 64 rows (tokens) x 256 columns (k), four waves of 64 x 64, two workgroups
+// per CU (their barriers are independent, so one's loads, widening and waits overlap the
+// other's MFMAs).  Per 64-channel step: dY [64][64] bf16 and the step's channel scales staged
+// in LDS (loaded a step ahead, double buffered); each wave reads its four W^T tiles (1 KB of
+// consecutive memory each) straight into registers, a step ahead, and widens them to bf16 as
+// code x channel scale (rounded to nearest even: the dequantised weight in 16 bits); two
+// bf16 MFMAs per 16 x 16 block cover the 64 channels (lane group g supplies channels
+// 16 g .. 16 g + 7 to the first and 16 g + 8 .. 16 g + 15 to the second, the same assignment
+// on both operands).
 // Adapter term: the rows' s_a u[t] split into two bf16 terms and staged in LDS; for each
 // adapter present in the tile (in increasing id order) and each 32 ranks, two MFMAs per
 // block with the rows of other adapters zeroed and A_a rows [K][rank_pad] as the other
@@ -133,11 +135,13 @@ __device__ __forceinline__ int wave_min(int v) {
 // ---------------------------------------------------------------------------------
 
 constexpr int BX_RS = 144;              // LDS row stride (bytes): 64 bf16 + 16 bytes of bank offset
-constexpr int BX_BUF = 128 * BX_RS;     // one 128-row buffer
+constexpr int BX_ROWS = 64;             // rows of a workgroup tile
+constexpr int BX_BUF = BX_ROWS * BX_RS; // one staged step
 
-__global__ __launch_bounds__(256, 1) void k_bwd_dx(BwdDxParams p) {
+__global__ __launch_bounds__(256, 2) void k_bwd_dx(BwdDxParams p) {
   __shared__ __align__(16) uint8_t lds[2 * BX_BUF];
-  __shared__ int rid[128];
+  __shared__ __align__(16) float lsc[2 * 64];   // channel scales of the staged steps
+  __shared__ int rid[BX_ROWS];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, i = lane & 15, g = lane >> 4;
 
   // tile order: workgroup b runs on XCD b % 8; each XCD takes a contiguous run of tiles in
@@ -146,52 +150,63 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dx(BwdDxParams p) {
   int tile = blockIdx.x;
   if ((ntiles & 7) == 0) tile = (tile & 7) * (ntiles >> 3) + (tile >> 3);
   const int tb = tile / p.n_kb, kb = tile % p.n_kb;
-  const int t0 = 128 * tb, k0w = 256 * kb + 64 * w;
+  const int t0 = BX_ROWS * tb, k0w = 256 * kb + 64 * w;
   const int NI = p.N >> 6, nkt = p.K >> 4;
 
-  // dY staging: thread loads row srow + 32 q, 16-byte part spart (8 channels)
+  // dY staging: thread loads row srow + 32 q (q = 0, 1), 16-byte part spart (8 channels)
   const int srow = tid >> 3, spart = tid & 7;
-  const uint16_t* dyp[4];
+  const uint16_t* dyp[2];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) dyp[q] = p.dy + (long)min(t0 + srow + 32 * q, p.T - 1) * p.N + 8 * spart;
+  for (int q = 0; q < 2; ++q) dyp[q] = p.dy + (long)min(t0 + srow + 32 * q, p.T - 1) * p.N + 8 * spart;
   const uint8_t* wp[4];
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) wp[ct] = p.wt + ((long)min((k0w >> 4) + ct, nkt - 1) * NI * 64 + lane) * 16;
-  const float* scp = p.wsc + 16 * g;
 
-  uint4 sd[4], wc[4];
-  float4 sc[4];
+  auto load_dy = [&](uint4 (&d)[2], float4& sv, int st) {
+    sv = ldg16f(p.wsc + 64 * st + 4 * (tid & 15));
 #pragma unroll
-  for (int q = 0; q < 4; ++q) sd[q] = ldg16(dyp[q]);
+    for (int q = 0; q < 2; ++q) d[q] = ldg16(dyp[q] + 64 * st);
+  };
+  auto load_w = [&](uint4 (&wv)[4], int st) {
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) wc[ct] = ldg16(wp[ct]);
+    for (int ct = 0; ct < 4; ++ct) wv[ct] = ldg16(wp[ct] + (long)st * 1024);
+  };
+  auto store_dy = [&](const uint4 (&d)[2], const float4& sv, int buf) {
 #pragma unroll
-  for (int e = 0; e < 4; ++e) sc[e] = ldg16f(scp + 4 * e);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4*>(lds + (srow + 32 * q) * BX_RS + 16 * spart) = sd[q];
+    for (int q = 0; q < 2; ++q)
+      *reinterpret_cast<uint4*>(lds + buf * BX_BUF + (srow + 32 * q) * BX_RS + 16 * spart) = d[q];
+    // 16 threads per slot write the same value: no branch
+    *reinterpret_cast<float4*>(lsc + 64 * buf + 4 * (tid & 15)) = sv;
+  };
+
+  // W^T of a step is loaded a step ahead into one of two register sets used alternately (no
+  // register copies, which would wait for the loads): N / 64 steps, an even number
+  uint4 dn[2], wA[4], wB[4];
+  float4 sn;
+  load_dy(dn, sn, 0);
+  load_w(wA, 0);
+  store_dy(dn, sn, 0);
   __syncthreads();
 
-  v4f acc[8][4];
+  v4f acc[4][4];
 #pragma unroll
-  for (int tt = 0; tt < 8; ++tt)
+  for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) acc[tt][ct] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int it = 0; it < NI; ++it) {
-    // next step's loads (the last step reloads its own: uniform code, no branch)
-    const int nx = min(it + 1, NI - 1);
-    uint4 sdn[4], wn[4];
-    float4 scn[4];
+  auto step = [&](int it, const uint4 (&wc)[4], uint4 (&wn)[4]) {
+    const int nx = min(it + 1, NI - 1);  // the last step reloads itself: uniform code
+    load_dy(dn, sn, nx);
+    load_w(wn, nx);
+    __builtin_amdgcn_sched_barrier(0);  // the loads stay at the top: a whole step hides them
+    // W^T codes -> bf16 (code x channel scale, round to nearest even)
+    const float* ls = lsc + 64 * (it & 1) + 16 * g;
+    float s16[16];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) sdn[q] = ldg16(dyp[q] + 64 * nx);
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) wn[ct] = ldg16(wp[ct] + (long)nx * 1024);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) scn[e] = ldg16f(scp + 64 * nx + 4 * e);
-
-    // W^T codes -> bf16 (code x channel scale)
-    const float s16[16] = {sc[0].x, sc[0].y, sc[0].z, sc[0].w, sc[1].x, sc[1].y, sc[1].z, sc[1].w,
-                           sc[2].x, sc[2].y, sc[2].z, sc[2].w, sc[3].x, sc[3].y, sc[3].z, sc[3].w};
+    for (int e = 0; e < 4; ++e) {
+      const float4 v = *reinterpret_cast<const float4*>(ls + 4 * e);
+      s16[4 * e] = v.x; s16[4 * e + 1] = v.y; s16[4 * e + 2] = v.z; s16[4 * e + 3] = v.w;
+    }
     uint4 wb[4][2];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
@@ -212,7 +227,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dx(BwdDxParams p) {
     }
     const uint8_t* B0 = lds + (it & 1) * BX_BUF;
 #pragma unroll
-    for (int tt = 0; tt < 8; ++tt) {
+    for (int tt = 0; tt < 4; ++tt) {
       const uint8_t* ra = B0 + (16 * tt + i) * BX_RS + 32 * g;
       const uint4 a0 = lds16(ra), a1 = lds16(ra + 16);
 #pragma unroll
@@ -221,18 +236,16 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dx(BwdDxParams p) {
         acc[tt][ct] = mfma_bf16_16x16x32(a1, wb[ct][1], acc[tt][ct]);
       }
     }
-    uint8_t* B1 = lds + ((it + 1) & 1) * BX_BUF;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4*>(B1 + (srow + 32 * q) * BX_RS + 16 * spart) = sdn[q];
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) wc[ct] = wn[ct];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sc[e] = scn[e];
+    store_dy(dn, sn, (it + 1) & 1);
     __syncthreads();
+  };
+  for (int it = 0; it < NI; it += 2) {
+    step(it, wA, wB);
+    step(it + 1, wB, wA);
   }
 
   // ---- adapter term
-  if (tid < 128) {
+  if (tid < BX_ROWS) {
     const int t = t0 + tid;
     int a = -1;
     if (t < p.T) {
@@ -249,7 +262,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dx(BwdDxParams p) {
   __syncthreads();
   // s_a u[t] as two bf16 terms: hi in buffer 0, lo in buffer 1, [row][64 ranks]
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < 2; ++q) {
     const int row = srow + 32 * q;
     const int a = rid[row];
     float v[8];
@@ -274,10 +287,8 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dx(BwdDxParams p) {
   __syncthreads();
   int prev = -1;
   for (;;) {
-    const int c0 = rid[lane], c1 = rid[lane + 64];
-    int m = 0x7fffffff;
-    if (c0 > prev) m = c0;
-    if (c1 > prev && c1 < m) m = c1;
+    const int c = rid[lane];
+    int m = c > prev ? c : 0x7fffffff;
     m = wave_min(m);
     if (m == 0x7fffffff) break;
     const int a = __builtin_amdgcn_readfirstlane(m);
@@ -294,7 +305,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dx(BwdDxParams p) {
         bop[ct] = keep_bf16(ldg16(Ar + (long)k * rp + off), r - jj);
       }
 #pragma unroll
-      for (int tt = 0; tt < 8; ++tt) {
+      for (int tt = 0; tt < 4; ++tt) {
         const int row = 16 * tt + i;
         const bool mine = rid[row] == a;
         const int o = row * BX_RS + 64 * rs + 16 * g;
@@ -310,24 +321,24 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dx(BwdDxParams p) {
   }
   __syncthreads();
 
-  // ---- bf16 stores through LDS, 64 rows per pass: wave w's region holds its 64 x 64 block
-  uint8_t* reg = lds + w * (64 * BX_RS);
+  // ---- bf16 stores through LDS, 32 rows per pass: wave w's region holds its 32 x 64 block
+  uint8_t* reg = lds + w * (32 * BX_RS);
 #pragma unroll
   for (int ph = 0; ph < 2; ++ph) {
 #pragma unroll
-    for (int tq = 0; tq < 4; ++tq)
+    for (int tq = 0; tq < 2; ++tq)
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
         for (int v = 0; v < 4; ++v)
           *reinterpret_cast<uint16_t*>(reg + (16 * tq + 4 * g + v) * BX_RS + 2 * (16 * ct + i)) =
-              (uint16_t)f32_to_bf16_rne(acc[4 * ph + tq][ct][v]);
+              (uint16_t)f32_to_bf16_rne(acc[2 * ph + tq][ct][v]);
     __syncthreads();
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int idx = lane + 64 * c;           // 64 rows x 8 parts of 16 bytes
+    for (int c = 0; c < 4; ++c) {
+      const int idx = lane + 64 * c;           // 32 rows x 8 parts of 16 bytes
       const int row = idx >> 3, part = idx & 7;
-      const int t = t0 + 64 * ph + row, k = k0w + 8 * part;
+      const int t = t0 + 32 * ph + row, k = k0w + 8 * part;
       const uint4 v = lds16(reg + row * BX_RS + 16 * part);
       if (t < p.T && k < p.K) *reinterpret_cast<uint4*>(p.dx + (long)t * p.K + k) = v;
     }
@@ -339,27 +350,33 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dx(BwdDxParams p) {
 // dA_a = s_a X_a^T U_a and dB_a = s_a T_a^T dY_a (the second computed as its transpose,
 // dY_a^T T_a): G [C][r] = s M[R]^T V[R] with M bf16 [T][C], V fp32 [T][r_lim].
 //
-// Item (adapter a, 128 rows c0 .. c0 + 127 of C): the four waves take the segment's
-// 32-token chunks in turn.  Lane (i, g) loads, for tokens q = 8 g .. 8 g + 7 of the chunk,
-// the 16 bytes M[tok_q][c0 + 8 i .. + 7] and transposes the 8 x 8 block in registers:
-// operand m holds M[tok_q][c0 + 8 i + m] over q, the A operand of MFMA block m whose row
-// i is C-row c0 + 8 i + m.  The B operand holds V[tok_q][16 jt + i] over q, split into two
-// bf16 terms.  The waves' sums are combined as ((w0 + w2) + (w1 + w3)): a fixed order, so
-// the result is bitwise reproducible.
+// Item (adapter a, 64 rows c0 .. c0 + 63 of C), two workgroups per CU: the segment's
+// positions go in rounds of 1024 whose token indices are staged in LDS; the four waves take
+// the round's 32-token chunks in turn.  Lane (i, g) loads, for tokens q = 8 g .. 8 g + 7 of
+// a chunk, the 8 bytes M[tok_q][c0 + 4 i .. + 3] and transposes the 8 x 4 block in
+// registers: operand m holds M[tok_q][c0 + 4 i + m] over q, the A operand of MFMA block m
+// whose row i is C-row c0 + 4 i + m.  The B operand holds V[tok_q][16 jt + i] over q, split
+// into two bf16 terms.  A chunk's rows and V are loaded while the previous chunk computes.
+// The waves' sums are combined as ((w0 + w2) + (w1 + w3)): a fixed order, so the result is
+// bitwise reproducible.
 // ---------------------------------------------------------------------------------
 
-constexpr int GR_RS = 68;  // floats per LDS row of a 128 x 64 partial-sum slot
+constexpr int GR_ROWS = 64;  // rows of C per item
+constexpr int GR_RS = 68;    // floats per LDS row of a 64 x 64 partial-sum slot
+constexpr int GR_ROUND = 1024;
 
-__device__ __forceinline__ uint32_t dw(const uint4& v, int d) {
-  return d == 0 ? v.x : (d == 1 ? v.y : (d == 2 ? v.z : v.w));
-}
+__device__ __forceinline__ uint32_t dw(const uint2& v, int d) { return d == 0 ? v.x : v.y; }
 
-__global__ __launch_bounds__(256, 1) void k_bwd_grad(BwdGradParams p) {
-  __shared__ float red[2][128 * GR_RS];
+// NJT: 16-rank tiles loaded per token (ceil(r_max / 16)); every load is unconditional (clamped
+// addresses, values masked at use), so the compiler's wait counts see the prefetch through.
+template <int NJT>
+__global__ __launch_bounds__(256, 2) void k_bwd_grad(BwdGradParams p) {
+  __shared__ float red[2][GR_ROWS * GR_RS];
+  __shared__ int stok[GR_ROUND];
   const int per_ad = p.nkb + p.nnb;
   const int a = blockIdx.x / per_ad, blk = blockIdx.x % per_ad;
   const bool isA = blk < p.nkb;
-  const int c0 = 128 * (isA ? blk : blk - p.nkb);
+  const int c0 = GR_ROWS * (isA ? blk : blk - p.nkb);
   const int C = isA ? p.K : p.N;
   const uint16_t* M = isA ? p.x : p.dy;
   const float* V = isA ? p.u : p.t;
@@ -372,73 +389,97 @@ __global__ __launch_bounds__(256, 1) void k_bwd_grad(BwdGradParams p) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, i = lane & 15, g = lane >> 4;
   const int njt = (r + 15) >> 4;
 
-  v4f acc[8][4];
+  v4f acc[4][NJT];
 #pragma unroll
-  for (int m = 0; m < 8; ++m)
+  for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt) acc[m][jt] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int jt = 0; jt < NJT; ++jt) acc[m][jt] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int p0 = s_beg + 32 * w; p0 < s_end; p0 += 128) {
-    int tok[8];
+  struct Chunk {
+    uint2 mr[8];
+    float v[NJT][8];
+  };
+  // loads of chunk c of the round (positions base + 32 c ..): rows of M and V; positions
+  // past the segment read a token of the round and are zeroed at use
+  auto load = [&](Chunk& ch, int c) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int tok = stok[min(32 * c + 8 * g + q, GR_ROUND - 1)];
+      ch.mr[q] = *reinterpret_cast<const uint2*>(M + (long)tok * C + c0 + 4 * i);
+#pragma unroll
+      for (int jt = 0; jt < NJT; ++jt) ch.v[jt][q] = V[(long)tok * p.r_lim + min(16 * jt + i, r - 1)];
+    }
+  };
+  auto compute = [&](const Chunk& ch, int base, int c) {
     bool ok[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int pos = p0 + 8 * g + q;
-      ok[q] = pos < s_end;
-      tok[q] = p.sorted_tok[ok[q] ? pos : s_beg];
-    }
-    uint4 mr[8];
+    for (int q = 0; q < 8; ++q) ok[q] = base + 32 * c + 8 * g + q < s_end;
+    uint4 op[4];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      mr[q] = ldg16(M + (long)tok[q] * C + c0 + 8 * i);
-      if (!ok[q]) mr[q] = zero4();
-    }
-    uint4 op[8];
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
+    for (int m = 0; m < 4; ++m) {
       uint32_t o[4];
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const uint32_t lo = dw(mr[2 * d], m >> 1), hi = dw(mr[2 * d + 1], m >> 1);
+        const uint2 lo2 = ok[2 * d] ? ch.mr[2 * d] : make_uint2(0u, 0u);
+        const uint2 hi2 = ok[2 * d + 1] ? ch.mr[2 * d + 1] : make_uint2(0u, 0u);
+        const uint32_t lo = dw(lo2, m >> 1), hi = dw(hi2, m >> 1);
         o[d] = (m & 1) ? __builtin_amdgcn_perm(hi, lo, 0x07060302u) : __builtin_amdgcn_perm(hi, lo, 0x05040100u);
       }
       op[m] = make_uint4(o[0], o[1], o[2], o[3]);
     }
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
+    for (int jt = 0; jt < NJT; ++jt) {
       if (jt < njt) {
-        const int j = 16 * jt + i;
+        const bool jok = 16 * jt + i < r;
         float v[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) v[q] = (ok[q] && j < r) ? V[(long)tok[q] * p.r_lim + j] : 0.f;
+        for (int q = 0; q < 8; ++q) v[q] = (ok[q] && jok) ? ch.v[jt][q] : 0.f;
         uint4 vh, vl;
         split8(v, vh, vl);
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
+        for (int m = 0; m < 4; ++m) {
           acc[m][jt] = mfma_bf16_16x16x32(op[m], vh, acc[m][jt]);
           acc[m][jt] = mfma_bf16_16x16x32(op[m], vl, acc[m][jt]);
         }
       }
     }
+  };
+
+  for (int base = s_beg; base < s_end; base += GR_ROUND) {
+    __syncthreads();  // the previous round's tokens are no longer read
+    for (int o = tid; o < GR_ROUND; o += 256) stok[o] = p.sorted_tok[min(base + o, s_end - 1)];
+    __syncthreads();
+    const int nch = (min(GR_ROUND, s_end - base) + 31) / 32;  // chunks of this round
+    // wave w takes chunks w, w + 4, ...; two register sets alternate, the next chunk's loads
+    // in flight while one computes (the loads past the last chunk reload it, unused)
+    Chunk A, B;
+    load(A, min(w, nch - 1));
+    for (int c = w; c < nch; c += 8) {
+      load(B, min(c + 4, nch - 1));
+      compute(A, base, c);
+      load(A, min(c + 8, nch - 1));
+      if (c + 4 < nch) compute(B, base, c + 4);
+    }
   }
 
-  // combine the waves: slot row 16 m + rho holds C-row c0 + 8 rho + m (rho = 4 g + v)
+  // combine the waves: slot row 16 m + rho holds C-row c0 + 4 rho + m (rho = 4 g + v)
   auto put = [&](float* s) {
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int jt = 0; jt < 4; ++jt)
+      for (int jt = 0; jt < NJT; ++jt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) s[(16 * m + 4 * g + v) * GR_RS + 16 * jt + i] = acc[m][jt][v];
   };
   auto add = [&](const float* s) {
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int jt = 0; jt < 4; ++jt)
+      for (int jt = 0; jt < NJT; ++jt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[m][jt][v] += s[(16 * m + 4 * g + v) * GR_RS + 16 * jt + i];
   };
+  __syncthreads();
   if (w >= 2) put(red[w - 2]);
   __syncthreads();
   if (w < 2) add(red[w]);
@@ -449,23 +490,23 @@ __global__ __launch_bounds__(256, 1) void k_bwd_grad(BwdGradParams p) {
     add(red[0]);
     const float sa = p.scales[a];
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int jt = 0; jt < 4; ++jt) acc[m][jt] *= sa;
+      for (int jt = 0; jt < NJT; ++jt) acc[m][jt] *= sa;
     put(red[1]);
   }
   __syncthreads();
   const float* fin = red[1];
   float* out = reinterpret_cast<float*>(isA ? p.dA_ptrs[a] : p.dB_ptrs[a]);
-  if (isA) {  // dA_a [K][r]: rows c0 .. c0 + 127 are 128 r consecutive floats
-    for (int o = tid; o < 128 * r; o += 256) {
+  if (isA) {  // dA_a [K][r]: rows c0 .. c0 + 63 are 64 r consecutive floats
+    for (int o = tid; o < GR_ROWS * r; o += 256) {
       const int row = o / r, j = o - row * r;
-      out[(long)(c0 + row) * r + j] = fin[(16 * (row & 7) + (row >> 3)) * GR_RS + j];
+      out[(long)(c0 + row) * r + j] = fin[(16 * (row & 3) + (row >> 2)) * GR_RS + j];
     }
-  } else {    // dB_a [r][N]: for each rank, 128 consecutive columns
-    for (int o = tid; o < 128 * r; o += 256) {
-      const int j = o >> 7, col = o & 127;
-      out[(long)j * p.N + c0 + col] = fin[(16 * (col & 7) + (col >> 3)) * GR_RS + j];
+  } else {    // dB_a [r][N]: for each rank, 64 consecutive columns
+    for (int o = tid; o < GR_ROWS * r; o += 256) {
+      const int j = o >> 6, col = o & 63;
+      out[(long)j * p.N + c0 + col] = fin[(16 * (col & 3) + (col >> 2)) * GR_RS + j];
     }
   }
 }
@@ -476,7 +517,13 @@ hipError_t launch_bwd_dx(const BwdDxParams& p, hipStream_t s) {
 }
 
 hipError_t launch_bwd_grad(const BwdGradParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(k_bwd_grad, dim3(p.n_ad * (p.nkb + p.nnb)), dim3(256), 0, s, p);
+  const dim3 grid(p.n_ad * (p.nkb + p.nnb));
+  switch ((p.r_lim + 15) >> 4) {
+    case 1: hipLaunchKernelGGL(k_bwd_grad<1>, grid, dim3(256), 0, s, p); break;
+    case 2: hipLaunchKernelGGL(k_bwd_grad<2>, grid, dim3(256), 0, s, p); break;
+    case 3: hipLaunchKernelGGL(k_bwd_grad<3>, grid, dim3(256), 0, s, p); break;
+    default: hipLaunchKernelGGL(k_bwd_grad<4>, grid, dim3(256), 0, s, p); break;
+  }
   return hipGetLastError();
 }
 

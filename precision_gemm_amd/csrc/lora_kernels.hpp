@@ -161,7 +161,7 @@ hipError_t launch_pack_weight(int fmt, const uint8_t* q, const uint8_t* sc, int 
 // `s` whenever it differs from the previous call's on this device).
 constexpr size_t SCRATCH_BYTES = (size_t)LORA_NOALLOC_SCRATCH_BYTES;
 hipError_t scratch_acquire(hipStream_t s, size_t tag_lo, size_t tag_hi, void** out);
-// Backward (lora_backward.hip).  dX = dY W_d^T + s_a u A_a^T: 128 x 256 tiles, W^T packed
+// Backward (lora_backward.hip).  dX = dY W_d^T + s_a u A_a^T: 64 x 256 tiles, W^T packed
 // by launch_pack_weight_t, A_a rows [K][rank_pad(r_a)] (launch_pack_adapter_bwd).
 struct BwdDxParams {
   const uint16_t* dy;      // bf16 [T][N]
@@ -176,10 +176,10 @@ struct BwdDxParams {
   const float* scales;
   int n_ad;
   uint16_t* dx;            // bf16 [T][K]
-  int n_tb, n_kb;          // 128-row and 256-column blocks
+  int n_tb, n_kb;          // 64-row and 256-column blocks
 };
 // dA_a = s_a X_a^T U_a [K][r_a] and dB_a = s_a T_a^T dY_a [r_a][N]: one workgroup per
-// (adapter, 128 rows of K) and (adapter, 128 columns of N).
+// (adapter, 64 rows of K) and (adapter, 64 columns of N).
 struct BwdGradParams {
   const uint16_t* x;       // bf16 [T][K]
   const uint16_t* dy;      // bf16 [T][N]

@@ -392,13 +392,41 @@ def pack_adapters_bwd(ad: Adapters) -> BackwardAdapters:
                             torch.tensor([a.data_ptr() for a in Ar], dtype=torch.int64, device=dev))
 
 
+@dataclass
+class Grads:
+    """Gradient buffers of an adapter set: ``dA[a]`` float32 [K, r_a], ``dB[a]`` float32
+    [r_a, N], and the device arrays of their addresses (built once, so that a call can be
+    captured in a HIP graph)."""
+
+    dA: list
+    dB: list
+    dA_ptrs: torch.Tensor
+    dB_ptrs: torch.Tensor
+
+
+def grads_from(dA: list, dB: list) -> Grads:
+    dev = dA[0].device
+    for m in dA + dB:
+        _dev(m, "gradient buffer", torch.float32)
+    return Grads(dA, dB, torch.tensor([m.data_ptr() for m in dA], dtype=torch.int64, device=dev),
+                 torch.tensor([m.data_ptr() for m in dB], dtype=torch.int64, device=dev))
+
+
+def alloc_grads(ad: Adapters, K: int, N: int) -> Grads:
+    dev = ad.scales.device
+    rk = [int(a.shape[1]) for a in ad.A]
+    return grads_from([torch.empty((K, r), dtype=torch.float32, device=dev) for r in rk],
+                      [torch.empty((r, N), dtype=torch.float32, device=dev) for r in rk])
+
+
 def lora_backward(x: torch.Tensor, dy: torch.Tensor, t: torch.Tensor, wt: torch.Tensor, w_scale: torch.Tensor,
-                  seg: Segments, ad: Adapters, bw: BackwardAdapters, *, dx=None, u=None, dA=None, dB=None,
+                  seg: Segments, ad: Adapters, bw: BackwardAdapters, *, dx=None, u=None, grads: Grads | None = None,
                   status: torch.Tensor | None = None):
-    """Gradients of the 16-bit-activation layer (lora_backward): returns ``(dx, u, dA, dB)``
-    with dx bf16 [T, K], u float32 [T, r_max], dA[a] float32 [K, r_a], dB[a] float32 [r_a, N].
-    ``wt`` from :func:`pack_weight_t`, ``w_scale`` the FP8 channel scales, ``t`` the forward's
-    down-projection.  Output buffers may be passed in."""
+    """Gradients of the 16-bit-activation layer (lora_backward): returns ``(dx, u, grads)``
+    with dx bf16 [T, K], u float32 [T, r_max] and ``grads`` (:class:`Grads`: dA[a] float32
+    [K, r_a], dB[a] float32 [r_a, N]).  ``wt`` from :func:`pack_weight_t`, ``w_scale`` the FP8
+    channel scales, ``t`` the forward's down-projection.  Output buffers may be passed in
+    (then the call allocates nothing and can be captured in a HIP graph)."""
     _dev(x, "x", torch.bfloat16)
     _dev(dy, "dy", torch.bfloat16)
     T, K = x.shape
@@ -408,15 +436,11 @@ def lora_backward(x: torch.Tensor, dy: torch.Tensor, t: torch.Tensor, wt: torch.
         dx = torch.empty((T, K), dtype=torch.bfloat16, device=dev)
     if u is None:
         u = torch.empty((T, ad.r_max), dtype=torch.float32, device=dev)
-    rk = [int(a.shape[1]) for a in ad.A]
-    if dA is None:
-        dA = [torch.empty((K, r), dtype=torch.float32, device=dev) for r in rk]
-    if dB is None:
-        dB = [torch.empty((r, N), dtype=torch.float32, device=dev) for r in rk]
-    dA_ptrs = torch.tensor([m.data_ptr() for m in dA], dtype=torch.int64, device=dev)
-    dB_ptrs = torch.tensor([m.data_ptr() for m in dB], dtype=torch.int64, device=dev)
+    if grads is None:
+        grads = alloc_grads(ad, K, N)
     check("lora_backward", lib().lora_backward(
         _ptr(x), _ptr(dy), _ptr(t), T, K, N, LORA_W_FP8_E4M3, _ptr(wt), _ptr(w_scale), _ptr(seg.adapter_id),
         _ptr(seg.seg_indptr), _ptr(seg.sorted_tok), _ptr(bw.Bop_ptrs), _ptr(bw.Ar_ptrs), _ptr(ad.ranks),
-        _ptr(ad.scales), ad.n, ad.r_max, _ptr(dx), _ptr(u), _ptr(dA_ptrs), _ptr(dB_ptrs), _ptr(status), _stream()))
-    return dx, u, dA, dB
+        _ptr(ad.scales), ad.n, ad.r_max, _ptr(dx), _ptr(u), _ptr(grads.dA_ptrs), _ptr(grads.dB_ptrs), _ptr(status),
+        _stream()))
+    return dx, u, grads

@@ -96,7 +96,7 @@ def run_backward(wl, dy_bits, t=None, nan_fill=True, repeat=1):
     for _ in range(repeat):
         dA = [torch.full((wl.K, int(r)), float("nan") if nan_fill else 0.0, device="cuda") for r in wl.ranks]
         dB = [torch.full((int(r), wl.N), float("nan") if nan_fill else 0.0, device="cuda") for r in wl.ranks]
-        dx, u, dA, dB = P.lora_backward(x, dy, tt, wt, sc, seg, ad, bw, dA=dA, dB=dB, status=st)
+        dx, u, gr = P.lora_backward(x, dy, tt, wt, sc, seg, ad, bw, grads=P.grads_from(dA, dB), status=st)
         torch.cuda.synchronize()
         outs.append({"dx_bits": dx.view(torch.int16).cpu().numpy().view(np.uint16),
                      "dx": dx.float().cpu().numpy().astype(np.float64), "u": u.cpu().numpy().astype(np.float64),
@@ -195,8 +195,8 @@ def test_backward_without_tokens_zero_fills():
     dA = [torch.full((wl.K, int(r)), float("nan"), device="cuda") for r in wl.ranks]
     dB = [torch.full((int(r), wl.N), float("nan"), device="cuda") for r in wl.ranks]
     z = torch.empty((0, wl.K), dtype=torch.bfloat16, device="cuda")
-    dx, u, dA, dB = P.lora_backward(z, torch.empty((0, wl.N), dtype=torch.bfloat16, device="cuda"),
-                                    torch.empty((0, ad.r_max), device="cuda"), wt, sc, seg, ad, bw, dA=dA, dB=dB)
+    P.lora_backward(z, torch.empty((0, wl.N), dtype=torch.bfloat16, device="cuda"),
+                    torch.empty((0, ad.r_max), device="cuda"), wt, sc, seg, ad, bw, grads=P.grads_from(dA, dB))
     torch.cuda.synchronize()
     assert all(not m.cpu().numpy().any() for m in dA + dB)
 
@@ -221,7 +221,7 @@ def test_backward_reports_an_invalid_rank():
     dA = [torch.full((wl.K, int(r)), 7.0, device="cuda") for r in wl.ranks]
     dB = [torch.full((int(r), wl.N), 7.0, device="cuda") for r in wl.ranks]
     t = torch.from_numpy(ref["t"].astype(np.float32)).cuda()
-    dx, u, dA, dB = P.lora_backward(x, bf16_tensor(dy_bits), t, wt, sc, seg, ad, bw, dA=dA, dB=dB, status=st)
+    dx, u, _ = P.lora_backward(x, bf16_tensor(dy_bits), t, wt, sc, seg, ad, bw, grads=P.grads_from(dA, dB), status=st)
     torch.cuda.synchronize()
     assert int(st.item()) == 2
     assert (dA[2].cpu().numpy() == 7.0).all() and (dB[2].cpu().numpy() == 7.0).all()
