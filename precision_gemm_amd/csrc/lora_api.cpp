@@ -521,7 +521,14 @@ lora_status lora_backward(const uint16_t* x, const uint16_t* dy, const float* t,
   sp.t_out = u; sp.t_tag = nullptr;
   sp.tblk = pl.s_tblk; sp.n_tblk = pl.s_ntblk; sp.n_jg = pl.s_njg; sp.jper = pl.s_jper;
   sp.kparts = pl.s_kparts; sp.kpart_len = pl.s_kpart_len;
-  if (launch_shrink(pl, s, sp) != hipSuccess) return LORA_ERR_HIP;
+  // above 128 tokens: the forward pre-pass's down-projection over 16-position blocks (every
+  // row of dY read once, four waves per block splitting N); below, the standalone kernel
+  if (T > 128) {
+    sp.ids = adapter_id;
+    if (launch_shrink_rows(sp, s) != hipSuccess) return LORA_ERR_HIP;
+  } else if (launch_shrink(pl, s, sp) != hipSuccess) {
+    return LORA_ERR_HIP;
+  }
   if (launch_bwd_grad(gp, s) != hipSuccess) return LORA_ERR_HIP;
   BwdDxParams dp{};
   dp.dy = dy; dp.wt = wt_q; dp.wsc = w_scale; dp.T = T; dp.K = K; dp.N = N;

@@ -1993,12 +1993,15 @@ constexpr int PREP_RS = 128 + 16;  // LDS row stride (bytes) of a wave's x slot:
 //    comes back through the wave's LDS slot.
 //  - SEP: the down-projection's rows (which differ from the quantisation's) are loaded in
 //    operand layout, lane (i, g) taking row i at 16 g .. 16 g + 15.
+//  - neither: the down-projection's rows p0 .. p0 + 15 loaded row-contiguously and relayed,
+//    with no quantisation (the backward's u = dY B_a^T).
 template <bool QUANT, bool SEP, int NJT>
 __device__ __forceinline__ void prep_pass(uint8_t* __restrict__ xq, uint8_t* __restrict__ xsc, int K, int T, int p0,
                                           const uint16_t* x, const uint16_t* xrow_s, char* slot, bool s_mine,
                                           const uint16_t* arow0, int r, int kb, int nst, v4f (&acc)[4]) {
   constexpr int U = PREP_U;
-  constexpr bool RELAY = QUANT && !SEP && NJT > 0;  // operands through the LDS slot
+  constexpr bool RELAY = !SEP && NJT > 0;  // operands through the LDS slot
+  constexpr bool CONTIG = QUANT || RELAY;  // rows p0 .. p0 + 15 loaded row-contiguously
   const int lane = threadIdx.x & 63, li = lane & 15, g = lane >> 4;
   if (nst <= 0) return;
   // A_a in operand order (tiles past r_a's last read that tile and are masked at the output;
@@ -2015,7 +2018,7 @@ __device__ __forceinline__ void prep_pass(uint8_t* __restrict__ xq, uint8_t* __r
   uint4 xr[U][2], xs[U][2], ar[U][NJT > 0 ? NJT : 1][2];
   auto issue = [&](int u, int st) {  // the clamped step is always valid
     const int k = kb + min(st, nst - 1) * 64;
-    if (QUANT) {
+    if (CONTIG) {
       xr[u][0] = ldg16(xc0 + k);
       xr[u][1] = ldg16(xc1 + k);
     }
@@ -2032,17 +2035,19 @@ __device__ __forceinline__ void prep_pass(uint8_t* __restrict__ xq, uint8_t* __r
   auto consume = [&](int u, int st) {
     const int k = kb + st * 64;
     uint4 xv[2] = {zero4(), zero4()};
-    if (QUANT) {
+    if (CONTIG) {
       // a block is 32 values = the pieces of a quad of lanes; all four lanes store its code
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        uint32_t mx = absmax8_bits(xr[u][i]);
-        mx = max(mx, quad_swap1(mx));
-        mx = max(mx, quad_swap2(mx));
-        const uint32_t code = mx_code_from_bits(mx);
-        const int row = i ? crow1 : crow0;
-        *reinterpret_cast<uint2*>(xq + (long)row * K + k + 8 * (lane & 7)) = mx_piece_quant(xr[u][i], code);
-        xsc[(long)row * (K / 32) + (k >> 5) + ((lane & 7) >> 2)] = (uint8_t)code;
+        if (QUANT) {
+          uint32_t mx = absmax8_bits(xr[u][i]);
+          mx = max(mx, quad_swap1(mx));
+          mx = max(mx, quad_swap2(mx));
+          const uint32_t code = mx_code_from_bits(mx);
+          const int row = i ? crow1 : crow0;
+          *reinterpret_cast<uint2*>(xq + (long)row * K + k + 8 * (lane & 7)) = mx_piece_quant(xr[u][i], code);
+          xsc[(long)row * (K / 32) + (k >> 5) + ((lane & 7) >> 2)] = (uint8_t)code;
+        }
         if (RELAY) *reinterpret_cast<uint4*>(slot + PREP_RS * (8 * i + (lane >> 3)) + 16 * (lane & 7)) = xr[u][i];
       }
     }
@@ -2079,8 +2084,11 @@ __device__ __forceinline__ void prep_pass(uint8_t* __restrict__ xq, uint8_t* __r
 }
 
 // NJT: rank tiles of 16 of the batch's largest rank (every adapter's pass runs them all;
-// the ranks past an adapter's own read its row 0 and are masked at the output).
-template <int NJT>
+// the ranks past an adapter's own read its row 0 and are masked at the output).  Q: the first
+// pass also quantises x; without it the kernel is the down-projection alone (the backward's
+// u = dY B_a^T, B_a in A_a's operand order), its passes relaying contiguous rows where the
+// positions are consecutive tokens.
+template <int NJT, bool Q>
 __global__ __launch_bounds__(256) void k_prep_rows(ShrinkParams sp, uint8_t* __restrict__ xq, uint8_t* __restrict__ xsc) {
   __shared__ __align__(16) float red[4][4][64][4];  // [wave][rank tile][lane][4]
   __shared__ __align__(16) char xslot[4][16 * PREP_RS];  // each wave's x relayout slot
@@ -2128,12 +2136,18 @@ __global__ __launch_bounds__(256) void k_prep_rows(ShrinkParams sp, uint8_t* __r
     const bool mine = a >= 0 && r > 0 && s_ok && a_s == a;
     const uint16_t* arow0 = reinterpret_cast<const uint16_t*>(r > 0 ? sp.A_ptrs[a] : (uint64_t)sp.x);
     char* slot = xslot[wave];
-    if (first && same)
+    if (!Q) {
+      if (r > 0 && same)
+        prep_pass<false, false, NJT>(xq, xsc, K, T, p0, sp.x, xrow_s, slot, mine, arow0, r, kb, nst, acc);
+      else if (r > 0)
+        prep_pass<false, true, NJT>(xq, xsc, K, T, p0, sp.x, xrow_s, slot, mine, arow0, r, kb, nst, acc);
+    } else if (first && same) {
       prep_pass<true, false, NJT>(xq, xsc, K, T, p0, sp.x, xrow_s, slot, mine, arow0, r, kb, nst, acc);
-    else if (first)
+    } else if (first) {
       prep_pass<true, true, NJT>(xq, xsc, K, T, p0, sp.x, xrow_s, slot, mine, arow0, r, kb, nst, acc);
-    else if (r > 0)
+    } else if (r > 0) {
       prep_pass<false, true, NJT>(xq, xsc, K, T, p0, sp.x, xrow_s, slot, mine, arow0, r, kb, nst, acc);
+    }
     first = false;
   } while (todo);
   // the quarters' sums in wave order; wave w writes rank tile w of t (plain fp32, zero past
@@ -2445,10 +2459,22 @@ hipError_t launch_quant_shrink(const LayerPlan& pl, const ShrinkParams& sp, cons
   (void)pl; (void)x; (void)K;
   const dim3 grid((T + 15) / 16), block(256);
   switch ((sp.r_lim + 15) / 16) {
-    case 1: hipLaunchKernelGGL(k_prep_rows<1>, grid, block, 0, s, sp, xq, xsc); break;
-    case 2: hipLaunchKernelGGL(k_prep_rows<2>, grid, block, 0, s, sp, xq, xsc); break;
-    case 3: hipLaunchKernelGGL(k_prep_rows<3>, grid, block, 0, s, sp, xq, xsc); break;
-    case 4: hipLaunchKernelGGL(k_prep_rows<4>, grid, block, 0, s, sp, xq, xsc); break;
+    case 1: hipLaunchKernelGGL((k_prep_rows<1, true>), grid, block, 0, s, sp, xq, xsc); break;
+    case 2: hipLaunchKernelGGL((k_prep_rows<2, true>), grid, block, 0, s, sp, xq, xsc); break;
+    case 3: hipLaunchKernelGGL((k_prep_rows<3, true>), grid, block, 0, s, sp, xq, xsc); break;
+    case 4: hipLaunchKernelGGL((k_prep_rows<4, true>), grid, block, 0, s, sp, xq, xsc); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_shrink_rows(const ShrinkParams& sp, hipStream_t s) {
+  const dim3 grid((sp.T + 15) / 16), block(256);
+  switch ((sp.r_lim + 15) / 16) {
+    case 1: hipLaunchKernelGGL((k_prep_rows<1, false>), grid, block, 0, s, sp, nullptr, nullptr); break;
+    case 2: hipLaunchKernelGGL((k_prep_rows<2, false>), grid, block, 0, s, sp, nullptr, nullptr); break;
+    case 3: hipLaunchKernelGGL((k_prep_rows<3, false>), grid, block, 0, s, sp, nullptr, nullptr); break;
+    case 4: hipLaunchKernelGGL((k_prep_rows<4, false>), grid, block, 0, s, sp, nullptr, nullptr); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

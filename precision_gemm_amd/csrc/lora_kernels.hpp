@@ -137,6 +137,9 @@ hipError_t launch_quant(const uint16_t* x, int T, int K, uint8_t* xq, uint8_t* x
 // the MXFP8 pre-pass with the down-projection items (plan with 64-token items) beside it
 hipError_t launch_quant_shrink(const LayerPlan& pl, const ShrinkParams& sp, const uint16_t* x, int T, int K, uint8_t* xq,
                                uint8_t* xsc, hipStream_t s);
+// the pre-pass's down-projection alone over 16-position blocks of the sorted order (no
+// quantisation): t_out plain, sp.ids the per-token adapter ids
+hipError_t launch_shrink_rows(const ShrinkParams& sp, hipStream_t s);
 hipError_t launch_quant_build(const uint16_t* x, int T, int K, uint8_t* xq, uint8_t* xsc, const int* ids, int n_ad,
                               int* seg, int* sorted, int* err, hipStream_t s);
 hipError_t launch_shrink(const LayerPlan& pl, hipStream_t stream, const ShrinkParams& sp);
