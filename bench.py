@@ -240,6 +240,62 @@ def tune_shrink(args, wl):
     print(json.dumps(out), flush=True)
 
 
+def shrink_sweep(args, wl):
+    """Every feasible configuration of the standalone down-projection on this workload, timed
+    (microseconds per launch, HIP events, median of three batches of 20): the bf16-MFMA tile
+    family against the wave-reduction (BGMV) kernel, with the library's default launch
+    (lora_shrink) beside them.  Each configuration's t is checked against lora_shrink's."""
+    import torch
+    import precision_gemm_amd as P
+    from precision_gemm_amd import tune
+    from workloads.device import upload
+    x, w, ad, ids = upload(wl)
+    seg = P.build_segments(ids, ad.n)
+    ref = P.shrink(x, seg, ad)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t = torch.empty_like(ref)
+
+    def timed(fn, reps=20):
+        fn()
+        times = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3 / reps)
+        return sorted(times)[1]
+
+    def info(tg, jp, u, m):
+        try:
+            return P.shrink_config_info(tg, jp, u, nt=m)
+        except Exception:
+            return None
+    default_us = timed(lambda: P.shrink(x, seg, ad, t=t))
+    rows = []
+    for node in tune.space():
+        if not tune.feasible(node, info, wl.T):
+            continue
+        cfg = tune.to_config(node)
+        us = timed(lambda: P.shrink_configured(x, seg, ad, cfg, t=t))
+        d = float((t - ref).norm() / ref.norm())
+        rows.append((node, cfg, us, d))
+    names = ("TG", "JP", "U", "TBLK", "ORDER")
+    fam = lambda tg: "wave_reduction" if tg == 0 else "mfma"  # noqa: E731
+    out = {"workload": args.workload, "what": "standalone down-projection, us per launch (HIP events)",
+           "default_us": default_us, "kernel_sha": kernel_source_sha(), "configurations": len(rows)}
+    for f in ("mfma", "wave_reduction"):
+        sub = [r for r in rows if fam(r[0][0]) == f]
+        if sub:
+            b = min(sub, key=lambda r: r[2])
+            out[f] = {"best": dict(zip(names, b[1])), "best_us": b[2], "max_rel_frob_vs_default": max(r[3] for r in sub),
+                      "all": [[list(r[1]), round(r[2], 3)] for r in sorted(sub, key=lambda r: r[2])]}
+    print(json.dumps(out), flush=True)
+
+
 def ablation_merged(args, wl):
     """The per-token merged-weight formulation against the fused layer (both with x in bf16:
     by the merged-weight identity they compute the same layer), microseconds per call from
@@ -427,6 +483,9 @@ def main():
     ap.add_argument("--ablation-merged", action="store_true",
                     help="instead of the layer call: time the per-token merged-weight layer (lora_merged_layer) "
                          "against the fused layer with 16-bit activations on the workload")
+    ap.add_argument("--shrink-sweep", action="store_true",
+                    help="instead of the layer call: time every feasible configuration of the standalone "
+                         "down-projection (MFMA tiles and wave reductions) on the workload")
     ap.add_argument("--backward", action="store_true",
                     help="instead of the layer call: time the backward (lora_backward) on the workload (FP8 base)")
     ap.add_argument("--copy-mb", type=int, default=0,
@@ -458,6 +517,9 @@ def main():
         return
     if args.backward:
         backward(args, wl)
+        return
+    if args.shrink_sweep:
+        shrink_sweep(args, wl)
         return
     a16 = args.act == "bf16"
     nbytes, flops = algorithmic(wl)

@@ -213,13 +213,19 @@ lora_status lora_shrink(const uint16_t* x, int32_t T, int32_t K,
  * multi-tenant LoRA serving via SGMV-specific operator autotuning", abstract: tiling,
  * caching and virtual-thread scheduling of the SGMV operator chosen by a stochastic search).
  * config [host] int32[5] = {TG, JP, U, TBLK, ORDER}:
- *   TG   token tiles of 16 per inner step (tiling)            1, 2 or 4
+ *   TG   token tiles of 16 per inner step on bf16 MFMA (tiling)   1, 2 or 4; or 0: the
+ *        wave-reduction kernel (BGMV: each lane multiplies 16 k of one rank with the tokens'
+ *        x in fp32, the lane groups and waves summed by shuffles and LDS), for segments of a
+ *        few tokens
  *   JP   rank tiles of 16 per workgroup item (tiling)          1, 2 or 4
- *   U    k-steps of 64 per prefetch buffer (caching)          1 or 2
- *   TBLK tokens of one segment per workgroup item, a multiple of 16 (scheduling)
+ *   U    k-steps of 64 per prefetch buffer (caching)          1 or 2 (TG = 0: 2 only with TBLK 1)
+ *   TBLK positions of one segment per workgroup item (scheduling): a multiple of 16, or for
+ *        TG = 0: 1, 2 or 4
  *   ORDER 0: items in workgroup-id order; 1: each XCD takes a contiguous run of items
  *         (scheduling).
- * Other values return LORA_ERR_UNSUPPORTED.  Other arguments as lora_shrink. */
+ * Other values return LORA_ERR_UNSUPPORTED.  Other arguments as lora_shrink.  The
+ * wave-reduction kernel sums in another order than the MFMA kernels (t agrees to fp32
+ * rounding, bitwise deterministic on its own). */
 lora_status lora_shrink_configured(const uint16_t* x, int32_t T, int32_t K,
                                    const int32_t* seg_indptr, const int32_t* sorted_tok,
                                    const uint64_t* A_ptrs, const int32_t* ranks,
@@ -243,6 +249,10 @@ lora_status lora_merged_layer(const uint16_t* x, int32_t T, int32_t K, int32_t N
                               const uint64_t* A_rows, const uint64_t* B_ptrs,
                               const int32_t* ranks, const float* scales, int32_t n_adapters,
                               int32_t r_max, uint16_t* y, void* stream);
+
+/* Resources of the compiled wave-reduction down-projection (TBLK = nt positions, jp, u) on the
+ * current device, as lora_shrink_config_info. */
+lora_status lora_shrink_bgmv_info(int32_t nt, int32_t jp, int32_t u, int32_t* out);
 
 /* Resources of the compiled down-projection instance (TG, JP, U) on the current device:
  * out [host] int32[3] = {registers per lane, scratch (spill) bytes per lane, LDS bytes}.

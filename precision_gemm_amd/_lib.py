@@ -41,6 +41,7 @@ _SIGNATURES = {
     "lora_backward": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                               c_vp, c_vp, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "lora_shrink_config_info": (c_i32, [c_i32, c_i32, c_i32, ctypes.POINTER(c_i32)]),
+    "lora_shrink_bgmv_info": (c_i32, [c_i32, c_i32, c_i32, ctypes.POINTER(c_i32)]),
     "lora_merged_layer": (c_i32, [c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,
                                   c_i32, c_vp, c_vp]),
     "lora_pack_adapter": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]),

@@ -547,9 +547,11 @@ lora_status lora_shrink_configured(const uint16_t* x, int32_t T, int32_t K, cons
   if (!config) return LORA_ERR_INVALID_ARG;
   const int tg = config[0], jp = config[1], u = config[2], tblk = config[3], order = config[4];
   auto in = [](int v, int a, int b, int c) { return v == a || v == b || v == c; };
-  if (!in(tg, 1, 2, 4) || !in(jp, 1, 2, 4) || (u != 1 && u != 2) || (order != 0 && order != 1))
+  const bool bgmv = tg == 0;  // wave reductions: TBLK positions per item, 1, 2 or 4
+  if (!(bgmv || in(tg, 1, 2, 4)) || !in(jp, 1, 2, 4) || (u != 1 && u != 2) || (order != 0 && order != 1))
     return LORA_ERR_UNSUPPORTED;
-  if (tblk < 16 || tblk % 16 != 0 || tblk > 65536) return LORA_ERR_UNSUPPORTED;
+  if (bgmv ? (!in(tblk, 1, 2, 4) || (u == 2 && tblk != 1)) : (tblk < 16 || tblk % 16 != 0 || tblk > 65536))
+    return LORA_ERR_UNSUPPORTED;
   if (T == 0) return LORA_OK;
   if (!x || !seg_indptr || !sorted_tok || !A_ptrs || !ranks || !t) return LORA_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(t)) return LORA_ERR_INVALID_ARG;
@@ -564,6 +566,8 @@ lora_status lora_shrink_configured(const uint16_t* x, int32_t T, int32_t K, cons
   sp.item_order = order;
   const long items = (long)n_adapters * sp.n_tblk * sp.n_jg;
   if (items > (1L << 30)) return LORA_ERR_UNSUPPORTED;
+  if (bgmv)
+    return launch_shrink_bgmv(tblk, jp, u, (int)items, as_stream(stream), sp) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
   return launch_shrink_cfg(tg, jp, u, (int)items, as_stream(stream), sp) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
@@ -571,6 +575,18 @@ lora_status lora_shrink_config_info(int32_t tg, int32_t jp, int32_t u, int32_t* 
   if (!out) return LORA_ERR_INVALID_ARG;
   int regs = 0, spill = 0, lds = 0;
   const hipError_t e = shrink_cfg_attr(tg, jp, u, &regs, &spill, &lds);
+  if (e == hipErrorInvalidValue) return LORA_ERR_UNSUPPORTED;
+  if (e != hipSuccess) return LORA_ERR_HIP;
+  out[0] = regs;
+  out[1] = spill;
+  out[2] = lds;
+  return LORA_OK;
+}
+
+lora_status lora_shrink_bgmv_info(int32_t nt, int32_t jp, int32_t u, int32_t* out) {
+  if (!out) return LORA_ERR_INVALID_ARG;
+  int regs = 0, spill = 0, lds = 0;
+  const hipError_t e = shrink_bgmv_attr(nt, jp, u, &regs, &spill, &lds);
   if (e == hipErrorInvalidValue) return LORA_ERR_UNSUPPORTED;
   if (e != hipSuccess) return LORA_ERR_HIP;
   out[0] = regs;

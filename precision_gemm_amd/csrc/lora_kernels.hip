@@ -586,6 +586,140 @@ __global__ __launch_bounds__(256) void k_shrink(ShrinkParams p) {
 }
 
 // ======================================================================================
+// Down-projection by wave reductions (BGMV) for segments of a few tokens, the standalone
+// launch's alternative to the MFMA tiles above (16-token tiles, mostly padding when a segment
+// holds one token).  Item (adapter a, NT consecutive positions of its segment, 16 JP ranks).
+// The packed A gives lane (i, g) rank i of a 16-rank tile at k = 64 ks + 16 g .. + 15 of each
+// 64-wide k-step: the lane multiplies those 16 values with the same 16 k of each token's x
+// row in fp32 and keeps one partial sum per (token, rank).  The four waves take interleaved
+// k-steps, U of them per buffer, two buffers in flight; at the end the four lane groups g
+// are summed by two butterfly shuffles and the four waves in LDS in wave order, so t is
+// deterministic.  Output as the MFMA kernel's: fp32 t in original token order, zero for
+// r_a <= j < r_max.
+// ======================================================================================
+template <int NT, int JP, int U>
+__global__ __launch_bounds__(256) void k_shrink_bgmv(ShrinkParams p) {
+  __shared__ float red[4][NT][JP * 16];
+  const int b = blockIdx.x, nb = gridDim.x;
+  const int item = (p.item_order == 1 && nb % 8 == 0) ? (b & 7) * (nb >> 3) + (b >> 3) : b;
+  const int jg = item % p.n_jg;
+  const int rest = item / p.n_jg;
+  const int tb = rest % p.n_tblk;
+  const int a = rest / p.n_tblk;
+  const int s0 = p.seg_indptr[a];
+  const int L = p.seg_indptr[a + 1] - s0;
+  const int tok_begin = tb * NT;
+  const int r = p.ranks[a];
+  const int j_begin = jg * JP * 16;
+  if (tok_begin >= L || r < 1 || r > p.r_lim) return;
+  const int tok_end = min(L, tok_begin + NT);
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, li = lane & 15,
+            g = lane >> 4;
+  if (j_begin < r) {
+    const int nsteps = p.K >> 6;
+    const uint16_t* __restrict__ A = reinterpret_cast<const uint16_t*>(p.A_ptrs[a]);
+    const uint16_t* arow[JP];
+    const int nat = a_tiles(r);
+#pragma unroll
+    for (int jt = 0; jt < JP; ++jt) arow[jt] = A + a_tile_off(min((j_begin >> 4) + jt, nat - 1), 0, 0, p.K) + 8 * lane;
+    const uint16_t* xrow[NT];
+#pragma unroll
+    for (int q = 0; q < NT; ++q) xrow[q] = p.x + (long)p.sorted_tok[s0 + min(tok_begin + q, tok_end - 1)] * p.K + 16 * g;
+    float acc[NT][JP];
+#pragma unroll
+    for (int q = 0; q < NT; ++q)
+#pragma unroll
+      for (int jt = 0; jt < JP; ++jt) acc[q][jt] = 0.f;
+    // unconditional loads from clamped addresses (see shrink_item)
+    uint4 xa[2][U][NT][2], aa[2][U][JP][2];
+    auto load = [&](int buf, int sbase) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int ks = min(sbase + 4 * u, nsteps - 1);
+#pragma unroll
+        for (int q = 0; q < NT; ++q) {
+          xa[buf][u][q][0] = ldg16(xrow[q] + ks * 64);
+          xa[buf][u][q][1] = ldg16(xrow[q] + ks * 64 + 8);
+        }
+#pragma unroll
+        for (int jt = 0; jt < JP; ++jt) {
+          aa[buf][u][jt][0] = ldg16(arow[jt] + a_tile_off(0, ks, 0, p.K));
+          aa[buf][u][jt][1] = ldg16(arow[jt] + a_tile_off(0, ks, 1, p.K));
+        }
+      }
+    };
+    auto fma_step = [&](int buf, int sbase) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (sbase + 4 * u >= nsteps) break;
+#pragma unroll
+        for (int jt = 0; jt < JP; ++jt) {
+          float av[16];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t w[4] = {aa[buf][u][jt][h].x, aa[buf][u][jt][h].y, aa[buf][u][jt][h].z, aa[buf][u][jt][h].w};
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+              av[8 * h + 2 * d] = bf16_lo(w[d]);
+              av[8 * h + 2 * d + 1] = bf16_hi(w[d]);
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < NT; ++q) {
+            float s = acc[q][jt];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const uint32_t w[4] = {xa[buf][u][q][h].x, xa[buf][u][q][h].y, xa[buf][u][q][h].z, xa[buf][u][q][h].w};
+#pragma unroll
+              for (int d = 0; d < 4; ++d) {
+                s = __builtin_fmaf(bf16_lo(w[d]), av[8 * h + 2 * d], s);
+                s = __builtin_fmaf(bf16_hi(w[d]), av[8 * h + 2 * d + 1], s);
+              }
+            }
+            acc[q][jt] = s;
+          }
+        }
+      }
+    };
+    load(0, wave);
+    for (int st = wave; st < nsteps; st += 8 * U) {
+      load(1, st + 4 * U);
+      fma_step(0, st);
+      load(0, st + 8 * U);
+      fma_step(1, st + 4 * U);
+    }
+    // the four lane groups: rank li of each group sums over its 16 k
+#pragma unroll
+    for (int q = 0; q < NT; ++q)
+#pragma unroll
+      for (int jt = 0; jt < JP; ++jt) {
+        float v = acc[q][jt];
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        if (g == 0) red[wave][q][jt * 16 + li] = v;
+      }
+    __syncthreads();
+    for (int idx = tid; idx < NT * JP * 16; idx += 256) {
+      const int q = idx / (JP * 16), jj = idx % (JP * 16);
+      const int j = j_begin + jj;
+      const int pos = tok_begin + q;
+      if (pos < tok_end && j < r && j < p.r_lim) {
+        const float sum = ((red[0][q][jj] + red[1][q][jj]) + red[2][q][jj]) + red[3][q][jj];
+        p.t_out[(long)p.sorted_tok[s0 + pos] * p.r_lim + j] = sum;
+      }
+    }
+  }
+  // columns j in [r, r_max) of the caller's t are zero
+  if (jg == 0 && r < p.r_lim) {
+    const int w = p.r_lim - r;
+    for (int idx = tid; idx < (tok_end - tok_begin) * w; idx += 256) {
+      const int pos = tok_begin + idx / w;
+      p.t_out[(long)p.sorted_tok[s0 + pos] * p.r_lim + r + idx % w] = 0.f;
+    }
+  }
+}
+
+// ======================================================================================
 // Standalone up-projection: y[tok][n] = bf16( y[tok][n] + s_a * sum_j t[tok][j] B_a[j][n] ),
 // B_a stored transposed, bf16 [N][rank_pad(r_a)].  One workgroup per (token, 256 columns).
 // ======================================================================================
@@ -2442,6 +2576,40 @@ hipError_t shrink_cfg_attr(int tg, int jp, int u, int* regs, int* spill, int* ld
   return hipSuccess;
 }
 #undef LORA_SHRINK_CFGS
+
+// compiled configurations of the wave-reduction down-projection: NT tokens, JP rank tiles,
+// U k-steps per buffer
+#define LORA_BGMV_CFGS(X) \
+  X(1, 1, 1) X(1, 2, 1) X(1, 4, 1) X(2, 1, 1) X(2, 2, 1) X(2, 4, 1) X(4, 1, 1) X(4, 2, 1) X(4, 4, 1) \
+  X(1, 1, 2) X(1, 2, 2) X(1, 4, 2)
+
+hipError_t launch_shrink_bgmv(int nt, int jp, int u, int grid, hipStream_t s, const ShrinkParams& sp) {
+#define X(NT_, JP_, U_) \
+  if (nt == NT_ && jp == JP_ && u == U_) {                                                   \
+    hipLaunchKernelGGL((k_shrink_bgmv<NT_, JP_, U_>), dim3(grid), dim3(256), 0, s, sp);      \
+    return hipGetLastError();                                                                \
+  }
+  LORA_BGMV_CFGS(X)
+#undef X
+  return hipErrorInvalidValue;
+}
+
+hipError_t shrink_bgmv_attr(int nt, int jp, int u, int* regs, int* spill, int* lds) {
+  hipFuncAttributes fa{};
+  hipError_t e = hipErrorInvalidValue;
+#define X(NT_, JP_, U_)                                                                        \
+  if (nt == NT_ && jp == JP_ && u == U_) {                                                     \
+    e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(k_shrink_bgmv<NT_, JP_, U_>)); \
+    *lds = 4 * NT_ * JP_ * 16 * 4;                                                             \
+  }
+  LORA_BGMV_CFGS(X)
+#undef X
+  if (e != hipSuccess) return e;
+  *regs = fa.numRegs;
+  *spill = (int)fa.localSizeBytes;
+  return hipSuccess;
+}
+#undef LORA_BGMV_CFGS
 
 hipError_t launch_build_segments(const int* ids, int T, int n_ad, int* seg, int* sorted, int* err, hipStream_t s) {
   return launch_kn(k_build_segments, 1, SEG_THREADS, seg_lds_bytes(T, n_ad), s, ids, T, n_ad, seg, sorted, err);

@@ -154,6 +154,11 @@ hipError_t launch_merged(const uint16_t* x, int T, int K, int N, int fmt, const 
 // per lane, scratch (spill) bytes per lane and LDS bytes.
 hipError_t launch_shrink_cfg(int tg, int jp, int u, int grid, hipStream_t s, const ShrinkParams& sp);
 hipError_t shrink_cfg_attr(int tg, int jp, int u, int* regs, int* spill, int* lds);
+// the wave-reduction (BGMV) down-projection: NT positions of a segment and JP rank tiles per
+// workgroup, U k-steps per buffer (compiled for NT in {1, 2, 4} with JP in {1, 2, 4} and U = 1,
+// and NT = 1 with U = 2); one workgroup per item (adapter, token block, rank group)
+hipError_t launch_shrink_bgmv(int nt, int jp, int u, int grid, hipStream_t s, const ShrinkParams& sp);
+hipError_t shrink_bgmv_attr(int nt, int jp, int u, int* regs, int* spill, int* lds);
 hipError_t launch_layer(const LayerPlan& pl, hipStream_t stream, const ShrinkParams& sp, const GemmParams& gp);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_pack_weight(int fmt, const uint8_t* q, const uint8_t* sc, int N, int K, uint8_t* qp, uint8_t* scp,

@@ -247,10 +247,14 @@ def shrink_configured(x: torch.Tensor, seg: Segments, ad: Adapters, config, t: t
     return t
 
 
-def shrink_config_info(tg: int, jp: int, u: int) -> dict:
-    """Registers, spill bytes and LDS bytes of a compiled down-projection instance."""
+def shrink_config_info(tg: int, jp: int, u: int, nt: int = 1) -> dict:
+    """Registers, spill bytes and LDS bytes of a compiled down-projection instance (tg = 0:
+    the wave-reduction kernel with nt positions per item)."""
     out = (ctypes.c_int32 * 3)()
-    check("lora_shrink_config_info", lib().lora_shrink_config_info(tg, jp, u, out))
+    if tg == 0:
+        check("lora_shrink_bgmv_info", lib().lora_shrink_bgmv_info(nt, jp, u, out))
+    else:
+        check("lora_shrink_config_info", lib().lora_shrink_config_info(tg, jp, u, out))
     return {"regs": out[0], "spill": out[1], "lds": out[2]}
 
 

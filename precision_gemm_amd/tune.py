@@ -7,11 +7,13 @@ used as a practical heuristic rather than a guarantee of optimality.  Here, for 
 down-projection (``lora_shrink_configured``):
 
 * nodes -- configurations ``(TG, JP, U, M, ORD)``:
-    TG  in {1, 2, 4}   tiling: token tiles of 16 per inner step
-    JP  in {1, 2, 4}   tiling: rank tiles of 16 per workgroup item
-    U   in {1, 2}      caching: 64-wide k-steps held per register prefetch buffer
-    M   in {1, 2, 4}   scheduling: inner steps per item (TBLK = 16 TG M tokens of a segment)
-    ORD in {0, 1}      scheduling: items in workgroup-id order, or a contiguous run per XCD
+    TG  in {0, 1, 2, 4}  tiling: token tiles of 16 per inner step on bf16 MFMA; 0 is the
+                         wave-reduction kernel (BGMV: fp32 lane products, shuffle and LDS sums)
+    JP  in {1, 2, 4}     tiling: rank tiles of 16 per workgroup item
+    U   in {1, 2}        caching: 64-wide k-steps held per register prefetch buffer
+    M   in {1, 2, 4}     scheduling: inner steps per item (TBLK = 16 TG M tokens of a segment);
+                         for TG = 0 the positions of a segment per item (TBLK = M)
+    ORD in {0, 1}        scheduling: items in workgroup-id order, or a contiguous run per XCD
 * edges -- two configurations differing in one parameter by one step of its ordered domain;
 * hardware awareness -- a node is kept only if its compiled instance spills no registers to
   scratch memory and needs no more LDS than a workgroup may have (the instance's resources
@@ -21,8 +23,9 @@ down-projection (``lora_shrink_configured``):
   accept it with probability min(1, exp(-(c' - c) / (tau c))) on the measured cost c; the best
   node seen is the result.  Costs are cached, so a revisit costs nothing.
 
-Every configuration computes the same sums in the same order (the four waves of a workgroup
-split K the same way whatever the tile shape), so t is bitwise the same for all of them.
+Every MFMA configuration computes the same sums in the same order (the four waves of a
+workgroup split K the same way whatever the tile shape), so t is bitwise the same for all of
+them; the wave-reduction kernel sums in another order (t within fp32 rounding).
 """
 
 from __future__ import annotations
@@ -31,7 +34,7 @@ import math
 import random
 from dataclasses import dataclass, field
 
-DOMAINS = {"TG": (1, 2, 4), "JP": (1, 2, 4), "U": (1, 2), "M": (1, 2, 4), "ORD": (0, 1)}
+DOMAINS = {"TG": (0, 1, 2, 4), "JP": (1, 2, 4), "U": (1, 2), "M": (1, 2, 4), "ORD": (0, 1)}
 KEYS = ("TG", "JP", "U", "M", "ORD")
 LDS_LIMIT = 64 * 1024
 
@@ -59,17 +62,18 @@ def neighbours(node):
 def to_config(node):
     """The int32[5] configuration of lora_shrink_configured for a node."""
     tg, jp, u, m, order = node
-    return (tg, jp, u, 16 * tg * m, order)
+    return (tg, jp, u, m if tg == 0 else 16 * tg * m, order)
 
 
 def feasible(node, info, T: int):
-    """Hardware and shape constraints: no spill, LDS within a workgroup's share, and an item
-    no longer than twice the batch (longer items only idle)."""
+    """Hardware and shape constraints: a compiled instance (``info(tg, jp, u, m)`` is None
+    otherwise) with no spill and LDS within a workgroup's share, and an item no longer than
+    twice the batch (longer items only idle)."""
     tg, jp, u, m, _ = node
-    r = info(tg, jp, u)
+    r = info(tg, jp, u, m)
     if r is None or r["spill"] > 0 or r["lds"] > LDS_LIMIT:
         return False
-    return 16 * tg * m <= max(16, 2 * T)
+    return m <= max(1, 2 * T) if tg == 0 else 16 * tg * m <= max(16, 2 * T)
 
 
 def default_node(T: int):
@@ -134,13 +138,14 @@ def tune_shrink(x, seg, ad, steps: int = 40, reps: int = 20, tau: float = 0.05, 
     t = torch.empty((T, ad.r_max), dtype=torch.float32, device=x.device)
     infos = {}
 
-    def info(tg, jp, u):
-        if (tg, jp, u) not in infos:
+    def info(tg, jp, u, m):
+        key = (tg, jp, u, m if tg == 0 else 0)
+        if key not in infos:
             try:
-                infos[(tg, jp, u)] = ops.shrink_config_info(tg, jp, u)
+                infos[key] = ops.shrink_config_info(tg, jp, u, nt=m)
             except Exception:  # not compiled
-                infos[(tg, jp, u)] = None
-        return infos[(tg, jp, u)]
+                infos[key] = None
+        return infos[key]
 
     stream = torch.cuda.current_stream()
 

@@ -9,7 +9,7 @@ from precision_gemm_amd import tune
 
 def test_space_and_neighbours():
     nodes = tune.space()
-    assert len(nodes) == 3 * 3 * 2 * 3 * 2 and len(set(nodes)) == len(nodes)
+    assert len(nodes) == 4 * 3 * 2 * 3 * 2 and len(set(nodes)) == len(nodes)
     for n in nodes:
         nb = tune.neighbours(n)
         assert n not in nb and len(set(nb)) == len(nb)
@@ -17,7 +17,10 @@ def test_space_and_neighbours():
             assert n in tune.neighbours(m)                        # symmetric
             assert sum(a != b for a, b in zip(n, m)) == 1          # one parameter changes
         cfg = tune.to_config(n)
-        assert cfg[3] % 16 == 0 and cfg[3] == 16 * n[0] * n[3]
+        if n[0] == 0:
+            assert cfg[3] == n[3] and cfg[0] == 0          # wave reductions: positions per item
+        else:
+            assert cfg[3] % 16 == 0 and cfg[3] == 16 * n[0] * n[3]
     # connected: every node is reachable from the default of any batch size
     for T in (1, 16, 64, 128, 4096):
         start = tune.default_node(T)
@@ -32,13 +35,17 @@ def test_space_and_neighbours():
 
 
 def test_feasibility_prunes_spills_lds_and_long_items():
-    def info(tg, jp, u):
-        return {"regs": 128, "spill": 16 if (tg, jp, u) == (4, 4, 2) else 0, "lds": 4 * tg * jp * 256 * 4}
+    def info(tg, jp, u, m):
+        if tg == 0 and u == 2 and m != 1:
+            return None                                              # not compiled
+        return {"regs": 128, "spill": 16 if (tg, jp, u) == (4, 4, 2) else 0, "lds": 4 * max(tg, 1) * jp * 256 * 4}
     assert not tune.feasible((4, 4, 2, 1, 0), info, 4096)            # spills
     assert tune.feasible((4, 4, 1, 1, 0), info, 4096)                # 64 KB of LDS: fits
     assert not tune.feasible((4, 2, 1, 4, 0), info, 16)              # 256-token items for 16 tokens
     assert tune.feasible((1, 1, 2, 1, 0), info, 16)
     assert not tune.feasible((1, 1, 1, 1, 0), lambda *a: None, 16)   # not compiled
+    assert tune.feasible((0, 4, 1, 4, 0), info, 16) and not tune.feasible((0, 4, 2, 4, 0), info, 16)
+    assert not tune.feasible((0, 1, 1, 4, 1), info, 1)               # 4 positions per item for 1 token
 
 
 def test_metropolis_finds_the_minimum_and_is_reproducible():
