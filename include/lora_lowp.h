@@ -357,8 +357,8 @@ lora_status lora_pack_adapter_bwd(const uint16_t* A, const uint16_t* B, int32_t 
  *    without tokens);
  *  - status: device int32 or NULL; bit 1 is OR-ed in when an adapter with tokens has a rank
  *    outside [1, r_max] (its dA_a and dB_a are not written and its tokens get dY W_d^T only).
- * Arithmetic: dY W_d^T on bf16 MFMA with W widened to bf16 as code x channel scale (round to
- * nearest even: the dequantised weight in 16 bits) and fp32 accumulation; u by the forward's
+ * Arithmetic: dY W_d^T = (dY diag(w_scale)) codes^T on bf16 MFMA: dY times the channel scale
+ * rounded to bf16 (nearest even), the FP8 codes widened exactly, fp32 accumulation; u by the forward's
  * down-projection kernel (exact bf16 products, fp32 sums); the fp32 factors u, t of the
  * adapter products enter bf16 MFMAs as two bf16 terms each (about 17 bits).  Bitwise
  * deterministic.  Tokens whose adapter id is outside [0, n_adapters) get dY W_d^T only.

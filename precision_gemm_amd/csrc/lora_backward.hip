@@ -121,13 +121,13 @@ __device__ __forceinline__ int wave_min(int v) {
 //
 // Workgroup tile: 64 rows (tokens) x 256 columns (k), four waves of 64 x 64, two workgroups
 // per CU (their barriers are independent, so one's loads, widening and waits overlap the
-// other's MFMAs).  Per 64-channel step: dY [64][64] bf16 and the step's channel scales staged
-// in LDS (loaded a step ahead, double buffered); each wave reads its four W^T tiles (1 KB of
-// consecutive memory each) straight into registers, a step ahead, and widens them to bf16 as
-// code x channel scale (rounded to nearest even: the dequantised weight in 16 bits); two
-// bf16 MFMAs per 16 x 16 block cover the 64 channels (lane group g supplies channels
-// 16 g .. 16 g + 7 to the first and 16 g + 8 .. 16 g + 15 to the second, the same assignment
-// on both operands).
+// other's MFMAs).  dY W_d^T = (dY diag(s_w)) codes^T: per 64-channel step, dY [64][64] times
+// the step's channel scales, rounded to bf16 (nearest even), is staged in LDS (loaded a step
+// ahead, double buffered; each value scaled once per workgroup); each wave reads its four W^T
+// tiles (1 KB of consecutive memory each) straight into registers, a step ahead, and widens
+// the codes to bf16 exactly (one conversion per two codes); two bf16 MFMAs per 16 x 16 block
+// cover the 64 channels (lane group g supplies channels 16 g .. 16 g + 7 to the first and
+// 16 g + 8 .. 16 g + 15 to the second, the same assignment on both operands).
 // Adapter term: the rows' s_a u[t] split into two bf16 terms and staged in LDS; for each
 // adapter present in the tile (in increasing id order) and each 32 ranks, two MFMAs per
 // block with the rows of other adapters zeroed and A_a rows [K][rank_pad] as the other
@@ -140,7 +140,6 @@ constexpr int BX_BUF = BX_ROWS * BX_RS; // one staged step
 
 __global__ __launch_bounds__(256, 2) void k_bwd_dx(BwdDxParams p) {
   __shared__ __align__(16) uint8_t lds[2 * BX_BUF];
-  __shared__ __align__(16) float lsc[2 * 64];   // channel scales of the staged steps
   __shared__ int rid[BX_ROWS];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, i = lane & 15, g = lane >> 4;
 
@@ -162,8 +161,10 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dx(BwdDxParams p) {
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) wp[ct] = p.wt + ((long)min((k0w >> 4) + ct, nkt - 1) * NI * 64 + lane) * 16;
 
-  auto load_dy = [&](uint4 (&d)[2], float4& sv, int st) {
-    sv = ldg16f(p.wsc + 64 * st + 4 * (tid & 15));
+  // dY staging: the thread's 8 channels 64 st + 8 spart .. + 7 share their 8 scales (two rows)
+  auto load_dy = [&](uint4 (&d)[2], float4 (&sv)[2], int st) {
+    sv[0] = ldg16f(p.wsc + 64 * st + 8 * spart);
+    sv[1] = ldg16f(p.wsc + 64 * st + 8 * spart + 4);
 #pragma unroll
     for (int q = 0; q < 2; ++q) d[q] = ldg16(dyp[q] + 64 * st);
   };
@@ -171,18 +172,24 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dx(BwdDxParams p) {
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) wv[ct] = ldg16(wp[ct] + (long)st * 1024);
   };
-  auto store_dy = [&](const uint4 (&d)[2], const float4& sv, int buf) {
+  // dY x channel scale -> bf16 (round to nearest even) into LDS buffer buf
+  auto store_dy = [&](const uint4 (&d)[2], const float4 (&sv)[2], int buf) {
+    const float sc[8] = {sv[0].x, sv[0].y, sv[0].z, sv[0].w, sv[1].x, sv[1].y, sv[1].z, sv[1].w};
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-      *reinterpret_cast<uint4*>(lds + buf * BX_BUF + (srow + 32 * q) * BX_RS + 16 * spart) = d[q];
-    // 16 threads per slot write the same value: no branch
-    *reinterpret_cast<float4*>(lsc + 64 * buf + 4 * (tid & 15)) = sv;
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t wv[4] = {d[q].x, d[q].y, d[q].z, d[q].w};
+      uint32_t o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = bf16x2_rne(bf16_lo(wv[e]) * sc[2 * e], bf16_hi(wv[e]) * sc[2 * e + 1]);
+      *reinterpret_cast<uint4*>(lds + buf * BX_BUF + (srow + 32 * q) * BX_RS + 16 * spart) =
+          make_uint4(o[0], o[1], o[2], o[3]);
+    }
   };
 
   // W^T of a step is loaded a step ahead into one of two register sets used alternately (no
   // register copies, which would wait for the loads): N / 64 steps, an even number
   uint4 dn[2], wA[4], wB[4];
-  float4 sn;
+  float4 sn[2];
   load_dy(dn, sn, 0);
   load_w(wA, 0);
   store_dy(dn, sn, 0);
@@ -199,31 +206,14 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dx(BwdDxParams p) {
     load_dy(dn, sn, nx);
     load_w(wn, nx);
     __builtin_amdgcn_sched_barrier(0);  // the loads stay at the top: a whole step hides them
-    // W^T codes -> bf16 (code x channel scale, round to nearest even)
-    const float* ls = lsc + 64 * (it & 1) + 16 * g;
-    float s16[16];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float4 v = *reinterpret_cast<const float4*>(ls + 4 * e);
-      s16[4 * e] = v.x; s16[4 * e + 1] = v.y; s16[4 * e + 2] = v.z; s16[4 * e + 3] = v.w;
-    }
+    // W^T codes -> bf16, exact: codes e = 8 s .. 8 s + 7 of the lane's 16 are operand s
     uint4 wb[4][2];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
-      const uint32_t d[4] = {wc[ct].x, wc[ct].y, wc[ct].z, wc[ct].w};
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        uint32_t o[4];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const v2f a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(d[2 * s + h], 1.0f, false);
-          const v2f b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(d[2 * s + h], 1.0f, true);
-          const int e0 = 8 * s + 4 * h;
-          o[2 * h] = bf16x2_rne(a.x * s16[e0], a.y * s16[e0 + 1]);
-          o[2 * h + 1] = bf16x2_rne(b.x * s16[e0 + 2], b.y * s16[e0 + 3]);
-        }
-        wb[ct][s] = make_uint4(o[0], o[1], o[2], o[3]);
-      }
+      const uint2 c0 = fp8x4_to_bf16(wc[ct].x), c1 = fp8x4_to_bf16(wc[ct].y);
+      const uint2 c2 = fp8x4_to_bf16(wc[ct].z), c3 = fp8x4_to_bf16(wc[ct].w);
+      wb[ct][0] = make_uint4(c0.x, c0.y, c1.x, c1.y);
+      wb[ct][1] = make_uint4(c2.x, c2.y, c3.x, c3.y);
     }
     const uint8_t* B0 = lds + (it & 1) * BX_BUF;
 #pragma unroll
