@@ -143,7 +143,10 @@ enum {
    * and the products run on bf16 MFMA with fp32 accumulation; the FP8 channel scale
    * and the adapter terms are applied as without the flag.  Any T: up to 16 tokens the
    * decode stream; above, 64-token x 128-channel tiles with bf16 x staged in LDS where
-   * N % 128 == 0, else 16-token tiles of the decode stream (much slower for large T). */
+   * N % 128 == 0, else 16-token tiles of the decode stream (much slower for large T).
+   * Past 128 tokens with FP8 W and N % 256 == 0 the fused call first runs the
+   * down-projection in a launch of its own (plain fp32 t, into t or the workspace) and
+   * then the GEMM in 64 x 256 tiles, two workgroups per CU. */
   LORA_ACT_BF16 = 1u << 2
 };
 

@@ -76,6 +76,10 @@ LayerPlan make_plan(int T, int K, int N, int n_ad, int r_max_in, int fmt, bool f
       pl.TT = 4;
     }
   }
+  // 16-bit activations past 128 tokens (FP8, N % 256 == 0): the down-projection runs first,
+  // over 16-position blocks of the sorted order, and writes plain fp32 t; the GEMM then has
+  // the whole GPU, in 64 x 256 tiles (two workgroups per CU) whose epilogue adds the term
+  pl.rows16 = a16 && T > 128 && fmt == LORA_W_FP8_E4M3 && N % 256 == 0;
   pl.KC = (pl.TT == 1) ? 2048 : ((pl.TT <= 4 && pl.CT == 1) ? 512 : (pl.CT == 4 ? 128 : 256));
   const int WN = pl.WC * pl.CT * 16;
   pl.n_cb = N / WN;
@@ -136,7 +140,7 @@ LayerPlan make_plan(int T, int K, int N, int n_ad, int r_max_in, int fmt, bool f
   if (pl.ksplit > 1) off += round256((size_t)tiles * pl.ksplit * pl.WC * pl.TT * pl.CT * 256 * 4);
   pl.off_xq = off;    if (pl.XQ) off += round256((size_t)T * K);
   pl.off_xsc = off;   if (pl.XQ) off += round256((size_t)T * (K / 32) + 8);  // + 8: padding read by a partial last chunk
-  pl.off_tpl = off;   if (pl.XQ && pl.s_cfg == 1) off += round256((size_t)T * r_max * 4);
+  pl.off_tpl = off;   if ((pl.XQ || pl.rows16) && pl.s_cfg == 1) off += round256((size_t)T * r_max * 4);
   pl.total = off;
   return pl;
 }
@@ -333,6 +337,29 @@ lora_status layer_call(const uint16_t* x, int32_t T, int32_t K, int32_t N, int32
     sp.compact = pl.compact ? 1 : 0;
     sp.spin_limit = SPIN_LIMIT;
   };
+  if (pl.rows16) {
+    float* t16 = fused ? (t ? t : reinterpret_cast<float*>(ws + pl.off_tpl)) : t;
+    if (fused) {
+      if (build && launch_build_segments(adapter_id, T, n_adapters, seg_indptr, sorted_tok, ctrl + CTRL_SEGERR, s) !=
+                       hipSuccess)
+        return LORA_ERR_HIP;
+      shrink_params();
+      sp.t_out = t16;
+      if (launch_shrink_rows(sp, s) != hipSuccess) return LORA_ERR_HIP;
+    }
+    GemmParams gp{};
+    gp.x = x; gp.T = T; gp.K = K; gp.N = N;
+    gp.wq = w_q;
+    gp.ws_fp8 = reinterpret_cast<const float*>(w_scale);
+    gp.t = t16;
+    gp.r_max = rank_pad(r_max);
+    gp.r_lim = r_max;
+    gp.ids = adapter_id; gp.B_ptrs = B_ptrs; gp.ranks = ranks; gp.scales = scales; gp.n_ad = n_adapters;
+    gp.y = y;
+    gp.lora = lora ? 1 : 0;
+    gp.ctrl = ctrl;
+    return launch_gemm_a16(gp, s) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+  }
   if (pre_shrink) {
     // the segments first (above 128 tokens never in the layer launch), then the pre-pass
     if (build && launch_build_segments(adapter_id, T, n_adapters, seg_indptr, sorted_tok, ctrl + CTRL_SEGERR, s) !=

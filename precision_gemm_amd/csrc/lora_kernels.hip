@@ -31,6 +31,8 @@
 #include "device_common.hpp"
 #include "lora_kernels.hpp"
 
+#include <type_traits>
+
 namespace lora {
 
 // ======================================================================================
@@ -2613,6 +2615,221 @@ hipError_t shrink_bgmv_attr(int nt, int jp, int u, int* regs, int* spill, int* l
 
 hipError_t launch_build_segments(const int* ids, int T, int n_ad, int* seg, int* sorted, int* err, hipStream_t s) {
   return launch_kn(k_build_segments, 1, SEG_THREADS, seg_lds_bytes(T, n_ad), s, ids, T, n_ad, seg, sorted, err);
+}
+
+// ======================================================================================
+// The 16-bit-activation GEMM of a long batch (FP8 W, N % 256 == 0; t from the pre-pass's
+// down-projection): y = bf16(s_w (x . codes) + s_a t B_a) on bf16 MFMA.  A 64-token x
+// 256-channel tile per workgroup, four waves of 64 x 64, two workgroups per CU (their
+// barriers are independent, so one's loads, widening and waits overlap the other's MFMAs).
+// Per 128-wide k-step the tile's bf16 x rows [64][128] are staged in LDS a step ahead, double
+// buffered; each wave loads its four packed W tiles (2 KB of consecutive memory each) a step
+// ahead into one of two alternating register sets, widens the codes exactly (one conversion
+// per two codes) and issues 64 MFMAs: lane group g's 32 codes of a tile (k = 16 g .., 16 g + 8
+// .., 64 + 16 g .., 72 + 16 g ..) are four operands, each paired with the x piece at the
+// same k.  The loads are pinned at the top of the step.  Epilogue as for the MXFP8 tiles:
+// the channel scale, the adapter term per adapter present (s_a t rounded to bf16, one bf16
+// MFMA per 32 ranks and block), bf16 stores through LDS.  Workgroups are dealt to the XCDs
+// in turn; XCD x takes a contiguous run of tiles in row-block-major order (the column blocks
+// of a row block share its x rows in L2).
+// ======================================================================================
+constexpr int GA_XRS = 256 + 16;      // LDS row stride of a staged step: 128 bf16 + 16 bytes
+constexpr int GA_XBUF = 64 * GA_XRS;  // one staged k-step of the tile's 64 rows
+constexpr int GA_ERS = 144;           // row stride of the epilogue's staging (64 bf16 + 16 bytes)
+
+__global__ __launch_bounds__(256, 2) void k_gemm_a16(GemmParams p) {
+  __shared__ __align__(16) uint8_t lds[2 * GA_XBUF];
+  __shared__ int rid[64];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, i = lane & 15, g = lane >> 4;
+  const int K = p.K, N = p.N, T = p.T;
+  const int n_tb = (T + 63) >> 6, n_cb = N >> 8;
+  const int ntiles = n_tb * n_cb;
+  int tile = blockIdx.x;
+  if ((ntiles & 7) == 0) tile = (tile & 7) * (ntiles >> 3) + (tile >> 3);
+  const int tb = tile / n_cb, cb = tile % n_cb;
+  const int t0 = 64 * tb, n0w = 256 * cb + 64 * w;
+  const int NS = K >> 7;
+
+  // staging: thread loads pieces P = tid + 256 m (m = 0..3), row P / 16 at 16 (P % 16) bytes
+  const int prow = tid >> 4, ppart = tid & 15;
+  const uint16_t* xrow[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) xrow[m] = p.x + (long)min(t0 + prow + 16 * m, T - 1) * K + 8 * ppart;
+  const uint8_t* wrow[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) wrow[ct] = p.wq + (long)((n0w >> 4) + ct) * NS * 2048 + lane * 16;
+
+  auto load_x = [&](uint4 (&d)[4], int st) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) d[m] = ldg16(xrow[m] + 128 * st);
+  };
+  auto load_w = [&](uint4 (&lo)[4], uint4 (&hi)[4], int st) {
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      lo[ct] = ldg16(wrow[ct] + (long)st * 2048);
+      hi[ct] = ldg16(wrow[ct] + (long)st * 2048 + 1024);
+    }
+  };
+  auto store_x = [&](const uint4 (&d)[4], int buf) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      *reinterpret_cast<uint4*>(lds + buf * GA_XBUF + (prow + 16 * m) * GA_XRS + 16 * ppart) = d[m];
+  };
+
+  uint4 xd[4], wl[2][4], wh[2][4];
+  load_x(xd, 0);
+  load_w(wl[0], wh[0], 0);
+  store_x(xd, 0);
+  __syncthreads();
+
+  v4f acc[4][4];
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) acc[tt][ct] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // one 128-wide step: register set C holds W of step it, set 1 - C receives step it + 1
+  auto step = [&](int it, auto set) {
+    constexpr int C = decltype(set)::value;
+    const int nx = min(it + 1, NS - 1);  // the last step reloads itself: uniform code
+    load_x(xd, nx);
+    load_w(wl[1 - C], wh[1 - C], nx);
+    __builtin_amdgcn_sched_barrier(0);  // the loads stay at the top: a whole step hides them
+    const uint8_t* B0 = lds + (it & 1) * GA_XBUF;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const uint8_t* ra = B0 + (16 * tt + i) * GA_XRS + 32 * g;
+      const uint4 xa[4] = {*reinterpret_cast<const uint4*>(ra), *reinterpret_cast<const uint4*>(ra + 16),
+                           *reinterpret_cast<const uint4*>(ra + 128), *reinterpret_cast<const uint4*>(ra + 144)};
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const uint2 c0 = fp8x4_to_bf16(wl[C][ct].x), c1 = fp8x4_to_bf16(wl[C][ct].y);
+        const uint2 c2 = fp8x4_to_bf16(wl[C][ct].z), c3 = fp8x4_to_bf16(wl[C][ct].w);
+        const uint2 c4 = fp8x4_to_bf16(wh[C][ct].x), c5 = fp8x4_to_bf16(wh[C][ct].y);
+        const uint2 c6 = fp8x4_to_bf16(wh[C][ct].z), c7 = fp8x4_to_bf16(wh[C][ct].w);
+        acc[tt][ct] = mfma_bf16_16x16x32(xa[0], make_uint4(c0.x, c0.y, c1.x, c1.y), acc[tt][ct]);
+        acc[tt][ct] = mfma_bf16_16x16x32(xa[1], make_uint4(c2.x, c2.y, c3.x, c3.y), acc[tt][ct]);
+        acc[tt][ct] = mfma_bf16_16x16x32(xa[2], make_uint4(c4.x, c4.y, c5.x, c5.y), acc[tt][ct]);
+        acc[tt][ct] = mfma_bf16_16x16x32(xa[3], make_uint4(c6.x, c6.y, c7.x, c7.y), acc[tt][ct]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // the next step's staging waits for its loads only here
+    store_x(xd, (it + 1) & 1);
+    __syncthreads();
+  };
+  int it = 0;
+  for (; it + 1 < NS; it += 2) {
+    step(it, std::integral_constant<int, 0>{});
+    step(it + 1, std::integral_constant<int, 1>{});
+  }
+  if (it < NS) step(it, std::integral_constant<int, 0>{});
+
+  // ---- epilogue: FP8 channel scale of the lane's columns
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    const float cs = p.ws_fp8[n0w + 16 * ct + i];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) acc[tt][ct] *= cs;
+  }
+  // ---- adapter term: s_a t[row] @ B_a for the adapter of each row
+  const int srow = tid >> 3, spart = tid & 7;  // the epilogue's staging: rows srow + 32 q, 16-byte part spart
+  if (p.lora) {
+    if (tid < 64) {
+      const int t = t0 + tid;
+      int a = -1;
+      if (t < T) {
+        a = p.ids[t];
+        if (a < 0 || a >= p.n_ad) {
+          a = -1;
+        } else {
+          const int r = p.ranks[a];
+          if (r < 1 || r > p.r_lim) {
+            or_agent(p.ctrl + CTRL_STATUS, 2);  // reported: the adapter's term is left out
+            a = -1;
+          }
+        }
+      }
+      rid[tid] = a;
+    }
+    __syncthreads();
+    // s_a t as bf16, [row][64 ranks] in LDS (zero past the rank and for other rows)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int row = srow + 32 * q;
+      const int a = rid[row];
+      uint32_t o[4] = {0u, 0u, 0u, 0u};
+      if (a >= 0) {
+        const int r = p.ranks[a];
+        const float sa = p.scales[a];
+        const float* trow = p.t + (long)(t0 + row) * p.r_lim;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const int j = 8 * spart + 2 * d;
+          o[d] = bf16x2_rne(j < r ? sa * trow[j] : 0.f, j + 1 < r ? sa * trow[j + 1] : 0.f);
+        }
+      }
+      *reinterpret_cast<uint4*>(lds + row * GA_ERS + 16 * spart) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+    __syncthreads();
+    int prev = -1;
+    for (;;) {
+      const int c = rid[lane];
+      int m = c > prev ? c : 0x7fffffff;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) m = min(m, __shfl_xor(m, o, 64));
+      if (m == 0x7fffffff) break;
+      const int a = __builtin_amdgcn_readfirstlane(m);
+      prev = a;
+      const int r = p.ranks[a], rp = rank_pad(r);
+      const uint16_t* Bt = reinterpret_cast<const uint16_t*>(p.B_ptrs[a]);
+      for (int rs = 0; 32 * rs < r; ++rs) {
+        const int jj = 32 * rs + 8 * g;
+        const int off = min(jj, rp - 8);
+        uint4 bop[4];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) bop[ct] = keep_bf16(ldg16(Bt + (long)(n0w + 16 * ct + i) * rp + off), r - jj);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          const int row = 16 * tt + i;
+          const uint4 ah = (rid[row] == a) ? *reinterpret_cast<const uint4*>(lds + row * GA_ERS + 64 * rs + 16 * g)
+                                           : zero4();
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) acc[tt][ct] = mfma_bf16_16x16x32(ah, bop[ct], acc[tt][ct]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- bf16 stores through LDS, 32 rows per pass: wave w's region holds its 32 x 64 block
+  uint8_t* reg = lds + w * (32 * GA_ERS);
+#pragma unroll
+  for (int ph = 0; ph < 2; ++ph) {
+#pragma unroll
+    for (int tq = 0; tq < 2; ++tq)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          *reinterpret_cast<uint16_t*>(reg + (16 * tq + 4 * g + v) * GA_ERS + 2 * (16 * ct + i)) =
+              (uint16_t)f32_to_bf16_rne(acc[2 * ph + tq][ct][v]);
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int idx = lane + 64 * c;  // 32 rows x 8 parts of 16 bytes
+      const int row = idx >> 3, part = idx & 7;
+      const int t = t0 + 32 * ph + row;
+      const uint4 v = *reinterpret_cast<const uint4*>(reg + row * GA_ERS + 16 * part);
+      if (t < T) *reinterpret_cast<uint4*>(p.y + (long)t * N + n0w + 8 * part) = v;
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_gemm_a16(const GemmParams& gp, hipStream_t s) {
+  const int grid = ((gp.T + 63) / 64) * (gp.N / 256);
+  hipLaunchKernelGGL(k_gemm_a16, dim3(grid), dim3(256), 0, s, gp);
+  return hipGetLastError();
 }
 
 hipError_t launch_quant(const uint16_t* x, int T, int K, uint8_t* xq, uint8_t* xsc, hipStream_t s) {

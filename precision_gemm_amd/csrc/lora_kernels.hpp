@@ -119,6 +119,7 @@ struct LayerPlan {
   int s_cfg;           // down-projection tile shape: 0 decode, 1 prefill
   int occ = 1;         // workgroups per CU the one-tile stream kernel is built for
   bool a16 = false;    // base product on the bf16 activations as they are (bf16 MFMA)
+  bool rows16 = false; // a16 long batch (FP8, N % 256 == 0): t by the rows pre-pass, then k_gemm_a16
   int KC;              // K-chunk staged in LDS
   int ksplit, krange, n_cb, n_tb, n_gemm_wg;
   // down-projection decomposition
@@ -133,6 +134,8 @@ struct LayerPlan {
 
 hipError_t launch_build_segments(const int* ids, int T, int n_ad, int* seg, int* sorted, int* err, hipStream_t s);
 hipError_t launch_quant(const uint16_t* x, int T, int K, uint8_t* xq, uint8_t* xsc, hipStream_t s);
+// the 16-bit-activation GEMM of a long batch: 64 x 256 tiles, FP8 W (N % 256 == 0), plain t
+hipError_t launch_gemm_a16(const GemmParams& gp, hipStream_t s);
 // the segment builder and the MXFP8 pre-pass in one launch (independent of each other)
 // the MXFP8 pre-pass with the down-projection items (plan with 64-token items) beside it
 hipError_t launch_quant_shrink(const LayerPlan& pl, const ShrinkParams& sp, const uint16_t* x, int T, int K, uint8_t* xq,

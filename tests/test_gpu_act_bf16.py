@@ -8,7 +8,9 @@ built in the launch); the 64-token gate-up and the 4096-token prefill workloads 
 tiles, prefill on sampled rows); 16-token batches at the gate-up and MXFP4 down-projection
 shapes; ragged, tiny and many-adapter shapes in both formats, on 64 x 128 tiles and, where
 N % 128 != 0, on 16-token stream tiles with column-tile counts of 6 and 10 (the XCD
-grouping with and without a tail)."""
+grouping with and without a tail); past 128 tokens with FP8 and N % 256 == 0, the
+down-projection pre-pass and 64 x 256 tiles (one row past a tile, a ragged last tile,
+segments built by the call)."""
 
 import numpy as np
 import pytest
@@ -74,6 +76,9 @@ CASES = [
     (130, 1024, 320, "fp8", [16, 64] * 32, 49),           # stream tiles, 10 column tiles (8 + a tail of 2)
     (300, 768, 256, "fp8", [48, 8, 16, 64], 50),          # down-projection items of 64 tokens
     (200, 4096, 256, "mxfp4", [64, 8, 32, 16, 48] * 14, 51),
+    # past 128 tokens, FP8, N % 256 == 0: the rows pre-pass then 64 x 256 tiles
+    (129, 640, 512, "fp8", [8, 64, 24], 53),              # one row past two token tiles
+    (1000, 1152, 768, "fp8", [16, 32] * 20, 54),          # 3 column blocks, 16 token tiles (last ragged)
 ]
 
 
@@ -90,14 +95,15 @@ def test_shapes_bf16_activations(case, fused):
     _check(wl, g, str(case))
 
 
-def test_bf16_activations_deterministic_and_segments_in_prepass_launch():
-    print("[case] act_bf16 T=300 build, determinism", flush=True)
+@pytest.mark.parametrize("N", [384, 512], ids=["tiles_64x128", "tiles_64x256"])
+def test_bf16_activations_deterministic_and_segments_built(N):
+    print(f"[case] act_bf16 T=300 N={N} build, determinism", flush=True)
     rng = np.random.default_rng(52)
     ids = rng.integers(0, 6, 300)
-    wl = workloads.make_custom(300, 1024, 384, "fp8", [8, 16, 32, 64, 16, 8], ids, [1.0] * 6, 52,
+    wl = workloads.make_custom(300, 1024, N, "fp8", [8, 16, 32, 64, 16, 8], ids, [1.0] * 6, 52,
                                a_std=0.1, b_std=0.05)
     g1 = run_gpu(wl, fused=True, build=True, act_bf16=True)
     g2 = run_gpu(wl, fused=True, act_bf16=True)
     assert g1["status"] == 0 and g1["err"] == 0
     assert np.array_equal(g1["y_bits"], g2["y_bits"])
-    _check(wl, g1, "T300 build")
+    _check(wl, g1, f"T300 N={N} build")

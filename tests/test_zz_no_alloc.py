@@ -17,7 +17,8 @@ CALLS = [
     (16, 2048, 256, "fp8", [1, 20, 60], (True, False)),          # smaller: the one-tile stream
     (100, 4096, 512, "mxfp4", [8, 16, 64], (False, False)),      # larger again: K-split partials
     (100, 4096, 512, "mxfp4", [8, 16, 64], (False, False)),      # same layout twice (no re-clear)
-    (48, 1024, 512, "fp8", [16] * 6, (True, True)),              # 16-bit activations
+    (200, 512, 512, "fp8", [8, 32], (True, True)),               # 16-bit activations, t in the scratch
+    (48, 1024, 512, "fp8", [16] * 6, (True, True)),              # 16-bit activations, smaller
 ]
 
 
