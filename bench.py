@@ -649,7 +649,10 @@ def main():
     sha = kernel_source_sha()
     tag = args.workload + ("_act_bf16" if a16 else "")
     roof["traffic"] = stored_traffic(tag, sha)
-    roof["kernel"] = ("layer call: k_layer (down-projection + bf16-MFMA GEMM on widened W + LoRA epilogue)"
+    a16_rows = a16 and wl.T > 128 and wl.fmt == "fp8" and wl.N % 256 == 0
+    roof["kernel"] = ("layer call: k_prep_rows (down-projection, plain t) + k_gemm_a16 (64 x 256 tiles, "
+                      "bf16-MFMA GEMM on widened W + LoRA epilogue)" if a16_rows else
+                      "layer call: k_layer (down-projection + bf16-MFMA GEMM on widened W + LoRA epilogue)"
                       if a16 else "layer call: MXFP8 pre-pass above 16 tokens (with the down-projection above 128 "
                       "tokens) + k_layer (scaled-MFMA GEMM + LoRA epilogue; down-projection in the same launch up "
                       "to 128 tokens)")

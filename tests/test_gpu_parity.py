@@ -3,7 +3,7 @@
 Bars: segment metadata and MXFP8 codes bit-exact; t within 1e-4 relative Frobenius;
 y within max|y - y_ref| <= 1e-2 max|y_ref| and relative Frobenius <= 5e-3.
 Cases: the five named workloads at full size (fused and unfused schedules), ragged
-and tiny shapes, mixed ranks, empty adapters, zero B / zero W, a LoRA-heavy input,
+and tiny shapes, long batches of many tiles (ragged, N / 256 odd, every schedule), mixed ranks, empty adapters, zero B / zero W, a LoRA-heavy input,
 bad adapter ids, bitwise determinism."""
 
 import numpy as np
@@ -199,6 +199,35 @@ def test_edge_shapes(case, fused):
     assert g["status"] == 0
     assert_y_close(g["y"], ref["y"], str(case))
     assert_t_close(g["t"].astype(np.float64), ref["t"], str(case))
+
+
+LONG = [
+    # T, K, N, ranks, seed: long batches of many tiles (128 x 256 tiles, pre-pass down-projection)
+    (4100, 256, 4096, [1, 4, 12, 20, 60, 64], 31),  # 33 x 16 tiles, XCD-grouped order; a 4-row last token tile
+    (3100, 384, 5376, [16, 64, 8], 32),              # 25 x 21 = 525 tiles: plain order
+]
+
+
+@pytest.mark.parametrize("case", LONG, ids=[f"T{c[0]}_K{c[1]}_N{c[2]}_a{len(c[3])}" for c in LONG])
+@pytest.mark.parametrize("mode", ["fused", "fused_t_in_workspace", "unfused", "base_only", "build"])
+def test_long_batch_shapes(case, mode):
+    T, K, N, ranks, seed = case
+    print(f"[case] long batch {case} {mode}", flush=True)
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(0, len(ranks), T)
+    wl = _custom(T, K, N, "fp8", ranks, ids, seed, a_std=0.1, b_std=0.05)
+    # sampled rows, both ends of every segment, and every row of the last (partial) token tiles
+    rows = tuple(sorted(set(sample_rows(wl, 256, seed)) | set(range(256 * (T // 256), T))))
+    ref = run_oracle(wl, rows)
+    g = run_gpu(wl, fused=(mode != "unfused"), want_t=(mode != "fused_t_in_workspace"),
+                base_only=(mode == "base_only"), build=(mode == "build"))
+    assert g["status"] == 0 and g["err"] == 0
+    sel = np.asarray(rows)
+    key = "y_base" if mode == "base_only" else "y"
+    m, f = assert_y_close(g["y"][sel], ref[key], f"{case} {mode}")
+    if "t" in g:
+        assert_t_close(g["t"][sel].astype(np.float64), ref["t"], f"{case} {mode}")
+    print(f"  y max_rel={m:.2e} frob={f:.2e}", flush=True)
 
 
 def test_zero_b_equals_base_only_and_zero_w_gives_lora():
