@@ -355,6 +355,17 @@ def backward_flops(wl):
     return 2.0 * wl.T * wl.K * wl.N + float(np.sum(4.0 * r_tok * (wl.K + wl.N)))
 
 
+def backward_bytes(wl):
+    """Algorithmic bytes of one backward call: x, dY and dX in bf16 (T K, T N, T K), the 8-bit
+    W^T codes and their channel scales (N K + 4 N), u and the forward t in fp32 (2 T r_max), and
+    per adapter present B_a and A_a in bf16 (2 r_a (N + K) each) and dA_a, dB_a in fp32
+    (4 r_a (K + N) each)."""
+    present = sorted(set(int(a) for a in np.asarray(wl.ids)))
+    r_max = int(max(wl.ranks))
+    per_ad = sum(6.0 * int(wl.ranks[a]) * (wl.K + wl.N) for a in present)
+    return (2.0 * wl.T * (2 * wl.K + wl.N) + wl.N * wl.K + 4.0 * wl.N + 8.0 * wl.T * r_max + per_ad)
+
+
 def backward(args, wl):
     """A step is one lora_backward call (u, dA and dB, dX) on the workload's batch with a
     seeded dY; K calls in one HIP graph, timed with HIP events on the launch stream; two input
@@ -431,11 +442,20 @@ def backward(args, wl):
                    "adapters": wl.n_adapters, "ranks": sorted(set(int(r) for r in wl.ranks)),
                    "timing": "hip graph of K steps"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None, "call_us": call_us,
-                     "per_call_flops": flops,
+                     "frac": achieved / BF16_PEAK_TFLOPS,
+                     "traffic": stored_traffic(args.workload + "_backward", kernel_source_sha()), "call_us": call_us,
+                     "per_call_flops": flops, "per_call_bytes": backward_bytes(wl),
                      "kernel": "backward call: down-projection of dY (u) + k_bwd_grad (dA, dB) + k_bwd_dx"},
         "parity": parity, "kernel_sha": kernel_source_sha(),
     }
+    if args.copy_mb > 0:  # counter calibration: three device copies of known size after the timed region
+        src = torch.ones(args.copy_mb << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = src.numel()
+        del src, dst
     if not args.no_cpu:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
