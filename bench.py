@@ -81,7 +81,7 @@ def cpu_baseline(wl, budget_s: float = 12.0, act: str = "mxfp8"):
         layer(wl.x[rows], w, wl.A, wl.B, wl.scale, np.asarray(wl.ids)[rows], act=act)
         runs += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or runs >= 50:
+        if el >= budget_s or runs >= 1000:  # the time budget binds: about 12 s of oracle work
             break
     per_call = el / runs * (wl.T / len(rows))      # scaled to one whole layer call
     sample = (f"{runs} oracle run(s) of the whole layer" if len(rows) == wl.T else
@@ -466,7 +466,7 @@ def backward(args, wl):
                              dy_bits[sub])
             runs += 1
             el = time.perf_counter() - c0
-            if el >= 12.0 or runs >= 50:
+            if el >= 12.0 or runs >= 1000:
                 break
         out["cpu_baseline"] = {"value": el / runs * (wl.T / len(sub)) * 1e6, "unit": "us/call", "cores": int(cores),
                                "kind": "oracle",
