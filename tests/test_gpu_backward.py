@@ -13,8 +13,9 @@ Tolerances, from the arithmetic the header states:
   <= 1e-5 against dY B_a^T.
 Cases: the tiny and the 4096-token prefill shapes of the layer, a ragged batch (T not a
 multiple of 128, K not a multiple of 256) with mixed ranks 1..60 in random order, several
-row blocks with contiguous segments, an adapter without tokens, t from the GPU's own
-forward, T = 0, an invalid rank, and bitwise repeatability.
+row blocks with contiguous segments, an adapter without tokens, largest ranks 62, 21, 40
+and 30 (two to four rank tiles in the gradient kernel), t from the GPU's own forward, T = 0,
+an invalid rank, and bitwise repeatability.
 """
 
 import functools
@@ -44,6 +45,12 @@ CASES = {
     "ragged_mixed": (77, 640, 384, [1, 12, 20, 60], "random"),
     "contig_rows": (300, 1024, 512, [16, 64, 8, 32], "contig"),
     "empty_adapter": (130, 512, 256, [16, 24, 8], "skip1"),
+    # the gradient kernel's rank tiles: largest ranks 62 (four tiles, the last partial), 21
+    # (two, the second holding one rank), 40 (three), 30 (two, with a rank-1 adapter)
+    "rmax62": (150, 512, 256, [62, 5, 33], "random"),
+    "rmax21": (100, 384, 256, [21, 3], "random"),
+    "rmax40": (90, 256, 384, [40, 17], "random"),
+    "rmax30": (100, 384, 256, [30, 7, 1], "contig"),
 }
 
 
@@ -149,7 +156,8 @@ def check_against_oracle(wl, dy, g, ref, what):
     return m, f, gfrob
 
 
-@pytest.mark.parametrize("name", ["tiny", "ragged_mixed", "contig_rows", "empty_adapter", "prefill"])
+@pytest.mark.parametrize("name", ["tiny", "ragged_mixed", "contig_rows", "empty_adapter", "rmax62", "rmax21", "rmax40",
+                                  "rmax30", "prefill"])
 def test_backward_matches_oracle(name):
     print(f"[case] backward {name}", flush=True)
     wl, dy = _case(name)
