@@ -106,24 +106,27 @@ def test_pack_adapter_layout():
 
 
 @pytest.mark.parametrize("bad", [0, 61, -5], ids=["rank0", "rank_above_rmax", "negative"])
-@pytest.mark.parametrize("T", [16, 100], ids=["stream", "rows128"])
-def test_rank_outside_limits_is_reported(bad, T):
+@pytest.mark.parametrize("T", [16, 100, 300], ids=["stream", "rows128", "prefill"])
+@pytest.mark.parametrize("act", ["mxfp8", "bf16"])
+def test_rank_outside_limits_is_reported(bad, T, act):
     """An adapter whose rank (in device memory) is outside [1, r_max]: its tokens get the
-    base term only, the other tokens are unaffected, and the status word says so."""
+    base term only, the other tokens are unaffected, and the status word says so (at 300
+    tokens: the pre-pass down-projection, then the 128 x 256 or, with 16-bit activations,
+    the 64 x 256 tiles)."""
     import torch
     import precision_gemm_amd as P
     from workloads.device import upload
     from gpu_util import bf16_to_f64
-    print(f"[case] bad rank {bad} T={T}", flush=True)
+    print(f"[case] bad rank {bad} T={T} act={act}", flush=True)
     wl = _wl(T, 1024, 512, "fp8", MIXED, 400 + T)
     x, w, ad, ids = upload(wl)
     ad.ranks[2] = bad                                         # adapter 2 (rank 12) made invalid
     ws = P.alloc_workspace(wl.T, wl.K, wl.N, ad.n, ad.r_max)
     seg = P.build_segments(ids, ad.n)
-    y = P.gemm_lowp_lora_epilogue(x, w, seg, ad, ws, fuse_shrink=True)
+    y = P.gemm_lowp_lora_epilogue(x, w, seg, ad, ws, fuse_shrink=True, act_bf16=(act == "bf16"))
     torch.cuda.synchronize()
     assert P.workspace_status(ws) == 2
-    ref = run_oracle(wl)
+    ref = run_oracle(wl, act=act)
     yg = bf16_to_f64(y)
     on2 = np.flatnonzero(wl.ids == 2)
     rest = np.flatnonzero(wl.ids != 2)
@@ -144,9 +147,10 @@ def test_zero_w_gives_the_adapter_term(plan):
     ref = run_oracle(wl)
     assert not ref["y_base"].any()
     for fused in (True, False):
-        g = run_gpu(wl, fused=fused)
-        assert g["status"] == 0
-        assert_y_close(g["y"], ref["y_lora"], f"zero W {plan} fused={fused}")
+        for a16 in (False, True):  # the adapter term does not depend on the activation form
+            g = run_gpu(wl, fused=fused, act_bf16=a16)
+            assert g["status"] == 0
+            assert_y_close(g["y"], ref["y_lora"], f"zero W {plan} fused={fused} act_bf16={a16}")
 
 
 @pytest.mark.parametrize("start", [0x7FFFFFFF - 2, 0x3FFFFFFF - 1], ids=["int_max-2", "mask_top-1"])
