@@ -2618,8 +2618,9 @@ hipError_t launch_build_segments(const int* ids, int T, int n_ad, int* seg, int*
 }
 
 // ======================================================================================
-// The 16-bit-activation GEMM of a long batch (FP8 W, N % 256 == 0; t from the pre-pass's
-// down-projection): y = bf16(s_w (x . codes) + s_a t B_a) on bf16 MFMA.  A 64-token x
+// The 16-bit-activation GEMM of a long batch (FP8 W, N % 256 == 0; plain fp32 t from the
+// down-projection launched before it, or the caller's): y = bf16(s_w (x . codes) + s_a t B_a)
+// on bf16 MFMA.  A 64-token x
 // 256-channel tile per workgroup, four waves of 64 x 64, two workgroups per CU (their
 // barriers are independent, so one's loads, widening and waits overlap the other's MFMAs).
 // Per 128-wide k-step the tile's bf16 x rows [64][128] are staged in LDS a step ahead, double
@@ -2627,9 +2628,10 @@ hipError_t launch_build_segments(const int* ids, int T, int n_ad, int* seg, int*
 // ahead into one of two alternating register sets, widens the codes exactly (one conversion
 // per two codes) and issues 64 MFMAs: lane group g's 32 codes of a tile (k = 16 g .., 16 g + 8
 // .., 64 + 16 g .., 72 + 16 g ..) are four operands, each paired with the x piece at the
-// same k.  The loads are pinned at the top of the step.  Epilogue as for the MXFP8 tiles:
-// the channel scale, the adapter term per adapter present (s_a t rounded to bf16, one bf16
-// MFMA per 32 ranks and block), bf16 stores through LDS.  Workgroups are dealt to the XCDs
+// same k.  The loads are pinned at the top of the step.  Epilogue: the channel scale, then
+// for each adapter present in the tile (in increasing id order) one bf16 MFMA per 32 ranks
+// and block with s_a t rounded to bf16 (rows of other adapters zeroed) and B_a^T rows as the
+// other operand, then bf16 stores through LDS.  Workgroups are dealt to the XCDs
 // in turn; XCD x takes a contiguous run of tiles in row-block-major order (the column blocks
 // of a row block share its x rows in L2).
 // ======================================================================================
