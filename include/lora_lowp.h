@@ -359,7 +359,12 @@ lora_status lora_pack_adapter_bwd(const uint16_t* A, const uint16_t* B, int32_t 
  *    addresses in dA_ptrs / dB_ptrs, written, not accumulated into (zero for an adapter
  *    without tokens);
  *  - status: device int32 or NULL; bit 1 is OR-ed in when an adapter with tokens has a rank
- *    outside [1, r_max] (its dA_a and dB_a are not written and its tokens get dY W_d^T only).
+ *    outside [1, r_max] (its dA_a and dB_a are not written and its tokens get dY W_d^T only);
+ *  - workspace: device memory of lora_backward_workspace_bytes(T, K, N, n_adapters, r_max)
+ *    bytes, 16-byte aligned (NULL where that is 0): short batches split dX's contraction and
+ *    u's over N across workgroups and keep their fp32 partial sums there (added in a fixed
+ *    order, so the result does not depend on the split's timing); LORA_ERR_WORKSPACE when it
+ *    is missing or short.
  * Arithmetic: dY W_d^T = (dY diag(w_scale)) codes^T on bf16 MFMA: dY times the channel scale
  * rounded to bf16 (nearest even), the FP8 codes widened exactly, fp32 accumulation; u by the forward's
  * down-projection kernel (exact bf16 products, fp32 sums); the fp32 factors u, t of the
@@ -372,7 +377,14 @@ lora_status lora_backward(const uint16_t* x, const uint16_t* dy, const float* t,
                           const int32_t* seg_indptr, const int32_t* sorted_tok, const uint64_t* Bop_ptrs,
                           const uint64_t* Ar_ptrs, const int32_t* ranks, const float* scales, int32_t n_adapters,
                           int32_t r_max, uint16_t* dx, float* u, const uint64_t* dA_ptrs, const uint64_t* dB_ptrs,
-                          int32_t* status, void* stream);
+                          int32_t* status, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes lora_backward needs for these sizes: 0 where the 64-token x 256-column
+ * tiles of dX fill the GPU (about 6,000 or more tokens at K = 4096) and T > 128; else the
+ * fp32 partial sums of the split work: dX's contraction in up to 32 ranges of N (ranges x T x
+ * K x 4 bytes) and, up to 128 tokens, u = dY B_a^T in up to 32 parts of N (parts x T x r_max x
+ * 4 bytes).  0 for sizes or adapter counts lora_backward does not accept. */
+size_t lora_backward_workspace_bytes(int32_t T, int32_t K, int32_t N, int32_t n_adapters, int32_t r_max);
 
 /* Device-side status word of the layer calls on this workspace since it was last
  * initialised (bits accumulate): copies one int32 to *status_dev (device pointer) on

@@ -39,7 +39,8 @@ _SIGNATURES = {
     "lora_pack_weight_t": (c_i32, [c_i32, c_vp, c_i32, c_i32, c_vp, c_vp]),
     "lora_pack_adapter_bwd": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]),
     "lora_backward": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
-                              c_vp, c_vp, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
+                              c_vp, c_vp, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
+    "lora_backward_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "lora_shrink_config_info": (c_i32, [c_i32, c_i32, c_i32, ctypes.POINTER(c_i32)]),
     "lora_shrink_bgmv_info": (c_i32, [c_i32, c_i32, c_i32, ctypes.POINTER(c_i32)]),
     "lora_merged_layer": (c_i32, [c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,

@@ -147,6 +147,46 @@ LayerPlan make_plan(int T, int K, int N, int n_ad, int r_max_in, int fmt, bool f
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// The backward's work split for short batches, with the workspace its partial sums need.
+// dX: with fewer 64-row x 256-column tiles than fill the GPU, each tile's contraction over N is
+// split into ranges of an even number of 64-wide steps taken by workgroups of their own
+// (towards 512 workgroups: at most 32 ranges a tile, four or more steps each).  u = dY B_a^T
+// up to 128 tokens (the standalone down-projection, one item per adapter present): N is split
+// into parts of at least 256 (towards 256 items, at most 32 parts).
+struct BwdPlan {
+  int n_split, steps;      // dX ranges
+  int u_kparts, u_kpart_len;
+  size_t dx_bytes, u_bytes, total;
+};
+BwdPlan bwd_plan(int T, int K, int N, int n_ad, int r_max) {
+  const int NI = N / 64, tiles = ceil_div(T, 64) * ceil_div(K, 256);
+  BwdPlan b{1, NI, 1, N, 0, 0, 0};
+  if (T <= 0) return b;
+  if (tiles < 384) {
+    const int want = std::min({ceil_div(512, tiles), std::max(1, NI / 4), 32});
+    if (want > 1) {
+      int steps = ceil_div(NI, want);
+      steps += steps & 1;  // even: the loop alternates two register sets
+      if (ceil_div(NI, steps) > 1) {
+        b.n_split = ceil_div(NI, steps);
+        b.steps = steps;
+        b.dx_bytes = round256((size_t)b.n_split * T * K * 4);
+      }
+    }
+  }
+  if (T <= 128) {
+    const int kp = std::min({ceil_div(256, std::max(1, std::min(n_ad, T))), std::max(1, N / 256), 32});
+    if (kp > 1) {
+      b.u_kpart_len = ceil_div(ceil_div(N, kp), 256) * 256;
+      b.u_kparts = ceil_div(N, b.u_kpart_len);
+      if (b.u_kparts > 1) b.u_bytes = round256((size_t)b.u_kparts * T * r_max * 4);
+      else b.u_kpart_len = N;
+    }
+  }
+  b.total = b.dx_bytes + b.u_bytes;
+  return b;
+}
+
 }  // namespace
 
 extern "C" {
@@ -516,7 +556,7 @@ lora_status lora_backward(const uint16_t* x, const uint16_t* dy, const float* t,
                           const int32_t* seg_indptr, const int32_t* sorted_tok, const uint64_t* Bop_ptrs,
                           const uint64_t* Ar_ptrs, const int32_t* ranks, const float* scales, int32_t n_adapters,
                           int32_t r_max, uint16_t* dx, float* u, const uint64_t* dA_ptrs, const uint64_t* dB_ptrs,
-                          int32_t* status, void* stream) {
+                          int32_t* status, void* workspace, size_t workspace_bytes, void* stream) {
   if (w_fmt != LORA_W_FP8_E4M3 && w_fmt != LORA_W_MXFP4_E2M1) return LORA_ERR_INVALID_ARG;
   if (T < 0 || K <= 0 || N <= 0) return LORA_ERR_INVALID_ARG;
   if (w_fmt != LORA_W_FP8_E4M3 || T > 65536 || K % 128 != 0 || N % 128 != 0) return LORA_ERR_UNSUPPORTED;
@@ -538,6 +578,9 @@ lora_status lora_backward(const uint16_t* x, const uint16_t* dy, const float* t,
     return LORA_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(dy) || !aligned16(wt_q) || !aligned16(w_scale) || !aligned16(dx) || !aligned16(u))
     return LORA_ERR_INVALID_ARG;
+  const BwdPlan bp = bwd_plan(T, K, N, n_adapters, r_max);  // the split work's partial sums
+  if (bp.total > 0 && (!workspace || !aligned16(workspace) || workspace_bytes < bp.total)) return LORA_ERR_WORKSPACE;
+  char* wsb = reinterpret_cast<char*>(workspace);
   // u = dY B_a^T: the forward's down-projection kernel over N, with B_a in A_a's place
   const LayerPlan pl = make_plan(T, N, 64, n_adapters, r_max, LORA_W_FP8_E4M3, /*fused=*/false);
   ShrinkParams sp{};
@@ -553,6 +596,16 @@ lora_status lora_backward(const uint16_t* x, const uint16_t* dy, const float* t,
   if (T > 128) {
     sp.ids = adapter_id;
     if (launch_shrink_rows(sp, s) != hipSuccess) return LORA_ERR_HIP;
+  } else if (bp.u_kparts > 1) {
+    // N in parts, one item each: fp32 partial sums in the workspace, then added in order
+    LayerPlan pu = pl;
+    sp.kparts = bp.u_kparts; sp.kpart_len = bp.u_kpart_len;
+    sp.t_out = nullptr; sp.t_part = reinterpret_cast<float*>(wsb + bp.dx_bytes);
+    pu.s_kparts = bp.u_kparts; pu.s_kpart_len = bp.u_kpart_len;
+    pu.n_shrink_items = n_adapters * pl.s_ntblk * pl.s_njg * bp.u_kparts;
+    if (launch_shrink(pu, s, sp) != hipSuccess) return LORA_ERR_HIP;
+    if (launch_part_reduce(sp.t_part, bp.u_kparts, T, r_max, adapter_id, ranks, n_adapters, u, s) != hipSuccess)
+      return LORA_ERR_HIP;
   } else if (launch_shrink(pl, s, sp) != hipSuccess) {
     return LORA_ERR_HIP;
   }
@@ -562,7 +615,17 @@ lora_status lora_backward(const uint16_t* x, const uint16_t* dy, const float* t,
   dp.u = u; dp.r_lim = r_max; dp.ids = adapter_id; dp.Ar_ptrs = Ar_ptrs; dp.ranks = ranks; dp.scales = scales;
   dp.n_ad = n_adapters; dp.dx = dx;
   dp.n_tb = ceil_div(T, 64); dp.n_kb = ceil_div(K, 256);
-  return launch_bwd_dx(dp, s) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+  dp.n_split = bp.n_split; dp.split_steps = bp.steps;
+  dp.part = reinterpret_cast<float*>(wsb);
+  if (launch_bwd_dx(dp, s) != hipSuccess) return LORA_ERR_HIP;
+  if (dp.n_split > 1 && launch_bwd_dx_reduce(dp, s) != hipSuccess) return LORA_ERR_HIP;
+  return LORA_OK;
+}
+
+size_t lora_backward_workspace_bytes(int32_t T, int32_t K, int32_t N, int32_t n_adapters, int32_t r_max) {
+  if (T <= 0 || K <= 0 || N <= 0 || T > 65536 || K % 128 != 0 || N % 128 != 0) return 0;
+  if (check_adapters(n_adapters, r_max) != LORA_OK) return 0;
+  return bwd_plan(T, K, N, n_adapters, r_max).total;
 }
 
 lora_status lora_shrink_configured(const uint16_t* x, int32_t T, int32_t K, const int32_t* seg_indptr,

@@ -132,6 +132,9 @@ __device__ __forceinline__ int wave_min(int v) {
 // adapter present in the tile (in increasing id order) and each 32 ranks, two MFMAs per
 // block with the rows of other adapters zeroed and A_a rows [K][rank_pad] as the other
 // operand.  Rows whose adapter id or rank is invalid get the base term only.
+// Short batches (too few tiles to fill the GPU) split the contraction over N: workgroup
+// (tile, range) walks its range of steps and writes fp32 partial sums, range 0 with the
+// adapter term, and k_bwd_dx_reduce adds the ranges in order.
 // ---------------------------------------------------------------------------------
 
 constexpr int BX_RS = 144;              // LDS row stride (bytes): 64 bf16 + 16 bytes of bank offset
@@ -143,14 +146,18 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dx(BwdDxParams p) {
   __shared__ int rid[BX_ROWS];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, i = lane & 15, g = lane >> 4;
 
-  // tile order: workgroup b runs on XCD b % 8; each XCD takes a contiguous run of tiles in
-  // row-block-major order, so that the column blocks of a row block share its L2 for dY
-  const int ntiles = p.n_tb * p.n_kb;
-  int tile = blockIdx.x;
-  if ((ntiles & 7) == 0) tile = (tile & 7) * (ntiles >> 3) + (tile >> 3);
+  // tile order: workgroup b runs on XCD b % 8; each XCD takes a contiguous run of (tile,
+  // range) items in row-block-major order, so that the column blocks of a row block (and the
+  // ranges of a tile) share its L2 for dY
+  const int nitems = p.n_tb * p.n_kb * p.n_split;
+  int item = blockIdx.x;
+  if ((nitems & 7) == 0) item = (item & 7) * (nitems >> 3) + (item >> 3);
+  const int tile = item / p.n_split, split = item - tile * p.n_split;
   const int tb = tile / p.n_kb, kb = tile % p.n_kb;
   const int t0 = BX_ROWS * tb, k0w = 256 * kb + 64 * w;
   const int NI = p.N >> 6, nkt = p.K >> 4;
+  // this workgroup's steps [it0, it1): an even count (split_steps is even, and so is NI)
+  const int it0 = split * p.split_steps, it1 = min(NI, it0 + p.split_steps);
 
   // dY staging: thread loads row srow + 32 q (q = 0, 1), 16-byte part spart (8 channels)
   const int srow = tid >> 3, spart = tid & 7;
@@ -190,8 +197,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dx(BwdDxParams p) {
   // register copies, which would wait for the loads): N / 64 steps, an even number
   uint4 dn[2], wA[4], wB[4];
   float4 sn[2];
-  load_dy(dn, sn, 0);
-  load_w(wA, 0);
+  load_dy(dn, sn, it0);
+  load_w(wA, it0);
   store_dy(dn, sn, 0);
   __syncthreads();
 
@@ -202,7 +209,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dx(BwdDxParams p) {
     for (int ct = 0; ct < 4; ++ct) acc[tt][ct] = v4f{0.f, 0.f, 0.f, 0.f};
 
   auto step = [&](int it, const uint4 (&wc)[4], uint4 (&wn)[4]) {
-    const int nx = min(it + 1, NI - 1);  // the last step reloads itself: uniform code
+    const int nx = min(it + 1, it1 - 1);  // the last step reloads itself: uniform code
     load_dy(dn, sn, nx);
     load_w(wn, nx);
     __builtin_amdgcn_sched_barrier(0);  // the loads stay at the top: a whole step hides them
@@ -215,7 +222,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dx(BwdDxParams p) {
       wb[ct][0] = make_uint4(c0.x, c0.y, c1.x, c1.y);
       wb[ct][1] = make_uint4(c2.x, c2.y, c3.x, c3.y);
     }
-    const uint8_t* B0 = lds + (it & 1) * BX_BUF;
+    const uint8_t* B0 = lds + ((it - it0) & 1) * BX_BUF;
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
       const uint8_t* ra = B0 + (16 * tt + i) * BX_RS + 32 * g;
@@ -226,90 +233,108 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dx(BwdDxParams p) {
         acc[tt][ct] = mfma_bf16_16x16x32(a1, wb[ct][1], acc[tt][ct]);
       }
     }
-    store_dy(dn, sn, (it + 1) & 1);
+    store_dy(dn, sn, (it - it0 + 1) & 1);
     __syncthreads();
   };
-  for (int it = 0; it < NI; it += 2) {
+  for (int it = it0; it < it1; it += 2) {
     step(it, wA, wB);
     step(it + 1, wB, wA);
   }
+  const bool with_term = split == 0;  // the adapter term: once, in range 0
 
   // ---- adapter term
-  if (tid < BX_ROWS) {
-    const int t = t0 + tid;
-    int a = -1;
-    if (t < p.T) {
-      a = p.ids[t];
-      if (a < 0 || a >= p.n_ad) {
-        a = -1;
-      } else {
+  if (with_term) {
+    if (tid < BX_ROWS) {
+      const int t = t0 + tid;
+      int a = -1;
+      if (t < p.T) {
+        a = p.ids[t];
+        if (a < 0 || a >= p.n_ad) {
+          a = -1;
+        } else {
+          const int r = p.ranks[a];
+          if (r < 1 || r > p.r_lim) a = -1;
+        }
+      }
+      rid[tid] = a;
+    }
+    __syncthreads();
+    // s_a u[t] as two bf16 terms: hi in buffer 0, lo in buffer 1, [row][64 ranks]
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int row = srow + 32 * q;
+      const int a = rid[row];
+      float v[8];
+      if (a >= 0) {
         const int r = p.ranks[a];
-        if (r < 1 || r > p.r_lim) a = -1;
+        const float sa = p.scales[a];
+        const float* urow = p.u + (long)(t0 + row) * p.r_lim;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = 8 * spart + e;
+          v[e] = j < r ? sa * urow[j] : 0.f;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = 0.f;
       }
+      uint4 hi, lo;
+      split8(v, hi, lo);
+      *reinterpret_cast<uint4*>(lds + row * BX_RS + 16 * spart) = hi;
+      *reinterpret_cast<uint4*>(lds + BX_BUF + row * BX_RS + 16 * spart) = lo;
     }
-    rid[tid] = a;
-  }
-  __syncthreads();
-  // s_a u[t] as two bf16 terms: hi in buffer 0, lo in buffer 1, [row][64 ranks]
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int row = srow + 32 * q;
-    const int a = rid[row];
-    float v[8];
-    if (a >= 0) {
-      const int r = p.ranks[a];
-      const float sa = p.scales[a];
-      const float* urow = p.u + (long)(t0 + row) * p.r_lim;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = 8 * spart + e;
-        v[e] = j < r ? sa * urow[j] : 0.f;
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = 0.f;
-    }
-    uint4 hi, lo;
-    split8(v, hi, lo);
-    *reinterpret_cast<uint4*>(lds + row * BX_RS + 16 * spart) = hi;
-    *reinterpret_cast<uint4*>(lds + BX_BUF + row * BX_RS + 16 * spart) = lo;
-  }
-  __syncthreads();
-  int prev = -1;
-  for (;;) {
-    const int c = rid[lane];
-    int m = c > prev ? c : 0x7fffffff;
-    m = wave_min(m);
-    if (m == 0x7fffffff) break;
-    const int a = __builtin_amdgcn_readfirstlane(m);
-    prev = a;
-    const int r = p.ranks[a], rp = rank_pad(r);
-    const uint16_t* Ar = reinterpret_cast<const uint16_t*>(p.Ar_ptrs[a]);
-    for (int rs = 0; 32 * rs < r; ++rs) {
-      const int jj = 32 * rs + 8 * g;
-      const int off = min(jj, rp - 8);
-      uint4 bop[4];
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        const int k = min(k0w + 16 * ct + i, p.K - 1);
-        bop[ct] = keep_bf16(ldg16(Ar + (long)k * rp + off), r - jj);
-      }
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const int row = 16 * tt + i;
-        const bool mine = rid[row] == a;
-        const int o = row * BX_RS + 64 * rs + 16 * g;
-        const uint4 ah = mine ? lds16(lds + o) : zero4();
-        const uint4 al = mine ? lds16(lds + BX_BUF + o) : zero4();
+    __syncthreads();
+    int prev = -1;
+    for (;;) {
+      const int c = rid[lane];
+      int m = c > prev ? c : 0x7fffffff;
+      m = wave_min(m);
+      if (m == 0x7fffffff) break;
+      const int a = __builtin_amdgcn_readfirstlane(m);
+      prev = a;
+      const int r = p.ranks[a], rp = rank_pad(r);
+      const uint16_t* Ar = reinterpret_cast<const uint16_t*>(p.Ar_ptrs[a]);
+      for (int rs = 0; 32 * rs < r; ++rs) {
+        const int jj = 32 * rs + 8 * g;
+        const int off = min(jj, rp - 8);
+        uint4 bop[4];
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
-          acc[tt][ct] = mfma_bf16_16x16x32(ah, bop[ct], acc[tt][ct]);
-          acc[tt][ct] = mfma_bf16_16x16x32(al, bop[ct], acc[tt][ct]);
+          const int k = min(k0w + 16 * ct + i, p.K - 1);
+          bop[ct] = keep_bf16(ldg16(Ar + (long)k * rp + off), r - jj);
+        }
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          const int row = 16 * tt + i;
+          const bool mine = rid[row] == a;
+          const int o = row * BX_RS + 64 * rs + 16 * g;
+          const uint4 ah = mine ? lds16(lds + o) : zero4();
+          const uint4 al = mine ? lds16(lds + BX_BUF + o) : zero4();
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) {
+            acc[tt][ct] = mfma_bf16_16x16x32(ah, bop[ct], acc[tt][ct]);
+            acc[tt][ct] = mfma_bf16_16x16x32(al, bop[ct], acc[tt][ct]);
+          }
         }
       }
     }
+    __syncthreads();
   }
-  __syncthreads();
+
+  // ---- a range of a split contraction: fp32 partial sums, not rounded
+  if (p.n_split > 1) {
+    float* P = p.part + (long)split * p.T * p.K;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int t = t0 + 16 * tt + 4 * g + v, k = k0w + 16 * ct + i;
+          if (t < p.T && k < p.K) P[(long)t * p.K + k] = acc[tt][ct][v];
+        }
+    return;
+  }
 
   // ---- bf16 stores through LDS, 32 rows per pass: wave w's region holds its 32 x 64 block
   uint8_t* reg = lds + w * (32 * BX_RS);
@@ -501,8 +526,54 @@ __global__ __launch_bounds__(256, 2) void k_bwd_grad(BwdGradParams p) {
   }
 }
 
+// dx[t][k] = bf16(sum over the ranges, in order, of the partial sums): four columns a thread
+__global__ __launch_bounds__(256) void k_bwd_dx_reduce(BwdDxParams p) {
+  const long q = (long)blockIdx.x * 256 + threadIdx.x;  // index of four consecutive elements
+  const long n4 = (long)p.T * p.K / 4;
+  if (q >= n4) return;
+  const long stride = (long)p.T * p.K;
+  float4 acc = *reinterpret_cast<const float4*>(p.part + 4 * q);
+  for (int r = 1; r < p.n_split; ++r) {
+    const float4 v = *reinterpret_cast<const float4*>(p.part + r * stride + 4 * q);
+    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  }
+  *reinterpret_cast<uint2*>(p.dx + 4 * q) = make_uint2(bf16x2_rne(acc.x, acc.y), bf16x2_rne(acc.z, acc.w));
+}
+
+// out[tok][j] = sum over the K-parts in order (j < r_a), 0 for r_a <= j < r_lim: one thread
+// per element
+__global__ __launch_bounds__(256) void k_part_reduce(const float* __restrict__ part, int kparts, int T, int r_lim,
+                                                     const int* __restrict__ ids, const int* __restrict__ ranks,
+                                                     int n_ad, float* __restrict__ out) {
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long)T * r_lim) return;
+  const int tok = (int)(idx / r_lim), j = (int)(idx - (long)tok * r_lim);
+  const int a = ids[tok];
+  if (a < 0 || a >= n_ad) return;
+  const int r = ranks[a];
+  if (r < 1 || r > r_lim) return;
+  float v = 0.f;
+  if (j < r)
+    for (int q = 0; q < kparts; ++q) v += part[((long)q * T + tok) * r_lim + j];
+  out[idx] = v;
+}
+
+hipError_t launch_part_reduce(const float* part, int kparts, int T, int r_lim, const int* ids, const int* ranks,
+                              int n_ad, float* out, hipStream_t s) {
+  const long n = (long)T * r_lim;
+  hipLaunchKernelGGL(k_part_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, kparts, T, r_lim, ids,
+                     ranks, n_ad, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd_dx(const BwdDxParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(k_bwd_dx, dim3(p.n_tb * p.n_kb), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(k_bwd_dx, dim3(p.n_tb * p.n_kb * p.n_split), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dx_reduce(const BwdDxParams& p, hipStream_t s) {
+  const long n4 = (long)p.T * p.K / 4;
+  hipLaunchKernelGGL(k_bwd_dx_reduce, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

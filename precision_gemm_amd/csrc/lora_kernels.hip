@@ -557,6 +557,7 @@ __device__ __forceinline__ void shrink_item(const ShrinkParams& p, int item, cha
               st_agent_u64(p.t_tag + ((long)kp * p.T + tok) * p.r_max + j, tagged(sum[v], tag));
             }
             if (p.t_out && p.kparts == 1) p.t_out[tok * p.r_lim + j] = sum[v];
+            if (p.t_part) p.t_part[((long)kp * p.T + tok) * p.r_lim + j] = sum[v];
           }
         }
       }

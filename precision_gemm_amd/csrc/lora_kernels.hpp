@@ -52,6 +52,7 @@ struct ShrinkParams {
   int r_max;           // rank_pad of the caller's r_max: row stride of the tagged t
   int r_lim;           // the caller's r_max: largest valid rank, row stride of t_out
   float* t_out;        // plain fp32 [T][r_lim] (may be null in the fused launch)
+  float* t_part;       // standalone launch with K-parts: plain fp32 partial sums [kparts][T][r_lim] (else null)
   uint64_t* t_tag;     // tagged [kparts][T][r_max] (fused launch only, else null)
   int t_pack;          // t_tag holds [T][r_max / 2] tagged bf16 pairs of s_a t (one K-part)
   const float* scales; // adapter scales (for the pairs)
@@ -188,6 +189,8 @@ struct BwdDxParams {
   int n_ad;
   uint16_t* dx;            // bf16 [T][K]
   int n_tb, n_kb;          // 64-row and 256-column blocks
+  int n_split, split_steps;  // the contraction over N in n_split ranges of split_steps 64-wide steps
+  float* part;             // n_split > 1: fp32 partial sums [n_split][T][K] (the adapter term in range 0)
 };
 // dA_a = s_a X_a^T U_a [K][r_a] and dB_a = s_a T_a^T dY_a [r_a][N]: one workgroup per
 // (adapter, 64 rows of K) and (adapter, 64 columns of N).
@@ -213,6 +216,12 @@ hipError_t launch_pack_adapter_bwd(const uint16_t* A, const uint16_t* B, int K, 
                                    uint16_t* Ar, hipStream_t s);
 hipError_t launch_bwd_dx(const BwdDxParams& p, hipStream_t s);
 hipError_t launch_bwd_grad(const BwdGradParams& p, hipStream_t s);
+// dx = bf16 of the partial sums added in range order (n_split > 1)
+hipError_t launch_bwd_dx_reduce(const BwdDxParams& p, hipStream_t s);
+// out[tok][j] = the K-parts of part [kparts][T][r_lim] added in order for j < r_a, 0 for
+// r_a <= j < r_lim; tokens without a valid adapter or rank are left as they are
+hipError_t launch_part_reduce(const float* part, int kparts, int T, int r_lim, const int* ids, const int* ranks,
+                              int n_ad, float* out, hipStream_t s);
 hipError_t launch_pack_adapter(const uint16_t* A, const uint16_t* B, int K, int N, int r, uint16_t* At, uint16_t* Bt,
                                hipStream_t s);
 

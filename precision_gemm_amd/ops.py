@@ -423,14 +423,20 @@ def alloc_grads(ad: Adapters, K: int, N: int) -> Grads:
                       [torch.empty((r, N), dtype=torch.float32, device=dev) for r in rk])
 
 
+def backward_workspace_bytes(T: int, K: int, N: int, n_adapters: int, r_max: int) -> int:
+    """Bytes of the workspace lora_backward needs (0: none)."""
+    return int(lib().lora_backward_workspace_bytes(T, K, N, n_adapters, r_max))
+
+
 def lora_backward(x: torch.Tensor, dy: torch.Tensor, t: torch.Tensor, wt: torch.Tensor, w_scale: torch.Tensor,
                   seg: Segments, ad: Adapters, bw: BackwardAdapters, *, dx=None, u=None, grads: Grads | None = None,
-                  status: torch.Tensor | None = None):
+                  status: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
     """Gradients of the 16-bit-activation layer (lora_backward): returns ``(dx, u, grads)``
     with dx bf16 [T, K], u float32 [T, r_max] and ``grads`` (:class:`Grads`: dA[a] float32
     [K, r_a], dB[a] float32 [r_a, N]).  ``wt`` from :func:`pack_weight_t`, ``w_scale`` the FP8
-    channel scales, ``t`` the forward's down-projection.  Output buffers may be passed in
-    (then the call allocates nothing and can be captured in a HIP graph)."""
+    channel scales, ``t`` the forward's down-projection.  Output buffers and the workspace
+    (:func:`backward_workspace_bytes` bytes) may be passed in (then the call allocates nothing
+    and can be captured in a HIP graph)."""
     _dev(x, "x", torch.bfloat16)
     _dev(dy, "dy", torch.bfloat16)
     T, K = x.shape
@@ -442,9 +448,12 @@ def lora_backward(x: torch.Tensor, dy: torch.Tensor, t: torch.Tensor, wt: torch.
         u = torch.empty((T, ad.r_max), dtype=torch.float32, device=dev)
     if grads is None:
         grads = alloc_grads(ad, K, N)
+    nws = backward_workspace_bytes(T, K, N, ad.n, ad.r_max)
+    if workspace is None and nws > 0:
+        workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
     check("lora_backward", lib().lora_backward(
         _ptr(x), _ptr(dy), _ptr(t), T, K, N, LORA_W_FP8_E4M3, _ptr(wt), _ptr(w_scale), _ptr(seg.adapter_id),
         _ptr(seg.seg_indptr), _ptr(seg.sorted_tok), _ptr(bw.Bop_ptrs), _ptr(bw.Ar_ptrs), _ptr(ad.ranks),
         _ptr(ad.scales), ad.n, ad.r_max, _ptr(dx), _ptr(u), _ptr(grads.dA_ptrs), _ptr(grads.dB_ptrs), _ptr(status),
-        _stream()))
+        _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(), _stream()))
     return dx, u, grads

@@ -234,11 +234,12 @@ def test_shrink_configured_validation(L):
 
 def _bwd(L, **kw):
     a = dict(x=FAKE, dy=FAKE, t=FAKE, T=64, K=4096, N=4096, fmt=0, wt=FAKE, ws=FAKE, ids=FAKE, seg=FAKE, srt=FAKE,
-             Bop=FAKE, Ar=FAKE, rk=FAKE, sc=FAKE, n=8, r=64, dx=FAKE, u=FAKE, dA=FAKE, dB=FAKE, status=NULL)
+             Bop=FAKE, Ar=FAKE, rk=FAKE, sc=FAKE, n=8, r=64, dx=FAKE, u=FAKE, dA=FAKE, dB=FAKE, status=NULL,
+             work=NULL, work_bytes=0)
     a.update(kw)
     return L.lora_backward(a["x"], a["dy"], a["t"], a["T"], a["K"], a["N"], a["fmt"], a["wt"], a["ws"], a["ids"],
                            a["seg"], a["srt"], a["Bop"], a["Ar"], a["rk"], a["sc"], a["n"], a["r"], a["dx"], a["u"],
-                           a["dA"], a["dB"], a["status"], NULL)
+                           a["dA"], a["dB"], a["status"], a["work"], a["work_bytes"], NULL)
 
 
 def test_backward_validation(L):
@@ -257,6 +258,16 @@ def test_backward_validation(L):
         assert _bwd(L, **{name: NULL}) == INVALID, name
     for name in ("x", "dy", "wt", "ws", "dx", "u"):
         assert _bwd(L, **{name: MISALIGNED}) == INVALID, name
+    # short batches split dX's contraction: the partial sums need the workspace the query names
+    need = L.lora_backward_workspace_bytes(64, 4096, 4096, 8, 64)
+    # 16 tiles: 16 ranges of 4 steps; u: 8 adapters at most, 16 parts of 256 channels
+    assert need == 16 * 64 * 4096 * 4 + 16 * 64 * 64 * 4
+    assert L.lora_backward_workspace_bytes(8192, 4096, 4096, 8, 64) == 0     # 2048 tiles fill the GPU, T > 128
+    assert L.lora_backward_workspace_bytes(64, 4096, 4096 + 64, 8, 64) == 0  # sizes the call does not accept
+    assert L.lora_backward_workspace_bytes(64, 4096, 4096, 8, 65) == 0
+    assert _bwd(L) == WORKSPACE
+    assert _bwd(L, work=FAKE, work_bytes=need - 1) == WORKSPACE
+    assert _bwd(L, work=MISALIGNED, work_bytes=need) == WORKSPACE
     assert L.lora_pack_weight_t(1, FAKE, 4096, 4096, ctypes.c_void_p(0x4000000), NULL) == UNSUPPORTED
     assert L.lora_pack_weight_t(0, FAKE, 4096 + 64, 4096, ctypes.c_void_p(0x4000000), NULL) == UNSUPPORTED
     assert L.lora_pack_weight_t(0, FAKE, 4096, 4096, FAKE, NULL) == INVALID           # in place

@@ -14,8 +14,9 @@ Tolerances, from the arithmetic the header states:
 Cases: the tiny and the 4096-token prefill shapes of the layer, a ragged batch (T not a
 multiple of 128, K not a multiple of 256) with mixed ranks 1..60 in random order, several
 row blocks with contiguous segments, an adapter without tokens, largest ranks 62, 21, 40
-and 30 (two to four rank tiles in the gradient kernel), t from the GPU's own forward, T = 0,
-an invalid rank, and bitwise repeatability.
+and 30 (two to four rank tiles in the gradient kernel), short batches whose dX contraction is
+split over N (16, 8 and 4 ranges, a partial column block, a shorter last range), t from the
+GPU's own forward, T = 0, an invalid rank, and bitwise repeatability (whole and split).
 """
 
 import functools
@@ -51,6 +52,10 @@ CASES = {
     "rmax21": (100, 384, 256, [21, 3], "random"),
     "rmax40": (90, 256, 384, [40, 17], "random"),
     "rmax30": (100, 384, 256, [30, 7, 1], "contig"),
+    # short batches: dX's contraction over N split into ranges (workspace partial sums)
+    "split16": (40, 1024, 4096, [16, 64, 8], "random"),       # 4 tiles x 16 ranges of 4 steps
+    "split8_raggedK": (70, 640, 2048, [32, 5], "contig"),     # a half column block; 8 ranges
+    "split4_tail": (20, 512, 1408, [24, 1, 64], "random"),    # 4 ranges, the last shorter
 }
 
 
@@ -157,7 +162,7 @@ def check_against_oracle(wl, dy, g, ref, what):
 
 
 @pytest.mark.parametrize("name", ["tiny", "ragged_mixed", "contig_rows", "empty_adapter", "rmax62", "rmax21", "rmax40",
-                                  "rmax30", "prefill"])
+                                  "rmax30", "split16", "split8_raggedK", "split4_tail", "prefill"])
 def test_backward_matches_oracle(name):
     print(f"[case] backward {name}", flush=True)
     wl, dy = _case(name)
@@ -178,9 +183,10 @@ def test_backward_on_the_gpu_forward_t(name):
     check_against_oracle(wl, dy, g, _oracle(name), name + " gpu t")
 
 
-def test_backward_is_bitwise_repeatable():
-    wl, dy = _case("contig_rows")
-    a, b = run_backward(wl, dy, t=_oracle("contig_rows")["t"].astype(np.float32), repeat=2)
+@pytest.mark.parametrize("name", ["contig_rows", "split16"])
+def test_backward_is_bitwise_repeatable(name):
+    wl, dy = _case(name)
+    a, b = run_backward(wl, dy, t=_oracle(name)["t"].astype(np.float32), repeat=2)
     assert np.array_equal(a["dx_bits"], b["dx_bits"]) and np.array_equal(a["u"], b["u"])
     for k in ("dA", "dB"):
         for x, y in zip(a[k], b[k]):
