@@ -414,12 +414,13 @@ __global__ __launch_bounds__(256, 2) void k_bwd_grad(BwdGradParams p) {
     uint2 mr[8];
     float v[NJT][8];
   };
+  int nin = 1;  // positions of the current round staged in stok (reads past them take its last)
   // loads of chunk c of the round (positions base + 32 c ..): rows of M and V; positions
-  // past the segment read a token of the round and are zeroed at use
+  // past the segment read the round's last token and are zeroed at use
   auto load = [&](Chunk& ch, int c) {
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const int tok = stok[min(32 * c + 8 * g + q, GR_ROUND - 1)];
+      const int tok = stok[min(32 * c + 8 * g + q, nin - 1)];
       ch.mr[q] = *reinterpret_cast<const uint2*>(M + (long)tok * C + c0 + 4 * i);
 #pragma unroll
       for (int jt = 0; jt < NJT; ++jt) ch.v[jt][q] = V[(long)tok * p.r_lim + min(16 * jt + i, r - 1)];
@@ -462,9 +463,10 @@ __global__ __launch_bounds__(256, 2) void k_bwd_grad(BwdGradParams p) {
 
   for (int base = s_beg; base < s_end; base += GR_ROUND) {
     __syncthreads();  // the previous round's tokens are no longer read
-    for (int o = tid; o < GR_ROUND; o += 256) stok[o] = p.sorted_tok[min(base + o, s_end - 1)];
+    nin = min(GR_ROUND, s_end - base);  // the round's positions: only these are staged
+    for (int o = tid; o < nin; o += 256) stok[o] = p.sorted_tok[base + o];
     __syncthreads();
-    const int nch = (min(GR_ROUND, s_end - base) + 31) / 32;  // chunks of this round
+    const int nch = (nin + 31) / 32;  // chunks of this round
     // wave w takes chunks w, w + 4, ...; two register sets alternate, the next chunk's loads
     // in flight while one computes (the loads past the last chunk reload it, unused)
     Chunk A, B;
