@@ -16,7 +16,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "liblora_lowp.so")
-SOURCES = ["lora_kernels.hip", "lora_backward.hip", "lora_api.cpp"]
+SOURCES = ["lora_kernels.hip", "lora_gemm_pf.hip", "lora_backward.hip", "lora_api.cpp"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops off: no v_pk_{add,mul,fma}_f32 in the device code.

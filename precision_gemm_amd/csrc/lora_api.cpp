@@ -76,11 +76,19 @@ LayerPlan make_plan(int T, int K, int N, int n_ad, int r_max_in, int fmt, bool f
       pl.TT = 4;
     }
   }
+  // MXFP8 long batches with FP8 W, K and N multiples of 512 and at least 128 tiles of 128
+  // tokens x 512 channels: the eight-wave tiles of k_gemm_pf (two waves per SIMD, W straight
+  // into registers, x through LDS), x quantised in their operand order
+  if (!a16 && fmt == LORA_W_FP8_E4M3 && T > 128 && N % 512 == 0 && K % 512 == 0 &&
+      ceil_div(T, 128) * (N / 512) >= 128) {
+    pl.pf = true;
+    pl.TT = 8; pl.CT = 8; pl.WC = 4; pl.WK = 1; pl.XQ = true;
+  }
   // 16-bit activations past 128 tokens (FP8, N % 256 == 0): the down-projection runs first,
   // over 16-position blocks of the sorted order, and writes plain fp32 t; the GEMM then has
   // the whole GPU, in 64 x 256 tiles (two workgroups per CU) whose epilogue adds the term
   pl.rows16 = a16 && T > 128 && fmt == LORA_W_FP8_E4M3 && N % 256 == 0;
-  pl.KC = (pl.TT == 1) ? 2048 : ((pl.TT <= 4 && pl.CT == 1) ? 512 : (pl.CT == 4 ? 128 : 256));
+  pl.KC = (pl.TT == 1) ? 2048 : ((pl.TT <= 4 && pl.CT == 1) ? 512 : (pl.CT >= 4 ? 128 : 256));
   const int WN = pl.WC * pl.CT * 16;
   pl.n_cb = N / WN;
   pl.n_tb = ceil_div(T, 16 * pl.TT);
@@ -91,7 +99,7 @@ LayerPlan make_plan(int T, int K, int N, int n_ad, int r_max_in, int fmt, bool f
   // workgroups fill at most seven eighths of the 256 CUs, so that they all start beside
   // the last down-projection workgroups (measured on the 42-tile down-projection, µs per
   // step: 5 splits 112.6, 4 splits 122.4, 6 splits 131.3, 7 splits 138.7, 10 splits 135.7)
-  int ks = (tiles >= 128) ? 1 : std::min(max_split, std::max(1, 224 / tiles));
+  int ks = (tiles >= 128 || pl.pf) ? 1 : std::min(max_split, std::max(1, 224 / tiles));
   ks = std::max(ks, 1);
   pl.krange = ceil_div(ceil_div(K, ks), pl.KC) * pl.KC;
   pl.ksplit = ceil_div(K, pl.krange);
@@ -138,8 +146,10 @@ LayerPlan make_plan(int T, int K, int N, int n_ad, int r_max_in, int fmt, bool f
   pl.off_gflag = off; off += round256((size_t)tiles * pl.ksplit * 4);
   pl.off_gpart = off;
   if (pl.ksplit > 1) off += round256((size_t)tiles * pl.ksplit * pl.WC * pl.TT * pl.CT * 256 * 4);
-  pl.off_xq = off;    if (pl.XQ) off += round256((size_t)T * K);
-  pl.off_xsc = off;   if (pl.XQ) off += round256((size_t)T * (K / 32) + 8);  // + 8: padding read by a partial last chunk
+  // (the operand order of k_gemm_pf holds whole 128-row tiles; rows past T are never written)
+  const size_t xrows = pl.pf ? (size_t)pl.n_tb * 128 : (size_t)T;
+  pl.off_xq = off;    if (pl.XQ) off += round256(xrows * K);
+  pl.off_xsc = off;   if (pl.XQ) off += round256(xrows * (K / 32) + 8);  // + 8: padding read by a partial last chunk
   pl.off_tpl = off;   if ((pl.XQ || pl.rows16) && pl.s_cfg == 1) off += round256((size_t)T * r_max * 4);
   pl.total = off;
   return pl;
@@ -412,7 +422,7 @@ lora_status layer_call(const uint16_t* x, int32_t T, int32_t K, int32_t N, int32
     sp.seg_wait = 0;
     if (launch_quant_shrink(pl, sp, x, T, K, xq, xsc, s) != hipSuccess) return LORA_ERR_HIP;
     sp = ShrinkParams{};
-  } else if (build && !build_in && pl.XQ) {
+  } else if (build && !build_in && pl.XQ && !pl.pf) {
     // the builder as a workgroup of the MXFP8 pre-pass's launch
     if (launch_quant_build(x, T, K, xq, xsc, adapter_id, n_adapters, seg_indptr, sorted_tok, ctrl + CTRL_SEGERR, s) !=
         hipSuccess)
@@ -421,7 +431,8 @@ lora_status layer_call(const uint16_t* x, int32_t T, int32_t K, int32_t N, int32
     if (build && !build_in &&
         launch_build_segments(adapter_id, T, n_adapters, seg_indptr, sorted_tok, ctrl + CTRL_SEGERR, s) != hipSuccess)
       return LORA_ERR_HIP;
-    if (pl.XQ && launch_quant(x, T, K, xq, xsc, s) != hipSuccess) return LORA_ERR_HIP;
+    if (pl.XQ && (pl.pf ? launch_quant_pf(x, T, K, xq, xsc, s) : launch_quant(x, T, K, xq, xsc, s)) != hipSuccess)
+      return LORA_ERR_HIP;
   }
 
   uint64_t* ttag = reinterpret_cast<uint64_t*>(ws + pl.off_ttag);
@@ -468,6 +479,7 @@ lora_status layer_call(const uint16_t* x, int32_t T, int32_t K, int32_t N, int32
   gp.tile_group = 0;
   if (T > 128 && pl.ksplit == 1 && tiles % 8 == 0 && first_gemm % 8 == 0 && pl.TT != 1)
     gp.tile_group = (pl.n_cb % 4 == 0) ? 4 : ((pl.n_cb % 2 == 0) ? 2 : 1);
+  if (pl.pf) return launch_gemm_pf(gp, s) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
   return launch_layer(pl, s, sp, gp) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 

@@ -224,6 +224,8 @@ __device__ __forceinline__ uint32_t quad_swap1(uint32_t v) {  // value of lane ^
 __device__ __forceinline__ uint32_t quad_swap2(uint32_t v) {  // value of lane ^ 2 (DPP quad_perm 2,3,0,1)
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
 }
+// PK: codes and scales in the long-batch GEMM's operand order (pf_xq_off, pf_xsc_off)
+template <bool PK = false>
 __device__ __forceinline__ void quant_mxfp8_part(const uint16_t* __restrict__ x, int T, int K, uint8_t* __restrict__ xq,
                                                  uint8_t* __restrict__ xsc, int block, int n_blocks) {
   const long total = (long)T * (K / 8);  // a multiple of 4: whole blocks, so quads stay together
@@ -233,13 +235,20 @@ __device__ __forceinline__ void quant_mxfp8_part(const uint16_t* __restrict__ x,
     mx = max(mx, quad_swap1(mx));
     mx = max(mx, quad_swap2(mx));
     const uint32_t code = mx_code_from_bits(mx);
-    *reinterpret_cast<uint2*>(xq + P * 8) = mx_piece_quant(in, code);
-    if ((P & 3) == 0) xsc[P >> 2] = (uint8_t)code;
+    if (PK) {
+      const int row = (int)(P / (K >> 3)), kk = (int)(P % (K >> 3)) * 8;
+      *reinterpret_cast<uint2*>(xq + pf_xq_off(row, kk, K >> 7)) = mx_piece_quant(in, code);
+      if ((P & 3) == 0) xsc[pf_xsc_off(row, kk >> 5, K >> 7)] = (uint8_t)code;
+    } else {
+      *reinterpret_cast<uint2*>(xq + P * 8) = mx_piece_quant(in, code);
+      if ((P & 3) == 0) xsc[P >> 2] = (uint8_t)code;
+    }
   }
 }
+template <bool PK>
 __global__ __launch_bounds__(256) void k_quant_mxfp8(const uint16_t* __restrict__ x, int T, int K,
                                                      uint8_t* __restrict__ xq, uint8_t* __restrict__ xsc) {
-  quant_mxfp8_part(x, T, K, xq, xsc, blockIdx.x, gridDim.x);
+  quant_mxfp8_part<PK>(x, T, K, xq, xsc, blockIdx.x, gridDim.x);
 }
 // The segment builder (workgroup 0) beside the MXFP8 pre-pass (the others) in one launch:
 // the two do not depend on each other, so the builder's latency hides behind the pre-pass.
@@ -257,7 +266,7 @@ __global__ __launch_bounds__(SEG_THREADS) void k_quant_build(const uint16_t* __r
     int* wcnt = pres + (T <= SEG_CACHE ? min(T, n_ad) : 0);
     build_segments_wg<false, SEG_THREADS>(ids, T, n_ad, seg_indptr, sorted_tok, err, cnt, ids_s, pres, wcnt, w, w + 16);
   } else {
-    quant_mxfp8_part(x, T, K, xq, xsc, blockIdx.x - 1, gridDim.x - 1);
+    quant_mxfp8_part<false>(x, T, K, xq, xsc, blockIdx.x - 1, gridDim.x - 1);
   }
 }
 
@@ -2132,7 +2141,7 @@ constexpr int PREP_RS = 128 + 16;  // LDS row stride (bytes) of a wave's x slot:
 //    operand layout, lane (i, g) taking row i at 16 g .. 16 g + 15.
 //  - neither: the down-projection's rows p0 .. p0 + 15 loaded row-contiguously and relayed,
 //    with no quantisation (the backward's u = dY B_a^T).
-template <bool QUANT, bool SEP, int NJT>
+template <bool QUANT, bool SEP, int NJT, bool PK = false>
 __device__ __forceinline__ void prep_pass(uint8_t* __restrict__ xq, uint8_t* __restrict__ xsc, int K, int T, int p0,
                                           const uint16_t* x, const uint16_t* xrow_s, char* slot, bool s_mine,
                                           const uint16_t* arow0, int r, int kb, int nst, v4f (&acc)[4]) {
@@ -2182,8 +2191,14 @@ __device__ __forceinline__ void prep_pass(uint8_t* __restrict__ xq, uint8_t* __r
           mx = max(mx, quad_swap2(mx));
           const uint32_t code = mx_code_from_bits(mx);
           const int row = i ? crow1 : crow0;
-          *reinterpret_cast<uint2*>(xq + (long)row * K + k + 8 * (lane & 7)) = mx_piece_quant(xr[u][i], code);
-          xsc[(long)row * (K / 32) + (k >> 5) + ((lane & 7) >> 2)] = (uint8_t)code;
+          const int kk = k + 8 * (lane & 7);
+          if (PK) {
+            *reinterpret_cast<uint2*>(xq + pf_xq_off(row, kk, K >> 7)) = mx_piece_quant(xr[u][i], code);
+            xsc[pf_xsc_off(row, kk >> 5, K >> 7)] = (uint8_t)code;
+          } else {
+            *reinterpret_cast<uint2*>(xq + (long)row * K + kk) = mx_piece_quant(xr[u][i], code);
+            xsc[(long)row * (K / 32) + (kk >> 5)] = (uint8_t)code;
+          }
         }
         if (RELAY) *reinterpret_cast<uint4*>(slot + PREP_RS * (8 * i + (lane >> 3)) + 16 * (lane & 7)) = xr[u][i];
       }
@@ -2225,7 +2240,7 @@ __device__ __forceinline__ void prep_pass(uint8_t* __restrict__ xq, uint8_t* __r
 // pass also quantises x; without it the kernel is the down-projection alone (the backward's
 // u = dY B_a^T, B_a in A_a's operand order), its passes relaying contiguous rows where the
 // positions are consecutive tokens.
-template <int NJT, bool Q>
+template <int NJT, bool Q, bool PK = false>
 __global__ __launch_bounds__(256) void k_prep_rows(ShrinkParams sp, uint8_t* __restrict__ xq, uint8_t* __restrict__ xsc) {
   __shared__ __align__(16) float red[4][4][64][4];  // [wave][rank tile][lane][4]
   __shared__ __align__(16) char xslot[4][16 * PREP_RS];  // each wave's x relayout slot
@@ -2279,9 +2294,9 @@ __global__ __launch_bounds__(256) void k_prep_rows(ShrinkParams sp, uint8_t* __r
       else if (r > 0)
         prep_pass<false, true, NJT>(xq, xsc, K, T, p0, sp.x, xrow_s, slot, mine, arow0, r, kb, nst, acc);
     } else if (first && same) {
-      prep_pass<true, false, NJT>(xq, xsc, K, T, p0, sp.x, xrow_s, slot, mine, arow0, r, kb, nst, acc);
+      prep_pass<true, false, NJT, PK>(xq, xsc, K, T, p0, sp.x, xrow_s, slot, mine, arow0, r, kb, nst, acc);
     } else if (first) {
-      prep_pass<true, true, NJT>(xq, xsc, K, T, p0, sp.x, xrow_s, slot, mine, arow0, r, kb, nst, acc);
+      prep_pass<true, true, NJT, PK>(xq, xsc, K, T, p0, sp.x, xrow_s, slot, mine, arow0, r, kb, nst, acc);
     } else if (r > 0) {
       prep_pass<false, true, NJT>(xq, xsc, K, T, p0, sp.x, xrow_s, slot, mine, arow0, r, kb, nst, acc);
     }
@@ -2838,14 +2853,31 @@ hipError_t launch_gemm_a16(const GemmParams& gp, hipStream_t s) {
 hipError_t launch_quant(const uint16_t* x, int T, int K, uint8_t* xq, uint8_t* xsc, hipStream_t s) {
   const long blocks = ((long)T * (K / 8) + 255) / 256;
   const int grid = (int)std::min<long>(blocks, 8192);
-  hipLaunchKernelGGL(k_quant_mxfp8, dim3(grid), dim3(256), 0, s, x, T, K, xq, xsc);
+  hipLaunchKernelGGL(k_quant_mxfp8<false>, dim3(grid), dim3(256), 0, s, x, T, K, xq, xsc);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_pf(const uint16_t* x, int T, int K, uint8_t* xq, uint8_t* xsc, hipStream_t s) {
+  const long blocks = ((long)T * (K / 8) + 255) / 256;
+  const int grid = (int)std::min<long>(blocks, 8192);
+  hipLaunchKernelGGL(k_quant_mxfp8<true>, dim3(grid), dim3(256), 0, s, x, T, K, xq, xsc);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_shrink(const LayerPlan& pl, const ShrinkParams& sp, const uint16_t* x, int T, int K,
                                uint8_t* xq, uint8_t* xsc, hipStream_t s) {
-  (void)pl; (void)x; (void)K;
+  (void)x; (void)K;
   const dim3 grid((T + 15) / 16), block(256);
+  if (pl.pf) {  // codes and scales in the 256 x 256 GEMM's operand order
+    switch ((sp.r_lim + 15) / 16) {
+      case 1: hipLaunchKernelGGL((k_prep_rows<1, true, true>), grid, block, 0, s, sp, xq, xsc); break;
+      case 2: hipLaunchKernelGGL((k_prep_rows<2, true, true>), grid, block, 0, s, sp, xq, xsc); break;
+      case 3: hipLaunchKernelGGL((k_prep_rows<3, true, true>), grid, block, 0, s, sp, xq, xsc); break;
+      case 4: hipLaunchKernelGGL((k_prep_rows<4, true, true>), grid, block, 0, s, sp, xq, xsc); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch ((sp.r_lim + 15) / 16) {
     case 1: hipLaunchKernelGGL((k_prep_rows<1, true>), grid, block, 0, s, sp, xq, xsc); break;
     case 2: hipLaunchKernelGGL((k_prep_rows<2, true>), grid, block, 0, s, sp, xq, xsc); break;

@@ -31,6 +31,19 @@ __host__ __device__ constexpr long a_tile_off(int jt, int ks, int h, int K) {
   return (((long)jt * (K >> 6) + ks) * 2 + h) * 512;
 }
 
+// MXFP8 activations in the long-batch GEMM's operand order (k_gemm_pf), KS = K / 128:
+// codes [row tile of 16][KS][half h][lane][16 B], lane l = 16 g + i holding row i at
+// k = 128 ks + 64 h + 16 g .. + 15 (the scaled MFMA's operand, 1 KB per tile and half);
+// scale codes [row group of 64][KS][lane][4 B], byte tt of lane l = 16 g + i the code of
+// row 16 tt + i, K-block 4 ks + g (one word is the scale operand of four row tiles).
+__host__ __device__ constexpr long pf_xq_off(int row, int kk, int KS) {
+  return ((((long)(row >> 4) * KS + (kk >> 7)) * 2 + ((kk >> 6) & 1)) * 64 + 16 * ((kk >> 4) & 3) + (row & 15)) * 16 +
+         (kk & 15);
+}
+__host__ __device__ constexpr long pf_xsc_off(int row, int blk, int KS) {
+  return (((long)(row >> 6) * KS + (blk >> 2)) * 64 + 16 * (blk & 3) + (row & 15)) * 4 + ((row >> 4) & 3);
+}
+
 // Workspace control block (int32 words at the start of every workspace)
 enum : int {
   CTRL_EPOCH = 0,    // number of fused launches completed on this workspace (tag = epoch + 1)
@@ -121,6 +134,8 @@ struct LayerPlan {
   int occ = 1;         // workgroups per CU the one-tile stream kernel is built for
   bool a16 = false;    // base product on the bf16 activations as they are (bf16 MFMA)
   bool rows16 = false; // a16 long batch (FP8, N % 256 == 0): t by the rows pre-pass, then k_gemm_a16
+  bool pf = false;     // long MXFP8 batch (FP8, K and N % 512 == 0, enough tiles): 128 x 512 tiles of
+                       // k_gemm_pf on x in operand order (pf_xq_off, pf_xsc_off)
   int KC;              // K-chunk staged in LDS
   int ksplit, krange, n_cb, n_tb, n_gemm_wg;
   // down-projection decomposition
@@ -135,6 +150,10 @@ struct LayerPlan {
 
 hipError_t launch_build_segments(const int* ids, int T, int n_ad, int* seg, int* sorted, int* err, hipStream_t s);
 hipError_t launch_quant(const uint16_t* x, int T, int K, uint8_t* xq, uint8_t* xsc, hipStream_t s);
+// the same quantisation written in the long-batch GEMM's operand order (pf_xq_off, pf_xsc_off)
+hipError_t launch_quant_pf(const uint16_t* x, int T, int K, uint8_t* xq, uint8_t* xsc, hipStream_t s);
+// the long-batch GEMM: 128 x 512 tiles, eight waves, W into registers, x copied to LDS (k_gemm_pf)
+hipError_t launch_gemm_pf(const GemmParams& gp, hipStream_t s);
 // the 16-bit-activation GEMM of a long batch: 64 x 256 tiles, FP8 W (N % 256 == 0), plain t
 hipError_t launch_gemm_a16(const GemmParams& gp, hipStream_t s);
 // the segment builder and the MXFP8 pre-pass in one launch (independent of each other)

@@ -108,6 +108,23 @@ def test_other_entry_points_validation(L):
     assert L.lora_workspace_status(NULL, FAKE, NULL) == INVALID
 
 
+def test_plan_long_batch_tiles():
+    """Host plan (no GPU): MXFP8 batches past 128 tokens with FP8 W, K and N multiples of 512
+    and at least 128 tiles of 128 tokens x 512 channels take the eight-wave tiles (8 token
+    tiles x 8 column tiles x 4 waves of columns, no K-split); MXFP4 W, fewer tiles or other
+    K and N keep the 128 x 256 tiles."""
+    from precision_gemm_amd.ops import plan_info
+    for T, K, N, fmt, pf in [(4096, 4096, 4096, "fp8", True), (1000, 512, 8192, "fp8", True),
+                             (4100, 1024, 4096, "fp8", True), (4100, 256, 4096, "fp8", False),
+                             (3100, 384, 5376, "fp8", False), (300, 1024, 512, "fp8", False),
+                             (4096, 4096, 4096, "mxfp4", False), (4096, 1024, 4352, "fp8", False),
+                             (128, 4096, 8192, "fp8", False), (1000, 512, 4096, "fp8", False)]:
+        p = plan_info(T, K, N, 8, 64, fmt)
+        assert ((p["TT"], p["CT"], p["WC"]) == (8, 8, 4)) == pf, (T, K, N, fmt, p)
+        if pf:
+            assert p["ksplit"] == 1 and p["n_tb"] == -(-T // 128) and p["n_cb"] == N // 512 and p["XQ"] == 1
+
+
 def test_plan_down_projection_grid_and_k_split():
     """Host plan (no GPU): past 128 tokens the fused launch's down-projection grid holds
     every item that has work for any segment structure of T tokens (each adapter adds at

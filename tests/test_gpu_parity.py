@@ -205,6 +205,10 @@ LONG = [
     # T, K, N, ranks, seed: long batches of many tiles (128 x 256 tiles, pre-pass down-projection)
     (4100, 256, 4096, [1, 4, 12, 20, 60, 64], 31),  # 33 x 16 tiles, XCD-grouped order; a 4-row last token tile
     (3100, 384, 5376, [16, 64, 8], 32),              # 25 x 21 = 525 tiles: plain order
+    # 128 x 512 eight-wave tiles (k_gemm_pf): 33 x 8 tiles in the XCD-grouped order, a
+    # 4-row last token tile; 25 x 6 = 150 tiles (an odd number of row blocks), plain order
+    (4100, 1024, 4096, [1, 4, 12, 20, 60, 64], 33),
+    (3100, 512, 3072, [16, 64, 8], 34),
 ]
 
 

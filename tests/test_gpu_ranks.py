@@ -34,6 +34,7 @@ PLANS = [
     (100, 2048, 512, "fp8"),     # 128-row tiles, register B operands, K-split
     (128, 4096, 256, "mxfp4"),   # 128-row tiles, K-split
     (300, 1024, 512, "fp8"),     # prefill plan: 128 x 256 tiles, 64-token down-projection items
+    (1000, 512, 8192, "fp8"),    # 128 x 512 eight-wave tiles (k_gemm_pf), a 104-row last row block
     (200, 768, 384, "mxfp4"),    # 64-token tiles, two workgroups per CU
 ]
 
@@ -106,9 +107,10 @@ def test_pack_adapter_layout():
 
 
 @pytest.mark.parametrize("bad", [0, 61, -5], ids=["rank0", "rank_above_rmax", "negative"])
-@pytest.mark.parametrize("T", [16, 100, 300], ids=["stream", "rows128", "prefill"])
+@pytest.mark.parametrize("shape", [(16, 1024, 512), (100, 1024, 512), (300, 1024, 512), (1000, 512, 8192)],
+                         ids=["stream", "rows128", "prefill", "tiles128x512"])
 @pytest.mark.parametrize("act", ["mxfp8", "bf16"])
-def test_rank_outside_limits_is_reported(bad, T, act):
+def test_rank_outside_limits_is_reported(bad, shape, act):
     """An adapter whose rank (in device memory) is outside [1, r_max]: its tokens get the
     base term only, the other tokens are unaffected, and the status word says so (at 300
     tokens: the pre-pass down-projection, then the 128 x 256 or, with 16-bit activations,
@@ -117,8 +119,9 @@ def test_rank_outside_limits_is_reported(bad, T, act):
     import precision_gemm_amd as P
     from workloads.device import upload
     from gpu_util import bf16_to_f64
-    print(f"[case] bad rank {bad} T={T} act={act}", flush=True)
-    wl = _wl(T, 1024, 512, "fp8", MIXED, 400 + T)
+    T, K, N = shape
+    print(f"[case] bad rank {bad} shape={shape} act={act}", flush=True)
+    wl = _wl(T, K, N, "fp8", MIXED, 400 + T)
     x, w, ad, ids = upload(wl)
     ad.ranks[2] = bad                                         # adapter 2 (rank 12) made invalid
     ws = P.alloc_workspace(wl.T, wl.K, wl.N, ad.n, ad.r_max)
@@ -136,8 +139,8 @@ def test_rank_outside_limits_is_reported(bad, T, act):
 
 
 @pytest.mark.parametrize("plan", [(16, 2048, 512, "fp8"), (48, 1024, 512, "fp8"), (100, 2048, 512, "mxfp4"),
-                                  (300, 1024, 512, "fp8")],
-                         ids=["stream", "rows64", "rows128_ksplit", "prefill"])
+                                  (300, 1024, 512, "fp8"), (1000, 512, 8192, "fp8")],
+                         ids=["stream", "rows64", "rows128_ksplit", "prefill", "tiles128x512"])
 def test_zero_w_gives_the_adapter_term(plan):
     """With W = 0 the output is bf16(s_a t B_a) alone: the epilogue's adapter term on its own,
     on every plan (the base term cannot hide an error in it)."""
