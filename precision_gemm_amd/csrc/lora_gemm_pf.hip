@@ -133,29 +133,33 @@ __global__ __launch_bounds__(512) void k_gemm_pf(GemmParams p) {
     for (int ct = 0; ct < 4; ++ct) acc[rt][ct] = v4f{0.f, 0.f, 0.f, 0.f};
 
   v8i wr[2][4];
-  // (K is a multiple of 512: KS >= 4)
+  // (K is a multiple of 512: KS >= 4, even)
   issue_x(stg0, 0);
   issue_x(stg1, 1);
-  issue_x(stg2, 2);
   load_w(wr[0], 0);
   // one 128-wide step ks: register set C holds W of step ks, set 1 - C receives step ks + 1;
-  // stage S = ks % 4 holds x of step ks, stage (S + 3) % 4 receives step ks + 3
+  // stage S = ks % 4 holds x of step ks.  Stages go in pairs: an even step waits for the
+  // copies of its pair, passes the step pair's one barrier and copies the next pair
+  // (steps ks + 2, ks + 3) into the other two stages, read last in the previous pair
   auto step = [&](int ks, auto set, auto stage) {
     constexpr int C = decltype(set)::value, S = decltype(stage)::value;
     uint8_t* st = pf_stage<S>(stg0, stg1, stg2, stg3);
-    // this wave's copies of stage ks have landed: only what was issued after them may still
-    // be in flight, the W loads of steps ks - 1 and ks (8 each) and the three copies of each
-    // of stages ks + 1 and ks + 2 (the prologue issues fewer: then this waits a little more)
-    // (and its LDS reads of step ks - 1 are done, so that no copy issued after the barrier
-    // can overtake one)
-    __builtin_amdgcn_s_waitcnt((0x0070 | (22 & 15)) | ((22 >> 4) << 14));  // vmcnt(22) lgkmcnt(0)
-    pf_barrier();
-    // the last steps reload W of the last step and copy the last stage again (the same
+    if (S % 2 == 0) {
+      // this wave's copies of stages ks and ks + 1 have landed: only the W loads of step ks,
+      // issued after them, may still be in flight; and its LDS reads of the previous pair
+      // are done, so that no copy issued after the barrier can overtake one
+      __builtin_amdgcn_s_waitcnt(0x0070 | 8);  // vmcnt(8) lgkmcnt(0)
+      pf_barrier();
+    }
+    // the last steps reload W of the last step and copy the last pair again (the same
     // bytes to the same place): uniform code, exact wait counts.  W first: the MFMAs of
     // step ks + 1 then wait for these loads only, not for the copies issued after them
     load_w(wr[1 - C], min(ks + 1, KS - 1));
-    __builtin_amdgcn_sched_barrier(0);
-    issue_x(pf_stage<(S + 3) % 4>(stg0, stg1, stg2, stg3), min(ks + 3, KS - 1));
+    if (S % 2 == 0) {
+      __builtin_amdgcn_sched_barrier(0);
+      issue_x(pf_stage<(S + 2) % 4>(stg0, stg1, stg2, stg3), min(ks + 2, KS - 2));
+      issue_x(pf_stage<(S + 3) % 4>(stg0, stg1, stg2, stg3), min(ks + 3, KS - 1));
+    }
     __builtin_amdgcn_sched_barrier(0);  // the loads stay at the top: a whole step hides them
     const int sw0 = *reinterpret_cast<const int*>(st + PF_XBYTES + 4 * lane);
     const int sw1 = *reinterpret_cast<const int*>(st + PF_XBYTES + 256 + 4 * lane);
