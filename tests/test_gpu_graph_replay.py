@@ -1,5 +1,6 @@
 """Long-batch calls captured in a HIP graph and replayed: the fused layer call past 128
-tokens (MXFP8: the pre-pass with the down-projection, then the GEMM launch; 16-bit
+tokens (MXFP8: the pre-pass with the down-projection, then the GEMM launch, on 128 x 256
+and on 128 x 512 tiles; 16-bit
 activations: the rows down-projection, then the 64 x 256-tile GEMM), with t left in the
 workspace and the segments built by the call, and one lora_backward call with every output
 buffer passed in.  Each graph is replayed three times with eager work and synchronisations
@@ -18,13 +19,15 @@ pytestmark = pytest.mark.gpu
 RANKS = [8, 64, 24, 1, 16]
 
 
-@pytest.mark.parametrize("act_bf16", [False, True], ids=["mxfp8", "bf16"])
-def test_long_batch_layer_call_in_graph(act_bf16):
+@pytest.mark.parametrize("shape,act_bf16", [((300, 1024, 512), False), ((300, 1024, 512), True),
+                                            ((1000, 512, 8192), False)],
+                         ids=["mxfp8", "bf16", "mxfp8_tiles128x512"])
+def test_long_batch_layer_call_in_graph(shape, act_bf16):
     import torch
     import precision_gemm_amd as P
     from workloads.device import upload
     from oracle.segments import build_segments as oracle_segments
-    T, K, N = 300, 1024, 512
+    T, K, N = shape
     print(f"[case] graph replay, layer call T={T} K={K} N={N} act_bf16={act_bf16}", flush=True)
     ids = np.random.default_rng(90).integers(0, len(RANKS), T)
     wl = workloads.make_custom(T, K, N, "fp8", RANKS, ids, [1.5] * len(RANKS), 91, a_std=0.1, b_std=0.05)

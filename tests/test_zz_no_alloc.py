@@ -13,6 +13,7 @@ pytestmark = pytest.mark.gpu
 
 CALLS = [
     # T, K, N, fmt, ranks, flags: (build segments in the call, 16-bit activations)
+    (1000, 512, 8192, "fp8", [16, 64, 4, 12], (True, False)),    # 128 x 512 tiles, x in operand order in the scratch
     (300, 1024, 512, "fp8", [16, 64, 4, 12], (True, False)),     # prefill plan, pre-pass in the scratch
     (16, 2048, 256, "fp8", [1, 20, 60], (True, False)),          # smaller: the one-tile stream
     (100, 4096, 512, "mxfp4", [8, 16, 64], (False, False)),      # larger again: K-split partials
