@@ -150,7 +150,9 @@ LayerPlan make_plan(int T, int K, int N, int n_ad, int r_max_in, int fmt, bool f
   const size_t xrows = pl.pf ? (size_t)pl.n_tb * 128 : (size_t)T;
   pl.off_xq = off;    if (pl.XQ) off += round256(xrows * K);
   pl.off_xsc = off;   if (pl.XQ) off += round256(xrows * (K / 32) + 8);  // + 8: padding read by a partial last chunk
-  pl.off_tpl = off;   if ((pl.XQ || pl.rows16) && pl.s_cfg == 1) off += round256((size_t)T * r_max * 4);
+  pl.off_tpl = off;
+  if (pl.pf) off += round256((size_t)PF_KP * T * PF_TPS * 4);  // the pre-pass's K-part sums of t
+  else if ((pl.XQ || pl.rows16) && pl.s_cfg == 1) off += round256((size_t)T * r_max * 4);
   pl.total = off;
   return pl;
 }
@@ -372,7 +374,9 @@ lora_status layer_call(const uint16_t* x, int32_t T, int32_t K, int32_t N, int32
   // GEMM alone (its epilogue reads that t).  In the layer launch they would hold CUs that
   // the GEMM tiles need (prefill: 144 workgroups for ~30 us each).
   const bool pre_shrink = fused && pl.XQ && pl.s_cfg == 1;
-  float* t_pl = pre_shrink ? (t ? t : reinterpret_cast<float*>(ws + pl.off_tpl)) : nullptr;
+  // (with k_gemm_pf the pre-pass writes K-part sums into the workspace, and the GEMM adds them
+  // and stores the caller's t)
+  float* t_pl = pre_shrink ? ((t && !pl.pf) ? t : reinterpret_cast<float*>(ws + pl.off_tpl)) : nullptr;
   uint8_t* xq = reinterpret_cast<uint8_t*>(ws + pl.off_xq);
   uint8_t* xsc = reinterpret_cast<uint8_t*>(ws + pl.off_xsc);
   ShrinkParams sp{};
@@ -416,7 +420,8 @@ lora_status layer_call(const uint16_t* x, int32_t T, int32_t K, int32_t N, int32
                      hipSuccess)
       return LORA_ERR_HIP;
     shrink_params();
-    sp.t_out = t_pl;
+    sp.t_out = pl.pf ? nullptr : t_pl;
+    sp.t_part = pl.pf ? t_pl : nullptr;
     sp.t_tag = nullptr;
     sp.t_pack = 0;
     sp.seg_wait = 0;
@@ -453,9 +458,9 @@ lora_status layer_call(const uint16_t* x, int32_t T, int32_t K, int32_t N, int32
   gp.ws_fp8 = (w_fmt == LORA_W_FP8_E4M3) ? reinterpret_cast<const float*>(w_scale) : nullptr;
   gp.ws_fp4 = (w_fmt == LORA_W_MXFP4_E2M1) ? reinterpret_cast<const uint8_t*>(w_scale) : nullptr;
   gp.t = pre_shrink ? t_pl : (fused ? nullptr : t);
-  gp.t_out = (in_launch && pl.s_kparts > 1) ? t : nullptr;
+  gp.t_out = ((in_launch && pl.s_kparts > 1) || (pre_shrink && pl.pf)) ? t : nullptr;
   gp.t_tag = in_launch ? ttag : nullptr;
-  gp.t_kparts = pl.s_kparts;
+  gp.t_kparts = pl.pf ? (pre_shrink ? PF_KP : 1) : pl.s_kparts;
   gp.t_pack = (in_launch && pl.s_kparts == 1 && T > 16 && pl.TT != 1) ? 1 : 0;
   gp.r_max = rank_pad(r_max);
   gp.r_lim = r_max;

@@ -233,25 +233,54 @@ __global__ __launch_bounds__(512) void k_gemm_pf(GemmParams p) {
     rid[tid] = a;
   }
   __syncthreads();
-  // s_a t as bf16, [row][64 ranks] (zero past the row's rank and for rows without an
-  // adapter): thread = (row, quarter of the ranks)
+  // t = the pre-pass's K-part sums added in part order; s_a t as bf16, [row][64 ranks] (zero
+  // past the row's rank and for rows without an adapter): thread = (row, quarter of the
+  // ranks).  The tiles of column block 0 also store t for the caller.
   {
     const int row = tid >> 2, qq = tid & 3;
     const int a = rid[row];
     const int r = a >= 0 ? p.ranks[a] : 0;
     const float sa = a >= 0 ? p.scales[a] : 0.f;
-    const float* trow = p.t + (long)(t0 + row) * p.r_lim;
+    float tv[16];
+    if (p.t_kparts == PF_KP) {  // the pre-pass's partial sums, rows of PF_TPS
+      const long tpart = (long)T * PF_TPS;
+      const float* trow = p.t + (long)(t0 + row) * PF_TPS + 16 * qq;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (4 * c + 16 * qq < r) {
+          v = *reinterpret_cast<const float4*>(trow + 4 * c);
+#pragma unroll
+          for (int kp = 1; kp < PF_KP; ++kp) {
+            const float4 u = *reinterpret_cast<const float4*>(trow + kp * tpart + 4 * c);
+            v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+          }
+        }
+        tv[4 * c] = v.x; tv[4 * c + 1] = v.y; tv[4 * c + 2] = v.z; tv[4 * c + 3] = v.w;
+      }
+    } else {  // the caller's t [T][r_lim]
+      const float* trow = p.t + (long)(t0 + row) * p.r_lim + 16 * qq;
+#pragma unroll
+      for (int jl = 0; jl < 16; ++jl) tv[jl] = (16 * qq + jl < r) ? trow[jl] : 0.f;
+    }
     uint8_t* dst = tstg + row * PF_TRS;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const int j0 = 16 * qq + 8 * q;
       uint32_t o[4];
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const int j = j0 + 2 * d;
-        o[d] = bf16x2_rne(j < r ? sa * trow[j] : 0.f, j + 1 < r ? sa * trow[j + 1] : 0.f);
+        const int jl = 8 * q + 2 * d, j = 16 * qq + jl;
+        o[d] = bf16x2_rne(j < r ? sa * tv[jl] : 0.f, j + 1 < r ? sa * tv[jl + 1] : 0.f);
       }
-      *reinterpret_cast<uint4*>(dst + 2 * j0) = make_uint4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<uint4*>(dst + 2 * (16 * qq + 8 * q)) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+    if (p.t_out && cb == 0 && a >= 0) {
+      float* trow_out = p.t_out + (long)(t0 + row) * p.r_lim;
+#pragma unroll
+      for (int jl = 0; jl < 16; ++jl) {
+        const int j = 16 * qq + jl;
+        if (j < p.r_lim) trow_out[j] = j < r ? tv[jl] : 0.f;
+      }
     }
   }
   __syncthreads();

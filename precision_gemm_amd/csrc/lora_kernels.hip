@@ -2323,6 +2323,79 @@ __global__ __launch_bounds__(256) void k_prep_rows(ShrinkParams sp, uint8_t* __r
   }
 }
 
+// The pre-pass of the long-batch GEMM k_gemm_pf: the MXFP8 quantisation of x into that GEMM's
+// operand order and the down-projection t = x A_a, with K in PF_KP parts across workgroups.
+// A workgroup takes 64 consecutive positions of the sorted order and one K-part; wave w takes
+// positions 16 w .. 16 w + 15 (and quantises token rows p0 .. p0 + 15 over the part), so the
+// four waves read the same A_a slice at about the same time and share it through the cache,
+// where one workgroup per 16 positions read every adapter's whole A_a per 16 positions.  Each
+// wave writes its partial sums straight to t_part [PF_KP][T][PF_TPS] (fp32, zero past the
+// row's rank up to 16 NJT), which the GEMM's epilogue adds in part order.  Rows without a
+// valid adapter or rank are not written (the epilogue reads no t for them).  Workgroups are
+// dealt to the XCDs in turn; XCD x takes a contiguous run of (position block, part) pairs, so
+// the A_a of its segments stays in its L2.
+template <int NJT>
+__global__ __launch_bounds__(256) void k_prep_pf(ShrinkParams sp, uint8_t* __restrict__ xq, uint8_t* __restrict__ xsc) {
+  __shared__ __align__(16) char xslot[4][16 * PREP_RS];  // each wave's x relayout slot
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, li = lane & 15,
+            g = lane >> 4;
+  const int T = sp.T, K = sp.K;
+  const int nblk = gridDim.x, b = blockIdx.x;
+  const int L = (nblk % 8 == 0) ? (b & 7) * (nblk >> 3) + (b >> 3) : b;
+  const int kp = L % PF_KP, p0 = (L / PF_KP) * 64 + 16 * wave;
+  if (p0 >= T) return;  // wave-uniform: no rows (the kernel has no barrier)
+  const int kpl = K / PF_KP, kb = kp * kpl, nst = kpl >> 6;
+  const int n_valid = sp.seg_indptr[sp.n_ad];  // positions of tokens with a valid adapter
+  const int pos = p0 + li;
+  const bool s_ok = pos < n_valid;
+  const int tok_s = s_ok ? sp.sorted_tok[pos] : 0;
+  const int a_s = s_ok ? sp.ids[tok_s] : -1;
+  const bool same = __ballot(s_ok && tok_s != pos) == 0ull;
+  const uint16_t* xrow_s = sp.x + (long)tok_s * K + 16 * g;
+  v4f acc[4];
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt) acc[jt] = v4f{0.f, 0.f, 0.f, 0.f};
+  // one pass per adapter present among the wave's rows (the first also quantises)
+  unsigned long long todo = __ballot(li == lane && s_ok);
+  bool first = true;
+  char* slot = xslot[wave];
+  do {
+    int a = -1, r = 0;
+    if (todo) {
+      const int lead = __ffsll((long long)todo) - 1;
+      a = __builtin_amdgcn_readlane(a_s, lead);
+      todo &= ~__ballot(li == lane && s_ok && a_s == a);
+      r = sp.ranks[a];
+      if (r < 1 || r > sp.r_lim) r = 0;  // reported by the GEMM epilogue; no term
+    }
+    const bool mine = a >= 0 && r > 0 && s_ok && a_s == a;
+    const uint16_t* arow0 = reinterpret_cast<const uint16_t*>(r > 0 ? sp.A_ptrs[a] : (uint64_t)sp.x);
+    if (first && same) {
+      prep_pass<true, false, NJT, true>(xq, xsc, K, T, p0, sp.x, xrow_s, slot, mine, arow0, r, kb, nst, acc);
+    } else if (first) {
+      prep_pass<true, true, NJT, true>(xq, xsc, K, T, p0, sp.x, xrow_s, slot, mine, arow0, r, kb, nst, acc);
+    } else if (r > 0) {
+      prep_pass<false, true, NJT>(xq, xsc, K, T, p0, sp.x, xrow_s, slot, mine, arow0, r, kb, nst, acc);
+    }
+    first = false;
+  } while (todo);
+  // lane (i, g) holds rank 16 jt + i of rows 4 g + v
+  float* tp = sp.t_part + (long)kp * T * PF_TPS;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int row = 4 * g + v;
+    const int tok = __shfl(tok_s, row, 64), a = __shfl(a_s, row, 64);
+    if (p0 + row >= n_valid) continue;
+    const int r = sp.ranks[a];
+    if (r < 1 || r > sp.r_lim) continue;
+#pragma unroll
+    for (int jt = 0; jt < NJT; ++jt) {
+      const int j = 16 * jt + li;
+      tp[(long)tok * PF_TPS + j] = (j < r) ? acc[jt][v] : 0.f;
+    }
+  }
+}
+
 // ======================================================================================
 // The per-token merged-weight formulation, as an alternative to ablate against ("LoRA-Switch"
 // abstract: each token's adapter is merged into the backbone weights for inference, the merges
@@ -2868,12 +2941,14 @@ hipError_t launch_quant_shrink(const LayerPlan& pl, const ShrinkParams& sp, cons
                                uint8_t* xq, uint8_t* xsc, hipStream_t s) {
   (void)x; (void)K;
   const dim3 grid((T + 15) / 16), block(256);
-  if (pl.pf) {  // codes and scales in the 256 x 256 GEMM's operand order
+  if (pl.pf) {  // codes and scales in k_gemm_pf's operand order, t as PF_KP partial sums
+    const dim3 gpf(((T + 63) / 64) * PF_KP);
+    if (!sp.t_part || K % (64 * PF_KP) != 0) return hipErrorInvalidValue;
     switch ((sp.r_lim + 15) / 16) {
-      case 1: hipLaunchKernelGGL((k_prep_rows<1, true, true>), grid, block, 0, s, sp, xq, xsc); break;
-      case 2: hipLaunchKernelGGL((k_prep_rows<2, true, true>), grid, block, 0, s, sp, xq, xsc); break;
-      case 3: hipLaunchKernelGGL((k_prep_rows<3, true, true>), grid, block, 0, s, sp, xq, xsc); break;
-      case 4: hipLaunchKernelGGL((k_prep_rows<4, true, true>), grid, block, 0, s, sp, xq, xsc); break;
+      case 1: hipLaunchKernelGGL((k_prep_pf<1>), gpf, block, 0, s, sp, xq, xsc); break;
+      case 2: hipLaunchKernelGGL((k_prep_pf<2>), gpf, block, 0, s, sp, xq, xsc); break;
+      case 3: hipLaunchKernelGGL((k_prep_pf<3>), gpf, block, 0, s, sp, xq, xsc); break;
+      case 4: hipLaunchKernelGGL((k_prep_pf<4>), gpf, block, 0, s, sp, xq, xsc); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

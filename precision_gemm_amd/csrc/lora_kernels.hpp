@@ -44,6 +44,11 @@ __host__ __device__ constexpr long pf_xsc_off(int row, int blk, int KS) {
   return (((long)(row >> 6) * KS + (blk >> 2)) * 64 + 16 * (blk & 3) + (row & 15)) * 4 + ((row >> 4) & 3);
 }
 
+// The long-batch pre-pass (k_prep_pf) splits the down-projection's K into PF_KP parts and
+// writes their partial sums as fp32 [PF_KP][T][PF_TPS]; k_gemm_pf's epilogue adds them in
+// part order.
+constexpr int PF_KP = 4, PF_TPS = 64;
+
 // Workspace control block (int32 words at the start of every workspace)
 enum : int {
   CTRL_EPOCH = 0,    // number of fused launches completed on this workspace (tag = epoch + 1)
@@ -89,8 +94,10 @@ struct GemmParams {
   const uint8_t* wq;
   const float* ws_fp8;    // FP8 channel scales [N]
   const uint8_t* ws_fp4;  // MXFP4 block scales [N][K/32]
-  const float* t;         // plain t [T][r_lim] (unfused), or null
-  float* t_out;           // fused launch: the caller's t, written when t_kparts > 1 (may be null)
+  const float* t;         // plain t [T][r_lim] (unfused), or null; k_gemm_pf: the pre-pass's
+                          // partial sums [PF_KP][T][PF_TPS] when t_kparts == PF_KP
+  float* t_out;           // fused launch: the caller's t, written when t_kparts > 1 (may be null);
+                          // k_gemm_pf: written by the tiles of column block 0 (may be null)
   const uint64_t* t_tag;  // tagged t partials (fused), or null
   int t_kparts;
   int t_pack;             // t_tag holds tagged bf16 pairs of s_a t (see ShrinkParams)
