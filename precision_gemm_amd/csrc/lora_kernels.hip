@@ -2141,10 +2141,13 @@ constexpr int PREP_RS = 128 + 16;  // LDS row stride (bytes) of a wave's x slot:
 //    operand layout, lane (i, g) taking row i at 16 g .. 16 g + 15.
 //  - neither: the down-projection's rows p0 .. p0 + 15 loaded row-contiguously and relayed,
 //    with no quantisation (the backward's u = dY B_a^T).
-template <bool QUANT, bool SEP, int NJT, bool PK = false>
+//  - PRE: the contiguous rows' first PREP_U k-steps were loaded by the caller (xpre), ahead of
+//    the adapter look-ups the other loads depend on.
+template <bool QUANT, bool SEP, int NJT, bool PK = false, bool PRE = false>
 __device__ __forceinline__ void prep_pass(uint8_t* __restrict__ xq, uint8_t* __restrict__ xsc, int K, int T, int p0,
                                           const uint16_t* x, const uint16_t* xrow_s, char* slot, bool s_mine,
-                                          const uint16_t* arow0, int r, int kb, int nst, v4f (&acc)[4]) {
+                                          const uint16_t* arow0, int r, int kb, int nst, v4f (&acc)[4],
+                                          const uint4 (*xpre)[2] = nullptr) {
   constexpr int U = PREP_U;
   constexpr bool RELAY = !SEP && NJT > 0;  // operands through the LDS slot
   constexpr bool CONTIG = QUANT || RELAY;  // rows p0 .. p0 + 15 loaded row-contiguously
@@ -2162,9 +2165,9 @@ __device__ __forceinline__ void prep_pass(uint8_t* __restrict__ xq, uint8_t* __r
   const uint16_t* xc0 = x + (long)crow0 * K + 8 * (lane & 7);
   const uint16_t* xc1 = x + (long)crow1 * K + 8 * (lane & 7);
   uint4 xr[U][2], xs[U][2], ar[U][NJT > 0 ? NJT : 1][2];
-  auto issue = [&](int u, int st) {  // the clamped step is always valid
+  auto issue = [&](int u, int st, bool contig) {  // the clamped step is always valid
     const int k = kb + min(st, nst - 1) * 64;
-    if (CONTIG) {
+    if (contig) {
       xr[u][0] = ldg16(xc0 + k);
       xr[u][1] = ldg16(xc1 + k);
     }
@@ -2221,13 +2224,21 @@ __device__ __forceinline__ void prep_pass(uint8_t* __restrict__ xq, uint8_t* __r
   // (past the last step a refill loads that step again, never consumed); the last round only
   // consumes.
 #pragma unroll
-  for (int u = 0; u < U; ++u) issue(u, u);
+  for (int u = 0; u < U; ++u) {
+    if (PRE) {
+      xr[u][0] = xpre[u][0];
+      xr[u][1] = xpre[u][1];
+      issue(u, u, false);
+    } else {
+      issue(u, u, CONTIG);
+    }
+  }
   const int nround = (nst + U - 1) / U;
   for (int rd = 0; rd + 1 < nround; ++rd) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       consume(u, rd * U + u);
-      issue(u, (rd + 1) * U + u);
+      issue(u, (rd + 1) * U + u, CONTIG);
     }
   }
 #pragma unroll
@@ -2345,11 +2356,28 @@ __global__ __launch_bounds__(256) void k_prep_pf(ShrinkParams sp, uint8_t* __res
   const int kp = L % PF_KP, p0 = (L / PF_KP) * 64 + 16 * wave;
   if (p0 >= T) return;  // wave-uniform: no rows (the kernel has no barrier)
   const int kpl = K / PF_KP, kb = kp * kpl, nst = kpl >> 6;
+  // the first k-steps of the rows this wave quantises go out first: they do not depend on
+  // the adapter look-ups below (the same clamped rows and steps as prep_pass's loads)
+  uint4 xpre[PREP_U][2];
+  {
+    const uint16_t* xc0 = sp.x + (long)min(p0 + (lane >> 3), T - 1) * K + 8 * (lane & 7);
+    const uint16_t* xc1 = sp.x + (long)min(p0 + 8 + (lane >> 3), T - 1) * K + 8 * (lane & 7);
+#pragma unroll
+    for (int u = 0; u < PREP_U; ++u) {
+      const int k = kb + min(u, nst - 1) * 64;
+      xpre[u][0] = ldg16(xc0 + k);
+      xpre[u][1] = ldg16(xc1 + k);
+    }
+  }
+  // the position's token and adapter are loaded beside the count of valid positions (at a
+  // clamped index; used only below that count)
   const int n_valid = sp.seg_indptr[sp.n_ad];  // positions of tokens with a valid adapter
   const int pos = p0 + li;
+  const int tok_c = sp.sorted_tok[min(pos, T - 1)];
+  const int a_c = sp.ids[min(max(tok_c, 0), T - 1)];
   const bool s_ok = pos < n_valid;
-  const int tok_s = s_ok ? sp.sorted_tok[pos] : 0;
-  const int a_s = s_ok ? sp.ids[tok_s] : -1;
+  const int tok_s = s_ok ? tok_c : 0;
+  const int a_s = s_ok ? a_c : -1;
   const bool same = __ballot(s_ok && tok_s != pos) == 0ull;
   const uint16_t* xrow_s = sp.x + (long)tok_s * K + 16 * g;
   v4f acc[4];
@@ -2371,9 +2399,9 @@ __global__ __launch_bounds__(256) void k_prep_pf(ShrinkParams sp, uint8_t* __res
     const bool mine = a >= 0 && r > 0 && s_ok && a_s == a;
     const uint16_t* arow0 = reinterpret_cast<const uint16_t*>(r > 0 ? sp.A_ptrs[a] : (uint64_t)sp.x);
     if (first && same) {
-      prep_pass<true, false, NJT, true>(xq, xsc, K, T, p0, sp.x, xrow_s, slot, mine, arow0, r, kb, nst, acc);
+      prep_pass<true, false, NJT, true, true>(xq, xsc, K, T, p0, sp.x, xrow_s, slot, mine, arow0, r, kb, nst, acc, xpre);
     } else if (first) {
-      prep_pass<true, true, NJT, true>(xq, xsc, K, T, p0, sp.x, xrow_s, slot, mine, arow0, r, kb, nst, acc);
+      prep_pass<true, true, NJT, true, true>(xq, xsc, K, T, p0, sp.x, xrow_s, slot, mine, arow0, r, kb, nst, acc, xpre);
     } else if (r > 0) {
       prep_pass<false, true, NJT>(xq, xsc, K, T, p0, sp.x, xrow_s, slot, mine, arow0, r, kb, nst, acc);
     }
