@@ -234,6 +234,39 @@ def test_long_batch_shapes(case, mode):
     print(f"  y max_rel={m:.2e} frob={f:.2e}", flush=True)
 
 
+# Long MXFP8 batches on the 128 x 512 tiles whose tokens come in runs of one adapter (the
+# prefill form: positions are tokens), with run lengths that are not multiples of 16: waves
+# of the pre-pass whose 16 positions hold two adapters, 64-position blocks split over several,
+# a last block of 4 positions, and (second case) a tail of tokens without an adapter.
+PF_RUNS = [
+    (4100, 1024, 4096, [1, 4, 12, 20, 60, 64], [7, 300, 1, 513, 29, 1000, 250, 2000], 41),
+    (1000, 512, 8192, [64, 16, 33], [100, 3, 17, 700], 42),
+]
+
+
+@pytest.mark.parametrize("case", PF_RUNS, ids=[f"T{c[0]}_K{c[1]}_N{c[2]}" for c in PF_RUNS])
+@pytest.mark.parametrize("mode", ["fused", "build"])
+def test_long_batch_adapter_runs(case, mode):
+    T, K, N, ranks, runs, seed = case
+    print(f"[case] long batch in adapter runs {case[:3]} {mode}", flush=True)
+    ids = np.concatenate([np.full(n, i % len(ranks)) for i, n in enumerate(runs)] +
+                         [np.full(T - sum(runs), -1)]).astype(np.int32)
+    wl = _custom(T, K, N, "fp8", ranks, np.maximum(ids, 0), seed, a_std=0.1, b_std=0.05)
+    wl.ids = ids
+    rows = np.asarray(sorted(set(sample_rows(wl, 256, seed)) | set(range(256 * (T // 256), T))))
+    good, bad = rows[ids[rows] >= 0], rows[ids[rows] < 0]
+    g = run_gpu(wl, fused=True, want_t=True, build=(mode == "build"))
+    assert g["status"] == 0 and (g["err"] != 0) == bool((ids < 0).any())
+    ref = run_oracle(wl, tuple(good.tolist()))
+    m, f = assert_y_close(g["y"][good], ref["y"], f"{case[:3]} {mode}")
+    assert_t_close(g["t"][good].astype(np.float64), ref["t"], f"{case[:3]} {mode}")
+    if len(bad):
+        from oracle.layer import LowpWeight as OW, base_gemm
+        xq, xs = quantize_mxfp8(wl.x[bad])
+        assert_y_close(g["y"][bad], base_gemm(xq, xs, OW(wl.fmt, wl.w_q, wl.w_scale)), "tokens without an adapter")
+    print(f"  y max_rel={m:.2e} frob={f:.2e}", flush=True)
+
+
 def test_zero_b_equals_base_only_and_zero_w_gives_lora():
     wl = _custom(48, 1024, 512, "fp8", [16, 32, 8], np.arange(48) % 3, 11, zero_b=True)
     fused = run_gpu(wl, fused=True)
