@@ -20,7 +20,8 @@
 // Epilogue: the channel scale, then for each adapter present among the tile's rows
 // (ascending id) one bf16 MFMA per 32 ranks, row tile and column tile with s_a t rounded to
 // bf16 (rows of other adapters zeroed) and B_a^T rows as the other operand, then 8-byte bf16
-// stores.  Workgroups are dealt to the eight XCDs in turn; XCD x takes a contiguous run of
+// stores.  t is the sum, in part order, of the pre-pass's partial sums over four parts of K
+// (the tiles of column block 0 also store it for the caller), or the caller's t.  Workgroups are dealt to the eight XCDs in turn; XCD x takes a contiguous run of
 // tiles in an order grouped by row blocks, so the tiles an XCD runs together share x and W in
 // its L2.
 #include "device_common.hpp"
