@@ -303,7 +303,7 @@ lora_status gemm_lowp_lora_epilogue(const uint16_t* x, int32_t T, int32_t K, int
  * the process ends); the call allocates nothing and calls no allocating routine.
  *  - Sizes whose lora_workspace_bytes exceed LORA_NOALLOC_SCRATCH_BYTES return
  *    LORA_ERR_SCRATCH_LIMIT and enqueue nothing (every shape of the pages' workloads
- *    fits: the 4096-token prefill needs 18.5 MiB).
+ *    fits: the 4096-token prefill needs 22.5 MiB).
  *  - All calls on one GPU share its array: calls on one GPU must be ordered on one
  *    stream (calls that overlap in time on one GPU race).  The first call on a GPU, and
  *    a call whose sizes lay the array out differently from the previous call's on that
